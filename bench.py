@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of the sigmoid-routed MXFP4 expert layer on one MI355X.
+
+One step = the whole hot path for one batch of synthetic tokens: route
+(router GEMV, sigmoid + bias top-k) and forward (token fp8 expansion,
+permutation, routed gate/up + activation, shared gate/up, down + router-order
+combine + shared down), through the C ABI on one HIP stream. Inputs are
+resident in HBM before the timed region starts.
+
+Workloads (full shape: hidden 7168, 896 experts, top-16, inter 1536, one bf16
+shared expert of inter 1536, bias N(0, 0.01)):
+  decode   T = 1 token per step (default; the metric's configuration)
+  batched  T = 64, uniformly random routing
+  prefill  T = 2048, Zipf(1.1)-skewed routing
+Steps rotate over a pool of token batches so consecutive steps select
+different experts (the 281 MB a decode step touches is not left in the
+256 MB last-level cache by the previous step).
+
+Prints one JSON line. ``value`` is routed-expert HBM GB/s: the algorithmic
+bytes of the experts the step selects (17,547,264 B each, counted once per
+distinct expert) over the whole step time. ``roofline`` is the dominant
+kernel's algorithmic bytes per launch over its event-timed average duration
+(measured in a second pass with per-stage events on), against 8 TB/s.
+``cpu_baseline`` times the fp64 oracle on this host's cores on a bounded
+sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed-expert HBM GB/s (decode) and tokens/s per MoE layer, % of roofline"
+HBM_PEAK_GBPS = 8000.0
+EXPERT_MATRIX_BYTES = None  # filled from the spec
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def matrix_bytes(rows, cols):
+    return rows * cols // 2 + rows * cols // 32
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", choices=("decode", "batched", "prefill"), default="decode")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the layer is measured "
+                          "on one MI355X (expert-parallel sharding is a design note, not a "
+                          "measured path)", "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mxfp4_routed_expert_sigmoid_amd as k3
+    import synth
+    import synth.device as sd
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    T, routing, pool = {"decode": (1, "normal", 64), "batched": (64, "normal", 8),
+                        "prefill": (2048, "zipf", 2)}[args.workload]
+    spec = synth.full_spec(seed=0, routing=routing)
+    H, I, E, K, Is = spec.hidden, spec.inter, spec.n_experts, spec.topk, spec.shared_inter
+    log(f"[bench] building layer: {E} experts x {spec.expert_bytes} B resident")
+    tens = sd.layer_tensors(spec, 0, dev)
+    layer = sd.make_layer(spec, tens)
+    xs_np = [synth.make_x(spec, T, attempt=100 + p) for p in range(pool)]
+    xs = [sd.bf16_tensor(x, dev) for x in xs_np]
+    ws = layer.workspace(T)
+    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
+    w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        x = xs[i % pool]
+        layer.route(x, idx, w, workspace=ws, stream=stream)
+        layer.forward(x, idx, w, out, workspace=ws, stream=stream)
+
+    # distinct experts per pool entry (for the algorithmic byte counts)
+    distinct = []
+    for p in range(pool):
+        step(p)
+        torch.cuda.synchronize()
+        distinct.append(len(set(idx.cpu().numpy().ravel().tolist())))
+    assert layer.error_count() == 0
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms:.4f} ms/step")
+
+    # second pass with per-stage events (same steps)
+    layer.profile(True)
+    layer.profile_read(stream)
+    for i in range(args.steps):
+        step(i)
+    stages = layer.profile_read(stream)
+    layer.profile(False)
+    stage_us = {k: (v[0] * 1e3 / v[1] if v[1] else 0.0) for k, v in stages.items()}
+    log(f"[bench] stage us/launch: " + ", ".join(f"{k} {v:.2f}" for k, v in stage_us.items()))
+
+    # algorithmic bytes, averaged over the rotation actually timed
+    nd = sum(distinct[i % pool] for i in range(args.steps)) / args.steps
+    gu = matrix_bytes(I, H)
+    dn = matrix_bytes(H, I)
+    expert_b = 2 * gu + dn
+    routed_bytes = nd * expert_b
+    router_bytes = E * H * 2
+    shared_bytes = 3 * Is * H * 2
+    act_terms = T * K * 4 * I * (1 + 1 / 32)
+    x_terms = T * 4 * H * (1 + 1 / 32)
+    stage_bytes = {
+        "gateup": nd * 2 * gu + x_terms + act_terms,
+        "down": nd * dn + Is * H * 2 + act_terms + T * Is * 4 + T * H * 4,
+    }
+    dom = max(stage_bytes, key=lambda s: stage_us[s])
+    achieved = stage_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9
+    value = routed_bytes / (ms * 1e-3) / 1e9
+    layer_bytes = routed_bytes + router_bytes + shared_bytes + T * H * 2 + T * H * 4
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: T={T} tokens/step, hidden {H}, {E} experts top-{K}, "
+                        f"expert inter {I} (MXFP4), bf16 shared expert inter {Is}, sigmoid "
+                        f"router + bias N(0,0.01), {routing} routing",
+            "tokens_per_step": T,
+            "distinct_experts_per_step": round(nd, 2),
+        },
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "layer_GBps": round(layer_bytes / (ms * 1e-3) / 1e9, 2),
+        "routed_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+        "stage_us": {k: round(v, 3) for k, v in stage_us.items()},
+        "roofline": {
+            "kernel": {"gateup": "k_gateup", "down": "k_down"}[dom],
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "bytes_per_launch": round(stage_bytes[dom]),
+            "traffic": None,
+        },
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(spec, xs_np, T, args.cpu_seconds, expert_b)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(spec, xs_np, T, budget_s, expert_b):
+    """The fp64 oracle (route + forward) on this host, on whole tokens of the
+    same workload until about budget_s seconds of oracle time have passed.
+    Expert bytes are regenerated on the host outside the timed region."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    Wr = synth.make_router(spec)
+    bias = synth.make_bias(spec)
+    shared = synth.make_shared(spec)
+    spent = 0.0
+    tokens = 0
+    routed = 0
+    cand = [(p, t) for t in range(T) for p in range(len(xs_np))]
+    for p, t in cand:
+        x = xs_np[p][t:t + 1]
+        t0 = time.perf_counter()
+        idx, w = oracle.route(x, Wr, bias, spec.topk)
+        spent += time.perf_counter() - t0
+        used = sorted(set(idx.ravel().tolist()))
+        h = synth.expert_host(spec, used)
+        es = oracle.ExpertSet(used, spec.n_experts, h["gate_packed"], h["gate_scales"],
+                              h["up_packed"], h["up_scales"], h["down_packed"], h["down_scales"])
+        t0 = time.perf_counter()
+        oracle.forward(x, idx, w, es, spec.hidden, spec.inter, shared=shared,
+                       act_kind=spec.act, b1=spec.situ_b1, b2=spec.situ_b2, want_denom=False)
+        spent += time.perf_counter() - t0
+        tokens += 1
+        routed += len(used) * expert_b
+        log(f"[bench] cpu baseline: {tokens} tokens, {spent:.1f} s")
+        if spent >= budget_s:
+            break
+    return {
+        "value": round(routed / spent / 1e9, 4),
+        "unit": "GB/s",
+        "tokens_per_s": round(tokens / spent, 4),
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": f"{tokens} whole tokens (route + 16 experts + shared expert) of this workload, "
+                  f"one token per oracle call, {spent:.1f} s of oracle time",
+    }
+
+
+if __name__ == "__main__":
+    main()

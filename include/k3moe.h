@@ -1,0 +1,186 @@
+/*
+ * k3moe — sigmoid-routed MXFP4 expert layer for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI. Plain pointers and sizes only. Every tensor pointer is a DEVICE
+ * pointer owned by the caller; every call is asynchronous on the caller's HIP
+ * stream (passed as void*, a hipStream_t; NULL is the null stream) unless its
+ * comment says it synchronises.
+ *
+ * What the layer computes is stated on the "kimi-k3-in-c" README
+ * (FareedKhan-dev): §9 "Picking 16 experts of 896" gives the router
+ * (k3_router) and the layer (k3_moe, k3_situ_glu); §4 "Reduction one: the
+ * experts already ship at half a byte" gives the MXFP4 weight format. In this
+ * library the layer is flat: experts take the hidden vector directly (no
+ * latent down/up projection and no norm on the aggregate).
+ *
+ * Per token x (bf16, hidden H):
+ *   route:   logit[e] = Wr[e] . x                (exact products, fp64 sum)
+ *            sc[e] = fp32(sigmoid(fp32(logit[e])))   unbiased score
+ *            ch[e] = sc[e] + bias[e]  (fp32)          selection score
+ *            idx[0..k) = the k largest ch, largest first, equal ch -> lower e
+ *            w[j] = sc[idx[j]]; if renorm and s = sum_j w[j] > 0: w[j] /= s;
+ *            w[j] *= routed_scale                     (fp32, j order)
+ *   forward: out = sum_j w[j] * W2_e( act(W1_e x, W3_e x) ),  e = idx[j],
+ *                  summed in router order j = 0..k-1, then
+ *            out += S2( act(S1 x, S3 x) )             shared expert, unweighted
+ *   act:     SiTU-GLU  b1*tanh(g/b1) * sigmoid(g) * b2*tanh(u/b2)   (default)
+ *            SwiGLU    g * sigmoid(g) * u
+ *
+ * MXFP4 (README §4): weight = E2M1[nibble] * 2^(scale - 127); one E8M0
+ * scale byte per 32 consecutive weights of a row; within a packed byte the
+ * low nibble is the even-indexed weight; scale byte 255 makes its 32-group
+ * contribute nothing; scale byte 0 is 2^-127.
+ */
+#ifndef K3MOE_H
+#define K3MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define K3MOE_ABI_VERSION 1u
+
+typedef enum {
+    K3MOE_OK = 0,
+    K3MOE_E_INVALID_ARG = 1,       /* NULL pointer, negative size, ...       */
+    K3MOE_E_CONFIG = 2,            /* config field missing or out of range   */
+    K3MOE_E_UNSUPPORTED_SHAPE = 3, /* a size this build's kernels refuse     */
+    K3MOE_E_ALIGNMENT = 4,         /* a pointer or stride not 16-byte aligned */
+    K3MOE_E_WORKSPACE = 5,         /* workspace NULL, too small or misaligned */
+    K3MOE_E_OUT_OF_MEMORY = 6,     /* device memory could not be had         */
+    K3MOE_E_HIP = 7                /* a HIP runtime call or launch failed    */
+} k3moe_status;
+
+typedef enum {
+    K3MOE_ACT_SITU = 1,   /* SiTU-GLU with betas situ_b1, situ_b2 */
+    K3MOE_ACT_SWIGLU = 2  /* g * sigmoid(g) * u                   */
+} k3moe_act;              /* 0 is not a kind: an unset field is refused */
+
+/* Layer configuration. No field has a default: every one must be set, and
+ * struct_size / abi_version must equal sizeof(k3moe_config) and
+ * K3MOE_ABI_VERSION (README §2 states the same refusal to guess for the
+ * model's config). Supported sizes: hidden and inter positive multiples of
+ * 128; shared_inter 0 (no shared expert) or a positive multiple of 128;
+ * 1 <= topk <= n_experts <= 4096. */
+typedef struct {
+    uint32_t struct_size;
+    uint32_t abi_version;
+    int32_t hidden;        /* H: token width                                */
+    int32_t inter;         /* I: routed expert intermediate width           */
+    int32_t n_experts;     /* E                                             */
+    int32_t topk;          /* k                                             */
+    int32_t shared_inter;  /* I_s of the one bf16 shared expert, 0 = none   */
+    int32_t renorm;        /* 1: weights renormalised to sum 1; 0: not      */
+    float routed_scale;    /* multiplies every routing weight (finite)      */
+    int32_t act;           /* k3moe_act                                     */
+    float situ_b1;         /* SiTU gate beta (> 0, finite; README uses 4)   */
+    float situ_b2;         /* SiTU up beta   (> 0, finite; README uses 25)  */
+} k3moe_config;
+
+/* One MXFP4 matrix per expert, E of them. Expert e's packed nibbles start
+ * at packed + e * expert_stride_packed and are [rows][cols/2] bytes; its
+ * scales start at scales + e * expert_stride_scales and are [rows][cols/32]
+ * bytes. packed and expert_stride_packed must be multiples of 16; strides
+ * must be at least the matrix size. */
+typedef struct {
+    const uint8_t *packed;
+    const uint8_t *scales;
+    int64_t expert_stride_packed;
+    int64_t expert_stride_scales;
+} k3moe_mxfp4;
+
+/* The layer's weights (device pointers, caller-owned, never copied).
+ * gate (W1) and up (W3) are [inter][hidden]; down (W2) is [hidden][inter].
+ * router_w is bf16 [n_experts][hidden]; router_bias is fp32 [n_experts] or
+ * NULL for no bias. Shared expert (bf16, NULL iff shared_inter == 0):
+ * sh_gate and sh_up [shared_inter][hidden], sh_down [hidden][shared_inter].
+ * bf16 tensors are uint16 bit patterns; all bases 16-byte aligned. */
+typedef struct {
+    const uint16_t *router_w;
+    const float *router_bias;
+    k3moe_mxfp4 gate, up, down;
+    const uint16_t *sh_gate, *sh_up, *sh_down;
+} k3moe_weights;
+
+typedef struct k3moe_layer k3moe_layer;
+
+/* Validate the config and weight descriptors and make a layer handle on the
+ * current HIP device. The handle references the weights (it never copies or
+ * repacks them) and owns one 8-byte device error counter. Checks that the
+ * device has room for that counter before allocating. */
+k3moe_status k3moe_layer_create(const k3moe_config *cfg, const k3moe_weights *w,
+                                k3moe_layer **out);
+
+/* Bytes of workspace k3moe_route and k3moe_forward need for up to
+ * max_tokens tokens (max_tokens >= 0). The caller allocates it (256-byte
+ * aligned) and may reuse it across calls on one stream; calls in flight on
+ * different streams need different workspaces. */
+k3moe_status k3moe_workspace_size(const k3moe_layer *layer, int32_t max_tokens,
+                                  size_t *bytes);
+
+/* Route T tokens (README §9, k3_router).
+ *   x       bf16 [T][hidden]
+ *   idx     int32 [T][topk]    out: selected experts, router order
+ *   w       fp32  [T][topk]    out: routing weights
+ *   logits  fp32  [T][n_experts] out (optional, NULL = not written): the
+ *           fp32 logits the scores were taken from
+ * T == 0 does nothing. */
+k3moe_status k3moe_route(const k3moe_layer *layer, const uint16_t *x, int32_t T,
+                         int32_t *idx, float *w, float *logits,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* Expert layer for T tokens given their routes (README §9, k3_moe steps 3
+ * and 6, flat).
+ *   x    bf16  [T][hidden]
+ *   idx  int32 [T][topk]   expert ids; an id outside [0, n_experts)
+ *                          contributes nothing and is counted (see
+ *                          k3moe_error_count), as the README counts dropped
+ *                          experts instead of hiding them
+ *   w    fp32  [T][topk]
+ *   out  fp32  [T][hidden] out: written, not accumulated into
+ * Deterministic: the same inputs give the same bits on every call; the
+ * routed sum is taken in router order with no atomics. T == 0 does nothing. */
+k3moe_status k3moe_forward(const k3moe_layer *layer, const uint16_t *x, int32_t T,
+                           const int32_t *idx, const float *w, float *out,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Number of (token, slot) assignments with an out-of-range expert id seen by
+ * k3moe_forward since create or the last reset. Synchronises the stream. */
+k3moe_status k3moe_error_count(const k3moe_layer *layer, uint64_t *n, void *stream);
+k3moe_status k3moe_error_reset(k3moe_layer *layer, void *stream);
+
+/* Per-stage timing on the caller's stream. While enabled, route and forward
+ * record a HIP event pair around each of their kernel launches (stages
+ * below); k3moe_profile_read synchronises the stream, returns per stage the
+ * summed elapsed milliseconds and the number of launches since the last
+ * read, and clears the record. Recording adds two event records per launch
+ * to the stream, so time the layer itself with profiling off. */
+typedef enum {
+    K3MOE_STAGE_ROUTER = 0,         /* router logits, scores              */
+    K3MOE_STAGE_TOPK = 1,           /* top-k, weights                     */
+    K3MOE_STAGE_XSPLIT = 2,         /* token fp8 expansion                */
+    K3MOE_STAGE_PERM = 3,           /* token -> expert permutation        */
+    K3MOE_STAGE_GATEUP = 4,         /* routed gate/up MXFP4 + activation  */
+    K3MOE_STAGE_SHARED_GATEUP = 5,  /* shared expert gate/up + activation */
+    K3MOE_STAGE_DOWN = 6,           /* down MXFP4 + combine + shared down */
+    K3MOE_N_STAGES = 7
+} k3moe_stage;
+
+k3moe_status k3moe_profile_enable(k3moe_layer *layer, int enable);
+k3moe_status k3moe_profile_read(k3moe_layer *layer, double *ms, int64_t *launches,
+                                int32_t n_stages, void *stream);
+
+/* Frees the handle and its error counter (synchronises the device first).
+ * NULL is accepted. */
+void k3moe_layer_destroy(k3moe_layer *layer);
+
+const char *k3moe_status_string(k3moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* K3MOE_H */

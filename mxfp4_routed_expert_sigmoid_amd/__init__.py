@@ -1,0 +1,232 @@
+"""Python binding of libk3moe, the MI355X sigmoid-routed MXFP4 expert layer.
+
+Argument marshalling only: every step of the layer runs in the library's
+gfx950 kernels (``csrc/``); PyTorch supplies device buffers and the stream.
+The C ABI is declared in ``include/k3moe.h``; the names here mirror it.
+If the library has not been built this module raises ImportError: there is
+no fallback path.
+"""
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libk3moe.so")
+
+ABI_VERSION = 1
+ACT_SITU, ACT_SWIGLU = 1, 2
+
+STATUS = {0: "ok", 1: "invalid argument", 2: "invalid or incomplete config",
+          3: "unsupported shape", 4: "pointer or stride not aligned",
+          5: "workspace missing, misaligned or too small", 6: "out of device memory",
+          7: "HIP runtime error"}
+
+
+class K3MoeError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__(f"{what}: {STATUS.get(status, status)} (status {status})")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("struct_size", ctypes.c_uint32), ("abi_version", ctypes.c_uint32),
+                ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("shared_inter", ctypes.c_int32), ("renorm", ctypes.c_int32),
+                ("routed_scale", ctypes.c_float), ("act", ctypes.c_int32),
+                ("situ_b1", ctypes.c_float), ("situ_b2", ctypes.c_float)]
+
+
+class MXFP4(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("expert_stride_packed", ctypes.c_int64),
+                ("expert_stride_scales", ctypes.c_int64)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
+                ("gate", MXFP4), ("up", MXFP4), ("down", MXFP4),
+                ("sh_gate", ctypes.c_void_p), ("sh_up", ctypes.c_void_p),
+                ("sh_down", ctypes.c_void_p)]
+
+
+_lib = None
+EXPORTS = ("k3moe_layer_create", "k3moe_workspace_size", "k3moe_route", "k3moe_forward",
+           "k3moe_error_count", "k3moe_error_reset", "k3moe_profile_enable",
+           "k3moe_profile_read", "k3moe_layer_destroy", "k3moe_status_string")
+STAGES = ("router", "topk", "xsplit", "perm", "gateup", "shared_gateup", "down")
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int
+        L.k3moe_layer_create.restype = st
+        L.k3moe_layer_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weights),
+                                         ctypes.POINTER(P)]
+        L.k3moe_workspace_size.restype = st
+        L.k3moe_workspace_size.argtypes = [P, i32, ctypes.POINTER(ctypes.c_size_t)]
+        L.k3moe_route.restype = st
+        L.k3moe_route.argtypes = [P, P, i32, P, P, P, P, ctypes.c_size_t, P]
+        L.k3moe_forward.restype = st
+        L.k3moe_forward.argtypes = [P, P, i32, P, P, P, P, ctypes.c_size_t, P]
+        L.k3moe_error_count.restype = st
+        L.k3moe_error_count.argtypes = [P, ctypes.POINTER(ctypes.c_uint64), P]
+        L.k3moe_error_reset.restype = st
+        L.k3moe_error_reset.argtypes = [P, P]
+        L.k3moe_profile_enable.restype = st
+        L.k3moe_profile_enable.argtypes = [P, st]
+        L.k3moe_profile_read.restype = st
+        L.k3moe_profile_read.argtypes = [P, ctypes.POINTER(ctypes.c_double),
+                                         ctypes.POINTER(ctypes.c_int64), i32, P]
+        L.k3moe_layer_destroy.restype = None
+        L.k3moe_layer_destroy.argtypes = [P]
+        L.k3moe_status_string.restype = ctypes.c_char_p
+        L.k3moe_status_string.argtypes = [st]
+        _lib = L
+    return _lib
+
+
+def make_config(hidden, inter, n_experts, topk, shared_inter=0, renorm=1, routed_scale=1.0,
+                act=ACT_SITU, situ_b1=4.0, situ_b2=25.0):
+    return Config(ctypes.sizeof(Config), ABI_VERSION, hidden, inter, n_experts, topk,
+                  shared_inter, renorm, routed_scale, act, situ_b1, situ_b2)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, device):
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status, what):
+    if status != 0:
+        raise K3MoeError(status, what)
+
+
+def _dev(t, dtype_sizes, name):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.element_size() not in dtype_sizes:
+        raise ValueError(f"{name}: element size {t.element_size()} not in {dtype_sizes}")
+
+
+class Layer:
+    """A k3moe layer handle over caller-owned device weights.
+
+    Weights (device tensors, contiguous): router_w bf16/int16 [E][H];
+    router_bias fp32 [E] or None; gate/up packed uint8 [E][I][H/2] and scales
+    uint8 [E][I][H/32]; down packed [E][H][I/2] and scales [E][H][I/32];
+    shared sh_gate/sh_up [Is][H], sh_down [H][Is] (bf16/int16) or None.
+    The handle keeps references to the tensors so they outlive it.
+    """
+
+    def __init__(self, cfg: Config, router_w, router_bias, gate_packed, gate_scales, up_packed,
+                 up_scales, down_packed, down_scales, sh_gate=None, sh_up=None, sh_down=None):
+        for t, n in ((router_w, "router_w"), (sh_gate, "sh_gate"), (sh_up, "sh_up"),
+                     (sh_down, "sh_down")):
+            _dev(t, (2,), n)
+        _dev(router_bias, (4,), "router_bias")
+        for t, n in ((gate_packed, "gate_packed"), (gate_scales, "gate_scales"),
+                     (up_packed, "up_packed"), (up_scales, "up_scales"),
+                     (down_packed, "down_packed"), (down_scales, "down_scales")):
+            _dev(t, (1,), n)
+        self.cfg = cfg
+        self.device = router_w.device
+        self._keep = (router_w, router_bias, gate_packed, gate_scales, up_packed, up_scales,
+                      down_packed, down_scales, sh_gate, sh_up, sh_down)
+        E = cfg.n_experts
+
+        def mx(p, s):
+            return MXFP4(p.data_ptr(), s.data_ptr(), p.numel() // E, s.numel() // E)
+
+        self.weights = Weights(router_w.data_ptr(), _ptr(router_bias),
+                               mx(gate_packed, gate_scales), mx(up_packed, up_scales),
+                               mx(down_packed, down_scales), _ptr(sh_gate), _ptr(sh_up),
+                               _ptr(sh_down))
+        h = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            _check(lib().k3moe_layer_create(ctypes.byref(cfg), ctypes.byref(self.weights),
+                                            ctypes.byref(h)), "k3moe_layer_create")
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().k3moe_layer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def workspace_size(self, max_tokens: int) -> int:
+        n = ctypes.c_size_t()
+        _check(lib().k3moe_workspace_size(self.handle, int(max_tokens), ctypes.byref(n)),
+               "k3moe_workspace_size")
+        return n.value
+
+    def workspace(self, max_tokens: int):
+        """A device byte tensor big enough for max_tokens tokens (256-aligned)."""
+        return torch.empty(self.workspace_size(max_tokens) + 256, dtype=torch.uint8,
+                           device=self.device)
+
+    @staticmethod
+    def _ws(ws):
+        base = ws.data_ptr()
+        off = (-base) % 256
+        return ctypes.c_void_p(base + off), ws.numel() - off
+
+    def route(self, x, idx, w, logits=None, workspace=None, stream=None):
+        """k3moe_route: x bf16 [T][H] -> idx int32 [T][k], w fp32 [T][k] (written)."""
+        T = x.shape[0]
+        _dev(x, (2,), "x"), _dev(idx, (4,), "idx"), _dev(w, (4,), "w"), _dev(logits, (4,), "logits")
+        ws = workspace if workspace is not None else self.workspace(T)
+        p, n = self._ws(ws)
+        _check(lib().k3moe_route(self.handle, x.data_ptr(), T, idx.data_ptr(), w.data_ptr(),
+                                 _ptr(logits), p, n, _stream(stream, self.device)), "k3moe_route")
+
+    def forward(self, x, idx, w, out, workspace=None, stream=None):
+        """k3moe_forward: out fp32 [T][H] (written) from x, idx, w."""
+        T = x.shape[0]
+        _dev(x, (2,), "x"), _dev(idx, (4,), "idx"), _dev(w, (4,), "w"), _dev(out, (4,), "out")
+        ws = workspace if workspace is not None else self.workspace(T)
+        p, n = self._ws(ws)
+        _check(lib().k3moe_forward(self.handle, x.data_ptr(), T, idx.data_ptr(), w.data_ptr(),
+                                   out.data_ptr(), p, n, _stream(stream, self.device)),
+               "k3moe_forward")
+
+    def error_count(self, stream=None) -> int:
+        n = ctypes.c_uint64()
+        _check(lib().k3moe_error_count(self.handle, ctypes.byref(n), _stream(stream, self.device)),
+               "k3moe_error_count")
+        return n.value
+
+    def profile(self, enable: bool):
+        """Turn per-stage event timing on or off (k3moe_profile_enable)."""
+        _check(lib().k3moe_profile_enable(self.handle, int(bool(enable))), "k3moe_profile_enable")
+
+    def profile_read(self, stream=None):
+        """{stage: (total_ms, launches)} since the last read (k3moe_profile_read)."""
+        n = len(STAGES)
+        ms = (ctypes.c_double * n)()
+        cnt = (ctypes.c_int64 * n)()
+        _check(lib().k3moe_profile_read(self.handle, ms, cnt, n, _stream(stream, self.device)),
+               "k3moe_profile_read")
+        return {STAGES[i]: (ms[i], cnt[i]) for i in range(n)}
+
+    def error_reset(self, stream=None):
+        _check(lib().k3moe_error_reset(self.handle, _stream(stream, self.device)),
+               "k3moe_error_reset")

@@ -1,0 +1,321 @@
+// C-ABI entry points of libk3moe: argument validation, workspace layout,
+// launches on the caller's stream. See include/k3moe.h for the contract.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+
+#include "k3moe_internal.h"
+
+struct k3moe_layer {
+    k3moe_config cfg;
+    k3moe_weights w;
+    int device;
+    unsigned long long *errors;  // device counter of out-of-range expert ids
+    k3moe::Profiler *prof;       // per-stage event timing (k3moe_profile_*)
+};
+
+namespace k3moe {
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const k3moe_config &c, int64_t T)
+{
+    const int64_t H = c.hidden, I = c.inter, E = c.n_experts, K = c.topk, Is = c.shared_inter;
+    const int64_t nchunks = std::max<int64_t>(1, (T + kPermChunk - 1) / kPermChunk);
+    WsLayout L;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align256(o + std::max<size_t>(bytes, 1));
+        return at;
+    };
+    L.sc = take(sizeof(float) * T * E);
+    L.ch = take(sizeof(float) * T * E);
+    L.xq = take((size_t)T * kXTerms * H);
+    L.xs = take((size_t)T * kXTerms * (H / 32));
+    L.chunk_cnt = take(sizeof(int32_t) * nchunks * E);
+    L.active_n = take(sizeof(int32_t));
+    L.active_e = take(sizeof(int32_t) * E);
+    L.active_off = take(sizeof(int32_t) * (E + 1));
+    L.sorted = take(sizeof(int32_t) * std::max<int64_t>(1, T * K));
+    L.aq = take((size_t)T * K * kATerms * I);
+    L.as = take((size_t)T * K * kATerms * (I / 32));
+    L.ash = take(sizeof(float) * T * std::max<int64_t>(Is, 1));
+    L.total = o;
+    return L;
+}
+
+static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static k3moe_status check_config(const k3moe_config *c)
+{
+    if (!c) return K3MOE_E_INVALID_ARG;
+    if (c->struct_size != sizeof(k3moe_config) || c->abi_version != K3MOE_ABI_VERSION)
+        return K3MOE_E_CONFIG;
+    if (c->hidden <= 0 || c->inter <= 0 || c->n_experts <= 0 || c->topk <= 0 || c->shared_inter < 0)
+        return K3MOE_E_CONFIG;
+    if (c->topk > c->n_experts) return K3MOE_E_CONFIG;
+    if (c->renorm != 0 && c->renorm != 1) return K3MOE_E_CONFIG;
+    if (c->act != K3MOE_ACT_SITU && c->act != K3MOE_ACT_SWIGLU) return K3MOE_E_CONFIG;
+    if (!isfinite(c->routed_scale)) return K3MOE_E_CONFIG;
+    if (c->act == K3MOE_ACT_SITU &&
+        !(isfinite(c->situ_b1) && isfinite(c->situ_b2) && c->situ_b1 > 0.0f && c->situ_b2 > 0.0f))
+        return K3MOE_E_CONFIG;
+    if (c->hidden % 128 || c->inter % 128 || c->shared_inter % 128) return K3MOE_E_UNSUPPORTED_SHAPE;
+    if (c->n_experts > kMaxExperts || c->topk > kMaxTopk) return K3MOE_E_UNSUPPORTED_SHAPE;
+    // 32-bit row/element indexing inside the kernels
+    if ((int64_t)c->hidden * c->inter > (int64_t)1 << 30) return K3MOE_E_UNSUPPORTED_SHAPE;
+    return K3MOE_OK;
+}
+
+static k3moe_status check_mxfp4(const k3moe_mxfp4 &m, int64_t rows, int64_t cols, int64_t E)
+{
+    if (!m.packed || !m.scales) return K3MOE_E_INVALID_ARG;
+    const int64_t pbytes = rows * cols / 2, sbytes = rows * cols / 32;
+    if (E > 1 && (m.expert_stride_packed < pbytes || m.expert_stride_scales < sbytes))
+        return K3MOE_E_INVALID_ARG;
+    if (!aligned(m.packed, 16) || m.expert_stride_packed % 16) return K3MOE_E_ALIGNMENT;
+    return K3MOE_OK;
+}
+
+static k3moe_status check_weights(const k3moe_config *c, const k3moe_weights *w)
+{
+    if (!w) return K3MOE_E_INVALID_ARG;
+    if (!w->router_w) return K3MOE_E_INVALID_ARG;
+    if (!aligned(w->router_w, 16) || (w->router_bias && !aligned(w->router_bias, 4)))
+        return K3MOE_E_ALIGNMENT;
+    k3moe_status s;
+    if ((s = check_mxfp4(w->gate, c->inter, c->hidden, c->n_experts)) != K3MOE_OK) return s;
+    if ((s = check_mxfp4(w->up, c->inter, c->hidden, c->n_experts)) != K3MOE_OK) return s;
+    if ((s = check_mxfp4(w->down, c->hidden, c->inter, c->n_experts)) != K3MOE_OK) return s;
+    const bool any = w->sh_gate || w->sh_up || w->sh_down;
+    const bool all = w->sh_gate && w->sh_up && w->sh_down;
+    if (c->shared_inter == 0 ? any : !all) return K3MOE_E_INVALID_ARG;
+    if (all && !(aligned(w->sh_gate, 16) && aligned(w->sh_up, 16) && aligned(w->sh_down, 16)))
+        return K3MOE_E_ALIGNMENT;
+    return K3MOE_OK;
+}
+
+static LayerView view(const k3moe_layer *l)
+{
+    const k3moe_config &c = l->cfg;
+    const k3moe_weights &w = l->w;
+    LayerView v;
+    v.H = c.hidden;
+    v.I = c.inter;
+    v.E = c.n_experts;
+    v.K = c.topk;
+    v.Is = c.shared_inter;
+    v.renorm = c.renorm;
+    v.act = c.act;
+    v.routed_scale = c.routed_scale;
+    v.b1 = c.situ_b1;
+    v.b2 = c.situ_b2;
+    v.router_w = w.router_w;
+    v.router_bias = w.router_bias;
+    v.gp = w.gate.packed;
+    v.gs = w.gate.scales;
+    v.up = w.up.packed;
+    v.us = w.up.scales;
+    v.dp = w.down.packed;
+    v.ds = w.down.scales;
+    v.g_sp = w.gate.expert_stride_packed;
+    v.g_ss = w.gate.expert_stride_scales;
+    v.u_sp = w.up.expert_stride_packed;
+    v.u_ss = w.up.expert_stride_scales;
+    v.d_sp = w.down.expert_stride_packed;
+    v.d_ss = w.down.expert_stride_scales;
+    v.sh_gate = w.sh_gate;
+    v.sh_up = w.sh_up;
+    v.sh_down = w.sh_down;
+    v.errors = l->errors;
+    return v;
+}
+
+// Common checks of a route/forward call; T == 0 is reported as "nothing to do".
+static k3moe_status check_call(const k3moe_layer *l, int32_t T, void *ws, size_t ws_bytes,
+                               bool *nothing)
+{
+    *nothing = false;
+    if (!l || T < 0) return K3MOE_E_INVALID_ARG;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return K3MOE_E_HIP;
+    if (dev != l->device) return K3MOE_E_INVALID_ARG;
+    if (T == 0) {
+        *nothing = true;
+        return K3MOE_OK;
+    }
+    if (!ws || !aligned(ws, 256)) return K3MOE_E_WORKSPACE;
+    if (ws_bytes < ws_layout(l->cfg, T).total) return K3MOE_E_WORKSPACE;
+    return K3MOE_OK;
+}
+
+}  // namespace k3moe
+
+using namespace k3moe;
+
+extern "C" {
+
+k3moe_status k3moe_layer_create(const k3moe_config *cfg, const k3moe_weights *w, k3moe_layer **out)
+{
+    if (!out) return K3MOE_E_INVALID_ARG;
+    *out = nullptr;
+    k3moe_status s = check_config(cfg);
+    if (s != K3MOE_OK) return s;
+    if ((s = check_weights(cfg, w)) != K3MOE_OK) return s;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return K3MOE_E_HIP;
+    size_t free_b = 0, total_b = 0;
+    if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) return K3MOE_E_HIP;
+    if (free_b < (size_t)1 << 20) return K3MOE_E_OUT_OF_MEMORY;
+    k3moe_layer *l = new (std::nothrow) k3moe_layer;
+    if (!l) return K3MOE_E_OUT_OF_MEMORY;
+    l->cfg = *cfg;
+    l->w = *w;
+    l->device = dev;
+    l->errors = nullptr;
+    l->prof = new (std::nothrow) Profiler;
+    if (!l->prof) {
+        delete l;
+        return K3MOE_E_OUT_OF_MEMORY;
+    }
+    if (hipMalloc(&l->errors, sizeof(unsigned long long)) != hipSuccess) {
+        delete l->prof;
+        delete l;
+        return K3MOE_E_OUT_OF_MEMORY;
+    }
+    if (hipMemset(l->errors, 0, sizeof(unsigned long long)) != hipSuccess) {
+        (void)hipFree(l->errors);
+        delete l->prof;
+        delete l;
+        return K3MOE_E_HIP;
+    }
+    *out = l;
+    return K3MOE_OK;
+}
+
+k3moe_status k3moe_workspace_size(const k3moe_layer *l, int32_t max_tokens, size_t *bytes)
+{
+    if (!l || !bytes || max_tokens < 0) return K3MOE_E_INVALID_ARG;
+    *bytes = ws_layout(l->cfg, max_tokens).total;
+    return K3MOE_OK;
+}
+
+k3moe_status k3moe_route(const k3moe_layer *l, const uint16_t *x, int32_t T, int32_t *idx, float *w,
+                         float *logits, void *ws, size_t ws_bytes, void *stream)
+{
+    bool nothing;
+    k3moe_status s = check_call(l, T, ws, ws_bytes, &nothing);
+    if (s != K3MOE_OK || nothing) return s;
+    if (!x || !idx || !w) return K3MOE_E_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(idx, 4) || !aligned(w, 4) || (logits && !aligned(logits, 4)))
+        return K3MOE_E_ALIGNMENT;
+    const WsLayout lay = ws_layout(l->cfg, T);
+    if (launch_route(view(l), x, T, idx, w, logits, static_cast<char *>(ws), lay,
+                     static_cast<hipStream_t>(stream), l->prof) != hipSuccess)
+        return K3MOE_E_HIP;
+    return K3MOE_OK;
+}
+
+k3moe_status k3moe_forward(const k3moe_layer *l, const uint16_t *x, int32_t T, const int32_t *idx,
+                           const float *w, float *out, void *ws, size_t ws_bytes, void *stream)
+{
+    bool nothing;
+    k3moe_status s = check_call(l, T, ws, ws_bytes, &nothing);
+    if (s != K3MOE_OK || nothing) return s;
+    if (!x || !idx || !w || !out) return K3MOE_E_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(idx, 4) || !aligned(w, 4) || !aligned(out, 4))
+        return K3MOE_E_ALIGNMENT;
+    const WsLayout lay = ws_layout(l->cfg, T);
+    if (launch_forward(view(l), x, T, idx, w, out, static_cast<char *>(ws), lay,
+                       static_cast<hipStream_t>(stream), l->prof) != hipSuccess)
+        return K3MOE_E_HIP;
+    return K3MOE_OK;
+}
+
+k3moe_status k3moe_error_count(const k3moe_layer *l, uint64_t *n, void *stream)
+{
+    if (!l || !n) return K3MOE_E_INVALID_ARG;
+    unsigned long long v = 0;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(&v, l->errors, sizeof v, hipMemcpyDeviceToHost, s) != hipSuccess)
+        return K3MOE_E_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return K3MOE_E_HIP;
+    *n = v;
+    return K3MOE_OK;
+}
+
+k3moe_status k3moe_error_reset(k3moe_layer *l, void *stream)
+{
+    if (!l) return K3MOE_E_INVALID_ARG;
+    if (hipMemsetAsync(l->errors, 0, sizeof(unsigned long long), static_cast<hipStream_t>(stream)) !=
+        hipSuccess)
+        return K3MOE_E_HIP;
+    return K3MOE_OK;
+}
+
+k3moe_status k3moe_profile_enable(k3moe_layer *l, int enable)
+{
+    if (!l) return K3MOE_E_INVALID_ARG;
+    l->prof->on = enable != 0;
+    return K3MOE_OK;
+}
+
+k3moe_status k3moe_profile_read(k3moe_layer *l, double *ms, int64_t *launches, int32_t n_stages,
+                                void *stream)
+{
+    if (!l || !ms || !launches || n_stages < 0) return K3MOE_E_INVALID_ARG;
+    if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess) return K3MOE_E_HIP;
+    for (int i = 0; i < n_stages; ++i) {
+        ms[i] = 0.0;
+        launches[i] = 0;
+    }
+    Profiler &p = *l->prof;
+    k3moe_status st = K3MOE_OK;
+    for (const Profiler::Rec &r : p.recs) {
+        float t = 0.0f;
+        if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
+            st = K3MOE_E_HIP;
+        if (r.stage < n_stages) {
+            ms[r.stage] += t;
+            launches[r.stage] += 1;
+        }
+        p.spare.push_back(r.a);
+        p.spare.push_back(r.b);
+    }
+    p.recs.clear();
+    return st;
+}
+
+void k3moe_layer_destroy(k3moe_layer *l)
+{
+    if (!l) return;
+    (void)hipDeviceSynchronize();
+    (void)hipFree(l->errors);
+    for (const Profiler::Rec &r : l->prof->recs) {
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
+    for (hipEvent_t e : l->prof->spare) (void)hipEventDestroy(e);
+    delete l->prof;
+    delete l;
+}
+
+const char *k3moe_status_string(k3moe_status s)
+{
+    switch (s) {
+    case K3MOE_OK: return "ok";
+    case K3MOE_E_INVALID_ARG: return "invalid argument";
+    case K3MOE_E_CONFIG: return "invalid or incomplete config";
+    case K3MOE_E_UNSUPPORTED_SHAPE: return "unsupported shape";
+    case K3MOE_E_ALIGNMENT: return "pointer or stride not aligned";
+    case K3MOE_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case K3MOE_E_OUT_OF_MEMORY: return "out of device memory";
+    case K3MOE_E_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+"""Shared helpers of the GPU parity tests (not collected by pytest)."""
+import numpy as np
+
+import oracle
+import synth
+
+# Bound on |ch_gpu - ch_oracle| for one expert: the logits of both sides are
+# fp64 sums of the same exact products (different order), so the fp32 logit
+# can differ by one ulp only when the sum sits on a rounding boundary; that
+# moves the fp32 score by at most ~2^-23 and the selection score by one more
+# rounding. Gaps above twice this bound cannot reorder the selection.
+CH_DELTA = 2.0 ** -20
+
+# Max relative error of an output element, |gpu - oracle| / D, where D is the
+# oracle's magnitude sum sum_j |w_j| sum_n |W2[o][n] a_j[n]| + shared terms.
+REL_TOL = 1e-4
+
+
+def route_certificate(ch, topk, delta=CH_DELTA):
+    """Per token: True when every adjacent gap among the top k+1 selection
+    scores (oracle fp32 values, order ch desc / expert asc) exceeds 2*delta."""
+    T, E = ch.shape
+    ok = np.zeros(T, bool)
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -ch[t].astype(np.float64)))[: min(E, topk + 1)]
+        v = ch[t, order].astype(np.float64)
+        ok[t] = bool(np.all(np.abs(np.diff(v)) > 2 * delta)) if v.size > 1 else True
+    return ok
+
+
+def check_route(idx_gpu, w_gpu, idx_ref, w_ref, ch_ref, topk, delta=CH_DELTA):
+    """Exact indices on certified tokens; on the others the GPU's choice must
+    be a valid top-k under +-delta perturbations of the scores. Weights within
+    a few fp32 ulps (both sides take them from the same fp32 scores).
+    Returns the number of certified tokens."""
+    cert = route_certificate(ch_ref, topk, delta)
+    for t in range(idx_ref.shape[0]):
+        if cert[t]:
+            assert np.array_equal(idx_gpu[t], idx_ref[t]), (t, idx_gpu[t], idx_ref[t])
+            np.testing.assert_allclose(w_gpu[t], w_ref[t], rtol=4e-7, atol=0)
+        else:
+            g = ch_ref[t, idx_gpu[t]].astype(np.float64)
+            r = ch_ref[t, idx_ref[t]].astype(np.float64)
+            assert len(set(idx_gpu[t].tolist())) == topk
+            assert np.all(np.abs(g - r) <= 2 * delta), (t, g, r)
+    return int(cert.sum())
+
+
+def rel_err(out_gpu, out_ref, denom):
+    err = np.abs(out_gpu.astype(np.float64) - out_ref)
+    d = np.where(denom > 0, denom, 1.0)
+    assert np.all(err[denom == 0] <= 1e-30)
+    return float((err / d).max())
+
+
+def oracle_forward(spec, x, idx, w, layer=0, tokens=None):
+    """Oracle output/denominators for the listed tokens (all by default)."""
+    if tokens is None:
+        tokens = np.arange(x.shape[0])
+    tokens = np.asarray(tokens)
+    xs, ids, ws = x[tokens], idx[tokens], w[tokens]
+    used = sorted({int(e) for e in ids.ravel() if 0 <= e < spec.n_experts})
+    h = synth.expert_host(spec, used, layer)
+    es = oracle.ExpertSet(used, spec.n_experts, h["gate_packed"], h["gate_scales"],
+                          h["up_packed"], h["up_scales"], h["down_packed"], h["down_scales"])
+    shared = synth.make_shared(spec, layer)
+    out, denom, drops = oracle.forward(xs, ids, ws, es, spec.hidden, spec.inter, shared=shared,
+                                       act_kind=spec.act, b1=spec.situ_b1, b2=spec.situ_b2)
+    return out, denom, drops

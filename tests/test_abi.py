@@ -1,0 +1,66 @@
+"""The C-ABI library loads, exports what include/k3moe.h declares, and
+refuses invalid configs on the host (no GPU needed: validation runs before
+any device call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_routed_expert_sigmoid_amd as k3
+from conftest import ROOT
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "k3moe.h")).read()
+    return sorted(set(re.findall(r"\b(k3moe_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(k3.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = k3.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = k3.lib()
+    for s, text in k3.STATUS.items():
+        assert L.k3moe_status_string(s).decode() == text
+
+
+def _weights(E, shared=False, misalign=False):
+    base = 0x10000000 + (8 if misalign else 0)
+    mx = k3.MXFP4(base, base + 0x1000000, 4096, 256)
+    sh = (base + 0x100, base + 0x200, base + 0x300) if shared else (None, None, None)
+    return k3.Weights(base, None, mx, mx, mx, *sh)
+
+
+def _create(cfg, w):
+    h = ctypes.c_void_p()
+    return k3.lib().k3moe_layer_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(h))
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("struct_size", 4, 2), ("abi_version", 99, 2), ("hidden", 0, 2), ("topk", 9, 2),
+    ("act", 0, 2), ("renorm", 2, 2), ("situ_b1", 0.0, 2), ("routed_scale", float("nan"), 2),
+    ("hidden", 96, 3), ("inter", 200, 3), ("shared_inter", 64, 3), ("n_experts", 5000, 3),
+])
+def test_config_refusals(field, value, status):
+    cfg = k3.make_config(256, 128, 8, 2)
+    setattr(cfg, field, value)
+    assert _create(cfg, _weights(8)) == status
+
+
+def test_weight_descriptor_refusals():
+    cfg = k3.make_config(256, 128, 8, 2)
+    w = _weights(8)
+    w.gate.expert_stride_packed = 100          # smaller than one matrix
+    assert _create(cfg, w) == 1
+    assert _create(cfg, _weights(8, misalign=True)) == 4
+    assert _create(cfg, _weights(8, shared=True)) == 1   # shared pointers without shared_inter
+    cfg2 = k3.make_config(256, 128, 8, 2, shared_inter=128)
+    assert _create(cfg2, _weights(8)) == 1               # shared_inter without pointers

@@ -1,0 +1,291 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Every input is seeded and synthetic (``synth``); expected values come only
+from ``oracle``."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import REL_TOL, check_route, oracle_forward, rel_err, route_certificate
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import synth.device as sd
+    return sd
+
+
+def _x_dev(x):
+    import synth.device as sd
+    return sd.bf16_tensor(x, DEV)
+
+
+def _route_gpu(layer, x_np, T, K, logits=False):
+    x = _x_dev(x_np)
+    idx = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, K), dtype=torch.float32, device=DEV)
+    lg = torch.empty((T, layer.cfg.n_experts), dtype=torch.float32, device=DEV) if logits else None
+    layer.route(x, idx, w, logits=lg)
+    torch.cuda.synchronize()
+    return x, idx, w, lg
+
+
+def _forward_gpu(layer, x, idx_np, w_np):
+    T, K = idx_np.shape
+    idx = torch.from_numpy(np.ascontiguousarray(idx_np, np.int32)).to(DEV)
+    w = torch.from_numpy(np.ascontiguousarray(w_np, np.float32)).to(DEV)
+    out = torch.empty((T, layer.cfg.hidden), dtype=torch.float32, device=DEV)
+    layer.forward(x, idx, w, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _certified_x(spec, T, Wr, bias, min_gap=None, max_attempts=50):
+    """Token batch whose oracle route is certified on every token (redraws
+    the batch with the next attempt number otherwise)."""
+    for attempt in range(max_attempts):
+        x = synth.make_x(spec, T, attempt=attempt)
+        idx, w, logits, ch = oracle.route(x, Wr, bias, spec.topk, want_detail=True)
+        ok = route_certificate(ch, spec.topk).all()
+        if min_gap is not None:
+            s = np.sort(logits, axis=1)
+            ok = ok and bool(np.all(np.diff(s, axis=1) >= min_gap))
+        if ok:
+            return x, idx, w, logits, ch, attempt
+    raise AssertionError("no certified batch")
+
+
+# --------------------------------------------------------------------------
+# Tiny layer (hidden 256, 8 experts, top-2, inter 128, no shared expert)
+
+def _tiny(seed=0, **kw):
+    spec = synth.tiny_spec(seed=seed)
+    for k, v in kw.items():
+        setattr(spec, k, v)
+    sd = _dev()
+    t = sd.layer_tensors(spec, 0, DEV)
+    return spec, t, sd.make_layer(spec, t)
+
+
+def test_tiny_route_and_forward_T1():
+    spec, t, layer = _tiny()
+    Wr, bias = synth.make_router(spec), synth.make_bias(spec)
+    x_np, idx_r, w_r, logits, ch, _ = _certified_x(spec, 1, Wr, bias, min_gap=1e-3)
+    x, idx, w, lg = _route_gpu(layer, x_np, 1, spec.topk, logits=True)
+    assert np.array_equal(idx.cpu().numpy(), idx_r)
+    assert np.array_equal(w.cpu().numpy(), w_r)
+    assert np.array_equal(lg.cpu().numpy(), logits.astype(np.float32))
+    out = _forward_gpu(layer, x, idx.cpu().numpy(), w.cpu().numpy())
+    ref, denom, drops = oracle_forward(spec, x_np, idx_r, w_r)
+    assert drops == 0 and layer.error_count() == 0
+    assert rel_err(out, ref, denom) <= REL_TOL
+
+
+@pytest.mark.parametrize("T", [2, 5, 16, 17, 40, 129])
+def test_tiny_ragged_batches(T):
+    spec, t, layer = _tiny(seed=1, bias_std=0.05)
+    Wr, bias = synth.make_router(spec), synth.make_bias(spec)
+    x_np = synth.make_x(spec, T)
+    idx_r, w_r, logits, ch = oracle.route(x_np, Wr, bias, spec.topk, want_detail=True)
+    x, idx, w, _ = _route_gpu(layer, x_np, T, spec.topk)
+    check_route(idx.cpu().numpy(), w.cpu().numpy(), idx_r, w_r, ch, spec.topk)
+    out = _forward_gpu(layer, x, idx_r, w_r)
+    ref, denom, _ = oracle_forward(spec, x_np, idx_r, w_r)
+    assert rel_err(out, ref, denom) <= REL_TOL
+
+
+def test_tiny_swiglu_and_no_renorm():
+    spec, t, layer = _tiny(seed=2, act=oracle.ACT_SWIGLU, renorm=0, routed_scale=1.5)
+    x_np = synth.make_x(spec, 7)
+    idx_r, w_r = oracle.route(x_np, synth.make_router(spec), None, spec.topk, renorm=0,
+                              routed_scale=1.5)
+    out = _forward_gpu(layer, _x_dev(x_np), idx_r, w_r)
+    ref, denom, _ = oracle_forward(spec, x_np, idx_r, w_r)
+    assert rel_err(out, ref, denom) <= REL_TOL
+
+
+def test_tiny_scale_edge_bytes():
+    # scale byte 255 drops a group; byte 0 is 2^-127 and must not flush
+    spec, t, layer = _tiny(seed=3)
+    g = torch.Generator().manual_seed(0)
+    for name in ("gate_scales", "up_scales", "down_scales"):
+        s = t[name]
+        m = torch.rand(s.shape, generator=g) < 0.05
+        s[m.to(DEV)] = 255
+        m0 = torch.rand(s.shape, generator=g) < 0.02
+        s[m0.to(DEV)] = 0
+    torch.cuda.synchronize()
+    x_np = synth.make_x(spec, 3)
+    idx_r, w_r = oracle.route(x_np, synth.make_router(spec), None, spec.topk)
+    out = _forward_gpu(layer, _x_dev(x_np), idx_r, w_r)
+    used = sorted(set(idx_r.ravel().tolist()))
+    es = oracle.ExpertSet(used, spec.n_experts, *(t[k][used].cpu().numpy() for k in (
+        "gate_packed", "gate_scales", "up_packed", "up_scales", "down_packed", "down_scales")))
+    ref, denom, _ = oracle.forward(x_np, idx_r, w_r, es, spec.hidden, spec.inter)
+    assert rel_err(out, ref, denom) <= REL_TOL
+
+
+def test_tiny_invariants_poison_double_relabel():
+    spec, t, layer = _tiny(seed=4)
+    x_np = synth.make_x(spec, 6)
+    idx_r, w_r = oracle.route(x_np, synth.make_router(spec), None, spec.topk)
+    x = _x_dev(x_np)
+    base = _forward_gpu(layer, x, idx_r, w_r)
+    # determinism
+    assert np.array_equal(base, _forward_gpu(layer, x, idx_r, w_r))
+    # poison every unselected expert: random bytes, scale 254
+    used = set(idx_r.ravel().tolist())
+    g = torch.Generator().manual_seed(1)
+    saved = {k: v.clone() for k, v in t.items() if v is not None and v.dtype == torch.uint8}
+    for e in range(spec.n_experts):
+        if e in used:
+            continue
+        for k in saved:
+            if k.endswith("packed"):
+                t[k][e] = torch.randint(0, 256, t[k][e].shape, generator=g, dtype=torch.uint8).to(DEV)
+            else:
+                t[k][e] = 254
+    assert np.array_equal(base, _forward_gpu(layer, x, idx_r, w_r))
+    for k, v in saved.items():
+        t[k].copy_(v)
+    # +1 on every down scale doubles the (routed-only) output exactly
+    t["down_scales"] += 1
+    assert np.array_equal(_forward_gpu(layer, x, idx_r, w_r), 2.0 * base)
+    t["down_scales"] -= 1
+    # relabelling experts (storage, router rows, ids) changes nothing
+    perm = np.random.default_rng(2).permutation(spec.n_experts)
+    inv = torch.from_numpy(np.argsort(perm)).to(DEV)
+    t2 = dict(t)
+    for k in saved:
+        t2[k] = t[k][inv].contiguous()
+    t2["router_w"] = t["router_w"][inv].contiguous()
+    import synth.device as sd
+    layer2 = sd.make_layer(spec, t2)
+    assert np.array_equal(base, _forward_gpu(layer2, x, perm[idx_r], w_r))
+
+
+def test_tiny_bad_ids_are_counted():
+    spec, t, layer = _tiny(seed=5)
+    x_np = synth.make_x(spec, 4)
+    idx_r, w_r = oracle.route(x_np, synth.make_router(spec), None, spec.topk)
+    x = _x_dev(x_np)
+    bad = idx_r.copy()
+    bad[0, 1] = -1
+    bad[2, 0] = spec.n_experts
+    layer.error_reset()
+    out_bad = _forward_gpu(layer, x, bad, w_r)
+    assert layer.error_count() == 2
+    w0 = w_r.copy()
+    w0[0, 1] = 0.0
+    w0[2, 0] = 0.0
+    assert np.array_equal(out_bad, _forward_gpu(layer, x, idx_r, w0))
+
+
+def test_empty_batch_is_a_no_op():
+    spec, t, layer = _tiny(seed=6)
+    x = torch.empty((0, spec.hidden), dtype=torch.bfloat16, device=DEV)
+    idx = torch.empty((0, spec.topk), dtype=torch.int32, device=DEV)
+    w = torch.empty((0, spec.topk), dtype=torch.float32, device=DEV)
+    out = torch.empty((0, spec.hidden), dtype=torch.float32, device=DEV)
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    layer.route(x, idx, w, workspace=ws)
+    layer.forward(x, idx, w, out, workspace=ws)
+
+
+def test_pages_expert_shape():
+    # the README's latent expert shape (width 3584, intermediate 3072), few experts
+    spec = synth.LayerSpec(hidden=3584, inter=3072, n_experts=6, topk=3, bias_std=0.01, seed=8)
+    sd = _dev()
+    layer = sd.make_layer(spec, sd.layer_tensors(spec, 0, DEV))
+    x_np = synth.make_x(spec, 3)
+    idx_r, w_r = oracle.route(x_np, synth.make_router(spec), synth.make_bias(spec), spec.topk)
+    out = _forward_gpu(layer, _x_dev(x_np), idx_r, w_r)
+    ref, denom, _ = oracle_forward(spec, x_np, idx_r, w_r)
+    assert rel_err(out, ref, denom) <= REL_TOL
+
+
+# --------------------------------------------------------------------------
+# Full shape (hidden 7168, 896 experts, top-16, inter 1536, bf16 shared expert)
+
+_FULL = {}
+
+
+def _full(routing="normal"):
+    if routing not in _FULL:
+        sd = _dev()
+        spec = synth.full_spec(seed=0, routing=routing)
+        t = sd.layer_tensors(spec, 0, DEV)
+        _FULL.clear()
+        _FULL[routing] = (spec, t, sd.make_layer(spec, t))
+    return _FULL[routing]
+
+
+def test_full_device_bytes_match_host_generator():
+    spec, t, _ = _full()
+    k = synth.stream_key(spec.seed, 0, synth.DOWN_PACKED)
+    e = 777
+    n = spec.hidden * spec.inter // 2
+    host = synth.packed_bytes(k, e * n + 4096, 4096)
+    assert np.array_equal(t["down_packed"][e].reshape(-1)[4096:8192].cpu().numpy(), host)
+    ks = synth.stream_key(spec.seed, 0, synth.UP_SCALES)
+    ns = spec.hidden * spec.inter // 32
+    assert np.array_equal(t["up_scales"][e].reshape(-1)[:1000].cpu().numpy(),
+                          synth.scale_bytes(ks, e * ns, 1000))
+
+
+def test_full_decode_T1():
+    spec, t, layer = _full()
+    Wr, bias = synth.make_router(spec), synth.make_bias(spec)
+    x_np, idx_r, w_r, logits, ch, _ = _certified_x(spec, 1, Wr, bias)
+    x, idx, w, lg = _route_gpu(layer, x_np, 1, spec.topk, logits=True)
+    check_route(idx.cpu().numpy(), w.cpu().numpy(), idx_r, w_r, ch, spec.topk)
+    l32 = logits.astype(np.float32)
+    assert np.max(np.abs(lg.cpu().numpy() - l32) / np.maximum(np.abs(l32), 1e-30)) <= 2.0 ** -23
+    out = _forward_gpu(layer, x, idx_r, w_r)
+    ref, denom, _ = oracle_forward(spec, x_np, idx_r, w_r)
+    assert rel_err(out, ref, denom) <= REL_TOL
+    # bitwise reproducible
+    assert np.array_equal(out, _forward_gpu(layer, x, idx_r, w_r))
+
+
+def test_full_batched_decode_T64_sampled():
+    spec, t, layer = _full()
+    T = 64
+    Wr, bias = synth.make_router(spec), synth.make_bias(spec)
+    x_np = synth.make_x(spec, T, attempt=1)
+    idx_r, w_r, logits, ch = oracle.route(x_np, Wr, bias, spec.topk, want_detail=True)
+    x, idx, w, _ = _route_gpu(layer, x_np, T, spec.topk)
+    ncert = check_route(idx.cpu().numpy(), w.cpu().numpy(), idx_r, w_r, ch, spec.topk)
+    assert ncert >= T - 4
+    out = _forward_gpu(layer, x, idx_r, w_r)
+    sample = [0, 13, 37, 63]
+    ref, denom, _ = oracle_forward(spec, x_np, idx_r, w_r, tokens=sample)
+    assert rel_err(out[sample], ref, denom) <= REL_TOL
+
+
+def test_full_prefill_T2048_zipf_sampled():
+    spec, t, layer = _full("zipf")
+    T = 2048
+    Wr, bias = synth.make_router(spec), synth.make_bias(spec)
+    x_np = synth.make_x(spec, T)
+    x, idx, w, _ = _route_gpu(layer, x_np, T, spec.topk)
+    idx_g, w_g = idx.cpu().numpy(), w.cpu().numpy()
+    rng = np.random.default_rng(0)
+    sample = np.sort(rng.choice(T, 24, replace=False))
+    idx_r, w_r, logits, ch = oracle.route(x_np[sample], Wr, bias, spec.topk, want_detail=True)
+    check_route(idx_g[sample], w_g[sample], idx_r, w_r, ch, spec.topk)
+    # forward with the oracle's routes on the sampled tokens
+    idx_in, w_in = idx_g.copy(), w_g.copy()
+    idx_in[sample], w_in[sample] = idx_r, w_r
+    out = _forward_gpu(layer, x, idx_in, w_in)
+    few = sample[:3]
+    ref, denom, _ = oracle_forward(spec, x_np, idx_in, w_in, tokens=few)
+    assert rel_err(out[few], ref, denom) <= REL_TOL
+    assert layer.error_count() == 0
