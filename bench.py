@@ -86,6 +86,12 @@ def main():
     out = torch.empty((T, H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
 
+    # calibration read of known size (256 MiB) for hardware byte counters
+    cal = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    sd.read_probe(cal, sink)
+    del cal
+
     def step(i):
         x = xs[i % pool]
         layer.route(x, idx, w, workspace=ws, stream=stream)

@@ -32,6 +32,8 @@
 //    with no atomics, so the output is bitwise reproducible.
 #include <math.h>
 
+#include <type_traits>
+
 #include "k3moe_internal.h"
 
 namespace k3moe {
@@ -47,6 +49,39 @@ __device__ __forceinline__ v4f mfma_fp4_fp8(const v8i &a, const v8i &b, v4f c, i
 {
     // A format 4 = fp4 (e2m1), B format 0 = fp8 (e4m3); scale bytes in byte 0.
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, sa, 0, sb);
+}
+
+// Same, with the scale bytes taken from byte S of packed scale words.
+template <int S>
+__device__ __forceinline__ v4f mfma_fp4_fp8_sel(const v8i &a, const v8i &b, v4f c, int sa, int sb)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, S, sa, S, sb);
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// A lane's scale bytes for 4 consecutive K steps: from the 16 bytes holding
+// K-blocks 4s+g (step s, lane group g) of a row, byte g of each dword.
+__device__ __forceinline__ uint32_t gather_scales(u4 v, uint32_t grp)
+{
+    const uint32_t lo = __builtin_amdgcn_perm(v.y, v.x, grp | ((4u + grp) << 8) | 0x0c0c0000u);
+    const uint32_t hi = __builtin_amdgcn_perm(v.w, v.z, 0x00000c0cu | (grp << 16) | ((4u + grp) << 24));
+    return lo | hi;
+}
+
+// 0x80 in each byte of x that is 0xFF (E8M0 255), 0 elsewhere.
+__device__ __forceinline__ uint32_t ff_bytes(uint32_t x)
+{
+    const uint32_t y = ~x;
+    return ~(((y & 0x7f7f7f7fu) + 0x7f7f7f7fu) | y | 0x7f7f7f7fu);
 }
 
 __device__ __forceinline__ v8i a_operand(u4 v) { return v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0}; }
@@ -119,14 +154,22 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t *__restrict__ x,
     const uint16_t *wr = Wr + (size_t)e * H;
     const uint16_t *xr = x + (size_t)t * H;
     double acc = 0.0;
-    for (int i = lane * 8; i < H; i += 512) {
-        const u4 wv = *reinterpret_cast<const u4 *>(wr + i);
-        const u4 xv = *reinterpret_cast<const u4 *>(xr + i);
+    constexpr int CH = 7;  // 512-element slices whose loads are issued together
+    for (int i0 = lane * 8; i0 < H; i0 += 512 * CH) {
+        u4 wv[CH], xv[CH];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            acc = fma((double)bf16f(wv[q] & 0xffffu), (double)bf16f(xv[q] & 0xffffu), acc);
-            acc = fma((double)bf16f(wv[q] >> 16), (double)bf16f(xv[q] >> 16), acc);
+        for (int c = 0; c < CH; ++c) {
+            const int i = i0 + 512 * c;
+            wv[c] = i < H ? *reinterpret_cast<const u4 *>(wr + i) : u4{0u, 0u, 0u, 0u};
+            xv[c] = i < H ? *reinterpret_cast<const u4 *>(xr + i) : u4{0u, 0u, 0u, 0u};
         }
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc = fma((double)bf16f(wv[c][q] & 0xffffu), (double)bf16f(xv[c][q] & 0xffffu), acc);
+                acc = fma((double)bf16f(wv[c][q] >> 16), (double)bf16f(xv[c][q] >> 16), acc);
+            }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
@@ -140,81 +183,102 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t *__restrict__ x,
     }
 }
 
-// Top-k by repeated maximum (README §9): one wave per token; lane l owns
-// experts l, l+64, ...; the order is (ch descending, expert ascending), so a
-// tie goes to the lower index. NaN selection scores rank as -inf. Weights
-// are the unbiased scores, renormalised in router order, then scaled.
-__global__ __launch_bounds__(64) void k_topk(const float *__restrict__ sc,
-                                             const float *__restrict__ ch, int E, int K,
-                                             int renorm, float rscale, int32_t *__restrict__ idx,
-                                             float *__restrict__ w)
+// Wave-wide max / min of a uint32 through DPP (row-local steps, then the
+// row broadcasts), read back from lane 63: the same value in every lane.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v)
+{
+    auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xb1, 0xf, 0xf, false));   // quad [1,0,3,2]
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4e, 0xf, 0xf, false));   // quad [2,3,0,1]
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xf, 0xf, false));  // row_mirror
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast15
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Top-k by repeated maximum (README §9): one wave per token; lane l holds the
+// selection scores of experts l, l+64, ... (NQ per lane) as order-preserving
+// uint32 keys and caches its best remaining one. Each round takes the
+// wave-wide maximum key, then the lowest expert index among the lanes holding
+// it (so equal scores go to the lower index, as the strict comparison of the
+// repeated maximum does); the winning lane rescans. NaN ranks as -inf.
+// Weights are the unbiased scores, renormalised in router order, then scaled.
+__device__ __forceinline__ uint32_t order_key(float v)
+{
+    if (v != v) v = -INFINITY;
+    const uint32_t b = __float_as_uint(v);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // > 0 for every float
+}
+
+template <int NQ>
+__global__ __launch_bounds__(64) void k_topk(const float *__restrict__ sc, const float *__restrict__ ch,
+                                             int E, int K, int renorm, float rscale,
+                                             int32_t *__restrict__ idx, float *__restrict__ w)
 {
     const int t = blockIdx.x;
     const int lane = threadIdx.x;
     const float *c = ch + (size_t)t * E;
-    uint64_t taken = 0;
+    uint32_t v[NQ];
+    uint64_t avail = 0;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const int e = lane + 64 * q;
+        v[q] = 0u;
+        if (e < E) {
+            v[q] = order_key(c[e]);
+            avail |= 1ull << q;
+        }
+    }
+    uint32_t bk;  // best key of this lane (0: none left)
+    int be;       // its expert
+    auto rescan = [&]() {
+        bk = 0u;
+        be = -1;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+            if (((avail >> q) & 1ull) && v[q] > bk) {
+                bk = v[q];
+                be = lane + 64 * q;
+            }
+    };
+    rescan();
     int mine = 0;
     for (int j = 0; j < K; ++j) {
-        float bv = 0.0f;
-        int bi = -1;
-        int q = 0;
-        for (int e = lane; e < E; e += 64, ++q) {
-            if ((taken >> q) & 1ull) continue;
-            float v = c[e];
-            if (v != v) v = -INFINITY;
-            if (bi < 0 || v > bv) {
-                bv = v;
-                bi = e;
-            }
+        const uint32_t m = wave_reduce_u32<true>(bk);
+        const uint32_t cand = (be >= 0 && bk == m) ? (uint32_t)be : 0xffffffffu;
+        const int win = (int)wave_reduce_u32<false>(cand);
+        if ((win & 63) == lane) {
+            avail &= ~(1ull << (win >> 6));
+            rescan();
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ov = __shfl_xor(bv, o);
-            const int oi = __shfl_xor(bi, o);
-            if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        if ((bi & 63) == lane) taken |= 1ull << (bi >> 6);
-        if (lane == j) mine = bi;
+        if (lane == j) mine = win;
     }
     __shared__ float wj[kMaxTopk];
-    __shared__ float ssum;
     if (lane < K) wj[lane] = sc[(size_t)t * E + mine];
     __syncthreads();
     if (lane == 0) {
         float s = 0.0f;
         for (int j = 0; j < K; ++j) s += wj[j];
-        ssum = s;
+        for (int j = 0; j < K; ++j) {
+            float v0 = wj[j];
+            if (renorm && s > 0.0f) v0 /= s;
+            w[(size_t)t * K + j] = v0 * rscale;
+        }
     }
-    __syncthreads();
-    if (lane < K) {
-        float v = wj[lane];
-        if (renorm && ssum > 0.0f) v /= ssum;
-        v *= rscale;
-        idx[(size_t)t * K + lane] = mine;
-        w[(size_t)t * K + lane] = v;
-    }
+    if (lane < K) idx[(size_t)t * K + lane] = mine;
 }
 
 // ---------------------------------------------------------------------------
-// Token activations -> kXTerms e4m3 terms per element, one E8M0 scale per term per
-// 32-element block. Thread per element; a half-wave is one block.
+// Token activations -> kXTerms e4m3 terms per element, one E8M0 scale per
+// term per 32-element block. Thread per element; a half-wave is one block.
+__device__ __forceinline__ void xsplit_slab(const uint16_t *__restrict__ x, int64_t n, int H, int64_t slab,
+                                            uint8_t *__restrict__ xq, uint8_t *__restrict__ xs);
 __global__ __launch_bounds__(256) void k_xsplit(const uint16_t *__restrict__ x, int64_t n, int H,
                                                 uint8_t *__restrict__ xq, uint8_t *__restrict__ xs)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;  // n is a multiple of 32: whole half-waves leave together
-    const int64_t t = i / H;
-    const int col = (int)(i - t * H);
-    int code[kXTerms], sb[kXTerms];
-    split_e4m3_32<kXTerms>(bf16f(x[i]), code, sb);
-#pragma unroll
-    for (int term = 0; term < kXTerms; ++term) {
-        xq[(t * kXTerms + term) * H + col] = (uint8_t)code[term];
-        if ((threadIdx.x & 31) == 0) xs[(t * kXTerms + term) * (H >> 5) + (col >> 5)] = (uint8_t)sb[term];
-    }
+    xsplit_slab(x, n, H, blockIdx.x, xq, xs);  // n is a multiple of 32: half-waves leave together
 }
 
 // ---------------------------------------------------------------------------
@@ -223,21 +287,18 @@ __global__ __launch_bounds__(256) void k_xsplit(const uint16_t *__restrict__ x, 
 // ascending id, their start offsets, and the sorted assignment list.
 // Out-of-range ids are left out (the combine counts them).
 
-// Exclusive scan, in place, of v[0..n) (n <= 4096) by a 1024-thread block;
-// returns the total.
+// Exclusive scan, in place, of v[0..n) (LDS) by the whole block (blockDim a
+// multiple of 64, at most 1024); returns the total.
 __device__ int block_exclusive_scan(int *v, int n)
 {
     __shared__ int wsum[16];
     __shared__ int total_sh;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int per = (n + 1023) >> 10;
-    int loc[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nt = blockDim.x;
+    const int per = (n + nt - 1) / nt;
     int s = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < per; ++q) {
         const int i = tid * per + q;
-        loc[q] = (q < per && i < n) ? v[i] : 0;
-        s += loc[q];
+        if (i < n) s += v[i];
     }
     int inc = s;
 #pragma unroll
@@ -249,7 +310,7 @@ __device__ int block_exclusive_scan(int *v, int n)
     __syncthreads();
     if (tid == 0) {
         int run = 0;
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < nt / 64; ++k) {
             const int c = wsum[k];
             wsum[k] = run;
             run += c;
@@ -258,12 +319,12 @@ __device__ int block_exclusive_scan(int *v, int n)
     }
     __syncthreads();
     int base = wsum[wv] + inc - s;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < per; ++q) {
         const int i = tid * per + q;
-        if (q < per && i < n) {
+        if (i < n) {
+            const int c = v[i];
             v[i] = base;
-            base += loc[q];
+            base += c;
         }
     }
     __syncthreads();
@@ -277,14 +338,14 @@ __device__ void build_active(const int *cnt, int *off, int *flag, int E, int32_t
                              int32_t *active_e, int32_t *active_off)
 {
     const int tid = threadIdx.x;
-    for (int e = tid; e < E; e += 1024) {
+    for (int e = tid; e < E; e += blockDim.x) {
         off[e] = cnt[e];
         flag[e] = cnt[e] > 0;
     }
     __syncthreads();
     const int total = block_exclusive_scan(off, E);
     const int nact = block_exclusive_scan(flag, E);
-    for (int e = tid; e < E; e += 1024) {
+    for (int e = tid; e < E; e += blockDim.x) {
         if (cnt[e] > 0) {
             active_e[flag[e]] = e;
             active_off[flag[e]] = off[e];
@@ -298,17 +359,16 @@ __device__ void build_active(const int *cnt, int *off, int *flag, int E, int32_t
 }
 
 // Whole permutation in one block, for T <= kPermChunk.
-__global__ __launch_bounds__(1024) void k_perm_single(const int32_t *__restrict__ idx, int T, int K,
-                                                      int E, int32_t *active_n, int32_t *active_e,
-                                                      int32_t *active_off, int32_t *sorted)
+__device__ void perm_single(const int32_t *__restrict__ idx, int T, int K, int E, int32_t *active_n,
+                            int32_t *active_e, int32_t *active_off, int32_t *sorted)
 {
     __shared__ int cnt[kMaxExperts];
     __shared__ int off[kMaxExperts];
     __shared__ int flag[kMaxExperts];
     const int tid = threadIdx.x;
-    for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+    for (int e = tid; e < E; e += blockDim.x) cnt[e] = 0;
     __syncthreads();
-    for (int a = tid; a < T * K; a += 1024) {
+    for (int a = tid; a < T * K; a += blockDim.x) {
         const int e = idx[a];
         if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
     }
@@ -321,6 +381,37 @@ __global__ __launch_bounds__(1024) void k_perm_single(const int32_t *__restrict_
                 if (e >= 0 && e < E) sorted[atomicAdd(&off[e], 1)] = t * K + j;
             }
     }
+}
+
+// Token fp8 expansion for one 256-element slab (see k_xsplit).
+__device__ __forceinline__ void xsplit_slab(const uint16_t *__restrict__ x, int64_t n, int H, int64_t slab,
+                                            uint8_t *__restrict__ xq, uint8_t *__restrict__ xs)
+{
+    const int64_t i = slab * 256 + threadIdx.x;
+    if (i >= n) return;
+    const int64_t t = i / H;
+    const int col = (int)(i - t * H);
+    int code[kXTerms], sb[kXTerms];
+    split_e4m3_32<kXTerms>(bf16f(x[i]), code, sb);
+#pragma unroll
+    for (int term = 0; term < kXTerms; ++term) {
+        xq[(t * kXTerms + term) * H + col] = (uint8_t)code[term];
+        if ((threadIdx.x & 31) == 0) xs[(t * kXTerms + term) * (H >> 5) + (col >> 5)] = (uint8_t)sb[term];
+    }
+}
+
+// Small batches (T <= kPermChunk): block 0 builds the permutation, the other
+// blocks expand the tokens to fp8 terms.
+__global__ __launch_bounds__(256) void k_prep_small(const uint16_t *__restrict__ x, int64_t n, int H,
+                                                    uint8_t *__restrict__ xq, uint8_t *__restrict__ xs,
+                                                    const int32_t *__restrict__ idx, int T, int K,
+                                                    int E, int32_t *active_n, int32_t *active_e,
+                                                    int32_t *active_off, int32_t *sorted)
+{
+    if (blockIdx.x == 0)
+        perm_single(idx, T, K, E, active_n, active_e, active_off, sorted);
+    else
+        xsplit_slab(x, n, H, blockIdx.x - 1, xq, xs);
 }
 
 // Multi-chunk permutation, phase 1: per-chunk expert counts.
@@ -384,90 +475,241 @@ __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Gate/up projections + activation for the routed experts (README §9, k3_moe
-// step 3, first half). One workgroup per (active expert, 32-row tile of I);
-// its 4 waves split the K steps (128 elements each) round-robin and meet in
-// LDS. Per K step a wave loads 4 A fragments (gate/up x two 16-row halves)
-// and one B fragment carrying up to 4 tokens x 4 terms, and issues 4 MFMAs.
-// The epilogue adds the term columns, applies the activation, and writes
-// the activation as 4 e4m3 terms (with E8M0 scales) for the down projection.
+// Gate/up projections + activation (README §9, k3_moe step 3 first half and
+// step 6 first half), one launch for the routed and the shared expert.
+//
+// Routed part: one workgroup per (active expert, 32-row tile of I); its 4
+// waves split the K steps (128 elements each) round-robin and meet in LDS.
+// Per K step a wave loads 4 A fragments (gate/up x two 16-row halves, 16 B
+// per lane straight from HBM) and one B fragment carrying up to 4 tokens x 4
+// terms, and issues 4 MFMAs; loads run D steps ahead of the MFMAs. The
+// epilogue adds the term columns, applies the activation, and writes the
+// activation as 4 e4m3 terms (with E8M0 scales) for the down projection.
+//
+// Shared part (blocks after the routed ones): one wave per shared row, bf16
+// weights, fp32 accumulation, tokens in groups of kShTok.
 struct GateUpParams {
     const uint8_t *gp, *gs, *up, *us;
     int64_t g_sp, g_ss, u_sp, u_ss;
-    int H, I, K, act;
+    int H, I, K, act, T, Is, routed_blocks, shared_blocks;
     float b1, b2;
+    const uint16_t *x;
     const uint8_t *xq, *xs;
     const int32_t *active_n, *active_e, *active_off, *sorted;
     uint8_t *aq, *as;
+    const uint16_t *sh_gate, *sh_up;
+    float *ash;
 };
 
-__global__ __launch_bounds__(256) void k_gateup(GateUpParams p)
+#ifndef K3MOE_SH_TOK
+#define K3MOE_SH_TOK 2
+#endif
+#ifndef K3MOE_GU_DEPTH
+#define K3MOE_GU_DEPTH 2
+#endif
+#ifndef K3MOE_DN_DEPTH
+#define K3MOE_DN_DEPTH 6
+#endif
+constexpr int kShTok = K3MOE_SH_TOK;  // shared gate/up tokens per pass
+
+__device__ void shared_gateup_rows(const GateUpParams &p, int blk)
 {
+    const int lane = threadIdx.x & 63;
+    const int r = blk * 4 + (threadIdx.x >> 6);
+    if (r >= p.Is) return;
+    const int H = p.H;
+    const uint16_t *g = p.sh_gate + (size_t)r * H;
+    const uint16_t *u = p.sh_up + (size_t)r * H;
+    constexpr int CH = 4;  // 512-element slices whose loads are issued together
+    for (int t0 = 0; t0 < p.T; t0 += kShTok) {
+        const int nt = min(kShTok, p.T - t0);
+        float ga[kShTok], ua[kShTok];
+#pragma unroll
+        for (int k = 0; k < kShTok; ++k) ga[k] = ua[k] = 0.0f;
+        for (int i0 = lane * 8; i0 < H; i0 += 512 * CH) {
+            u4 gv[CH], uv[CH];
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int i = i0 + 512 * c;
+                gv[c] = i < H ? *reinterpret_cast<const u4 *>(g + i) : u4{0u, 0u, 0u, 0u};
+                uv[c] = i < H ? *reinterpret_cast<const u4 *>(u + i) : u4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int k = 0; k < kShTok; ++k) {
+                if (k >= nt) break;
+                u4 xv[CH];
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    const int i = i0 + 512 * c;
+                    xv[c] = i < H ? *reinterpret_cast<const u4 *>(p.x + (size_t)(t0 + k) * H + i)
+                                  : u4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int c = 0; c < CH; ++c)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float x0 = bf16f(xv[c][q] & 0xffffu), x1 = bf16f(xv[c][q] >> 16);
+                        ga[k] = fmaf(bf16f(gv[c][q] & 0xffffu), x0, ga[k]);
+                        ga[k] = fmaf(bf16f(gv[c][q] >> 16), x1, ga[k]);
+                        ua[k] = fmaf(bf16f(uv[c][q] & 0xffffu), x0, ua[k]);
+                        ua[k] = fmaf(bf16f(uv[c][q] >> 16), x1, ua[k]);
+                    }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kShTok; ++k) {
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                ga[k] += __shfl_xor(ga[k], o);
+                ua[k] += __shfl_xor(ua[k], o);
+            }
+        }
+        if (lane == 0)
+            for (int k = 0; k < nt; ++k) p.ash[(size_t)(t0 + k) * p.Is + r] = act_fn(ga[k], ua[k], p.act, p.b1, p.b2);
+    }
+}
+
+#ifndef K3MOE_GU_MIN_WAVES
+#define K3MOE_GU_MIN_WAVES 2
+#endif
+#ifndef K3MOE_MIN_WAVES
+#define K3MOE_MIN_WAVES 4
+#endif
+
+template <bool WIDE>
+__global__ __launch_bounds__(256, K3MOE_GU_MIN_WAVES) void k_gateup(GateUpParams p)
+{
+    // shared-expert blocks are spread evenly through the grid (one every
+    // `stride` blocks) so they run alongside the routed blocks, not after them
+    int bid = blockIdx.x;
+    if (p.shared_blocks > 0) {
+        const int stride = (p.routed_blocks + p.shared_blocks) / p.shared_blocks;
+        const int k = bid / stride;
+        if (bid % stride == stride - 1 && k < p.shared_blocks) {
+            shared_gateup_rows(p, k);
+            return;
+        }
+        bid -= min(p.shared_blocks, (bid + 1) / stride);
+    }
     const int RT = p.I >> 5;
-    const int slot = blockIdx.x / RT;
-    const int rt = blockIdx.x - slot * RT;
+    const int slot = bid / RT;
+    const int rt = bid - slot * RT;
     if (slot >= *p.active_n) return;
     const int e = p.active_e[slot];
     const int a0 = p.active_off[slot], a1 = p.active_off[slot + 1];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int rl = lane & 15, grp = lane >> 4;
-    const int H = p.H, KS = H >> 7;
-    const int64_t rowb = H >> 1, rows = H >> 5;
+    const int H = p.H, KS = H >> 7, SR = H >> 5;
+    constexpr bool wide = WIDE;  // H % 512 == 0: 16-byte aligned scale chunks
 
-    const uint8_t *ap[4];
-    const uint8_t *asp[4];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int64_t row = (int64_t)rt * 32 + h * 16 + rl;
-            ap[m * 2 + h] = (m ? p.up + e * p.u_sp : p.gp + e * p.g_sp) + row * rowb + grp * 16;
-            asp[m * 2 + h] = (m ? p.us + e * p.u_ss : p.gs + e * p.g_ss) + row * rows + grp;
-        }
+    // wave-uniform expert bases; per-lane 32-bit offsets (row, K-block group)
+    const uint8_t *gpe = p.gp + e * p.g_sp, *upe = p.up + e * p.u_sp;
+    const uint8_t *gse = p.gs + e * p.g_ss, *use = p.us + e * p.u_ss;
+    const uint32_t rowb = (uint32_t)H >> 1;
+    const uint32_t r0 = (uint32_t)rt * 32 + rl;
+    const uint32_t po0 = r0 * rowb + grp * 16, po1 = po0 + 16 * rowb;  // packed, rows r0 / r0+16
+    const uint32_t sr0 = r0 * SR, sr1 = sr0 + 16 * SR;                 // scale rows
 
     __shared__ float red[4][4][4][64];  // [wave][tile][reg][lane]
 
+    // K is walked in chunks of 4 steps (512 elements); wave w takes a
+    // contiguous range of chunks. One 16-byte load per tile and chunk brings
+    // the lane's scale bytes of all 4 steps (selected per step by op_sel).
+    const int NCH = (KS + 3) >> 2;
+    const int per = (NCH + 3) >> 2;
+    const int c0 = min(NCH, wave * per), c1 = min(NCH, c0 + per);
     constexpr int kTok = 16 / kXTerms;  // tokens per B fragment
+    const int col = lane & 15, term = col % kXTerms;
+
+    struct Batch {
+        u4 a[4][4];  // [step][tile]
+        u4 lo[4], hi[4];
+        uint32_t sa[4], sb;
+    };
+    auto load_a = [&](int c, Batch &B) {
+        static_for<0, 4>([&](auto s_) {
+            constexpr int st = decltype(s_)::value;
+            if (4 * c + st < KS) {
+                const uint32_t o = (uint32_t)(4 * c + st) * 64;
+                B.a[st][0] = *reinterpret_cast<const u4 *>(gpe + (po0 + o));
+                B.a[st][1] = *reinterpret_cast<const u4 *>(gpe + (po1 + o));
+                B.a[st][2] = *reinterpret_cast<const u4 *>(upe + (po0 + o));
+                B.a[st][3] = *reinterpret_cast<const u4 *>(upe + (po1 + o));
+            }
+        });
+        if constexpr (wide) {
+            B.sa[0] = gather_scales(*reinterpret_cast<const u4 *>(gse + sr0 + 16 * c), grp);
+            B.sa[1] = gather_scales(*reinterpret_cast<const u4 *>(gse + sr1 + 16 * c), grp);
+            B.sa[2] = gather_scales(*reinterpret_cast<const u4 *>(use + sr0 + 16 * c), grp);
+            B.sa[3] = gather_scales(*reinterpret_cast<const u4 *>(use + sr1 + 16 * c), grp);
+        } else {  // short rows: byte loads, steps past K left at 127
+#pragma unroll
+            for (int q = 0; q < 4; ++q) B.sa[q] = 0x7f7f7f7fu;
+            for (int st = 0; st < 4 && 4 * c + st < KS; ++st) {
+                const uint32_t so = (4 * c + st) * 4 + grp, sh8 = 8 * st, m = ~(0xffu << sh8);
+                B.sa[0] = (B.sa[0] & m) | ((uint32_t)gse[sr0 + so] << sh8);
+                B.sa[1] = (B.sa[1] & m) | ((uint32_t)gse[sr1 + so] << sh8);
+                B.sa[2] = (B.sa[2] & m) | ((uint32_t)use[sr0 + so] << sh8);
+                B.sa[3] = (B.sa[3] & m) | ((uint32_t)use[sr1 + so] << sh8);
+            }
+        }
+    };
+    auto load_b = [&](int c, Batch &B, const uint8_t *xb, const uint8_t *xsr) {
+        static_for<0, 4>([&](auto s_) {
+            constexpr int st = decltype(s_)::value;
+            if (4 * c + st < KS) {
+                const uint32_t o = (uint32_t)(4 * c + st) * 128;
+                B.lo[st] = *reinterpret_cast<const u4 *>(xb + o);
+                B.hi[st] = *reinterpret_cast<const u4 *>(xb + o + 64);
+            }
+        });
+        if constexpr (wide) {
+            B.sb = gather_scales(*reinterpret_cast<const u4 *>(xsr + 16 * c), grp);
+        } else {
+            B.sb = 0x7f7f7f7fu;
+            for (int st = 0; st < 4 && 4 * c + st < KS; ++st) {
+                const uint32_t sh8 = 8 * st;
+                B.sb = (B.sb & ~(0xffu << sh8)) | ((uint32_t)xsr[(4 * c + st) * 4 + grp] << sh8);
+            }
+        }
+    };
+
     for (int g0 = a0; g0 < a1; g0 += kTok) {
         const int ntok = min(kTok, a1 - g0);
-        const int col = lane & 15, s = col / kXTerms, term = col - kXTerms * s;
-        const bool bvalid = (s < kTok) && (s < ntok);
-        const uint8_t *xb = p.xq;
-        const uint8_t *xsb = p.xs;
-        if (bvalid) {
-            const int64_t tok = p.sorted[g0 + s] / p.K;
-            xb += (tok * kXTerms + term) * H + grp * 16;
-            xsb += (tok * kXTerms + term) * (H >> 5) + grp;
-        }
+        // B column (token slot, term); slots past ntok read slot 0's data into
+        // columns the epilogue ignores (duplicate addresses coalesce)
+        const int slot_tok = col / kXTerms < ntok ? col / kXTerms : 0;
+        const int64_t tok = p.sorted[g0 + slot_tok] / p.K;
+        const uint8_t *xb = p.xq + (tok * kXTerms + term) * H + grp * 16;
+        const uint8_t *xsr = p.xs + (tok * kXTerms + term) * SR;
         v4f acc[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-        for (int st = wave; st < KS; st += 4) {
-            u4 av[4];
-            int sa[4];
+        for (int c = c0; c < c1; ++c) {
+            Batch bt;
+            load_a(c, bt);
+            load_b(c, bt, xb, xsr);
+            uint32_t drop[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                av[q] = __builtin_nontemporal_load(reinterpret_cast<const u4 *>(ap[q] + st * 64));
-                sa[q] = asp[q][st * 4];
+            for (int q = 0; q < 4; ++q) {  // scale byte 255: the 32-group drops out
+                drop[q] = ff_bytes(bt.sa[q]);
+                bt.sa[q] ^= drop[q];
             }
-            u4 lo = u4{0u, 0u, 0u, 0u}, hi = u4{0u, 0u, 0u, 0u};
-            int sb = 127;
-            if (bvalid) {
-                lo = *reinterpret_cast<const u4 *>(xb + st * 128);
-                hi = *reinterpret_cast<const u4 *>(xb + st * 128 + 64);
-                sb = xsb[st * 4];
-            }
-            const v8i B = b_operand(lo, hi);
+            static_for<0, 4>([&](auto s_) {
+                constexpr int st = decltype(s_)::value;
+                if (4 * c + st < KS) {
+                    const v8i B = b_operand(bt.lo[st], bt.hi[st]);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (sa[q] == 255) {  // scale byte 255: the 32-group drops out
-                    av[q] = u4{0u, 0u, 0u, 0u};
-                    sa[q] = 127;
+                    for (int q = 0; q < 4; ++q) {
+                        const u4 av = ((drop[q] >> (8 * st + 7)) & 1u) ? u4{0u, 0u, 0u, 0u} : bt.a[st][q];
+                        acc[q] = mfma_fp4_fp8_sel<st>(a_operand(av), B, acc[q], (int)bt.sa[q], (int)bt.sb);
+                    }
                 }
-                acc[q] = mfma_fp4_fp8(a_operand(av[q]), B, acc[q], sa[q], sb);
-            }
+            });
         }
+
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -503,52 +745,20 @@ __global__ __launch_bounds__(256) void k_gateup(GateUpParams p)
                 }
             }
         }
-        __syncthreads();
-    }
-}
-
-// Shared expert gate/up + activation (README §9, k3_moe step 6, first half),
-// bf16 weights, fp32 accumulation. One wave per shared row, tokens in turn.
-__global__ __launch_bounds__(256) void k_shared_gateup(const uint16_t *__restrict__ x, int T, int H,
-                                                       int Is, const uint16_t *__restrict__ S1,
-                                                       const uint16_t *__restrict__ S3, int act,
-                                                       float b1, float b2, float *__restrict__ ash)
-{
-    const int lane = threadIdx.x & 63;
-    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (r >= Is) return;
-    const uint16_t *g = S1 + (size_t)r * H;
-    const uint16_t *u = S3 + (size_t)r * H;
-    for (int t = 0; t < T; ++t) {
-        const uint16_t *xr = x + (size_t)t * H;
-        float ga = 0.0f, ua = 0.0f;
-        for (int i = lane * 8; i < H; i += 512) {
-            const u4 gv = *reinterpret_cast<const u4 *>(g + i);
-            const u4 uv = *reinterpret_cast<const u4 *>(u + i);
-            const u4 xv = *reinterpret_cast<const u4 *>(xr + i);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float x0 = bf16f(xv[q] & 0xffffu), x1 = bf16f(xv[q] >> 16);
-                ga = fmaf(bf16f(gv[q] & 0xffffu), x0, ga);
-                ga = fmaf(bf16f(gv[q] >> 16), x1, ga);
-                ua = fmaf(bf16f(uv[q] & 0xffffu), x0, ua);
-                ua = fmaf(bf16f(uv[q] >> 16), x1, ua);
-            }
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            ga += __shfl_xor(ga, o);
-            ua += __shfl_xor(ua, o);
-        }
-        if (lane == 0) ash[(size_t)t * Is + r] = act_fn(ga, ua, act, b1, b2);
+        __syncthreads();  // red is reused by the next token group
     }
 }
 
 // Down projection + router-order combine + shared expert (README §9, k3_moe
-// step 3 second half and step 6). One workgroup per (16-row tile of H,
-// token); wave w runs the experts j = w, w+4, ...; each expert's 16 outputs
-// land in LDS, then 16 threads sum w_j * y_j in j order and add the shared
-// expert's rows. An expert id outside [0, E) contributes zero and is counted.
+// step 3 second half and step 6). One workgroup of 8 waves per (16-row tile
+// of H, token); wave w runs the experts j = w, w+8, ... K is walked in
+// chunks of 4 steps: per lane one 16-byte load brings the W2 scale bytes of
+// the chunk (and one the activation-term scales), gathered into a word whose
+// byte the MFMA selects with op_sel. All loads of a chunk are issued before
+// its MFMAs. Each expert's 16 outputs land in LDS; then every wave computes 2
+// rows of the shared expert (bf16 weights, activation staged in LDS), and 16
+// threads sum w_j * y_j in j order and add the shared rows. An expert id
+// outside [0, E) contributes zero (no load, no MFMA) and is counted.
 struct DownParams {
     const uint8_t *dp, *ds;
     int64_t d_sp, d_ss;
@@ -562,47 +772,79 @@ struct DownParams {
     unsigned long long *errors;
 };
 
-__global__ __launch_bounds__(256) void k_down(DownParams p)
+constexpr int kDnWaves = 8;
+
+__host__ __device__ constexpr int dn_lds_bytes(int Is) { return 4 * Is; }
+
+template <bool WIDE>
+__global__ __launch_bounds__(64 * kDnWaves, K3MOE_MIN_WAVES) void k_down(DownParams p)
 {
     const int rt = blockIdx.x, t = blockIdx.y;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int rl = lane & 15, grp = lane >> 4;
-    const int KS = p.I >> 7;
-    const int64_t rowb = p.I >> 1, rows = p.I >> 5;
-    const int64_t row = (int64_t)rt * 16 + rl;
+    const int I = p.I, KS = I >> 7, SR = I >> 5;
+    constexpr bool wide = WIDE;  // I % 512 == 0: 16-byte aligned scale chunks
+    const int Is = p.Is;
+    const int32_t *idxr = p.idx + (size_t)t * p.K;
     __shared__ float ys[kMaxTopk][16];
     __shared__ float sh[16];
+    extern __shared__ float ash_l[];  // [Is]
 
-    for (int j = wave; j < p.K; j += 4) {
-        const int e = p.idx[(size_t)t * p.K + j];
-        const bool ok = (e >= 0) && (e < p.E);
+    if (rt == 0 && lane == 0)
+        for (int j = wave; j < p.K; j += kDnWaves)
+            if (idxr[j] < 0 || idxr[j] >= p.E) atomicAdd(p.errors, 1ull);
+    for (int i = threadIdx.x; i < Is; i += 64 * kDnWaves) ash_l[i] = p.ash[(size_t)t * Is + i];
+
+    const int bcol = (lane & 15) < kATerms ? (lane & 15) : 0;  // other columns: ignored copies
+    const uint32_t row = (uint32_t)rt * 16 + rl;
+    const uint32_t po = row * ((uint32_t)I >> 1) + grp * 16;
+    const uint32_t bo = bcol * (uint32_t)I + grp * 16;
+    const int NCH = (KS + 3) >> 2;
+
+    for (int j = wave; j < p.K; j += kDnWaves) {
+        const int e = idxr[j];
         v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        if (ok) {
-            const uint8_t *ap = p.dp + (int64_t)e * p.d_sp + row * rowb + grp * 16;
-            const uint8_t *asp = p.ds + (int64_t)e * p.d_ss + row * rows + grp;
-            const int col = lane & 15;
-            const bool bvalid = col < kATerms;
-            const int64_t asg = (int64_t)t * p.K + j;
-            const uint8_t *bp = p.aq + (asg * kATerms + (bvalid ? col : 0)) * p.I + grp * 16;
-            const uint8_t *bsp = p.as + (asg * kATerms + (bvalid ? col : 0)) * (p.I >> 5) + grp;
-            for (int st = 0; st < KS; ++st) {
-                u4 av = __builtin_nontemporal_load(reinterpret_cast<const u4 *>(ap + st * 64));
-                int sa = asp[st * 4];
-                if (sa == 255) {
-                    av = u4{0u, 0u, 0u, 0u};
-                    sa = 127;
+        if (e >= 0 && e < p.E) {
+            const uint8_t *ap = p.dp + (int64_t)e * p.d_sp;
+            const uint8_t *asr = p.ds + (int64_t)e * p.d_ss + (size_t)row * SR;
+            const uint8_t *bp = p.aq + ((int64_t)t * p.K + j) * kATerms * I;
+            const uint8_t *bsr = p.as + (((int64_t)t * p.K + j) * kATerms + bcol) * SR;
+            for (int c = 0; c < NCH; ++c) {
+                const int nst = min(4, KS - 4 * c);
+                u4 a[4], lo[4], hi[4];
+                uint32_t sa, sb;
+                static_for<0, 4>([&](auto s_) {
+                    constexpr int st = decltype(s_)::value;
+                    if (st < nst) {
+                        const uint32_t k = 4 * c + st;
+                        a[st] = *reinterpret_cast<const u4 *>(ap + (po + k * 64));
+                        lo[st] = *reinterpret_cast<const u4 *>(bp + (bo + k * 128));
+                        hi[st] = *reinterpret_cast<const u4 *>(bp + (bo + k * 128 + 64));
+                    }
+                });
+                if constexpr (wide) {
+                    sa = gather_scales(*reinterpret_cast<const u4 *>(asr + 16 * c), grp);
+                    sb = gather_scales(*reinterpret_cast<const u4 *>(bsr + 16 * c), grp);
+                } else {  // short rows: byte loads, steps past K left at 127
+                    sa = sb = 0x7f7f7f7fu;
+                    for (int st = 0; st < nst; ++st) {
+                        const uint32_t sh8 = 8 * st, m = ~(0xffu << sh8);
+                        sa = (sa & m) | ((uint32_t)asr[(4 * c + st) * 4 + grp] << sh8);
+                        sb = (sb & m) | ((uint32_t)bsr[(4 * c + st) * 4 + grp] << sh8);
+                    }
                 }
-                u4 lo = u4{0u, 0u, 0u, 0u}, hi = u4{0u, 0u, 0u, 0u};
-                int sb = 127;
-                if (bvalid) {
-                    lo = *reinterpret_cast<const u4 *>(bp + st * 128);
-                    hi = *reinterpret_cast<const u4 *>(bp + st * 128 + 64);
-                    sb = bsp[st * 4];
-                }
-                acc = mfma_fp4_fp8(a_operand(av), b_operand(lo, hi), acc, sa, sb);
+                const uint32_t drop = ff_bytes(sa);  // scale byte 255: the group drops out
+                sa ^= drop;
+                static_for<0, 4>([&](auto s_) {
+                    constexpr int st = decltype(s_)::value;
+                    if (st < nst) {
+                        const u4 av = ((drop >> (8 * st + 7)) & 1u) ? u4{0u, 0u, 0u, 0u} : a[st];
+                        acc = mfma_fp4_fp8_sel<st>(a_operand(av), b_operand(lo[st], hi[st]), acc, (int)sa,
+                                                   (int)sb);
+                    }
+                });
             }
-        } else if (rt == 0 && lane == 0) {
-            atomicAdd(p.errors, 1ull);
         }
         float y[4];
 #pragma unroll
@@ -615,40 +857,70 @@ __global__ __launch_bounds__(256) void k_down(DownParams p)
             for (int r = 0; r < 4; ++r) ys[j][4 * q + r] = y[r];
         }
     }
-    if (p.Is > 0) {
-        const float *a = p.ash + (size_t)t * p.Is;
-        for (int rr = 0; rr < 4; ++rr) {
-            const int64_t orow = (int64_t)rt * 16 + wave * 4 + rr;
-            const uint16_t *srow = p.sh_down + orow * p.Is;
-            float acc = 0.0f;
-            for (int i = lane * 8; i < p.Is; i += 512) {
-                const u4 wv = *reinterpret_cast<const u4 *>(srow + i);
-                const float4 a0 = *reinterpret_cast<const float4 *>(a + i);
-                const float4 a1 = *reinterpret_cast<const float4 *>(a + i + 4);
-                acc = fmaf(bf16f(wv[0] & 0xffffu), a0.x, acc);
-                acc = fmaf(bf16f(wv[0] >> 16), a0.y, acc);
-                acc = fmaf(bf16f(wv[1] & 0xffffu), a0.z, acc);
-                acc = fmaf(bf16f(wv[1] >> 16), a0.w, acc);
-                acc = fmaf(bf16f(wv[2] & 0xffffu), a1.x, acc);
-                acc = fmaf(bf16f(wv[2] >> 16), a1.y, acc);
-                acc = fmaf(bf16f(wv[3] & 0xffffu), a1.z, acc);
-                acc = fmaf(bf16f(wv[3] >> 16), a1.w, acc);
-            }
+
+    // shared expert: 2 rows of S2 per wave against the staged activation
+    __syncthreads();
+    if (Is > 0) {
+        static_assert(kDnWaves * 2 == 16, "2 shared rows per wave");
+        const uint16_t *srow0 = p.sh_down + ((int64_t)rt * 16 + wave * 2) * Is;
+        float a2[2] = {0.0f, 0.0f};
+        constexpr int CH = 4;  // 512-element slices whose loads are issued together
+        for (int i0 = lane * 8; i0 < Is; i0 += 512 * CH) {
+            u4 wv[2][CH];
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-            if (lane == 0) sh[wave * 4 + rr] = acc;
+            for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+                for (int c = 0; c < CH; ++c) {
+                    const int i = i0 + 512 * c;
+                    wv[rr][c] = i < Is ? *reinterpret_cast<const u4 *>(srow0 + (size_t)rr * Is + i)
+                                       : u4{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int i = i0 + 512 * c;
+                if (i >= Is) break;
+                const float4 x0 = *reinterpret_cast<const float4 *>(ash_l + i);
+                const float4 x1 = *reinterpret_cast<const float4 *>(ash_l + i + 4);
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) {
+                    const u4 w4 = wv[rr][c];
+                    float v = a2[rr];
+                    v = fmaf(bf16f(w4[0] & 0xffffu), x0.x, v);
+                    v = fmaf(bf16f(w4[0] >> 16), x0.y, v);
+                    v = fmaf(bf16f(w4[1] & 0xffffu), x0.z, v);
+                    v = fmaf(bf16f(w4[1] >> 16), x0.w, v);
+                    v = fmaf(bf16f(w4[2] & 0xffffu), x1.x, v);
+                    v = fmaf(bf16f(w4[2] >> 16), x1.y, v);
+                    v = fmaf(bf16f(w4[3] & 0xffffu), x1.z, v);
+                    v = fmaf(bf16f(w4[3] >> 16), x1.w, v);
+                    a2[rr] = v;
+                }
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) a2[rr] += __shfl_xor(a2[rr], o);
+            if (lane == 0) sh[wave * 2 + rr] = a2[rr];
         }
     }
     __syncthreads();
     if (threadIdx.x < 16) {
         float o = 0.0f;
         for (int j = 0; j < p.K; ++j) o = fmaf(p.w[(size_t)t * p.K + j], ys[j][threadIdx.x], o);
-        if (p.Is > 0) o += sh[threadIdx.x];
+        if (Is > 0) o += sh[threadIdx.x];
         p.out[(size_t)t * p.H + rt * 16 + threadIdx.x] = o;
     }
 }
 
 }  // namespace
+
+template <int NQ>
+static void topk_launch(int T, hipStream_t s, const float *sc, const float *ch, const LayerView &L,
+                        int32_t *idx, float *w)
+{
+    k_topk<NQ><<<T, 64, 0, s>>>(sc, ch, L.E, L.K, L.renorm, L.routed_scale, idx, w);
+}
 
 hipError_t launch_route(const LayerView &L, const uint16_t *x, int T, int32_t *idx, float *w,
                         float *logits, char *ws, const WsLayout &lay, hipStream_t s, Profiler *prof)
@@ -662,7 +934,14 @@ hipError_t launch_route(const LayerView &L, const uint16_t *x, int T, int32_t *i
     }
     {
         StageMark m(prof, K3MOE_STAGE_TOPK, s);
-        k_topk<<<T, 64, 0, s>>>(sc, ch, L.E, L.K, L.renorm, L.routed_scale, idx, w);
+        const int nq = (L.E + 63) / 64;
+        if (nq <= 1) topk_launch<1>(T, s, sc, ch, L, idx, w);
+        else if (nq <= 2) topk_launch<2>(T, s, sc, ch, L, idx, w);
+        else if (nq <= 4) topk_launch<4>(T, s, sc, ch, L, idx, w);
+        else if (nq <= 8) topk_launch<8>(T, s, sc, ch, L, idx, w);
+        else if (nq <= 16) topk_launch<16>(T, s, sc, ch, L, idx, w);
+        else if (nq <= 32) topk_launch<32>(T, s, sc, ch, L, idx, w);
+        else topk_launch<64>(T, s, sc, ch, L, idx, w);
     }
     return hipGetLastError();
 }
@@ -683,21 +962,22 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const in
     float *ash = reinterpret_cast<float *>(ws + lay.ash);
 
     const int64_t n = (int64_t)T * L.H;
-    {
-        StageMark m(prof, K3MOE_STAGE_XSPLIT, s);
-        k_xsplit<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(x, n, L.H, xq, xs);
-    }
-
+    const unsigned slabs = (unsigned)((n + 255) / 256);
     const int nchunks = (T + kPermChunk - 1) / kPermChunk;
-    StageMark *pm = new StageMark(prof, K3MOE_STAGE_PERM, s);
     if (nchunks == 1) {
-        k_perm_single<<<1, 1024, 0, s>>>(idx, T, L.K, L.E, active_n, active_e, active_off, sorted);
+        StageMark m(prof, K3MOE_STAGE_PERM, s);
+        k_prep_small<<<1 + slabs, 256, 0, s>>>(x, n, L.H, xq, xs, idx, T, L.K, L.E, active_n, active_e,
+                                               active_off, sorted);
     } else {
+        {
+            StageMark m(prof, K3MOE_STAGE_XSPLIT, s);
+            k_xsplit<<<slabs, 256, 0, s>>>(x, n, L.H, xq, xs);
+        }
+        StageMark m(prof, K3MOE_STAGE_PERM, s);
         k_perm_hist<<<nchunks, 256, 0, s>>>(idx, T, L.K, L.E, chunk_cnt);
         k_perm_scan<<<1, 1024, 0, s>>>(nchunks, L.E, chunk_cnt, active_n, active_e, active_off);
         k_perm_scatter<<<nchunks, 64, 0, s>>>(idx, T, L.K, L.E, chunk_cnt, sorted);
     }
-    delete pm;
 
     GateUpParams gp;
     gp.gp = L.gp;
@@ -712,8 +992,11 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const in
     gp.I = L.I;
     gp.K = L.K;
     gp.act = L.act;
+    gp.T = T;
+    gp.Is = L.Is;
     gp.b1 = L.b1;
     gp.b2 = L.b2;
+    gp.x = x;
     gp.xq = xq;
     gp.xs = xs;
     gp.active_n = active_n;
@@ -722,15 +1005,20 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const in
     gp.sorted = sorted;
     gp.aq = aq;
     gp.as = as;
+    gp.sh_gate = L.sh_gate;
+    gp.sh_up = L.sh_up;
+    gp.ash = ash;
     const int64_t max_active = std::min<int64_t>(L.E, (int64_t)T * L.K);
+    gp.routed_blocks = (int)(max_active * (L.I / 32));
+    const int shared_blocks = (L.Is + 3) / 4;
+    gp.shared_blocks = shared_blocks;
     {
         StageMark m(prof, K3MOE_STAGE_GATEUP, s);
-        k_gateup<<<(unsigned)(max_active * (L.I / 32)), 256, 0, s>>>(gp);
-    }
-    if (L.Is > 0) {
-        StageMark m(prof, K3MOE_STAGE_SHARED_GATEUP, s);
-        k_shared_gateup<<<(L.Is + 3) / 4, 256, 0, s>>>(x, T, L.H, L.Is, L.sh_gate, L.sh_up, L.act,
-                                                        L.b1, L.b2, ash);
+        const unsigned nblk = (unsigned)(gp.routed_blocks + shared_blocks);
+        if (L.H % 512 == 0)
+            k_gateup<true><<<nblk, 256, 0, s>>>(gp);
+        else
+            k_gateup<false><<<nblk, 256, 0, s>>>(gp);
     }
 
     DownParams dp;
@@ -753,7 +1041,10 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const in
     dp.errors = L.errors;
     {
         StageMark m(prof, K3MOE_STAGE_DOWN, s);
-        k_down<<<dim3(L.H / 16, T), 256, 0, s>>>(dp);
+        if (L.I % 512 == 0)
+            k_down<true><<<dim3(L.H / 16, T), 64 * kDnWaves, dn_lds_bytes(L.Is), s>>>(dp);
+        else
+            k_down<false><<<dim3(L.H / 16, T), 64 * kDnWaves, dn_lds_bytes(L.Is), s>>>(dp);
     }
     return hipGetLastError();
 }

@@ -31,6 +31,20 @@ __global__ void k_fill_scales(uint8_t *dst, int64_t n, uint64_t key, int64_t sta
         dst[i] = (uint8_t)(lo + mix64(key + (uint64_t)(start + i + 1) * kGamma) % (uint64_t)span);
 }
 
+// Reads every 16-byte word of a buffer once (a calibration kernel of known
+// traffic for hardware byte counters); writes one word only if the xor of the
+// data hits a fixed value.
+__global__ void k_read_probe(const uint4 *src, int64_t n16, unsigned *sink)
+{
+    unsigned acc = 0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const uint4 v = src[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
 unsigned grid_for(int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 65536); }
 
 }  // namespace
@@ -55,6 +69,15 @@ int k3synth_fill_scales(void *dst, int64_t n, uint64_t key, int64_t start, int l
     if (!dst || n < 0 || start < 0 || span <= 0 || lo < 0 || lo + span > 256) return -1;
     if (n == 0) return 0;
     k_fill_scales<<<grid_for(n), 256, 0, (hipStream_t)stream>>>((uint8_t *)dst, n, key, start, lo, span);
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// Launch the read-probe over nbytes (a multiple of 16) of src; sink is a
+// 4-byte device word.
+int k3synth_read_probe(const void *src, int64_t nbytes, void *sink, void *stream)
+{
+    if (!src || !sink || nbytes < 0 || nbytes % 16 || (uintptr_t)src % 16) return -1;
+    k_read_probe<<<4096, 256, 0, (hipStream_t)stream>>>((const uint4 *)src, nbytes / 16, (unsigned *)sink);
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 

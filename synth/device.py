@@ -27,6 +27,8 @@ def lib():
         L.k3synth_fill_packed.argtypes = [P, i64, ctypes.c_uint64, i64, P]
         L.k3synth_fill_scales.restype = ctypes.c_int
         L.k3synth_fill_scales.argtypes = [P, i64, ctypes.c_uint64, i64, ctypes.c_int, ctypes.c_int, P]
+        L.k3synth_read_probe.restype = ctypes.c_int
+        L.k3synth_read_probe.argtypes = [P, i64, P, P]
         _lib = L
     return _lib
 
@@ -46,6 +48,14 @@ def fill_scales(t, key, start=0):
                                    synth.SCALE_SPAN, _stream(t.device))
     if rc != 0:
         raise RuntimeError(f"k3synth_fill_scales failed ({rc})")
+
+
+def read_probe(t, sink):
+    """Launch the calibration read kernel over tensor t (every byte once)."""
+    rc = lib().k3synth_read_probe(t.data_ptr(), t.numel() * t.element_size(), sink.data_ptr(),
+                                  _stream(t.device))
+    if rc != 0:
+        raise RuntimeError(f"k3synth_read_probe failed ({rc})")
 
 
 def bf16_tensor(bits, device):
