@@ -165,8 +165,9 @@ typedef enum {
     K3MOE_STAGE_PERM = 3,           /* token -> expert permutation        */
     K3MOE_STAGE_GATEUP = 4,         /* routed gate/up MXFP4 + activation  */
     K3MOE_STAGE_SHARED_GATEUP = 5,  /* shared expert gate/up + activation */
-    K3MOE_STAGE_DOWN = 6,           /* down MXFP4 + combine + shared down */
-    K3MOE_N_STAGES = 7
+    K3MOE_STAGE_DOWN = 6,           /* down MXFP4 (+ shared down)         */
+    K3MOE_STAGE_COMBINE = 7,        /* router-order weighted sum + shared */
+    K3MOE_N_STAGES = 8
 } k3moe_stage;
 
 k3moe_status k3moe_profile_enable(k3moe_layer *layer, int enable);

@@ -55,7 +55,7 @@ _lib = None
 EXPORTS = ("k3moe_layer_create", "k3moe_workspace_size", "k3moe_route", "k3moe_forward",
            "k3moe_error_count", "k3moe_error_reset", "k3moe_profile_enable",
            "k3moe_profile_read", "k3moe_layer_destroy", "k3moe_status_string")
-STAGES = ("router", "topk", "xsplit", "perm", "gateup", "shared_gateup", "down")
+STAGES = ("router", "topk", "xsplit", "perm", "gateup", "shared_gateup", "down", "combine")
 
 
 def lib():

@@ -43,6 +43,7 @@ WsLayout ws_layout(const k3moe_config &c, int64_t T)
     L.aq = take((size_t)T * K * kATerms * I);
     L.as = take((size_t)T * K * kATerms * (I / 32));
     L.ash = take(sizeof(float) * T * std::max<int64_t>(Is, 1));
+    L.ys = take(sizeof(float) * T * (K + 1) * H);
     L.total = o;
     return L;
 }

@@ -33,6 +33,7 @@ struct WsLayout {
     size_t sorted;            // int32 [T * k]
     size_t aq, as;            // activation fp8 terms [T*k][4][I], scales [T*k][4][I/32]
     size_t ash;               // shared activation fp32 [T][I_s]
+    size_t ys;                // expert outputs fp32 [T][k + 1][H] (slot k: shared expert)
     size_t total;
 };
 

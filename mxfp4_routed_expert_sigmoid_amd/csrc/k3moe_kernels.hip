@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t *__restrict__ x,
     const uint16_t *wr = Wr + (size_t)e * H;
     const uint16_t *xr = x + (size_t)t * H;
     double acc = 0.0;
-    constexpr int CH = 7;  // 512-element slices whose loads are issued together
+    constexpr int CH = 14;  // 512-element slices whose loads are issued together
     for (int i0 = lane * 8; i0 < H; i0 += 512 * CH) {
         u4 wv[CH], xv[CH];
 #pragma unroll
@@ -198,13 +198,15 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v)
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Top-k by repeated maximum (README §9): one wave per token; lane l holds the
-// selection scores of experts l, l+64, ... (NQ per lane) as order-preserving
-// uint32 keys and caches its best remaining one. Each round takes the
-// wave-wide maximum key, then the lowest expert index among the lanes holding
-// it (so equal scores go to the lower index, as the strict comparison of the
-// repeated maximum does); the winning lane rescans. NaN ranks as -inf.
-// Weights are the unbiased scores, renormalised in router order, then scaled.
+// Top-k by repeated maximum (README §9). One wave per token; lane l holds
+// the selection scores of experts l*NQ .. l*NQ+NQ-1 (a contiguous range, so
+// a lower lane always holds lower expert indices) as order-preserving uint32
+// keys, and keeps its best remaining key and the lowest position holding it.
+// Each round takes the wave-wide maximum key; among the lanes holding it the
+// lowest lane wins (hence the lowest expert index, as the strict comparison
+// of the repeated maximum gives); the winner zeroes that key and rescans.
+// NaN ranks as -inf. Weights are the unbiased scores of the picks,
+// renormalised in router order, then scaled.
 __device__ __forceinline__ uint32_t order_key(float v)
 {
     if (v != v) v = -INFINITY;
@@ -220,37 +222,37 @@ __global__ __launch_bounds__(64) void k_topk(const float *__restrict__ sc, const
     const int t = blockIdx.x;
     const int lane = threadIdx.x;
     const float *c = ch + (size_t)t * E;
-    uint32_t v[NQ];
-    uint64_t avail = 0;
+    const int e0 = lane * NQ;
+    // every load is issued before the first is used (clamped index, no branch)
+    float raw[NQ];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        const int e = lane + 64 * q;
-        v[q] = 0u;
-        if (e < E) {
-            v[q] = order_key(c[e]);
-            avail |= 1ull << q;
-        }
-    }
-    uint32_t bk;  // best key of this lane (0: none left)
-    int be;       // its expert
+    for (int q = 0; q < NQ; ++q) raw[q] = c[min(e0 + q, E - 1)];
+    uint32_t v[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) v[q] = e0 + q < E ? order_key(raw[q]) : 0u;  // 0: none / taken
+    uint32_t bk;  // best remaining key of this lane (0: none)
+    int bq;       // its position
     auto rescan = [&]() {
         bk = 0u;
-        be = -1;
+        bq = 0;
 #pragma unroll
-        for (int q = 0; q < NQ; ++q)
-            if (((avail >> q) & 1ull) && v[q] > bk) {
-                bk = v[q];
-                be = lane + 64 * q;
-            }
+        for (int q = 0; q < NQ; ++q) {
+            const bool gt = v[q] > bk;
+            bk = gt ? v[q] : bk;
+            bq = gt ? q : bq;
+        }
     };
     rescan();
     int mine = 0;
     for (int j = 0; j < K; ++j) {
         const uint32_t m = wave_reduce_u32<true>(bk);
-        const uint32_t cand = (be >= 0 && bk == m) ? (uint32_t)be : 0xffffffffu;
-        const int win = (int)wave_reduce_u32<false>(cand);
-        if ((win & 63) == lane) {
-            avail &= ~(1ull << (win >> 6));
+        const uint64_t holders = __ballot(bk == m);
+        const int wl = (int)__builtin_ctzll(holders);  // lowest lane holding the maximum
+        const int win = wl * NQ + __builtin_amdgcn_readlane(bq, wl);
+        if (lane == wl) {
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                if (q == bq) v[q] = 0u;
             rescan();
         }
         if (lane == j) mine = win;
@@ -491,12 +493,14 @@ __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t *__restrict__
 struct GateUpParams {
     const uint8_t *gp, *gs, *up, *us;
     int64_t g_sp, g_ss, u_sp, u_ss;
-    int H, I, K, act, T, Is, routed_blocks, shared_blocks;
+    int H, I, K, E, act, T, Is, routed_blocks, shared_blocks;
     float b1, b2;
     const uint16_t *x;
     const uint8_t *xq, *xs;
+    const int32_t *idx;
     const int32_t *active_n, *active_e, *active_off, *sorted;
     uint8_t *aq, *as;
+    float *act_f;  // T = 1 path: fp32 activations [k][I]
     const uint16_t *sh_gate, *sh_up;
     float *ash;
 };
@@ -913,6 +917,584 @@ __global__ __launch_bounds__(64 * kDnWaves, K3MOE_MIN_WAVES) void k_down(DownPar
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// Single-token path (T = 1). The k assignments are the router slots j
+// themselves (slot j takes expert idx[j]), so no permutation is built.
+
+// ---------------------------------------------------------------------------
+// Single-token kernels. On MI355X a CU streams weights at ~23-26 GB/s with
+// the MFMA operand access pattern, so these grids give every CU the same
+// number of bytes: the kernel time is the most loaded CU's time.
+
+// Gate/up, T = 1. Routed work comes in units of (slot, 16-row tile of I),
+// gate and up, over the whole K range: 2 weight fragments per K step straight
+// from HBM into the MFMA A operand. A block of 4 waves runs 3 units (waves
+// 0..2) and a slice of the shared expert's rows (wave 3); with two blocks per
+// CU every CU moves the same bytes. The token's e4m3 terms and scales and the
+// units' E8M0 rows are staged in LDS once per block; K is walked in chunks of
+// 4 steps, double-buffered in registers. The activation is written in fp32
+// (act_f[slot][I]); the down kernel expands it into e4m3 terms.
+constexpr int kGuDecWaves = 4;                 // waves per block
+constexpr int kGuDecUnits = 3;                 // routed units per block (waves 0..2)
+constexpr int kGuUnitRows = 16;                // rows per routed unit
+constexpr int kGuShMaxRows = 4;                // shared rows per pass of wave 3
+constexpr int kXqPad = 64;                     // LDS term-row padding (banks)
+constexpr int kScPad = 16;                     // LDS scale-row padding (banks)
+constexpr int kGuStgQ = 8;                     // token-term staging copies per thread
+constexpr int kGuStgS = 6;                     // scale-row staging copies per thread
+
+__host__ __device__ constexpr int gu_dec_lds_bytes(int H)
+{
+    return 4 * (H + kXqPad) + 4 * (H / 32) + kGuDecUnits * 2 * kGuUnitRows * (H / 32 + kScPad);
+}
+
+// Wave 3 of a gate/up block: shared rows [r0, r1) of gate and up (bf16,
+// fp32 FMA), activation to ash. 512-element slices, 8 elements per lane,
+// double-buffered; unconditional clamped loads (a lane past the row end
+// multiplies 0).
+__device__ void shared_gateup_rows(const GateUpParams &p, int r0, int r1)
+{
+    const int lane = threadIdx.x & 63;
+    const int H = p.H;
+    const int NS = (H + 511) >> 9;
+    struct Slice {
+        u4 w[2 * kGuShMaxRows];  // gate rows, up rows
+        u4 x;
+    };
+    for (int ra = r0; ra < r1; ra += kGuShMaxRows) {
+        const int nr = min(kGuShMaxRows, r1 - ra);
+        float acc[2 * kGuShMaxRows];
+#pragma unroll
+        for (int q = 0; q < 2 * kGuShMaxRows; ++q) acc[q] = 0.0f;
+        auto load = [&](int sl, Slice &b) {
+            const int i = sl * 512 + lane * 8;
+            const int ic = min(i, H - 8);
+#pragma unroll
+            for (int q = 0; q < kGuShMaxRows; ++q) {
+                const int r = ra + min(q, nr - 1);
+                b.w[q] = *reinterpret_cast<const u4 *>(p.sh_gate + (size_t)r * H + ic);
+                b.w[kGuShMaxRows + q] = *reinterpret_cast<const u4 *>(p.sh_up + (size_t)r * H + ic);
+            }
+            b.x = *reinterpret_cast<const u4 *>(p.x + ic);
+            if (i >= H) b.x = u4{0u, 0u, 0u, 0u};
+        };
+        auto compute = [&](const Slice &b) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const float x0 = bf16f(b.x[h] & 0xffffu), x1 = bf16f(b.x[h] >> 16);
+#pragma unroll
+                for (int q = 0; q < 2 * kGuShMaxRows; ++q) {
+                    acc[q] = fmaf(bf16f(b.w[q][h] & 0xffffu), x0, acc[q]);
+                    acc[q] = fmaf(bf16f(b.w[q][h] >> 16), x1, acc[q]);
+                }
+            }
+        };
+        Slice b0, b1;
+        load(0, b0);
+        load(min(1, NS - 1), b1);
+        for (int sl = 0; sl < NS; sl += 2) {
+            compute(b0);
+            load(min(sl + 2, NS - 1), b0);
+            if (sl + 1 < NS) compute(b1);
+            load(min(sl + 3, NS - 1), b1);
+        }
+#pragma unroll
+        for (int q = 0; q < 2 * kGuShMaxRows; ++q)
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) acc[q] += __shfl_xor(acc[q], o);
+        if (lane == 0)
+#pragma unroll
+            for (int q = 0; q < kGuShMaxRows; ++q)
+                if (q < nr) p.ash[ra + q] = act_fn(acc[q], acc[kGuShMaxRows + q], p.act, p.b1, p.b2);
+    }
+}
+
+template <bool WIDE>
+__global__ __launch_bounds__(64 * kGuDecWaves) void k_gateup_dec(GateUpParams p)
+{
+    static_assert(kXTerms == 4, "4-term expansion: term = column % 4");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int grp = lane >> 4, col = lane & 15, term = col & 3;
+    const int H = p.H, KS = H >> 7, SR = H >> 5, NCH = (KS + 3) >> 2;
+    const int XQS = H + kXqPad, SRP = SR + kScPad;
+    const int RT = p.I / kGuUnitRows;
+    const int nunits = p.K * RT;
+    const int b = blockIdx.x;
+
+    extern __shared__ __align__(16) uint8_t lds[];
+    uint8_t *xq_l = lds;                  // [4][H + pad]  token terms
+    uint8_t *xs_l = xq_l + 4 * XQS;       // [4][H/32]     their scales
+    uint8_t *sc_l = xs_l + 4 * SR;        // [3][2][16][H/32 + pad] unit scale rows
+
+    // this wave's routed unit (waves 0..2) and its expert
+    const int u = kGuDecUnits * b + wave;
+    const bool routed = wave < kGuDecUnits && u < nunits;
+    const int slot = routed ? u / RT : 0, rt = routed ? u - (u / RT) * RT : 0;
+    int e = routed ? p.idx[slot] : 0;
+    const bool active = routed && e >= 0 && e < p.E;  // an invalid id: nothing (the combine counts it)
+    e = active ? e : 0;
+    const uint8_t *gpe = p.gp + e * p.g_sp, *upe = p.up + e * p.u_sp;
+    const uint32_t po = ((uint32_t)rt * kGuUnitRows + (lane & 15)) * ((uint32_t)H >> 1) + grp * 16;
+
+    struct Chunk {
+        u4 a[4][2];  // [step][gate, up]
+    };
+    // unconditional loads (a step past K re-reads the last step; never used)
+    auto load = [&](int c, Chunk &bf) {
+        static_for<0, 4>([&](auto s_) {
+            constexpr int st = decltype(s_)::value;
+            const uint32_t k = (uint32_t)min(4 * c + st, KS - 1) * 64;
+            bf.a[st][0] = *reinterpret_cast<const u4 *>(gpe + (po + k));
+            bf.a[st][1] = *reinterpret_cast<const u4 *>(upe + (po + k));
+        });
+    };
+
+    // Staging: all staging loads first, then the routed waves' first two
+    // weight chunks, then the LDS stores (which wait only for the staging
+    // loads). A unit's scale rows are 16 consecutive rows, contiguous.
+    Chunk b0, b1;
+    if constexpr (WIDE) {  // SR % 16 == 0
+        const int nxq = H >> 2, nxs = SR >> 2;  // u4 counts
+        const int nrow = SR >> 4, nsc = kGuDecUnits * 2 * kGuUnitRows * nrow;
+        u4 tq[kGuStgQ], ts[kGuStgS], tx;
+#pragma unroll
+        for (int q = 0; q < kGuStgQ; ++q) {
+            const int i = min((int)threadIdx.x + q * 64 * kGuDecWaves, nxq - 1);
+            const int t = i / (H >> 4), o = i - t * (H >> 4);
+            tq[q] = *reinterpret_cast<const u4 *>(p.xq + (size_t)t * H + 16 * o);
+        }
+#pragma unroll
+        for (int q = 0; q < kGuStgS; ++q) {
+            const int i = min((int)threadIdx.x + q * 64 * kGuDecWaves, nsc - 1);
+            const int un = i / (2 * kGuUnitRows * nrow), rem = i - un * (2 * kGuUnitRows * nrow);
+            const int mat = rem / (kGuUnitRows * nrow), rem2 = rem - mat * (kGuUnitRows * nrow);
+            const int uu = min(kGuDecUnits * b + un, nunits - 1);
+            const int su = uu / RT, srt = uu - su * RT;
+            int se = p.idx[su];
+            se = (se >= 0 && se < p.E) ? se : 0;
+            const uint8_t *sbase = mat ? p.us + se * p.u_ss : p.gs + se * p.g_ss;
+            ts[q] = *reinterpret_cast<const u4 *>(sbase + (size_t)srt * kGuUnitRows * SR + 16 * rem2);
+        }
+        tx = *reinterpret_cast<const u4 *>(p.xs + 16 * min((int)threadIdx.x, nxs - 1));
+        __builtin_amdgcn_sched_barrier(0);
+        if (active) {
+            load(0, b0);
+            load(min(1, NCH - 1), b1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if ((int)threadIdx.x < nxs) *reinterpret_cast<u4 *>(xs_l + 16 * threadIdx.x) = tx;
+#pragma unroll
+        for (int q = 0; q < kGuStgQ; ++q) {
+            const int i = (int)threadIdx.x + q * 64 * kGuDecWaves;
+            if (i < nxq) {
+                const int t = i / (H >> 4), o = i - t * (H >> 4);
+                *reinterpret_cast<u4 *>(xq_l + t * XQS + 16 * o) = tq[q];
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < kGuStgS; ++q) {
+            const int i = (int)threadIdx.x + q * 64 * kGuDecWaves;
+            if (i < nsc) {
+                const int row = i / nrow, o = i - row * nrow;  // row over [unit][mat][16]
+                *reinterpret_cast<u4 *>(sc_l + row * SRP + 16 * o) = ts[q];
+            }
+        }
+    } else {  // short rows (small layers): byte copies
+        for (int i = threadIdx.x; i < 4 * H; i += blockDim.x) xq_l[(i / H) * XQS + i % H] = p.xq[i];
+        for (int i = threadIdx.x; i < 4 * SR; i += blockDim.x) xs_l[i] = p.xs[i];
+        for (int i = threadIdx.x; i < kGuDecUnits * 2 * kGuUnitRows * SR; i += blockDim.x) {
+            const int row = i / SR, o = i - row * SR;
+            const int un = row / (2 * kGuUnitRows), mat = (row / kGuUnitRows) & 1, r = row % kGuUnitRows;
+            const int uu = min(kGuDecUnits * b + un, nunits - 1);
+            const int su = uu / RT, srt = uu - su * RT;
+            int se = p.idx[su];
+            se = (se >= 0 && se < p.E) ? se : 0;
+            const uint8_t *sbase = mat ? p.us + se * p.u_ss : p.gs + se * p.g_ss;
+            sc_l[row * SRP + o] = sbase[((size_t)srt * kGuUnitRows + r) * SR + o];
+        }
+        if (active) {
+            load(0, b0);
+            load(min(1, NCH - 1), b1);
+        }
+    }
+    __syncthreads();
+
+    if (wave == kGuDecUnits) {  // the shared expert's slice of rows
+        if (p.Is > 0) {
+            const int nb = gridDim.x;
+            shared_gateup_rows(p, (int)((int64_t)p.Is * b / nb), (int)((int64_t)p.Is * (b + 1) / nb));
+        }
+        return;
+    }
+    if (!active) return;
+
+    const uint8_t *xb = xq_l + term * XQS + grp * 16;  // B column = term of token 0
+    const uint8_t *xsr = xs_l + term * SR;
+    const uint8_t *s_g = sc_l + (wave * 2 * kGuUnitRows + (lane & 15)) * SRP;  // this lane's gate row
+    const uint8_t *s_u = s_g + kGuUnitRows * SRP;
+    v4f accg = v4f{0.0f, 0.0f, 0.0f, 0.0f}, accu = accg;
+    auto compute = [&](int c, const Chunk &bf) {
+        uint32_t sg, su, sx;
+        if constexpr (WIDE) {
+            sg = gather_scales(*reinterpret_cast<const u4 *>(s_g + 16 * c), grp);
+            su = gather_scales(*reinterpret_cast<const u4 *>(s_u + 16 * c), grp);
+            sx = gather_scales(*reinterpret_cast<const u4 *>(xsr + 16 * c), grp);
+        } else {  // short rows: steps past K left at 127 (never multiplied)
+            sg = su = sx = 0x7f7f7f7fu;
+            for (int st = 0; st < 4 && 4 * c + st < KS; ++st) {
+                const int o = (4 * c + st) * 4 + grp, sh8 = 8 * st;
+                const uint32_t m = ~(0xffu << sh8);
+                sg = (sg & m) | ((uint32_t)s_g[o] << sh8);
+                su = (su & m) | ((uint32_t)s_u[o] << sh8);
+                sx = (sx & m) | ((uint32_t)xsr[o] << sh8);
+            }
+        }
+        const uint32_t dg = ff_bytes(sg), du = ff_bytes(su);  // scale byte 255: group drops out
+        sg ^= dg;
+        su ^= du;
+        static_for<0, 4>([&](auto s_) {
+            constexpr int st = decltype(s_)::value;
+            if (4 * c + st < KS) {
+                const uint32_t k = 4 * c + st;
+                const v8i B = b_operand(*reinterpret_cast<const u4 *>(xb + k * 128),
+                                        *reinterpret_cast<const u4 *>(xb + k * 128 + 64));
+                const u4 ag = ((dg >> (8 * st + 7)) & 1u) ? u4{0u, 0u, 0u, 0u} : bf.a[st][0];
+                const u4 au = ((du >> (8 * st + 7)) & 1u) ? u4{0u, 0u, 0u, 0u} : bf.a[st][1];
+                accg = mfma_fp4_fp8_sel<st>(a_operand(ag), B, accg, (int)sg, (int)sx);
+                accu = mfma_fp4_fp8_sel<st>(a_operand(au), B, accu, (int)su, (int)sx);
+            }
+        });
+    };
+    for (int c = 0; c < NCH; c += 2) {
+        compute(c, b0);
+        load(min(c + 2, NCH - 1), b0);
+        if (c + 1 < NCH) compute(c + 1, b1);
+        load(min(c + 3, NCH - 1), b1);
+    }
+
+    // columns 4m..4m+3 hold the 4 terms: add them (lane 16g gets rows 4g..4g+3)
+    float g[4], uu[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        g[r] = accg[r] + __shfl_xor(accg[r], 1);
+        g[r] += __shfl_xor(g[r], 2);
+        uu[r] = accu[r] + __shfl_xor(accu[r], 1);
+        uu[r] += __shfl_xor(uu[r], 2);
+    }
+    if (col == 0) {
+        float4 a4;
+        a4.x = act_fn(g[0], uu[0], p.act, p.b1, p.b2);
+        a4.y = act_fn(g[1], uu[1], p.act, p.b1, p.b2);
+        a4.z = act_fn(g[2], uu[2], p.act, p.b1, p.b2);
+        a4.w = act_fn(g[3], uu[3], p.act, p.b1, p.b2);
+        *reinterpret_cast<float4 *>(p.act_f + (size_t)slot * p.I + rt * kGuUnitRows + 4 * grp) = a4;
+    }
+}
+
+// Down projection, T = 1. Block (j, i) of K x M blocks takes router slot j,
+// the 16-row tiles [T16*i/M, T16*(i+1)/M) of H (T16 = H/16) and the shared
+// rows [H*(jM+i)/(KM), ...): every block moves about the same bytes. The
+// slot's fp32 activation is expanded into 4 e4m3 terms (one E8M0 scale per
+// 32 elements per term) while it is staged in LDS, with the tiles' E8M0 rows; wave w takes tiles t0+w, t0+w+4, ... (K in chunks of 4 MFMA steps, a
+// 4-deep register ring) and shared rows r0+w, r0+w+4, ... (bf16, fp32 FMA,
+// loads issued before the routed stream). Results go to the staging rows
+// ys[j][.] and ys[k][.] (shared); the combine sums them in router order.
+struct DownDecParams {
+    const uint8_t *dp, *ds;
+    int64_t d_sp, d_ss;
+    int H, I, E, K, Is, M;
+    const int32_t *idx;
+    const float *act_f;  // fp32 activations [k][I]
+    const uint16_t *sh_down;
+    const float *ash;
+    float *ys;
+};
+
+constexpr int kDnDecWaves = 4;
+constexpr int kDnMaxTiles = 16;      // tiles per block (LDS sizing)
+constexpr int kDnShPerWave = 4;      // shared rows per wave (at most)
+constexpr int kDnShSl = 3;           // shared slices of 512 prefetched (I_s <= 1536)
+constexpr int kDnStgQ = 8;           // activation elements per thread (I <= 2048)
+constexpr int kDnStgS = 4;           // scale-row staging copies per thread
+
+__host__ __device__ constexpr int dn_dec_lds_bytes(int I)
+{
+    return 4 * (I + kXqPad) + 4 * (I / 32) + 16 * kDnMaxTiles * (I / 32 + kScPad) + 4 * 16 * kDnMaxTiles +
+           4 * 16;
+}
+
+template <bool WIDE>
+__global__ __launch_bounds__(64 * kDnDecWaves) void k_down_dec(DownDecParams p)
+{
+    static_assert(kATerms == 4, "4-term expansion");
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int grp = lane >> 4, col = lane & 15;
+    const int I = p.I, KS = I >> 7, SR = I >> 5, NCH = (KS + 3) >> 2;
+    const int AQS = I + kXqPad, SRP = SR + kScPad;
+    const int T16 = p.H >> 4, M = p.M;
+    const int j = blockIdx.x / M, i = blockIdx.x - j * M;
+    const int t0 = T16 * i / M, t1 = T16 * (i + 1) / M, nt = t1 - t0;
+    const int nblk = p.K * M;
+    const int r0 = (int)((int64_t)p.H * blockIdx.x / nblk), r1 = (int)((int64_t)p.H * (blockIdx.x + 1) / nblk);
+    const int e_raw = p.idx[j];
+    const bool ok = e_raw >= 0 && e_raw < p.E;  // an invalid id: zeros (the combine counts it)
+    const int e = ok ? e_raw : 0;
+
+    extern __shared__ __align__(16) uint8_t lds[];
+    uint8_t *aq_l = lds;                                   // [4][I + pad] activation terms of slot j
+    uint8_t *as_l = aq_l + 4 * AQS;                        // [4][I/32]    their scales
+    uint8_t *sc_l = as_l + 4 * SR;                         // [nt*16][I/32 + pad] the tiles' scale rows
+    float *y_l = reinterpret_cast<float *>(sc_l + 16 * kDnMaxTiles * SRP);  // [nt*16]
+    float *sh_l = y_l + 16 * kDnMaxTiles;                                   // [r1 - r0]
+
+    const uint8_t *ape = p.dp + (int64_t)e * p.d_sp;
+    const uint8_t *ase = p.ds + (int64_t)e * p.d_ss + (size_t)t0 * 16 * SR;
+    const float *afj = p.act_f + (size_t)j * I;
+    const int ntw = (nt - wave + kDnDecWaves - 1) / kDnDecWaves;  // tiles of this wave
+    const int nq = ok ? ntw * NCH : 0;                            // chunks of this wave
+    const uint32_t rowb = (uint32_t)I >> 1;
+    const uint32_t pl = (uint32_t)(lane & 15) * rowb + grp * 16;
+
+    // shared rows of this wave (prefetched) and the shared activation
+    const int nsr = (r1 - r0 - wave + kDnDecWaves - 1) / kDnDecWaves;
+    const int Is = p.Is;
+    u4 shw[kDnShPerWave][kDnShSl];
+    float4 shx[kDnShSl][2];
+    const bool sh_pf = Is > 0 && Is <= 512 * kDnShSl && nsr <= kDnShPerWave;
+    if (sh_pf) {
+#pragma unroll
+        for (int c = 0; c < kDnShSl; ++c) {
+            const int ic = min(c * 512 + lane * 8, Is - 8);
+#pragma unroll
+            for (int q = 0; q < kDnShPerWave; ++q) {
+                const int r = r0 + wave + kDnDecWaves * min(q, max(nsr - 1, 0));
+                shw[q][c] = *reinterpret_cast<const u4 *>(p.sh_down + (size_t)min(r, p.H - 1) * Is + ic);
+            }
+            shx[c][0] = *reinterpret_cast<const float4 *>(p.ash + ic);
+            shx[c][1] = *reinterpret_cast<const float4 *>(p.ash + ic + 4);
+        }
+    }
+
+    struct Chunk {
+        u4 a[4];
+    };
+    auto load = [&](int q, Chunk &bf) {
+        const int tw = q / NCH, c = q - tw * NCH;
+        const uint32_t tile = (uint32_t)(t0 + wave + kDnDecWaves * tw);
+        const uint32_t base = tile * 16u * rowb + pl;
+        static_for<0, 4>([&](auto s_) {
+            constexpr int st = decltype(s_)::value;
+            const uint32_t k = (uint32_t)min(4 * c + st, KS - 1);
+            bf.a[st] = *reinterpret_cast<const u4 *>(ape + (base + k * 64));
+        });
+    };
+
+    // staging loads (the slot's activation, the tiles' scale rows), then the
+    // first 4 weight chunks, then the expansion and the LDS stores
+    Chunk b0, b1, b2, b3;
+    float av[kDnStgQ];
+#pragma unroll
+    for (int q = 0; q < kDnStgQ; ++q) av[q] = afj[min((int)threadIdx.x + q * 64 * kDnDecWaves, I - 1)];
+    if constexpr (WIDE) {  // SR % 16 == 0
+        const int nrow = SR >> 4, nsc = nt * 16 * nrow;
+        u4 ts[kDnStgS];
+#pragma unroll
+        for (int q = 0; q < kDnStgS; ++q) {
+            const int ii = min((int)threadIdx.x + q * 64 * kDnDecWaves, nsc - 1);
+            ts[q] = *reinterpret_cast<const u4 *>(ase + 16 * ii);  // the tiles' rows are contiguous
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (nq > 0) {
+            load(0, b0);
+            load(min(1, nq - 1), b1);
+            load(min(2, nq - 1), b2);
+            load(min(3, nq - 1), b3);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < kDnStgS; ++q) {
+            const int ii = (int)threadIdx.x + q * 64 * kDnDecWaves;
+            if (ii < nsc) {
+                const int row = ii / nrow, o = ii - row * nrow;
+                *reinterpret_cast<u4 *>(sc_l + row * SRP + 16 * o) = ts[q];
+            }
+        }
+    } else {  // short rows (small layers): byte copies
+        for (int ii = threadIdx.x; ii < nt * 16 * SR; ii += blockDim.x) {
+            const int row = ii / SR, o = ii - row * SR;
+            sc_l[row * SRP + o] = ase[ii];
+        }
+        if (nq > 0) {
+            load(0, b0);
+            load(min(1, nq - 1), b1);
+            load(min(2, nq - 1), b2);
+            load(min(3, nq - 1), b3);
+        }
+    }
+    // activation -> 4 e4m3 terms; element i = tid + 256q, so each half-wave
+    // holds one 32-element block (I is a multiple of 128: whole half-waves)
+#pragma unroll
+    for (int q = 0; q < kDnStgQ; ++q) {
+        const int ii = (int)threadIdx.x + q * 64 * kDnDecWaves;
+        if (q * 64 * kDnDecWaves < I && ii < I) {
+            int code[kATerms], sbt[kATerms];
+            split_e4m3_32<kATerms>(av[q], code, sbt);
+#pragma unroll
+            for (int k = 0; k < kATerms; ++k) {
+                aq_l[k * AQS + ii] = (uint8_t)code[k];
+                if ((ii & 31) == 0) as_l[k * SR + (ii >> 5)] = (uint8_t)sbt[k];
+            }
+        }
+    }
+    __syncthreads();
+
+    const int term = col & 3;  // columns 4..15: copies of columns 0..3, ignored
+    const uint8_t *bb = aq_l + term * AQS + grp * 16;
+    const uint8_t *bsr = as_l + term * SR;
+    v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    // chunk q: tile t0 + wave + 4*(q / NCH), steps 4*(q % NCH)..+3; a tile's
+    // result is parked in LDS when its last chunk is done (no global stores
+    // inside the loop, so the weight loads' wait counts stay exact)
+    auto compute = [&](int q, const Chunk &bf) {
+        if (q >= nq) return;
+        const int tw = q / NCH, c = q - tw * NCH;
+        const int trow = (wave + kDnDecWaves * tw) * 16;  // first row of the tile, block-relative
+        const uint8_t *sr = sc_l + (trow + (lane & 15)) * SRP;
+        uint32_t sa, sb;
+        if constexpr (WIDE) {
+            sa = gather_scales(*reinterpret_cast<const u4 *>(sr + 16 * c), grp);
+            sb = gather_scales(*reinterpret_cast<const u4 *>(bsr + 16 * c), grp);
+        } else {  // short rows: steps past K left at 127 (never multiplied)
+            sa = sb = 0x7f7f7f7fu;
+            for (int st = 0; st < 4 && 4 * c + st < KS; ++st) {
+                const int o = (4 * c + st) * 4 + grp, sh8 = 8 * st;
+                const uint32_t m = ~(0xffu << sh8);
+                sa = (sa & m) | ((uint32_t)sr[o] << sh8);
+                sb = (sb & m) | ((uint32_t)bsr[o] << sh8);
+            }
+        }
+        const uint32_t drop = ff_bytes(sa);  // scale byte 255: the group drops out
+        sa ^= drop;
+        static_for<0, 4>([&](auto s_) {
+            constexpr int st = decltype(s_)::value;
+            if (4 * c + st < KS) {
+                const uint32_t k = 4 * c + st;
+                const v8i B = b_operand(*reinterpret_cast<const u4 *>(bb + k * 128),
+                                        *reinterpret_cast<const u4 *>(bb + k * 128 + 64));
+                const u4 av = ((drop >> (8 * st + 7)) & 1u) ? u4{0u, 0u, 0u, 0u} : bf.a[st];
+                acc = mfma_fp4_fp8_sel<st>(a_operand(av), B, acc, (int)sa, (int)sb);
+            }
+        });
+        if (c == NCH - 1) {
+            float y[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                y[r] = acc[r] + __shfl_xor(acc[r], 1);
+                y[r] += __shfl_xor(y[r], 2);
+            }
+            if (col == 0)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) y_l[trow + 4 * grp + r] = y[r];
+            acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    };
+    for (int q = 0; q < nq; q += 4) {
+        compute(q, b0);
+        load(min(q + 4, nq - 1), b0);
+        compute(q + 1, b1);
+        load(min(q + 5, nq - 1), b1);
+        compute(q + 2, b2);
+        load(min(q + 6, nq - 1), b2);
+        compute(q + 3, b3);
+        load(min(q + 7, nq - 1), b3);
+    }
+
+    // shared rows r0 + wave + 4q
+    if (Is > 0) {
+        auto dot8 = [&](float &a, const u4 &w4, const float4 &x0, const float4 &x1) {
+            float v = a;
+            v = fmaf(bf16f(w4[0] & 0xffffu), x0.x, v);
+            v = fmaf(bf16f(w4[0] >> 16), x0.y, v);
+            v = fmaf(bf16f(w4[1] & 0xffffu), x0.z, v);
+            v = fmaf(bf16f(w4[1] >> 16), x0.w, v);
+            v = fmaf(bf16f(w4[2] & 0xffffu), x1.x, v);
+            v = fmaf(bf16f(w4[2] >> 16), x1.y, v);
+            v = fmaf(bf16f(w4[3] & 0xffffu), x1.z, v);
+            v = fmaf(bf16f(w4[3] >> 16), x1.w, v);
+            a = v;
+        };
+        if (sh_pf) {
+            float a4[kDnShPerWave];
+#pragma unroll
+            for (int q = 0; q < kDnShPerWave; ++q) a4[q] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < kDnShSl; ++c)
+                if (c * 512 + lane * 8 < Is)
+#pragma unroll
+                    for (int q = 0; q < kDnShPerWave; ++q) dot8(a4[q], shw[q][c], shx[c][0], shx[c][1]);
+#pragma unroll
+            for (int q = 0; q < kDnShPerWave; ++q) {
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) a4[q] += __shfl_xor(a4[q], o);
+                if (lane == 0 && q < nsr) sh_l[wave + kDnDecWaves * q] = a4[q];
+            }
+        } else {
+            for (int q = 0; q < nsr; ++q) {
+                const int r = r0 + wave + kDnDecWaves * q;
+                float a = 0.0f;
+                for (int ii = lane * 8; ii < Is; ii += 512) {
+                    const float4 x0 = *reinterpret_cast<const float4 *>(p.ash + ii);
+                    const float4 x1 = *reinterpret_cast<const float4 *>(p.ash + ii + 4);
+                    dot8(a, *reinterpret_cast<const u4 *>(p.sh_down + (size_t)r * Is + ii), x0, x1);
+                }
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o);
+                if (lane == 0) sh_l[wave + kDnDecWaves * q] = a;
+            }
+        }
+    }
+    __syncthreads();
+    for (int ii = threadIdx.x; ii < nt * 16; ii += blockDim.x)
+        p.ys[(size_t)j * p.H + (size_t)t0 * 16 + ii] = ok ? y_l[ii] : 0.0f;
+    if (Is > 0)
+        for (int ii = threadIdx.x; ii < r1 - r0; ii += blockDim.x) p.ys[(size_t)p.K * p.H + r0 + ii] = sh_l[ii];
+}
+
+// Router-order combine: out[t][o] = sum_j w[t][j] * ys[t][j][o] (j = 0..k-1
+// in order, one fma each), then + ys[t][k][o] (the shared expert, if any).
+// Slots with an out-of-range id hold 0 and are counted once here.
+__global__ __launch_bounds__(256) void k_combine(const float *__restrict__ ys, const float *__restrict__ w,
+                                                 const int32_t *__restrict__ idx, int T, int K, int H,
+                                                 int E, int shared, float *__restrict__ out,
+                                                 unsigned long long *errors)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < (int64_t)T * H) {
+        const int64_t t = i / H;
+        const int o = (int)(i - t * H);
+        const float *y = ys + (size_t)t * (K + 1) * H + o;
+        const float *wt = w + (size_t)t * K;
+        float acc = 0.0f;
+        int j = 0;
+        for (; j + 8 <= K; j += 8) {  // 8 loads in flight, then 8 fmas in order
+            float v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = y[(size_t)(j + q) * H];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc = fmaf(wt[j + q], v[q], acc);
+        }
+        for (; j < K; ++j) acc = fmaf(wt[j], y[(size_t)j * H], acc);
+        if (shared) acc += y[(size_t)K * H];
+        out[i] = acc;
+    }
+    if (blockIdx.x == 0 && threadIdx.x < 64)
+        for (int64_t a = threadIdx.x; a < (int64_t)T * K; a += 64)
+            if (idx[a] < 0 || idx[a] >= E) atomicAdd(errors, 1ull);
+}
+
 }  // namespace
 
 template <int NQ>
@@ -946,6 +1528,111 @@ hipError_t launch_route(const LayerView &L, const uint16_t *x, int T, int32_t *i
     return hipGetLastError();
 }
 
+// Sizes the single-token kernels take (one pass of LDS staging copies per
+// thread; row tiles dividing I and H; a down block's tiles fit its LDS).
+static int down_blocks_per_slot(const LayerView &L, int ncu)
+{
+    const int T16 = L.H / 16;
+    int M = std::max(1, (2 * ncu + L.K - 1) / L.K);
+    M = std::min(M, T16);
+    while ((T16 + M - 1) / M > kDnMaxTiles) ++M;  // tiles per block fit the LDS staging
+    return M;
+}
+
+static bool decode_path_ok(const LayerView &L)
+{
+    const bool gu = L.H % 512 != 0 || L.H / 4 <= 64 * kGuDecWaves * kGuStgQ;
+    const bool gu_sc = L.H % 512 != 0 || kGuDecUnits * 2 * kGuUnitRows * (L.H / 512) <= 64 * kGuDecWaves * kGuStgS;
+    const bool dn = L.I % 512 != 0 || (L.I / 4 <= 64 * kDnDecWaves * kDnStgQ &&
+                                       kDnMaxTiles * 16 * (L.I / 512) <= 64 * kDnDecWaves * kDnStgS);
+    return gu && gu_sc && dn && L.I % kGuUnitRows == 0 && L.H % 16 == 0 && L.H >= 16 * kDnDecWaves;
+}
+
+// T = 1: token fp8 expansion, gate/up, down, router-order combine. The
+// router slots are the assignment list (no permutation).
+static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const int32_t *idx,
+                                    const float *w, float *out, uint8_t *xq, uint8_t *xs, uint8_t *aq,
+                                    float *ash, char *ys_base, hipStream_t s, Profiler *prof)
+{
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    {
+        StageMark m(prof, K3MOE_STAGE_XSPLIT, s);
+        k_xsplit<<<(unsigned)((L.H + 255) / 256), 256, 0, s>>>(x, L.H, L.H, xq, xs);
+    }
+    GateUpParams gp{};
+    gp.gp = L.gp;
+    gp.gs = L.gs;
+    gp.up = L.up;
+    gp.us = L.us;
+    gp.g_sp = L.g_sp;
+    gp.g_ss = L.g_ss;
+    gp.u_sp = L.u_sp;
+    gp.u_ss = L.u_ss;
+    gp.H = L.H;
+    gp.I = L.I;
+    gp.K = L.K;
+    gp.E = L.E;
+    gp.act = L.act;
+    gp.T = 1;
+    gp.Is = L.Is;
+    gp.b1 = L.b1;
+    gp.b2 = L.b2;
+    gp.x = x;
+    gp.xq = xq;
+    gp.xs = xs;
+    gp.idx = idx;
+    // the fp32 activations [k][I] take the place of the e4m3 terms [k][4][I]
+    // (same size: 4 terms of 1 byte vs one 4-byte float per element)
+    static_assert(kATerms == sizeof(float), "activation buffer reuse");
+    gp.act_f = reinterpret_cast<float *>(aq);
+    gp.sh_gate = L.sh_gate;
+    gp.sh_up = L.sh_up;
+    gp.ash = ash;
+    {
+        StageMark m(prof, K3MOE_STAGE_GATEUP, s);
+        const int nunits = L.K * (L.I / kGuUnitRows);
+        const unsigned nblk = (unsigned)((nunits + kGuDecUnits - 1) / kGuDecUnits);
+        const size_t lds = gu_dec_lds_bytes(L.H);
+        if (L.H % 512 == 0)
+            k_gateup_dec<true><<<nblk, 64 * kGuDecWaves, lds, s>>>(gp);
+        else
+            k_gateup_dec<false><<<nblk, 64 * kGuDecWaves, lds, s>>>(gp);
+    }
+    float *ys = reinterpret_cast<float *>(ys_base);
+    DownDecParams dp{};
+    dp.dp = L.dp;
+    dp.ds = L.ds;
+    dp.d_sp = L.d_sp;
+    dp.d_ss = L.d_ss;
+    dp.H = L.H;
+    dp.I = L.I;
+    dp.E = L.E;
+    dp.K = L.K;
+    dp.Is = L.Is;
+    dp.M = down_blocks_per_slot(L, ncu);
+    dp.idx = idx;
+    dp.act_f = gp.act_f;
+    dp.sh_down = L.sh_down;
+    dp.ash = ash;
+    dp.ys = ys;
+    {
+        StageMark m(prof, K3MOE_STAGE_DOWN, s);
+        const unsigned nblk = (unsigned)(L.K * dp.M);
+        const size_t lds = dn_dec_lds_bytes(L.I) + 4 * (L.H / nblk + 1);
+        if (L.I % 512 == 0)
+            k_down_dec<true><<<nblk, 64 * kDnDecWaves, lds, s>>>(dp);
+        else
+            k_down_dec<false><<<nblk, 64 * kDnDecWaves, lds, s>>>(dp);
+    }
+    {
+        StageMark m(prof, K3MOE_STAGE_COMBINE, s);
+        k_combine<<<(unsigned)((L.H + 255) / 256), 256, 0, s>>>(ys, w, idx, 1, L.K, L.H, L.E, L.Is > 0, out,
+                                                               L.errors);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const int32_t *idx,
                           const float *w, float *out, char *ws, const WsLayout &lay, hipStream_t s,
                           Profiler *prof)
@@ -964,6 +1651,8 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const in
     const int64_t n = (int64_t)T * L.H;
     const unsigned slabs = (unsigned)((n + 255) / 256);
     const int nchunks = (T + kPermChunk - 1) / kPermChunk;
+    if (T == 1 && decode_path_ok(L))
+        return launch_forward_t1(L, x, idx, w, out, xq, xs, aq, ash, ws + lay.ys, s, prof);
     if (nchunks == 1) {
         StageMark m(prof, K3MOE_STAGE_PERM, s);
         k_prep_small<<<1 + slabs, 256, 0, s>>>(x, n, L.H, xq, xs, idx, T, L.K, L.E, active_n, active_e,
@@ -991,6 +1680,8 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const in
     gp.H = L.H;
     gp.I = L.I;
     gp.K = L.K;
+    gp.E = L.E;
+    gp.idx = idx;
     gp.act = L.act;
     gp.T = T;
     gp.Is = L.Is;
