@@ -83,7 +83,7 @@ typedef struct {
 /* One MXFP4 matrix per expert, E of them. Expert e's packed nibbles start
  * at packed + e * expert_stride_packed and are [rows][cols/2] bytes; its
  * scales start at scales + e * expert_stride_scales and are [rows][cols/32]
- * bytes. packed and expert_stride_packed must be multiples of 16; strides
+ * bytes. packed, scales and both strides must be multiples of 16; strides
  * must be at least the matrix size. */
 typedef struct {
     const uint8_t *packed;

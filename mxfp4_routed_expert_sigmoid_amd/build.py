@@ -7,7 +7,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libk3moe.so")
-SOURCES = [os.path.join(CSRC, "k3moe_api.cpp"), os.path.join(CSRC, "k3moe_kernels.hip")]
+SOURCES = [os.path.join(CSRC, "k3moe_api.cpp"), os.path.join(CSRC, "k3moe_kernels.hip"),
+           os.path.join(CSRC, "k3moe_grouped.hip")]
 HEADERS = [os.path.join(CSRC, "k3moe_internal.h"), os.path.join(ROOT, "include", "k3moe.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

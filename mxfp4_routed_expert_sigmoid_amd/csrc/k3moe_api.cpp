@@ -33,17 +33,20 @@ WsLayout ws_layout(const k3moe_config &c, int64_t T)
     };
     L.sc = take(sizeof(float) * T * E);
     L.ch = take(sizeof(float) * T * E);
-    L.xq = take((size_t)T * kXTerms * H);
-    L.xs = take((size_t)T * kXTerms * (H / 32));
+    const int64_t T1 = std::min<int64_t>(T, 1);  // the fp8 token terms serve T = 1 only
+    L.xq = take((size_t)T1 * kXTerms * H);
+    L.xs = take((size_t)T1 * kXTerms * (H / 32));
     L.chunk_cnt = take(sizeof(int32_t) * nchunks * E);
     L.active_n = take(sizeof(int32_t));
     L.active_e = take(sizeof(int32_t) * E);
     L.active_off = take(sizeof(int32_t) * (E + 1));
     L.sorted = take(sizeof(int32_t) * std::max<int64_t>(1, T * K));
-    L.aq = take((size_t)T * K * kATerms * I);
-    L.as = take((size_t)T * K * kATerms * (I / 32));
+    L.act = take((size_t)T * K * 4 * I);
     L.ash = take(sizeof(float) * T * std::max<int64_t>(Is, 1));
     L.ys = take(sizeof(float) * T * (K + 1) * H);
+    L.tiles_gu = take(sizeof(int2) * grouped_tile_cap_gu(T, (int)K, (int)E));
+    L.tiles_dn = take(sizeof(int2) * grouped_tile_cap_dn(T, (int)K, (int)E));
+    L.tile_n = take(2 * sizeof(int32_t));
     L.total = o;
     return L;
 }
@@ -78,6 +81,7 @@ static k3moe_status check_mxfp4(const k3moe_mxfp4 &m, int64_t rows, int64_t cols
     if (E > 1 && (m.expert_stride_packed < pbytes || m.expert_stride_scales < sbytes))
         return K3MOE_E_INVALID_ARG;
     if (!aligned(m.packed, 16) || m.expert_stride_packed % 16) return K3MOE_E_ALIGNMENT;
+    if (!aligned(m.scales, 16) || m.expert_stride_scales % 16) return K3MOE_E_ALIGNMENT;
     return K3MOE_OK;
 }
 

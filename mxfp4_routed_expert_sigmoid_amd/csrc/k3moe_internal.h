@@ -25,15 +25,18 @@ constexpr int kPermChunk = 16;
 // Byte offsets of the workspace regions for T tokens (all 256-aligned).
 struct WsLayout {
     size_t sc, ch;            // router scores, fp32 [T][E] each
-    size_t xq, xs;            // token fp8 terms [T][3][H], scales [T][3][H/32]
+    size_t xq, xs;            // single token's fp8 terms [4][H], scales [4][H/32]
     size_t chunk_cnt;         // int32 [nchunks][E]
     size_t active_n;          // int32 [1]
     size_t active_e;          // int32 [E]
     size_t active_off;        // int32 [E + 1]
     size_t sorted;            // int32 [T * k]
-    size_t aq, as;            // activation fp8 terms [T*k][4][I], scales [T*k][4][I/32]
-    size_t ash;               // shared activation fp32 [T][I_s]
+    size_t act;               // routed activations, 4 bytes per element [T*k][I]:
+                              //   fp32 (one token), or bf16 hi then bf16 lo planes
+    size_t ash;               // shared activations, 4 bytes per element [T][I_s], same forms
     size_t ys;                // expert outputs fp32 [T][k + 1][H] (slot k: shared expert)
+    size_t tiles_gu, tiles_dn;  // grouped-GEMM tile lists, int2 each
+    size_t tile_n;            // int32 [2]: tile counts
     size_t total;
 };
 
@@ -104,5 +107,14 @@ hipError_t launch_route(const LayerView &L, const uint16_t *x, int T, int32_t *i
 hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T,
                           const int32_t *idx, const float *w, float *out, char *ws,
                           const WsLayout &lay, hipStream_t s, Profiler *prof);
+
+// Grouped GEMMs for batches (k3moe_grouped.hip).
+size_t grouped_tile_cap_gu(int64_t T, int K, int E);
+size_t grouped_tile_cap_dn(int64_t T, int K, int E);
+hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const int32_t *active_n,
+                          const int32_t *active_e, const int32_t *active_off, const int32_t *sorted,
+                          uint16_t *act_hi, uint16_t *act_lo, uint16_t *ash_hi, uint16_t *ash_lo,
+                          int2 *tiles_gu, int2 *tiles_dn, int32_t *tile_n, float *ys, hipStream_t s,
+                          Profiler *prof);
 
 }  // namespace k3moe

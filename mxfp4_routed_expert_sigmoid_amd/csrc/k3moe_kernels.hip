@@ -402,18 +402,12 @@ __device__ __forceinline__ void xsplit_slab(const uint16_t *__restrict__ x, int6
     }
 }
 
-// Small batches (T <= kPermChunk): block 0 builds the permutation, the other
-// blocks expand the tokens to fp8 terms.
-__global__ __launch_bounds__(256) void k_prep_small(const uint16_t *__restrict__ x, int64_t n, int H,
-                                                    uint8_t *__restrict__ xq, uint8_t *__restrict__ xs,
-                                                    const int32_t *__restrict__ idx, int T, int K,
-                                                    int E, int32_t *active_n, int32_t *active_e,
+// Small batches (T <= kPermChunk): the whole permutation in one block.
+__global__ __launch_bounds__(256) void k_perm_small(const int32_t *__restrict__ idx, int T, int K, int E,
+                                                    int32_t *active_n, int32_t *active_e,
                                                     int32_t *active_off, int32_t *sorted)
 {
-    if (blockIdx.x == 0)
-        perm_single(idx, T, K, E, active_n, active_e, active_off, sorted);
-    else
-        xsplit_slab(x, n, H, blockIdx.x - 1, xq, xs);
+    perm_single(idx, T, K, E, active_n, active_e, active_off, sorted);
 }
 
 // Multi-chunk permutation, phase 1: per-chunk expert counts.
@@ -477,446 +471,19 @@ __global__ __launch_bounds__(64) void k_perm_scatter(const int32_t *__restrict__
 }
 
 // ---------------------------------------------------------------------------
-// Gate/up projections + activation (README §9, k3_moe step 3 first half and
-// step 6 first half), one launch for the routed and the shared expert.
-//
-// Routed part: one workgroup per (active expert, 32-row tile of I); its 4
-// waves split the K steps (128 elements each) round-robin and meet in LDS.
-// Per K step a wave loads 4 A fragments (gate/up x two 16-row halves, 16 B
-// per lane straight from HBM) and one B fragment carrying up to 4 tokens x 4
-// terms, and issues 4 MFMAs; loads run D steps ahead of the MFMAs. The
-// epilogue adds the term columns, applies the activation, and writes the
-// activation as 4 e4m3 terms (with E8M0 scales) for the down projection.
-//
-// Shared part (blocks after the routed ones): one wave per shared row, bf16
-// weights, fp32 accumulation, tokens in groups of kShTok.
+// Parameters of the single-token gate/up kernel (below).
 struct GateUpParams {
     const uint8_t *gp, *gs, *up, *us;
     int64_t g_sp, g_ss, u_sp, u_ss;
-    int H, I, K, E, act, T, Is, routed_blocks, shared_blocks;
+    int H, I, K, E, act, Is;
     float b1, b2;
     const uint16_t *x;
     const uint8_t *xq, *xs;
     const int32_t *idx;
-    const int32_t *active_n, *active_e, *active_off, *sorted;
-    uint8_t *aq, *as;
-    float *act_f;  // T = 1 path: fp32 activations [k][I]
+    float *act_f;  // fp32 activations [k][I]
     const uint16_t *sh_gate, *sh_up;
     float *ash;
 };
-
-#ifndef K3MOE_SH_TOK
-#define K3MOE_SH_TOK 2
-#endif
-#ifndef K3MOE_GU_DEPTH
-#define K3MOE_GU_DEPTH 2
-#endif
-#ifndef K3MOE_DN_DEPTH
-#define K3MOE_DN_DEPTH 6
-#endif
-constexpr int kShTok = K3MOE_SH_TOK;  // shared gate/up tokens per pass
-
-__device__ void shared_gateup_rows(const GateUpParams &p, int blk)
-{
-    const int lane = threadIdx.x & 63;
-    const int r = blk * 4 + (threadIdx.x >> 6);
-    if (r >= p.Is) return;
-    const int H = p.H;
-    const uint16_t *g = p.sh_gate + (size_t)r * H;
-    const uint16_t *u = p.sh_up + (size_t)r * H;
-    constexpr int CH = 4;  // 512-element slices whose loads are issued together
-    for (int t0 = 0; t0 < p.T; t0 += kShTok) {
-        const int nt = min(kShTok, p.T - t0);
-        float ga[kShTok], ua[kShTok];
-#pragma unroll
-        for (int k = 0; k < kShTok; ++k) ga[k] = ua[k] = 0.0f;
-        for (int i0 = lane * 8; i0 < H; i0 += 512 * CH) {
-            u4 gv[CH], uv[CH];
-#pragma unroll
-            for (int c = 0; c < CH; ++c) {
-                const int i = i0 + 512 * c;
-                gv[c] = i < H ? *reinterpret_cast<const u4 *>(g + i) : u4{0u, 0u, 0u, 0u};
-                uv[c] = i < H ? *reinterpret_cast<const u4 *>(u + i) : u4{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int k = 0; k < kShTok; ++k) {
-                if (k >= nt) break;
-                u4 xv[CH];
-#pragma unroll
-                for (int c = 0; c < CH; ++c) {
-                    const int i = i0 + 512 * c;
-                    xv[c] = i < H ? *reinterpret_cast<const u4 *>(p.x + (size_t)(t0 + k) * H + i)
-                                  : u4{0u, 0u, 0u, 0u};
-                }
-#pragma unroll
-                for (int c = 0; c < CH; ++c)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float x0 = bf16f(xv[c][q] & 0xffffu), x1 = bf16f(xv[c][q] >> 16);
-                        ga[k] = fmaf(bf16f(gv[c][q] & 0xffffu), x0, ga[k]);
-                        ga[k] = fmaf(bf16f(gv[c][q] >> 16), x1, ga[k]);
-                        ua[k] = fmaf(bf16f(uv[c][q] & 0xffffu), x0, ua[k]);
-                        ua[k] = fmaf(bf16f(uv[c][q] >> 16), x1, ua[k]);
-                    }
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < kShTok; ++k) {
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                ga[k] += __shfl_xor(ga[k], o);
-                ua[k] += __shfl_xor(ua[k], o);
-            }
-        }
-        if (lane == 0)
-            for (int k = 0; k < nt; ++k) p.ash[(size_t)(t0 + k) * p.Is + r] = act_fn(ga[k], ua[k], p.act, p.b1, p.b2);
-    }
-}
-
-#ifndef K3MOE_GU_MIN_WAVES
-#define K3MOE_GU_MIN_WAVES 2
-#endif
-#ifndef K3MOE_MIN_WAVES
-#define K3MOE_MIN_WAVES 4
-#endif
-
-template <bool WIDE>
-__global__ __launch_bounds__(256, K3MOE_GU_MIN_WAVES) void k_gateup(GateUpParams p)
-{
-    // shared-expert blocks are spread evenly through the grid (one every
-    // `stride` blocks) so they run alongside the routed blocks, not after them
-    int bid = blockIdx.x;
-    if (p.shared_blocks > 0) {
-        const int stride = (p.routed_blocks + p.shared_blocks) / p.shared_blocks;
-        const int k = bid / stride;
-        if (bid % stride == stride - 1 && k < p.shared_blocks) {
-            shared_gateup_rows(p, k);
-            return;
-        }
-        bid -= min(p.shared_blocks, (bid + 1) / stride);
-    }
-    const int RT = p.I >> 5;
-    const int slot = bid / RT;
-    const int rt = bid - slot * RT;
-    if (slot >= *p.active_n) return;
-    const int e = p.active_e[slot];
-    const int a0 = p.active_off[slot], a1 = p.active_off[slot + 1];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int rl = lane & 15, grp = lane >> 4;
-    const int H = p.H, KS = H >> 7, SR = H >> 5;
-    constexpr bool wide = WIDE;  // H % 512 == 0: 16-byte aligned scale chunks
-
-    // wave-uniform expert bases; per-lane 32-bit offsets (row, K-block group)
-    const uint8_t *gpe = p.gp + e * p.g_sp, *upe = p.up + e * p.u_sp;
-    const uint8_t *gse = p.gs + e * p.g_ss, *use = p.us + e * p.u_ss;
-    const uint32_t rowb = (uint32_t)H >> 1;
-    const uint32_t r0 = (uint32_t)rt * 32 + rl;
-    const uint32_t po0 = r0 * rowb + grp * 16, po1 = po0 + 16 * rowb;  // packed, rows r0 / r0+16
-    const uint32_t sr0 = r0 * SR, sr1 = sr0 + 16 * SR;                 // scale rows
-
-    __shared__ float red[4][4][4][64];  // [wave][tile][reg][lane]
-
-    // K is walked in chunks of 4 steps (512 elements); wave w takes a
-    // contiguous range of chunks. One 16-byte load per tile and chunk brings
-    // the lane's scale bytes of all 4 steps (selected per step by op_sel).
-    const int NCH = (KS + 3) >> 2;
-    const int per = (NCH + 3) >> 2;
-    const int c0 = min(NCH, wave * per), c1 = min(NCH, c0 + per);
-    constexpr int kTok = 16 / kXTerms;  // tokens per B fragment
-    const int col = lane & 15, term = col % kXTerms;
-
-    struct Batch {
-        u4 a[4][4];  // [step][tile]
-        u4 lo[4], hi[4];
-        uint32_t sa[4], sb;
-    };
-    auto load_a = [&](int c, Batch &B) {
-        static_for<0, 4>([&](auto s_) {
-            constexpr int st = decltype(s_)::value;
-            if (4 * c + st < KS) {
-                const uint32_t o = (uint32_t)(4 * c + st) * 64;
-                B.a[st][0] = *reinterpret_cast<const u4 *>(gpe + (po0 + o));
-                B.a[st][1] = *reinterpret_cast<const u4 *>(gpe + (po1 + o));
-                B.a[st][2] = *reinterpret_cast<const u4 *>(upe + (po0 + o));
-                B.a[st][3] = *reinterpret_cast<const u4 *>(upe + (po1 + o));
-            }
-        });
-        if constexpr (wide) {
-            B.sa[0] = gather_scales(*reinterpret_cast<const u4 *>(gse + sr0 + 16 * c), grp);
-            B.sa[1] = gather_scales(*reinterpret_cast<const u4 *>(gse + sr1 + 16 * c), grp);
-            B.sa[2] = gather_scales(*reinterpret_cast<const u4 *>(use + sr0 + 16 * c), grp);
-            B.sa[3] = gather_scales(*reinterpret_cast<const u4 *>(use + sr1 + 16 * c), grp);
-        } else {  // short rows: byte loads, steps past K left at 127
-#pragma unroll
-            for (int q = 0; q < 4; ++q) B.sa[q] = 0x7f7f7f7fu;
-            for (int st = 0; st < 4 && 4 * c + st < KS; ++st) {
-                const uint32_t so = (4 * c + st) * 4 + grp, sh8 = 8 * st, m = ~(0xffu << sh8);
-                B.sa[0] = (B.sa[0] & m) | ((uint32_t)gse[sr0 + so] << sh8);
-                B.sa[1] = (B.sa[1] & m) | ((uint32_t)gse[sr1 + so] << sh8);
-                B.sa[2] = (B.sa[2] & m) | ((uint32_t)use[sr0 + so] << sh8);
-                B.sa[3] = (B.sa[3] & m) | ((uint32_t)use[sr1 + so] << sh8);
-            }
-        }
-    };
-    auto load_b = [&](int c, Batch &B, const uint8_t *xb, const uint8_t *xsr) {
-        static_for<0, 4>([&](auto s_) {
-            constexpr int st = decltype(s_)::value;
-            if (4 * c + st < KS) {
-                const uint32_t o = (uint32_t)(4 * c + st) * 128;
-                B.lo[st] = *reinterpret_cast<const u4 *>(xb + o);
-                B.hi[st] = *reinterpret_cast<const u4 *>(xb + o + 64);
-            }
-        });
-        if constexpr (wide) {
-            B.sb = gather_scales(*reinterpret_cast<const u4 *>(xsr + 16 * c), grp);
-        } else {
-            B.sb = 0x7f7f7f7fu;
-            for (int st = 0; st < 4 && 4 * c + st < KS; ++st) {
-                const uint32_t sh8 = 8 * st;
-                B.sb = (B.sb & ~(0xffu << sh8)) | ((uint32_t)xsr[(4 * c + st) * 4 + grp] << sh8);
-            }
-        }
-    };
-
-    for (int g0 = a0; g0 < a1; g0 += kTok) {
-        const int ntok = min(kTok, a1 - g0);
-        // B column (token slot, term); slots past ntok read slot 0's data into
-        // columns the epilogue ignores (duplicate addresses coalesce)
-        const int slot_tok = col / kXTerms < ntok ? col / kXTerms : 0;
-        const int64_t tok = p.sorted[g0 + slot_tok] / p.K;
-        const uint8_t *xb = p.xq + (tok * kXTerms + term) * H + grp * 16;
-        const uint8_t *xsr = p.xs + (tok * kXTerms + term) * SR;
-        v4f acc[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-        for (int c = c0; c < c1; ++c) {
-            Batch bt;
-            load_a(c, bt);
-            load_b(c, bt, xb, xsr);
-            uint32_t drop[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {  // scale byte 255: the 32-group drops out
-                drop[q] = ff_bytes(bt.sa[q]);
-                bt.sa[q] ^= drop[q];
-            }
-            static_for<0, 4>([&](auto s_) {
-                constexpr int st = decltype(s_)::value;
-                if (4 * c + st < KS) {
-                    const v8i B = b_operand(bt.lo[st], bt.hi[st]);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const u4 av = ((drop[q] >> (8 * st + 7)) & 1u) ? u4{0u, 0u, 0u, 0u} : bt.a[st][q];
-                        acc[q] = mfma_fp4_fp8_sel<st>(a_operand(av), B, acc[q], (int)bt.sa[q], (int)bt.sb);
-                    }
-                }
-            });
-        }
-
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) red[wave][q][r][lane] = acc[q][r];
-        __syncthreads();
-        {
-            const int q = threadIdx.x >> 6;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                red[0][q][r][lane] = ((red[0][q][r][lane] + red[1][q][r][lane]) + red[2][q][r][lane]) +
-                                     red[3][q][r][lane];
-        }
-        __syncthreads();
-        if (threadIdx.x < 32 * kTok) {
-            const int ts = threadIdx.x >> 5, r = threadIdx.x & 31;
-            if (ts < ntok) {  // uniform over each half-wave
-                const int h = r >> 4, rho = r & 15;
-                const int ln = 16 * (rho >> 2) + kXTerms * ts, rg = rho & 3;
-                float g = 0.0f, u = 0.0f;
-#pragma unroll
-                for (int k = 0; k < kXTerms; ++k) {
-                    g += red[0][h][rg][ln + k];
-                    u += red[0][2 + h][rg][ln + k];
-                }
-                const float a = act_fn(g, u, p.act, p.b1, p.b2);
-                int code[kATerms], sbt[kATerms];
-                split_e4m3_32<kATerms>(a, code, sbt);
-                const int64_t asg = p.sorted[g0 + ts];
-#pragma unroll
-                for (int k = 0; k < kATerms; ++k) {
-                    p.aq[(asg * kATerms + k) * p.I + rt * 32 + r] = (uint8_t)code[k];
-                    if (r == 0) p.as[(asg * kATerms + k) * (p.I >> 5) + rt] = (uint8_t)sbt[k];
-                }
-            }
-        }
-        __syncthreads();  // red is reused by the next token group
-    }
-}
-
-// Down projection + router-order combine + shared expert (README §9, k3_moe
-// step 3 second half and step 6). One workgroup of 8 waves per (16-row tile
-// of H, token); wave w runs the experts j = w, w+8, ... K is walked in
-// chunks of 4 steps: per lane one 16-byte load brings the W2 scale bytes of
-// the chunk (and one the activation-term scales), gathered into a word whose
-// byte the MFMA selects with op_sel. All loads of a chunk are issued before
-// its MFMAs. Each expert's 16 outputs land in LDS; then every wave computes 2
-// rows of the shared expert (bf16 weights, activation staged in LDS), and 16
-// threads sum w_j * y_j in j order and add the shared rows. An expert id
-// outside [0, E) contributes zero (no load, no MFMA) and is counted.
-struct DownParams {
-    const uint8_t *dp, *ds;
-    int64_t d_sp, d_ss;
-    int H, I, E, K, Is;
-    const int32_t *idx;
-    const float *w;
-    const uint8_t *aq, *as;
-    const uint16_t *sh_down;
-    const float *ash;
-    float *out;
-    unsigned long long *errors;
-};
-
-constexpr int kDnWaves = 8;
-
-__host__ __device__ constexpr int dn_lds_bytes(int Is) { return 4 * Is; }
-
-template <bool WIDE>
-__global__ __launch_bounds__(64 * kDnWaves, K3MOE_MIN_WAVES) void k_down(DownParams p)
-{
-    const int rt = blockIdx.x, t = blockIdx.y;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int rl = lane & 15, grp = lane >> 4;
-    const int I = p.I, KS = I >> 7, SR = I >> 5;
-    constexpr bool wide = WIDE;  // I % 512 == 0: 16-byte aligned scale chunks
-    const int Is = p.Is;
-    const int32_t *idxr = p.idx + (size_t)t * p.K;
-    __shared__ float ys[kMaxTopk][16];
-    __shared__ float sh[16];
-    extern __shared__ float ash_l[];  // [Is]
-
-    if (rt == 0 && lane == 0)
-        for (int j = wave; j < p.K; j += kDnWaves)
-            if (idxr[j] < 0 || idxr[j] >= p.E) atomicAdd(p.errors, 1ull);
-    for (int i = threadIdx.x; i < Is; i += 64 * kDnWaves) ash_l[i] = p.ash[(size_t)t * Is + i];
-
-    const int bcol = (lane & 15) < kATerms ? (lane & 15) : 0;  // other columns: ignored copies
-    const uint32_t row = (uint32_t)rt * 16 + rl;
-    const uint32_t po = row * ((uint32_t)I >> 1) + grp * 16;
-    const uint32_t bo = bcol * (uint32_t)I + grp * 16;
-    const int NCH = (KS + 3) >> 2;
-
-    for (int j = wave; j < p.K; j += kDnWaves) {
-        const int e = idxr[j];
-        v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-        if (e >= 0 && e < p.E) {
-            const uint8_t *ap = p.dp + (int64_t)e * p.d_sp;
-            const uint8_t *asr = p.ds + (int64_t)e * p.d_ss + (size_t)row * SR;
-            const uint8_t *bp = p.aq + ((int64_t)t * p.K + j) * kATerms * I;
-            const uint8_t *bsr = p.as + (((int64_t)t * p.K + j) * kATerms + bcol) * SR;
-            for (int c = 0; c < NCH; ++c) {
-                const int nst = min(4, KS - 4 * c);
-                u4 a[4], lo[4], hi[4];
-                uint32_t sa, sb;
-                static_for<0, 4>([&](auto s_) {
-                    constexpr int st = decltype(s_)::value;
-                    if (st < nst) {
-                        const uint32_t k = 4 * c + st;
-                        a[st] = *reinterpret_cast<const u4 *>(ap + (po + k * 64));
-                        lo[st] = *reinterpret_cast<const u4 *>(bp + (bo + k * 128));
-                        hi[st] = *reinterpret_cast<const u4 *>(bp + (bo + k * 128 + 64));
-                    }
-                });
-                if constexpr (wide) {
-                    sa = gather_scales(*reinterpret_cast<const u4 *>(asr + 16 * c), grp);
-                    sb = gather_scales(*reinterpret_cast<const u4 *>(bsr + 16 * c), grp);
-                } else {  // short rows: byte loads, steps past K left at 127
-                    sa = sb = 0x7f7f7f7fu;
-                    for (int st = 0; st < nst; ++st) {
-                        const uint32_t sh8 = 8 * st, m = ~(0xffu << sh8);
-                        sa = (sa & m) | ((uint32_t)asr[(4 * c + st) * 4 + grp] << sh8);
-                        sb = (sb & m) | ((uint32_t)bsr[(4 * c + st) * 4 + grp] << sh8);
-                    }
-                }
-                const uint32_t drop = ff_bytes(sa);  // scale byte 255: the group drops out
-                sa ^= drop;
-                static_for<0, 4>([&](auto s_) {
-                    constexpr int st = decltype(s_)::value;
-                    if (st < nst) {
-                        const u4 av = ((drop >> (8 * st + 7)) & 1u) ? u4{0u, 0u, 0u, 0u} : a[st];
-                        acc = mfma_fp4_fp8_sel<st>(a_operand(av), b_operand(lo[st], hi[st]), acc, (int)sa,
-                                                   (int)sb);
-                    }
-                });
-            }
-        }
-        float y[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = acc[r] + __shfl_xor(acc[r], 1);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) y[r] = y[r] + __shfl_xor(y[r], 2);
-        if ((lane & 15) == 0) {
-            const int q = lane >> 4;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ys[j][4 * q + r] = y[r];
-        }
-    }
-
-    // shared expert: 2 rows of S2 per wave against the staged activation
-    __syncthreads();
-    if (Is > 0) {
-        static_assert(kDnWaves * 2 == 16, "2 shared rows per wave");
-        const uint16_t *srow0 = p.sh_down + ((int64_t)rt * 16 + wave * 2) * Is;
-        float a2[2] = {0.0f, 0.0f};
-        constexpr int CH = 4;  // 512-element slices whose loads are issued together
-        for (int i0 = lane * 8; i0 < Is; i0 += 512 * CH) {
-            u4 wv[2][CH];
-#pragma unroll
-            for (int rr = 0; rr < 2; ++rr)
-#pragma unroll
-                for (int c = 0; c < CH; ++c) {
-                    const int i = i0 + 512 * c;
-                    wv[rr][c] = i < Is ? *reinterpret_cast<const u4 *>(srow0 + (size_t)rr * Is + i)
-                                       : u4{0u, 0u, 0u, 0u};
-                }
-#pragma unroll
-            for (int c = 0; c < CH; ++c) {
-                const int i = i0 + 512 * c;
-                if (i >= Is) break;
-                const float4 x0 = *reinterpret_cast<const float4 *>(ash_l + i);
-                const float4 x1 = *reinterpret_cast<const float4 *>(ash_l + i + 4);
-#pragma unroll
-                for (int rr = 0; rr < 2; ++rr) {
-                    const u4 w4 = wv[rr][c];
-                    float v = a2[rr];
-                    v = fmaf(bf16f(w4[0] & 0xffffu), x0.x, v);
-                    v = fmaf(bf16f(w4[0] >> 16), x0.y, v);
-                    v = fmaf(bf16f(w4[1] & 0xffffu), x0.z, v);
-                    v = fmaf(bf16f(w4[1] >> 16), x0.w, v);
-                    v = fmaf(bf16f(w4[2] & 0xffffu), x1.x, v);
-                    v = fmaf(bf16f(w4[2] >> 16), x1.y, v);
-                    v = fmaf(bf16f(w4[3] & 0xffffu), x1.z, v);
-                    v = fmaf(bf16f(w4[3] >> 16), x1.w, v);
-                    a2[rr] = v;
-                }
-            }
-        }
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) a2[rr] += __shfl_xor(a2[rr], o);
-            if (lane == 0) sh[wave * 2 + rr] = a2[rr];
-        }
-    }
-    __syncthreads();
-    if (threadIdx.x < 16) {
-        float o = 0.0f;
-        for (int j = 0; j < p.K; ++j) o = fmaf(p.w[(size_t)t * p.K + j], ys[j][threadIdx.x], o);
-        if (Is > 0) o += sh[threadIdx.x];
-        p.out[(size_t)t * p.H + rt * 16 + threadIdx.x] = o;
-    }
-}
-
 
 // ---------------------------------------------------------------------------
 // Single-token path (T = 1). The k assignments are the router slots j
@@ -1465,7 +1032,8 @@ __global__ __launch_bounds__(64 * kDnDecWaves) void k_down_dec(DownDecParams p)
 
 // Router-order combine: out[t][o] = sum_j w[t][j] * ys[t][j][o] (j = 0..k-1
 // in order, one fma each), then + ys[t][k][o] (the shared expert, if any).
-// Slots with an out-of-range id hold 0 and are counted once here.
+// A slot with an out-of-range id adds nothing (its staging row is not read)
+// and is counted once here.
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ ys, const float *__restrict__ w,
                                                  const int32_t *__restrict__ idx, int T, int K, int H,
                                                  int E, int shared, float *__restrict__ out,
@@ -1477,16 +1045,25 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ ys, c
         const int o = (int)(i - t * H);
         const float *y = ys + (size_t)t * (K + 1) * H + o;
         const float *wt = w + (size_t)t * K;
+        const int32_t *it = idx + (size_t)t * K;
         float acc = 0.0f;
         int j = 0;
         for (; j + 8 <= K; j += 8) {  // 8 loads in flight, then 8 fmas in order
             float v[8];
+            bool ok[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = y[(size_t)(j + q) * H];
+            for (int q = 0; q < 8; ++q) {
+                const int e = it[j + q];
+                ok[q] = e >= 0 && e < E;
+                v[q] = ok[q] ? y[(size_t)(j + q) * H] : 0.0f;
+            }
 #pragma unroll
-            for (int q = 0; q < 8; ++q) acc = fmaf(wt[j + q], v[q], acc);
+            for (int q = 0; q < 8; ++q) acc = ok[q] ? fmaf(wt[j + q], v[q], acc) : acc;
         }
-        for (; j < K; ++j) acc = fmaf(wt[j], y[(size_t)j * H], acc);
+        for (; j < K; ++j) {
+            const int e = it[j];
+            if (e >= 0 && e < E) acc = fmaf(wt[j], y[(size_t)j * H], acc);
+        }
         if (shared) acc += y[(size_t)K * H];
         out[i] = acc;
     }
@@ -1551,7 +1128,7 @@ static bool decode_path_ok(const LayerView &L)
 // T = 1: token fp8 expansion, gate/up, down, router-order combine. The
 // router slots are the assignment list (no permutation).
 static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const int32_t *idx,
-                                    const float *w, float *out, uint8_t *xq, uint8_t *xs, uint8_t *aq,
+                                    const float *w, float *out, uint8_t *xq, uint8_t *xs, float *act,
                                     float *ash, char *ys_base, hipStream_t s, Profiler *prof)
 {
     int dev = 0, ncu = 256;
@@ -1574,7 +1151,6 @@ static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const
     gp.K = L.K;
     gp.E = L.E;
     gp.act = L.act;
-    gp.T = 1;
     gp.Is = L.Is;
     gp.b1 = L.b1;
     gp.b2 = L.b2;
@@ -1582,10 +1158,7 @@ static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const
     gp.xq = xq;
     gp.xs = xs;
     gp.idx = idx;
-    // the fp32 activations [k][I] take the place of the e4m3 terms [k][4][I]
-    // (same size: 4 terms of 1 byte vs one 4-byte float per element)
-    static_assert(kATerms == sizeof(float), "activation buffer reuse");
-    gp.act_f = reinterpret_cast<float *>(aq);
+    gp.act_f = act;
     gp.sh_gate = L.sh_gate;
     gp.sh_up = L.sh_up;
     gp.ash = ash;
@@ -1633,109 +1206,51 @@ static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const
     return hipGetLastError();
 }
 
+// T > 1 (or shapes the single-token kernels do not take): token -> expert
+// permutation, grouped GEMMs, router-order combine.
 hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const int32_t *idx,
                           const float *w, float *out, char *ws, const WsLayout &lay, hipStream_t s,
                           Profiler *prof)
 {
-    uint8_t *xq = reinterpret_cast<uint8_t *>(ws + lay.xq);
-    uint8_t *xs = reinterpret_cast<uint8_t *>(ws + lay.xs);
-    int32_t *chunk_cnt = reinterpret_cast<int32_t *>(ws + lay.chunk_cnt);
     int32_t *active_n = reinterpret_cast<int32_t *>(ws + lay.active_n);
     int32_t *active_e = reinterpret_cast<int32_t *>(ws + lay.active_e);
     int32_t *active_off = reinterpret_cast<int32_t *>(ws + lay.active_off);
     int32_t *sorted = reinterpret_cast<int32_t *>(ws + lay.sorted);
-    uint8_t *aq = reinterpret_cast<uint8_t *>(ws + lay.aq);
-    uint8_t *as = reinterpret_cast<uint8_t *>(ws + lay.as);
-    float *ash = reinterpret_cast<float *>(ws + lay.ash);
+    float *ys = reinterpret_cast<float *>(ws + lay.ys);
 
-    const int64_t n = (int64_t)T * L.H;
-    const unsigned slabs = (unsigned)((n + 255) / 256);
-    const int nchunks = (T + kPermChunk - 1) / kPermChunk;
     if (T == 1 && decode_path_ok(L))
-        return launch_forward_t1(L, x, idx, w, out, xq, xs, aq, ash, ws + lay.ys, s, prof);
-    if (nchunks == 1) {
+        return launch_forward_t1(L, x, idx, w, out, reinterpret_cast<uint8_t *>(ws + lay.xq),
+                                 reinterpret_cast<uint8_t *>(ws + lay.xs), reinterpret_cast<float *>(ws + lay.act),
+                                 reinterpret_cast<float *>(ws + lay.ash), ws + lay.ys, s, prof);
+    const int nchunks = (T + kPermChunk - 1) / kPermChunk;
+    {
         StageMark m(prof, K3MOE_STAGE_PERM, s);
-        k_prep_small<<<1 + slabs, 256, 0, s>>>(x, n, L.H, xq, xs, idx, T, L.K, L.E, active_n, active_e,
-                                               active_off, sorted);
-    } else {
-        {
-            StageMark m(prof, K3MOE_STAGE_XSPLIT, s);
-            k_xsplit<<<slabs, 256, 0, s>>>(x, n, L.H, xq, xs);
+        if (nchunks == 1) {
+            k_perm_small<<<1, 256, 0, s>>>(idx, T, L.K, L.E, active_n, active_e, active_off, sorted);
+        } else {
+            int32_t *chunk_cnt = reinterpret_cast<int32_t *>(ws + lay.chunk_cnt);
+            k_perm_hist<<<nchunks, 256, 0, s>>>(idx, T, L.K, L.E, chunk_cnt);
+            k_perm_scan<<<1, 1024, 0, s>>>(nchunks, L.E, chunk_cnt, active_n, active_e, active_off);
+            k_perm_scatter<<<nchunks, 64, 0, s>>>(idx, T, L.K, L.E, chunk_cnt, sorted);
         }
-        StageMark m(prof, K3MOE_STAGE_PERM, s);
-        k_perm_hist<<<nchunks, 256, 0, s>>>(idx, T, L.K, L.E, chunk_cnt);
-        k_perm_scan<<<1, 1024, 0, s>>>(nchunks, L.E, chunk_cnt, active_n, active_e, active_off);
-        k_perm_scatter<<<nchunks, 64, 0, s>>>(idx, T, L.K, L.E, chunk_cnt, sorted);
     }
-
-    GateUpParams gp;
-    gp.gp = L.gp;
-    gp.gs = L.gs;
-    gp.up = L.up;
-    gp.us = L.us;
-    gp.g_sp = L.g_sp;
-    gp.g_ss = L.g_ss;
-    gp.u_sp = L.u_sp;
-    gp.u_ss = L.u_ss;
-    gp.H = L.H;
-    gp.I = L.I;
-    gp.K = L.K;
-    gp.E = L.E;
-    gp.idx = idx;
-    gp.act = L.act;
-    gp.T = T;
-    gp.Is = L.Is;
-    gp.b1 = L.b1;
-    gp.b2 = L.b2;
-    gp.x = x;
-    gp.xq = xq;
-    gp.xs = xs;
-    gp.active_n = active_n;
-    gp.active_e = active_e;
-    gp.active_off = active_off;
-    gp.sorted = sorted;
-    gp.aq = aq;
-    gp.as = as;
-    gp.sh_gate = L.sh_gate;
-    gp.sh_up = L.sh_up;
-    gp.ash = ash;
-    const int64_t max_active = std::min<int64_t>(L.E, (int64_t)T * L.K);
-    gp.routed_blocks = (int)(max_active * (L.I / 32));
-    const int shared_blocks = (L.Is + 3) / 4;
-    gp.shared_blocks = shared_blocks;
+    // activations: routed bf16 hi and lo [T*k][I] in the fp8-term region
+    // (4 bytes per element either way); shared bf16 hi and lo [T][Is] in the
+    // fp32 shared-activation region
+    uint16_t *act_hi = reinterpret_cast<uint16_t *>(ws + lay.act);
+    uint16_t *act_lo = act_hi + (size_t)T * L.K * L.I;
+    uint16_t *ash_hi = reinterpret_cast<uint16_t *>(ws + lay.ash);
+    uint16_t *ash_lo = ash_hi + (size_t)T * L.Is;
+    hipError_t e = launch_grouped(L, x, T, active_n, active_e, active_off, sorted, act_hi, act_lo, ash_hi,
+                                  ash_lo, reinterpret_cast<int2 *>(ws + lay.tiles_gu),
+                                  reinterpret_cast<int2 *>(ws + lay.tiles_dn),
+                                  reinterpret_cast<int32_t *>(ws + lay.tile_n), ys, s, prof);
+    if (e != hipSuccess) return e;
     {
-        StageMark m(prof, K3MOE_STAGE_GATEUP, s);
-        const unsigned nblk = (unsigned)(gp.routed_blocks + shared_blocks);
-        if (L.H % 512 == 0)
-            k_gateup<true><<<nblk, 256, 0, s>>>(gp);
-        else
-            k_gateup<false><<<nblk, 256, 0, s>>>(gp);
-    }
-
-    DownParams dp;
-    dp.dp = L.dp;
-    dp.ds = L.ds;
-    dp.d_sp = L.d_sp;
-    dp.d_ss = L.d_ss;
-    dp.H = L.H;
-    dp.I = L.I;
-    dp.E = L.E;
-    dp.K = L.K;
-    dp.Is = L.Is;
-    dp.idx = idx;
-    dp.w = w;
-    dp.aq = aq;
-    dp.as = as;
-    dp.sh_down = L.sh_down;
-    dp.ash = ash;
-    dp.out = out;
-    dp.errors = L.errors;
-    {
-        StageMark m(prof, K3MOE_STAGE_DOWN, s);
-        if (L.I % 512 == 0)
-            k_down<true><<<dim3(L.H / 16, T), 64 * kDnWaves, dn_lds_bytes(L.Is), s>>>(dp);
-        else
-            k_down<false><<<dim3(L.H / 16, T), 64 * kDnWaves, dn_lds_bytes(L.Is), s>>>(dp);
+        StageMark m(prof, K3MOE_STAGE_COMBINE, s);
+        const int64_t n = (int64_t)T * L.H;
+        k_combine<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(ys, w, idx, T, L.K, L.H, L.E, L.Is > 0, out,
+                                                             L.errors);
     }
     return hipGetLastError();
 }

@@ -34,7 +34,7 @@ def test_status_strings():
 
 def _weights(E, shared=False, misalign=False):
     base = 0x10000000 + (8 if misalign else 0)
-    mx = k3.MXFP4(base, base + 0x1000000, 4096, 256)
+    mx = k3.MXFP4(base, base + 0x1000000, 0x10000, 0x1000)
     sh = (base + 0x100, base + 0x200, base + 0x300) if shared else (None, None, None)
     return k3.Weights(base, None, mx, mx, mx, *sh)
 
@@ -60,7 +60,16 @@ def test_weight_descriptor_refusals():
     w = _weights(8)
     w.gate.expert_stride_packed = 100          # smaller than one matrix
     assert _create(cfg, w) == 1
+    w = _weights(8)
+    w.router_w = None
+    assert _create(cfg, w) == 1
     assert _create(cfg, _weights(8, misalign=True)) == 4
+    w = _weights(8)
+    w.down.scales += 4                           # scales must be 16-byte aligned too
+    assert _create(cfg, w) == 4
+    w = _weights(8)
+    w.up.expert_stride_scales = 0x1008
+    assert _create(cfg, w) == 4
     assert _create(cfg, _weights(8, shared=True)) == 1   # shared pointers without shared_inter
     cfg2 = k3.make_config(256, 128, 8, 2, shared_inter=128)
     assert _create(cfg2, _weights(8)) == 1               # shared_inter without pointers
