@@ -33,6 +33,17 @@ WsLayout ws_layout(const k3moe_config &c, int64_t T)
     };
     L.sc = take(sizeof(float) * T * E);
     L.ch = take(sizeof(float) * T * E);
+    {
+        // a call may take fewer tokens than the workspace was sized for, and
+        // the slice count falls as T grows: the largest partial buffer over
+        // every T' <= T (no batch of more than 64 * 512 tokens is sliced)
+        size_t part = 0;
+        for (int64_t t = kRouterWaveMaxT + 1; t <= std::min<int64_t>(T, 64 * 512); ++t) {
+            const int S = router_splits(t, (int)E, (int)H);
+            if (S > 1) part = std::max(part, sizeof(double) * S * t * E);
+        }
+        L.rt_part = take(part);
+    }
     const int64_t T1 = std::min<int64_t>(T, 1);  // the fp8 token terms serve T = 1 only
     L.xq = take((size_t)T1 * kXTerms * H);
     L.xs = take((size_t)T1 * kXTerms * (H / 32));

@@ -25,6 +25,7 @@ constexpr int kPermChunk = 16;
 // Byte offsets of the workspace regions for T tokens (all 256-aligned).
 struct WsLayout {
     size_t sc, ch;            // router scores, fp32 [T][E] each
+    size_t rt_part;           // batched router fp64 partial sums [slices][T][E]
     size_t xq, xs;            // single token's fp8 terms [4][H], scales [4][H/32]
     size_t chunk_cnt;         // int32 [nchunks][E]
     size_t active_n;          // int32 [1]
@@ -101,6 +102,11 @@ struct StageMark {
 
 // Launchers (kernels live in k3moe_kernels.hip). Each returns the status of
 // hipGetLastError() after its launches.
+// Batched router (T > kRouterWaveMaxT): hidden-dimension slices and their width.
+constexpr int kRouterWaveMaxT = 4;
+int router_splits(int64_t T, int E, int H);
+int router_kspan(int H, int S);
+
 hipError_t launch_route(const LayerView &L, const uint16_t *x, int T, int32_t *idx,
                         float *w, float *logits, char *ws, const WsLayout &lay,
                         hipStream_t s, Profiler *prof);

@@ -136,6 +136,20 @@ __device__ __forceinline__ void split_e4m3_32(float v, int (&code)[NT], int (&sb
 }
 
 // ---------------------------------------------------------------------------
+// Router epilogue for one (token, expert): the fp32 logit, the fp32 score
+// (sigmoid evaluated in fp64, rounded once) and the fp32 selection score.
+__device__ __forceinline__ void router_finish(double acc, int t, int e, int E, const float *__restrict__ bias,
+                                              float *__restrict__ sc, float *__restrict__ ch,
+                                              float *__restrict__ logits)
+{
+    const float l32 = (float)acc;
+    const float s = (float)(1.0 / (1.0 + exp(-(double)l32)));
+    const size_t o = (size_t)t * E + e;
+    sc[o] = s;
+    ch[o] = s + (bias ? bias[e] : 0.0f);
+    if (logits) logits[o] = l32;
+}
+
 // Router (README §9, k3_router). One wave per (expert, token): 16-byte loads
 // of the router row and the token, exact bf16 products summed in fp64, a
 // fixed-order butterfly across the wave. Lane 0 then forms the fp32 logit,
@@ -173,14 +187,104 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t *__restrict__ x,
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-    if (lane == 0) {
-        const float l32 = (float)acc;
-        const float s = (float)(1.0 / (1.0 + exp(-(double)l32)));
-        const size_t o = (size_t)t * E + e;
-        sc[o] = s;
-        ch[o] = s + (bias ? bias[e] : 0.0f);
-        if (logits) logits[o] = l32;
+    if (lane == 0) router_finish(acc, t, e, E, bias, sc, ch, logits);
+}
+
+// Batched router: logits = Wr X^T on the fp64 MFMA v_mfma_f64_16x16x4_f64
+// (bf16 inputs converted exactly to fp64, fp64 accumulation), so each logit
+// is an fp64 sum of the exact products, as in the one-wave kernel above. A
+// block of 4 waves takes 64 experts x 64 tokens over one slice of the hidden
+// dimension (the grid's z); each wave a 32 x 32 tile (2 x 2 MFMA tiles).
+// Within a 32-element chunk the lane group g (lanes 16g..16g+15) carries the
+// elements 8g..8g+7, one per MFMA step, so one 16-byte load per lane and
+// operand covers the chunk; the summation order is immaterial to an fp64 sum
+// of this kind up to its rounding. One slice: finished in place; several:
+// fp64 partial sums [slice][T][E], added in slice order by k_router_reduce.
+typedef double v4d __attribute__((ext_vector_type(4)));
+constexpr int kRtTile = 64;   // experts and tokens per block
+constexpr int kRtDepth = 3;   // chunks in flight ahead of the MFMAs
+
+__global__ __launch_bounds__(256) void k_router_mm(const uint16_t *__restrict__ x,
+                                                   const uint16_t *__restrict__ Wr, int T, int H, int E,
+                                                   int kspan, double *__restrict__ part,
+                                                   const float *__restrict__ bias, float *__restrict__ sc,
+                                                   float *__restrict__ ch, float *__restrict__ logits)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave & 1, wn = wave >> 1, g = lane >> 4, l16 = lane & 15;
+    const int e0 = blockIdx.x * kRtTile + wm * 32, t0 = blockIdx.y * kRtTile + wn * 32;
+    const int k0 = blockIdx.z * kspan, nch = (min(H, k0 + kspan) - k0) / 32;
+    const uint16_t *ap[2], *bp[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        ap[f] = Wr + (size_t)min(e0 + 16 * f + l16, E - 1) * H + k0 + 8 * g;
+        bp[f] = x + (size_t)min(t0 + 16 * f + l16, T - 1) * H + k0 + 8 * g;
     }
+    v4d acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = v4d{0.0, 0.0, 0.0, 0.0};
+    u4 buf[kRtDepth + 1][4];
+    auto load = [&](int c, u4 (&b)[4]) {
+        const int cc = min(c, nch - 1) * 32;
+        b[0] = *reinterpret_cast<const u4 *>(ap[0] + cc);
+        b[1] = *reinterpret_cast<const u4 *>(ap[1] + cc);
+        b[2] = *reinterpret_cast<const u4 *>(bp[0] + cc);
+        b[3] = *reinterpret_cast<const u4 *>(bp[1] + cc);
+    };
+    auto half = [](uint32_t w, int hi) { return (double)bf16f(hi ? w >> 16 : w & 0xffffu); };
+#pragma unroll
+    for (int d = 0; d < kRtDepth; ++d) load(d, buf[d]);
+    for (int c = 0; c < nch; c += kRtDepth + 1) {
+#pragma unroll
+        for (int u = 0; u <= kRtDepth; ++u) {
+            load(c + u + kRtDepth, buf[(u + kRtDepth) % (kRtDepth + 1)]);
+            if (c + u < nch) {
+                const u4(&b)[4] = buf[u];
+#pragma unroll
+                for (int st = 0; st < 8; ++st) {
+                    const double a0 = half(b[0][st >> 1], st & 1), a1 = half(b[1][st >> 1], st & 1);
+                    const double x0 = half(b[2][st >> 1], st & 1), x1 = half(b[3][st >> 1], st & 1);
+                    acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, x0, acc[0][0], 0, 0, 0);
+                    acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, x1, acc[0][1], 0, 0, 0);
+                    acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, x0, acc[1][0], 0, 0, 0);
+                    acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, x1, acc[1][1], 0, 0, 0);
+                }
+            }
+        }
+    }
+    // tile (i, j): the fp64 MFMA leaves row 4 r + g of column l16 in result
+    // register r, i.e. expert e0 + 16 i + 4 r + g of token t0 + 16 j + l16
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int t = t0 + 16 * j + l16;
+            if (t >= T) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int e = e0 + 16 * i + 4 * r + g;
+                if (e >= E) continue;
+                if (part)
+                    part[((size_t)blockIdx.z * T + t) * E + e] = acc[i][j][r];
+                else
+                    router_finish(acc[i][j][r], t, e, E, bias, sc, ch, logits);
+            }
+        }
+}
+
+// Slice partial sums -> logits, in slice order.
+__global__ __launch_bounds__(256) void k_router_reduce(const double *__restrict__ part, int S, int T, int E,
+                                                       const float *__restrict__ bias, float *__restrict__ sc,
+                                                       float *__restrict__ ch, float *__restrict__ logits)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x, n = (int64_t)T * E;
+    if (i >= n) return;
+    double acc = part[i];
+    for (int s = 1; s < S; ++s) acc += part[(size_t)s * n + i];
+    const int t = (int)(i / E);
+    router_finish(acc, t, (int)(i - (int64_t)t * E), E, bias, sc, ch, logits);
 }
 
 // Wave-wide max / min of a uint32 through DPP (row-local steps, then the
@@ -1074,6 +1178,18 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ ys, c
 
 }  // namespace
 
+// Hidden-dimension slices of the batched router: enough blocks to cover the
+// chip about twice (512 blocks), slices of at least 256 elements.
+int router_splits(int64_t T, int E, int H)
+{
+    const int64_t tiles = (int64_t)((E + kRtTile - 1) / kRtTile) * ((T + kRtTile - 1) / kRtTile);
+    const int64_t want = (512 + tiles - 1) / tiles;
+    const int64_t S = std::max<int64_t>(1, std::min<int64_t>(want, H / 256));
+    return (int)((H + router_kspan(H, (int)S) - 1) / router_kspan(H, (int)S));
+}
+
+int router_kspan(int H, int S) { return (H / 32 + S - 1) / S * 32; }
+
 template <int NQ>
 static void topk_launch(int T, hipStream_t s, const float *sc, const float *ch, const LayerView &L,
                         int32_t *idx, float *w)
@@ -1088,8 +1204,22 @@ hipError_t launch_route(const LayerView &L, const uint16_t *x, int T, int32_t *i
     float *ch = reinterpret_cast<float *>(ws + lay.ch);
     {
         StageMark m(prof, K3MOE_STAGE_ROUTER, s);
-        k_router<<<dim3((L.E + 3) / 4, T), 256, 0, s>>>(x, L.router_w, L.router_bias, L.H, L.E, sc,
-                                                        ch, logits);
+        if (T <= kRouterWaveMaxT) {
+            k_router<<<dim3((L.E + 3) / 4, T), 256, 0, s>>>(x, L.router_w, L.router_bias, L.H, L.E, sc,
+                                                            ch, logits);
+        } else {
+            const int S = router_splits(T, L.E, L.H);
+            const int kspan = router_kspan(L.H, S);
+            double *part = S > 1 ? reinterpret_cast<double *>(ws + lay.rt_part) : nullptr;
+            const dim3 grid((L.E + kRtTile - 1) / kRtTile, (T + kRtTile - 1) / kRtTile, S);
+            k_router_mm<<<grid, 256, 0, s>>>(x, L.router_w, T, L.H, L.E, kspan, part, L.router_bias, sc, ch,
+                                             logits);
+            if (S > 1) {
+                const int64_t n = (int64_t)T * L.E;
+                k_router_reduce<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, S, T, L.E, L.router_bias, sc,
+                                                                            ch, logits);
+            }
+        }
     }
     {
         StageMark m(prof, K3MOE_STAGE_TOPK, s);
