@@ -87,64 +87,70 @@ __device__ __forceinline__ float act_fn(float g, float u, int kind, float b1, fl
 }
 
 // ---------------------------------------------------------------------------
-// Tile lists. Active expert q (ascending id) with n_q assignments gets
-// ceil(n_q / BN) token tiles; tiles[i] = (q, token block).
+// Work lists. Active expert q (ascending id) with n_q assignments goes to the
+// weight-streaming kernels when n_q <= smax (light[] lists such q in order),
+// else gets ceil(n_q / BN) GEMM tiles; tiles[i] = (q, token block).
+// counts: [0] gate/up tiles, [1] down tiles, [2] light experts.
 __global__ __launch_bounds__(1024) void k_tiles(const int32_t *__restrict__ active_n,
                                                 const int32_t *__restrict__ active_off, int bn_gu,
-                                                int bn_dn, int2 *__restrict__ tiles_gu, int32_t *tile_n_gu,
-                                                int2 *__restrict__ tiles_dn, int32_t *tile_n_dn)
+                                                int bn_dn, int smax, int2 *__restrict__ tiles_gu,
+                                                int2 *__restrict__ tiles_dn, int32_t *__restrict__ light,
+                                                int32_t *counts)
 {
-    __shared__ int wsum[2][16];
-    __shared__ int tot[2];
+    __shared__ int wsum[3][16];
     const int n = *active_n;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int per = (n + 1023) / 1024;
     const int q0 = tid * per;
-    int cg = 0, cd = 0;
+    int cnt[3] = {0, 0, 0};
     for (int i = 0; i < per; ++i) {
         const int q = q0 + i;
         if (q < n) {
             const int m = active_off[q + 1] - active_off[q];
-            cg += (m + bn_gu - 1) / bn_gu;
-            cd += (m + bn_dn - 1) / bn_dn;
+            if (m <= smax) {
+                cnt[2] += 1;
+            } else {
+                cnt[0] += (m + bn_gu - 1) / bn_gu;
+                cnt[1] += (m + bn_dn - 1) / bn_dn;
+            }
         }
     }
-    int ig = cg, id = cd;  // inclusive scans across the wave
+    int inc[3] = {cnt[0], cnt[1], cnt[2]};  // inclusive scans across the wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-        const int a = __shfl_up(ig, o), b = __shfl_up(id, o);
-        if (lane >= o) {
-            ig += a;
-            id += b;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int a = __shfl_up(inc[k], o);
+            if (lane >= o) inc[k] += a;
         }
     }
-    if (lane == 63) {
-        wsum[0][wv] = ig;
-        wsum[1][wv] = id;
-    }
+    if (lane == 63)
+        for (int k = 0; k < 3; ++k) wsum[k][wv] = inc[k];
     __syncthreads();
     if (tid == 0) {
-        int rg = 0, rd = 0;
-        for (int k = 0; k < 16; ++k) {
-            const int a = wsum[0][k], b = wsum[1][k];
-            wsum[0][k] = rg;
-            wsum[1][k] = rd;
-            rg += a;
-            rd += b;
+        for (int k = 0; k < 3; ++k) {
+            int r = 0;
+            for (int w = 0; w < 16; ++w) {
+                const int a = wsum[k][w];
+                wsum[k][w] = r;
+                r += a;
+            }
+            counts[k] = r;
         }
-        tot[0] = rg;
-        tot[1] = rd;
-        *tile_n_gu = rg;
-        *tile_n_dn = rd;
     }
     __syncthreads();
-    int bg = wsum[0][wv] + ig - cg, bd = wsum[1][wv] + id - cd;
+    int bg = wsum[0][wv] + inc[0] - cnt[0], bd = wsum[1][wv] + inc[1] - cnt[1];
+    int bl = wsum[2][wv] + inc[2] - cnt[2];
     for (int i = 0; i < per; ++i) {
         const int q = q0 + i;
         if (q < n) {
             const int m = active_off[q + 1] - active_off[q];
-            for (int tb = 0; tb * bn_gu < m; ++tb) tiles_gu[bg++] = int2{q, tb};
-            for (int tb = 0; tb * bn_dn < m; ++tb) tiles_dn[bd++] = int2{q, tb};
+            if (m <= smax) {
+                light[bl++] = q;
+            } else {
+                for (int tb = 0; tb * bn_gu < m; ++tb) tiles_gu[bg++] = int2{q, tb};
+                for (int tb = 0; tb * bn_dn < m; ++tb) tiles_dn[bd++] = int2{q, tb};
+            }
         }
     }
 }
@@ -577,15 +583,18 @@ size_t grouped_tile_cap_dn(int64_t T, int K, int E) { return grouped_tile_cap(T,
 hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const int32_t *active_n,
                           const int32_t *active_e, const int32_t *active_off, const int32_t *sorted,
                           uint16_t *act_hi, uint16_t *act_lo, uint16_t *ash_hi, uint16_t *ash_lo,
-                          int2 *tiles_gu, int2 *tiles_dn, int32_t *tile_n, float *ys, hipStream_t s,
-                          Profiler *prof)
+                          int2 *tiles_gu, int2 *tiles_dn, int32_t *light, int32_t *counts, float *ys,
+                          hipStream_t s, Profiler *prof)
 {
     static const bool lds_set = set_lds_limits();  // once per process (thread-safe static)
     (void)lds_set;
     const size_t cap_gu = grouped_tile_cap(T, L.K, L.E, kGuTok), cap_dn = grouped_tile_cap(T, L.K, L.E, kDnTok);
     const int rb_i = (L.I + kGRows - 1) / kGRows, rb_h = (L.H + kGRows - 1) / kGRows;
     const int rb_s = (L.Is + kGRows - 1) / kGRows;
-    k_tiles<<<1, 1024, 0, s>>>(active_n, active_off, kGuTok, kDnTok, tiles_gu, tile_n, tiles_dn, tile_n + 1);
+    const bool stream = stream_path_ok(L);
+    const bool sh_stream = stream && stream_shared_ok(L, T);
+    k_tiles<<<1, 1024, 0, s>>>(active_n, active_off, kGuTok, kDnTok, stream ? stream_max_tokens() : 0, tiles_gu,
+                               tiles_dn, light, counts);
 
     GuGemmParams gp{};
     gp.H = L.H;
@@ -608,15 +617,20 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const in
     gp.active_off = active_off;
     gp.sorted = sorted;
     gp.tiles = tiles_gu;
-    gp.tile_n = tile_n;
+    gp.tile_n = counts;
     gp.act_hi = act_hi;
     gp.act_lo = act_lo;
     {
         StageMark m(prof, K3MOE_STAGE_GATEUP, s);
+        if (stream) {
+            const hipError_t e = launch_stream_gu(L, x, T, active_e, active_off, sorted, light, counts + 2, sh_stream,
+                                                  act_hi, act_lo, ash_hi, ash_lo, s);
+            if (e != hipSuccess) return e;
+        }
         const unsigned nblk = (unsigned)(cap_gu * rb_i);
         k_gu_gemm<true><<<nblk, 64 * kGWaves, gu_gemm_lds_bytes<true>(), s>>>(gp);
     }
-    if (L.Is > 0) {
+    if (L.Is > 0 && !sh_stream) {
         StageMark m(prof, K3MOE_STAGE_SHARED_GATEUP, s);
         GuGemmParams sp = gp;
         sp.I = L.Is;
@@ -643,13 +657,18 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const in
     dp.active_off = active_off;
     dp.sorted = sorted;
     dp.tiles = tiles_dn;
-    dp.tile_n = tile_n + 1;
+    dp.tile_n = counts + 1;
     dp.ys = ys;
     {
         StageMark m(prof, K3MOE_STAGE_DOWN, s);
+        if (stream) {
+            const hipError_t e = launch_stream_dn(L, T, active_e, active_off, sorted, light, counts + 2, sh_stream,
+                                                  act_hi, act_lo, ash_hi, ash_lo, ys, s);
+            if (e != hipSuccess) return e;
+        }
         const unsigned nblk = (unsigned)(cap_dn * rb_h);
         k_dn_gemm<true><<<nblk, 64 * kGWaves, dn_gemm_lds_bytes<true>(), s>>>(dp);
-        if (L.Is > 0) {
+        if (L.Is > 0 && !sh_stream) {
             DnGemmParams sp = dp;
             sp.I = L.Is;
             sp.wd = L.sh_down;

@@ -1374,6 +1374,7 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const in
     hipError_t e = launch_grouped(L, x, T, active_n, active_e, active_off, sorted, act_hi, act_lo, ash_hi,
                                   ash_lo, reinterpret_cast<int2 *>(ws + lay.tiles_gu),
                                   reinterpret_cast<int2 *>(ws + lay.tiles_dn),
+                                  reinterpret_cast<int32_t *>(ws + lay.light),
                                   reinterpret_cast<int32_t *>(ws + lay.tile_n), ys, s, prof);
     if (e != hipSuccess) return e;
     {

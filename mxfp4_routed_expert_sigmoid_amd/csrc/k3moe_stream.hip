@@ -1,0 +1,555 @@
+// gfx950 weight-streaming kernels for experts that hold few tokens (T > 1).
+//
+// What is computed follows the "kimi-k3-in-c" README, §9 "Picking 16 experts
+// of 896" (k3_moe steps 3 and 6, k3_situ_glu) on the MXFP4 format of §4
+// "Reduction one: the experts already ship at half a byte".
+//
+// When an expert holds at most 16 of the batch's assignments its projections
+// are bound by streaming its weights, not by the MFMA. Here every wave owns 32
+// weight rows (two 16-row MFMA tiles) over the whole K range and all of the
+// expert's tokens (one 16-column B tile), so weight bytes go from HBM straight
+// into registers, each loaded once, with the next group of K in flight while
+// the current one is multiplied. The tokens (bf16 x, or the bf16 hi/lo
+// activation planes) pass through LDS, staged one K group ahead by the whole
+// block. Products run on v_mfma_f32_16x16x32_bf16 after an exact fp4 -> bf16
+// expansion (v_cvt_scalef32_pk_bf16_fp4 applies the E8M0 scale; byte 255
+// gives zeros), as in the grouped GEMMs.
+//
+// K mapping. An MFMA step multiplies 32 K elements; lane group g (lanes
+// 16g..16g+15) supplies 8 of them. A lane's 16-byte weight load holds 32
+// consecutive fp4 values of its row, i.e. 4 steps' worth for its group: in
+// chunk c of a group the lane's group covers K = 128c + 32g + [0, 32) and step
+// s takes K = 128c + 32g + 8s + [0, 8). The token side reads the same K from
+// LDS, so the sum runs over every K exactly once. For bf16 weights (shared
+// expert) a 16-byte load is 8 values, one step: chunk c covers K = 32c + 8g +
+// [0, 8).
+//
+// The same launch also runs the shared expert for small batches: its blocks
+// come first in the grid (token groups of 16 x 128-row blocks, bf16 weights),
+// so they stream alongside the routed blocks.
+#include "k3moe_internal.h"
+
+namespace k3moe {
+namespace {
+
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSWaves = 4;                 // waves per block
+constexpr int kSRows = 32;                 // weight rows per wave
+constexpr int kSBlkRows = kSWaves * kSRows;
+constexpr int kSTok = 16;                  // tokens per stream item (one B tile)
+constexpr int kSChunks = 4;                // 16-byte weight loads per row per K group
+constexpr int kSPad = 16;                  // LDS padding per token row
+
+__device__ __forceinline__ float bf16f(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ uint16_t bf16_rne(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float e8m0_scale(uint32_t s)
+{
+    return s == 255u ? 0.0f : __uint_as_float(s == 0u ? 0x00400000u : s << 23);
+}
+
+__device__ __forceinline__ bf8 dequant8(uint32_t w, float scale)
+{
+    const bf2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+    const bf2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+    const bf2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+    const bf2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+    return bf8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+__device__ __forceinline__ bf8 as_bf8(u4 v)
+{
+    bf8 r;
+    __builtin_memcpy(&r, &v, 16);
+    return r;
+}
+
+__device__ __forceinline__ v4f mfma_bf16(const bf8 &a, const bf8 &b, v4f c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float act_fn(float g, float u, int kind, float b1, float b2)
+{
+    const float sg = 1.0f / (1.0f + expf(-g));
+    if (kind == K3MOE_ACT_SITU) return (b1 * tanhf(g / b1) * sg) * (b2 * tanhf(u / b2));
+    return g * sg * u;
+}
+
+// K elements per group and token-row bytes per group.
+template <bool FP4> constexpr int group_k() { return FP4 ? 128 * kSChunks : 8 * 4 * kSChunks; }
+template <bool FP4> constexpr int brow_bytes() { return group_k<FP4>() * 2 + kSPad; }
+
+// One stream item as a wave sees it.
+struct Item {
+    int n;          // tokens (1..16)
+    int rows;       // weight rows of the matrix (I or H)
+    int row0;       // first row of this wave
+    const uint8_t *w[2];   // weight row bases (gate/up, or down twice)
+    const uint8_t *s[2];   // FP4: scale row bases
+};
+
+// ---------------------------------------------------------------------------
+// Gate/up.
+struct GuStreamParams {
+    int H, I, K, T, Is, act;
+    float b1, b2;
+    const uint8_t *gp, *gs, *up, *us;
+    int64_t g_sp, g_ss, u_sp, u_ss;
+    const uint16_t *sh_gate, *sh_up;
+    const uint16_t *x;
+    const int32_t *active_e, *active_off, *sorted;
+    const int32_t *light, *light_n;
+    int sh_blocks;            // leading blocks that run the shared expert
+    uint16_t *act_hi, *act_lo, *ash_hi, *ash_lo;
+};
+
+constexpr int gu_stream_lds_bytes() { return 2 * kSTok * brow_bytes<true>() + kSTok * 4; }
+
+// The wave's part of one block: gate and up rows row0 + 16 rf + l16 (rf = 0, 1)
+// of an item with token rows tok_l[0..15] (clamped to the item's tokens).
+template <bool FP4>
+__device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const uint8_t *wg, const uint8_t *wu,
+                                                const uint8_t *sg, const uint8_t *su, int rows, int row0,
+                                                const int *tok_l, int n, uint8_t *B_l, uint16_t *ohi,
+                                                uint16_t *olo, int64_t orow0, int ostride)
+{
+    constexpr int GK = group_k<FP4>();
+    constexpr int BROW = brow_bytes<FP4>();
+    constexpr int BU4 = GK * 2 / 16;                           // u4 per token row per group
+    constexpr int NB = (kSTok * BU4 + 64 * kSWaves - 1) / (64 * kSWaves);  // staging u4 per thread
+    const int H = p.H, tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+    const int NG = H / GK;
+    const size_t rowb = FP4 ? (size_t)H / 2 : (size_t)H * 2;
+    const uint8_t *wr[2][2];
+    const uint8_t *sr[2][2] = {{nullptr, nullptr}, {nullptr, nullptr}};
+#pragma unroll
+    for (int rf = 0; rf < 2; ++rf) {
+        const int r = min(row0 + 16 * rf + l16, rows - 1);
+        wr[0][rf] = wg + (size_t)r * rowb + 16 * g;
+        wr[1][rf] = wu + (size_t)r * rowb + 16 * g;
+        if constexpr (FP4) {
+            sr[0][rf] = sg + (size_t)r * (H / 32);
+            sr[1][rf] = su + (size_t)r * (H / 32);
+        }
+    }
+    const uint8_t *xb = reinterpret_cast<const uint8_t *>(p.x);
+
+    struct Grp {
+        u4 a[2][2][kSChunks];  // [mat][rf][chunk]
+        u4 s[2][2];            // FP4: the group's 16 scale bytes per row
+    };
+    auto gload = [&](int gi, Grp &b) {
+        const int gc = min(gi, NG - 1);
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int rf = 0; rf < 2; ++rf) {
+#pragma unroll
+                for (int c = 0; c < kSChunks; ++c)
+                    b.a[m][rf][c] = *reinterpret_cast<const u4 *>(wr[m][rf] + (size_t)gc * (kSChunks * 64) + 64 * c);
+                if constexpr (FP4) b.s[m][rf] = *reinterpret_cast<const u4 *>(sr[m][rf] + 16 * gc);
+            }
+    };
+    u4 xs[NB];
+    auto xload = [&](int gi) {
+        const int gc = min(gi, NG - 1);
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            const int v = min(tid + 64 * kSWaves * q, kSTok * BU4 - 1);
+            const int col = v / BU4, seg = v - col * BU4;
+            xs[q] = *reinterpret_cast<const u4 *>(xb + ((size_t)tok_l[col] * H + (size_t)gc * GK) * 2 + 16 * seg);
+        }
+    };
+    auto xstore = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            const int v = tid + 64 * kSWaves * q;
+            if (v < kSTok * BU4) {
+                const int col = v / BU4, seg = v - col * BU4;
+                *reinterpret_cast<u4 *>(B_l + (buf * kSTok + col) * BROW + 16 * seg) = xs[q];
+            }
+        }
+    };
+
+    v4f acc[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int rf = 0; rf < 2; ++rf) acc[m][rf] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto compute = [&](const Grp &b, int buf) {
+        const uint8_t *Bb = B_l + (buf * kSTok + l16) * BROW;
+#pragma unroll
+        for (int c = 0; c < kSChunks; ++c) {
+            float sc[2][2];
+            if constexpr (FP4) {
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int rf = 0; rf < 2; ++rf) sc[m][rf] = e8m0_scale((b.s[m][rf][c] >> (8 * g)) & 0xffu);
+            }
+            constexpr int SPC = FP4 ? 4 : 1;  // MFMA steps per 16-byte load
+#pragma unroll
+            for (int st = 0; st < SPC; ++st) {
+                const int kb = FP4 ? (128 * c + 32 * g + 8 * st) : (32 * c + 8 * g);
+                const bf8 bv = as_bf8(*reinterpret_cast<const u4 *>(Bb + 2 * kb));
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int rf = 0; rf < 2; ++rf) {
+                        bf8 a;
+                        if constexpr (FP4)
+                            a = dequant8(b.a[m][rf][c][st], sc[m][rf]);
+                        else
+                            a = as_bf8(b.a[m][rf][c]);
+                        acc[m][rf] = mfma_bf16(a, bv, acc[m][rf]);
+                    }
+            }
+        }
+    };
+
+    Grp b0, b1;
+    xload(0);
+    gload(0, b0);
+    xstore(0);
+    __syncthreads();
+    for (int gi = 0; gi < NG; gi += 2) {
+        gload(gi + 1, b1);
+        xload(gi + 1);
+        compute(b0, 0);
+        xstore(1);
+        __syncthreads();
+        if (gi + 1 >= NG) break;
+        gload(gi + 2, b0);
+        xload(gi + 2);
+        compute(b1, 1);
+        xstore(0);
+        __syncthreads();
+    }
+
+    // epilogue: lane holds rows 4g + i (i = 0..3) of token column l16
+    if (l16 < n) {
+#pragma unroll
+        for (int rf = 0; rf < 2; ++rf) {
+            const int row = row0 + 16 * rf + 4 * g;
+            if (row >= rows) continue;
+            uint32_t hi2[2], lo2[2];
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+                const float a0 = act_fn(acc[0][rf][i], acc[1][rf][i], p.act, p.b1, p.b2);
+                const float a1 = act_fn(acc[0][rf][i + 1], acc[1][rf][i + 1], p.act, p.b1, p.b2);
+                const uint16_t h0 = bf16_rne(a0), h1 = bf16_rne(a1);
+                const uint16_t q0 = bf16_rne(a0 - bf16f(h0)), q1 = bf16_rne(a1 - bf16f(h1));
+                hi2[i / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                lo2[i / 2] = (uint32_t)q0 | ((uint32_t)q1 << 16);
+            }
+            const size_t o = (size_t)(orow0 + l16) * ostride + row;
+            *reinterpret_cast<uint2 *>(ohi + o) = uint2{hi2[0], hi2[1]};
+            *reinterpret_cast<uint2 *>(olo + o) = uint2{lo2[0], lo2[1]};
+        }
+    }
+}
+
+__global__ __launch_bounds__(64 * kSWaves) void k_gu_stream(GuStreamParams p)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    int *tok_l = reinterpret_cast<int *>(lds);
+    uint8_t *B_l = lds + kSTok * 4;
+    const int wave = threadIdx.x >> 6;
+    int b = blockIdx.x;
+    if (b < p.sh_blocks) {  // shared expert: token group tg, rows [rb*128, rb*128 + 128) of I_s
+        const int RB = p.Is / kSBlkRows;
+        const int tg = b / RB, rb = b - tg * RB;
+        const int t0 = tg * kSTok, n = min(kSTok, p.T - t0);
+        if (threadIdx.x < kSTok) tok_l[threadIdx.x] = t0 + min((int)threadIdx.x, n - 1);
+        __syncthreads();
+        gu_stream_block<false>(p, reinterpret_cast<const uint8_t *>(p.sh_gate),
+                               reinterpret_cast<const uint8_t *>(p.sh_up), nullptr, nullptr, p.Is,
+                               rb * kSBlkRows + wave * kSRows, tok_l, n, B_l, p.ash_hi, p.ash_lo, t0, p.Is);
+        return;
+    }
+    b -= p.sh_blocks;
+    const int RB = p.I / kSBlkRows;
+    const int li = b / RB, rb = b - li * RB;
+    if (li >= *p.light_n) return;
+    const int q = p.light[li], e = p.active_e[q];
+    const int off = p.active_off[q], n = p.active_off[q + 1] - off;
+    if (threadIdx.x < kSTok) tok_l[threadIdx.x] = p.sorted[off + min((int)threadIdx.x, n - 1)] / p.K;
+    __syncthreads();
+    gu_stream_block<true>(p, p.gp + e * p.g_sp, p.up + e * p.u_sp, p.gs + e * p.g_ss, p.us + e * p.u_ss, p.I,
+                          rb * kSBlkRows + wave * kSRows, tok_l, n, B_l, p.act_hi, p.act_lo, off, p.I);
+}
+
+// ---------------------------------------------------------------------------
+// Down: rows of H; the activation fed as bf16 hi and lo (two MFMAs into one
+// accumulator); outputs to the staging rows ys[t][j] (shared: ys[t][k]).
+struct DnStreamParams {
+    int H, I, K, T, Is;
+    const uint8_t *dp, *ds;
+    int64_t d_sp, d_ss;
+    const uint16_t *sh_down;
+    const uint16_t *act_hi, *act_lo, *ash_hi, *ash_lo;
+    const int32_t *active_e, *active_off, *sorted;
+    const int32_t *light, *light_n;
+    int sh_blocks;
+    float *ys;
+};
+
+constexpr int dn_stream_lds_bytes() { return 2 * 2 * kSTok * brow_bytes<true>() + kSTok * 8; }
+
+template <bool FP4>
+__device__ __forceinline__ void dn_stream_block(const DnStreamParams &p, const uint8_t *wd, const uint8_t *sd,
+                                                int KD, int row0, const int *arow_l, const int *orow_l, int n,
+                                                const uint16_t *ahi, const uint16_t *alo, uint8_t *B_l)
+{
+    constexpr int GK = group_k<FP4>();
+    constexpr int BROW = brow_bytes<FP4>();
+    constexpr int BU4 = GK * 2 / 16;
+    constexpr int NB = (2 * kSTok * BU4 + 64 * kSWaves - 1) / (64 * kSWaves);
+    const int H = p.H, tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+    const int NG = KD / GK;
+    const size_t rowb = FP4 ? (size_t)KD / 2 : (size_t)KD * 2;
+    const uint8_t *wr[2];
+    const uint8_t *sr[2] = {nullptr, nullptr};
+#pragma unroll
+    for (int rf = 0; rf < 2; ++rf) {
+        const int r = min(row0 + 16 * rf + l16, H - 1);
+        wr[rf] = wd + (size_t)r * rowb + 16 * g;
+        if constexpr (FP4) sr[rf] = sd + (size_t)r * (KD / 32);
+    }
+    const uint8_t *hb = reinterpret_cast<const uint8_t *>(ahi);
+    const uint8_t *lb = reinterpret_cast<const uint8_t *>(alo);
+
+    struct Grp {
+        u4 a[2][kSChunks];
+        u4 s[2];
+    };
+    auto gload = [&](int gi, Grp &b) {
+        const int gc = min(gi, NG - 1);
+#pragma unroll
+        for (int rf = 0; rf < 2; ++rf) {
+#pragma unroll
+            for (int c = 0; c < kSChunks; ++c)
+                b.a[rf][c] = *reinterpret_cast<const u4 *>(wr[rf] + (size_t)gc * (kSChunks * 64) + 64 * c);
+            if constexpr (FP4) b.s[rf] = *reinterpret_cast<const u4 *>(sr[rf] + 16 * gc);
+        }
+    };
+    u4 xs[NB];
+    auto xload = [&](int gi) {
+        const int gc = min(gi, NG - 1);
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            const int v = min(tid + 64 * kSWaves * q, 2 * kSTok * BU4 - 1);
+            const int half = v / (kSTok * BU4), vv = v - half * (kSTok * BU4);
+            const int col = vv / BU4, seg = vv - col * BU4;
+            const uint8_t *src = half ? lb : hb;
+            xs[q] = *reinterpret_cast<const u4 *>(src + ((size_t)arow_l[col] * KD + (size_t)gc * GK) * 2 + 16 * seg);
+        }
+    };
+    auto xstore = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            const int v = tid + 64 * kSWaves * q;
+            if (v < 2 * kSTok * BU4) {
+                const int half = v / (kSTok * BU4), vv = v - half * (kSTok * BU4);
+                const int col = vv / BU4, seg = vv - col * BU4;
+                *reinterpret_cast<u4 *>(B_l + ((buf * 2 + half) * kSTok + col) * BROW + 16 * seg) = xs[q];
+            }
+        }
+    };
+
+    v4f acc[2] = {v4f{0.0f, 0.0f, 0.0f, 0.0f}, v4f{0.0f, 0.0f, 0.0f, 0.0f}};
+    auto compute = [&](const Grp &b, int buf) {
+        const uint8_t *Bh = B_l + ((buf * 2) * kSTok + l16) * BROW;
+        const uint8_t *Bl = B_l + ((buf * 2 + 1) * kSTok + l16) * BROW;
+#pragma unroll
+        for (int c = 0; c < kSChunks; ++c) {
+            float sc[2];
+            if constexpr (FP4) {
+#pragma unroll
+                for (int rf = 0; rf < 2; ++rf) sc[rf] = e8m0_scale((b.s[rf][c] >> (8 * g)) & 0xffu);
+            }
+            constexpr int SPC = FP4 ? 4 : 1;
+#pragma unroll
+            for (int st = 0; st < SPC; ++st) {
+                const int kb = FP4 ? (128 * c + 32 * g + 8 * st) : (32 * c + 8 * g);
+                const bf8 bh = as_bf8(*reinterpret_cast<const u4 *>(Bh + 2 * kb));
+                const bf8 bl = as_bf8(*reinterpret_cast<const u4 *>(Bl + 2 * kb));
+#pragma unroll
+                for (int rf = 0; rf < 2; ++rf) {
+                    bf8 a;
+                    if constexpr (FP4)
+                        a = dequant8(b.a[rf][c][st], sc[rf]);
+                    else
+                        a = as_bf8(b.a[rf][c]);
+                    acc[rf] = mfma_bf16(a, bh, acc[rf]);
+                    acc[rf] = mfma_bf16(a, bl, acc[rf]);
+                }
+            }
+        }
+    };
+
+    Grp b0, b1;
+    xload(0);
+    gload(0, b0);
+    xstore(0);
+    __syncthreads();
+    for (int gi = 0; gi < NG; gi += 2) {
+        gload(gi + 1, b1);
+        xload(gi + 1);
+        compute(b0, 0);
+        xstore(1);
+        __syncthreads();
+        if (gi + 1 >= NG) break;
+        gload(gi + 2, b0);
+        xload(gi + 2);
+        compute(b1, 1);
+        xstore(0);
+        __syncthreads();
+    }
+
+    if (l16 < n) {
+        float *yr = p.ys + (size_t)orow_l[l16] * H;
+#pragma unroll
+        for (int rf = 0; rf < 2; ++rf) {
+            const int row = row0 + 16 * rf + 4 * g;
+            if (row < H) *reinterpret_cast<float4 *>(yr + row) = float4{acc[rf][0], acc[rf][1], acc[rf][2], acc[rf][3]};
+        }
+    }
+}
+
+__global__ __launch_bounds__(64 * kSWaves) void k_dn_stream(DnStreamParams p)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    int *arow_l = reinterpret_cast<int *>(lds);
+    int *orow_l = arow_l + kSTok;
+    uint8_t *B_l = lds + kSTok * 8;
+    const int wave = threadIdx.x >> 6;
+    const int RB = p.H / kSBlkRows;
+    int b = blockIdx.x;
+    if (b < p.sh_blocks) {
+        const int tg = b / RB, rb = b - tg * RB;
+        const int t0 = tg * kSTok, n = min(kSTok, p.T - t0);
+        if (threadIdx.x < kSTok) {
+            const int t = t0 + min((int)threadIdx.x, n - 1);
+            arow_l[threadIdx.x] = t;
+            orow_l[threadIdx.x] = t * (p.K + 1) + p.K;
+        }
+        __syncthreads();
+        dn_stream_block<false>(p, reinterpret_cast<const uint8_t *>(p.sh_down), nullptr, p.Is,
+                               rb * kSBlkRows + wave * kSRows, arow_l, orow_l, n, p.ash_hi, p.ash_lo, B_l);
+        return;
+    }
+    b -= p.sh_blocks;
+    const int li = b / RB, rb = b - li * RB;
+    if (li >= *p.light_n) return;
+    const int q = p.light[li], e = p.active_e[q];
+    const int off = p.active_off[q], n = p.active_off[q + 1] - off;
+    if (threadIdx.x < kSTok) {
+        const int c = min((int)threadIdx.x, n - 1);
+        const int a = p.sorted[off + c];
+        arow_l[threadIdx.x] = off + c;
+        orow_l[threadIdx.x] = (a / p.K) * (p.K + 1) + a % p.K;
+    }
+    __syncthreads();
+    dn_stream_block<true>(p, p.dp + e * p.d_sp, p.ds + e * p.d_ss, p.I, rb * kSBlkRows + wave * kSRows, arow_l,
+                          orow_l, n, p.act_hi, p.act_lo, B_l);
+}
+
+}  // namespace
+
+bool stream_path_ok(const LayerView &L)
+{
+    return L.H % group_k<true>() == 0 && L.I % group_k<true>() == 0 && L.I % kSBlkRows == 0 &&
+           L.H % kSBlkRows == 0 && L.Is % kSBlkRows == 0;
+}
+
+int stream_max_tokens() { return kSTok; }
+
+bool stream_shared_ok(const LayerView &L, int T) { return L.Is > 0 && T <= 8 * kSTok; }
+
+hipError_t launch_stream_gu(const LayerView &L, const uint16_t *x, int T, const int32_t *active_e,
+                            const int32_t *active_off, const int32_t *sorted, const int32_t *light,
+                            const int32_t *light_n, bool with_shared, uint16_t *act_hi, uint16_t *act_lo,
+                            uint16_t *ash_hi, uint16_t *ash_lo, hipStream_t s)
+{
+    GuStreamParams p{};
+    p.H = L.H;
+    p.I = L.I;
+    p.K = L.K;
+    p.T = T;
+    p.Is = L.Is;
+    p.act = L.act;
+    p.b1 = L.b1;
+    p.b2 = L.b2;
+    p.gp = L.gp;
+    p.gs = L.gs;
+    p.up = L.up;
+    p.us = L.us;
+    p.g_sp = L.g_sp;
+    p.g_ss = L.g_ss;
+    p.u_sp = L.u_sp;
+    p.u_ss = L.u_ss;
+    p.sh_gate = L.sh_gate;
+    p.sh_up = L.sh_up;
+    p.x = x;
+    p.active_e = active_e;
+    p.active_off = active_off;
+    p.sorted = sorted;
+    p.light = light;
+    p.light_n = light_n;
+    p.sh_blocks = with_shared ? ((T + kSTok - 1) / kSTok) * (L.Is / kSBlkRows) : 0;
+    p.act_hi = act_hi;
+    p.act_lo = act_lo;
+    p.ash_hi = ash_hi;
+    p.ash_lo = ash_lo;
+    const int64_t cap = std::min<int64_t>(L.E, (int64_t)T * L.K);
+    const unsigned nblk = (unsigned)(p.sh_blocks + cap * (L.I / kSBlkRows));
+    k_gu_stream<<<nblk, 64 * kSWaves, gu_stream_lds_bytes(), s>>>(p);
+    return hipGetLastError();
+}
+
+hipError_t launch_stream_dn(const LayerView &L, int T, const int32_t *active_e, const int32_t *active_off,
+                            const int32_t *sorted, const int32_t *light, const int32_t *light_n,
+                            bool with_shared, const uint16_t *act_hi, const uint16_t *act_lo,
+                            const uint16_t *ash_hi, const uint16_t *ash_lo, float *ys, hipStream_t s)
+{
+    DnStreamParams p{};
+    p.H = L.H;
+    p.I = L.I;
+    p.K = L.K;
+    p.T = T;
+    p.Is = L.Is;
+    p.dp = L.dp;
+    p.ds = L.ds;
+    p.d_sp = L.d_sp;
+    p.d_ss = L.d_ss;
+    p.sh_down = L.sh_down;
+    p.act_hi = act_hi;
+    p.act_lo = act_lo;
+    p.ash_hi = ash_hi;
+    p.ash_lo = ash_lo;
+    p.active_e = active_e;
+    p.active_off = active_off;
+    p.sorted = sorted;
+    p.light = light;
+    p.light_n = light_n;
+    p.sh_blocks = with_shared ? ((T + kSTok - 1) / kSTok) * (L.H / kSBlkRows) : 0;
+    p.ys = ys;
+    const int64_t cap = std::min<int64_t>(L.E, (int64_t)T * L.K);
+    const unsigned nblk = (unsigned)(p.sh_blocks + cap * (L.H / kSBlkRows));
+    k_dn_stream<<<nblk, 64 * kSWaves, dn_stream_lds_bytes(), s>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace k3moe

@@ -188,6 +188,57 @@ def test_tiny_bad_ids_are_counted():
     assert np.array_equal(out_bad, _forward_gpu(layer, x, idx_r, w0))
 
 
+# --------------------------------------------------------------------------
+# Mid-size layer (hidden 512, inter 512, 16 experts, top-4, shared 256): the
+# sizes that take the weight-streaming kernels for experts with at most 16
+# tokens and the grouped GEMMs for the rest; the shared expert streams for
+# batches up to 128 tokens and runs as a GEMM above that.
+
+def _mid(seed, routing="normal", T_bad=False):
+    spec = synth.LayerSpec(hidden=512, inter=512, n_experts=16, topk=4, shared_inter=256,
+                           bias_std=0.05, routing=routing, seed=seed)
+    sd = _dev()
+    t = sd.layer_tensors(spec, 0, DEV)
+    return spec, t, sd.make_layer(spec, t)
+
+
+@pytest.mark.parametrize("T,routing", [(2, "normal"), (5, "normal"), (17, "normal"), (40, "normal"),
+                                       (128, "normal"), (129, "zipf"), (300, "zipf")])
+def test_mid_stream_and_gemm_mix(T, routing):
+    spec, t, layer = _mid(seed=20 + T, routing=routing)
+    Wr, bias = synth.make_router(spec), synth.make_bias(spec)
+    x_np = synth.make_x(spec, T)
+    idx_r, w_r, logits, ch = oracle.route(x_np, Wr, bias, spec.topk, want_detail=True)
+    x, idx, w, _ = _route_gpu(layer, x_np, T, spec.topk)
+    check_route(idx.cpu().numpy(), w.cpu().numpy(), idx_r, w_r, ch, spec.topk)
+    counts = np.bincount(idx_r.ravel(), minlength=spec.n_experts)
+    if T >= 129:
+        assert counts.max() > 16 and 0 < counts[counts > 0].min() <= 16  # both kernel kinds run
+    out = _forward_gpu(layer, x, idx_r, w_r)
+    ref, denom, _ = oracle_forward(spec, x_np, idx_r, w_r)
+    assert rel_err(out, ref, denom) <= REL_TOL
+    # deterministic: a second call gives the same bits
+    assert np.array_equal(out, _forward_gpu(layer, x, idx_r, w_r))
+
+
+def test_mid_bad_ids_are_counted():
+    spec, t, layer = _mid(seed=40)
+    T = 24
+    x_np = synth.make_x(spec, T)
+    idx_r, w_r = oracle.route(x_np, synth.make_router(spec), synth.make_bias(spec), spec.topk)
+    x = _x_dev(x_np)
+    bad = idx_r.copy()
+    bad[0, 1] = -1
+    bad[5, 0] = spec.n_experts
+    bad[23, 3] = 1 << 30
+    layer.error_reset()
+    out_bad = _forward_gpu(layer, x, bad, w_r)
+    assert layer.error_count() == 3
+    ref, denom, drops = oracle_forward(spec, x_np, bad, w_r)
+    assert drops == 3
+    assert rel_err(out_bad, ref, denom) <= REL_TOL
+
+
 def test_empty_batch_is_a_no_op():
     spec, t, layer = _tiny(seed=6)
     x = torch.empty((0, spec.hidden), dtype=torch.bfloat16, device=DEV)
