@@ -88,47 +88,47 @@ __device__ __forceinline__ float act_fn(float g, float u, int kind, float b1, fl
 
 // ---------------------------------------------------------------------------
 // Work lists. Active expert q (ascending id) with n_q assignments goes to the
-// weight-streaming kernels when n_q <= smax (light[] lists such q in order),
-// else gets ceil(n_q / BN) GEMM tiles; tiles[i] = (q, token block).
-// counts: [0] gate/up tiles, [1] down tiles, [2] light experts.
+// gate/up weight-streaming kernel when n_q <= smax_gu (light_gu[] lists such
+// q in order), else gets ceil(n_q / bn_gu) GEMM tiles (q, token block); the
+// same for the down projection with smax_dn, bn_dn.
+// counts: [0] gate/up tiles, [1] down tiles, [2] gate/up light, [3] down light.
 __global__ __launch_bounds__(1024) void k_tiles(const int32_t *__restrict__ active_n,
                                                 const int32_t *__restrict__ active_off, int bn_gu,
-                                                int bn_dn, int smax, int2 *__restrict__ tiles_gu,
-                                                int2 *__restrict__ tiles_dn, int32_t *__restrict__ light,
+                                                int bn_dn, int smax_gu, int smax_dn,
+                                                int2 *__restrict__ tiles_gu, int2 *__restrict__ tiles_dn,
+                                                int32_t *__restrict__ light_gu, int32_t *__restrict__ light_dn,
                                                 int32_t *counts)
 {
-    __shared__ int wsum[3][16];
+    __shared__ int wsum[4][16];
     const int n = *active_n;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int per = (n + 1023) / 1024;
     const int q0 = tid * per;
-    int cnt[3] = {0, 0, 0};
+    int cnt[4] = {0, 0, 0, 0};
     for (int i = 0; i < per; ++i) {
         const int q = q0 + i;
         if (q < n) {
             const int m = active_off[q + 1] - active_off[q];
-            if (m <= smax) {
-                cnt[2] += 1;
-            } else {
-                cnt[0] += (m + bn_gu - 1) / bn_gu;
-                cnt[1] += (m + bn_dn - 1) / bn_dn;
-            }
+            if (m <= smax_gu) cnt[2] += 1;
+            else cnt[0] += (m + bn_gu - 1) / bn_gu;
+            if (m <= smax_dn) cnt[3] += 1;
+            else cnt[1] += (m + bn_dn - 1) / bn_dn;
         }
     }
-    int inc[3] = {cnt[0], cnt[1], cnt[2]};  // inclusive scans across the wave
+    int inc[4] = {cnt[0], cnt[1], cnt[2], cnt[3]};  // inclusive scans across the wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
+        for (int k = 0; k < 4; ++k) {
             const int a = __shfl_up(inc[k], o);
             if (lane >= o) inc[k] += a;
         }
     }
     if (lane == 63)
-        for (int k = 0; k < 3; ++k) wsum[k][wv] = inc[k];
+        for (int k = 0; k < 4; ++k) wsum[k][wv] = inc[k];
     __syncthreads();
     if (tid == 0) {
-        for (int k = 0; k < 3; ++k) {
+        for (int k = 0; k < 4; ++k) {
             int r = 0;
             for (int w = 0; w < 16; ++w) {
                 const int a = wsum[k][w];
@@ -140,17 +140,17 @@ __global__ __launch_bounds__(1024) void k_tiles(const int32_t *__restrict__ acti
     }
     __syncthreads();
     int bg = wsum[0][wv] + inc[0] - cnt[0], bd = wsum[1][wv] + inc[1] - cnt[1];
-    int bl = wsum[2][wv] + inc[2] - cnt[2];
+    int lg = wsum[2][wv] + inc[2] - cnt[2], ld = wsum[3][wv] + inc[3] - cnt[3];
     for (int i = 0; i < per; ++i) {
         const int q = q0 + i;
         if (q < n) {
             const int m = active_off[q + 1] - active_off[q];
-            if (m <= smax) {
-                light[bl++] = q;
-            } else {
+            if (m <= smax_gu) light_gu[lg++] = q;
+            else
                 for (int tb = 0; tb * bn_gu < m; ++tb) tiles_gu[bg++] = int2{q, tb};
+            if (m <= smax_dn) light_dn[ld++] = q;
+            else
                 for (int tb = 0; tb * bn_dn < m; ++tb) tiles_dn[bd++] = int2{q, tb};
-            }
         }
     }
 }
@@ -591,10 +591,11 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const in
     const size_t cap_gu = grouped_tile_cap(T, L.K, L.E, kGuTok), cap_dn = grouped_tile_cap(T, L.K, L.E, kDnTok);
     const int rb_i = (L.I + kGRows - 1) / kGRows, rb_h = (L.H + kGRows - 1) / kGRows;
     const int rb_s = (L.Is + kGRows - 1) / kGRows;
-    const bool stream = stream_path_ok(L);
-    const bool sh_stream = stream && stream_shared_ok(L, T);
-    k_tiles<<<1, 1024, 0, s>>>(active_n, active_off, kGuTok, kDnTok, stream ? stream_max_tokens() : 0, tiles_gu,
-                               tiles_dn, light, counts);
+    const bool stream = stream_path_ok(L), stream_dn = stream_down_ok(L);
+    const bool sh_stream = stream_shared_ok(L, T);
+    int32_t *light_gu = light, *light_dn = light + L.E;
+    k_tiles<<<1, 1024, 0, s>>>(active_n, active_off, kGuTok, kDnTok, stream ? stream_max_tokens() : 0,
+                               stream_dn ? stream_max_tokens() : 0, tiles_gu, tiles_dn, light_gu, light_dn, counts);
 
     GuGemmParams gp{};
     gp.H = L.H;
@@ -623,8 +624,8 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const in
     {
         StageMark m(prof, K3MOE_STAGE_GATEUP, s);
         if (stream) {
-            const hipError_t e = launch_stream_gu(L, x, T, active_e, active_off, sorted, light, counts + 2, sh_stream,
-                                                  act_hi, act_lo, ash_hi, ash_lo, s);
+            const hipError_t e = launch_stream_gu(L, x, T, active_e, active_off, sorted, light_gu, counts + 2,
+                                                  sh_stream, act_hi, act_lo, ash_hi, ash_lo, s);
             if (e != hipSuccess) return e;
         }
         const unsigned nblk = (unsigned)(cap_gu * rb_i);
@@ -661,9 +662,9 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const in
     dp.ys = ys;
     {
         StageMark m(prof, K3MOE_STAGE_DOWN, s);
-        if (stream) {
-            const hipError_t e = launch_stream_dn(L, T, active_e, active_off, sorted, light, counts + 2, sh_stream,
-                                                  act_hi, act_lo, ash_hi, ash_lo, ys, s);
+        if (stream_dn) {
+            const hipError_t e = launch_stream_dn(L, T, active_e, active_off, sorted, light_dn, counts + 3,
+                                                  sh_stream, act_hi, act_lo, ash_hi, ash_lo, ys, s);
             if (e != hipSuccess) return e;
         }
         const unsigned nblk = (unsigned)(cap_dn * rb_h);

@@ -37,8 +37,8 @@ struct WsLayout {
     size_t ash;               // shared activations, 4 bytes per element [T][I_s], same forms
     size_t ys;                // expert outputs fp32 [T][k + 1][H] (slot k: shared expert)
     size_t tiles_gu, tiles_dn;  // grouped-GEMM tile lists, int2 each
-    size_t light;             // int32 [E]: experts for the weight-streaming kernels
-    size_t tile_n;            // int32 [3]: gate/up tiles, down tiles, light experts
+    size_t light;             // int32 [2][E]: experts for the weight-streaming kernels (gate/up, down)
+    size_t tile_n;            // int32 [4]: gate/up tiles, down tiles, light gate/up, light down
     size_t total;
 };
 
@@ -126,6 +126,7 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const in
 
 // Weight-streaming kernels for experts with few tokens (k3moe_stream.hip).
 bool stream_path_ok(const LayerView &L);
+bool stream_down_ok(const LayerView &L);
 int stream_max_tokens();
 bool stream_shared_ok(const LayerView &L, int T);
 hipError_t launch_stream_gu(const LayerView &L, const uint16_t *x, int T, const int32_t *active_e,

@@ -24,9 +24,9 @@
 // expert) a 16-byte load is 8 values, one step: chunk c covers K = 32c + 8g +
 // [0, 8).
 //
-// The same launch also runs the shared expert for small batches: its blocks
-// come first in the grid (token groups of 16 x 128-row blocks, bf16 weights),
-// so they stream alongside the routed blocks.
+// The same launches also run the shared expert for small batches: its blocks
+// come first in the grid (token groups of 16, bf16 weights), so they stream
+// alongside the routed blocks.
 #include "k3moe_internal.h"
 
 namespace k3moe {
@@ -88,15 +88,6 @@ __device__ __forceinline__ float act_fn(float g, float u, int kind, float b1, fl
 // K elements per group and token-row bytes per group.
 template <bool FP4> constexpr int group_k() { return FP4 ? 128 * kSChunks : 8 * 4 * kSChunks; }
 template <bool FP4> constexpr int brow_bytes() { return group_k<FP4>() * 2 + kSPad; }
-
-// One stream item as a wave sees it.
-struct Item {
-    int n;          // tokens (1..16)
-    int rows;       // weight rows of the matrix (I or H)
-    int row0;       // first row of this wave
-    const uint8_t *w[2];   // weight row bases (gate/up, or down twice)
-    const uint8_t *s[2];   // FP4: scale row bases
-};
 
 // ---------------------------------------------------------------------------
 // Gate/up.
@@ -293,6 +284,14 @@ __global__ __launch_bounds__(64 * kSWaves) void k_gu_stream(GuStreamParams p)
 // ---------------------------------------------------------------------------
 // Down: rows of H; the activation fed as bf16 hi and lo (two MFMAs into one
 // accumulator); outputs to the staging rows ys[t][j] (shared: ys[t][k]).
+// A block of 8 waves stages the item's activation planes for the whole K
+// range in LDS once (16 tokens x I x hi/lo), then walks a run of 256-row
+// blocks of H; each wave streams its 32 rows per row block, its weight loads
+// running one K group ahead across row-block boundaries, with no further
+// barriers.
+constexpr int kDWaves = 8;
+constexpr int kDBlkRows = kDWaves * kSRows;  // 256
+
 struct DnStreamParams {
     int H, I, K, T, Is;
     const uint8_t *dp, *ds;
@@ -301,77 +300,60 @@ struct DnStreamParams {
     const uint16_t *act_hi, *act_lo, *ash_hi, *ash_lo;
     const int32_t *active_e, *active_off, *sorted;
     const int32_t *light, *light_n;
-    int sh_blocks;
+    int sh_items;             // leading items that run the shared expert (token groups)
+    int runs, run_rb;         // blocks per item, 256-row blocks per block
     float *ys;
 };
 
-constexpr int dn_stream_lds_bytes() { return 2 * 2 * kSTok * brow_bytes<true>() + kSTok * 8; }
+__host__ __device__ constexpr int dn_stream_lds_bytes(int KD) { return 2 * kSTok * (2 * KD + kSPad) + kSTok * 8; }
 
 template <bool FP4>
-__device__ __forceinline__ void dn_stream_block(const DnStreamParams &p, const uint8_t *wd, const uint8_t *sd,
-                                                int KD, int row0, const int *arow_l, const int *orow_l, int n,
-                                                const uint16_t *ahi, const uint16_t *alo, uint8_t *B_l)
+__device__ __forceinline__ void dn_stream_run(const DnStreamParams &p, const uint8_t *wd, const uint8_t *sd, int KD,
+                                              int rb0, int rb1, const int *arow_l, const int *orow_l, int n,
+                                              const uint16_t *ahi, const uint16_t *alo, uint8_t *B_l)
 {
     constexpr int GK = group_k<FP4>();
-    constexpr int BROW = brow_bytes<FP4>();
-    constexpr int BU4 = GK * 2 / 16;
-    constexpr int NB = (2 * kSTok * BU4 + 64 * kSWaves - 1) / (64 * kSWaves);
-    const int H = p.H, tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
-    const int NG = KD / GK;
+    const int BROW = 2 * KD + kSPad;
+    const int H = p.H, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+    const int NG = KD / GK, total = (rb1 - rb0) * NG;
     const size_t rowb = FP4 ? (size_t)KD / 2 : (size_t)KD * 2;
-    const uint8_t *wr[2];
-    const uint8_t *sr[2] = {nullptr, nullptr};
-#pragma unroll
-    for (int rf = 0; rf < 2; ++rf) {
-        const int r = min(row0 + 16 * rf + l16, H - 1);
-        wr[rf] = wd + (size_t)r * rowb + 16 * g;
-        if constexpr (FP4) sr[rf] = sd + (size_t)r * (KD / 32);
+
+    // stage both activation planes of the item's tokens, whole K range
+    {
+        const int ru4 = KD * 2 / 16;  // u4 per token row
+        for (int v = tid; v < 2 * kSTok * ru4; v += 64 * kDWaves) {
+            const int half = v / (kSTok * ru4), vv = v - half * (kSTok * ru4);
+            const int col = vv / ru4, seg = vv - col * ru4;
+            const uint16_t *src = half ? alo : ahi;
+            *reinterpret_cast<u4 *>(B_l + (half * kSTok + col) * BROW + 16 * seg) =
+                *reinterpret_cast<const u4 *>(src + (size_t)arow_l[col] * KD + 8 * seg);
+        }
     }
-    const uint8_t *hb = reinterpret_cast<const uint8_t *>(ahi);
-    const uint8_t *lb = reinterpret_cast<const uint8_t *>(alo);
+    __syncthreads();
 
     struct Grp {
         u4 a[2][kSChunks];
         u4 s[2];
     };
-    auto gload = [&](int gi, Grp &b) {
-        const int gc = min(gi, NG - 1);
+    auto gload = [&](int it, Grp &b) {
+        const int ic = min(it, total - 1);
+        const int rb = rb0 + ic / NG, gi = ic - (ic / NG) * NG;
 #pragma unroll
         for (int rf = 0; rf < 2; ++rf) {
+            const int r = min(rb * kDBlkRows + wave * kSRows + 16 * rf + l16, H - 1);
+            const uint8_t *w = wd + (size_t)r * rowb + 16 * g + (size_t)gi * (kSChunks * 64);
 #pragma unroll
-            for (int c = 0; c < kSChunks; ++c)
-                b.a[rf][c] = *reinterpret_cast<const u4 *>(wr[rf] + (size_t)gc * (kSChunks * 64) + 64 * c);
-            if constexpr (FP4) b.s[rf] = *reinterpret_cast<const u4 *>(sr[rf] + 16 * gc);
-        }
-    };
-    u4 xs[NB];
-    auto xload = [&](int gi) {
-        const int gc = min(gi, NG - 1);
-#pragma unroll
-        for (int q = 0; q < NB; ++q) {
-            const int v = min(tid + 64 * kSWaves * q, 2 * kSTok * BU4 - 1);
-            const int half = v / (kSTok * BU4), vv = v - half * (kSTok * BU4);
-            const int col = vv / BU4, seg = vv - col * BU4;
-            const uint8_t *src = half ? lb : hb;
-            xs[q] = *reinterpret_cast<const u4 *>(src + ((size_t)arow_l[col] * KD + (size_t)gc * GK) * 2 + 16 * seg);
-        }
-    };
-    auto xstore = [&](int buf) {
-#pragma unroll
-        for (int q = 0; q < NB; ++q) {
-            const int v = tid + 64 * kSWaves * q;
-            if (v < 2 * kSTok * BU4) {
-                const int half = v / (kSTok * BU4), vv = v - half * (kSTok * BU4);
-                const int col = vv / BU4, seg = vv - col * BU4;
-                *reinterpret_cast<u4 *>(B_l + ((buf * 2 + half) * kSTok + col) * BROW + 16 * seg) = xs[q];
-            }
+            for (int c = 0; c < kSChunks; ++c) b.a[rf][c] = *reinterpret_cast<const u4 *>(w + 64 * c);
+            if constexpr (FP4) b.s[rf] = *reinterpret_cast<const u4 *>(sd + (size_t)r * (KD / 32) + 16 * gi);
         }
     };
 
     v4f acc[2] = {v4f{0.0f, 0.0f, 0.0f, 0.0f}, v4f{0.0f, 0.0f, 0.0f, 0.0f}};
-    auto compute = [&](const Grp &b, int buf) {
-        const uint8_t *Bh = B_l + ((buf * 2) * kSTok + l16) * BROW;
-        const uint8_t *Bl = B_l + ((buf * 2 + 1) * kSTok + l16) * BROW;
+    const uint8_t *Bh = B_l + l16 * BROW;
+    const uint8_t *Bl = B_l + (kSTok + l16) * BROW;
+    auto compute = [&](const Grp &b, int it) {
+        const int rb = rb0 + it / NG, gi = it - (it / NG) * NG;
+        const int kg = gi * GK;
 #pragma unroll
         for (int c = 0; c < kSChunks; ++c) {
             float sc[2];
@@ -382,7 +364,7 @@ __device__ __forceinline__ void dn_stream_block(const DnStreamParams &p, const u
             constexpr int SPC = FP4 ? 4 : 1;
 #pragma unroll
             for (int st = 0; st < SPC; ++st) {
-                const int kb = FP4 ? (128 * c + 32 * g + 8 * st) : (32 * c + 8 * g);
+                const int kb = kg + (FP4 ? (128 * c + 32 * g + 8 * st) : (32 * c + 8 * g));
                 const bf8 bh = as_bf8(*reinterpret_cast<const u4 *>(Bh + 2 * kb));
                 const bf8 bl = as_bf8(*reinterpret_cast<const u4 *>(Bl + 2 * kb));
 #pragma unroll
@@ -397,61 +379,54 @@ __device__ __forceinline__ void dn_stream_block(const DnStreamParams &p, const u
                 }
             }
         }
+        if (gi == NG - 1) {  // row block done: lane holds rows 4g + i of token column l16
+            if (l16 < n) {
+                float *yr = p.ys + (size_t)orow_l[l16] * H;
+#pragma unroll
+                for (int rf = 0; rf < 2; ++rf) {
+                    const int row = rb * kDBlkRows + wave * kSRows + 16 * rf + 4 * g;
+                    if (row < H)
+                        *reinterpret_cast<float4 *>(yr + row) = float4{acc[rf][0], acc[rf][1], acc[rf][2], acc[rf][3]};
+                }
+            }
+            acc[0] = acc[1] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        }
     };
 
     Grp b0, b1;
-    xload(0);
     gload(0, b0);
-    xstore(0);
-    __syncthreads();
-    for (int gi = 0; gi < NG; gi += 2) {
-        gload(gi + 1, b1);
-        xload(gi + 1);
-        compute(b0, 0);
-        xstore(1);
-        __syncthreads();
-        if (gi + 1 >= NG) break;
-        gload(gi + 2, b0);
-        xload(gi + 2);
-        compute(b1, 1);
-        xstore(0);
-        __syncthreads();
-    }
-
-    if (l16 < n) {
-        float *yr = p.ys + (size_t)orow_l[l16] * H;
-#pragma unroll
-        for (int rf = 0; rf < 2; ++rf) {
-            const int row = row0 + 16 * rf + 4 * g;
-            if (row < H) *reinterpret_cast<float4 *>(yr + row) = float4{acc[rf][0], acc[rf][1], acc[rf][2], acc[rf][3]};
-        }
+    for (int it = 0; it < total; it += 2) {
+        gload(it + 1, b1);
+        compute(b0, it);
+        if (it + 1 >= total) break;
+        gload(it + 2, b0);
+        compute(b1, it + 1);
     }
 }
 
-__global__ __launch_bounds__(64 * kSWaves) void k_dn_stream(DnStreamParams p)
+__global__ __launch_bounds__(64 * kDWaves) void k_dn_stream(DnStreamParams p)
 {
     extern __shared__ __align__(16) uint8_t lds[];
     int *arow_l = reinterpret_cast<int *>(lds);
     int *orow_l = arow_l + kSTok;
     uint8_t *B_l = lds + kSTok * 8;
-    const int wave = threadIdx.x >> 6;
-    const int RB = p.H / kSBlkRows;
-    int b = blockIdx.x;
-    if (b < p.sh_blocks) {
-        const int tg = b / RB, rb = b - tg * RB;
-        const int t0 = tg * kSTok, n = min(kSTok, p.T - t0);
+    const int RBT = (p.H + kDBlkRows - 1) / kDBlkRows;
+    const int item = blockIdx.x / p.runs, run = blockIdx.x - item * p.runs;
+    const int rb0 = run * p.run_rb, rb1 = min(RBT, rb0 + p.run_rb);
+    if (rb0 >= rb1) return;
+    if (item < p.sh_items) {  // shared expert, token group `item`
+        const int t0 = item * kSTok, n = min(kSTok, p.T - t0);
         if (threadIdx.x < kSTok) {
             const int t = t0 + min((int)threadIdx.x, n - 1);
             arow_l[threadIdx.x] = t;
             orow_l[threadIdx.x] = t * (p.K + 1) + p.K;
         }
         __syncthreads();
-        dn_stream_block<false>(p, reinterpret_cast<const uint8_t *>(p.sh_down), nullptr, p.Is,
-                               rb * kSBlkRows + wave * kSRows, arow_l, orow_l, n, p.ash_hi, p.ash_lo, B_l);
+        dn_stream_run<false>(p, reinterpret_cast<const uint8_t *>(p.sh_down), nullptr, p.Is, rb0, rb1, arow_l,
+                             orow_l, n, p.ash_hi, p.ash_lo, B_l);
         return;
     }
-    b -= p.sh_blocks;
-    const int li = b / RB, rb = b - li * RB;
+    const int li = item - p.sh_items;
     if (li >= *p.light_n) return;
     const int q = p.light[li], e = p.active_e[q];
     const int off = p.active_off[q], n = p.active_off[q + 1] - off;
@@ -462,8 +437,8 @@ __global__ __launch_bounds__(64 * kSWaves) void k_dn_stream(DnStreamParams p)
         orow_l[threadIdx.x] = (a / p.K) * (p.K + 1) + a % p.K;
     }
     __syncthreads();
-    dn_stream_block<true>(p, p.dp + e * p.d_sp, p.ds + e * p.d_ss, p.I, rb * kSBlkRows + wave * kSRows, arow_l,
-                          orow_l, n, p.act_hi, p.act_lo, B_l);
+    dn_stream_run<true>(p, p.dp + e * p.d_sp, p.ds + e * p.d_ss, p.I, rb0, rb1, arow_l, orow_l, n, p.act_hi,
+                        p.act_lo, B_l);
 }
 
 }  // namespace
@@ -474,9 +449,17 @@ bool stream_path_ok(const LayerView &L)
            L.H % kSBlkRows == 0 && L.Is % kSBlkRows == 0;
 }
 
+// The down kernel stages a whole item's activations: it takes the routed
+// light experts when they fit in LDS (and the shared expert likewise).
+bool stream_down_ok(const LayerView &L)
+{
+    return stream_path_ok(L) && dn_stream_lds_bytes(std::max(L.I, L.Is)) <= 160 * 1024 &&
+           (L.Is == 0 || L.Is % group_k<true>() == 0);
+}
+
 int stream_max_tokens() { return kSTok; }
 
-bool stream_shared_ok(const LayerView &L, int T) { return L.Is > 0 && T <= 8 * kSTok; }
+bool stream_shared_ok(const LayerView &L, int T) { return L.Is > 0 && T <= 8 * kSTok && stream_down_ok(L); }
 
 hipError_t launch_stream_gu(const LayerView &L, const uint16_t *x, int T, const int32_t *active_e,
                             const int32_t *active_off, const int32_t *sorted, const int32_t *light,
@@ -524,6 +507,12 @@ hipError_t launch_stream_dn(const LayerView &L, int T, const int32_t *active_e, 
                             bool with_shared, const uint16_t *act_hi, const uint16_t *act_lo,
                             const uint16_t *ash_hi, const uint16_t *ash_lo, float *ys, hipStream_t s)
 {
+    static const bool lds_set = [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_dn_stream),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+        return true;
+    }();
+    (void)lds_set;
     DnStreamParams p{};
     p.H = L.H;
     p.I = L.I;
@@ -544,11 +533,15 @@ hipError_t launch_stream_dn(const LayerView &L, int T, const int32_t *active_e, 
     p.sorted = sorted;
     p.light = light;
     p.light_n = light_n;
-    p.sh_blocks = with_shared ? ((T + kSTok - 1) / kSTok) * (L.H / kSBlkRows) : 0;
+    p.sh_items = with_shared ? (T + kSTok - 1) / kSTok : 0;
+    // each item's rows in `runs` blocks of run_rb 256-row blocks (about 7)
+    const int rbt = (L.H + kDBlkRows - 1) / kDBlkRows;
+    p.runs = (rbt + 6) / 7;
+    p.run_rb = (rbt + p.runs - 1) / p.runs;
     p.ys = ys;
     const int64_t cap = std::min<int64_t>(L.E, (int64_t)T * L.K);
-    const unsigned nblk = (unsigned)(p.sh_blocks + cap * (L.H / kSBlkRows));
-    k_dn_stream<<<nblk, 64 * kSWaves, dn_stream_lds_bytes(), s>>>(p);
+    const unsigned nblk = (unsigned)((p.sh_items + cap) * p.runs);
+    k_dn_stream<<<nblk, 64 * kDWaves, dn_stream_lds_bytes(std::max(L.I, L.Is)), s>>>(p);
     return hipGetLastError();
 }
 
