@@ -20,7 +20,9 @@ Prints one JSON line. ``value`` is routed-expert HBM GB/s: the algorithmic
 bytes of the experts the step selects (17,547,264 B each, counted once per
 distinct expert) over the whole step time. ``roofline`` is the dominant
 kernel's algorithmic bytes per launch over its event-timed average duration
-(measured in a second pass with per-stage events on), against 8 TB/s.
+(measured in a second pass with per-stage events on), against 8 TB/s;
+its ``traffic`` is the HBM bytes per dispatch that rocprofv3's counters
+recorded for the same kernel source (profiles/), or null.
 ``cpu_baseline`` times the fp64 oracle on this host's cores on a bounded
 sample of the same workload.
 """
@@ -134,14 +136,21 @@ def main():
     routed_bytes = nd * expert_b
     router_bytes = E * H * 2
     shared_bytes = 3 * Is * H * 2
-    act_terms = T * K * 4 * I * (1 + 1 / 32)
-    x_terms = T * 4 * H * (1 + 1 / 32)
+    # per stage: weights read once, token side read, activations written/read
+    # (4 B per element: fp32, or bf16 hi + lo), expert outputs staged in fp32
+    x_read = T * H * 4 * (1 + 1 / 32) if T == 1 else T * H * 2   # fp8 terms (one token) or bf16
+    act_b = T * K * I * 4 + T * Is * 4
+    shared_in_gateup = stages["shared_gateup"][1] == 0  # no separate shared gate/up launch
     stage_bytes = {
-        "gateup": nd * 2 * gu + x_terms + act_terms,
-        "down": nd * dn + Is * H * 2 + act_terms + T * Is * 4 + T * H * 4,
+        "gateup": nd * 2 * gu + (2 * Is * H * 2 if shared_in_gateup else 0) + x_read + act_b,
+        "down": nd * dn + Is * H * 2 + act_b + T * (K + 1) * H * 4,
     }
+    kernels = {"decode": {"gateup": "k_gateup_dec", "down": "k_down_dec"},
+               "batched": {"gateup": "k_gu_stream", "down": "k_dn_stream"},
+               "prefill": {"gateup": "k_gu_gemm + k_gu_stream", "down": "k_dn_gemm + k_dn_stream"}}[args.workload]
     dom = max(stage_bytes, key=lambda s: stage_us[s])
     achieved = stage_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9
+    traffic = measured_traffic(kernels[dom])
     value = routed_bytes / (ms * 1e-3) / 1e9
     layer_bytes = routed_bytes + router_bytes + shared_bytes + T * H * 2 + T * H * 4
     result = {
@@ -169,20 +178,40 @@ def main():
         "routed_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "stage_us": {k: round(v, 3) for k, v in stage_us.items()},
         "roofline": {
-            "kernel": {"gateup": "k_gateup", "down": "k_down"}[dom],
+            "kernel": kernels[dom],
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "bytes_per_launch": round(stage_bytes[dom]),
-            "traffic": None,
+            "traffic": traffic,
         },
     }
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(spec, xs_np, T, args.cpu_seconds, expert_b)
     print(json.dumps(result), flush=True)
+
+
+def measured_traffic(kernel):
+    """HBM bytes per dispatch of `kernel` from the committed rocprofv3 counter
+    runs (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for
+    a copy of known size), or None when no such run exists or the kernel
+    source has changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "decode_T1_pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    k = rec.get("kernels", {}).get(kernel)
+    if k is None:
+        return None
+    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["kernel_source_sha256"]:
+            return None
+    return k["hbm_bytes"]
 
 
 def cpu_baseline(spec, xs_np, T, budget_s, expert_b):
