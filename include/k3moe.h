@@ -117,7 +117,10 @@ k3moe_status k3moe_layer_create(const k3moe_config *cfg, const k3moe_weights *w,
 /* Bytes of workspace k3moe_route and k3moe_forward need for up to
  * max_tokens tokens (max_tokens >= 0). The caller allocates it (256-byte
  * aligned) and may reuse it across calls on one stream; calls in flight on
- * different streams need different workspaces. */
+ * different streams need different workspaces. A batch is limited to
+ * T*hidden*2 and T*topk*max(inter, shared_inter)*2 bytes below 2 GiB
+ * (K3MOE_E_UNSUPPORTED_SHAPE above that; 43,690 tokens at hidden 7168,
+ * top-16, inter 1536), here and in route/forward. */
 k3moe_status k3moe_workspace_size(const k3moe_layer *layer, int32_t max_tokens,
                                   size_t *bytes);
 

@@ -151,6 +151,15 @@ static LayerView view(const k3moe_layer *l)
     return v;
 }
 
+// The batched kernels address token rows, activation rows and staging rows
+// with 32-bit byte offsets: a batch whose planes exceed 2 GiB is refused.
+static bool batch_fits(const k3moe_config &c, int64_t T)
+{
+    const int64_t lim = (int64_t)1 << 31;
+    const int64_t I = std::max(c.inter, c.shared_inter);
+    return T * c.hidden * 2 < lim && T * c.topk * I * 2 < lim;
+}
+
 // Common checks of a route/forward call; T == 0 is reported as "nothing to do".
 static k3moe_status check_call(const k3moe_layer *l, int32_t T, void *ws, size_t ws_bytes,
                                bool *nothing)
@@ -164,6 +173,7 @@ static k3moe_status check_call(const k3moe_layer *l, int32_t T, void *ws, size_t
         *nothing = true;
         return K3MOE_OK;
     }
+    if (!batch_fits(l->cfg, T)) return K3MOE_E_UNSUPPORTED_SHAPE;
     if (!ws || !aligned(ws, 256)) return K3MOE_E_WORKSPACE;
     if (ws_bytes < ws_layout(l->cfg, T).total) return K3MOE_E_WORKSPACE;
     return K3MOE_OK;
@@ -216,6 +226,7 @@ k3moe_status k3moe_layer_create(const k3moe_config *cfg, const k3moe_weights *w,
 k3moe_status k3moe_workspace_size(const k3moe_layer *l, int32_t max_tokens, size_t *bytes)
 {
     if (!l || !bytes || max_tokens < 0) return K3MOE_E_INVALID_ARG;
+    if (!batch_fits(l->cfg, max_tokens)) return K3MOE_E_UNSUPPORTED_SHAPE;
     *bytes = ws_layout(l->cfg, max_tokens).total;
     return K3MOE_OK;
 }

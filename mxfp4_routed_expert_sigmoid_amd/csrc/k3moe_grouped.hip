@@ -24,6 +24,8 @@
 //
 // The expert outputs go to the staging rows ys[t][j][.] (and ys[t][k][.] for
 // the shared expert); the combine sums them in router order.
+#include <type_traits>
+
 #include "k3moe_internal.h"
 
 namespace k3moe {
@@ -34,11 +36,6 @@ typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGRows = 256;     // weight rows per block
-constexpr int kGWaves = 8;      // 4 row groups (64 rows) x 2 token groups
-constexpr int kGuTok = 128;     // tokens per gate/up block (64 per wave)
-constexpr int kDnTok = 64;      // tokens per down block (32 per wave)
-constexpr int kARowB = 80;      // LDS bytes per weight row per chunk (64 + 16 pad)
 constexpr int kBPad = 16;       // LDS padding per token row
 
 __device__ __forceinline__ float bf16f(uint32_t h) { return __uint_as_float(h << 16); }
@@ -156,403 +153,286 @@ __global__ __launch_bounds__(1024) void k_tiles(const int32_t *__restrict__ acti
 }
 
 // ---------------------------------------------------------------------------
-// Gate/up GEMM. FP4: routed experts, tile from the list; else the shared
-// expert (bf16 weights), token block = blockIdx / RB in token order.
-// Chunk = 64 bytes of weight row: 128 K (fp4) or 32 K (bf16).
-struct GuGemmParams {
-    int H, I, K, T, act;
+// Grouped GEMM tiles. A block owns 256 weight rows of one expert (or of the
+// shared expert) and one tile of its tokens. Each wave owns RF 16-row MFMA
+// tiles over the whole K range and all of the tile's tokens (TF 16-column
+// fragments), so a weight fragment is loaded from HBM into registers once,
+// expanded to bf16 once, and used for every token fragment; the next K chunk's
+// weights are in flight while the current one is multiplied. The tokens (x,
+// or the activation's hi and lo planes) pass through double-buffered LDS, one
+// barrier per chunk.
+//
+// K mapping (fp4): a lane's 16-byte weight load in chunk c holds K =
+// 128c + 32g + [0, 32) of its row (g = lane / 16); MFMA step s uses
+// K = 128c + 32g + 8s + [0, 8), and the token side reads the same K from LDS.
+// bf16 weights: chunk c, lane group g holds K = 32c + 8g + [0, 8), one step.
+template <bool GU> struct GemmShape;
+template <> struct GemmShape<true> {   // gate/up: 8 waves x 32 rows, 128 tokens
+    static constexpr int WAVES = 8, RF = 2, TF = 8, NMAT = 2, NPL = 1, TOK = 128;
+};
+template <> struct GemmShape<false> {  // down: 4 waves x 64 rows, 64 tokens (hi, lo)
+    static constexpr int WAVES = 4, RF = 4, TF = 4, NMAT = 1, NPL = 2, TOK = 64;
+};
+constexpr int kTileRows = 256;  // weight rows per block (both shapes)
+static_assert(GemmShape<true>::WAVES * GemmShape<true>::RF * 16 == kTileRows, "gate/up tile rows");
+static_assert(GemmShape<false>::WAVES * GemmShape<false>::RF * 16 == kTileRows, "down tile rows");
+
+struct GemmParams {
+    int rows, KD, K, T, act;   // weight rows (I / I_s or H), reduction length (H or I / I_s), top-k
     float b1, b2;
-    const uint8_t *gp, *gs, *up, *us;     // routed fp4 gate/up
-    int64_t g_sp, g_ss, u_sp, u_ss;
-    const uint16_t *wg, *wu;              // shared bf16 gate/up [I][H]
-    const uint16_t *x;                    // bf16 [T][H]
+    // routed fp4 weights per matrix (gate, up | down), per-expert strides
+    const uint8_t *wp[2], *ws[2];
+    int64_t wsp[2], wss[2];
+    // shared expert: bf16 weights [rows][KD] per matrix
+    const uint16_t *wb[2];
+    // token planes [.][KD] bf16: x (gate/up), or the activation's hi and lo (down)
+    const uint16_t *bp[2];
     const int32_t *active_e, *active_off, *sorted;
     const int2 *tiles;
     const int32_t *tile_n;
-    uint16_t *act_hi, *act_lo;            // bf16 [rows of assignments / tokens][I]
+    int sh_blocks;             // leading blocks that run the shared expert
+    uint16_t *ohi, *olo;       // gate/up: activation hi/lo [row][rows]
+    float *ys;                 // down: staging [T][K + 1][H]
 };
 
-template <bool FP4>
-__host__ __device__ constexpr int gu_gemm_lds_bytes()
+template <bool GU>
+__host__ __device__ constexpr int gemm_lds_bytes()
 {
-    return 2 * (2 * kGRows * kARowB + (FP4 ? 2 * kGRows * 4 : 0) +
-                kGuTok * ((FP4 ? 256 : 64) + kBPad)) +
-           kGuTok * 4;
+    using S = GemmShape<GU>;
+    return 2 * S::NPL * S::TOK * (128 * 2 + kBPad) + 2 * S::TOK * 4;
 }
 
-template <bool FP4>
-__global__ __launch_bounds__(64 * kGWaves) void k_gu_gemm(GuGemmParams p)
+template <bool GU, bool FP4>
+__device__ __forceinline__ void gemm_tile(const GemmParams &p, int e, int rb, int p0, int n, const int *bro_l,
+                                          const int *oro_l, uint8_t *B_l)
 {
-    constexpr int KC = FP4 ? 128 : 32;          // K elements per chunk
-    constexpr int SPC = KC / 32;                // MFMA steps per chunk
-    constexpr int BROW = KC * 2 + kBPad;        // LDS bytes per token row
-    constexpr int ABUF = 2 * kGRows * kARowB;   // one A buffer (gate + up)
-    constexpr int SBUF = FP4 ? 2 * kGRows * 4 : 0;
-    constexpr int BBUF = kGuTok * BROW;
-    const int H = p.H, I = p.I, RB = (I + kGRows - 1) / kGRows;
-    const int tile = blockIdx.x / RB, rb = blockIdx.x - tile * RB;
-    const int nrows = min(kGRows, I - rb * kGRows);  // a multiple of 64 (I % 128 == 0)
-    int e = 0, p0, n;
-    if constexpr (FP4) {
-        if (tile >= *p.tile_n) return;
-        const int2 tl = p.tiles[tile];
-        e = p.active_e[tl.x];
-        p0 = p.active_off[tl.x] + tl.y * kGuTok;
-        n = min(kGuTok, p.active_off[tl.x + 1] - p0);
-    } else {
-        p0 = tile * kGuTok;
-        n = min(kGuTok, p.T - p0);
-    }
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 3, wn = wave >> 2;  // row group, token group
-    const int g = lane >> 4, l16 = lane & 15;
+    using S = GemmShape<GU>;
+    constexpr int WAVES = S::WAVES, RF = S::RF, TF = S::TF, NMAT = S::NMAT, NPL = S::NPL, TOK = S::TOK;
+    constexpr int NT = 64 * WAVES;
+    constexpr int KC = FP4 ? 128 : 32;           // K per chunk
+    constexpr int SPC = FP4 ? 4 : 1;             // MFMA steps per chunk
+    constexpr int BROW = KC * 2 + kBPad;         // LDS bytes per token row per chunk
+    constexpr int BSEG = KC * 2 / 16;            // u4 per token row per chunk
+    constexpr int NBU4 = NPL * TOK * BSEG;       // u4 of one chunk's token tile
+    constexpr int NB = (NBU4 + NT - 1) / NT;
+    constexpr int BBUF = NPL * TOK * BROW;
+    const int KD = p.KD, rows = p.rows, NCH = KD / KC;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+    const int nrows = min(kTileRows, rows - rb * kTileRows);
+    const int row0 = rb * kTileRows + wave * RF * 16;
+    const int ntf = wave * RF * 16 < nrows ? (n + 15) / 16 : 0;  // token fragments with data
 
-    extern __shared__ __align__(16) uint8_t lds[];
-    uint8_t *A_l = lds;                        // [2 bufs][2 mats][256 rows][80 B]
-    uint8_t *S_l = A_l + 2 * ABUF;             // [2 bufs][2 mats][256 rows][4 B] (fp4)
-    uint8_t *B_l = S_l + 2 * SBUF;             // [2 bufs][128 tokens][BROW]
-    int *tok_l = reinterpret_cast<int *>(B_l + 2 * BBUF);  // [128] token of each column
-
-    for (int c = tid; c < kGuTok; c += 64 * kGWaves) {
-        const int cc = min(c, n - 1);
-        tok_l[c] = FP4 ? p.sorted[p0 + cc] / p.K : p0 + cc;
-    }
-    __syncthreads();
-
-    // weight rows of this block
-    const size_t rowb = FP4 ? (size_t)H / 2 : (size_t)H * 2;  // bytes per weight row
-    const uint8_t *wbase[2];
-    const uint8_t *sbase[2] = {nullptr, nullptr};
-    if constexpr (FP4) {
-        wbase[0] = p.gp + e * p.g_sp + (size_t)rb * kGRows * rowb;
-        wbase[1] = p.up + e * p.u_sp + (size_t)rb * kGRows * rowb;
-        sbase[0] = p.gs + e * p.g_ss + (size_t)rb * kGRows * (H / 32);
-        sbase[1] = p.us + e * p.u_ss + (size_t)rb * kGRows * (H / 32);
-    } else {
-        wbase[0] = reinterpret_cast<const uint8_t *>(p.wg) + (size_t)rb * kGRows * rowb;
-        wbase[1] = reinterpret_cast<const uint8_t *>(p.wu) + (size_t)rb * kGRows * rowb;
-    }
-    const uint8_t *xb = reinterpret_cast<const uint8_t *>(p.x);
-
-    // staging of chunk c: A = 2 mats x 256 rows x 4 u4; S = 512 dwords; B = 128 tokens x (KC*2/16) u4
-    constexpr int BSEG = KC * 2 / 16;  // u4 per token row per chunk
-    u4 ra[4], rbv[(kGuTok * BSEG + 511) / 512];
-    uint32_t rs = 0;
-    auto gload = [&](int c) {
+    // weight rows: a uniform base per matrix and 32-bit per-lane offsets
+    const uint32_t rowb = FP4 ? (uint32_t)KD / 2 : (uint32_t)KD * 2;
+    const uint8_t *wbase[NMAT];
+    const uint8_t *sbase[NMAT];
+    uint32_t woff[RF], soff[RF];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int v = tid + 512 * q;  // 0..2047
-            const int mat = v >> 10, row = min((v >> 2) & 255, nrows - 1), seg = v & 3;
-            ra[q] = *reinterpret_cast<const u4 *>(wbase[mat] + (size_t)row * rowb + (size_t)c * 64 + 16 * seg);
-        }
+    for (int m = 0; m < NMAT; ++m) {
         if constexpr (FP4) {
-            const int mat = tid >> 8, row = min(tid & 255, nrows - 1);
-            rs = *reinterpret_cast<const uint32_t *>(sbase[mat] + (size_t)row * (H / 32) + 4 * c);
-        }
-#pragma unroll
-        for (int q = 0; q < (kGuTok * BSEG + 511) / 512; ++q) {
-            const int v = tid + 512 * q;
-            const int col = v / BSEG, seg = v - col * BSEG;
-            rbv[q] = *reinterpret_cast<const u4 *>(xb + ((size_t)tok_l[col] * H + (size_t)c * KC) * 2 + 16 * seg);
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int v = tid + 512 * q;
-            const int mat = v >> 10, row = (v >> 2) & 255, seg = v & 3;
-            *reinterpret_cast<u4 *>(A_l + buf * ABUF + (mat * kGRows + row) * kARowB + 16 * seg) = ra[q];
-        }
-        if constexpr (FP4) *reinterpret_cast<uint32_t *>(S_l + buf * SBUF + 4 * tid) = rs;
-#pragma unroll
-        for (int q = 0; q < (kGuTok * BSEG + 511) / 512; ++q) {
-            const int v = tid + 512 * q;
-            const int col = v / BSEG, seg = v - col * BSEG;
-            *reinterpret_cast<u4 *>(B_l + buf * BBUF + col * BROW + 16 * seg) = rbv[q];
-        }
-    };
-
-    // this wave: rows wm*64 + 16 rf + l16; token columns wn*64 + 16 tf + l16
-    // token fragments with data (none if the wave's 64 rows are past the end)
-    const int ntf = wm * 64 < nrows ? min(4, max(0, (n - wn * 64 + 15) / 16)) : 0;
-    v4f acc[2][4][4];
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int rf = 0; rf < 4; ++rf)
-#pragma unroll
-            for (int tf = 0; tf < 4; ++tf) acc[m][rf][tf] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-    const int NCH = H / KC;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int c = 0; c < NCH; ++c) {
-        const int buf = c & 1;
-        if (c + 1 < NCH) gload(c + 1);
-        if (ntf > 0) {
-            const uint8_t *Ab = A_l + buf * ABUF;
-            const uint8_t *Bb = B_l + buf * BBUF;
-            uint32_t s4[2][4];  // E8M0 bytes of the chunk's 4 steps, per row fragment
-            if constexpr (FP4) {
-#pragma unroll
-                for (int m = 0; m < 2; ++m)
-#pragma unroll
-                    for (int rf = 0; rf < 4; ++rf) {
-                        const int row = wm * 64 + 16 * rf + l16;
-                        s4[m][rf] = *reinterpret_cast<const uint32_t *>(S_l + buf * SBUF + 4 * (m * kGRows + row));
-                    }
-            }
-#pragma unroll
-            for (int st = 0; st < SPC; ++st) {
-                bf8 b[4];
-#pragma unroll
-                for (int tf = 0; tf < 4; ++tf) {
-                    const int col = wn * 64 + 16 * tf + l16;
-                    b[tf] = as_bf8(*reinterpret_cast<const u4 *>(Bb + col * BROW + 64 * st + 16 * g));
-                }
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    bf8 a[4];
-#pragma unroll
-                    for (int rf = 0; rf < 4; ++rf) {
-                        const int row = wm * 64 + 16 * rf + l16;
-                        const uint8_t *ar = Ab + (m * kGRows + row) * kARowB;
-                        if constexpr (FP4)
-                            a[rf] = dequant8(*reinterpret_cast<const uint32_t *>(ar + 16 * st + 4 * g),
-                                             e8m0_scale((s4[m][rf] >> (8 * st)) & 0xffu));
-                        else
-                            a[rf] = as_bf8(*reinterpret_cast<const u4 *>(ar + 16 * g));
-                    }
-#pragma unroll
-                    for (int tf = 0; tf < 4; ++tf)
-                        if (tf < ntf)
-#pragma unroll
-                            for (int rf = 0; rf < 4; ++rf) acc[m][rf][tf] = mfma_bf16(a[rf], b[tf], acc[m][rf][tf]);
-                }
-            }
-        }
-        if (c + 1 < NCH) lstore(buf ^ 1);
-        __syncthreads();
-    }
-
-    // epilogue: act(g, u) -> bf16 hi + lo, rows of this token column
-#pragma unroll
-    for (int tf = 0; tf < 4; ++tf) {
-        const int col = wn * 64 + 16 * tf + l16;
-        if (tf < ntf && col < n) {
-            const size_t orow = (size_t)(p0 + col) * I + (size_t)rb * kGRows;
-#pragma unroll
-            for (int rf = 0; rf < 4; ++rf) {
-                const int row = wm * 64 + 16 * rf + 4 * g;
-                uint32_t hi2[2], lo2[2];
-#pragma unroll
-                for (int r = 0; r < 4; r += 2) {
-                    const float a0 = act_fn(acc[0][rf][tf][r], acc[1][rf][tf][r], p.act, p.b1, p.b2);
-                    const float a1 = act_fn(acc[0][rf][tf][r + 1], acc[1][rf][tf][r + 1], p.act, p.b1, p.b2);
-                    const uint16_t h0 = bf16_rne(a0), h1 = bf16_rne(a1);
-                    const uint16_t q0 = bf16_rne(a0 - bf16f(h0)), q1 = bf16_rne(a1 - bf16f(h1));
-                    hi2[r / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                    lo2[r / 2] = (uint32_t)q0 | ((uint32_t)q1 << 16);
-                }
-                *reinterpret_cast<uint2 *>(p.act_hi + orow + row) = uint2{hi2[0], hi2[1]};
-                *reinterpret_cast<uint2 *>(p.act_lo + orow + row) = uint2{lo2[0], lo2[1]};
-            }
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Down GEMM: rows of H, tokens of one expert (or the shared expert), the
-// activation fed as bf16 hi and lo (two MFMAs into one accumulator).
-struct DnGemmParams {
-    int H, I, K, T;
-    const uint8_t *dp, *ds;               // routed fp4 down [E][H][I/2], scales
-    int64_t d_sp, d_ss;
-    const uint16_t *wd;                   // shared bf16 down [H][I]
-    const uint16_t *act_hi, *act_lo;      // [rows][I]
-    const int32_t *active_e, *active_off, *sorted;
-    const int2 *tiles;
-    const int32_t *tile_n;
-    float *ys;                            // [T][K+1][H]
-};
-
-template <bool FP4>
-__host__ __device__ constexpr int dn_gemm_lds_bytes()
-{
-    return 2 * (kGRows * kARowB + (FP4 ? kGRows * 4 : 0) + 2 * kDnTok * ((FP4 ? 256 : 64) + kBPad)) +
-           kDnTok * 4 * 2;
-}
-
-template <bool FP4>
-__global__ __launch_bounds__(64 * kGWaves) void k_dn_gemm(DnGemmParams p)
-{
-    constexpr int KC = FP4 ? 128 : 32;
-    constexpr int SPC = KC / 32;
-    constexpr int BROW = KC * 2 + kBPad;
-    constexpr int ABUF = kGRows * kARowB;
-    constexpr int SBUF = FP4 ? kGRows * 4 : 0;
-    constexpr int BBUF = 2 * kDnTok * BROW;   // hi rows then lo rows
-    const int H = p.H, I = p.I, RB = (H + kGRows - 1) / kGRows;
-    const int tile = blockIdx.x / RB, rb = blockIdx.x - tile * RB;
-    const int nrows = min(kGRows, H - rb * kGRows);  // a multiple of 64 (H % 128 == 0)
-    int e = 0, p0, n;
-    if constexpr (FP4) {
-        if (tile >= *p.tile_n) return;
-        const int2 tl = p.tiles[tile];
-        e = p.active_e[tl.x];
-        p0 = p.active_off[tl.x] + tl.y * kDnTok;
-        n = min(kDnTok, p.active_off[tl.x + 1] - p0);
-    } else {
-        p0 = tile * kDnTok;
-        n = min(kDnTok, p.T - p0);
-    }
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 3, wn = wave >> 2;
-    const int g = lane >> 4, l16 = lane & 15;
-
-    extern __shared__ __align__(16) uint8_t lds[];
-    uint8_t *A_l = lds;
-    uint8_t *S_l = A_l + 2 * ABUF;
-    uint8_t *B_l = S_l + 2 * SBUF;
-    int *orow_l = reinterpret_cast<int *>(B_l + 2 * BBUF);  // [64] output row (t*(K+1)+j) of each column
-    int *arow_l = orow_l + kDnTok;                          // [64] activation row of each column
-
-    for (int c = tid; c < kDnTok; c += 64 * kGWaves) {
-        const int cc = min(c, n - 1);
-        if constexpr (FP4) {
-            const int a = p.sorted[p0 + cc];
-            orow_l[c] = (a / p.K) * (p.K + 1) + (a % p.K);
+            wbase[m] = p.wp[m] + e * p.wsp[m];
+            sbase[m] = p.ws[m] + e * p.wss[m];
         } else {
-            orow_l[c] = (p0 + cc) * (p.K + 1) + p.K;
+            wbase[m] = reinterpret_cast<const uint8_t *>(p.wb[m]);
+            sbase[m] = nullptr;
         }
-        arow_l[c] = p0 + cc;
     }
-    __syncthreads();
-
-    const size_t rowb = FP4 ? (size_t)I / 2 : (size_t)I * 2;
-    const uint8_t *wbase, *sbase = nullptr;
-    if constexpr (FP4) {
-        wbase = p.dp + e * p.d_sp + (size_t)rb * kGRows * rowb;
-        sbase = p.ds + e * p.d_ss + (size_t)rb * kGRows * (I / 32);
-    } else {
-        wbase = reinterpret_cast<const uint8_t *>(p.wd) + (size_t)rb * kGRows * rowb;
-    }
-    const uint8_t *hib = reinterpret_cast<const uint8_t *>(p.act_hi);
-    const uint8_t *lob = reinterpret_cast<const uint8_t *>(p.act_lo);
-
-    constexpr int BSEG = KC * 2 / 16;
-    constexpr int NB = (2 * kDnTok * BSEG + 511) / 512;
-    u4 ra[2], rbv[NB];
-    uint32_t rs = 0;
-    auto gload = [&](int c) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int v = tid + 512 * q;  // 0..1023
-            const int row = min(v >> 2, nrows - 1), seg = v & 3;
-            ra[q] = *reinterpret_cast<const u4 *>(wbase + (size_t)row * rowb + (size_t)c * 64 + 16 * seg);
+    for (int rf = 0; rf < RF; ++rf) {
+        const uint32_t r = (uint32_t)min(row0 + 16 * rf + l16, rows - 1);
+        woff[rf] = r * rowb + 16 * g;
+        soff[rf] = r * ((uint32_t)KD / 32);
+    }
+    struct Chunk {
+        u4 a[NMAT][RF];
+        uint32_t s[NMAT][RF];
+    };
+    auto aload = [&](int c, Chunk &b) {
+        const uint32_t cc = (uint32_t)min(c, NCH - 1);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int rf = 0; rf < RF; ++rf) {
+                b.a[m][rf] = *reinterpret_cast<const u4 *>(wbase[m] + (woff[rf] + cc * 64));
+                if constexpr (FP4) b.s[m][rf] = *reinterpret_cast<const uint32_t *>(sbase[m] + (soff[rf] + cc * 4));
+            }
+    };
+    // token tile: fixed per-thread source offsets (32-bit), chunk added per load
+    uint32_t boff[NB];
+    const uint8_t *bbase[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+        const int v = min(tid + NT * q, NBU4 - 1);
+        const int pl = v / (TOK * BSEG), vv = v - pl * (TOK * BSEG);
+        const int col = vv / BSEG, seg = vv - col * BSEG;
+        bbase[q] = reinterpret_cast<const uint8_t *>(p.bp[pl]);
+        boff[q] = (uint32_t)bro_l[col] * (uint32_t)KD * 2 + 16 * seg;
+    }
+    u4 xs[NB];
+    auto bload = [&](int c) {
+        const uint32_t cc = (uint32_t)min(c, NCH - 1);
+#pragma unroll
+        for (int q = 0; q < NB; ++q) xs[q] = *reinterpret_cast<const u4 *>(bbase[q] + (boff[q] + cc * (KC * 2)));
+    };
+    auto bstore = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            const int v = tid + NT * q;
+            if (NBU4 % NT == 0 || v < NBU4) {
+                const int pl = v / (TOK * BSEG), vv = v - pl * (TOK * BSEG);
+                const int col = vv / BSEG, seg = vv - col * BSEG;
+                *reinterpret_cast<u4 *>(B_l + buf * BBUF + (pl * TOK + col) * BROW + 16 * seg) = xs[q];
+            }
         }
+    };
+
+    v4f acc[NMAT][RF][TF];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int rf = 0; rf < RF; ++rf)
+#pragma unroll
+            for (int tf = 0; tf < TF; ++tf) acc[m][rf][tf] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // one chunk with NTF token fragments: no branches inside
+    auto compute_n = [&](const Chunk &b, int buf, auto ntf_c) {
+        constexpr int NTF = decltype(ntf_c)::value;
+        const uint8_t *Bb = B_l + buf * BBUF + l16 * BROW;
+        float sc[NMAT][RF];
         if constexpr (FP4) {
-            const int row = min(tid & 255, nrows - 1);
-            rs = *reinterpret_cast<const uint32_t *>(sbase + (size_t)row * (I / 32) + 4 * c);
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int rf = 0; rf < RF; ++rf) sc[m][rf] = e8m0_scale((b.s[m][rf] >> (8 * g)) & 0xffu);
         }
 #pragma unroll
-        for (int q = 0; q < NB; ++q) {
-            const int v = tid + 512 * q;
-            const int half = v / (kDnTok * BSEG), vv = v - half * (kDnTok * BSEG);
-            const int col = vv / BSEG, seg = vv - col * BSEG;
-            const uint8_t *src = half ? lob : hib;
-            rbv[q] = *reinterpret_cast<const u4 *>(src + ((size_t)arow_l[col] * I + (size_t)c * KC) * 2 + 16 * seg);
-        }
-    };
-    auto lstore = [&](int buf) {
+        for (int st = 0; st < SPC; ++st) {
+            bf8 a[NMAT][RF];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int v = tid + 512 * q;
-            const int row = v >> 2, seg = v & 3;
-            *reinterpret_cast<u4 *>(A_l + buf * ABUF + row * kARowB + 16 * seg) = ra[q];
-        }
-        if constexpr (FP4)
-            if (tid < kGRows) *reinterpret_cast<uint32_t *>(S_l + buf * SBUF + 4 * tid) = rs;
+            for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-        for (int q = 0; q < NB; ++q) {
-            const int v = tid + 512 * q;
-            const int half = v / (kDnTok * BSEG), vv = v - half * (kDnTok * BSEG);
-            const int col = vv / BSEG, seg = vv - col * BSEG;
-            *reinterpret_cast<u4 *>(B_l + buf * BBUF + (half * kDnTok + col) * BROW + 16 * seg) = rbv[q];
-        }
-    };
-
-    const int ntf = wm * 64 < nrows ? min(2, max(0, (n - wn * 32 + 15) / 16)) : 0;
-    v4f acc[4][2];
-#pragma unroll
-    for (int rf = 0; rf < 4; ++rf)
-#pragma unroll
-        for (int tf = 0; tf < 2; ++tf) acc[rf][tf] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-
-    const int NCH = I / KC;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int c = 0; c < NCH; ++c) {
-        const int buf = c & 1;
-        if (c + 1 < NCH) gload(c + 1);
-        if (ntf > 0) {
-            const uint8_t *Ab = A_l + buf * ABUF;
-            const uint8_t *Bb = B_l + buf * BBUF;
-            uint32_t s4[4];
-            if constexpr (FP4) {
-#pragma unroll
-                for (int rf = 0; rf < 4; ++rf) {
-                    const int row = wm * 64 + 16 * rf + l16;
-                    s4[rf] = *reinterpret_cast<const uint32_t *>(S_l + buf * SBUF + 4 * row);
-                }
-            }
-#pragma unroll
-            for (int st = 0; st < SPC; ++st) {
-                bf8 a[4];
-#pragma unroll
-                for (int rf = 0; rf < 4; ++rf) {
-                    const int row = wm * 64 + 16 * rf + l16;
-                    const uint8_t *ar = Ab + row * kARowB;
+                for (int rf = 0; rf < RF; ++rf) {
                     if constexpr (FP4)
-                        a[rf] = dequant8(*reinterpret_cast<const uint32_t *>(ar + 16 * st + 4 * g),
-                                         e8m0_scale((s4[rf] >> (8 * st)) & 0xffu));
+                        a[m][rf] = dequant8(b.a[m][rf][st], sc[m][rf]);
                     else
-                        a[rf] = as_bf8(*reinterpret_cast<const u4 *>(ar + 16 * g));
+                        a[m][rf] = as_bf8(b.a[m][rf]);
                 }
+            const int kb = FP4 ? (64 * g + 16 * st) : 16 * g;  // byte offset in the token row
 #pragma unroll
-                for (int tf = 0; tf < 2; ++tf) {
-                    if (tf < ntf) {
-                        const int col = wn * 32 + 16 * tf + l16;
-                        const bf8 bh = as_bf8(*reinterpret_cast<const u4 *>(Bb + col * BROW + 64 * st + 16 * g));
-                        const bf8 bl = as_bf8(*reinterpret_cast<const u4 *>(Bb + (kDnTok + col) * BROW + 64 * st + 16 * g));
+            for (int tf = 0; tf < NTF; ++tf) {
 #pragma unroll
-                        for (int rf = 0; rf < 4; ++rf) {
-                            acc[rf][tf] = mfma_bf16(a[rf], bh, acc[rf][tf]);
-                            acc[rf][tf] = mfma_bf16(a[rf], bl, acc[rf][tf]);
-                        }
-                    }
+                for (int pl = 0; pl < NPL; ++pl) {
+                    const bf8 bv = as_bf8(*reinterpret_cast<const u4 *>(Bb + (pl * TOK + 16 * tf) * BROW + kb));
+#pragma unroll
+                    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                        for (int rf = 0; rf < RF; ++rf) acc[m][rf][tf] = mfma_bf16(a[m][rf], bv, acc[m][rf][tf]);
                 }
             }
         }
-        if (c + 1 < NCH) lstore(buf ^ 1);
+    };
+    // Every chunk runs over all TF fragments (a partial tile multiplies
+    // clamped copies of its last token, never stored): one branch-free body
+    // lets the compiler keep the accumulators in registers and overlap the
+    // LDS reads with the MFMAs; per-fragment branches serialised them.
+    auto compute = [&](const Chunk &b, int buf) {
+        if (ntf == 0) return;
+        compute_n(b, buf, std::integral_constant<int, TF>{});
+    };
+
+    // Token loads are issued before weight loads: the LDS store of the next
+    // token chunk then waits only for the token loads (memory counters retire
+    // in issue order), and the weight loads stay in flight across it.
+    Chunk c0, c1;
+    bload(0);
+    aload(0, c0);
+    bstore(0);
+    __syncthreads();
+    for (int c = 0; c < NCH; c += 2) {
+        bload(c + 1);
+        aload(c + 1, c1);
+        compute(c0, 0);
+        bstore(1);
+        __syncthreads();
+        if (c + 1 >= NCH) break;
+        bload(c + 2);
+        aload(c + 2, c0);
+        compute(c1, 1);
+        bstore(0);
         __syncthreads();
     }
 
+    // epilogue: lane holds rows 4g + i (i = 0..3) of token column 16 tf + l16
 #pragma unroll
-    for (int tf = 0; tf < 2; ++tf) {
-        const int col = wn * 32 + 16 * tf + l16;
+    for (int tf = 0; tf < TF; ++tf) {
+        const int col = 16 * tf + l16;
         if (tf < ntf && col < n) {
-            float *yr = p.ys + (size_t)orow_l[col] * H + (size_t)rb * kGRows;
 #pragma unroll
-            for (int rf = 0; rf < 4; ++rf) {
-                const int row = wm * 64 + 16 * rf + 4 * g;
-                *reinterpret_cast<float4 *>(yr + row) =
-                    float4{acc[rf][tf][0], acc[rf][tf][1], acc[rf][tf][2], acc[rf][tf][3]};
+            for (int rf = 0; rf < RF; ++rf) {
+                const int row = row0 + 16 * rf + 4 * g;
+                if constexpr (GU) {
+                    uint32_t hi2[2], lo2[2];
+#pragma unroll
+                    for (int i = 0; i < 4; i += 2) {
+                        const float a0 = act_fn(acc[0][rf][tf][i], acc[1][rf][tf][i], p.act, p.b1, p.b2);
+                        const float a1 = act_fn(acc[0][rf][tf][i + 1], acc[1][rf][tf][i + 1], p.act, p.b1, p.b2);
+                        const uint16_t h0 = bf16_rne(a0), h1 = bf16_rne(a1);
+                        const uint16_t q0 = bf16_rne(a0 - bf16f(h0)), q1 = bf16_rne(a1 - bf16f(h1));
+                        hi2[i / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                        lo2[i / 2] = (uint32_t)q0 | ((uint32_t)q1 << 16);
+                    }
+                    const size_t o = (size_t)oro_l[col] * rows + row;
+                    *reinterpret_cast<uint2 *>(p.ohi + o) = uint2{hi2[0], hi2[1]};
+                    *reinterpret_cast<uint2 *>(p.olo + o) = uint2{lo2[0], lo2[1]};
+                } else {
+                    *reinterpret_cast<float4 *>(p.ys + (size_t)oro_l[col] * rows + row) =
+                        float4{acc[0][rf][tf][0], acc[0][rf][tf][1], acc[0][rf][tf][2], acc[0][rf][tf][3]};
+                }
             }
         }
     }
+}
+
+// One launch: the shared expert's tiles first (bf16 weights, tokens in
+// order), then the routed tiles from the list (fp4 weights).
+template <bool GU>
+__global__ __launch_bounds__(64 * GemmShape<GU>::WAVES) void k_gemm(GemmParams p)
+{
+    using S = GemmShape<GU>;
+    extern __shared__ __align__(16) uint8_t lds[];
+    uint8_t *B_l = lds;
+    int *bro_l = reinterpret_cast<int *>(lds + 2 * S::NPL * S::TOK * (128 * 2 + kBPad));  // token plane row per column
+    int *oro_l = bro_l + S::TOK;                                                          // output row per column
+    const int RB = (p.rows + kTileRows - 1) / kTileRows;
+    int b = blockIdx.x;
+    if (b < p.sh_blocks) {
+        // shared expert: rows of I_s (gate/up) or H (down); p.rows/KD already
+        // describe the shared matrices when sh_blocks > 0 in a shared launch
+        const int tile = b / RB, rb = b - tile * RB;
+        const int p0 = tile * S::TOK, n = min(S::TOK, p.T - p0);
+        for (int c = threadIdx.x; c < S::TOK; c += 64 * S::WAVES) {
+            const int t = p0 + min(c, n - 1);
+            bro_l[c] = t;
+            oro_l[c] = GU ? t : t * (p.K + 1) + p.K;
+        }
+        __syncthreads();
+        gemm_tile<GU, false>(p, 0, rb, p0, n, bro_l, oro_l, B_l);
+        return;
+    }
+    b -= p.sh_blocks;
+    const int tile = b / RB, rb = b - tile * RB;
+    if (tile >= *p.tile_n) return;
+    const int2 tl = p.tiles[tile];
+    const int e = p.active_e[tl.x];
+    const int p0 = p.active_off[tl.x] + tl.y * S::TOK, n = min(S::TOK, p.active_off[tl.x + 1] - p0);
+    for (int c = threadIdx.x; c < S::TOK; c += 64 * S::WAVES) {
+        const int cc = min(c, n - 1);
+        const int a = p.sorted[p0 + cc];
+        bro_l[c] = GU ? a / p.K : p0 + cc;
+        oro_l[c] = GU ? p0 + cc : (a / p.K) * (p.K + 1) + a % p.K;
+    }
+    __syncthreads();
+    gemm_tile<GU, true>(p, e, rb, p0, n, bro_l, oro_l, B_l);
 }
 
 }  // namespace
@@ -561,14 +441,10 @@ __global__ __launch_bounds__(64 * kGWaves) void k_dn_gemm(DnGemmParams p)
 // validated multiples of 128 at layer creation).
 static bool set_lds_limits()
 {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gu_gemm<true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, gu_gemm_lds_bytes<true>());
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gu_gemm<false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, gu_gemm_lds_bytes<false>());
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_dn_gemm<true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, dn_gemm_lds_bytes<true>());
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_dn_gemm<false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, dn_gemm_lds_bytes<false>());
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm<true>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes<true>());
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm<false>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes<false>());
     return true;
 }
 
@@ -577,8 +453,8 @@ size_t grouped_tile_cap(int64_t T, int K, int E, int bn)
     return (size_t)(T * K / bn + std::min<int64_t>(E, T * K) + 1);
 }
 
-size_t grouped_tile_cap_gu(int64_t T, int K, int E) { return grouped_tile_cap(T, K, E, kGuTok); }
-size_t grouped_tile_cap_dn(int64_t T, int K, int E) { return grouped_tile_cap(T, K, E, kDnTok); }
+size_t grouped_tile_cap_gu(int64_t T, int K, int E) { return grouped_tile_cap(T, K, E, GemmShape<true>::TOK); }
+size_t grouped_tile_cap_dn(int64_t T, int K, int E) { return grouped_tile_cap(T, K, E, GemmShape<false>::TOK); }
 
 hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const int32_t *active_n,
                           const int32_t *active_e, const int32_t *active_off, const int32_t *sorted,
@@ -588,39 +464,18 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const in
 {
     static const bool lds_set = set_lds_limits();  // once per process (thread-safe static)
     (void)lds_set;
-    const size_t cap_gu = grouped_tile_cap(T, L.K, L.E, kGuTok), cap_dn = grouped_tile_cap(T, L.K, L.E, kDnTok);
-    const int rb_i = (L.I + kGRows - 1) / kGRows, rb_h = (L.H + kGRows - 1) / kGRows;
-    const int rb_s = (L.Is + kGRows - 1) / kGRows;
+    constexpr int TG = GemmShape<true>::TOK, TD = GemmShape<false>::TOK;
+    const size_t cap_gu = grouped_tile_cap(T, L.K, L.E, TG), cap_dn = grouped_tile_cap(T, L.K, L.E, TD);
+    const int rb_i = (L.I + kTileRows - 1) / kTileRows, rb_h = (L.H + kTileRows - 1) / kTileRows;
+    const int rb_s = (L.Is + kTileRows - 1) / kTileRows;
     const bool stream = stream_path_ok(L), stream_dn = stream_down_ok(L);
     const bool sh_stream = stream_shared_ok(L, T);
     int32_t *light_gu = light, *light_dn = light + L.E;
-    k_tiles<<<1, 1024, 0, s>>>(active_n, active_off, kGuTok, kDnTok, stream ? stream_max_tokens() : 0,
+    k_tiles<<<1, 1024, 0, s>>>(active_n, active_off, TG, TD, stream ? stream_max_tokens() : 0,
                                stream_dn ? stream_max_tokens() : 0, tiles_gu, tiles_dn, light_gu, light_dn, counts);
 
-    GuGemmParams gp{};
-    gp.H = L.H;
-    gp.I = L.I;
-    gp.K = L.K;
-    gp.T = T;
-    gp.act = L.act;
-    gp.b1 = L.b1;
-    gp.b2 = L.b2;
-    gp.gp = L.gp;
-    gp.gs = L.gs;
-    gp.up = L.up;
-    gp.us = L.us;
-    gp.g_sp = L.g_sp;
-    gp.g_ss = L.g_ss;
-    gp.u_sp = L.u_sp;
-    gp.u_ss = L.u_ss;
-    gp.x = x;
-    gp.active_e = active_e;
-    gp.active_off = active_off;
-    gp.sorted = sorted;
-    gp.tiles = tiles_gu;
-    gp.tile_n = counts;
-    gp.act_hi = act_hi;
-    gp.act_lo = act_lo;
+    // gate/up: routed tiles (fp4); the shared expert's tiles go in a launch of
+    // their own (different weight rows) unless they stream with the light experts
     {
         StageMark m(prof, K3MOE_STAGE_GATEUP, s);
         if (stream) {
@@ -628,38 +483,43 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const in
                                                   sh_stream, act_hi, act_lo, ash_hi, ash_lo, s);
             if (e != hipSuccess) return e;
         }
-        const unsigned nblk = (unsigned)(cap_gu * rb_i);
-        k_gu_gemm<true><<<nblk, 64 * kGWaves, gu_gemm_lds_bytes<true>(), s>>>(gp);
+        GemmParams gp{};
+        gp.rows = L.I;
+        gp.KD = L.H;
+        gp.K = L.K;
+        gp.T = T;
+        gp.act = L.act;
+        gp.b1 = L.b1;
+        gp.b2 = L.b2;
+        gp.wp[0] = L.gp;
+        gp.wp[1] = L.up;
+        gp.ws[0] = L.gs;
+        gp.ws[1] = L.us;
+        gp.wsp[0] = L.g_sp;
+        gp.wsp[1] = L.u_sp;
+        gp.wss[0] = L.g_ss;
+        gp.wss[1] = L.u_ss;
+        gp.bp[0] = gp.bp[1] = x;
+        gp.active_e = active_e;
+        gp.active_off = active_off;
+        gp.sorted = sorted;
+        gp.tiles = tiles_gu;
+        gp.tile_n = counts;
+        gp.ohi = act_hi;
+        gp.olo = act_lo;
+        k_gemm<true><<<(unsigned)(cap_gu * rb_i), 64 * GemmShape<true>::WAVES, gemm_lds_bytes<true>(), s>>>(gp);
+        if (L.Is > 0 && !sh_stream) {
+            StageMark m2(prof, K3MOE_STAGE_SHARED_GATEUP, s);
+            GemmParams sp = gp;
+            sp.rows = L.Is;
+            sp.wb[0] = L.sh_gate;
+            sp.wb[1] = L.sh_up;
+            sp.ohi = ash_hi;
+            sp.olo = ash_lo;
+            sp.sh_blocks = ((T + TG - 1) / TG) * rb_s;
+            k_gemm<true><<<(unsigned)sp.sh_blocks, 64 * GemmShape<true>::WAVES, gemm_lds_bytes<true>(), s>>>(sp);
+        }
     }
-    if (L.Is > 0 && !sh_stream) {
-        StageMark m(prof, K3MOE_STAGE_SHARED_GATEUP, s);
-        GuGemmParams sp = gp;
-        sp.I = L.Is;
-        sp.wg = L.sh_gate;
-        sp.wu = L.sh_up;
-        sp.act_hi = ash_hi;
-        sp.act_lo = ash_lo;
-        const unsigned nblk = (unsigned)(((T + kGuTok - 1) / kGuTok) * rb_s);
-        k_gu_gemm<false><<<nblk, 64 * kGWaves, gu_gemm_lds_bytes<false>(), s>>>(sp);
-    }
-
-    DnGemmParams dp{};
-    dp.H = L.H;
-    dp.I = L.I;
-    dp.K = L.K;
-    dp.T = T;
-    dp.dp = L.dp;
-    dp.ds = L.ds;
-    dp.d_sp = L.d_sp;
-    dp.d_ss = L.d_ss;
-    dp.act_hi = act_hi;
-    dp.act_lo = act_lo;
-    dp.active_e = active_e;
-    dp.active_off = active_off;
-    dp.sorted = sorted;
-    dp.tiles = tiles_dn;
-    dp.tile_n = counts + 1;
-    dp.ys = ys;
     {
         StageMark m(prof, K3MOE_STAGE_DOWN, s);
         if (stream_dn) {
@@ -667,16 +527,32 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const in
                                                   sh_stream, act_hi, act_lo, ash_hi, ash_lo, ys, s);
             if (e != hipSuccess) return e;
         }
-        const unsigned nblk = (unsigned)(cap_dn * rb_h);
-        k_dn_gemm<true><<<nblk, 64 * kGWaves, dn_gemm_lds_bytes<true>(), s>>>(dp);
+        GemmParams dp{};
+        dp.rows = L.H;
+        dp.KD = L.I;
+        dp.K = L.K;
+        dp.T = T;
+        dp.wp[0] = dp.wp[1] = L.dp;
+        dp.ws[0] = dp.ws[1] = L.ds;
+        dp.wsp[0] = dp.wsp[1] = L.d_sp;
+        dp.wss[0] = dp.wss[1] = L.d_ss;
+        dp.bp[0] = act_hi;
+        dp.bp[1] = act_lo;
+        dp.active_e = active_e;
+        dp.active_off = active_off;
+        dp.sorted = sorted;
+        dp.tiles = tiles_dn;
+        dp.tile_n = counts + 1;
+        dp.ys = ys;
+        k_gemm<false><<<(unsigned)(cap_dn * rb_h), 64 * GemmShape<false>::WAVES, gemm_lds_bytes<false>(), s>>>(dp);
         if (L.Is > 0 && !sh_stream) {
-            DnGemmParams sp = dp;
-            sp.I = L.Is;
-            sp.wd = L.sh_down;
-            sp.act_hi = ash_hi;
-            sp.act_lo = ash_lo;
-            const unsigned nb2 = (unsigned)(((T + kDnTok - 1) / kDnTok) * rb_h);
-            k_dn_gemm<false><<<nb2, 64 * kGWaves, dn_gemm_lds_bytes<false>(), s>>>(sp);
+            GemmParams sp = dp;
+            sp.KD = L.Is;
+            sp.wb[0] = sp.wb[1] = L.sh_down;
+            sp.bp[0] = ash_hi;
+            sp.bp[1] = ash_lo;
+            sp.sh_blocks = ((T + TD - 1) / TD) * rb_h;
+            k_gemm<false><<<(unsigned)sp.sh_blocks, 64 * GemmShape<false>::WAVES, gemm_lds_bytes<false>(), s>>>(sp);
         }
     }
     return hipGetLastError();

@@ -209,20 +209,23 @@ __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const u
         }
     };
 
+    // Token loads go before weight loads: the LDS store of the next token
+    // group then waits only for the token loads (memory counters retire in
+    // issue order) while the weight loads stay in flight.
     Grp b0, b1;
     xload(0);
     gload(0, b0);
     xstore(0);
     __syncthreads();
     for (int gi = 0; gi < NG; gi += 2) {
-        gload(gi + 1, b1);
         xload(gi + 1);
+        gload(gi + 1, b1);
         compute(b0, 0);
         xstore(1);
         __syncthreads();
         if (gi + 1 >= NG) break;
-        gload(gi + 2, b0);
         xload(gi + 2);
+        gload(gi + 2, b0);
         compute(b1, 1);
         xstore(0);
         __syncthreads();
