@@ -2,9 +2,9 @@
 """Benchmark of the sigmoid-routed MXFP4 expert layer on one MI355X.
 
 One step = the whole hot path for one batch of synthetic tokens: route
-(router GEMV, sigmoid + bias top-k) and forward (token fp8 expansion,
-permutation, routed gate/up + activation, shared gate/up, down + router-order
-combine + shared down), through the C ABI on one HIP stream. Inputs are
+(router GEMV, sigmoid + bias top-k) and forward (permutation for batches,
+routed gate/up + activation, shared gate/up, down, shared down, router-order
+combine), through the C ABI on one HIP stream. Inputs are
 resident in HBM before the timed region starts.
 
 Workloads (full shape: hidden 7168, 896 experts, top-16, inter 1536, one bf16
@@ -138,7 +138,7 @@ def main():
     shared_bytes = 3 * Is * H * 2
     # per stage: weights read once, token side read, activations written/read
     # (4 B per element: fp32, or bf16 hi + lo), expert outputs staged in fp32
-    x_read = T * H * 4 * (1 + 1 / 32) if T == 1 else T * H * 2   # fp8 terms (one token) or bf16
+    x_read = T * H * 2   # the bf16 tokens
     act_b = T * K * I * 4 + T * Is * 4
     shared_in_gateup = stages["shared_gateup"][1] == 0  # no separate shared gate/up launch
     stage_bytes = {

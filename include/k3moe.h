@@ -164,7 +164,7 @@ k3moe_status k3moe_error_reset(k3moe_layer *layer, void *stream);
 typedef enum {
     K3MOE_STAGE_ROUTER = 0,         /* router logits, scores              */
     K3MOE_STAGE_TOPK = 1,           /* top-k, weights                     */
-    K3MOE_STAGE_XSPLIT = 2,         /* token fp8 expansion                */
+    K3MOE_STAGE_XSPLIT = 2,         /* reserved: no kernel records it     */
     K3MOE_STAGE_PERM = 3,           /* token -> expert permutation        */
     K3MOE_STAGE_GATEUP = 4,         /* routed gate/up MXFP4 + activation  */
     K3MOE_STAGE_SHARED_GATEUP = 5,  /* shared expert gate/up + activation */

@@ -44,9 +44,6 @@ WsLayout ws_layout(const k3moe_config &c, int64_t T)
         }
         L.rt_part = take(part);
     }
-    const int64_t T1 = std::min<int64_t>(T, 1);  // the fp8 token terms serve T = 1 only
-    L.xq = take((size_t)T1 * kXTerms * H);
-    L.xs = take((size_t)T1 * kXTerms * (H / 32));
     L.chunk_cnt = take(sizeof(int32_t) * nchunks * E);
     L.active_n = take(sizeof(int32_t));
     L.active_e = take(sizeof(int32_t) * E);

@@ -15,7 +15,6 @@ namespace k3moe {
 // Activation split widths (number of e4m3 terms in the fp8 expansion that
 // feeds the scaled MFMA's B operand): 4 for a bf16 token vector (exact) and
 // 4 for the fp32 expert activation.
-constexpr int kXTerms = 4;
 constexpr int kATerms = 4;
 constexpr int kMaxExperts = 4096;
 constexpr int kMaxTopk = 64;
@@ -26,7 +25,6 @@ constexpr int kPermChunk = 16;
 struct WsLayout {
     size_t sc, ch;            // router scores, fp32 [T][E] each
     size_t rt_part;           // batched router fp64 partial sums [slices][T][E]
-    size_t xq, xs;            // single token's fp8 terms [4][H], scales [4][H/32]
     size_t chunk_cnt;         // int32 [nchunks][E]
     size_t active_n;          // int32 [1]
     size_t active_e;          // int32 [E]

@@ -42,8 +42,39 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned u4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16f(uint32_t h) { return __uint_as_float(h << 16); }
+
+// E8M0 byte -> the fp32 factor 2^(s-127) for the scaled converter; byte 0 is
+// the subnormal 2^-127, byte 255 drops its group (factor 0).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s)
+{
+    return s == 255u ? 0.0f : __uint_as_float(s == 0u ? 0x00400000u : s << 23);
+}
+
+// 8 fp4 weights (one 32-bit word, low nibble first) -> 8 bf16, scaled exactly.
+__device__ __forceinline__ bf8 dequant8_bf16(uint32_t w, float scale)
+{
+    const bf2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+    const bf2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+    const bf2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+    const bf2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+    return bf8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+__device__ __forceinline__ bf8 as_bf8(u4 v)
+{
+    bf8 r;
+    __builtin_memcpy(&r, &v, 16);
+    return r;
+}
+
+__device__ __forceinline__ v4f mfma_bf16_32(const bf8 &a, const bf8 &b, v4f c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 __device__ __forceinline__ v4f mfma_fp4_fp8(const v8i &a, const v8i &b, v4f c, int sa, int sb)
 {
@@ -377,15 +408,6 @@ __global__ __launch_bounds__(64) void k_topk(const float *__restrict__ sc, const
 }
 
 // ---------------------------------------------------------------------------
-// Token activations -> kXTerms e4m3 terms per element, one E8M0 scale per
-// term per 32-element block. Thread per element; a half-wave is one block.
-__device__ __forceinline__ void xsplit_slab(const uint16_t *__restrict__ x, int64_t n, int H, int64_t slab,
-                                            uint8_t *__restrict__ xq, uint8_t *__restrict__ xs);
-__global__ __launch_bounds__(256) void k_xsplit(const uint16_t *__restrict__ x, int64_t n, int H,
-                                                uint8_t *__restrict__ xq, uint8_t *__restrict__ xs)
-{
-    xsplit_slab(x, n, H, blockIdx.x, xq, xs);  // n is a multiple of 32: half-waves leave together
-}
 
 // ---------------------------------------------------------------------------
 // Token -> expert permutation: a stable counting sort of the T*k assignments
@@ -489,23 +511,6 @@ __device__ void perm_single(const int32_t *__restrict__ idx, int T, int K, int E
     }
 }
 
-// Token fp8 expansion for one 256-element slab (see k_xsplit).
-__device__ __forceinline__ void xsplit_slab(const uint16_t *__restrict__ x, int64_t n, int H, int64_t slab,
-                                            uint8_t *__restrict__ xq, uint8_t *__restrict__ xs)
-{
-    const int64_t i = slab * 256 + threadIdx.x;
-    if (i >= n) return;
-    const int64_t t = i / H;
-    const int col = (int)(i - t * H);
-    int code[kXTerms], sb[kXTerms];
-    split_e4m3_32<kXTerms>(bf16f(x[i]), code, sb);
-#pragma unroll
-    for (int term = 0; term < kXTerms; ++term) {
-        xq[(t * kXTerms + term) * H + col] = (uint8_t)code[term];
-        if ((threadIdx.x & 31) == 0) xs[(t * kXTerms + term) * (H >> 5) + (col >> 5)] = (uint8_t)sb[term];
-    }
-}
-
 // Small batches (T <= kPermChunk): the whole permutation in one block.
 __global__ __launch_bounds__(256) void k_perm_small(const int32_t *__restrict__ idx, int T, int K, int E,
                                                     int32_t *active_n, int32_t *active_e,
@@ -582,7 +587,6 @@ struct GateUpParams {
     int H, I, K, E, act, Is;
     float b1, b2;
     const uint16_t *x;
-    const uint8_t *xq, *xs;
     const int32_t *idx;
     float *act_f;  // fp32 activations [k][I]
     const uint16_t *sh_gate, *sh_up;
@@ -612,12 +616,12 @@ constexpr int kGuUnitRows = 16;                // rows per routed unit
 constexpr int kGuShMaxRows = 4;                // shared rows per pass of wave 3
 constexpr int kXqPad = 64;                     // LDS term-row padding (banks)
 constexpr int kScPad = 16;                     // LDS scale-row padding (banks)
-constexpr int kGuStgQ = 8;                     // token-term staging copies per thread
+constexpr int kGuStgQ = 8;                     // token staging copies per thread (16 B of bf16)
 constexpr int kGuStgS = 6;                     // scale-row staging copies per thread
 
 __host__ __device__ constexpr int gu_dec_lds_bytes(int H)
 {
-    return 4 * (H + kXqPad) + 4 * (H / 32) + kGuDecUnits * 2 * kGuUnitRows * (H / 32 + kScPad);
+    return 2 * H + kGuDecUnits * 2 * kGuUnitRows * (H / 32 + kScPad);
 }
 
 // Wave 3 of a gate/up block: shared rows [r0, r1) of gate and up (bf16,
@@ -684,20 +688,18 @@ __device__ void shared_gateup_rows(const GateUpParams &p, int r0, int r1)
 template <bool WIDE>
 __global__ __launch_bounds__(64 * kGuDecWaves) void k_gateup_dec(GateUpParams p)
 {
-    static_assert(kXTerms == 4, "4-term expansion: term = column % 4");
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int grp = lane >> 4, col = lane & 15, term = col & 3;
+    const int grp = lane >> 4, col = lane & 15;
     const int H = p.H, KS = H >> 7, SR = H >> 5, NCH = (KS + 3) >> 2;
-    const int XQS = H + kXqPad, SRP = SR + kScPad;
+    const int SRP = SR + kScPad;
     const int RT = p.I / kGuUnitRows;
     const int nunits = p.K * RT;
     const int b = blockIdx.x;
 
     extern __shared__ __align__(16) uint8_t lds[];
-    uint8_t *xq_l = lds;                  // [4][H + pad]  token terms
-    uint8_t *xs_l = xq_l + 4 * XQS;       // [4][H/32]     their scales
-    uint8_t *sc_l = xs_l + 4 * SR;        // [3][2][16][H/32 + pad] unit scale rows
+    uint8_t *x_l = lds;                   // [H]           the token, bf16
+    uint8_t *sc_l = x_l + 2 * H;          // [3][2][16][H/32 + pad] unit scale rows
 
     // this wave's routed unit (waves 0..2) and its expert
     const int u = kGuDecUnits * b + wave;
@@ -727,14 +729,13 @@ __global__ __launch_bounds__(64 * kGuDecWaves) void k_gateup_dec(GateUpParams p)
     // loads). A unit's scale rows are 16 consecutive rows, contiguous.
     Chunk b0, b1;
     if constexpr (WIDE) {  // SR % 16 == 0
-        const int nxq = H >> 2, nxs = SR >> 2;  // u4 counts
+        const int nxq = H >> 3;  // u4 count of the bf16 token
         const int nrow = SR >> 4, nsc = kGuDecUnits * 2 * kGuUnitRows * nrow;
-        u4 tq[kGuStgQ], ts[kGuStgS], tx;
+        u4 tq[kGuStgQ], ts[kGuStgS];
 #pragma unroll
         for (int q = 0; q < kGuStgQ; ++q) {
             const int i = min((int)threadIdx.x + q * 64 * kGuDecWaves, nxq - 1);
-            const int t = i / (H >> 4), o = i - t * (H >> 4);
-            tq[q] = *reinterpret_cast<const u4 *>(p.xq + (size_t)t * H + 16 * o);
+            tq[q] = *reinterpret_cast<const u4 *>(p.x + 8 * i);
         }
 #pragma unroll
         for (int q = 0; q < kGuStgS; ++q) {
@@ -748,21 +749,16 @@ __global__ __launch_bounds__(64 * kGuDecWaves) void k_gateup_dec(GateUpParams p)
             const uint8_t *sbase = mat ? p.us + se * p.u_ss : p.gs + se * p.g_ss;
             ts[q] = *reinterpret_cast<const u4 *>(sbase + (size_t)srt * kGuUnitRows * SR + 16 * rem2);
         }
-        tx = *reinterpret_cast<const u4 *>(p.xs + 16 * min((int)threadIdx.x, nxs - 1));
         __builtin_amdgcn_sched_barrier(0);
         if (active) {
             load(0, b0);
             load(min(1, NCH - 1), b1);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if ((int)threadIdx.x < nxs) *reinterpret_cast<u4 *>(xs_l + 16 * threadIdx.x) = tx;
 #pragma unroll
         for (int q = 0; q < kGuStgQ; ++q) {
             const int i = (int)threadIdx.x + q * 64 * kGuDecWaves;
-            if (i < nxq) {
-                const int t = i / (H >> 4), o = i - t * (H >> 4);
-                *reinterpret_cast<u4 *>(xq_l + t * XQS + 16 * o) = tq[q];
-            }
+            if (i < nxq) *reinterpret_cast<u4 *>(x_l + 16 * i) = tq[q];
         }
 #pragma unroll
         for (int q = 0; q < kGuStgS; ++q) {
@@ -773,8 +769,7 @@ __global__ __launch_bounds__(64 * kGuDecWaves) void k_gateup_dec(GateUpParams p)
             }
         }
     } else {  // short rows (small layers): byte copies
-        for (int i = threadIdx.x; i < 4 * H; i += blockDim.x) xq_l[(i / H) * XQS + i % H] = p.xq[i];
-        for (int i = threadIdx.x; i < 4 * SR; i += blockDim.x) xs_l[i] = p.xs[i];
+        for (int i = threadIdx.x; i < H; i += blockDim.x) reinterpret_cast<uint16_t *>(x_l)[i] = p.x[i];
         for (int i = threadIdx.x; i < kGuDecUnits * 2 * kGuUnitRows * SR; i += blockDim.x) {
             const int row = i / SR, o = i - row * SR;
             const int un = row / (2 * kGuUnitRows), mat = (row / kGuUnitRows) & 1, r = row % kGuUnitRows;
@@ -801,40 +796,39 @@ __global__ __launch_bounds__(64 * kGuDecWaves) void k_gateup_dec(GateUpParams p)
     }
     if (!active) return;
 
-    const uint8_t *xb = xq_l + term * XQS + grp * 16;  // B column = term of token 0
-    const uint8_t *xsr = xs_l + term * SR;
+    // B operand: the bf16 token, the same in every column (columns 1..15 are
+    // copies). Lane group grp's 16-byte weight load of 128-K step k holds
+    // K = 128k + 32 grp + [0, 32); MFMA sub-step ss takes K = 128k + 32 grp +
+    // 8 ss + [0, 8) on both sides.
+    const uint8_t *xb = x_l + 64 * grp;
     const uint8_t *s_g = sc_l + (wave * 2 * kGuUnitRows + (lane & 15)) * SRP;  // this lane's gate row
     const uint8_t *s_u = s_g + kGuUnitRows * SRP;
     v4f accg = v4f{0.0f, 0.0f, 0.0f, 0.0f}, accu = accg;
     auto compute = [&](int c, const Chunk &bf) {
-        uint32_t sg, su, sx;
+        uint32_t sg, su;
         if constexpr (WIDE) {
             sg = gather_scales(*reinterpret_cast<const u4 *>(s_g + 16 * c), grp);
             su = gather_scales(*reinterpret_cast<const u4 *>(s_u + 16 * c), grp);
-            sx = gather_scales(*reinterpret_cast<const u4 *>(xsr + 16 * c), grp);
-        } else {  // short rows: steps past K left at 127 (never multiplied)
-            sg = su = sx = 0x7f7f7f7fu;
+        } else {  // short rows: steps past K are never multiplied
+            sg = su = 0x7f7f7f7fu;
             for (int st = 0; st < 4 && 4 * c + st < KS; ++st) {
                 const int o = (4 * c + st) * 4 + grp, sh8 = 8 * st;
                 const uint32_t m = ~(0xffu << sh8);
                 sg = (sg & m) | ((uint32_t)s_g[o] << sh8);
                 su = (su & m) | ((uint32_t)s_u[o] << sh8);
-                sx = (sx & m) | ((uint32_t)xsr[o] << sh8);
             }
         }
-        const uint32_t dg = ff_bytes(sg), du = ff_bytes(su);  // scale byte 255: group drops out
-        sg ^= dg;
-        su ^= du;
         static_for<0, 4>([&](auto s_) {
             constexpr int st = decltype(s_)::value;
             if (4 * c + st < KS) {
                 const uint32_t k = 4 * c + st;
-                const v8i B = b_operand(*reinterpret_cast<const u4 *>(xb + k * 128),
-                                        *reinterpret_cast<const u4 *>(xb + k * 128 + 64));
-                const u4 ag = ((dg >> (8 * st + 7)) & 1u) ? u4{0u, 0u, 0u, 0u} : bf.a[st][0];
-                const u4 au = ((du >> (8 * st + 7)) & 1u) ? u4{0u, 0u, 0u, 0u} : bf.a[st][1];
-                accg = mfma_fp4_fp8_sel<st>(a_operand(ag), B, accg, (int)sg, (int)sx);
-                accu = mfma_fp4_fp8_sel<st>(a_operand(au), B, accu, (int)su, (int)sx);
+                const float fg = e8m0_to_f32((sg >> (8 * st)) & 0xffu), fu = e8m0_to_f32((su >> (8 * st)) & 0xffu);
+#pragma unroll
+                for (int ss = 0; ss < 4; ++ss) {
+                    const bf8 B = as_bf8(*reinterpret_cast<const u4 *>(xb + k * 256 + 16 * ss));
+                    accg = mfma_bf16_32(dequant8_bf16(bf.a[st][0][ss], fg), B, accg);
+                    accu = mfma_bf16_32(dequant8_bf16(bf.a[st][1][ss], fu), B, accu);
+                }
             }
         });
     };
@@ -845,21 +839,13 @@ __global__ __launch_bounds__(64 * kGuDecWaves) void k_gateup_dec(GateUpParams p)
         load(min(c + 3, NCH - 1), b1);
     }
 
-    // columns 4m..4m+3 hold the 4 terms: add them (lane 16g gets rows 4g..4g+3)
-    float g[4], uu[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        g[r] = accg[r] + __shfl_xor(accg[r], 1);
-        g[r] += __shfl_xor(g[r], 2);
-        uu[r] = accu[r] + __shfl_xor(accu[r], 1);
-        uu[r] += __shfl_xor(uu[r], 2);
-    }
+    // every column holds the token's result: lane 16g (column 0) has rows 4g..4g+3
     if (col == 0) {
         float4 a4;
-        a4.x = act_fn(g[0], uu[0], p.act, p.b1, p.b2);
-        a4.y = act_fn(g[1], uu[1], p.act, p.b1, p.b2);
-        a4.z = act_fn(g[2], uu[2], p.act, p.b1, p.b2);
-        a4.w = act_fn(g[3], uu[3], p.act, p.b1, p.b2);
+        a4.x = act_fn(accg[0], accu[0], p.act, p.b1, p.b2);
+        a4.y = act_fn(accg[1], accu[1], p.act, p.b1, p.b2);
+        a4.z = act_fn(accg[2], accu[2], p.act, p.b1, p.b2);
+        a4.w = act_fn(accg[3], accu[3], p.act, p.b1, p.b2);
         *reinterpret_cast<float4 *>(p.act_f + (size_t)slot * p.I + rt * kGuUnitRows + 4 * grp) = a4;
     }
 }
@@ -1137,42 +1123,56 @@ __global__ __launch_bounds__(64 * kDnDecWaves) void k_down_dec(DownDecParams p)
 // Router-order combine: out[t][o] = sum_j w[t][j] * ys[t][j][o] (j = 0..k-1
 // in order, one fma each), then + ys[t][k][o] (the shared expert, if any).
 // A slot with an out-of-range id adds nothing (its staging row is not read)
-// and is counted once here.
-__global__ __launch_bounds__(256) void k_combine(const float *__restrict__ ys, const float *__restrict__ w,
-                                                 const int32_t *__restrict__ idx, int T, int K, int H,
-                                                 int E, int shared, float *__restrict__ out,
-                                                 unsigned long long *errors)
+// and is counted once here. A thread takes 4 consecutive outputs (16-byte
+// loads); the loads of up to 16 slots are issued before the first fma.
+constexpr int kCombineThreads = 64;
+__global__ __launch_bounds__(kCombineThreads) void k_combine(const float *__restrict__ ys,
+                                                             const float *__restrict__ w,
+                                                             const int32_t *__restrict__ idx, int T, int K,
+                                                             int H, int E, int shared, float *__restrict__ out,
+                                                             unsigned long long *errors)
 {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (i < (int64_t)T * H) {
-        const int64_t t = i / H;
-        const int o = (int)(i - t * H);
+    const int64_t i4 = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x;  // float4 index
+    const int H4 = H >> 2;
+    if (i4 < (int64_t)T * H4) {
+        const int64_t t = i4 / H4;
+        const int o = (int)(i4 - t * H4) * 4;
         const float *y = ys + (size_t)t * (K + 1) * H + o;
         const float *wt = w + (size_t)t * K;
         const int32_t *it = idx + (size_t)t * K;
-        float acc = 0.0f;
-        int j = 0;
-        for (; j + 8 <= K; j += 8) {  // 8 loads in flight, then 8 fmas in order
-            float v[8];
-            bool ok[8];
+        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        for (int j0 = 0; j0 < K; j0 += 16) {
+            float4 v[16];
+            bool ok[16];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int e = it[j + q];
-                ok[q] = e >= 0 && e < E;
-                v[q] = ok[q] ? y[(size_t)(j + q) * H] : 0.0f;
+            for (int q = 0; q < 16; ++q) {
+                const int j = j0 + q;
+                const int e = it[min(j, K - 1)];
+                ok[q] = j < K && e >= 0 && e < E;
+                v[q] = ok[q] ? *reinterpret_cast<const float4 *>(y + (size_t)j * H) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
             }
 #pragma unroll
-            for (int q = 0; q < 8; ++q) acc = ok[q] ? fmaf(wt[j + q], v[q], acc) : acc;
+            for (int q = 0; q < 16; ++q) {
+                if (ok[q]) {
+                    const float wj = wt[min(j0 + q, K - 1)];
+                    acc.x = fmaf(wj, v[q].x, acc.x);
+                    acc.y = fmaf(wj, v[q].y, acc.y);
+                    acc.z = fmaf(wj, v[q].z, acc.z);
+                    acc.w = fmaf(wj, v[q].w, acc.w);
+                }
+            }
         }
-        for (; j < K; ++j) {
-            const int e = it[j];
-            if (e >= 0 && e < E) acc = fmaf(wt[j], y[(size_t)j * H], acc);
+        if (shared) {
+            const float4 sv = *reinterpret_cast<const float4 *>(y + (size_t)K * H);
+            acc.x += sv.x;
+            acc.y += sv.y;
+            acc.z += sv.z;
+            acc.w += sv.w;
         }
-        if (shared) acc += y[(size_t)K * H];
-        out[i] = acc;
+        *reinterpret_cast<float4 *>(out + (size_t)t * H + o) = acc;
     }
-    if (blockIdx.x == 0 && threadIdx.x < 64)
-        for (int64_t a = threadIdx.x; a < (int64_t)T * K; a += 64)
+    if (blockIdx.x == 0)
+        for (int64_t a = threadIdx.x; a < (int64_t)T * K; a += kCombineThreads)
             if (idx[a] < 0 || idx[a] >= E) atomicAdd(errors, 1ull);
 }
 
@@ -1248,7 +1248,7 @@ static int down_blocks_per_slot(const LayerView &L, int ncu)
 
 static bool decode_path_ok(const LayerView &L)
 {
-    const bool gu = L.H % 512 != 0 || L.H / 4 <= 64 * kGuDecWaves * kGuStgQ;
+    const bool gu = L.H % 512 != 0 || L.H / 8 <= 64 * kGuDecWaves * kGuStgQ;
     const bool gu_sc = L.H % 512 != 0 || kGuDecUnits * 2 * kGuUnitRows * (L.H / 512) <= 64 * kGuDecWaves * kGuStgS;
     const bool dn = L.I % 512 != 0 || (L.I / 4 <= 64 * kDnDecWaves * kDnStgQ &&
                                        kDnMaxTiles * 16 * (L.I / 512) <= 64 * kDnDecWaves * kDnStgS);
@@ -1258,15 +1258,11 @@ static bool decode_path_ok(const LayerView &L)
 // T = 1: token fp8 expansion, gate/up, down, router-order combine. The
 // router slots are the assignment list (no permutation).
 static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const int32_t *idx,
-                                    const float *w, float *out, uint8_t *xq, uint8_t *xs, float *act,
-                                    float *ash, char *ys_base, hipStream_t s, Profiler *prof)
+                                    const float *w, float *out, float *act, float *ash, char *ys_base,
+                                    hipStream_t s, Profiler *prof)
 {
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    {
-        StageMark m(prof, K3MOE_STAGE_XSPLIT, s);
-        k_xsplit<<<(unsigned)((L.H + 255) / 256), 256, 0, s>>>(x, L.H, L.H, xq, xs);
-    }
     GateUpParams gp{};
     gp.gp = L.gp;
     gp.gs = L.gs;
@@ -1285,8 +1281,6 @@ static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const
     gp.b1 = L.b1;
     gp.b2 = L.b2;
     gp.x = x;
-    gp.xq = xq;
-    gp.xs = xs;
     gp.idx = idx;
     gp.act_f = act;
     gp.sh_gate = L.sh_gate;
@@ -1330,8 +1324,8 @@ static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const
     }
     {
         StageMark m(prof, K3MOE_STAGE_COMBINE, s);
-        k_combine<<<(unsigned)((L.H + 255) / 256), 256, 0, s>>>(ys, w, idx, 1, L.K, L.H, L.E, L.Is > 0, out,
-                                                               L.errors);
+        k_combine<<<(unsigned)((L.H / 4 + kCombineThreads - 1) / kCombineThreads), kCombineThreads, 0, s>>>(
+            ys, w, idx, 1, L.K, L.H, L.E, L.Is > 0, out, L.errors);
     }
     return hipGetLastError();
 }
@@ -1349,8 +1343,7 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const in
     float *ys = reinterpret_cast<float *>(ws + lay.ys);
 
     if (T == 1 && decode_path_ok(L))
-        return launch_forward_t1(L, x, idx, w, out, reinterpret_cast<uint8_t *>(ws + lay.xq),
-                                 reinterpret_cast<uint8_t *>(ws + lay.xs), reinterpret_cast<float *>(ws + lay.act),
+        return launch_forward_t1(L, x, idx, w, out, reinterpret_cast<float *>(ws + lay.act),
                                  reinterpret_cast<float *>(ws + lay.ash), ws + lay.ys, s, prof);
     const int nchunks = (T + kPermChunk - 1) / kPermChunk;
     {
@@ -1379,9 +1372,9 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const in
     if (e != hipSuccess) return e;
     {
         StageMark m(prof, K3MOE_STAGE_COMBINE, s);
-        const int64_t n = (int64_t)T * L.H;
-        k_combine<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(ys, w, idx, T, L.K, L.H, L.E, L.Is > 0, out,
-                                                             L.errors);
+        const int64_t n4 = (int64_t)T * L.H / 4;
+        k_combine<<<(unsigned)((n4 + kCombineThreads - 1) / kCombineThreads), kCombineThreads, 0, s>>>(
+            ys, w, idx, T, L.K, L.H, L.E, L.Is > 0, out, L.errors);
     }
     return hipGetLastError();
 }
