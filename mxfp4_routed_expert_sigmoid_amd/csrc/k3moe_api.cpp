@@ -52,6 +52,15 @@ WsLayout ws_layout(const k3moe_config &c, int64_t T)
     L.act = take((size_t)T * K * 4 * I);
     L.ash = take(sizeof(float) * T * std::max<int64_t>(Is, 1));
     L.ys = take(sizeof(float) * T * (K + 1) * H);
+    {
+        // the slice count is non-increasing in T: the largest buffer over T' <= T
+        size_t part = 0;
+        for (int64_t t = 2; t <= std::min<int64_t>(T, 4096); ++t) {
+            const int S = stream_shared_slices((int)t);
+            if (S > 1) part = std::max(part, sizeof(float) * S * t * 2 * Is);
+        }
+        L.sh_part = take(part);
+    }
     L.tiles_gu = take(sizeof(int2) * grouped_tile_cap_gu(T, (int)K, (int)E));
     L.tiles_dn = take(sizeof(int2) * grouped_tile_cap_dn(T, (int)K, (int)E));
     L.light = take(sizeof(int32_t) * 2 * E);

@@ -459,8 +459,8 @@ size_t grouped_tile_cap_dn(int64_t T, int K, int E) { return grouped_tile_cap(T,
 hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const int32_t *active_n,
                           const int32_t *active_e, const int32_t *active_off, const int32_t *sorted,
                           uint16_t *act_hi, uint16_t *act_lo, uint16_t *ash_hi, uint16_t *ash_lo,
-                          int2 *tiles_gu, int2 *tiles_dn, int32_t *light, int32_t *counts, float *ys,
-                          hipStream_t s, Profiler *prof)
+                          float *sh_part, int2 *tiles_gu, int2 *tiles_dn, int32_t *light, int32_t *counts,
+                          float *ys, hipStream_t s, Profiler *prof)
 {
     static const bool lds_set = set_lds_limits();  // once per process (thread-safe static)
     (void)lds_set;
@@ -480,7 +480,7 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const in
         StageMark m(prof, K3MOE_STAGE_GATEUP, s);
         if (stream) {
             const hipError_t e = launch_stream_gu(L, x, T, active_e, active_off, sorted, light_gu, counts + 2,
-                                                  sh_stream, act_hi, act_lo, ash_hi, ash_lo, s);
+                                                  sh_stream, act_hi, act_lo, ash_hi, ash_lo, sh_part, s);
             if (e != hipSuccess) return e;
         }
         GemmParams gp{};

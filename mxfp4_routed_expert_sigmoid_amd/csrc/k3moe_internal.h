@@ -33,6 +33,7 @@ struct WsLayout {
     size_t act;               // routed activations, 4 bytes per element [T*k][I]:
                               //   fp32 (one token), or bf16 hi then bf16 lo planes
     size_t ash;               // shared activations, 4 bytes per element [T][I_s], same forms
+    size_t sh_part;           // shared gate/up fp32 slice sums [slices][T][2][I_s] (small batches)
     size_t ys;                // expert outputs fp32 [T][k + 1][H] (slot k: shared expert)
     size_t tiles_gu, tiles_dn;  // grouped-GEMM tile lists, int2 each
     size_t light;             // int32 [2][E]: experts for the weight-streaming kernels (gate/up, down)
@@ -119,18 +120,19 @@ size_t grouped_tile_cap_dn(int64_t T, int K, int E);
 hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const int32_t *active_n,
                           const int32_t *active_e, const int32_t *active_off, const int32_t *sorted,
                           uint16_t *act_hi, uint16_t *act_lo, uint16_t *ash_hi, uint16_t *ash_lo,
-                          int2 *tiles_gu, int2 *tiles_dn, int32_t *light, int32_t *counts, float *ys,
-                          hipStream_t s, Profiler *prof);
+                          float *sh_part, int2 *tiles_gu, int2 *tiles_dn, int32_t *light, int32_t *counts,
+                          float *ys, hipStream_t s, Profiler *prof);
 
 // Weight-streaming kernels for experts with few tokens (k3moe_stream.hip).
 bool stream_path_ok(const LayerView &L);
 bool stream_down_ok(const LayerView &L);
 int stream_max_tokens();
+int stream_shared_slices(int T);
 bool stream_shared_ok(const LayerView &L, int T);
 hipError_t launch_stream_gu(const LayerView &L, const uint16_t *x, int T, const int32_t *active_e,
                             const int32_t *active_off, const int32_t *sorted, const int32_t *light,
                             const int32_t *light_n, bool with_shared, uint16_t *act_hi, uint16_t *act_lo,
-                            uint16_t *ash_hi, uint16_t *ash_lo, hipStream_t s);
+                            uint16_t *ash_hi, uint16_t *ash_lo, float *sh_part, hipStream_t s);
 hipError_t launch_stream_dn(const LayerView &L, int T, const int32_t *active_e, const int32_t *active_off,
                             const int32_t *sorted, const int32_t *light, const int32_t *light_n,
                             bool with_shared, const uint16_t *act_hi, const uint16_t *act_lo,

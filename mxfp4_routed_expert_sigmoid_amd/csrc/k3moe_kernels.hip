@@ -1365,7 +1365,8 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const in
     uint16_t *ash_hi = reinterpret_cast<uint16_t *>(ws + lay.ash);
     uint16_t *ash_lo = ash_hi + (size_t)T * L.Is;
     hipError_t e = launch_grouped(L, x, T, active_n, active_e, active_off, sorted, act_hi, act_lo, ash_hi,
-                                  ash_lo, reinterpret_cast<int2 *>(ws + lay.tiles_gu),
+                                  ash_lo, reinterpret_cast<float *>(ws + lay.sh_part),
+                                  reinterpret_cast<int2 *>(ws + lay.tiles_gu),
                                   reinterpret_cast<int2 *>(ws + lay.tiles_dn),
                                   reinterpret_cast<int32_t *>(ws + lay.light),
                                   reinterpret_cast<int32_t *>(ws + lay.tile_n), ys, s, prof);

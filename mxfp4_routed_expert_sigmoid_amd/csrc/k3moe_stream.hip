@@ -101,25 +101,30 @@ struct GuStreamParams {
     const int32_t *active_e, *active_off, *sorted;
     const int32_t *light, *light_n;
     int sh_blocks;            // leading blocks that run the shared expert
+    int sh_slices;            // hidden-dimension slices of a shared block (1: whole K)
+    float *sh_part;           // sh_slices > 1: fp32 partial sums [slice][T][gate, up][I_s]
     uint16_t *act_hi, *act_lo, *ash_hi, *ash_lo;
 };
 
 constexpr int gu_stream_lds_bytes() { return 2 * kSTok * brow_bytes<true>() + kSTok * 4; }
 
 // The wave's part of one block: gate and up rows row0 + 16 rf + l16 (rf = 0, 1)
-// of an item with token rows tok_l[0..15] (clamped to the item's tokens).
+// of an item with token rows tok_l[0..15] (clamped to the item's tokens),
+// over the K groups [g0, g1). part == null: the activation goes to ohi/olo
+// rows orow0 + column; else the fp32 gate and up sums go to
+// part[(orow0 + column) * 2 + {0, 1}][row] (a slice's partials).
 template <bool FP4>
 __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const uint8_t *wg, const uint8_t *wu,
                                                 const uint8_t *sg, const uint8_t *su, int rows, int row0,
                                                 const int *tok_l, int n, uint8_t *B_l, uint16_t *ohi,
-                                                uint16_t *olo, int64_t orow0, int ostride)
+                                                uint16_t *olo, int64_t orow0, int ostride, int g0, int g1,
+                                                float *part)
 {
     constexpr int GK = group_k<FP4>();
     constexpr int BROW = brow_bytes<FP4>();
     constexpr int BU4 = GK * 2 / 16;                           // u4 per token row per group
     constexpr int NB = (kSTok * BU4 + 64 * kSWaves - 1) / (64 * kSWaves);  // staging u4 per thread
     const int H = p.H, tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
-    const int NG = H / GK;
     const size_t rowb = FP4 ? (size_t)H / 2 : (size_t)H * 2;
     const uint8_t *wr[2][2];
     const uint8_t *sr[2][2] = {{nullptr, nullptr}, {nullptr, nullptr}};
@@ -140,7 +145,7 @@ __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const u
         u4 s[2][2];            // FP4: the group's 16 scale bytes per row
     };
     auto gload = [&](int gi, Grp &b) {
-        const int gc = min(gi, NG - 1);
+        const int gc = min(gi, g1 - 1);
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -153,7 +158,7 @@ __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const u
     };
     u4 xs[NB];
     auto xload = [&](int gi) {
-        const int gc = min(gi, NG - 1);
+        const int gc = min(gi, g1 - 1);
 #pragma unroll
         for (int q = 0; q < NB; ++q) {
             const int v = min(tid + 64 * kSWaves * q, kSTok * BU4 - 1);
@@ -213,17 +218,17 @@ __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const u
     // group then waits only for the token loads (memory counters retire in
     // issue order) while the weight loads stay in flight.
     Grp b0, b1;
-    xload(0);
-    gload(0, b0);
+    xload(g0);
+    gload(g0, b0);
     xstore(0);
     __syncthreads();
-    for (int gi = 0; gi < NG; gi += 2) {
+    for (int gi = g0; gi < g1; gi += 2) {
         xload(gi + 1);
         gload(gi + 1, b1);
         compute(b0, 0);
         xstore(1);
         __syncthreads();
-        if (gi + 1 >= NG) break;
+        if (gi + 1 >= g1) break;
         xload(gi + 2);
         gload(gi + 2, b0);
         compute(b1, 1);
@@ -231,6 +236,20 @@ __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const u
         __syncthreads();
     }
 
+    if (part) {  // a slice's fp32 partial sums
+        if (l16 < n) {
+#pragma unroll
+            for (int rf = 0; rf < 2; ++rf) {
+                const int row = row0 + 16 * rf + 4 * g;
+                if (row >= rows) continue;
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    *reinterpret_cast<float4 *>(part + ((size_t)(orow0 + l16) * 2 + m) * rows + row) =
+                        float4{acc[m][rf][0], acc[m][rf][1], acc[m][rf][2], acc[m][rf][3]};
+            }
+        }
+        return;
+    }
     // epilogue: lane holds rows 4g + i (i = 0..3) of token column l16
     if (l16 < n) {
 #pragma unroll
@@ -261,15 +280,19 @@ __global__ __launch_bounds__(64 * kSWaves) void k_gu_stream(GuStreamParams p)
     uint8_t *B_l = lds + kSTok * 4;
     const int wave = threadIdx.x >> 6;
     int b = blockIdx.x;
-    if (b < p.sh_blocks) {  // shared expert: token group tg, rows [rb*128, rb*128 + 128) of I_s
-        const int RB = p.Is / kSBlkRows;
-        const int tg = b / RB, rb = b - tg * RB;
+    if (b < p.sh_blocks) {  // shared expert: token group tg, rows [rb*128, rb*128 + 128) of I_s, slice ks
+        const int RB = p.Is / kSBlkRows, S = p.sh_slices;
+        const int ks = b % S, tb = b / S;
+        const int tg = tb / RB, rb = tb - tg * RB;
         const int t0 = tg * kSTok, n = min(kSTok, p.T - t0);
+        const int NG = p.H / group_k<false>();
         if (threadIdx.x < kSTok) tok_l[threadIdx.x] = t0 + min((int)threadIdx.x, n - 1);
         __syncthreads();
         gu_stream_block<false>(p, reinterpret_cast<const uint8_t *>(p.sh_gate),
                                reinterpret_cast<const uint8_t *>(p.sh_up), nullptr, nullptr, p.Is,
-                               rb * kSBlkRows + wave * kSRows, tok_l, n, B_l, p.ash_hi, p.ash_lo, t0, p.Is);
+                               rb * kSBlkRows + wave * kSRows, tok_l, n, B_l, p.ash_hi, p.ash_lo, t0, p.Is,
+                               NG * ks / S, NG * (ks + 1) / S,
+                               S > 1 ? p.sh_part + (size_t)ks * p.T * 2 * p.Is : nullptr);
         return;
     }
     b -= p.sh_blocks;
@@ -281,7 +304,30 @@ __global__ __launch_bounds__(64 * kSWaves) void k_gu_stream(GuStreamParams p)
     if (threadIdx.x < kSTok) tok_l[threadIdx.x] = p.sorted[off + min((int)threadIdx.x, n - 1)] / p.K;
     __syncthreads();
     gu_stream_block<true>(p, p.gp + e * p.g_sp, p.up + e * p.u_sp, p.gs + e * p.g_ss, p.us + e * p.u_ss, p.I,
-                          rb * kSBlkRows + wave * kSRows, tok_l, n, B_l, p.act_hi, p.act_lo, off, p.I);
+                          rb * kSBlkRows + wave * kSRows, tok_l, n, B_l, p.act_hi, p.act_lo, off, p.I, 0,
+                          p.H / group_k<true>(), nullptr);
+}
+
+// Shared expert's slices -> activation: g and u summed over the slices in
+// order, act(g, u) as bf16 hi + lo.
+__global__ __launch_bounds__(256) void k_sh_act(const float *__restrict__ part, int S, int T, int Is, int act,
+                                                float b1, float b2, uint16_t *__restrict__ ash_hi,
+                                                uint16_t *__restrict__ ash_lo)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)T * Is) return;
+    const int64_t t = i / Is;
+    const int r = (int)(i - t * Is);
+    float gs = 0.0f, us = 0.0f;
+    for (int k = 0; k < S; ++k) {
+        const float *pk = part + ((size_t)k * T + t) * 2 * Is;
+        gs += pk[r];
+        us += pk[Is + r];
+    }
+    const float a = act_fn(gs, us, act, b1, b2);
+    const uint16_t h = bf16_rne(a);
+    ash_hi[i] = h;
+    ash_lo[i] = bf16_rne(a - bf16f(h));
 }
 
 // ---------------------------------------------------------------------------
@@ -464,10 +510,15 @@ int stream_max_tokens() { return kSTok; }
 
 bool stream_shared_ok(const LayerView &L, int T) { return L.Is > 0 && T <= 8 * kSTok && stream_down_ok(L); }
 
+// Slices of the shared expert's hidden dimension for small batches, where
+// its few gate/up blocks (one per 128 rows and token group) would otherwise
+// outlast the routed experts' blocks.
+int stream_shared_slices(int T) { return T <= 2 * kSTok ? 8 : 1; }
+
 hipError_t launch_stream_gu(const LayerView &L, const uint16_t *x, int T, const int32_t *active_e,
                             const int32_t *active_off, const int32_t *sorted, const int32_t *light,
                             const int32_t *light_n, bool with_shared, uint16_t *act_hi, uint16_t *act_lo,
-                            uint16_t *ash_hi, uint16_t *ash_lo, hipStream_t s)
+                            uint16_t *ash_hi, uint16_t *ash_lo, float *sh_part, hipStream_t s)
 {
     GuStreamParams p{};
     p.H = L.H;
@@ -494,7 +545,9 @@ hipError_t launch_stream_gu(const LayerView &L, const uint16_t *x, int T, const 
     p.sorted = sorted;
     p.light = light;
     p.light_n = light_n;
-    p.sh_blocks = with_shared ? ((T + kSTok - 1) / kSTok) * (L.Is / kSBlkRows) : 0;
+    p.sh_slices = with_shared ? std::min(stream_shared_slices(T), L.H / group_k<false>()) : 1;  // no empty slice
+    p.sh_part = sh_part;
+    p.sh_blocks = with_shared ? ((T + kSTok - 1) / kSTok) * (L.Is / kSBlkRows) * p.sh_slices : 0;
     p.act_hi = act_hi;
     p.act_lo = act_lo;
     p.ash_hi = ash_hi;
@@ -502,6 +555,11 @@ hipError_t launch_stream_gu(const LayerView &L, const uint16_t *x, int T, const 
     const int64_t cap = std::min<int64_t>(L.E, (int64_t)T * L.K);
     const unsigned nblk = (unsigned)(p.sh_blocks + cap * (L.I / kSBlkRows));
     k_gu_stream<<<nblk, 64 * kSWaves, gu_stream_lds_bytes(), s>>>(p);
+    if (with_shared && p.sh_slices > 1) {
+        const int64_t n = (int64_t)T * L.Is;
+        k_sh_act<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(sh_part, p.sh_slices, T, L.Is, L.act, L.b1, L.b2,
+                                                             ash_hi, ash_lo);
+    }
     return hipGetLastError();
 }
 
@@ -537,12 +595,15 @@ hipError_t launch_stream_dn(const LayerView &L, int T, const int32_t *active_e, 
     p.light = light;
     p.light_n = light_n;
     p.sh_items = with_shared ? (T + kSTok - 1) / kSTok : 0;
-    // each item's rows in `runs` blocks of run_rb 256-row blocks (about 7)
-    const int rbt = (L.H + kDBlkRows - 1) / kDBlkRows;
-    p.runs = (rbt + 6) / 7;
-    p.run_rb = (rbt + p.runs - 1) / p.runs;
-    p.ys = ys;
+    // each item's rows in `runs` blocks of run_rb 256-row blocks: about 7 row
+    // blocks per run, fewer when there are few items (about 512 blocks)
     const int64_t cap = std::min<int64_t>(L.E, (int64_t)T * L.K);
+    const int rbt = (L.H + kDBlkRows - 1) / kDBlkRows;
+    const int64_t items = p.sh_items + cap;
+    const int want = (int)std::max<int64_t>((rbt + 6) / 7, (512 + items - 1) / items);
+    p.run_rb = (rbt + std::min(want, rbt) - 1) / std::min(want, rbt);
+    p.runs = (rbt + p.run_rb - 1) / p.run_rb;
+    p.ys = ys;
     const unsigned nblk = (unsigned)((p.sh_items + cap) * p.runs);
     k_dn_stream<<<nblk, 64 * kDWaves, dn_stream_lds_bytes(std::max(L.I, L.Is)), s>>>(p);
     return hipGetLastError();
