@@ -202,8 +202,8 @@ def _mid(seed, routing="normal", T_bad=False):
     return spec, t, sd.make_layer(spec, t)
 
 
-@pytest.mark.parametrize("T,routing", [(2, "normal"), (5, "normal"), (17, "normal"), (40, "normal"),
-                                       (128, "normal"), (129, "zipf"), (300, "zipf")])
+@pytest.mark.parametrize("T,routing", [(1, "normal"), (2, "normal"), (5, "normal"), (17, "normal"),
+                                       (40, "normal"), (128, "normal"), (129, "zipf"), (300, "zipf")])
 def test_mid_stream_and_gemm_mix(T, routing):
     spec, t, layer = _mid(seed=20 + T, routing=routing)
     Wr, bias = synth.make_router(spec), synth.make_bias(spec)
@@ -250,14 +250,37 @@ def test_empty_batch_is_a_no_op():
     layer.forward(x, idx, w, out, workspace=ws)
 
 
-def test_pages_expert_shape():
-    # the README's latent expert shape (width 3584, intermediate 3072), few experts
-    spec = synth.LayerSpec(hidden=3584, inter=3072, n_experts=6, topk=3, bias_std=0.01, seed=8)
+@pytest.mark.parametrize("T,shared", [(1, 0), (3, 0), (3, 3072), (40, 3072)])
+def test_pages_expert_shape(T, shared):
+    # the README's latent expert shape (width 3584, intermediate 3072), few
+    # experts: one token, light experts, and heavy ones (40 tokens x top-3
+    # over 6 experts), with and without a shared expert of that width
+    spec = synth.LayerSpec(hidden=3584, inter=3072, n_experts=6, topk=3, shared_inter=shared,
+                           bias_std=0.01, seed=8)
     sd = _dev()
     layer = sd.make_layer(spec, sd.layer_tensors(spec, 0, DEV))
-    x_np = synth.make_x(spec, 3)
+    x_np = synth.make_x(spec, T)
     idx_r, w_r = oracle.route(x_np, synth.make_router(spec), synth.make_bias(spec), spec.topk)
     out = _forward_gpu(layer, _x_dev(x_np), idx_r, w_r)
+    ref, denom, _ = oracle_forward(spec, x_np, idx_r, w_r)
+    assert rel_err(out, ref, denom) <= REL_TOL
+
+
+@pytest.mark.parametrize("T,routing", [(1, "normal"), (5, "normal"), (129, "zipf")])
+def test_mid_swiglu_no_renorm(T, routing):
+    # SwiGLU, no renormalisation, a routed scale: the single-token kernels,
+    # the streaming kernels and the grouped GEMMs
+    spec = synth.LayerSpec(hidden=512, inter=512, n_experts=16, topk=4, shared_inter=256,
+                           bias_std=0.05, routing=routing, seed=60 + T, act=oracle.ACT_SWIGLU,
+                           renorm=0, routed_scale=2.5)
+    sd = _dev()
+    layer = sd.make_layer(spec, sd.layer_tensors(spec, 0, DEV))
+    x_np = synth.make_x(spec, T)
+    idx_r, w_r, _, ch = oracle.route(x_np, synth.make_router(spec), synth.make_bias(spec), spec.topk,
+                                     renorm=0, routed_scale=2.5, want_detail=True)
+    x, idx, w, _ = _route_gpu(layer, x_np, T, spec.topk)
+    check_route(idx.cpu().numpy(), w.cpu().numpy(), idx_r, w_r, ch, spec.topk)
+    out = _forward_gpu(layer, x, idx_r, w_r)
     ref, denom, _ = oracle_forward(spec, x_np, idx_r, w_r)
     assert rel_err(out, ref, denom) <= REL_TOL
 
