@@ -130,20 +130,29 @@ __device__ __forceinline__ float act_fn(float g, float u, int kind, float b1, fl
     return g * sg * u;
 }
 
-// Split this lane's value into NT e4m3 terms; the 32 lanes of a half-wave
-// form one 32-element block and share one E8M0 scale per term. The scale
-// puts the block's largest remainder in [224, 448]; a term takes only the
-// elements within 6 binades of that maximum (the rest stay in the remainder)
-// and each term's rounding error is carried exactly into the next term.
-template <int NT>
-__device__ __forceinline__ void split_e4m3_32(float v, int (&code)[NT], int (&sbyte)[NT])
+// Maximum over the 8 lanes of each aligned lane octet (DPP: swap neighbours,
+// swap pairs, mirror the half-row).
+__device__ __forceinline__ float octet_max(float m)
 {
-    float r = v;
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xb1, 0xf, 0xf, false)));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4e, 0xf, 0xf, false)));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xf, 0xf, false)));
+    return m;
+}
+
+// Split this lane's 4 consecutive values into NT e4m3 terms; the 8 lanes of
+// an aligned octet hold one 32-element block and share one E8M0 scale per
+// term. The scale puts the block's largest remainder in [224, 448]; a term
+// takes only the elements within 6 binades of that maximum (the rest stay in
+// the remainder) and each term's rounding error is carried exactly into the
+// next term. code4[t] packs the 4 codes of term t, first value lowest.
+template <int NT>
+__device__ __forceinline__ void split_e4m3_octet(const float4 v, uint32_t (&code4)[NT], int (&sbyte)[NT])
+{
+    float r[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-        float m = fabsf(r);
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+        const float m = octet_max(fmaxf(fmaxf(fabsf(r[0]), fabsf(r[1])), fmaxf(fabsf(r[2]), fabsf(r[3]))));
         int S = 0;
         float keep_min = INFINITY;
         if (m > 0.0f) {
@@ -155,13 +164,17 @@ __device__ __forceinline__ void split_e4m3_32(float v, int (&code)[NT], int (&sb
             frexpf(ldexpf(m, -S), &ex);
             keep_min = ldexpf(1.0f, ex - 7);  // 6 binades below the block maximum
         }
-        const float q = ldexpf(r, -S);
-        int c = 0;
-        if (fabsf(q) >= keep_min) {
-            c = __builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xff;
-            r -= ldexpf(__builtin_amdgcn_cvt_f32_fp8(c, 0), S);
+        uint32_t c4 = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float q = ldexpf(r[i], -S);
+            if (fabsf(q) >= keep_min) {
+                const uint32_t c = __builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xffu;
+                r[i] -= ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)c, 0), S);
+                c4 |= c << (8 * i);
+            }
         }
-        code[t] = c;
+        code4[t] = c4;
         sbyte[t] = S + 127;
     }
 }
@@ -357,11 +370,16 @@ __global__ __launch_bounds__(64) void k_topk(const float *__restrict__ sc, const
     const int t = blockIdx.x;
     const int lane = threadIdx.x;
     const float *c = ch + (size_t)t * E;
+    const float *sr = sc + (size_t)t * E;
     const int e0 = lane * NQ;
-    // every load is issued before the first is used (clamped index, no branch)
-    float raw[NQ];
+    // the selection scores and the scores are loaded together, every load
+    // issued before the first is used (clamped index, no branch)
+    float raw[NQ], sv[NQ];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) raw[q] = c[min(e0 + q, E - 1)];
+    for (int q = 0; q < NQ; ++q) {
+        raw[q] = c[min(e0 + q, E - 1)];
+        sv[q] = sr[min(e0 + q, E - 1)];
+    }
     uint32_t v[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) v[q] = e0 + q < E ? order_key(raw[q]) : 0u;  // 0: none / taken
@@ -379,32 +397,37 @@ __global__ __launch_bounds__(64) void k_topk(const float *__restrict__ sc, const
     };
     rescan();
     int mine = 0;
+    float mine_s = 0.0f;  // score of pick j, held by lane j
     for (int j = 0; j < K; ++j) {
         const uint32_t m = wave_reduce_u32<true>(bk);
         const uint64_t holders = __ballot(bk == m);
         const int wl = (int)__builtin_ctzll(holders);  // lowest lane holding the maximum
         const int win = wl * NQ + __builtin_amdgcn_readlane(bq, wl);
+        float ws = 0.0f;
         if (lane == wl) {
 #pragma unroll
             for (int q = 0; q < NQ; ++q)
-                if (q == bq) v[q] = 0u;
+                if (q == bq) {
+                    ws = sv[q];
+                    v[q] = 0u;
+                }
             rescan();
         }
-        if (lane == j) mine = win;
-    }
-    __shared__ float wj[kMaxTopk];
-    if (lane < K) wj[lane] = sc[(size_t)t * E + mine];
-    __syncthreads();
-    if (lane == 0) {
-        float s = 0.0f;
-        for (int j = 0; j < K; ++j) s += wj[j];
-        for (int j = 0; j < K; ++j) {
-            float v0 = wj[j];
-            if (renorm && s > 0.0f) v0 /= s;
-            w[(size_t)t * K + j] = v0 * rscale;
+        ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ws), wl));
+        if (lane == j) {
+            mine = win;
+            mine_s = ws;
         }
     }
-    if (lane < K) idx[(size_t)t * K + lane] = mine;
+    // renormalisation: the sum runs over the picks in router order
+    float s = 0.0f;
+    for (int j = 0; j < K; ++j) s += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine_s), j));
+    if (lane < K) {
+        float v0 = mine_s;
+        if (renorm && s > 0.0f) v0 /= s;
+        w[(size_t)t * K + lane] = v0 * rscale;
+        idx[(size_t)t * K + lane] = mine;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -854,7 +877,9 @@ __global__ __launch_bounds__(64 * kGuDecWaves) void k_gateup_dec(GateUpParams p)
 // the 16-row tiles [T16*i/M, T16*(i+1)/M) of H (T16 = H/16) and the shared
 // rows [H*(jM+i)/(KM), ...): every block moves about the same bytes. The
 // slot's fp32 activation is expanded into 4 e4m3 terms (one E8M0 scale per
-// 32 elements per term) while it is staged in LDS, with the tiles' E8M0 rows; wave w takes tiles t0+w, t0+w+4, ... (K in chunks of 4 MFMA steps, a
+// 32 elements per term; 8 lanes per 32-element block, DPP maxima) while it
+// is staged in LDS, with the tiles' E8M0 rows; wave w takes tiles t0+w,
+// t0+w+4, ... (K in chunks of 4 MFMA steps, a
 // 4-deep register ring) and shared rows r0+w, r0+w+4, ... (bf16, fp32 FMA,
 // loads issued before the routed stream). Results go to the staging rows
 // ys[j][.] and ys[k][.] (shared); the combine sums them in router order.
@@ -873,7 +898,7 @@ constexpr int kDnDecWaves = 4;
 constexpr int kDnMaxTiles = 16;      // tiles per block (LDS sizing)
 constexpr int kDnShPerWave = 4;      // shared rows per wave (at most)
 constexpr int kDnShSl = 3;           // shared slices of 512 prefetched (I_s <= 1536)
-constexpr int kDnStgQ = 8;           // activation elements per thread (I <= 2048)
+constexpr int kDnStgQ = 2;           // activation float4s per thread (I <= 2048)
 constexpr int kDnStgS = 4;           // scale-row staging copies per thread
 
 __host__ __device__ constexpr int dn_dec_lds_bytes(int I)
@@ -952,9 +977,10 @@ __global__ __launch_bounds__(64 * kDnDecWaves) void k_down_dec(DownDecParams p)
     // staging loads (the slot's activation, the tiles' scale rows), then the
     // first 4 weight chunks, then the expansion and the LDS stores
     Chunk b0, b1, b2, b3;
-    float av[kDnStgQ];
+    float4 av[kDnStgQ];  // elements 4 (tid + 256 q) + [0, 4)
 #pragma unroll
-    for (int q = 0; q < kDnStgQ; ++q) av[q] = afj[min((int)threadIdx.x + q * 64 * kDnDecWaves, I - 1)];
+    for (int q = 0; q < kDnStgQ; ++q)
+        av[q] = *reinterpret_cast<const float4 *>(afj + min(4 * ((int)threadIdx.x + q * 64 * kDnDecWaves), I - 4));
     if constexpr (WIDE) {  // SR % 16 == 0
         const int nrow = SR >> 4, nsc = nt * 16 * nrow;
         u4 ts[kDnStgS];
@@ -991,19 +1017,22 @@ __global__ __launch_bounds__(64 * kDnDecWaves) void k_down_dec(DownDecParams p)
             load(min(3, nq - 1), b3);
         }
     }
-    // activation -> 4 e4m3 terms; element i = tid + 256q, so each half-wave
-    // holds one 32-element block (I is a multiple of 128: whole half-waves)
+    // activation -> 4 e4m3 terms; the octet of lanes 8m..8m+7 holds one
+    // 32-element block (I is a multiple of 128: whole octets), every lane
+    // splits (clamped copies past I are not stored)
 #pragma unroll
     for (int q = 0; q < kDnStgQ; ++q) {
-        const int ii = (int)threadIdx.x + q * 64 * kDnDecWaves;
-        if (q * 64 * kDnDecWaves < I && ii < I) {
-            int code[kATerms], sbt[kATerms];
-            split_e4m3_32<kATerms>(av[q], code, sbt);
+        const int i4 = 4 * ((int)threadIdx.x + q * 64 * kDnDecWaves);
+        if (q * 4 * 64 * kDnDecWaves < I) {
+            uint32_t code4[kATerms];
+            int sbt[kATerms];
+            split_e4m3_octet<kATerms>(av[q], code4, sbt);
+            if (i4 < I)
 #pragma unroll
-            for (int k = 0; k < kATerms; ++k) {
-                aq_l[k * AQS + ii] = (uint8_t)code[k];
-                if ((ii & 31) == 0) as_l[k * SR + (ii >> 5)] = (uint8_t)sbt[k];
-            }
+                for (int k = 0; k < kATerms; ++k) {
+                    *reinterpret_cast<uint32_t *>(aq_l + k * AQS + i4) = code4[k];
+                    if ((i4 & 31) == 0) as_l[k * SR + (i4 >> 5)] = (uint8_t)sbt[k];
+                }
         }
     }
     __syncthreads();
@@ -1122,9 +1151,9 @@ __global__ __launch_bounds__(64 * kDnDecWaves) void k_down_dec(DownDecParams p)
 
 // Router-order combine: out[t][o] = sum_j w[t][j] * ys[t][j][o] (j = 0..k-1
 // in order, one fma each), then + ys[t][k][o] (the shared expert, if any).
-// A slot with an out-of-range id adds nothing (its staging row is not read)
-// and is counted once here. A thread takes 4 consecutive outputs (16-byte
-// loads); the loads of up to 16 slots are issued before the first fma.
+// A slot with an out-of-range id adds nothing (its staging row is loaded but
+// dropped) and is counted once here. A thread takes 4 consecutive outputs
+// (16-byte loads); the loads of up to 16 slots are issued before the first fma.
 constexpr int kCombineThreads = 64;
 __global__ __launch_bounds__(kCombineThreads) void k_combine(const float *__restrict__ ys,
                                                              const float *__restrict__ w,
@@ -1142,23 +1171,25 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const float *__rest
         const int32_t *it = idx + (size_t)t * K;
         float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         for (int j0 = 0; j0 < K; j0 += 16) {
+            // ids, weights and staging rows are loaded together (clamped,
+            // unconditional); a slot with an invalid id is dropped after
             float4 v[16];
-            bool ok[16];
+            float wj[16];
+            int e[16];
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                const int j = j0 + q;
-                const int e = it[min(j, K - 1)];
-                ok[q] = j < K && e >= 0 && e < E;
-                v[q] = ok[q] ? *reinterpret_cast<const float4 *>(y + (size_t)j * H) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                const int j = min(j0 + q, K - 1);
+                e[q] = it[j];
+                wj[q] = wt[j];
+                v[q] = *reinterpret_cast<const float4 *>(y + (size_t)j * H);
             }
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                if (ok[q]) {
-                    const float wj = wt[min(j0 + q, K - 1)];
-                    acc.x = fmaf(wj, v[q].x, acc.x);
-                    acc.y = fmaf(wj, v[q].y, acc.y);
-                    acc.z = fmaf(wj, v[q].z, acc.z);
-                    acc.w = fmaf(wj, v[q].w, acc.w);
+                if (j0 + q < K && e[q] >= 0 && e[q] < E) {
+                    acc.x = fmaf(wj[q], v[q].x, acc.x);
+                    acc.y = fmaf(wj[q], v[q].y, acc.y);
+                    acc.z = fmaf(wj[q], v[q].z, acc.z);
+                    acc.w = fmaf(wj[q], v[q].w, acc.w);
                 }
             }
         }
@@ -1250,8 +1281,8 @@ static bool decode_path_ok(const LayerView &L)
 {
     const bool gu = L.H % 512 != 0 || L.H / 8 <= 64 * kGuDecWaves * kGuStgQ;
     const bool gu_sc = L.H % 512 != 0 || kGuDecUnits * 2 * kGuUnitRows * (L.H / 512) <= 64 * kGuDecWaves * kGuStgS;
-    const bool dn = L.I % 512 != 0 || (L.I / 4 <= 64 * kDnDecWaves * kDnStgQ &&
-                                       kDnMaxTiles * 16 * (L.I / 512) <= 64 * kDnDecWaves * kDnStgS);
+    const bool dn = L.I <= 4 * 64 * kDnDecWaves * kDnStgQ &&  // the activation staging, both row forms
+                    (L.I % 512 != 0 || kDnMaxTiles * 16 * (L.I / 512) <= 64 * kDnDecWaves * kDnStgS);
     return gu && gu_sc && dn && L.I % kGuUnitRows == 0 && L.H % 16 == 0 && L.H >= 16 * kDnDecWaves;
 }
 

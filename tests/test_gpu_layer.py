@@ -266,6 +266,22 @@ def test_pages_expert_shape(T, shared):
     assert rel_err(out, ref, denom) <= REL_TOL
 
 
+@pytest.mark.parametrize("T,inter", [(1, 2176), (1, 1664), (2, 2176)])
+def test_inter_widths_past_and_below_decode_staging(T, inter):
+    # intermediate widths that are not multiples of 512, one past the
+    # single-token down kernel's activation staging (2048 elements: such a
+    # layer takes the grouped path) and one within it
+    spec = synth.LayerSpec(hidden=256, inter=inter, n_experts=4, topk=2, shared_inter=128,
+                           bias_std=0.05, seed=70 + inter)
+    sd = _dev()
+    layer = sd.make_layer(spec, sd.layer_tensors(spec, 0, DEV))
+    x_np = synth.make_x(spec, T)
+    idx_r, w_r = oracle.route(x_np, synth.make_router(spec), synth.make_bias(spec), spec.topk)
+    out = _forward_gpu(layer, _x_dev(x_np), idx_r, w_r)
+    ref, denom, _ = oracle_forward(spec, x_np, idx_r, w_r)
+    assert rel_err(out, ref, denom) <= REL_TOL
+
+
 @pytest.mark.parametrize("T,routing", [(1, "normal"), (5, "normal"), (129, "zipf")])
 def test_mid_swiglu_no_renorm(T, routing):
     # SwiGLU, no renormalisation, a routed scale: the single-token kernels,
