@@ -346,15 +346,23 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v)
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Top-k by repeated maximum (README §9). One wave per token; lane l holds
-// the selection scores of experts l*NQ .. l*NQ+NQ-1 (a contiguous range, so
-// a lower lane always holds lower expert indices) as order-preserving uint32
-// keys, and keeps its best remaining key and the lowest position holding it.
-// Each round takes the wave-wide maximum key; among the lanes holding it the
-// lowest lane wins (hence the lowest expert index, as the strict comparison
-// of the repeated maximum gives); the winner zeroes that key and rescans.
-// NaN ranks as -inf. Weights are the unbiased scores of the picks,
-// renormalised in router order, then scaled.
+// Top-k (README §9): the k largest selection scores, in descending order,
+// equal scores by ascending expert index (the order of a repeated strict
+// maximum). One wave per token; lane l holds the selection scores of experts
+// l*NQ .. l*NQ+NQ-1 (a contiguous range, so a lower lane always holds lower
+// expert indices) as order-preserving uint32 keys; NaN ranks as -inf.
+//
+// Threshold and rank: tau = the k-th largest of the 64 lane maxima. k lanes
+// hold a key >= tau, so the k-th largest key is >= tau and every pick is
+// among the candidates {key >= tau}. When there are at most 64 candidates
+// (the usual case: about k of them), they are gathered in LDS, each takes
+// its rank in the order above by comparing against all of them, and the
+// first k ranks are the picks. With more candidates (heavy ties) the wave
+// falls back to k rounds of a wave-wide maximum, the lowest lane holding it
+// winning and rescanning its keys.
+//
+// Weights are the unbiased scores of the picks, renormalised in router
+// order, then scaled.
 __device__ __forceinline__ uint32_t order_key(float v)
 {
     if (v != v) v = -INFINITY;
@@ -367,6 +375,12 @@ __global__ __launch_bounds__(64) void k_topk(const float *__restrict__ sc, const
                                              int E, int K, int renorm, float rscale,
                                              int32_t *__restrict__ idx, float *__restrict__ w)
 {
+    __shared__ uint32_t lmax_l[64];
+    __shared__ uint32_t ck_l[64];  // candidates: key, expert, score
+    __shared__ int ci_l[64];
+    __shared__ float cs_l[64];
+    __shared__ int pi_l[kMaxTopk];  // picks in router order: expert, score
+    __shared__ float ps_l[kMaxTopk];
     const int t = blockIdx.x;
     const int lane = threadIdx.x;
     const float *c = ch + (size_t)t * E;
@@ -383,40 +397,94 @@ __global__ __launch_bounds__(64) void k_topk(const float *__restrict__ sc, const
     uint32_t v[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) v[q] = e0 + q < E ? order_key(raw[q]) : 0u;  // 0: none / taken
-    uint32_t bk;  // best remaining key of this lane (0: none)
-    int bq;       // its position
-    auto rescan = [&]() {
-        bk = 0u;
-        bq = 0;
+    uint32_t lm = 0u;
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            const bool gt = v[q] > bk;
-            bk = gt ? v[q] : bk;
-            bq = gt ? q : bq;
+    for (int q = 0; q < NQ; ++q) lm = v[q] > lm ? v[q] : lm;
+
+    // tau: the lane maximum of rank k-1 (ranks 0..63 distinct: equal maxima
+    // by lane)
+    lmax_l[lane] = lm;
+    __syncthreads();
+    int rank = 0;
+#pragma unroll 16
+    for (int j = 0; j < 64; ++j) {
+        const uint32_t u = lmax_l[j];
+        rank += (u > lm || (u == lm && j < lane)) ? 1 : 0;
+    }
+    const uint64_t at = __ballot(rank == K - 1);
+    const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)lm, (int)__builtin_ctzll(at));
+
+    // gather the candidates (key >= tau; a key of 0 is no expert)
+    int C = 0;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const bool in = v[q] >= tau && v[q] != 0u;
+        const uint64_t m = __ballot(in);
+        const int pos = C + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (in && pos < 64) {
+            ck_l[pos] = v[q];
+            ci_l[pos] = e0 + q;
+            cs_l[pos] = sv[q];
         }
-    };
-    rescan();
+        C += __popcll(m);
+    }
+    __syncthreads();
+
     int mine = 0;
     float mine_s = 0.0f;  // score of pick j, held by lane j
-    for (int j = 0; j < K; ++j) {
-        const uint32_t m = wave_reduce_u32<true>(bk);
-        const uint64_t holders = __ballot(bk == m);
-        const int wl = (int)__builtin_ctzll(holders);  // lowest lane holding the maximum
-        const int win = wl * NQ + __builtin_amdgcn_readlane(bq, wl);
-        float ws = 0.0f;
-        if (lane == wl) {
-#pragma unroll
-            for (int q = 0; q < NQ; ++q)
-                if (q == bq) {
-                    ws = sv[q];
-                    v[q] = 0u;
-                }
-            rescan();
+    if (C <= 64) {
+        if (lane < C) {
+            const uint32_t k0 = ck_l[lane];
+            const int i0 = ci_l[lane];
+            int r = 0;
+            for (int j = 0; j < C; ++j) {
+                const uint32_t kj = ck_l[j];
+                r += (kj > k0 || (kj == k0 && ci_l[j] < i0)) ? 1 : 0;
+            }
+            if (r < K) {
+                pi_l[r] = i0;
+                ps_l[r] = cs_l[lane];
+            }
         }
-        ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ws), wl));
-        if (lane == j) {
-            mine = win;
-            mine_s = ws;
+        __syncthreads();
+        if (lane < K) {
+            mine = pi_l[lane];
+            mine_s = ps_l[lane];
+        }
+    } else {
+        uint32_t bk;  // best remaining key of this lane (0: none)
+        int bq;       // its position
+        auto rescan = [&]() {
+            bk = 0u;
+            bq = 0;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const bool gt = v[q] > bk;
+                bk = gt ? v[q] : bk;
+                bq = gt ? q : bq;
+            }
+        };
+        rescan();
+        for (int j = 0; j < K; ++j) {
+            const uint32_t m = wave_reduce_u32<true>(bk);
+            const uint64_t holders = __ballot(bk == m);
+            const int wl = (int)__builtin_ctzll(holders);  // lowest lane holding the maximum
+            const int win = wl * NQ + __builtin_amdgcn_readlane(bq, wl);
+            float ws = 0.0f;
+            if (lane == wl) {
+#pragma unroll
+                for (int q = 0; q < NQ; ++q)
+                    if (q == bq) {
+                        ws = sv[q];
+                        v[q] = 0u;
+                    }
+                rescan();
+            }
+            ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ws), wl));
+            if (lane == j) {
+                mine = win;
+                mine_s = ws;
+            }
         }
     }
     // renormalisation: the sum runs over the picks in router order

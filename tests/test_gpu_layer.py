@@ -171,6 +171,29 @@ def test_tiny_invariants_poison_double_relabel():
     assert np.array_equal(base, _forward_gpu(layer2, x, perm[idx_r], w_r))
 
 
+@pytest.mark.parametrize("n_experts,groups,bias", [(128, 8, False), (128, 1, False), (128, 1, True),
+                                                    (16, 4, False), (896, 7, False)])
+def test_route_exact_ties(n_experts, groups, bias):
+    # router rows repeat with period `groups`, so experts e and e + groups tie
+    # exactly: equal selection scores go to the lowest expert index. With one
+    # group and no bias every expert ties (more than 64 candidates in the
+    # threshold step: the round-by-round fallback); 8 groups give 16 tied
+    # copies of each logit (the rank step with ties)
+    spec = synth.LayerSpec(hidden=256, inter=128, n_experts=n_experts, topk=8, shared_inter=0,
+                           bias_std=0.05 if bias else 0.0, seed=80 + groups)
+    sd = _dev()
+    t = sd.layer_tensors(spec, 0, DEV)
+    Wr = synth.make_router(spec)[np.arange(n_experts) % groups]
+    t["router_w"].copy_(sd.bf16_tensor(np.ascontiguousarray(Wr), DEV))
+    layer = sd.make_layer(spec, t)
+    bias_np = synth.make_bias(spec)
+    x_np = synth.make_x(spec, 5)
+    idx_r, w_r = oracle.route(x_np, Wr, bias_np, spec.topk)
+    _, idx, w, _ = _route_gpu(layer, x_np, 5, spec.topk)
+    assert np.array_equal(idx.cpu().numpy(), idx_r)
+    np.testing.assert_allclose(w.cpu().numpy(), w_r, rtol=4e-7, atol=0)
+
+
 def test_tiny_bad_ids_are_counted():
     spec, t, layer = _tiny(seed=5)
     x_np = synth.make_x(spec, 4)
