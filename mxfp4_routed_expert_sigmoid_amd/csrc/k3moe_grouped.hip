@@ -448,13 +448,18 @@ static bool set_lds_limits()
     return true;
 }
 
-size_t grouped_tile_cap(int64_t T, int K, int E, int bn)
+// Upper bound on the tiles of bn tokens: every expert with more than smax
+// assignments (smax: the light-expert limit of the streaming kernels, 0 when
+// they are off) adds at most one partial tile, and there are at most
+// min(E, T*K / (smax + 1)) such experts.
+size_t grouped_tile_cap(int64_t T, int K, int E, int bn, int smax)
 {
-    return (size_t)(T * K / bn + std::min<int64_t>(E, T * K) + 1);
+    const int64_t n = T * K;
+    return (size_t)(n / bn + std::min<int64_t>(E, n / (smax + 1)) + 1);
 }
 
-size_t grouped_tile_cap_gu(int64_t T, int K, int E) { return grouped_tile_cap(T, K, E, GemmShape<true>::TOK); }
-size_t grouped_tile_cap_dn(int64_t T, int K, int E) { return grouped_tile_cap(T, K, E, GemmShape<false>::TOK); }
+size_t grouped_tile_cap_gu(int64_t T, int K, int E) { return grouped_tile_cap(T, K, E, GemmShape<true>::TOK, 0); }
+size_t grouped_tile_cap_dn(int64_t T, int K, int E) { return grouped_tile_cap(T, K, E, GemmShape<false>::TOK, 0); }
 
 hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const int32_t *active_n,
                           const int32_t *active_e, const int32_t *active_off, const int32_t *sorted,
@@ -465,14 +470,16 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const in
     static const bool lds_set = set_lds_limits();  // once per process (thread-safe static)
     (void)lds_set;
     constexpr int TG = GemmShape<true>::TOK, TD = GemmShape<false>::TOK;
-    const size_t cap_gu = grouped_tile_cap(T, L.K, L.E, TG), cap_dn = grouped_tile_cap(T, L.K, L.E, TD);
     const int rb_i = (L.I + kTileRows - 1) / kTileRows, rb_h = (L.H + kTileRows - 1) / kTileRows;
     const int rb_s = (L.Is + kTileRows - 1) / kTileRows;
     const bool stream = stream_path_ok(L), stream_dn = stream_down_ok(L);
     const bool sh_stream = stream_shared_ok(L, T);
+    const int smax_gu = stream ? stream_max_tokens() : 0, smax_dn = stream_dn ? stream_max_tokens() : 0;
+    // grids cover the most tiles the split can produce (most blocks exit at once)
+    const size_t cap_gu = grouped_tile_cap(T, L.K, L.E, TG, smax_gu), cap_dn = grouped_tile_cap(T, L.K, L.E, TD, smax_dn);
     int32_t *light_gu = light, *light_dn = light + L.E;
-    k_tiles<<<1, 1024, 0, s>>>(active_n, active_off, TG, TD, stream ? stream_max_tokens() : 0,
-                               stream_dn ? stream_max_tokens() : 0, tiles_gu, tiles_dn, light_gu, light_dn, counts);
+    k_tiles<<<1, 1024, 0, s>>>(active_n, active_off, TG, TD, smax_gu, smax_dn, tiles_gu, tiles_dn, light_gu, light_dn,
+                               counts);
 
     // gate/up: routed tiles (fp4); the shared expert's tiles go in a launch of
     // their own (different weight rows) unless they stream with the light experts

@@ -635,17 +635,36 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int nchunks, int E, int32_t 
     __shared__ int cnt[kMaxExperts];
     __shared__ int off[kMaxExperts];
     __shared__ int flag[kMaxExperts];
+    // a thread per expert walks the chunks in batches of 16 loads in flight
+    constexpr int B = 16;
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += 1024) {
-        int s = 0;
-        for (int c = 0; c < nchunks; ++c) s += chunk_cnt[(size_t)c * E + e];
+        int s = 0, c = 0;
+        for (; c + B <= nchunks; c += B) {
+            int v[B];
+#pragma unroll
+            for (int q = 0; q < B; ++q) v[q] = chunk_cnt[(size_t)(c + q) * E + e];
+#pragma unroll
+            for (int q = 0; q < B; ++q) s += v[q];
+        }
+        for (; c < nchunks; ++c) s += chunk_cnt[(size_t)c * E + e];
         cnt[e] = s;
     }
     __syncthreads();
     build_active(cnt, off, flag, E, active_n, active_e, active_off);
     for (int e = tid; e < E; e += 1024) {
-        int run = off[e];
-        for (int c = 0; c < nchunks; ++c) {
+        int run = off[e], c = 0;
+        for (; c + B <= nchunks; c += B) {
+            int v[B];
+#pragma unroll
+            for (int q = 0; q < B; ++q) v[q] = chunk_cnt[(size_t)(c + q) * E + e];
+#pragma unroll
+            for (int q = 0; q < B; ++q) {
+                chunk_cnt[(size_t)(c + q) * E + e] = run;
+                run += v[q];
+            }
+        }
+        for (; c < nchunks; ++c) {
             const int v = chunk_cnt[(size_t)c * E + e];
             chunk_cnt[(size_t)c * E + e] = run;
             run += v;
