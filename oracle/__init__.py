@@ -5,9 +5,10 @@ benchmark's ``cpu_baseline`` leg may import this package. The product path
 never does, and the two share no code.
 
 Every function follows the "kimi-k3-in-c" README: §4 (MXFP4 format and the
-matrix-vector product over nibbles), §5 (bf16 widening), §9 (k3_router,
-k3_moe, k3_situ_glu). The arithmetic lives in ``k3moe_oracle.c``; this module
-only marshals numpy arrays.
+matrix-vector product over nibbles), §5 (bf16 widening, k3_rmsnorm), §9
+(k3_router, k3_moe with and without its latent projections, k3_situ_glu).
+The arithmetic lives in ``k3moe_oracle.c``; this module only marshals numpy
+arrays.
 """
 import ctypes
 import os
@@ -51,6 +52,12 @@ def lib():
         L.k3o_forward.argtypes = [P, P, P, i64, i64, i64, P, P, i64, i64, P,
                                   P, P, P, P, P, P, P, P, P, i64,
                                   ctypes.c_int, ctypes.c_double, ctypes.c_double]
+        L.k3o_rmsnorm.restype = ctypes.c_double
+        L.k3o_rmsnorm.argtypes = [P, P, P, i64, ctypes.c_double]
+        L.k3o_forward_latent.restype = i64
+        L.k3o_forward_latent.argtypes = [P, P, P, i64, i64, i64, i64, P, P, i64, i64, P,
+                                         P, P, P, P, P, P, P, P, ctypes.c_int, P, ctypes.c_double,
+                                         P, P, P, i64, ctypes.c_int, ctypes.c_double, ctypes.c_double]
         L.k3o_threads.restype = ctypes.c_int
         L.k3o_threads.argtypes = []
         _lib = L
@@ -192,4 +199,62 @@ def forward(x, idx, w, experts: ExpertSet, H, I, shared=None, act_kind=ACT_SITU,
         _ptr(S1), _ptr(S3), _ptr(S2), Is, int(act_kind), float(b1), float(b2))
     if drops < 0:
         raise ValueError("oracle forward: a selected expert has no slot, or bad sizes")
+    return out, denom, int(drops)
+
+
+def rmsnorm(v, gamma=None, eps=1e-5):
+    """RMSNorm of an fp64 vector (epsilon inside the square root); returns
+    (out, inv)."""
+    v = _c(v, np.float64)
+    gamma = _c(gamma, np.float32)
+    if gamma is not None:
+        assert gamma.size == v.size
+    out = np.empty_like(v)
+    inv = lib().k3o_rmsnorm(_ptr(out), _ptr(v), _ptr(gamma), v.size, float(eps))
+    return out, inv
+
+
+def forward_latent(x, idx, w, experts: ExpertSet, H, L, I, lat_down, lat_up, norm=True,
+                   gamma=None, eps=1e-5, shared=None, act_kind=ACT_SITU, b1=4.0, b2=25.0,
+                   want_denom=True):
+    """Latent layer output (fp64 [T][H]), error denominators and drops.
+
+    Experts are at width L: gate/up [I][L], down [L][I]. lat_down bf16 [L][H],
+    lat_up bf16 [H][L]; gamma fp32 [L] (norm only); shared as in ``forward``."""
+    x = _c(x, np.uint16)
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float32)
+    T = x.shape[0]
+    topk = idx.shape[1]
+    assert x.shape == (T, H) and idx.shape == (T, topk) and w.shape == (T, topk)
+    ns = experts.experts.size
+    assert experts.gate_packed.size == ns * I * ((L + 1) // 2)
+    assert experts.gate_scales.size == ns * I * ((L + 31) // 32)
+    assert experts.down_packed.size == ns * L * ((I + 1) // 2)
+    assert experts.down_scales.size == ns * L * ((I + 31) // 32)
+    Wd = _c(lat_down, np.uint16)
+    Wu = _c(lat_up, np.uint16)
+    assert Wd.shape == (L, H) and Wu.shape == (H, L)
+    gamma = _c(gamma, np.float32)
+    if norm and gamma is not None:
+        assert gamma.shape == (L,)
+    if shared is not None:
+        S1, S3, S2 = (_c(s, np.uint16) for s in shared)
+        Is = S1.shape[0]
+        assert S1.shape == (Is, H) and S3.shape == (Is, H) and S2.shape == (H, Is)
+    else:
+        S1 = S3 = S2 = None
+        Is = 0
+    out = np.empty((T, H), np.float64)
+    denom = np.empty((T, H), np.float64) if want_denom else None
+    drops = lib().k3o_forward_latent(
+        _ptr(out), _ptr(denom), _ptr(x), T, H, L, I, _ptr(idx), _ptr(w), topk,
+        experts.n_experts, _ptr(experts.slot_of),
+        _ptr(experts.gate_packed), _ptr(experts.gate_scales),
+        _ptr(experts.up_packed), _ptr(experts.up_scales),
+        _ptr(experts.down_packed), _ptr(experts.down_scales),
+        _ptr(Wd), _ptr(Wu), int(bool(norm)), _ptr(gamma), float(eps),
+        _ptr(S1), _ptr(S3), _ptr(S2), Is, int(act_kind), float(b1), float(b2))
+    if drops < 0:
+        raise ValueError("oracle forward_latent: a selected expert has no slot, or bad sizes")
     return out, denom, int(drops)

@@ -24,6 +24,10 @@
  *     gate and up projections, SiTU-GLU, down projection; weighted sum in
  *     router order; the shared expert on the original input, added unweighted
  *     after the routed sum).
+ *   - Latent layer: §9, all six steps of k3_moe (down-projection of x into
+ *     the expert latent, the experts at the latent width, RMSNorm of the
+ *     aggregate, up-projection, shared experts on the original x) and §5,
+ *     k3_rmsnorm (epsilon inside the square root).
  * Expert failures that the pages count as drops are mirrored: an index outside
  * [0, n_experts) contributes nothing and is counted.
  *
@@ -280,6 +284,130 @@ int64_t k3o_forward(double *out, double *denom,
     }
 done:
     free(xd); free(g); free(u); free(a); free(y); free(yabs);
+    return drops;
+}
+
+/* RMSNorm of n values (§5 "Kernels with a floating point contract",
+ * k3_rmsnorm): inv = 1 / sqrt(sum_i v_i^2 / n + eps), epsilon inside the
+ * square root; out_i = v_i * inv * gamma_i (gamma NULL: 1). fp64 throughout.
+ * Returns inv. out may equal v. */
+double k3o_rmsnorm(double *out, const double *v, const float *gamma, int64_t n, double eps)
+{
+    double ss = 0.0;
+    for (int64_t i = 0; i < n; i++) ss += v[i] * v[i];
+    const double inv = 1.0 / sqrt(ss / (double)n + eps);
+    for (int64_t i = 0; i < n; i++) out[i] = v[i] * inv * (gamma ? (double)gamma[i] : 1.0);
+    return inv;
+}
+
+/* Stable LatentMoE layer for T tokens (§9 "Picking 16 experts of 896", the
+ * six steps of k3_moe): the experts run in a narrow latent of width L.
+ *   z    = Wd x                           down-projection (bf16 [L][H])
+ *   accL = sum_j w_j * W2_e act(W1_e z, W3_e z)   experts at width L (gate/up
+ *          [I][L], down [L][I]), router order; bad ids counted, skipped
+ *   accN = RMSNorm(accL) with gamma, if norm  (the AGGREGATE is normed, not
+ *          each expert); else accN = accL
+ *   out  = Wu accN                        up-projection (bf16 [H][L])
+ *   out += S2 act(S1 x, S3 x)             shared expert on the ORIGINAL x,
+ *                                         unweighted, after the routed part
+ * The routing (idx, w) comes from k3o_route on the full-width x.
+ * denom (optional), per output element o: the magnitude the output is made
+ * of, propagated through each step,
+ *   DL[l] = sum_j |w_j| sum_n |W2_e[l][n] a_j[n]|        (routed sum)
+ *   DN[l] = inv |gamma_l| DL[l] + |accN[l]| * (sum_m |accL[m]| DL[m]) / ss
+ *           (the second term: the norm's own dependence on every accL[m];
+ *           without the norm DN = DL)
+ *   denom[o] = sum_l |Wu[o][l]| DN[l] + sum_n |S2[o][n] a_s[n]|.
+ * Returns the number of dropped assignments, or -1 (missing slot, sizes). */
+int64_t k3o_forward_latent(double *out, double *denom,
+                           const uint16_t *x, int64_t T, int64_t H, int64_t L, int64_t I,
+                           const int32_t *idx, const float *w, int64_t topk, int64_t E,
+                           const int32_t *slot_of,
+                           const uint8_t *gate_packed, const uint8_t *gate_scales,
+                           const uint8_t *up_packed, const uint8_t *up_scales,
+                           const uint8_t *down_packed, const uint8_t *down_scales,
+                           const uint16_t *lat_down, const uint16_t *lat_up,
+                           int norm, const float *gamma, double eps,
+                           const uint16_t *sh_gate, const uint16_t *sh_up,
+                           const uint16_t *sh_down, int64_t Is,
+                           int act, double b1, double b2)
+{
+    if (T < 0 || H <= 0 || L <= 0 || I <= 0 || topk <= 0 || E <= 0 || Is < 0) return -1;
+    if (act != K3O_ACT_SITU && act != K3O_ACT_SWIGLU) return -1;
+    if (!lat_down || !lat_up) return -1;
+    const int64_t gp = I * ((L + 1) / 2), gs = I * ((L + 31) / 32);
+    const int64_t dp = L * ((I + 1) / 2), ds = L * ((I + 31) / 32);
+    int64_t inner = (I > Is) ? I : Is;
+    if (L > inner) inner = L;
+    const int64_t wide = (H > inner) ? H : inner;
+    double *xd = (double *)malloc(sizeof(double) * H);
+    double *z = (double *)malloc(sizeof(double) * L);
+    double *g = (double *)malloc(sizeof(double) * inner);
+    double *u = (double *)malloc(sizeof(double) * inner);
+    double *a = (double *)malloc(sizeof(double) * inner);
+    double *y = (double *)malloc(sizeof(double) * wide);
+    double *yabs = (double *)malloc(sizeof(double) * wide);
+    double *accL = (double *)malloc(sizeof(double) * L);
+    double *DL = (double *)malloc(sizeof(double) * L);
+    double *accN = (double *)malloc(sizeof(double) * L);
+    double *DN = (double *)malloc(sizeof(double) * L);
+    int64_t drops = 0;
+    if (!xd || !z || !g || !u || !a || !y || !yabs || !accL || !DL || !accN || !DN) { drops = -1; goto done; }
+
+    for (int64_t t = 0; t < T; t++) {
+        double *ot = out + t * H;
+        double *dt = denom ? denom + t * H : NULL;
+        for (int64_t i = 0; i < H; i++) xd[i] = k3o_bf16(x[t * H + i]);
+        k3o_bf16_gemv(z, NULL, xd, lat_down, H, L);
+        for (int64_t l = 0; l < L; l++) { accL[l] = 0.0; DL[l] = 0.0; }
+        for (int64_t j = 0; j < topk; j++) {
+            const int32_t e = idx[t * topk + j];
+            if (e < 0 || e >= E) { drops++; continue; }
+            const int32_t s = slot_of[e];
+            if (s < 0) { drops = -1; goto done; }
+            k3o_mxfp4_gemv(g, NULL, z, gate_packed + s * gp, gate_scales + s * gs, L, I);
+            k3o_mxfp4_gemv(u, NULL, z, up_packed + s * gp, up_scales + s * gs, L, I);
+            for (int64_t n = 0; n < I; n++) a[n] = k3o_act(g[n], u[n], act, b1, b2);
+            k3o_mxfp4_gemv(y, yabs, a, down_packed + s * dp, down_scales + s * ds, I, L);
+            const double wj = (double)w[t * topk + j];
+            for (int64_t l = 0; l < L; l++) {
+                accL[l] += wj * y[l];
+                DL[l] += fabs(wj) * yabs[l];
+            }
+        }
+        if (norm) {
+            double ss = 0.0, cross = 0.0;
+            for (int64_t l = 0; l < L; l++) { ss += accL[l] * accL[l]; cross += fabs(accL[l]) * DL[l]; }
+            const double inv = k3o_rmsnorm(accN, accL, gamma, L, eps);
+            for (int64_t l = 0; l < L; l++) {
+                const double gl = gamma ? fabs((double)gamma[l]) : 1.0;
+                DN[l] = inv * gl * DL[l] + (ss > 0.0 ? fabs(accN[l]) * cross / ss : 0.0);
+            }
+        } else {
+            for (int64_t l = 0; l < L; l++) { accN[l] = accL[l]; DN[l] = DL[l]; }
+        }
+        k3o_bf16_gemv(ot, NULL, accN, lat_up, L, H);
+        if (dt) {
+            for (int64_t o = 0; o < H; o++) {
+                double d = 0.0;
+                for (int64_t l = 0; l < L; l++) d += fabs(k3o_bf16(lat_up[o * L + l])) * DN[l];
+                dt[o] = d;
+            }
+        }
+        if (Is > 0) {
+            k3o_bf16_gemv(g, NULL, xd, sh_gate, H, Is);
+            k3o_bf16_gemv(u, NULL, xd, sh_up, H, Is);
+            for (int64_t n = 0; n < Is; n++) a[n] = k3o_act(g[n], u[n], act, b1, b2);
+            k3o_bf16_gemv(y, yabs, a, sh_down, Is, H);
+            for (int64_t o = 0; o < H; o++) {
+                ot[o] += y[o];
+                if (dt) dt[o] += yabs[o];
+            }
+        }
+    }
+done:
+    free(xd); free(z); free(g); free(u); free(a); free(y); free(yabs);
+    free(accL); free(DL); free(accN); free(DN);
     return drops;
 }
 

@@ -65,7 +65,7 @@ def bf16_tensor(bits, device):
 
 def layer_tensors(spec: synth.LayerSpec, layer: int = 0, device="cuda"):
     """All weights of one synthetic layer, resident in HBM."""
-    E, H, I = spec.n_experts, spec.hidden, spec.inter
+    E, H, I = spec.n_experts, spec.ek, spec.inter
     d = {}
     d["router_w"] = bf16_tensor(synth.make_router(spec, layer), device)
     b = synth.make_bias(spec, layer)
@@ -84,6 +84,12 @@ def layer_tensors(spec: synth.LayerSpec, layer: int = 0, device="cuda"):
         d["sh_gate"] = d["sh_up"] = d["sh_down"] = None
     else:
         d["sh_gate"], d["sh_up"], d["sh_down"] = (bf16_tensor(s, device) for s in sh)
+    lat = synth.make_latent(spec, layer)
+    if lat is None:
+        d["lat_down"] = d["lat_up"] = d["lat_norm"] = None
+    else:
+        d["lat_down"], d["lat_up"] = bf16_tensor(lat[0], device), bf16_tensor(lat[1], device)
+        d["lat_norm"] = torch.from_numpy(lat[2]).to(device)
     return d
 
 
