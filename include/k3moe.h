@@ -9,9 +9,11 @@
  * What the layer computes is stated on the "kimi-k3-in-c" README
  * (FareedKhan-dev): §9 "Picking 16 experts of 896" gives the router
  * (k3_router) and the layer (k3_moe, k3_situ_glu); §4 "Reduction one: the
- * experts already ship at half a byte" gives the MXFP4 weight format. In this
- * library the layer is flat: experts take the hidden vector directly (no
- * latent down/up projection and no norm on the aggregate).
+ * experts already ship at half a byte" gives the MXFP4 weight format; §5
+ * "Kernels with a floating point contract" gives k3_rmsnorm. A layer is flat
+ * (latent = 0: the experts take the hidden vector directly) or latent (the
+ * pages' k3_moe: the experts run in a narrow latent between a bf16 down- and
+ * up-projection, with an RMSNorm on their aggregate).
  *
  * Per token x (bf16, hidden H):
  *   route:   logit[e] = Wr[e] . x                (exact products, fp64 sum)
@@ -20,9 +22,19 @@
  *            idx[0..k) = the k largest ch, largest first, equal ch -> lower e
  *            w[j] = sc[idx[j]]; if renorm and s = sum_j w[j] > 0: w[j] /= s;
  *            w[j] *= routed_scale                     (fp32, j order)
- *   forward: out = sum_j w[j] * W2_e( act(W1_e x, W3_e x) ),  e = idx[j],
+ *   forward (flat):
+ *            out = sum_j w[j] * W2_e( act(W1_e x, W3_e x) ),  e = idx[j],
  *                  summed in router order j = 0..k-1, then
  *            out += S2( act(S1 x, S3 x) )             shared expert, unweighted
+ *   forward (latent, width L):
+ *            z    = Wd x                              bf16 [L][H], fp32 result
+ *            acc  = sum_j w[j] * W2_e( act(W1_e z, W3_e z) )   router order;
+ *                   the experts are [I][L] (W1, W3) and [L][I] (W2)
+ *            acc  = acc * inv * gamma,  inv = 1/sqrt(sum(acc^2)/L + eps)
+ *                   if latent_norm (the AGGREGATE is normed, not each expert)
+ *            out  = Wu acc                            bf16 [H][L]
+ *            out += S2( act(S1 x, S3 x) )             shared expert on the
+ *                                                     ORIGINAL x, unweighted
  *   act:     SiTU-GLU  b1*tanh(g/b1) * sigmoid(g) * b2*tanh(u/b2)   (default)
  *            SwiGLU    g * sigmoid(g) * u
  *
@@ -41,7 +53,7 @@
 extern "C" {
 #endif
 
-#define K3MOE_ABI_VERSION 1u
+#define K3MOE_ABI_VERSION 2u
 
 typedef enum {
     K3MOE_OK = 0,
@@ -64,7 +76,10 @@ typedef enum {
  * K3MOE_ABI_VERSION (README §2 states the same refusal to guess for the
  * model's config). Supported sizes: hidden and inter positive multiples of
  * 128; shared_inter 0 (no shared expert) or a positive multiple of 128;
- * 1 <= topk <= n_experts <= 4096. */
+ * 1 <= topk <= n_experts <= 4096; latent 0 or a positive multiple of 128.
+ * Two shared experts of width I_s each (the pages' n_shared = 2) are one
+ * shared expert of width 2 I_s with their rows stacked (the activation is
+ * elementwise, so the sum of the two is the stacked one). */
 typedef struct {
     uint32_t struct_size;
     uint32_t abi_version;
@@ -78,6 +93,11 @@ typedef struct {
     int32_t act;           /* k3moe_act                                     */
     float situ_b1;         /* SiTU gate beta (> 0, finite; README uses 4)   */
     float situ_b2;         /* SiTU up beta   (> 0, finite; README uses 25)  */
+    int32_t latent;        /* L: 0 = flat layer; > 0 = experts at width L   */
+    int32_t latent_norm;   /* latent: 1 = RMSNorm on the aggregate, 0 = none;
+                              flat: must be 0                               */
+    float rms_eps;         /* latent_norm: epsilon inside the square root
+                              (> 0, finite; README uses 1e-5); else ignored */
 } k3moe_config;
 
 /* One MXFP4 matrix per expert, E of them. Expert e's packed nibbles start
@@ -97,12 +117,18 @@ typedef struct {
  * router_w is bf16 [n_experts][hidden]; router_bias is fp32 [n_experts] or
  * NULL for no bias. Shared expert (bf16, NULL iff shared_inter == 0):
  * sh_gate and sh_up [shared_inter][hidden], sh_down [hidden][shared_inter].
+ * Latent layer (latent = L > 0; all three NULL for a flat layer): lat_down
+ * bf16 [L][hidden], lat_up bf16 [hidden][L], lat_norm fp32 [L] (the norm's
+ * gamma; NULL iff latent_norm == 0); the experts' gate and up are then
+ * [inter][L] and down [L][inter].
  * bf16 tensors are uint16 bit patterns; all bases 16-byte aligned. */
 typedef struct {
     const uint16_t *router_w;
     const float *router_bias;
     k3moe_mxfp4 gate, up, down;
     const uint16_t *sh_gate, *sh_up, *sh_down;
+    const uint16_t *lat_down, *lat_up;
+    const float *lat_norm;
 } k3moe_weights;
 
 typedef struct k3moe_layer k3moe_layer;
@@ -170,7 +196,9 @@ typedef enum {
     K3MOE_STAGE_SHARED_GATEUP = 5,  /* shared expert gate/up + activation */
     K3MOE_STAGE_DOWN = 6,           /* down MXFP4 (+ shared down)         */
     K3MOE_STAGE_COMBINE = 7,        /* router-order weighted sum + shared */
-    K3MOE_N_STAGES = 8
+    K3MOE_STAGE_LATENT_IN = 8,      /* latent: down-projection of x       */
+    K3MOE_STAGE_LATENT_OUT = 9,     /* latent: norm and up-projection     */
+    K3MOE_N_STAGES = 10
 } k3moe_stage;
 
 k3moe_status k3moe_profile_enable(k3moe_layer *layer, int enable);

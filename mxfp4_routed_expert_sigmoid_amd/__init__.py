@@ -14,7 +14,7 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libk3moe.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 ACT_SITU, ACT_SWIGLU = 1, 2
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "invalid or incomplete config",
@@ -35,7 +35,9 @@ class Config(ctypes.Structure):
                 ("n_experts", ctypes.c_int32), ("topk", ctypes.c_int32),
                 ("shared_inter", ctypes.c_int32), ("renorm", ctypes.c_int32),
                 ("routed_scale", ctypes.c_float), ("act", ctypes.c_int32),
-                ("situ_b1", ctypes.c_float), ("situ_b2", ctypes.c_float)]
+                ("situ_b1", ctypes.c_float), ("situ_b2", ctypes.c_float),
+                ("latent", ctypes.c_int32), ("latent_norm", ctypes.c_int32),
+                ("rms_eps", ctypes.c_float)]
 
 
 class MXFP4(ctypes.Structure):
@@ -48,14 +50,16 @@ class Weights(ctypes.Structure):
     _fields_ = [("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
                 ("gate", MXFP4), ("up", MXFP4), ("down", MXFP4),
                 ("sh_gate", ctypes.c_void_p), ("sh_up", ctypes.c_void_p),
-                ("sh_down", ctypes.c_void_p)]
+                ("sh_down", ctypes.c_void_p), ("lat_down", ctypes.c_void_p),
+                ("lat_up", ctypes.c_void_p), ("lat_norm", ctypes.c_void_p)]
 
 
 _lib = None
 EXPORTS = ("k3moe_layer_create", "k3moe_workspace_size", "k3moe_route", "k3moe_forward",
            "k3moe_error_count", "k3moe_error_reset", "k3moe_profile_enable",
            "k3moe_profile_read", "k3moe_layer_destroy", "k3moe_status_string")
-STAGES = ("router", "topk", "xsplit", "perm", "gateup", "shared_gateup", "down", "combine")
+STAGES = ("router", "topk", "xsplit", "perm", "gateup", "shared_gateup", "down", "combine",
+          "latent_in", "latent_out")
 
 
 def lib():
@@ -92,9 +96,10 @@ def lib():
 
 
 def make_config(hidden, inter, n_experts, topk, shared_inter=0, renorm=1, routed_scale=1.0,
-                act=ACT_SITU, situ_b1=4.0, situ_b2=25.0):
+                act=ACT_SITU, situ_b1=4.0, situ_b2=25.0, latent=0, latent_norm=0, rms_eps=0.0):
     return Config(ctypes.sizeof(Config), ABI_VERSION, hidden, inter, n_experts, topk,
-                  shared_inter, renorm, routed_scale, act, situ_b1, situ_b2)
+                  shared_inter, renorm, routed_scale, act, situ_b1, situ_b2, latent,
+                  latent_norm, rms_eps)
 
 
 def _ptr(t):
@@ -129,15 +134,20 @@ class Layer:
     router_bias fp32 [E] or None; gate/up packed uint8 [E][I][H/2] and scales
     uint8 [E][I][H/32]; down packed [E][H][I/2] and scales [E][H][I/32];
     shared sh_gate/sh_up [Is][H], sh_down [H][Is] (bf16/int16) or None.
+    Latent layer (cfg.latent = L > 0): the experts are [E][I][L/2] (gate, up)
+    and [E][L][I/2] (down), lat_down bf16 [L][H], lat_up bf16 [H][L],
+    lat_norm fp32 [L] (None without the norm).
     The handle keeps references to the tensors so they outlive it.
     """
 
     def __init__(self, cfg: Config, router_w, router_bias, gate_packed, gate_scales, up_packed,
-                 up_scales, down_packed, down_scales, sh_gate=None, sh_up=None, sh_down=None):
+                 up_scales, down_packed, down_scales, sh_gate=None, sh_up=None, sh_down=None,
+                 lat_down=None, lat_up=None, lat_norm=None):
         for t, n in ((router_w, "router_w"), (sh_gate, "sh_gate"), (sh_up, "sh_up"),
-                     (sh_down, "sh_down")):
+                     (sh_down, "sh_down"), (lat_down, "lat_down"), (lat_up, "lat_up")):
             _dev(t, (2,), n)
         _dev(router_bias, (4,), "router_bias")
+        _dev(lat_norm, (4,), "lat_norm")
         for t, n in ((gate_packed, "gate_packed"), (gate_scales, "gate_scales"),
                      (up_packed, "up_packed"), (up_scales, "up_scales"),
                      (down_packed, "down_packed"), (down_scales, "down_scales")):
@@ -145,7 +155,7 @@ class Layer:
         self.cfg = cfg
         self.device = router_w.device
         self._keep = (router_w, router_bias, gate_packed, gate_scales, up_packed, up_scales,
-                      down_packed, down_scales, sh_gate, sh_up, sh_down)
+                      down_packed, down_scales, sh_gate, sh_up, sh_down, lat_down, lat_up, lat_norm)
         E = cfg.n_experts
 
         def mx(p, s):
@@ -154,7 +164,7 @@ class Layer:
         self.weights = Weights(router_w.data_ptr(), _ptr(router_bias),
                                mx(gate_packed, gate_scales), mx(up_packed, up_scales),
                                mx(down_packed, down_scales), _ptr(sh_gate), _ptr(sh_up),
-                               _ptr(sh_down))
+                               _ptr(sh_down), _ptr(lat_down), _ptr(lat_up), _ptr(lat_norm))
         h = ctypes.c_void_p()
         with torch.cuda.device(self.device):
             _check(lib().k3moe_layer_create(ctypes.byref(cfg), ctypes.byref(self.weights),

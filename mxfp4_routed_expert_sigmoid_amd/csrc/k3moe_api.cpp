@@ -23,6 +23,7 @@ static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 WsLayout ws_layout(const k3moe_config &c, int64_t T)
 {
     const int64_t H = c.hidden, I = c.inter, E = c.n_experts, K = c.topk, Is = c.shared_inter;
+    const int64_t Lt = c.latent, EK = Lt ? Lt : H;
     const int64_t nchunks = std::max<int64_t>(1, (T + kPermChunk - 1) / kPermChunk);
     WsLayout L;
     size_t o = 0;
@@ -51,11 +52,11 @@ WsLayout ws_layout(const k3moe_config &c, int64_t T)
     L.sorted = take(sizeof(int32_t) * std::max<int64_t>(1, T * K));
     L.act = take((size_t)T * K * 4 * I);
     L.ash = take(sizeof(float) * T * std::max<int64_t>(Is, 1));
-    L.ys = take(sizeof(float) * T * (K + 1) * H);
+    L.ys = take(sizeof(float) * T * (K + 1) * std::max(H, EK));
     {
         // the slice count is non-increasing in T: the largest buffer over T' <= T
         size_t part = 0;
-        for (int64_t t = 2; t <= std::min<int64_t>(T, 4096); ++t) {
+        for (int64_t t = 1; t <= std::min<int64_t>(T, 4096); ++t) {  // one token too: the grouped path can take it
             const int S = stream_shared_slices((int)t);
             if (S > 1) part = std::max(part, sizeof(float) * S * t * 2 * Is);
         }
@@ -65,6 +66,21 @@ WsLayout ws_layout(const k3moe_config &c, int64_t T)
     L.tiles_dn = take(sizeof(int2) * grouped_tile_cap_dn(T, (int)K, (int)E));
     L.light = take(sizeof(int32_t) * 2 * E);
     L.tile_n = take(4 * sizeof(int32_t));
+    if (Lt > 0) {
+        L.lat_z = take((size_t)T * Lt * 4);
+        L.lat_acc = take(sizeof(float) * T * Lt);
+        L.lat_n = take((size_t)T * Lt * 4);
+        L.lat_ysh = take(sizeof(float) * T * H);
+        // projection partial sums: the largest over T' <= T of either projection
+        // (one slice at least: the projections always sum through them)
+        size_t part = sizeof(float) * T * std::max(Lt, H);
+        for (int64_t t = 1; t <= std::min<int64_t>(T, 4096); ++t) {
+            const int Sd = proj_splits(t, (int)Lt, (int)H), Su = proj_splits(t, (int)H, (int)Lt);
+            if (Sd > 1) part = std::max(part, sizeof(float) * Sd * t * Lt);
+            if (Su > 1) part = std::max(part, sizeof(float) * Su * t * H);
+        }
+        L.lat_part = take(part);
+    }
     L.total = o;
     return L;
 }
@@ -87,8 +103,19 @@ static k3moe_status check_config(const k3moe_config *c)
         return K3MOE_E_CONFIG;
     if (c->hidden % 128 || c->inter % 128 || c->shared_inter % 128) return K3MOE_E_UNSUPPORTED_SHAPE;
     if (c->n_experts > kMaxExperts || c->topk > kMaxTopk) return K3MOE_E_UNSUPPORTED_SHAPE;
+    if (c->latent < 0) return K3MOE_E_CONFIG;
+    if (c->latent == 0) {
+        if (c->latent_norm != 0) return K3MOE_E_CONFIG;
+    } else {
+        if (c->latent_norm != 0 && c->latent_norm != 1) return K3MOE_E_CONFIG;
+        if (c->latent_norm && !(isfinite(c->rms_eps) && c->rms_eps > 0.0f)) return K3MOE_E_CONFIG;
+        if (c->latent % 128) return K3MOE_E_UNSUPPORTED_SHAPE;
+    }
     // 32-bit row/element indexing inside the kernels
-    if ((int64_t)c->hidden * c->inter > (int64_t)1 << 30) return K3MOE_E_UNSUPPORTED_SHAPE;
+    const int64_t ek = c->latent ? c->latent : c->hidden;
+    if ((int64_t)c->hidden * c->inter > (int64_t)1 << 30 || ek * c->inter > (int64_t)1 << 30 ||
+        ek * c->hidden > (int64_t)1 << 30)
+        return K3MOE_E_UNSUPPORTED_SHAPE;
     return K3MOE_OK;
 }
 
@@ -110,9 +137,18 @@ static k3moe_status check_weights(const k3moe_config *c, const k3moe_weights *w)
     if (!aligned(w->router_w, 16) || (w->router_bias && !aligned(w->router_bias, 4)))
         return K3MOE_E_ALIGNMENT;
     k3moe_status s;
-    if ((s = check_mxfp4(w->gate, c->inter, c->hidden, c->n_experts)) != K3MOE_OK) return s;
-    if ((s = check_mxfp4(w->up, c->inter, c->hidden, c->n_experts)) != K3MOE_OK) return s;
-    if ((s = check_mxfp4(w->down, c->hidden, c->inter, c->n_experts)) != K3MOE_OK) return s;
+    const int64_t ek = c->latent ? c->latent : c->hidden;  // width the experts run at
+    if ((s = check_mxfp4(w->gate, c->inter, ek, c->n_experts)) != K3MOE_OK) return s;
+    if ((s = check_mxfp4(w->up, c->inter, ek, c->n_experts)) != K3MOE_OK) return s;
+    if ((s = check_mxfp4(w->down, ek, c->inter, c->n_experts)) != K3MOE_OK) return s;
+    if (c->latent == 0) {
+        if (w->lat_down || w->lat_up || w->lat_norm) return K3MOE_E_INVALID_ARG;
+    } else {
+        if (!w->lat_down || !w->lat_up || (c->latent_norm ? !w->lat_norm : w->lat_norm != nullptr))
+            return K3MOE_E_INVALID_ARG;
+        if (!aligned(w->lat_down, 16) || !aligned(w->lat_up, 16) || (w->lat_norm && !aligned(w->lat_norm, 16)))
+            return K3MOE_E_ALIGNMENT;
+    }
     const bool any = w->sh_gate || w->sh_up || w->sh_down;
     const bool all = w->sh_gate && w->sh_up && w->sh_down;
     if (c->shared_inter == 0 ? any : !all) return K3MOE_E_INVALID_ARG;
@@ -153,6 +189,13 @@ static LayerView view(const k3moe_layer *l)
     v.sh_gate = w.sh_gate;
     v.sh_up = w.sh_up;
     v.sh_down = w.sh_down;
+    v.Lt = c.latent;
+    v.EK = c.latent ? c.latent : c.hidden;
+    v.lat_norm_on = c.latent ? c.latent_norm : 0;
+    v.lat_eps = c.rms_eps;
+    v.lat_down = w.lat_down;
+    v.lat_up = w.lat_up;
+    v.lat_norm = w.lat_norm;
     v.errors = l->errors;
     return v;
 }

@@ -166,16 +166,23 @@ __global__ __launch_bounds__(1024) void k_tiles(const int32_t *__restrict__ acti
 // 128c + 32g + [0, 32) of its row (g = lane / 16); MFMA step s uses
 // K = 128c + 32g + 8s + [0, 8), and the token side reads the same K from LDS.
 // bf16 weights: chunk c, lane group g holds K = 32c + 8g + [0, 8), one step.
-template <bool GU> struct GemmShape;
-template <> struct GemmShape<true> {   // gate/up: 8 waves x 32 rows, 128 tokens
+// Tile kinds: gate/up on bf16 tokens, down on the activation's hi and lo,
+// gate/up on tokens given as hi and lo (a latent layer's fp32 z).
+constexpr int kGU = 0, kDN = 1, kGU2 = 2;
+template <int KIND> struct GemmShape;
+template <> struct GemmShape<kGU> {   // gate/up: 8 waves x 32 rows, 128 tokens
     static constexpr int WAVES = 8, RF = 2, TF = 8, NMAT = 2, NPL = 1, TOK = 128;
 };
-template <> struct GemmShape<false> {  // down: 4 waves x 64 rows, 64 tokens (hi, lo)
+template <> struct GemmShape<kDN> {   // down: 4 waves x 64 rows, 64 tokens (hi, lo)
     static constexpr int WAVES = 4, RF = 4, TF = 4, NMAT = 1, NPL = 2, TOK = 64;
 };
-constexpr int kTileRows = 256;  // weight rows per block (both shapes)
-static_assert(GemmShape<true>::WAVES * GemmShape<true>::RF * 16 == kTileRows, "gate/up tile rows");
-static_assert(GemmShape<false>::WAVES * GemmShape<false>::RF * 16 == kTileRows, "down tile rows");
+template <> struct GemmShape<kGU2> {  // gate/up, tokens as hi and lo: 8 waves x 32 rows, 64 tokens
+    static constexpr int WAVES = 8, RF = 2, TF = 4, NMAT = 2, NPL = 2, TOK = 64;
+};
+constexpr int kTileRows = 256;  // weight rows per block (every shape)
+static_assert(GemmShape<kGU>::WAVES * GemmShape<kGU>::RF * 16 == kTileRows, "gate/up tile rows");
+static_assert(GemmShape<kDN>::WAVES * GemmShape<kDN>::RF * 16 == kTileRows, "down tile rows");
+static_assert(GemmShape<kGU2>::WAVES * GemmShape<kGU2>::RF * 16 == kTileRows, "gate/up tile rows");
 
 struct GemmParams {
     int rows, KD, K, T, act;   // weight rows (I / I_s or H), reduction length (H or I / I_s), top-k
@@ -195,18 +202,19 @@ struct GemmParams {
     float *ys;                 // down: staging [T][K + 1][H]
 };
 
-template <bool GU>
+template <int KIND>
 __host__ __device__ constexpr int gemm_lds_bytes()
 {
-    using S = GemmShape<GU>;
+    using S = GemmShape<KIND>;
     return 2 * S::NPL * S::TOK * (128 * 2 + kBPad) + 2 * S::TOK * 4;
 }
 
-template <bool GU, bool FP4>
+template <int KIND, bool FP4>
 __device__ __forceinline__ void gemm_tile(const GemmParams &p, int e, int rb, int p0, int n, const int *bro_l,
                                           const int *oro_l, uint8_t *B_l)
 {
-    using S = GemmShape<GU>;
+    using S = GemmShape<KIND>;
+    constexpr bool GU = KIND != kDN;
     constexpr int WAVES = S::WAVES, RF = S::RF, TF = S::TF, NMAT = S::NMAT, NPL = S::NPL, TOK = S::TOK;
     constexpr int NT = 64 * WAVES;
     constexpr int KC = FP4 ? 128 : 32;           // K per chunk
@@ -395,10 +403,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &p, int e, int rb, in
 
 // One launch: the shared expert's tiles first (bf16 weights, tokens in
 // order), then the routed tiles from the list (fp4 weights).
-template <bool GU>
-__global__ __launch_bounds__(64 * GemmShape<GU>::WAVES) void k_gemm(GemmParams p)
+template <int KIND>
+__global__ __launch_bounds__(64 * GemmShape<KIND>::WAVES) void k_gemm(GemmParams p)
 {
-    using S = GemmShape<GU>;
+    using S = GemmShape<KIND>;
+    constexpr bool GU = KIND != kDN;
     extern __shared__ __align__(16) uint8_t lds[];
     uint8_t *B_l = lds;
     int *bro_l = reinterpret_cast<int *>(lds + 2 * S::NPL * S::TOK * (128 * 2 + kBPad));  // token plane row per column
@@ -416,7 +425,7 @@ __global__ __launch_bounds__(64 * GemmShape<GU>::WAVES) void k_gemm(GemmParams p
             oro_l[c] = GU ? t : t * (p.K + 1) + p.K;
         }
         __syncthreads();
-        gemm_tile<GU, false>(p, 0, rb, p0, n, bro_l, oro_l, B_l);
+        gemm_tile<KIND, false>(p, 0, rb, p0, n, bro_l, oro_l, B_l);
         return;
     }
     b -= p.sh_blocks;
@@ -432,7 +441,7 @@ __global__ __launch_bounds__(64 * GemmShape<GU>::WAVES) void k_gemm(GemmParams p
         oro_l[c] = GU ? p0 + cc : (a / p.K) * (p.K + 1) + a % p.K;
     }
     __syncthreads();
-    gemm_tile<GU, true>(p, e, rb, p0, n, bro_l, oro_l, B_l);
+    gemm_tile<KIND, true>(p, e, rb, p0, n, bro_l, oro_l, B_l);
 }
 
 }  // namespace
@@ -441,10 +450,12 @@ __global__ __launch_bounds__(64 * GemmShape<GU>::WAVES) void k_gemm(GemmParams p
 // validated multiples of 128 at layer creation).
 static bool set_lds_limits()
 {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm<true>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes<true>());
-    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm<false>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes<false>());
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm<kGU>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes<kGU>());
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm<kDN>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes<kDN>());
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm<kGU2>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes<kGU2>());
     return true;
 }
 
@@ -458,19 +469,26 @@ size_t grouped_tile_cap(int64_t T, int K, int E, int bn, int smax)
     return (size_t)(n / bn + std::min<int64_t>(E, n / (smax + 1)) + 1);
 }
 
-size_t grouped_tile_cap_gu(int64_t T, int K, int E) { return grouped_tile_cap(T, K, E, GemmShape<true>::TOK, 0); }
-size_t grouped_tile_cap_dn(int64_t T, int K, int E) { return grouped_tile_cap(T, K, E, GemmShape<false>::TOK, 0); }
+// Workspace sizes: the smaller gate/up tile of the two token forms
+size_t grouped_tile_cap_gu(int64_t T, int K, int E)
+{
+    return grouped_tile_cap(T, K, E, std::min(GemmShape<kGU>::TOK, GemmShape<kGU2>::TOK), 0);
+}
+size_t grouped_tile_cap_dn(int64_t T, int K, int E) { return grouped_tile_cap(T, K, E, GemmShape<kDN>::TOK, 0); }
 
-hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const int32_t *active_n,
-                          const int32_t *active_e, const int32_t *active_off, const int32_t *sorted,
-                          uint16_t *act_hi, uint16_t *act_lo, uint16_t *ash_hi, uint16_t *ash_lo,
-                          float *sh_part, int2 *tiles_gu, int2 *tiles_dn, int32_t *light, int32_t *counts,
-                          float *ys, hipStream_t s, Profiler *prof)
+hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t *xr, const uint16_t *xr_lo, int T,
+                          const int32_t *active_n, const int32_t *active_e, const int32_t *active_off,
+                          const int32_t *sorted, uint16_t *act_hi, uint16_t *act_lo, uint16_t *ash_hi,
+                          uint16_t *ash_lo, float *sh_part, int2 *tiles_gu, int2 *tiles_dn, int32_t *light,
+                          int32_t *counts, float *ys, float *ysh, hipStream_t s, Profiler *prof)
 {
     static const bool lds_set = set_lds_limits();  // once per process (thread-safe static)
     (void)lds_set;
-    constexpr int TG = GemmShape<true>::TOK, TD = GemmShape<false>::TOK;
+    const bool two = xr_lo != nullptr;  // routed tokens as hi and lo planes
+    const int TG = two ? GemmShape<kGU2>::TOK : GemmShape<kGU>::TOK, TD = GemmShape<kDN>::TOK;
+    constexpr int TGS = GemmShape<kGU>::TOK;  // the shared expert's gate/up tiles
     const int rb_i = (L.I + kTileRows - 1) / kTileRows, rb_h = (L.H + kTileRows - 1) / kTileRows;
+    const int rb_r = (L.EK + kTileRows - 1) / kTileRows;  // routed down rows
     const int rb_s = (L.Is + kTileRows - 1) / kTileRows;
     const bool stream = stream_path_ok(L), stream_dn = stream_down_ok(L);
     const bool sh_stream = stream_shared_ok(L, T);
@@ -486,13 +504,13 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const in
     {
         StageMark m(prof, K3MOE_STAGE_GATEUP, s);
         if (stream) {
-            const hipError_t e = launch_stream_gu(L, x, T, active_e, active_off, sorted, light_gu, counts + 2,
-                                                  sh_stream, act_hi, act_lo, ash_hi, ash_lo, sh_part, s);
+            const hipError_t e = launch_stream_gu(L, x, xr, xr_lo, T, active_e, active_off, sorted, light_gu,
+                                                  counts + 2, sh_stream, act_hi, act_lo, ash_hi, ash_lo, sh_part, s);
             if (e != hipSuccess) return e;
         }
         GemmParams gp{};
         gp.rows = L.I;
-        gp.KD = L.H;
+        gp.KD = L.EK;
         gp.K = L.K;
         gp.T = T;
         gp.act = L.act;
@@ -506,7 +524,8 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const in
         gp.wsp[1] = L.u_sp;
         gp.wss[0] = L.g_ss;
         gp.wss[1] = L.u_ss;
-        gp.bp[0] = gp.bp[1] = x;
+        gp.bp[0] = xr;
+        gp.bp[1] = two ? xr_lo : xr;
         gp.active_e = active_e;
         gp.active_off = active_off;
         gp.sorted = sorted;
@@ -514,28 +533,33 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const in
         gp.tile_n = counts;
         gp.ohi = act_hi;
         gp.olo = act_lo;
-        k_gemm<true><<<(unsigned)(cap_gu * rb_i), 64 * GemmShape<true>::WAVES, gemm_lds_bytes<true>(), s>>>(gp);
+        if (two)
+            k_gemm<kGU2><<<(unsigned)(cap_gu * rb_i), 64 * GemmShape<kGU2>::WAVES, gemm_lds_bytes<kGU2>(), s>>>(gp);
+        else
+            k_gemm<kGU><<<(unsigned)(cap_gu * rb_i), 64 * GemmShape<kGU>::WAVES, gemm_lds_bytes<kGU>(), s>>>(gp);
         if (L.Is > 0 && !sh_stream) {
             StageMark m2(prof, K3MOE_STAGE_SHARED_GATEUP, s);
             GemmParams sp = gp;
             sp.rows = L.Is;
+            sp.KD = L.H;
+            sp.bp[0] = sp.bp[1] = x;
             sp.wb[0] = L.sh_gate;
             sp.wb[1] = L.sh_up;
             sp.ohi = ash_hi;
             sp.olo = ash_lo;
-            sp.sh_blocks = ((T + TG - 1) / TG) * rb_s;
-            k_gemm<true><<<(unsigned)sp.sh_blocks, 64 * GemmShape<true>::WAVES, gemm_lds_bytes<true>(), s>>>(sp);
+            sp.sh_blocks = ((T + TGS - 1) / TGS) * rb_s;
+            k_gemm<kGU><<<(unsigned)sp.sh_blocks, 64 * GemmShape<kGU>::WAVES, gemm_lds_bytes<kGU>(), s>>>(sp);
         }
     }
     {
         StageMark m(prof, K3MOE_STAGE_DOWN, s);
         if (stream_dn) {
             const hipError_t e = launch_stream_dn(L, T, active_e, active_off, sorted, light_dn, counts + 3,
-                                                  sh_stream, act_hi, act_lo, ash_hi, ash_lo, ys, s);
+                                                  sh_stream, act_hi, act_lo, ash_hi, ash_lo, ys, ysh, s);
             if (e != hipSuccess) return e;
         }
         GemmParams dp{};
-        dp.rows = L.H;
+        dp.rows = L.EK;
         dp.KD = L.I;
         dp.K = L.K;
         dp.T = T;
@@ -551,15 +575,19 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const in
         dp.tiles = tiles_dn;
         dp.tile_n = counts + 1;
         dp.ys = ys;
-        k_gemm<false><<<(unsigned)(cap_dn * rb_h), 64 * GemmShape<false>::WAVES, gemm_lds_bytes<false>(), s>>>(dp);
+        k_gemm<kDN><<<(unsigned)(cap_dn * rb_r), 64 * GemmShape<kDN>::WAVES, gemm_lds_bytes<kDN>(), s>>>(dp);
         if (L.Is > 0 && !sh_stream) {
+            // shared rows of H: to slot k of ys (flat), or to ysh [T][H] (K = 0 makes the row t)
             GemmParams sp = dp;
+            sp.rows = L.H;
             sp.KD = L.Is;
+            sp.K = ysh ? 0 : L.K;
+            sp.ys = ysh ? ysh : ys;
             sp.wb[0] = sp.wb[1] = L.sh_down;
             sp.bp[0] = ash_hi;
             sp.bp[1] = ash_lo;
             sp.sh_blocks = ((T + TD - 1) / TD) * rb_h;
-            k_gemm<false><<<(unsigned)sp.sh_blocks, 64 * GemmShape<false>::WAVES, gemm_lds_bytes<false>(), s>>>(sp);
+            k_gemm<kDN><<<(unsigned)sp.sh_blocks, 64 * GemmShape<kDN>::WAVES, gemm_lds_bytes<kDN>(), s>>>(sp);
         }
     }
     return hipGetLastError();

@@ -38,6 +38,12 @@ struct WsLayout {
     size_t tiles_gu, tiles_dn;  // grouped-GEMM tile lists, int2 each
     size_t light;             // int32 [2][E]: experts for the weight-streaming kernels (gate/up, down)
     size_t tile_n;            // int32 [4]: gate/up tiles, down tiles, light gate/up, light down
+    // latent layer only (0 otherwise)
+    size_t lat_z = 0;         // z = Wd x as bf16 hi then lo planes [T][L] (4 bytes per element)
+    size_t lat_acc = 0;       // routed aggregate fp32 [T][L]
+    size_t lat_n = 0;         // normed aggregate as bf16 hi then lo planes [T][L]
+    size_t lat_ysh = 0;       // shared expert output fp32 [T][H]
+    size_t lat_part = 0;      // projection partial sums fp32 [slices][T][rows]
     size_t total;
 };
 
@@ -52,6 +58,11 @@ struct LayerView {
     const uint8_t *gp, *gs, *up, *us, *dp, *ds;
     int64_t g_sp, g_ss, u_sp, u_ss, d_sp, d_ss;
     const uint16_t *sh_gate, *sh_up, *sh_down;
+    int Lt, EK;               // latent width (0: flat); the width the experts run at
+    int lat_norm_on;
+    float lat_eps;
+    const uint16_t *lat_down, *lat_up;
+    const float *lat_norm;
     unsigned long long *errors;
 };
 
@@ -114,14 +125,24 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T,
                           const int32_t *idx, const float *w, float *out, char *ws,
                           const WsLayout &lay, hipStream_t s, Profiler *prof);
 
+// Latent layer (k3moe_latent.hip): projections with bf16 weights, the norm.
+int proj_splits(int64_t T, int R, int Kd);
+hipError_t launch_latent_forward(const LayerView &L, const uint16_t *x, int T, const int32_t *idx,
+                                 const float *w, float *out, char *ws, const WsLayout &lay, hipStream_t s,
+                                 Profiler *prof);
+
 // Grouped GEMMs for batches (k3moe_grouped.hip).
 size_t grouped_tile_cap_gu(int64_t T, int K, int E);
 size_t grouped_tile_cap_dn(int64_t T, int K, int E);
-hipError_t launch_grouped(const LayerView &L, const uint16_t *x, int T, const int32_t *active_n,
-                          const int32_t *active_e, const int32_t *active_off, const int32_t *sorted,
-                          uint16_t *act_hi, uint16_t *act_lo, uint16_t *ash_hi, uint16_t *ash_lo,
-                          float *sh_part, int2 *tiles_gu, int2 *tiles_dn, int32_t *light, int32_t *counts,
-                          float *ys, hipStream_t s, Profiler *prof);
+// xr: the routed experts' tokens, bf16 [T][EK] (x for a flat layer); xr_lo:
+// a second plane (lo of an fp32 input) or null. ysh: the shared expert's
+// output fp32 [T][H], or null for slot k of ys. Routed outputs go to ys
+// [T][k + 1][EK].
+hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t *xr, const uint16_t *xr_lo, int T,
+                          const int32_t *active_n, const int32_t *active_e, const int32_t *active_off,
+                          const int32_t *sorted, uint16_t *act_hi, uint16_t *act_lo, uint16_t *ash_hi,
+                          uint16_t *ash_lo, float *sh_part, int2 *tiles_gu, int2 *tiles_dn, int32_t *light,
+                          int32_t *counts, float *ys, float *ysh, hipStream_t s, Profiler *prof);
 
 // Weight-streaming kernels for experts with few tokens (k3moe_stream.hip).
 bool stream_path_ok(const LayerView &L);
@@ -129,13 +150,19 @@ bool stream_down_ok(const LayerView &L);
 int stream_max_tokens();
 int stream_shared_slices(int T);
 bool stream_shared_ok(const LayerView &L, int T);
-hipError_t launch_stream_gu(const LayerView &L, const uint16_t *x, int T, const int32_t *active_e,
-                            const int32_t *active_off, const int32_t *sorted, const int32_t *light,
-                            const int32_t *light_n, bool with_shared, uint16_t *act_hi, uint16_t *act_lo,
-                            uint16_t *ash_hi, uint16_t *ash_lo, float *sh_part, hipStream_t s);
+hipError_t launch_stream_gu(const LayerView &L, const uint16_t *x, const uint16_t *xr, const uint16_t *xr_lo,
+                            int T, const int32_t *active_e, const int32_t *active_off, const int32_t *sorted,
+                            const int32_t *light, const int32_t *light_n, bool with_shared, uint16_t *act_hi,
+                            uint16_t *act_lo, uint16_t *ash_hi, uint16_t *ash_lo, float *sh_part, hipStream_t s);
 hipError_t launch_stream_dn(const LayerView &L, int T, const int32_t *active_e, const int32_t *active_off,
                             const int32_t *sorted, const int32_t *light, const int32_t *light_n,
                             bool with_shared, const uint16_t *act_hi, const uint16_t *act_lo,
-                            const uint16_t *ash_hi, const uint16_t *ash_lo, float *ys, hipStream_t s);
+                            const uint16_t *ash_hi, const uint16_t *ash_lo, float *ys, float *ysh, hipStream_t s);
+
+// Token -> expert permutation and router-order combine (k3moe_kernels.hip).
+void launch_perm(const LayerView &L, const int32_t *idx, int T, char *ws, const WsLayout &lay, hipStream_t s,
+                 Profiler *prof);
+void launch_combine(const LayerView &L, const float *ys, const float *w, const int32_t *idx, int T, int width,
+                    bool shared, float *out, hipStream_t s);
 
 }  // namespace k3moe

@@ -1366,6 +1366,7 @@ static int down_blocks_per_slot(const LayerView &L, int ncu)
 
 static bool decode_path_ok(const LayerView &L)
 {
+    if (L.Lt > 0) return false;  // a latent layer takes the grouped path at every T
     const bool gu = L.H % 512 != 0 || L.H / 8 <= 64 * kGuDecWaves * kGuStgQ;
     const bool gu_sc = L.H % 512 != 0 || kGuDecUnits * 2 * kGuUnitRows * (L.H / 512) <= 64 * kGuDecWaves * kGuStgS;
     const bool dn = L.I <= 4 * 64 * kDnDecWaves * kDnStgQ &&  // the activation staging, both row forms
@@ -1450,10 +1451,40 @@ static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const
 
 // T > 1 (or shapes the single-token kernels do not take): token -> expert
 // permutation, grouped GEMMs, router-order combine.
+void launch_perm(const LayerView &L, const int32_t *idx, int T, char *ws, const WsLayout &lay, hipStream_t s,
+                 Profiler *prof)
+{
+    int32_t *active_n = reinterpret_cast<int32_t *>(ws + lay.active_n);
+    int32_t *active_e = reinterpret_cast<int32_t *>(ws + lay.active_e);
+    int32_t *active_off = reinterpret_cast<int32_t *>(ws + lay.active_off);
+    int32_t *sorted = reinterpret_cast<int32_t *>(ws + lay.sorted);
+    const int nchunks = (T + kPermChunk - 1) / kPermChunk;
+    StageMark m(prof, K3MOE_STAGE_PERM, s);
+    if (nchunks == 1) {
+        k_perm_small<<<1, 256, 0, s>>>(idx, T, L.K, L.E, active_n, active_e, active_off, sorted);
+    } else {
+        int32_t *chunk_cnt = reinterpret_cast<int32_t *>(ws + lay.chunk_cnt);
+        k_perm_hist<<<nchunks, 256, 0, s>>>(idx, T, L.K, L.E, chunk_cnt);
+        k_perm_scan<<<1, 1024, 0, s>>>(nchunks, L.E, chunk_cnt, active_n, active_e, active_off);
+        k_perm_scatter<<<nchunks, 64, 0, s>>>(idx, T, L.K, L.E, chunk_cnt, sorted);
+    }
+}
+
+// out[t][0..width) = router-order sum of the staging rows ys[t][j] (stride
+// width, k + 1 slots), plus slot k when `shared`.
+void launch_combine(const LayerView &L, const float *ys, const float *w, const int32_t *idx, int T, int width,
+                    bool shared, float *out, hipStream_t s)
+{
+    const int64_t n4 = (int64_t)T * width / 4;
+    k_combine<<<(unsigned)((n4 + kCombineThreads - 1) / kCombineThreads), kCombineThreads, 0, s>>>(
+        ys, w, idx, T, L.K, width, L.E, shared, out, L.errors);
+}
+
 hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const int32_t *idx,
                           const float *w, float *out, char *ws, const WsLayout &lay, hipStream_t s,
                           Profiler *prof)
 {
+    if (L.Lt > 0) return launch_latent_forward(L, x, T, idx, w, out, ws, lay, s, prof);
     int32_t *active_n = reinterpret_cast<int32_t *>(ws + lay.active_n);
     int32_t *active_e = reinterpret_cast<int32_t *>(ws + lay.active_e);
     int32_t *active_off = reinterpret_cast<int32_t *>(ws + lay.active_off);
@@ -1463,18 +1494,7 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const in
     if (T == 1 && decode_path_ok(L))
         return launch_forward_t1(L, x, idx, w, out, reinterpret_cast<float *>(ws + lay.act),
                                  reinterpret_cast<float *>(ws + lay.ash), ws + lay.ys, s, prof);
-    const int nchunks = (T + kPermChunk - 1) / kPermChunk;
-    {
-        StageMark m(prof, K3MOE_STAGE_PERM, s);
-        if (nchunks == 1) {
-            k_perm_small<<<1, 256, 0, s>>>(idx, T, L.K, L.E, active_n, active_e, active_off, sorted);
-        } else {
-            int32_t *chunk_cnt = reinterpret_cast<int32_t *>(ws + lay.chunk_cnt);
-            k_perm_hist<<<nchunks, 256, 0, s>>>(idx, T, L.K, L.E, chunk_cnt);
-            k_perm_scan<<<1, 1024, 0, s>>>(nchunks, L.E, chunk_cnt, active_n, active_e, active_off);
-            k_perm_scatter<<<nchunks, 64, 0, s>>>(idx, T, L.K, L.E, chunk_cnt, sorted);
-        }
-    }
+    launch_perm(L, idx, T, ws, lay, s, prof);
     // activations: routed bf16 hi and lo [T*k][I] in the fp8-term region
     // (4 bytes per element either way); shared bf16 hi and lo [T][Is] in the
     // fp32 shared-activation region
@@ -1482,18 +1502,16 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const in
     uint16_t *act_lo = act_hi + (size_t)T * L.K * L.I;
     uint16_t *ash_hi = reinterpret_cast<uint16_t *>(ws + lay.ash);
     uint16_t *ash_lo = ash_hi + (size_t)T * L.Is;
-    hipError_t e = launch_grouped(L, x, T, active_n, active_e, active_off, sorted, act_hi, act_lo, ash_hi,
-                                  ash_lo, reinterpret_cast<float *>(ws + lay.sh_part),
+    hipError_t e = launch_grouped(L, x, x, nullptr, T, active_n, active_e, active_off, sorted, act_hi, act_lo,
+                                  ash_hi, ash_lo, reinterpret_cast<float *>(ws + lay.sh_part),
                                   reinterpret_cast<int2 *>(ws + lay.tiles_gu),
                                   reinterpret_cast<int2 *>(ws + lay.tiles_dn),
                                   reinterpret_cast<int32_t *>(ws + lay.light),
-                                  reinterpret_cast<int32_t *>(ws + lay.tile_n), ys, s, prof);
+                                  reinterpret_cast<int32_t *>(ws + lay.tile_n), ys, nullptr, s, prof);
     if (e != hipSuccess) return e;
     {
         StageMark m(prof, K3MOE_STAGE_COMBINE, s);
-        const int64_t n4 = (int64_t)T * L.H / 4;
-        k_combine<<<(unsigned)((n4 + kCombineThreads - 1) / kCombineThreads), kCombineThreads, 0, s>>>(
-            ys, w, idx, T, L.K, L.H, L.E, L.Is > 0, out, L.errors);
+        launch_combine(L, ys, w, idx, T, L.H, L.Is > 0, out, s);
     }
     return hipGetLastError();
 }

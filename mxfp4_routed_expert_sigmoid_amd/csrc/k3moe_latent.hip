@@ -1,0 +1,281 @@
+// The latent layer's own steps (the "kimi-k3-in-c" README, §9 "Picking 16
+// experts of 896", k3_moe steps 2, 4 and 5; §5 "Kernels with a floating point
+// contract", k3_rmsnorm): the bf16 down-projection of x into the experts'
+// latent, the RMSNorm of the routed aggregate, the bf16 up-projection back to
+// the hidden width. The routing, the experts, the shared expert and the
+// router-order sum are the flat layer's kernels.
+#include <algorithm>
+
+#include "k3moe_internal.h"
+
+namespace k3moe {
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ float bf16f(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ uint16_t bf16_rne(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ bf8 as_bf8(u4 v)
+{
+    bf8 r;
+    __builtin_memcpy(&r, &v, 16);
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Projection with bf16 weights W [R][Kd] of NP token planes [T][Kd] (bf16; two
+// planes carry the hi and lo of an fp32 input and go into one accumulator):
+// part[s][t][r] = sum over K slice s of W[r][k] * (sum of the planes)[t][k].
+// Block: 4 waves x 16 rows, 64 tokens, one K slice (grid z) walked in chunks
+// of 128; each lane's weight fragment comes from HBM into registers once per
+// chunk (one chunk ahead), the tokens through double-buffered LDS. Slices
+// give small batches enough blocks to stream the weights at full width; their
+// fp32 sums are added in slice order by k_proj_finish.
+//
+// K mapping: lane group g (lanes 16g..16g+15) holds K = 128c + 32st + 8g +
+// [0, 8) of MFMA step st of chunk c on both sides (v_mfma_f32_16x16x32_bf16:
+// lane l holds A row l % 16 and B column l % 16).
+constexpr int kPjRows = 64;    // rows per block (4 waves x 16)
+constexpr int kPjTok = 64;     // tokens per block
+constexpr int kPjKC = 128;     // K per chunk
+constexpr int kPjPad = 16;     // LDS bytes after each token row
+constexpr int kPjRow = kPjKC * 2 + kPjPad;
+
+__host__ __device__ constexpr int proj_lds_bytes(int np) { return 2 * np * kPjTok * kPjRow; }
+
+template <int NP>
+__global__ __launch_bounds__(256) void k_proj(const uint16_t *__restrict__ W, const uint16_t *__restrict__ p0,
+                                              const uint16_t *__restrict__ p1, int T, int R, int Kd, int kspan,
+                                              float *__restrict__ part)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+    const int r0 = blockIdx.x * kPjRows + wave * 16, t0 = blockIdx.y * kPjTok;
+    const int k0 = blockIdx.z * kspan, k1 = min(Kd, k0 + kspan);
+    const int NCH = (k1 - k0) / kPjKC;
+    const uint8_t *wrow = reinterpret_cast<const uint8_t *>(W) + ((size_t)min(r0 + l16, R - 1) * Kd + k0) * 2 + 16 * g;
+    const uint8_t *pp[2] = {reinterpret_cast<const uint8_t *>(p0), reinterpret_cast<const uint8_t *>(p1)};
+
+    // token staging: thread -> (plane, token, 16-byte segment) of a chunk
+    constexpr int SEG = kPjKC * 2 / 16;                         // 16 per token row
+    constexpr int NB = NP * kPjTok * SEG / 256;                 // u4 per thread
+    u4 xs[NB];
+    auto bload = [&](int c) {
+        const int cc = min(c, NCH - 1);
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            const int v = tid + 256 * q;
+            const int pl = v / (kPjTok * SEG), vv = v - pl * (kPjTok * SEG);
+            const int col = vv / SEG, seg = vv - col * SEG;
+            const int t = min(t0 + col, T - 1);
+            xs[q] = *reinterpret_cast<const u4 *>(pp[pl] + ((size_t)t * Kd + k0 + cc * kPjKC) * 2 + 16 * seg);
+        }
+    };
+    auto bstore = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            const int v = tid + 256 * q;
+            const int pl = v / (kPjTok * SEG), vv = v - pl * (kPjTok * SEG);
+            const int col = vv / SEG, seg = vv - col * SEG;
+            *reinterpret_cast<u4 *>(lds + ((buf * NP + pl) * kPjTok + col) * kPjRow + 16 * seg) = xs[q];
+        }
+    };
+    struct Chunk {
+        u4 a[4];
+    };
+    auto aload = [&](int c, Chunk &b) {
+        const int cc = min(c, NCH - 1);
+#pragma unroll
+        for (int st = 0; st < 4; ++st) b.a[st] = *reinterpret_cast<const u4 *>(wrow + (cc * kPjKC + 32 * st) * 2);
+    };
+    v4f acc[4];
+#pragma unroll
+    for (int tf = 0; tf < 4; ++tf) acc[tf] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    auto compute = [&](const Chunk &b, int buf) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const bf8 a = as_bf8(b.a[st]);
+#pragma unroll
+            for (int tf = 0; tf < 4; ++tf)
+#pragma unroll
+                for (int pl = 0; pl < NP; ++pl) {
+                    const bf8 bv = as_bf8(*reinterpret_cast<const u4 *>(
+                        lds + ((buf * NP + pl) * kPjTok + 16 * tf + l16) * kPjRow + (32 * st + 8 * g) * 2));
+                    acc[tf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, acc[tf], 0, 0, 0);
+                }
+        }
+    };
+
+    if (NCH > 0) {
+        Chunk c0, c1;
+        bload(0);
+        aload(0, c0);
+        bstore(0);
+        __syncthreads();
+        for (int c = 0; c < NCH; c += 2) {
+            bload(c + 1);
+            aload(c + 1, c1);
+            compute(c0, 0);
+            bstore(1);
+            __syncthreads();
+            if (c + 1 >= NCH) break;
+            bload(c + 2);
+            aload(c + 2, c0);
+            compute(c1, 1);
+            bstore(0);
+            __syncthreads();
+        }
+    }
+    // lane holds rows 4g + i of token column 16 tf + l16
+    if (r0 >= R) return;
+    float *ps = part + (size_t)blockIdx.z * T * R;
+#pragma unroll
+    for (int tf = 0; tf < 4; ++tf) {
+        const int t = t0 + 16 * tf + l16;
+        if (t < T)
+            *reinterpret_cast<float4 *>(ps + (size_t)t * R + r0 + 4 * g) =
+                float4{acc[tf][0], acc[tf][1], acc[tf][2], acc[tf][3]};
+    }
+}
+
+// Slices added in order (+ addend): fp32 out [T][R], or bf16 hi/lo planes.
+__global__ __launch_bounds__(256) void k_proj_finish(const float *__restrict__ part, int S, int T, int R,
+                                                     const float *__restrict__ addend, float *__restrict__ out,
+                                                     uint16_t *__restrict__ hi, uint16_t *__restrict__ lo)
+{
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x, n = (int64_t)T * R;
+    if (i >= n) return;
+    float v = part[i];
+    for (int s = 1; s < S; ++s) v += part[(size_t)s * n + i];
+    if (addend) v += addend[i];
+    if (out) {
+        out[i] = v;
+    } else {
+        const uint16_t h = bf16_rne(v);
+        hi[i] = h;
+        lo[i] = bf16_rne(v - bf16f(h));
+    }
+}
+
+// RMSNorm of the routed aggregate (k3_rmsnorm: sum of squares in fp64,
+// epsilon inside the root, x * inv * gamma in fp32), then bf16 hi and lo
+// planes for the up-projection. One block per token.
+template <bool NORM>
+__global__ __launch_bounds__(256) void k_rms_split(const float *__restrict__ acc, int L, const float *__restrict__ gamma,
+                                                   float eps, uint16_t *__restrict__ hi, uint16_t *__restrict__ lo)
+{
+    __shared__ double red[4];
+    __shared__ float inv_sh;
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const float *a = acc + (size_t)t * L;
+    float inv = 1.0f;
+    if constexpr (NORM) {
+        double ss = 0.0;
+        for (int l = tid; l < L; l += 256) ss = fma((double)a[l], (double)a[l], ss);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+        if ((tid & 63) == 0) red[tid >> 6] = ss;
+        __syncthreads();
+        if (tid == 0) inv_sh = (float)(1.0 / sqrt((red[0] + red[1] + red[2] + red[3]) / (double)L + (double)eps));
+        __syncthreads();
+        inv = inv_sh;
+    }
+    for (int l = tid; l < L; l += 256) {
+        const float v = NORM ? a[l] * inv * gamma[l] : a[l];
+        const uint16_t h = bf16_rne(v);
+        hi[(size_t)t * L + l] = h;
+        lo[(size_t)t * L + l] = bf16_rne(v - bf16f(h));
+    }
+}
+
+// out = W (planes) as fp32 [T][R] (+ addend), or as bf16 hi/lo planes.
+static hipError_t launch_proj(const uint16_t *W, const uint16_t *p0, const uint16_t *p1, int T, int R, int Kd,
+                              float *part, const float *addend, float *out, uint16_t *hi, uint16_t *lo, hipStream_t s)
+{
+    static const bool lds_set = [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_proj<1>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, proj_lds_bytes(1));
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_proj<2>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, proj_lds_bytes(2));
+        return true;
+    }();
+    (void)lds_set;
+    const int S = proj_splits(T, R, Kd);
+    const int kspan = (Kd / kPjKC + S - 1) / S * kPjKC;
+    const dim3 grid((unsigned)((R + kPjRows - 1) / kPjRows), (unsigned)((T + kPjTok - 1) / kPjTok), (unsigned)S);
+    if (p1)
+        k_proj<2><<<grid, 256, proj_lds_bytes(2), s>>>(W, p0, p1, T, R, Kd, kspan, part);
+    else
+        k_proj<1><<<grid, 256, proj_lds_bytes(1), s>>>(W, p0, nullptr, T, R, Kd, kspan, part);
+    const int64_t n = (int64_t)T * R;
+    k_proj_finish<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, S, T, R, addend, out, hi, lo);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// K slices of a projection: enough blocks for about 1024 on the chip, each
+// slice at least 512 wide, and no empty slice.
+int proj_splits(int64_t T, int R, int Kd)
+{
+    const int64_t blocks = (int64_t)((R + kPjRows - 1) / kPjRows) * ((T + kPjTok - 1) / kPjTok);
+    const int64_t want = (1024 + blocks - 1) / blocks;
+    const int64_t S = std::max<int64_t>(1, std::min<int64_t>(want, Kd / 512));
+    const int kspan = (int)((Kd / kPjKC + S - 1) / S * kPjKC);
+    return (Kd + kspan - 1) / kspan;
+}
+
+hipError_t launch_latent_forward(const LayerView &L, const uint16_t *x, int T, const int32_t *idx,
+                                 const float *w, float *out, char *ws, const WsLayout &lay, hipStream_t s,
+                                 Profiler *prof)
+{
+    const int Lt = L.Lt;
+    uint16_t *zh = reinterpret_cast<uint16_t *>(ws + lay.lat_z), *zl = zh + (size_t)T * Lt;
+    float *acc = reinterpret_cast<float *>(ws + lay.lat_acc);
+    uint16_t *nh = reinterpret_cast<uint16_t *>(ws + lay.lat_n), *nl = nh + (size_t)T * Lt;
+    float *ysh = L.Is > 0 ? reinterpret_cast<float *>(ws + lay.lat_ysh) : nullptr;
+    float *part = reinterpret_cast<float *>(ws + lay.lat_part);
+    float *ys = reinterpret_cast<float *>(ws + lay.ys);
+    hipError_t e;
+    {
+        StageMark m(prof, K3MOE_STAGE_LATENT_IN, s);  // z = Wd x, as bf16 hi and lo
+        if ((e = launch_proj(L.lat_down, x, nullptr, T, Lt, L.H, part, nullptr, nullptr, zh, zl, s)) != hipSuccess)
+            return e;
+    }
+    launch_perm(L, idx, T, ws, lay, s, prof);
+    uint16_t *act_hi = reinterpret_cast<uint16_t *>(ws + lay.act);
+    uint16_t *act_lo = act_hi + (size_t)T * L.K * L.I;
+    uint16_t *ash_hi = reinterpret_cast<uint16_t *>(ws + lay.ash);
+    uint16_t *ash_lo = ash_hi + (size_t)T * L.Is;
+    e = launch_grouped(L, x, zh, zl, T, reinterpret_cast<int32_t *>(ws + lay.active_n),
+                       reinterpret_cast<int32_t *>(ws + lay.active_e), reinterpret_cast<int32_t *>(ws + lay.active_off),
+                       reinterpret_cast<int32_t *>(ws + lay.sorted), act_hi, act_lo, ash_hi, ash_lo,
+                       reinterpret_cast<float *>(ws + lay.sh_part), reinterpret_cast<int2 *>(ws + lay.tiles_gu),
+                       reinterpret_cast<int2 *>(ws + lay.tiles_dn), reinterpret_cast<int32_t *>(ws + lay.light),
+                       reinterpret_cast<int32_t *>(ws + lay.tile_n), ys, ysh, s, prof);
+    if (e != hipSuccess) return e;
+    {
+        StageMark m(prof, K3MOE_STAGE_COMBINE, s);  // the routed aggregate [T][L], router order
+        launch_combine(L, ys, w, idx, T, Lt, false, acc, s);
+    }
+    {
+        StageMark m(prof, K3MOE_STAGE_LATENT_OUT, s);  // norm, then out = Wu acc (+ shared)
+        if (L.lat_norm_on)
+            k_rms_split<true><<<(unsigned)T, 256, 0, s>>>(acc, Lt, L.lat_norm, L.lat_eps, nh, nl);
+        else
+            k_rms_split<false><<<(unsigned)T, 256, 0, s>>>(acc, Lt, nullptr, 0.0f, nh, nl);
+        if ((e = launch_proj(L.lat_up, nh, nl, T, L.H, Lt, part, ysh, out, nullptr, nullptr, s)) != hipSuccess)
+            return e;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace k3moe

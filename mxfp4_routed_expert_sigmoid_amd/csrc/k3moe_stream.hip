@@ -97,7 +97,9 @@ struct GuStreamParams {
     const uint8_t *gp, *gs, *up, *us;
     int64_t g_sp, g_ss, u_sp, u_ss;
     const uint16_t *sh_gate, *sh_up;
-    const uint16_t *x;
+    const uint16_t *x;        // tokens of the shared expert, bf16 [T][H]
+    const uint16_t *xr, *xr_lo;  // tokens of the routed experts, bf16 [T][Kr]; xr_lo: a second plane or null
+    int Kr;                   // routed experts' width (H, or the latent)
     const int32_t *active_e, *active_off, *sorted;
     const int32_t *light, *light_n;
     int sh_blocks;            // leading blocks that run the shared expert
@@ -106,25 +108,28 @@ struct GuStreamParams {
     uint16_t *act_hi, *act_lo, *ash_hi, *ash_lo;
 };
 
-constexpr int gu_stream_lds_bytes() { return 2 * kSTok * brow_bytes<true>() + kSTok * 4; }
+// np: token planes (1, or 2 when the routed tokens come as bf16 hi and lo)
+constexpr int gu_stream_lds_bytes(int np) { return 2 * np * kSTok * brow_bytes<true>() + kSTok * 4; }
 
 // The wave's part of one block: gate and up rows row0 + 16 rf + l16 (rf = 0, 1)
 // of an item with token rows tok_l[0..15] (clamped to the item's tokens),
-// over the K groups [g0, g1). part == null: the activation goes to ohi/olo
-// rows orow0 + column; else the fp32 gate and up sums go to
-// part[(orow0 + column) * 2 + {0, 1}][row] (a slice's partials).
-template <bool FP4>
+// over the K groups [g0, g1). The tokens are NP bf16 planes of width KW
+// (xp[0], xp[1]: hi and lo of an fp32 input, multiplied into one
+// accumulator). part == null: the activation goes to ohi/olo rows orow0 +
+// column; else the fp32 gate and up sums go to part[(orow0 + column) * 2 +
+// {0, 1}][row] (a slice's partials).
+template <bool FP4, int NP>
 __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const uint8_t *wg, const uint8_t *wu,
                                                 const uint8_t *sg, const uint8_t *su, int rows, int row0,
                                                 const int *tok_l, int n, uint8_t *B_l, uint16_t *ohi,
                                                 uint16_t *olo, int64_t orow0, int ostride, int g0, int g1,
-                                                float *part)
+                                                float *part, const uint16_t *x0, const uint16_t *x1, int KW)
 {
     constexpr int GK = group_k<FP4>();
     constexpr int BROW = brow_bytes<FP4>();
     constexpr int BU4 = GK * 2 / 16;                           // u4 per token row per group
-    constexpr int NB = (kSTok * BU4 + 64 * kSWaves - 1) / (64 * kSWaves);  // staging u4 per thread
-    const int H = p.H, tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+    constexpr int NB = (kSTok * BU4 + 64 * kSWaves - 1) / (64 * kSWaves);  // staging u4 per thread and plane
+    const int H = KW, tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const size_t rowb = FP4 ? (size_t)H / 2 : (size_t)H * 2;
     const uint8_t *wr[2][2];
     const uint8_t *sr[2][2] = {{nullptr, nullptr}, {nullptr, nullptr}};
@@ -138,7 +143,7 @@ __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const u
             sr[1][rf] = su + (size_t)r * (H / 32);
         }
     }
-    const uint8_t *xb = reinterpret_cast<const uint8_t *>(p.x);
+    const uint8_t *xb[2] = {reinterpret_cast<const uint8_t *>(x0), reinterpret_cast<const uint8_t *>(x1)};
 
     struct Grp {
         u4 a[2][2][kSChunks];  // [mat][rf][chunk]
@@ -156,25 +161,30 @@ __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const u
                 if constexpr (FP4) b.s[m][rf] = *reinterpret_cast<const u4 *>(sr[m][rf] + 16 * gc);
             }
     };
-    u4 xs[NB];
+    u4 xs[NP][NB];
     auto xload = [&](int gi) {
         const int gc = min(gi, g1 - 1);
 #pragma unroll
-        for (int q = 0; q < NB; ++q) {
-            const int v = min(tid + 64 * kSWaves * q, kSTok * BU4 - 1);
-            const int col = v / BU4, seg = v - col * BU4;
-            xs[q] = *reinterpret_cast<const u4 *>(xb + ((size_t)tok_l[col] * H + (size_t)gc * GK) * 2 + 16 * seg);
-        }
+        for (int pl = 0; pl < NP; ++pl)
+#pragma unroll
+            for (int q = 0; q < NB; ++q) {
+                const int v = min(tid + 64 * kSWaves * q, kSTok * BU4 - 1);
+                const int col = v / BU4, seg = v - col * BU4;
+                xs[pl][q] = *reinterpret_cast<const u4 *>(xb[pl] + ((size_t)tok_l[col] * H + (size_t)gc * GK) * 2 +
+                                                           16 * seg);
+            }
     };
     auto xstore = [&](int buf) {
 #pragma unroll
-        for (int q = 0; q < NB; ++q) {
-            const int v = tid + 64 * kSWaves * q;
-            if (v < kSTok * BU4) {
-                const int col = v / BU4, seg = v - col * BU4;
-                *reinterpret_cast<u4 *>(B_l + (buf * kSTok + col) * BROW + 16 * seg) = xs[q];
+        for (int pl = 0; pl < NP; ++pl)
+#pragma unroll
+            for (int q = 0; q < NB; ++q) {
+                const int v = tid + 64 * kSWaves * q;
+                if (v < kSTok * BU4) {
+                    const int col = v / BU4, seg = v - col * BU4;
+                    *reinterpret_cast<u4 *>(B_l + ((buf * NP + pl) * kSTok + col) * BROW + 16 * seg) = xs[pl][q];
+                }
             }
-        }
     };
 
     v4f acc[2][2];
@@ -184,7 +194,7 @@ __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const u
         for (int rf = 0; rf < 2; ++rf) acc[m][rf] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
     auto compute = [&](const Grp &b, int buf) {
-        const uint8_t *Bb = B_l + (buf * kSTok + l16) * BROW;
+        const uint8_t *Bb = B_l + (buf * NP * kSTok + l16) * BROW;
 #pragma unroll
         for (int c = 0; c < kSChunks; ++c) {
             float sc[2][2];
@@ -198,7 +208,10 @@ __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const u
 #pragma unroll
             for (int st = 0; st < SPC; ++st) {
                 const int kb = FP4 ? (128 * c + 32 * g + 8 * st) : (32 * c + 8 * g);
-                const bf8 bv = as_bf8(*reinterpret_cast<const u4 *>(Bb + 2 * kb));
+                bf8 bv[NP];
+#pragma unroll
+                for (int pl = 0; pl < NP; ++pl)
+                    bv[pl] = as_bf8(*reinterpret_cast<const u4 *>(Bb + pl * kSTok * BROW + 2 * kb));
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -208,7 +221,8 @@ __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const u
                             a = dequant8(b.a[m][rf][c][st], sc[m][rf]);
                         else
                             a = as_bf8(b.a[m][rf][c]);
-                        acc[m][rf] = mfma_bf16(a, bv, acc[m][rf]);
+#pragma unroll
+                        for (int pl = 0; pl < NP; ++pl) acc[m][rf] = mfma_bf16(a, bv[pl], acc[m][rf]);
                     }
             }
         }
@@ -288,11 +302,11 @@ __global__ __launch_bounds__(64 * kSWaves) void k_gu_stream(GuStreamParams p)
         const int NG = p.H / group_k<false>();
         if (threadIdx.x < kSTok) tok_l[threadIdx.x] = t0 + min((int)threadIdx.x, n - 1);
         __syncthreads();
-        gu_stream_block<false>(p, reinterpret_cast<const uint8_t *>(p.sh_gate),
-                               reinterpret_cast<const uint8_t *>(p.sh_up), nullptr, nullptr, p.Is,
-                               rb * kSBlkRows + wave * kSRows, tok_l, n, B_l, p.ash_hi, p.ash_lo, t0, p.Is,
-                               NG * ks / S, NG * (ks + 1) / S,
-                               S > 1 ? p.sh_part + (size_t)ks * p.T * 2 * p.Is : nullptr);
+        gu_stream_block<false, 1>(p, reinterpret_cast<const uint8_t *>(p.sh_gate),
+                                  reinterpret_cast<const uint8_t *>(p.sh_up), nullptr, nullptr, p.Is,
+                                  rb * kSBlkRows + wave * kSRows, tok_l, n, B_l, p.ash_hi, p.ash_lo, t0, p.Is,
+                                  NG * ks / S, NG * (ks + 1) / S,
+                                  S > 1 ? p.sh_part + (size_t)ks * p.T * 2 * p.Is : nullptr, p.x, nullptr, p.H);
         return;
     }
     b -= p.sh_blocks;
@@ -303,9 +317,14 @@ __global__ __launch_bounds__(64 * kSWaves) void k_gu_stream(GuStreamParams p)
     const int off = p.active_off[q], n = p.active_off[q + 1] - off;
     if (threadIdx.x < kSTok) tok_l[threadIdx.x] = p.sorted[off + min((int)threadIdx.x, n - 1)] / p.K;
     __syncthreads();
-    gu_stream_block<true>(p, p.gp + e * p.g_sp, p.up + e * p.u_sp, p.gs + e * p.g_ss, p.us + e * p.u_ss, p.I,
-                          rb * kSBlkRows + wave * kSRows, tok_l, n, B_l, p.act_hi, p.act_lo, off, p.I, 0,
-                          p.H / group_k<true>(), nullptr);
+    if (p.xr_lo)
+        gu_stream_block<true, 2>(p, p.gp + e * p.g_sp, p.up + e * p.u_sp, p.gs + e * p.g_ss, p.us + e * p.u_ss,
+                                 p.I, rb * kSBlkRows + wave * kSRows, tok_l, n, B_l, p.act_hi, p.act_lo, off, p.I,
+                                 0, p.Kr / group_k<true>(), nullptr, p.xr, p.xr_lo, p.Kr);
+    else
+        gu_stream_block<true, 1>(p, p.gp + e * p.g_sp, p.up + e * p.u_sp, p.gs + e * p.g_ss, p.us + e * p.u_ss,
+                                 p.I, rb * kSBlkRows + wave * kSRows, tok_l, n, B_l, p.act_hi, p.act_lo, off, p.I,
+                                 0, p.Kr / group_k<true>(), nullptr, p.xr, nullptr, p.Kr);
 }
 
 // Shared expert's slices -> activation: g and u summed over the slices in
@@ -343,6 +362,8 @@ constexpr int kDBlkRows = kDWaves * kSRows;  // 256
 
 struct DnStreamParams {
     int H, I, K, T, Is;
+    int Hr;                   // routed experts' output rows (H, or the latent)
+    float *ysh;               // shared expert's output fp32 [T][H]; null: ys slot K
     const uint8_t *dp, *ds;
     int64_t d_sp, d_ss;
     const uint16_t *sh_down;
@@ -359,11 +380,12 @@ __host__ __device__ constexpr int dn_stream_lds_bytes(int KD) { return 2 * kSTok
 template <bool FP4>
 __device__ __forceinline__ void dn_stream_run(const DnStreamParams &p, const uint8_t *wd, const uint8_t *sd, int KD,
                                               int rb0, int rb1, const int *arow_l, const int *orow_l, int n,
-                                              const uint16_t *ahi, const uint16_t *alo, uint8_t *B_l)
+                                              const uint16_t *ahi, const uint16_t *alo, uint8_t *B_l, int R,
+                                              float *yout)
 {
     constexpr int GK = group_k<FP4>();
     const int BROW = 2 * KD + kSPad;
-    const int H = p.H, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+    const int H = R, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
     const int NG = KD / GK, total = (rb1 - rb0) * NG;
     const size_t rowb = FP4 ? (size_t)KD / 2 : (size_t)KD * 2;
 
@@ -430,7 +452,7 @@ __device__ __forceinline__ void dn_stream_run(const DnStreamParams &p, const uin
         }
         if (gi == NG - 1) {  // row block done: lane holds rows 4g + i of token column l16
             if (l16 < n) {
-                float *yr = p.ys + (size_t)orow_l[l16] * H;
+                float *yr = yout + (size_t)orow_l[l16] * H;
 #pragma unroll
                 for (int rf = 0; rf < 2; ++rf) {
                     const int row = rb * kDBlkRows + wave * kSRows + 16 * rf + 4 * g;
@@ -459,8 +481,9 @@ __global__ __launch_bounds__(64 * kDWaves) void k_dn_stream(DnStreamParams p)
     int *arow_l = reinterpret_cast<int *>(lds);
     int *orow_l = arow_l + kSTok;
     uint8_t *B_l = lds + kSTok * 8;
-    const int RBT = (p.H + kDBlkRows - 1) / kDBlkRows;
     const int item = blockIdx.x / p.runs, run = blockIdx.x - item * p.runs;
+    const int R = item < p.sh_items ? p.H : p.Hr;  // output rows of this item
+    const int RBT = (R + kDBlkRows - 1) / kDBlkRows;
     const int rb0 = run * p.run_rb, rb1 = min(RBT, rb0 + p.run_rb);
     if (rb0 >= rb1) return;
     if (item < p.sh_items) {  // shared expert, token group `item`
@@ -468,11 +491,11 @@ __global__ __launch_bounds__(64 * kDWaves) void k_dn_stream(DnStreamParams p)
         if (threadIdx.x < kSTok) {
             const int t = t0 + min((int)threadIdx.x, n - 1);
             arow_l[threadIdx.x] = t;
-            orow_l[threadIdx.x] = t * (p.K + 1) + p.K;
+            orow_l[threadIdx.x] = p.ysh ? t : t * (p.K + 1) + p.K;
         }
         __syncthreads();
         dn_stream_run<false>(p, reinterpret_cast<const uint8_t *>(p.sh_down), nullptr, p.Is, rb0, rb1, arow_l,
-                             orow_l, n, p.ash_hi, p.ash_lo, B_l);
+                             orow_l, n, p.ash_hi, p.ash_lo, B_l, p.H, p.ysh ? p.ysh : p.ys);
         return;
     }
     const int li = item - p.sh_items;
@@ -487,15 +510,15 @@ __global__ __launch_bounds__(64 * kDWaves) void k_dn_stream(DnStreamParams p)
     }
     __syncthreads();
     dn_stream_run<true>(p, p.dp + e * p.d_sp, p.ds + e * p.d_ss, p.I, rb0, rb1, arow_l, orow_l, n, p.act_hi,
-                        p.act_lo, B_l);
+                        p.act_lo, B_l, p.Hr, p.ys);
 }
 
 }  // namespace
 
 bool stream_path_ok(const LayerView &L)
 {
-    return L.H % group_k<true>() == 0 && L.I % group_k<true>() == 0 && L.I % kSBlkRows == 0 &&
-           L.H % kSBlkRows == 0 && L.Is % kSBlkRows == 0;
+    return L.H % group_k<true>() == 0 && L.EK % group_k<true>() == 0 && L.I % group_k<true>() == 0 &&
+           L.I % kSBlkRows == 0 && L.H % kSBlkRows == 0 && L.EK % kSBlkRows == 0 && L.Is % kSBlkRows == 0;
 }
 
 // The down kernel stages a whole item's activations: it takes the routed
@@ -515,11 +538,17 @@ bool stream_shared_ok(const LayerView &L, int T) { return L.Is > 0 && T <= 8 * k
 // outlast the routed experts' blocks.
 int stream_shared_slices(int T) { return T <= 2 * kSTok ? 8 : 1; }
 
-hipError_t launch_stream_gu(const LayerView &L, const uint16_t *x, int T, const int32_t *active_e,
-                            const int32_t *active_off, const int32_t *sorted, const int32_t *light,
-                            const int32_t *light_n, bool with_shared, uint16_t *act_hi, uint16_t *act_lo,
-                            uint16_t *ash_hi, uint16_t *ash_lo, float *sh_part, hipStream_t s)
+hipError_t launch_stream_gu(const LayerView &L, const uint16_t *x, const uint16_t *xr, const uint16_t *xr_lo,
+                            int T, const int32_t *active_e, const int32_t *active_off, const int32_t *sorted,
+                            const int32_t *light, const int32_t *light_n, bool with_shared, uint16_t *act_hi,
+                            uint16_t *act_lo, uint16_t *ash_hi, uint16_t *ash_lo, float *sh_part, hipStream_t s)
 {
+    static const bool lds_set = [] {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gu_stream),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, gu_stream_lds_bytes(2));
+        return true;
+    }();
+    (void)lds_set;
     GuStreamParams p{};
     p.H = L.H;
     p.I = L.I;
@@ -540,6 +569,9 @@ hipError_t launch_stream_gu(const LayerView &L, const uint16_t *x, int T, const 
     p.sh_gate = L.sh_gate;
     p.sh_up = L.sh_up;
     p.x = x;
+    p.xr = xr;
+    p.xr_lo = xr_lo;
+    p.Kr = L.EK;
     p.active_e = active_e;
     p.active_off = active_off;
     p.sorted = sorted;
@@ -554,7 +586,7 @@ hipError_t launch_stream_gu(const LayerView &L, const uint16_t *x, int T, const 
     p.ash_lo = ash_lo;
     const int64_t cap = std::min<int64_t>(L.E, (int64_t)T * L.K);
     const unsigned nblk = (unsigned)(p.sh_blocks + cap * (L.I / kSBlkRows));
-    k_gu_stream<<<nblk, 64 * kSWaves, gu_stream_lds_bytes(), s>>>(p);
+    k_gu_stream<<<nblk, 64 * kSWaves, gu_stream_lds_bytes(xr_lo ? 2 : 1), s>>>(p);
     if (with_shared && p.sh_slices > 1) {
         const int64_t n = (int64_t)T * L.Is;
         k_sh_act<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(sh_part, p.sh_slices, T, L.Is, L.act, L.b1, L.b2,
@@ -566,7 +598,7 @@ hipError_t launch_stream_gu(const LayerView &L, const uint16_t *x, int T, const 
 hipError_t launch_stream_dn(const LayerView &L, int T, const int32_t *active_e, const int32_t *active_off,
                             const int32_t *sorted, const int32_t *light, const int32_t *light_n,
                             bool with_shared, const uint16_t *act_hi, const uint16_t *act_lo,
-                            const uint16_t *ash_hi, const uint16_t *ash_lo, float *ys, hipStream_t s)
+                            const uint16_t *ash_hi, const uint16_t *ash_lo, float *ys, float *ysh, hipStream_t s)
 {
     static const bool lds_set = [] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_dn_stream),
@@ -576,6 +608,8 @@ hipError_t launch_stream_dn(const LayerView &L, int T, const int32_t *active_e, 
     (void)lds_set;
     DnStreamParams p{};
     p.H = L.H;
+    p.Hr = L.EK;
+    p.ysh = ysh;
     p.I = L.I;
     p.K = L.K;
     p.T = T;
@@ -598,7 +632,7 @@ hipError_t launch_stream_dn(const LayerView &L, int T, const int32_t *active_e, 
     // each item's rows in `runs` blocks of run_rb 256-row blocks: about 7 row
     // blocks per run, fewer when there are few items (about 512 blocks)
     const int64_t cap = std::min<int64_t>(L.E, (int64_t)T * L.K);
-    const int rbt = (L.H + kDBlkRows - 1) / kDBlkRows;
+    const int rbt = (std::max(L.H, L.EK) + kDBlkRows - 1) / kDBlkRows;
     const int64_t items = p.sh_items + cap;
     const int want = (int)std::max<int64_t>((rbt + 6) / 7, (512 + items - 1) / items);
     p.run_rb = (rbt + std::min(want, rbt) - 1) / std::min(want, rbt);

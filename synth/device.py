@@ -96,9 +96,12 @@ def layer_tensors(spec: synth.LayerSpec, layer: int = 0, device="cuda"):
 def make_layer(spec: synth.LayerSpec, tensors):
     """A library Layer over the tensors of ``layer_tensors``."""
     import mxfp4_routed_expert_sigmoid_amd as k3
+    lat = spec.latent > 0
     cfg = k3.make_config(spec.hidden, spec.inter, spec.n_experts, spec.topk, spec.shared_inter,
-                         spec.renorm, spec.routed_scale, spec.act, spec.situ_b1, spec.situ_b2)
+                         spec.renorm, spec.routed_scale, spec.act, spec.situ_b1, spec.situ_b2,
+                         spec.latent, spec.latent_norm if lat else 0, spec.rms_eps if lat else 0.0)
     t = tensors
     return k3.Layer(cfg, t["router_w"], t["router_bias"], t["gate_packed"], t["gate_scales"],
                     t["up_packed"], t["up_scales"], t["down_packed"], t["down_scales"],
-                    t["sh_gate"], t["sh_up"], t["sh_down"])
+                    t["sh_gate"], t["sh_up"], t["sh_down"], t.get("lat_down"), t.get("lat_up"),
+                    t.get("lat_norm") if lat and spec.latent_norm else None)

@@ -12,7 +12,9 @@ import synth
 CH_DELTA = 2.0 ** -20
 
 # Max relative error of an output element, |gpu - oracle| / D, where D is the
-# oracle's magnitude sum sum_j |w_j| sum_n |W2[o][n] a_j[n]| + shared terms.
+# oracle's magnitude sum sum_j |w_j| sum_n |W2[o][n] a_j[n]| + shared terms
+# (a latent layer: the same magnitude carried through the norm and the
+# up-projection).
 REL_TOL = 1e-4
 
 
@@ -64,6 +66,11 @@ def oracle_forward(spec, x, idx, w, layer=0, tokens=None):
     es = oracle.ExpertSet(used, spec.n_experts, h["gate_packed"], h["gate_scales"],
                           h["up_packed"], h["up_scales"], h["down_packed"], h["down_scales"])
     shared = synth.make_shared(spec, layer)
+    if spec.latent:
+        wd, wu, gamma = synth.make_latent(spec, layer)
+        return oracle.forward_latent(xs, ids, ws, es, spec.hidden, spec.latent, spec.inter, wd, wu,
+                                     norm=bool(spec.latent_norm), gamma=gamma, eps=spec.rms_eps,
+                                     shared=shared, act_kind=spec.act, b1=spec.situ_b1, b2=spec.situ_b2)
     out, denom, drops = oracle.forward(xs, ids, ws, es, spec.hidden, spec.inter, shared=shared,
                                        act_kind=spec.act, b1=spec.situ_b1, b2=spec.situ_b2)
     return out, denom, drops

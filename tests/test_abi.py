@@ -73,3 +73,35 @@ def test_weight_descriptor_refusals():
     assert _create(cfg, _weights(8, shared=True)) == 1   # shared pointers without shared_inter
     cfg2 = k3.make_config(256, 128, 8, 2, shared_inter=128)
     assert _create(cfg2, _weights(8)) == 1               # shared_inter without pointers
+
+
+@pytest.mark.parametrize("latent,norm,eps,status", [
+    (0, 1, 1e-5, 2),        # a flat layer has no latent norm
+    (-128, 0, 0.0, 2),
+    (128, 2, 1e-5, 2),      # norm flag 0 or 1
+    (128, 1, 0.0, 2),       # the norm needs a positive epsilon
+    (128, 1, float("inf"), 2),
+    (96, 0, 0.0, 3),        # latent a multiple of 128
+])
+def test_latent_config_refusals(latent, norm, eps, status):
+    cfg = k3.make_config(256, 128, 8, 2, latent=latent, latent_norm=norm, rms_eps=eps)
+    assert _create(cfg, _weights(8)) == status
+
+
+def test_latent_weight_refusals():
+    base = 0x20000000
+    lat = k3.make_config(256, 128, 8, 2, latent=128, latent_norm=1, rms_eps=1e-5)
+    w = _weights(8)                                   # latent layer without its projections
+    assert _create(lat, w) == 1
+    w.lat_down, w.lat_up = base, base + 0x100000      # norm on, no gamma
+    assert _create(lat, w) == 1
+    w.lat_norm = base + 0x200004                      # gamma not 16-byte aligned
+    assert _create(lat, w) == 4
+    flat = k3.make_config(256, 128, 8, 2)
+    w2 = _weights(8)
+    w2.lat_up = base                                  # projections on a flat layer
+    assert _create(flat, w2) == 1
+    nonorm = k3.make_config(256, 128, 8, 2, latent=128, latent_norm=0)
+    w3 = _weights(8)
+    w3.lat_down, w3.lat_up, w3.lat_norm = base, base + 0x100000, base + 0x200000
+    assert _create(nonorm, w3) == 1                   # gamma without the norm

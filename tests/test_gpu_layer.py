@@ -289,12 +289,15 @@ def test_pages_expert_shape(T, shared):
     assert rel_err(out, ref, denom) <= REL_TOL
 
 
-@pytest.mark.parametrize("T,inter", [(1, 2176), (1, 1664), (2, 2176)])
-def test_inter_widths_past_and_below_decode_staging(T, inter):
+@pytest.mark.parametrize("T,inter,hidden", [(1, 2176, 256), (1, 1664, 256), (2, 2176, 256), (1, 2560, 512)])
+def test_inter_widths_past_and_below_decode_staging(T, inter, hidden):
     # intermediate widths that are not multiples of 512, one past the
     # single-token down kernel's activation staging (2048 elements: such a
-    # layer takes the grouped path) and one within it
-    spec = synth.LayerSpec(hidden=256, inter=inter, n_experts=4, topk=2, shared_inter=128,
+    # layer takes the grouped path) and one within it; and 2560 at hidden
+    # 512, where one token takes the streaming kernels with the shared
+    # expert cut into hidden-dimension slices (their partials need room in
+    # the workspace at T = 1 too)
+    spec = synth.LayerSpec(hidden=hidden, inter=inter, n_experts=4, topk=2, shared_inter=128,
                            bias_std=0.05, seed=70 + inter)
     sd = _dev()
     layer = sd.make_layer(spec, sd.layer_tensors(spec, 0, DEV))
