@@ -12,6 +12,10 @@ shared expert of inter 1536, bias N(0, 0.01)):
   decode   T = 1 token per step (default; the metric's configuration)
   batched  T = 64, uniformly random routing
   prefill  T = 2048, Zipf(1.1)-skewed routing
+  latent   T = 1 on the pages' latent layer: hidden 7168, experts in a 3584
+           latent with inter 3072 (the same 17,547,264 B per expert), two
+           shared experts of 3072 (one of 6144) on x, bf16 down- and
+           up-projections, RMSNorm of the aggregate
 Steps rotate over a pool of token batches so consecutive steps select
 different experts (the 281 MB a decode step touches is not left in the
 256 MB last-level cache by the previous step).
@@ -53,7 +57,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", choices=("decode", "batched", "prefill"), default="decode")
+    ap.add_argument("--workload", choices=("decode", "batched", "prefill", "latent"), default="decode")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -74,9 +78,13 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     T, routing, pool = {"decode": (1, "normal", 64), "batched": (64, "normal", 8),
-                        "prefill": (2048, "zipf", 2)}[args.workload]
-    spec = synth.full_spec(seed=0, routing=routing)
+                        "prefill": (2048, "zipf", 2), "latent": (1, "normal", 64)}[args.workload]
+    if args.workload == "latent":
+        spec = synth.pages_latent_spec(seed=0, routing=routing)
+    else:
+        spec = synth.full_spec(seed=0, routing=routing)
     H, I, E, K, Is = spec.hidden, spec.inter, spec.n_experts, spec.topk, spec.shared_inter
+    Lt, EKw = spec.latent, spec.ek   # latent width (0: flat); width the experts run at
     log(f"[bench] building layer: {E} experts x {spec.expert_bytes} B resident")
     tens = sd.layer_tensors(spec, 0, dev)
     layer = sd.make_layer(spec, tens)
@@ -130,29 +138,35 @@ def main():
 
     # algorithmic bytes, averaged over the rotation actually timed
     nd = sum(distinct[i % pool] for i in range(args.steps)) / args.steps
-    gu = matrix_bytes(I, H)
-    dn = matrix_bytes(H, I)
+    gu = matrix_bytes(I, EKw)
+    dn = matrix_bytes(EKw, I)
     expert_b = 2 * gu + dn
     routed_bytes = nd * expert_b
     router_bytes = E * H * 2
     shared_bytes = 3 * Is * H * 2
+    proj_bytes = 2 * Lt * H * 2 + Lt * 4   # latent down- and up-projection, norm weights
     # per stage: weights read once, token side read, activations written/read
     # (4 B per element: fp32, or bf16 hi + lo), expert outputs staged in fp32
-    x_read = T * H * 2   # the bf16 tokens
+    x_read = T * H * 2 + (T * Lt * 4 if Lt else 0)   # the bf16 tokens (+ the latent's hi/lo planes)
     act_b = T * K * I * 4 + T * Is * 4
     shared_in_gateup = stages["shared_gateup"][1] == 0  # no separate shared gate/up launch
     stage_bytes = {
         "gateup": nd * 2 * gu + (2 * Is * H * 2 if shared_in_gateup else 0) + x_read + act_b,
-        "down": nd * dn + Is * H * 2 + act_b + T * (K + 1) * H * 4,
+        "down": nd * dn + Is * H * 2 + act_b + T * (K + 1) * EKw * 4 + (T * H * 4 if Lt else 0),
     }
+    if Lt:
+        stage_bytes["latent_in"] = Lt * H * 2 + T * H * 2 + T * Lt * 4
+        stage_bytes["latent_out"] = H * Lt * 2 + Lt * 4 + T * Lt * 12 + T * H * 8
     kernels = {"decode": {"gateup": "k_gateup_dec", "down": "k_down_dec"},
                "batched": {"gateup": "k_gu_stream", "down": "k_dn_stream"},
-               "prefill": {"gateup": "k_gu_gemm + k_gu_stream", "down": "k_dn_gemm + k_dn_stream"}}[args.workload]
+               "prefill": {"gateup": "k_gu_gemm + k_gu_stream", "down": "k_dn_gemm + k_dn_stream"},
+               "latent": {"gateup": "k_gu_stream", "down": "k_dn_stream", "latent_in": "k_proj",
+                          "latent_out": "k_proj + k_rms_split"}}[args.workload]
     dom = max(stage_bytes, key=lambda s: stage_us[s])
     achieved = stage_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9
     traffic = measured_traffic(kernels[dom])
     value = routed_bytes / (ms * 1e-3) / 1e9
-    layer_bytes = routed_bytes + router_bytes + shared_bytes + T * H * 2 + T * H * 4
+    layer_bytes = routed_bytes + router_bytes + shared_bytes + proj_bytes + T * H * 2 + T * H * 4
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -168,7 +182,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{args.workload}: T={T} tokens/step, hidden {H}, {E} experts top-{K}, "
-                        f"expert inter {I} (MXFP4), bf16 shared expert inter {Is}, sigmoid "
+                        + (f"experts in a {Lt} latent (bf16 down/up projections, RMSNorm of the "
+                           f"aggregate), " if Lt else "")
+                        + f"expert inter {I} (MXFP4), bf16 shared expert inter {Is}, sigmoid "
                         f"router + bias N(0,0.01), {routing} routing",
             "tokens_per_step": T,
             "distinct_experts_per_step": round(nd, 2),
@@ -226,6 +242,7 @@ def cpu_baseline(spec, xs_np, T, budget_s, expert_b):
     Wr = synth.make_router(spec)
     bias = synth.make_bias(spec)
     shared = synth.make_shared(spec)
+    lat = synth.make_latent(spec)
     spent = 0.0
     tokens = 0
     routed = 0
@@ -240,8 +257,15 @@ def cpu_baseline(spec, xs_np, T, budget_s, expert_b):
         es = oracle.ExpertSet(used, spec.n_experts, h["gate_packed"], h["gate_scales"],
                               h["up_packed"], h["up_scales"], h["down_packed"], h["down_scales"])
         t0 = time.perf_counter()
-        oracle.forward(x, idx, w, es, spec.hidden, spec.inter, shared=shared,
-                       act_kind=spec.act, b1=spec.situ_b1, b2=spec.situ_b2, want_denom=False)
+        if spec.latent:
+            wd, wu, gamma = lat
+            oracle.forward_latent(x, idx, w, es, spec.hidden, spec.latent, spec.inter, wd, wu,
+                                  norm=bool(spec.latent_norm), gamma=gamma, eps=spec.rms_eps,
+                                  shared=shared, act_kind=spec.act, b1=spec.situ_b1, b2=spec.situ_b2,
+                                  want_denom=False)
+        else:
+            oracle.forward(x, idx, w, es, spec.hidden, spec.inter, shared=shared,
+                           act_kind=spec.act, b1=spec.situ_b1, b2=spec.situ_b2, want_denom=False)
         spent += time.perf_counter() - t0
         tokens += 1
         routed += len(used) * expert_b

@@ -490,7 +490,7 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t 
     const int rb_i = (L.I + kTileRows - 1) / kTileRows, rb_h = (L.H + kTileRows - 1) / kTileRows;
     const int rb_r = (L.EK + kTileRows - 1) / kTileRows;  // routed down rows
     const int rb_s = (L.Is + kTileRows - 1) / kTileRows;
-    const bool stream = stream_path_ok(L), stream_dn = stream_down_ok(L);
+    const bool stream = stream_path_ok(L), stream_dn = stream_down_ok(L, T);
     const bool sh_stream = stream_shared_ok(L, T);
     const int smax_gu = stream ? stream_max_tokens() : 0, smax_dn = stream_dn ? stream_max_tokens() : 0;
     // grids cover the most tiles the split can produce (most blocks exit at once)

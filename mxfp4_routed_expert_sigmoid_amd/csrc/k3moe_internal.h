@@ -146,10 +146,11 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t 
 
 // Weight-streaming kernels for experts with few tokens (k3moe_stream.hip).
 bool stream_path_ok(const LayerView &L);
-bool stream_down_ok(const LayerView &L);
+bool stream_down_ok(const LayerView &L, int T);
 int stream_max_tokens();
 int stream_shared_slices(int T);
 bool stream_shared_ok(const LayerView &L, int T);
+int stream_shared_down_slices(int Lt, int Is, int T);
 hipError_t launch_stream_gu(const LayerView &L, const uint16_t *x, const uint16_t *xr, const uint16_t *xr_lo,
                             int T, const int32_t *active_e, const int32_t *active_off, const int32_t *sorted,
                             const int32_t *light, const int32_t *light_n, bool with_shared, uint16_t *act_hi,

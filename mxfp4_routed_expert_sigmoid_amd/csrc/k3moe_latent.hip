@@ -146,16 +146,21 @@ __global__ __launch_bounds__(256) void k_proj(const uint16_t *__restrict__ W, co
     }
 }
 
-// Slices added in order (+ addend): fp32 out [T][R], or bf16 hi/lo planes.
+// Slices added in order, then the addend's AS slices in order: fp32 out
+// [T][R], or bf16 hi/lo planes.
 __global__ __launch_bounds__(256) void k_proj_finish(const float *__restrict__ part, int S, int T, int R,
-                                                     const float *__restrict__ addend, float *__restrict__ out,
+                                                     const float *__restrict__ addend, int AS, float *__restrict__ out,
                                                      uint16_t *__restrict__ hi, uint16_t *__restrict__ lo)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x, n = (int64_t)T * R;
     if (i >= n) return;
     float v = part[i];
     for (int s = 1; s < S; ++s) v += part[(size_t)s * n + i];
-    if (addend) v += addend[i];
+    if (addend) {
+        float a = addend[i];
+        for (int s = 1; s < AS; ++s) a += addend[(size_t)s * n + i];
+        v += a;
+    }
     if (out) {
         out[i] = v;
     } else {
@@ -198,7 +203,8 @@ __global__ __launch_bounds__(256) void k_rms_split(const float *__restrict__ acc
 
 // out = W (planes) as fp32 [T][R] (+ addend), or as bf16 hi/lo planes.
 static hipError_t launch_proj(const uint16_t *W, const uint16_t *p0, const uint16_t *p1, int T, int R, int Kd,
-                              float *part, const float *addend, float *out, uint16_t *hi, uint16_t *lo, hipStream_t s)
+                              float *part, const float *addend, int AS, float *out, uint16_t *hi, uint16_t *lo,
+                              hipStream_t s)
 {
     static const bool lds_set = [] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_proj<1>),
@@ -216,7 +222,7 @@ static hipError_t launch_proj(const uint16_t *W, const uint16_t *p0, const uint1
     else
         k_proj<1><<<grid, 256, proj_lds_bytes(1), s>>>(W, p0, nullptr, T, R, Kd, kspan, part);
     const int64_t n = (int64_t)T * R;
-    k_proj_finish<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, S, T, R, addend, out, hi, lo);
+    k_proj_finish<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, S, T, R, addend, AS, out, hi, lo);
     return hipGetLastError();
 }
 
@@ -242,12 +248,14 @@ hipError_t launch_latent_forward(const LayerView &L, const uint16_t *x, int T, c
     float *acc = reinterpret_cast<float *>(ws + lay.lat_acc);
     uint16_t *nh = reinterpret_cast<uint16_t *>(ws + lay.lat_n), *nl = nh + (size_t)T * Lt;
     float *ysh = L.Is > 0 ? reinterpret_cast<float *>(ws + lay.lat_ysh) : nullptr;
+    // the streamed shared down rows leave K-slice partials (the grouped GEMM one sum)
+    const int ysh_slices = stream_shared_ok(L, T) ? stream_shared_down_slices(L.Lt, L.Is, T) : 1;
     float *part = reinterpret_cast<float *>(ws + lay.lat_part);
     float *ys = reinterpret_cast<float *>(ws + lay.ys);
     hipError_t e;
     {
         StageMark m(prof, K3MOE_STAGE_LATENT_IN, s);  // z = Wd x, as bf16 hi and lo
-        if ((e = launch_proj(L.lat_down, x, nullptr, T, Lt, L.H, part, nullptr, nullptr, zh, zl, s)) != hipSuccess)
+        if ((e = launch_proj(L.lat_down, x, nullptr, T, Lt, L.H, part, nullptr, 1, nullptr, zh, zl, s)) != hipSuccess)
             return e;
     }
     launch_perm(L, idx, T, ws, lay, s, prof);
@@ -272,7 +280,7 @@ hipError_t launch_latent_forward(const LayerView &L, const uint16_t *x, int T, c
             k_rms_split<true><<<(unsigned)T, 256, 0, s>>>(acc, Lt, L.lat_norm, L.lat_eps, nh, nl);
         else
             k_rms_split<false><<<(unsigned)T, 256, 0, s>>>(acc, Lt, nullptr, 0.0f, nh, nl);
-        if ((e = launch_proj(L.lat_up, nh, nl, T, L.H, Lt, part, ysh, out, nullptr, nullptr, s)) != hipSuccess)
+        if ((e = launch_proj(L.lat_up, nh, nl, T, L.H, Lt, part, ysh, ysh_slices, out, nullptr, nullptr, s)) != hipSuccess)
             return e;
     }
     return hipGetLastError();

@@ -363,7 +363,8 @@ constexpr int kDBlkRows = kDWaves * kSRows;  // 256
 struct DnStreamParams {
     int H, I, K, T, Is;
     int Hr;                   // routed experts' output rows (H, or the latent)
-    float *ysh;               // shared expert's output fp32 [T][H]; null: ys slot K
+    float *ysh;               // shared expert's output fp32 [sh_ks][T][H]; null: ys slot K
+    int sh_ks;                // K slices of the shared rows (ysh only): fp32 partial sums
     const uint8_t *dp, *ds;
     int64_t d_sp, d_ss;
     const uint16_t *sh_down;
@@ -371,33 +372,44 @@ struct DnStreamParams {
     const int32_t *active_e, *active_off, *sorted;
     const int32_t *light, *light_n;
     int sh_items;             // leading items that run the shared expert (token groups)
+    int stg;                  // token rows staged per item (min(16, T): no item has more)
     int runs, run_rb;         // blocks per item, 256-row blocks per block
     float *ys;
 };
 
-__host__ __device__ constexpr int dn_stream_lds_bytes(int KD) { return 2 * kSTok * (2 * KD + kSPad) + kSTok * 8; }
+// LDS of a down block: both planes of stg staged token rows of width KD
+__host__ __device__ constexpr int dn_stream_lds_bytes(int KD, int stg)
+{
+    return 2 * stg * (2 * KD + kSPad) + kSTok * 8;
+}
 
+// Rows [rb0, rb1) x 256 of an R-row matrix, K columns [k0, k0 + KD) of rows
+// KW long (weights and activations), into yout rows orow * R.
 template <bool FP4>
 __device__ __forceinline__ void dn_stream_run(const DnStreamParams &p, const uint8_t *wd, const uint8_t *sd, int KD,
                                               int rb0, int rb1, const int *arow_l, const int *orow_l, int n,
                                               const uint16_t *ahi, const uint16_t *alo, uint8_t *B_l, int R,
-                                              float *yout)
+                                              float *yout, int KW, int k0)
 {
     constexpr int GK = group_k<FP4>();
     const int BROW = 2 * KD + kSPad;
     const int H = R, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
     const int NG = KD / GK, total = (rb1 - rb0) * NG;
-    const size_t rowb = FP4 ? (size_t)KD / 2 : (size_t)KD * 2;
+    const size_t rowb = FP4 ? (size_t)KW / 2 : (size_t)KW * 2;
+    wd += FP4 ? k0 / 2 : (size_t)k0 * 2;
+    if (FP4) sd += k0 / 32;
 
-    // stage both activation planes of the item's tokens, whole K range
+    // stage both activation planes of the item's tokens (stg rows: every
+    // item has at most that many), whole K range
+    const int stg = p.stg;
     {
         const int ru4 = KD * 2 / 16;  // u4 per token row
-        for (int v = tid; v < 2 * kSTok * ru4; v += 64 * kDWaves) {
-            const int half = v / (kSTok * ru4), vv = v - half * (kSTok * ru4);
+        for (int v = tid; v < 2 * stg * ru4; v += 64 * kDWaves) {
+            const int half = v / (stg * ru4), vv = v - half * (stg * ru4);
             const int col = vv / ru4, seg = vv - col * ru4;
             const uint16_t *src = half ? alo : ahi;
-            *reinterpret_cast<u4 *>(B_l + (half * kSTok + col) * BROW + 16 * seg) =
-                *reinterpret_cast<const u4 *>(src + (size_t)arow_l[col] * KD + 8 * seg);
+            *reinterpret_cast<u4 *>(B_l + (half * stg + col) * BROW + 16 * seg) =
+                *reinterpret_cast<const u4 *>(src + (size_t)arow_l[col] * KW + k0 + 8 * seg);
         }
     }
     __syncthreads();
@@ -415,13 +427,15 @@ __device__ __forceinline__ void dn_stream_run(const DnStreamParams &p, const uin
             const uint8_t *w = wd + (size_t)r * rowb + 16 * g + (size_t)gi * (kSChunks * 64);
 #pragma unroll
             for (int c = 0; c < kSChunks; ++c) b.a[rf][c] = *reinterpret_cast<const u4 *>(w + 64 * c);
-            if constexpr (FP4) b.s[rf] = *reinterpret_cast<const u4 *>(sd + (size_t)r * (KD / 32) + 16 * gi);
+            if constexpr (FP4) b.s[rf] = *reinterpret_cast<const u4 *>(sd + (size_t)r * (KW / 32) + 16 * gi);
         }
     };
 
     v4f acc[2] = {v4f{0.0f, 0.0f, 0.0f, 0.0f}, v4f{0.0f, 0.0f, 0.0f, 0.0f}};
-    const uint8_t *Bh = B_l + l16 * BROW;
-    const uint8_t *Bl = B_l + (kSTok + l16) * BROW;
+    // B column l16 reads a staged row (columns past stg repeat the last one,
+    // never stored)
+    const uint8_t *Bh = B_l + min(l16, stg - 1) * BROW;
+    const uint8_t *Bl = B_l + (stg + min(l16, stg - 1)) * BROW;
     auto compute = [&](const Grp &b, int it) {
         const int rb = rb0 + it / NG, gi = it - (it / NG) * NG;
         const int kg = gi * GK;
@@ -486,16 +500,19 @@ __global__ __launch_bounds__(64 * kDWaves) void k_dn_stream(DnStreamParams p)
     const int RBT = (R + kDBlkRows - 1) / kDBlkRows;
     const int rb0 = run * p.run_rb, rb1 = min(RBT, rb0 + p.run_rb);
     if (rb0 >= rb1) return;
-    if (item < p.sh_items) {  // shared expert, token group `item`
-        const int t0 = item * kSTok, n = min(kSTok, p.T - t0);
+    if (item < p.sh_items) {  // shared expert: token group tg, K slice ks
+        const int tg = item / p.sh_ks, ks = item - tg * p.sh_ks;
+        const int t0 = tg * kSTok, n = min(kSTok, p.T - t0);
         if (threadIdx.x < kSTok) {
             const int t = t0 + min((int)threadIdx.x, n - 1);
             arow_l[threadIdx.x] = t;
             orow_l[threadIdx.x] = p.ysh ? t : t * (p.K + 1) + p.K;
         }
         __syncthreads();
-        dn_stream_run<false>(p, reinterpret_cast<const uint8_t *>(p.sh_down), nullptr, p.Is, rb0, rb1, arow_l,
-                             orow_l, n, p.ash_hi, p.ash_lo, B_l, p.H, p.ysh ? p.ysh : p.ys);
+        const int KS = p.Is / p.sh_ks;
+        dn_stream_run<false>(p, reinterpret_cast<const uint8_t *>(p.sh_down), nullptr, KS, rb0, rb1, arow_l,
+                             orow_l, n, p.ash_hi, p.ash_lo, B_l, p.H,
+                             p.ysh ? p.ysh + (size_t)ks * p.T * p.H : p.ys, p.Is, ks * KS);
         return;
     }
     const int li = item - p.sh_items;
@@ -510,7 +527,7 @@ __global__ __launch_bounds__(64 * kDWaves) void k_dn_stream(DnStreamParams p)
     }
     __syncthreads();
     dn_stream_run<true>(p, p.dp + e * p.d_sp, p.ds + e * p.d_ss, p.I, rb0, rb1, arow_l, orow_l, n, p.act_hi,
-                        p.act_lo, B_l, p.Hr, p.ys);
+                        p.act_lo, B_l, p.Hr, p.ys, p.I, 0);
 }
 
 }  // namespace
@@ -521,17 +538,30 @@ bool stream_path_ok(const LayerView &L)
            L.I % kSBlkRows == 0 && L.H % kSBlkRows == 0 && L.EK % kSBlkRows == 0 && L.Is % kSBlkRows == 0;
 }
 
-// The down kernel stages a whole item's activations: it takes the routed
-// light experts when they fit in LDS (and the shared expert likewise).
-bool stream_down_ok(const LayerView &L)
+// The down kernel stages a whole item's activations (at most min(16, T)
+// token rows): it takes the routed light experts when they fit in LDS (and
+// the shared expert likewise).
+bool stream_down_ok(const LayerView &L, int T)
 {
-    return stream_path_ok(L) && dn_stream_lds_bytes(std::max(L.I, L.Is)) <= 160 * 1024 &&
+    return stream_path_ok(L) && dn_stream_lds_bytes(std::max(L.I, L.Is), std::min(T, kSTok)) <= 160 * 1024 &&
            (L.Is == 0 || L.Is % group_k<true>() == 0);
 }
 
 int stream_max_tokens() { return kSTok; }
 
-bool stream_shared_ok(const LayerView &L, int T) { return L.Is > 0 && T <= 8 * kSTok && stream_down_ok(L); }
+bool stream_shared_ok(const LayerView &L, int T) { return L.Is > 0 && T <= 8 * kSTok && stream_down_ok(L, T); }
+
+// K slices of the shared expert's down rows when its output goes to a
+// buffer of its own (fp32 partials summed in order by the consumer): for one
+// token group, so its few row blocks (one per 256 rows of H) do not outlast
+// the routed experts' blocks. Each slice a multiple of the bf16 K group.
+int stream_shared_down_slices(int Lt, int Is, int T)
+{
+    if (Lt == 0 || Is == 0 || T > kSTok) return 1;
+    for (int S = 8; S > 1; S /= 2)
+        if (Is % (S * group_k<false>()) == 0) return S;
+    return 1;
+}
 
 // Slices of the shared expert's hidden dimension for small batches, where
 // its few gate/up blocks (one per 128 rows and token group) would otherwise
@@ -628,7 +658,9 @@ hipError_t launch_stream_dn(const LayerView &L, int T, const int32_t *active_e, 
     p.sorted = sorted;
     p.light = light;
     p.light_n = light_n;
-    p.sh_items = with_shared ? (T + kSTok - 1) / kSTok : 0;
+    p.sh_ks = ysh ? stream_shared_down_slices(L.Lt, L.Is, T) : 1;
+    p.sh_items = with_shared ? (T + kSTok - 1) / kSTok * p.sh_ks : 0;
+    p.stg = std::min(T, kSTok);
     // each item's rows in `runs` blocks of run_rb 256-row blocks: about 7 row
     // blocks per run, fewer when there are few items (about 512 blocks)
     const int64_t cap = std::min<int64_t>(L.E, (int64_t)T * L.K);
@@ -639,7 +671,7 @@ hipError_t launch_stream_dn(const LayerView &L, int T, const int32_t *active_e, 
     p.runs = (rbt + p.run_rb - 1) / p.run_rb;
     p.ys = ys;
     const unsigned nblk = (unsigned)((p.sh_items + cap) * p.runs);
-    k_dn_stream<<<nblk, 64 * kDWaves, dn_stream_lds_bytes(std::max(L.I, L.Is)), s>>>(p);
+    k_dn_stream<<<nblk, 64 * kDWaves, dn_stream_lds_bytes(std::max(L.I, L.Is / p.sh_ks), p.stg), s>>>(p);
     return hipGetLastError();
 }
 
