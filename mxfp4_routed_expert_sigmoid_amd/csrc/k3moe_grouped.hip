@@ -496,6 +496,11 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t 
     // grids cover the most tiles the split can produce (most blocks exit at once)
     const size_t cap_gu = grouped_tile_cap(T, L.K, L.E, TG, smax_gu), cap_dn = grouped_tile_cap(T, L.K, L.E, TD, smax_dn);
     int32_t *light_gu = light, *light_dn = light + L.E;
+    // no expert can hold more than T * K assignments (ids may repeat within a
+    // token): when that fits the streamed limit, no tile is heavy and the
+    // tile GEMMs would only exit
+    const int64_t most = (int64_t)T * L.K;
+    const bool gemm_gu = !(stream && most <= smax_gu), gemm_dn = !(stream_dn && most <= smax_dn);
     k_tiles<<<1, 1024, 0, s>>>(active_n, active_off, TG, TD, smax_gu, smax_dn, tiles_gu, tiles_dn, light_gu, light_dn,
                                counts);
 
@@ -533,9 +538,9 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t 
         gp.tile_n = counts;
         gp.ohi = act_hi;
         gp.olo = act_lo;
-        if (two)
+        if (gemm_gu && two)
             k_gemm<kGU2><<<(unsigned)(cap_gu * rb_i), 64 * GemmShape<kGU2>::WAVES, gemm_lds_bytes<kGU2>(), s>>>(gp);
-        else
+        else if (gemm_gu)
             k_gemm<kGU><<<(unsigned)(cap_gu * rb_i), 64 * GemmShape<kGU>::WAVES, gemm_lds_bytes<kGU>(), s>>>(gp);
         if (L.Is > 0 && !sh_stream) {
             StageMark m2(prof, K3MOE_STAGE_SHARED_GATEUP, s);
@@ -575,7 +580,8 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t 
         dp.tiles = tiles_dn;
         dp.tile_n = counts + 1;
         dp.ys = ys;
-        k_gemm<kDN><<<(unsigned)(cap_dn * rb_r), 64 * GemmShape<kDN>::WAVES, gemm_lds_bytes<kDN>(), s>>>(dp);
+        if (gemm_dn)
+            k_gemm<kDN><<<(unsigned)(cap_dn * rb_r), 64 * GemmShape<kDN>::WAVES, gemm_lds_bytes<kDN>(), s>>>(dp);
         if (L.Is > 0 && !sh_stream) {
             // shared rows of H: to slot k of ys (flat), or to ysh [T][H] (K = 0 makes the row t)
             GemmParams sp = dp;

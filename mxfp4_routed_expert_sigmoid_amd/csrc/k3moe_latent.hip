@@ -172,19 +172,36 @@ __global__ __launch_bounds__(256) void k_proj_finish(const float *__restrict__ p
 
 // RMSNorm of the routed aggregate (k3_rmsnorm: sum of squares in fp64,
 // epsilon inside the root, x * inv * gamma in fp32), then bf16 hi and lo
-// planes for the up-projection. One block per token.
+// planes for the up-projection. One block per token; L % 4 == 0. Each pass
+// issues its loads kRmsV float4 per thread at a time, so a pass over a row of
+// up to 4096 costs one memory latency.
+constexpr int kRmsV = 4;
 template <bool NORM>
 __global__ __launch_bounds__(256) void k_rms_split(const float *__restrict__ acc, int L, const float *__restrict__ gamma,
                                                    float eps, uint16_t *__restrict__ hi, uint16_t *__restrict__ lo)
 {
     __shared__ double red[4];
     __shared__ float inv_sh;
-    const int t = blockIdx.x, tid = threadIdx.x;
-    const float *a = acc + (size_t)t * L;
+    const int t = blockIdx.x, tid = threadIdx.x, nv = L / 4;
+    const float4 *a = reinterpret_cast<const float4 *>(acc + (size_t)t * L);
     float inv = 1.0f;
     if constexpr (NORM) {
         double ss = 0.0;
-        for (int l = tid; l < L; l += 256) ss = fma((double)a[l], (double)a[l], ss);
+        for (int c0 = 0; c0 < nv; c0 += 256 * kRmsV) {
+            float4 v[kRmsV];
+#pragma unroll
+            for (int j = 0; j < kRmsV; ++j) {
+                const int i = c0 + tid + 256 * j;
+                v[j] = i < nv ? a[i] : float4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+#pragma unroll
+            for (int j = 0; j < kRmsV; ++j) {
+                ss = fma((double)v[j].x, (double)v[j].x, ss);
+                ss = fma((double)v[j].y, (double)v[j].y, ss);
+                ss = fma((double)v[j].z, (double)v[j].z, ss);
+                ss = fma((double)v[j].w, (double)v[j].w, ss);
+            }
+        }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
         if ((tid & 63) == 0) red[tid >> 6] = ss;
@@ -193,11 +210,36 @@ __global__ __launch_bounds__(256) void k_rms_split(const float *__restrict__ acc
         __syncthreads();
         inv = inv_sh;
     }
-    for (int l = tid; l < L; l += 256) {
-        const float v = NORM ? a[l] * inv * gamma[l] : a[l];
-        const uint16_t h = bf16_rne(v);
-        hi[(size_t)t * L + l] = h;
-        lo[(size_t)t * L + l] = bf16_rne(v - bf16f(h));
+    const float4 *gm = reinterpret_cast<const float4 *>(gamma);
+    uint2 *h2 = reinterpret_cast<uint2 *>(hi + (size_t)t * L), *l2 = reinterpret_cast<uint2 *>(lo + (size_t)t * L);
+    for (int c0 = 0; c0 < nv; c0 += 256 * kRmsV) {
+        float4 v[kRmsV], gv[kRmsV];
+#pragma unroll
+        for (int j = 0; j < kRmsV; ++j) {
+            const int i = min(c0 + tid + 256 * j, nv - 1);
+            v[j] = a[i];
+            if constexpr (NORM) gv[j] = gm[i];
+        }
+#pragma unroll
+        for (int j = 0; j < kRmsV; ++j) {
+            const int i = c0 + tid + 256 * j;
+            if (i >= nv) break;
+            float f[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+            if constexpr (NORM) {
+                f[0] = f[0] * inv * gv[j].x;
+                f[1] = f[1] * inv * gv[j].y;
+                f[2] = f[2] * inv * gv[j].z;
+                f[3] = f[3] * inv * gv[j].w;
+            }
+            uint16_t h[4], l[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                h[q] = bf16_rne(f[q]);
+                l[q] = bf16_rne(f[q] - bf16f(h[q]));
+            }
+            h2[i] = uint2{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
+            l2[i] = uint2{l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16)};
+        }
     }
 }
 
