@@ -58,6 +58,10 @@ def lib():
         L.k3o_forward_latent.argtypes = [P, P, P, i64, i64, i64, i64, P, P, i64, i64, P,
                                          P, P, P, P, P, P, P, P, ctypes.c_int, P, ctypes.c_double,
                                          P, P, P, i64, ctypes.c_int, ctypes.c_double, ctypes.c_double]
+        L.k3o_bf16_rne.restype = ctypes.c_uint16
+        L.k3o_bf16_rne.argtypes = [ctypes.c_float]
+        L.k3o_prenorm_bf16.restype = None
+        L.k3o_prenorm_bf16.argtypes = [P, P, P, i64, i64, ctypes.c_float]
         L.k3o_threads.restype = ctypes.c_int
         L.k3o_threads.argtypes = []
         _lib = L
@@ -212,6 +216,23 @@ def rmsnorm(v, gamma=None, eps=1e-5):
     out = np.empty_like(v)
     inv = lib().k3o_rmsnorm(_ptr(out), _ptr(v), _ptr(gamma), v.size, float(eps))
     return out, inv
+
+
+def bf16_rne(v: float) -> int:
+    """fp32 value -> bf16 bits, nearest with ties to even (by the definition)."""
+    return int(lib().k3o_bf16_rne(float(np.float32(v))))
+
+
+def prenorm_bf16(h, gamma, eps):
+    """The pre-MoE norm of a decoder layer, rounded to bf16: uint16 [T][n]
+    from fp32 h [T][n] and gain fp32 [n] (k3_rmsnorm's float form)."""
+    h = _c(h, np.float32)
+    gamma = _c(gamma, np.float32)
+    T, n = h.shape
+    assert gamma.shape == (n,)
+    x = np.empty((T, n), np.uint16)
+    lib().k3o_prenorm_bf16(_ptr(x), _ptr(h), _ptr(gamma), T, n, float(np.float32(eps)))
+    return x
 
 
 def forward_latent(x, idx, w, experts: ExpertSet, H, L, I, lat_down, lat_up, norm=True,

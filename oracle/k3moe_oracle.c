@@ -28,6 +28,10 @@
  *     the expert latent, the experts at the latent width, RMSNorm of the
  *     aggregate, up-projection, shared experts on the original x) and §5,
  *     k3_rmsnorm (epsilon inside the square root).
+ *   - Pre-MoE norm of a decoder layer: the decoder-layer listing after
+ *     "Aggregate, attend, aggregate again" (the MoE reads k3_rmsnorm of the
+ *     residual stream with the post-attention gain) in the exact float form
+ *     of §5 k3_rmsnorm, rounded once to the layer's bf16 tokens.
  * Expert failures that the pages count as drops are mirrored: an index outside
  * [0, n_experts) contributes nothing and is counted.
  *
@@ -420,4 +424,39 @@ int k3o_threads(void)
 #else
     return 0;
 #endif
+}
+
+/* fp32 -> bf16 by its definition: of the two bf16 values around v (the
+ * truncation toward zero and the next value away from zero) the nearer one,
+ * and on a tie the one whose last bit is 0. Finite v below the bf16 maximum. */
+uint16_t k3o_bf16_rne(float v)
+{
+    uint32_t u;
+    memcpy(&u, &v, sizeof u);
+    const uint16_t toward = (uint16_t)(u >> 16), away = (uint16_t)(toward + 1);
+    const double dt = fabs((double)v - k3o_bf16(toward)), da = fabs(k3o_bf16(away) - (double)v);
+    if (dt < da) return toward;
+    if (da < dt) return away;
+    return (toward & 1) ? away : toward;
+}
+
+/* The pre-MoE norm (decoder-layer listing: hin = k3_rmsnorm(h, post_norm);
+ * §5 k3_rmsnorm as printed): for each of T rows of n floats,
+ *   ss  = sum_i (double)h_i * (double)h_i        (index order, double)
+ *   inv = (float)(1 / sqrt(ss / n + eps))         epsilon inside the root
+ *   v_i = (h_i * inv) * gamma_i                   two float products
+ *   x_i = bf16_RNE(v_i)                           the layer's bf16 token */
+void k3o_prenorm_bf16(uint16_t *x, const float *h, const float *gamma, int64_t T, int64_t n, float eps)
+{
+    for (int64_t t = 0; t < T; t++) {
+        const float *ht = h + t * n;
+        double ss = 0.0;
+        for (int64_t i = 0; i < n; i++) ss += (double)ht[i] * (double)ht[i];
+        const float inv = (float)(1.0 / sqrt(ss / (double)n + (double)eps));
+        for (int64_t i = 0; i < n; i++) {
+            const float p = ht[i] * inv;
+            const float v = p * gamma[i];
+            x[t * n + i] = k3o_bf16_rne(v);
+        }
+    }
 }
