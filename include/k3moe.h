@@ -35,6 +35,9 @@
  *            out  = Wu acc                            bf16 [H][L]
  *            out += S2( act(S1 x, S3 x) )             shared expert on the
  *                                                     ORIGINAL x, unweighted
+ *   step (one decoder layer's MoE on the fp32 residual stream h):
+ *            x    = bf16_RNE( h * inv * gamma ),  inv = fp32(1/sqrt(sum(h^2)/H + eps))
+ *            h   += forward(x, route(x))          fp32, after the whole output
  *   act:     SiTU-GLU  b1*tanh(g/b1) * sigmoid(g) * b2*tanh(u/b2)   (default)
  *            SwiGLU    g * sigmoid(g) * u
  *
@@ -169,19 +172,44 @@ k3moe_status k3moe_route(const k3moe_layer *layer, const uint16_t *x, int32_t T,
  *                          k3moe_error_count), as the README counts dropped
  *                          experts instead of hiding them
  *   w    fp32  [T][topk]
- *   out  fp32  [T][hidden] out: written, not accumulated into
+ *   out  fp32  [T][hidden] out: written, not accumulated into (16-byte
+ *                          aligned)
  * Deterministic: the same inputs give the same bits on every call; the
  * routed sum is taken in router order with no atomics. T == 0 does nothing. */
 k3moe_status k3moe_forward(const k3moe_layer *layer, const uint16_t *x, int32_t T,
                            const int32_t *idx, const float *w, float *out,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* One decoder layer's MoE on the residual stream (README, the decoder-layer
+ * listing after "Aggregate, attend, aggregate again": the layer input is
+ * k3_rmsnorm of h with the post-attention gain, then k3_moe; the output is
+ * added into the residual stream):
+ *   x = bf16_RNE(h[t] * inv * gamma), inv = (float)(1 / sqrt(sum h^2 / H + eps))
+ *       (README §5 k3_rmsnorm: fp64 sum of squares, epsilon inside the root,
+ *       two fp32 products in that order; rounded once to bf16 because the
+ *       layer takes bf16 tokens)
+ *   idx, w = route(x)               as k3moe_route
+ *   h[t] += forward(x, idx, w)      fp32, the complete layer output added once
+ *   h      fp32 [T][hidden]  in/out, 16-byte aligned
+ *   gamma  fp32 [hidden]     the norm's gain, 16-byte aligned
+ *   eps    > 0 and finite, else K3MOE_E_INVALID_ARG
+ *   x_out  bf16 [T][hidden]  out (optional, NULL = kept in the workspace): x
+ *   idx    int32 [T][topk]   out
+ *   w      fp32  [T][topk]   out
+ *   hb     bf16 [T][hidden]  out (optional, NULL = not written):
+ *                            bf16_RNE of the updated h
+ * Uses the same workspace as route/forward (k3moe_workspace_size). Ids are
+ * those of the router, so no drop can occur. T == 0 does nothing. */
+k3moe_status k3moe_step(const k3moe_layer *layer, float *h, int32_t T, const float *gamma,
+                        float eps, uint16_t *x_out, int32_t *idx, float *w, uint16_t *hb,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
 /* Number of (token, slot) assignments with an out-of-range expert id seen by
  * k3moe_forward since create or the last reset. Synchronises the stream. */
 k3moe_status k3moe_error_count(const k3moe_layer *layer, uint64_t *n, void *stream);
 k3moe_status k3moe_error_reset(k3moe_layer *layer, void *stream);
 
-/* Per-stage timing on the caller's stream. While enabled, route and forward
+/* Per-stage timing on the caller's stream. While enabled, route, forward and step
  * record a HIP event pair around each of their kernel launches (stages
  * below); k3moe_profile_read synchronises the stream, returns per stage the
  * summed elapsed milliseconds and the number of launches since the last
@@ -198,7 +226,8 @@ typedef enum {
     K3MOE_STAGE_COMBINE = 7,        /* router-order weighted sum + shared */
     K3MOE_STAGE_LATENT_IN = 8,      /* latent: down-projection of x       */
     K3MOE_STAGE_LATENT_OUT = 9,     /* latent: norm and up-projection     */
-    K3MOE_N_STAGES = 10
+    K3MOE_STAGE_PRENORM = 10,       /* step: norm of the residual stream  */
+    K3MOE_N_STAGES = 11
 } k3moe_stage;
 
 k3moe_status k3moe_profile_enable(k3moe_layer *layer, int enable);

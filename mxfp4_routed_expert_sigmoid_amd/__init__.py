@@ -56,10 +56,10 @@ class Weights(ctypes.Structure):
 
 _lib = None
 EXPORTS = ("k3moe_layer_create", "k3moe_workspace_size", "k3moe_route", "k3moe_forward",
-           "k3moe_error_count", "k3moe_error_reset", "k3moe_profile_enable",
+           "k3moe_step", "k3moe_error_count", "k3moe_error_reset", "k3moe_profile_enable",
            "k3moe_profile_read", "k3moe_layer_destroy", "k3moe_status_string")
 STAGES = ("router", "topk", "xsplit", "perm", "gateup", "shared_gateup", "down", "combine",
-          "latent_in", "latent_out")
+          "latent_in", "latent_out", "prenorm")
 
 
 def lib():
@@ -78,6 +78,8 @@ def lib():
         L.k3moe_route.argtypes = [P, P, i32, P, P, P, P, ctypes.c_size_t, P]
         L.k3moe_forward.restype = st
         L.k3moe_forward.argtypes = [P, P, i32, P, P, P, P, ctypes.c_size_t, P]
+        L.k3moe_step.restype = st
+        L.k3moe_step.argtypes = [P, P, i32, P, ctypes.c_float, P, P, P, P, P, ctypes.c_size_t, P]
         L.k3moe_error_count.restype = st
         L.k3moe_error_count.argtypes = [P, ctypes.POINTER(ctypes.c_uint64), P]
         L.k3moe_error_reset.restype = st
@@ -217,6 +219,19 @@ class Layer:
         _check(lib().k3moe_forward(self.handle, x.data_ptr(), T, idx.data_ptr(), w.data_ptr(),
                                    out.data_ptr(), p, n, _stream(stream, self.device)),
                "k3moe_forward")
+
+    def step(self, h, gamma, eps, idx, w, x_out=None, hb=None, workspace=None, stream=None):
+        """k3moe_step: h fp32 [T][H] += layer(bf16(RMSNorm(h) * gamma)), in place;
+        idx int32 [T][k] and w fp32 [T][k] written; x_out / hb (bf16 [T][H],
+        optional) receive the normed input and bf16 of the updated h."""
+        T = h.shape[0]
+        _dev(h, (4,), "h"), _dev(gamma, (4,), "gamma"), _dev(idx, (4,), "idx"), _dev(w, (4,), "w")
+        _dev(x_out, (2,), "x_out"), _dev(hb, (2,), "hb")
+        ws = workspace if workspace is not None else self.workspace(T)
+        p, n = self._ws(ws)
+        _check(lib().k3moe_step(self.handle, h.data_ptr(), T, gamma.data_ptr(), float(eps),
+                                _ptr(x_out), idx.data_ptr(), w.data_ptr(), _ptr(hb), p, n,
+                                _stream(stream, self.device)), "k3moe_step")
 
     def error_count(self, stream=None) -> int:
         n = ctypes.c_uint64()

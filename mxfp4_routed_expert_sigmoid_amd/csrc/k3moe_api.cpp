@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <new>
 
 #include "k3moe_internal.h"
@@ -85,6 +86,7 @@ WsLayout ws_layout(const k3moe_config &c, int64_t T)
         }
         L.lat_part = take(part);
     }
+    L.step_x = take((size_t)T * H * 2);
     L.total = o;
     return L;
 }
@@ -307,12 +309,40 @@ k3moe_status k3moe_forward(const k3moe_layer *l, const uint16_t *x, int32_t T, c
     k3moe_status s = check_call(l, T, ws, ws_bytes, &nothing);
     if (s != K3MOE_OK || nothing) return s;
     if (!x || !idx || !w || !out) return K3MOE_E_INVALID_ARG;
-    if (!aligned(x, 16) || !aligned(idx, 4) || !aligned(w, 4) || !aligned(out, 4))
+    if (!aligned(x, 16) || !aligned(idx, 4) || !aligned(w, 4) || !aligned(out, 16))
         return K3MOE_E_ALIGNMENT;
     const WsLayout lay = ws_layout(l->cfg, T);
     if (launch_forward(view(l), x, T, idx, w, out, static_cast<char *>(ws), lay,
                        static_cast<hipStream_t>(stream), l->prof) != hipSuccess)
         return K3MOE_E_HIP;
+    return K3MOE_OK;
+}
+
+k3moe_status k3moe_step(const k3moe_layer *l, float *h, int32_t T, const float *gamma, float eps,
+                        uint16_t *x_out, int32_t *idx, float *w, uint16_t *hb, void *ws, size_t ws_bytes,
+                        void *stream)
+{
+    bool nothing;
+    k3moe_status s = check_call(l, T, ws, ws_bytes, &nothing);
+    if (s != K3MOE_OK || nothing) return s;
+    if (!h || !gamma || !idx || !w || !(eps > 0.0f) || !std::isfinite(eps)) return K3MOE_E_INVALID_ARG;
+    if (!aligned(h, 16) || !aligned(gamma, 16) || !aligned(idx, 4) || !aligned(w, 4) ||
+        (x_out && !aligned(x_out, 16)) || (hb && !aligned(hb, 16)))
+        return K3MOE_E_ALIGNMENT;
+    const WsLayout lay = ws_layout(l->cfg, T);
+    char *wsc = static_cast<char *>(ws);
+    uint16_t *x = x_out ? x_out : reinterpret_cast<uint16_t *>(wsc + lay.step_x);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const LayerView v = view(l);
+    {
+        StageMark m(l->prof, K3MOE_STAGE_PRENORM, st);
+        if (launch_prenorm(h, T, v.H, gamma, eps, x, st) != hipSuccess) return K3MOE_E_HIP;
+    }
+    if (launch_route(v, x, T, idx, w, nullptr, wsc, lay, st, l->prof) != hipSuccess) return K3MOE_E_HIP;
+    OutEpi epi;
+    epi.resid = true;
+    epi.ob = hb;
+    if (launch_forward(v, x, T, idx, w, h, wsc, lay, st, l->prof, epi) != hipSuccess) return K3MOE_E_HIP;
     return K3MOE_OK;
 }
 

@@ -44,6 +44,7 @@ struct WsLayout {
     size_t lat_n = 0;         // normed aggregate as bf16 hi then lo planes [T][L]
     size_t lat_ysh = 0;       // shared expert output fp32 [T][H]
     size_t lat_part = 0;      // projection partial sums fp32 [slices][T][rows]
+    size_t step_x = 0;        // k3moe_step: the normed bf16 tokens [T][H]
     size_t total;
 };
 
@@ -121,15 +122,26 @@ int router_kspan(int H, int S);
 hipError_t launch_route(const LayerView &L, const uint16_t *x, int T, int32_t *idx,
                         float *w, float *logits, char *ws, const WsLayout &lay,
                         hipStream_t s, Profiler *prof);
+// What the layer's last kernel does with a result v of out[t][o]: store it
+// (resid = false) or add it to the value already there (out += v, fp32, the
+// residual stream); ob, when set, also receives bf16_RNE of the stored value.
+struct OutEpi {
+    bool resid = false;
+    uint16_t *ob = nullptr;
+};
+
 hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T,
                           const int32_t *idx, const float *w, float *out, char *ws,
-                          const WsLayout &lay, hipStream_t s, Profiler *prof);
+                          const WsLayout &lay, hipStream_t s, Profiler *prof, const OutEpi &epi = OutEpi());
+
+// Pre-MoE norm (k3moe_step.hip): x[t] = bf16_RNE(RMSNorm(h[t]) * gamma).
+hipError_t launch_prenorm(const float *h, int T, int H, const float *gamma, float eps, uint16_t *x, hipStream_t s);
 
 // Latent layer (k3moe_latent.hip): projections with bf16 weights, the norm.
 int proj_splits(int64_t T, int R, int Kd);
 hipError_t launch_latent_forward(const LayerView &L, const uint16_t *x, int T, const int32_t *idx,
                                  const float *w, float *out, char *ws, const WsLayout &lay, hipStream_t s,
-                                 Profiler *prof);
+                                 Profiler *prof, const OutEpi &epi);
 
 // Grouped GEMMs for batches (k3moe_grouped.hip).
 size_t grouped_tile_cap_gu(int64_t T, int K, int E);
@@ -164,6 +176,6 @@ hipError_t launch_stream_dn(const LayerView &L, int T, const int32_t *active_e, 
 void launch_perm(const LayerView &L, const int32_t *idx, int T, char *ws, const WsLayout &lay, hipStream_t s,
                  Profiler *prof);
 void launch_combine(const LayerView &L, const float *ys, const float *w, const int32_t *idx, int T, int width,
-                    bool shared, float *out, hipStream_t s);
+                    bool shared, float *out, hipStream_t s, const OutEpi &epi = OutEpi());
 
 }  // namespace k3moe

@@ -47,6 +47,13 @@ typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf16f(uint32_t h) { return __uint_as_float(h << 16); }
 
+// fp32 -> bf16 bits, round to nearest even (finite values)
+__device__ __forceinline__ uint32_t bf16_rne_u32(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
 // E8M0 byte -> the fp32 factor 2^(s-127) for the scaled converter; byte 0 is
 // the subnormal 2^-127, byte 255 drops its group (factor 0).
 __device__ __forceinline__ float e8m0_to_f32(uint32_t s)
@@ -1246,7 +1253,8 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const float *__rest
                                                              const float *__restrict__ w,
                                                              const int32_t *__restrict__ idx, int T, int K,
                                                              int H, int E, int shared, float *__restrict__ out,
-                                                             unsigned long long *errors)
+                                                             unsigned long long *errors, int resid,
+                                                             uint16_t *__restrict__ ob)
 {
     const int64_t i4 = (int64_t)blockIdx.x * kCombineThreads + threadIdx.x;  // float4 index
     const int H4 = H >> 2;
@@ -1287,7 +1295,16 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const float *__rest
             acc.z += sv.z;
             acc.w += sv.w;
         }
-        *reinterpret_cast<float4 *>(out + (size_t)t * H + o) = acc;
+        float4 *op = reinterpret_cast<float4 *>(out + (size_t)t * H + o);
+        if (resid) {  // the residual stream: h + (complete layer output)
+            const float4 hv = *op;
+            acc = make_float4(hv.x + acc.x, hv.y + acc.y, hv.z + acc.z, hv.w + acc.w);
+        }
+        *op = acc;
+        if (ob)
+            *reinterpret_cast<uint2 *>(ob + (size_t)t * H + o) =
+                make_uint2(bf16_rne_u32(acc.x) | (bf16_rne_u32(acc.y) << 16),
+                           bf16_rne_u32(acc.z) | (bf16_rne_u32(acc.w) << 16));
     }
     if (blockIdx.x == 0)
         for (int64_t a = threadIdx.x; a < (int64_t)T * K; a += kCombineThreads)
@@ -1378,7 +1395,7 @@ static bool decode_path_ok(const LayerView &L)
 // router slots are the assignment list (no permutation).
 static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const int32_t *idx,
                                     const float *w, float *out, float *act, float *ash, char *ys_base,
-                                    hipStream_t s, Profiler *prof)
+                                    hipStream_t s, Profiler *prof, const OutEpi &epi)
 {
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1444,7 +1461,7 @@ static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const
     {
         StageMark m(prof, K3MOE_STAGE_COMBINE, s);
         k_combine<<<(unsigned)((L.H / 4 + kCombineThreads - 1) / kCombineThreads), kCombineThreads, 0, s>>>(
-            ys, w, idx, 1, L.K, L.H, L.E, L.Is > 0, out, L.errors);
+            ys, w, idx, 1, L.K, L.H, L.E, L.Is > 0, out, L.errors, epi.resid, epi.ob);
     }
     return hipGetLastError();
 }
@@ -1473,18 +1490,18 @@ void launch_perm(const LayerView &L, const int32_t *idx, int T, char *ws, const 
 // out[t][0..width) = router-order sum of the staging rows ys[t][j] (stride
 // width, k + 1 slots), plus slot k when `shared`.
 void launch_combine(const LayerView &L, const float *ys, const float *w, const int32_t *idx, int T, int width,
-                    bool shared, float *out, hipStream_t s)
+                    bool shared, float *out, hipStream_t s, const OutEpi &epi)
 {
     const int64_t n4 = (int64_t)T * width / 4;
     k_combine<<<(unsigned)((n4 + kCombineThreads - 1) / kCombineThreads), kCombineThreads, 0, s>>>(
-        ys, w, idx, T, L.K, width, L.E, shared, out, L.errors);
+        ys, w, idx, T, L.K, width, L.E, shared, out, L.errors, epi.resid, epi.ob);
 }
 
 hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const int32_t *idx,
                           const float *w, float *out, char *ws, const WsLayout &lay, hipStream_t s,
-                          Profiler *prof)
+                          Profiler *prof, const OutEpi &epi)
 {
-    if (L.Lt > 0) return launch_latent_forward(L, x, T, idx, w, out, ws, lay, s, prof);
+    if (L.Lt > 0) return launch_latent_forward(L, x, T, idx, w, out, ws, lay, s, prof, epi);
     int32_t *active_n = reinterpret_cast<int32_t *>(ws + lay.active_n);
     int32_t *active_e = reinterpret_cast<int32_t *>(ws + lay.active_e);
     int32_t *active_off = reinterpret_cast<int32_t *>(ws + lay.active_off);
@@ -1493,7 +1510,7 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const in
 
     if (T == 1 && decode_path_ok(L))
         return launch_forward_t1(L, x, idx, w, out, reinterpret_cast<float *>(ws + lay.act),
-                                 reinterpret_cast<float *>(ws + lay.ash), ws + lay.ys, s, prof);
+                                 reinterpret_cast<float *>(ws + lay.ash), ws + lay.ys, s, prof, epi);
     launch_perm(L, idx, T, ws, lay, s, prof);
     // activations: routed bf16 hi and lo [T*k][I] in the fp8-term region
     // (4 bytes per element either way); shared bf16 hi and lo [T][Is] in the
@@ -1511,7 +1528,7 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const in
     if (e != hipSuccess) return e;
     {
         StageMark m(prof, K3MOE_STAGE_COMBINE, s);
-        launch_combine(L, ys, w, idx, T, L.H, L.Is > 0, out, s);
+        launch_combine(L, ys, w, idx, T, L.H, L.Is > 0, out, s, epi);
     }
     return hipGetLastError();
 }

@@ -150,7 +150,8 @@ __global__ __launch_bounds__(256) void k_proj(const uint16_t *__restrict__ W, co
 // [T][R], or bf16 hi/lo planes.
 __global__ __launch_bounds__(256) void k_proj_finish(const float *__restrict__ part, int S, int T, int R,
                                                      const float *__restrict__ addend, int AS, float *__restrict__ out,
-                                                     uint16_t *__restrict__ hi, uint16_t *__restrict__ lo)
+                                                     uint16_t *__restrict__ hi, uint16_t *__restrict__ lo, int resid,
+                                                     uint16_t *__restrict__ ob)
 {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x, n = (int64_t)T * R;
     if (i >= n) return;
@@ -162,7 +163,9 @@ __global__ __launch_bounds__(256) void k_proj_finish(const float *__restrict__ p
         v += a;
     }
     if (out) {
+        if (resid) v = out[i] + v;  // the residual stream: h + (complete layer output)
         out[i] = v;
+        if (ob) ob[i] = bf16_rne(v);
     } else {
         const uint16_t h = bf16_rne(v);
         hi[i] = h;
@@ -246,7 +249,7 @@ __global__ __launch_bounds__(256) void k_rms_split(const float *__restrict__ acc
 // out = W (planes) as fp32 [T][R] (+ addend), or as bf16 hi/lo planes.
 static hipError_t launch_proj(const uint16_t *W, const uint16_t *p0, const uint16_t *p1, int T, int R, int Kd,
                               float *part, const float *addend, int AS, float *out, uint16_t *hi, uint16_t *lo,
-                              hipStream_t s)
+                              hipStream_t s, const OutEpi &epi = OutEpi())
 {
     static const bool lds_set = [] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_proj<1>),
@@ -264,7 +267,8 @@ static hipError_t launch_proj(const uint16_t *W, const uint16_t *p0, const uint1
     else
         k_proj<1><<<grid, 256, proj_lds_bytes(1), s>>>(W, p0, nullptr, T, R, Kd, kspan, part);
     const int64_t n = (int64_t)T * R;
-    k_proj_finish<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, S, T, R, addend, AS, out, hi, lo);
+    k_proj_finish<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, S, T, R, addend, AS, out, hi, lo, epi.resid,
+                                                                 epi.ob);
     return hipGetLastError();
 }
 
@@ -283,7 +287,7 @@ int proj_splits(int64_t T, int R, int Kd)
 
 hipError_t launch_latent_forward(const LayerView &L, const uint16_t *x, int T, const int32_t *idx,
                                  const float *w, float *out, char *ws, const WsLayout &lay, hipStream_t s,
-                                 Profiler *prof)
+                                 Profiler *prof, const OutEpi &epi)
 {
     const int Lt = L.Lt;
     uint16_t *zh = reinterpret_cast<uint16_t *>(ws + lay.lat_z), *zl = zh + (size_t)T * Lt;
@@ -322,7 +326,7 @@ hipError_t launch_latent_forward(const LayerView &L, const uint16_t *x, int T, c
             k_rms_split<true><<<(unsigned)T, 256, 0, s>>>(acc, Lt, L.lat_norm, L.lat_eps, nh, nl);
         else
             k_rms_split<false><<<(unsigned)T, 256, 0, s>>>(acc, Lt, nullptr, 0.0f, nh, nl);
-        if ((e = launch_proj(L.lat_up, nh, nl, T, L.H, Lt, part, ysh, ysh_slices, out, nullptr, nullptr, s)) != hipSuccess)
+        if ((e = launch_proj(L.lat_up, nh, nl, T, L.H, Lt, part, ysh, ysh_slices, out, nullptr, nullptr, s, epi)) != hipSuccess)
             return e;
     }
     return hipGetLastError();

@@ -1,0 +1,88 @@
+// The pre-MoE norm of a decoder layer: the layer's input is the RMSNorm of
+// the residual stream with the post-attention gain (the "kimi-k3-in-c"
+// README, the decoder-layer listing after "Aggregate, attend, aggregate
+// again": hin = k3_rmsnorm(h, post_norm) feeds k3_moe), in the exact form of
+// §5 "Kernels with a floating point contract" (k3_rmsnorm): the sum of
+// squares in fp64, epsilon inside the root, inv = (float)(1 / sqrt(ss / n +
+// eps)), then x * inv * gain as two fp32 products. The expert layer takes
+// bf16 tokens, so the normed value is rounded once, to nearest even.
+#include "k3moe_internal.h"
+
+namespace k3moe {
+namespace {
+
+constexpr int kPnThreads = 256;
+constexpr int kPnV = 8;  // float4 loads in flight per thread and pass (rows up to 8192 in one pass)
+
+__device__ __forceinline__ uint32_t pn_bf16(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// One block per token; n % 4 == 0.
+__global__ __launch_bounds__(kPnThreads) void k_prenorm(const float *__restrict__ h, int n,
+                                                        const float *__restrict__ gamma, float eps,
+                                                        uint16_t *__restrict__ x)
+{
+    __shared__ double red[kPnThreads / 64];
+    __shared__ float inv_sh;
+    const int t = blockIdx.x, tid = threadIdx.x, nv = n / 4;
+    const float4 *a = reinterpret_cast<const float4 *>(h + (size_t)t * n);
+    double ss = 0.0;
+    for (int c0 = 0; c0 < nv; c0 += kPnThreads * kPnV) {
+        float4 v[kPnV];
+#pragma unroll
+        for (int j = 0; j < kPnV; ++j) {
+            const int i = c0 + tid + kPnThreads * j;
+            v[j] = i < nv ? a[i] : float4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+#pragma unroll
+        for (int j = 0; j < kPnV; ++j) {
+            ss = fma((double)v[j].x, (double)v[j].x, ss);
+            ss = fma((double)v[j].y, (double)v[j].y, ss);
+            ss = fma((double)v[j].z, (double)v[j].z, ss);
+            ss = fma((double)v[j].w, (double)v[j].w, ss);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    __syncthreads();
+    if (tid == 0) {
+        double tot = 0.0;
+#pragma unroll
+        for (int q = 0; q < kPnThreads / 64; ++q) tot += red[q];
+        inv_sh = (float)(1.0 / sqrt(tot / (double)n + (double)eps));
+    }
+    __syncthreads();
+    const float inv = inv_sh;
+    const float4 *gm = reinterpret_cast<const float4 *>(gamma);
+    uint2 *xo = reinterpret_cast<uint2 *>(x + (size_t)t * n);
+    for (int c0 = 0; c0 < nv; c0 += kPnThreads * kPnV) {
+        float4 v[kPnV], g[kPnV];
+#pragma unroll
+        for (int j = 0; j < kPnV; ++j) {
+            const int i = min(c0 + tid + kPnThreads * j, nv - 1);
+            v[j] = a[i];
+            g[j] = gm[i];
+        }
+#pragma unroll
+        for (int j = 0; j < kPnV; ++j) {
+            const int i = c0 + tid + kPnThreads * j;
+            if (i < nv)
+                xo[i] = uint2{pn_bf16(v[j].x * inv * g[j].x) | (pn_bf16(v[j].y * inv * g[j].y) << 16),
+                              pn_bf16(v[j].z * inv * g[j].z) | (pn_bf16(v[j].w * inv * g[j].w) << 16)};
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prenorm(const float *h, int T, int H, const float *gamma, float eps, uint16_t *x, hipStream_t s)
+{
+    k_prenorm<<<(unsigned)T, kPnThreads, 0, s>>>(h, H, gamma, eps, x);
+    return hipGetLastError();
+}
+
+}  // namespace k3moe
