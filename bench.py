@@ -16,6 +16,9 @@ shared expert of inter 1536, bias N(0, 0.01)):
            latent with inter 3072 (the same 17,547,264 B per expert), two
            shared experts of 3072 (one of 6144) on x, bf16 down- and
            up-projections, RMSNorm of the aggregate
+  step     T = 1 through k3moe_step on the full shape: the decoder layer's
+           pre-MoE RMSNorm of an fp32 residual stream into bf16 tokens, route,
+           experts, the residual add fused into the last kernel
 Steps rotate over a pool of token batches so consecutive steps select
 different experts (the 281 MB a decode step touches is not left in the
 256 MB last-level cache by the previous step).
@@ -41,6 +44,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "routed-expert HBM GB/s (decode) and tokens/s per MoE layer, % of roofline"
 HBM_PEAK_GBPS = 8000.0
+STEP_EPS = 1e-5  # the pre-MoE norm's epsilon (the pages' rms_eps)
 EXPERT_MATRIX_BYTES = None  # filled from the spec
 
 
@@ -57,7 +61,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", choices=("decode", "batched", "prefill", "latent"), default="decode")
+    ap.add_argument("--workload", choices=("decode", "batched", "prefill", "latent", "step"), default="decode")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -78,7 +82,8 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     T, routing, pool = {"decode": (1, "normal", 64), "batched": (64, "normal", 8),
-                        "prefill": (2048, "zipf", 2), "latent": (1, "normal", 64)}[args.workload]
+                        "prefill": (2048, "zipf", 2), "latent": (1, "normal", 64),
+                        "step": (1, "normal", 64)}[args.workload]
     if args.workload == "latent":
         spec = synth.pages_latent_spec(seed=0, routing=routing)
     else:
@@ -95,6 +100,12 @@ def main():
     w = torch.empty((T, K), dtype=torch.float32, device=dev)
     out = torch.empty((T, H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    if args.workload == "step":
+        # residual streams (each step adds the layer's output into its row)
+        hs_np = [synth.make_residual(spec, T, attempt=100 + p) for p in range(pool)]
+        hs = [torch.from_numpy(h).to(dev) for h in hs_np]
+        gamma_np = synth.make_post_norm(spec)
+        gamma = torch.from_numpy(gamma_np).to(dev)
 
     # calibration read of known size (256 MiB) for hardware byte counters
     cal = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -103,6 +114,9 @@ def main():
     del cal
 
     def step(i):
+        if args.workload == "step":
+            layer.step(hs[i % pool], gamma, STEP_EPS, idx, w, workspace=ws, stream=stream)
+            return
         x = xs[i % pool]
         layer.route(x, idx, w, workspace=ws, stream=stream)
         layer.forward(x, idx, w, out, workspace=ws, stream=stream)
@@ -154,6 +168,8 @@ def main():
         "gateup": nd * 2 * gu + (2 * Is * H * 2 if shared_in_gateup else 0) + x_read + act_b,
         "down": nd * dn + Is * H * 2 + act_b + T * (K + 1) * EKw * 4 + (T * H * 4 if Lt else 0),
     }
+    if args.workload == "step":
+        stage_bytes["prenorm"] = T * H * 4 + H * 4 + T * H * 2
     if Lt:
         stage_bytes["latent_in"] = Lt * H * 2 + T * H * 2 + T * Lt * 4
         stage_bytes["latent_out"] = H * Lt * 2 + Lt * 4 + T * Lt * 12 + T * H * 8
@@ -161,12 +177,15 @@ def main():
                "batched": {"gateup": "k_gu_stream", "down": "k_dn_stream"},
                "prefill": {"gateup": "k_gu_gemm + k_gu_stream", "down": "k_dn_gemm + k_dn_stream"},
                "latent": {"gateup": "k_gu_stream", "down": "k_dn_stream", "latent_in": "k_proj",
-                          "latent_out": "k_proj + k_rms_split"}}[args.workload]
+                          "latent_out": "k_proj + k_rms_split"},
+               "step": {"gateup": "k_gateup_dec", "down": "k_down_dec", "prenorm": "k_prenorm"}}[args.workload]
     dom = max(stage_bytes, key=lambda s: stage_us[s])
     achieved = stage_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9
     traffic = measured_traffic(kernels[dom])
     value = routed_bytes / (ms * 1e-3) / 1e9
     layer_bytes = routed_bytes + router_bytes + shared_bytes + proj_bytes + T * H * 2 + T * H * 4
+    if args.workload == "step":
+        layer_bytes += T * H * 8 + H * 4   # the stream read twice (norm, add) and the gain
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -182,6 +201,8 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{args.workload}: T={T} tokens/step, hidden {H}, {E} experts top-{K}, "
+                        + ("pre-MoE RMSNorm of an fp32 residual stream into bf16 tokens and the "
+                           "residual add (k3moe_step), " if args.workload == "step" else "")
                         + (f"experts in a {Lt} latent (bf16 down/up projections, RMSNorm of the "
                            f"aggregate), " if Lt else "")
                         + f"expert inter {I} (MXFP4), bf16 shared expert inter {Is}, sigmoid "
@@ -206,7 +227,11 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(spec, xs_np, T, args.cpu_seconds, expert_b)
+        if args.workload == "step":
+            result["cpu_baseline"] = cpu_baseline(spec, hs_np, T, args.cpu_seconds, expert_b,
+                                                  gamma=gamma_np)
+        else:
+            result["cpu_baseline"] = cpu_baseline(spec, xs_np, T, args.cpu_seconds, expert_b)
     print(json.dumps(result), flush=True)
 
 
@@ -230,10 +255,12 @@ def measured_traffic(kernel):
     return k["hbm_bytes"]
 
 
-def cpu_baseline(spec, xs_np, T, budget_s, expert_b):
+def cpu_baseline(spec, xs_np, T, budget_s, expert_b, gamma=None):
     """The fp64 oracle (route + forward) on this host, on whole tokens of the
     same workload until about budget_s seconds of oracle time have passed.
-    Expert bytes are regenerated on the host outside the timed region."""
+    Expert bytes are regenerated on the host outside the timed region. With
+    gamma, xs_np holds residual streams and the oracle's pre-MoE norm makes
+    the tokens (timed)."""
     import numpy as np
 
     import oracle
@@ -250,6 +277,8 @@ def cpu_baseline(spec, xs_np, T, budget_s, expert_b):
     for p, t in cand:
         x = xs_np[p][t:t + 1]
         t0 = time.perf_counter()
+        if gamma is not None:
+            x = oracle.prenorm_bf16(x, gamma, STEP_EPS)
         idx, w = oracle.route(x, Wr, bias, spec.topk)
         spent += time.perf_counter() - t0
         used = sorted(set(idx.ravel().tolist()))
