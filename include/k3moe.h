@@ -227,12 +227,80 @@ typedef enum {
     K3MOE_STAGE_LATENT_IN = 8,      /* latent: down-projection of x       */
     K3MOE_STAGE_LATENT_OUT = 9,     /* latent: norm and up-projection     */
     K3MOE_STAGE_PRENORM = 10,       /* step: norm of the residual stream  */
-    K3MOE_N_STAGES = 11
+    K3MOE_STAGE_CACHE_PLAN = 11,    /* cache: hits, victims, slot ids     */
+    K3MOE_STAGE_CACHE_FILL = 12,    /* cache: host -> HBM expert reads    */
+    K3MOE_N_STAGES = 13
 } k3moe_stage;
 
 k3moe_status k3moe_profile_enable(k3moe_layer *layer, int enable);
 k3moe_status k3moe_profile_read(k3moe_layer *layer, double *ms, int64_t *launches,
                                 int32_t n_stages, void *stream);
+
+/* Experts beyond HBM: an arena of expert slots in HBM fed from host memory
+ * (README §12 "An LRU cache for the experts"; the Kimi-K3.cpp README, "The
+ * consumer-memory idea").
+ *
+ * The layer's routed expert tensors (gate, up, down: packed and scales) may
+ * live in host memory: pinned pages the device can read (hipHostMalloc), or
+ * device memory. The cache holds n_slots experts in HBM. Each
+ * k3moe_cache_forward call, in stream order on the device:
+ *   1. lists the distinct experts of idx in order of first appearance in the
+ *      (token, slot) assignments;
+ *   2. pins every one already resident (a hit) and stamps it as used;
+ *   3. gives each miss, in that order, a victim slot: an empty slot (lowest
+ *      index) if any, else the least recently used slot that is not pinned
+ *      or already reserved in this call (ties: lowest index); a miss with no
+ *      such slot left is dropped (its assignments contribute nothing and are
+ *      counted in k3moe_error_count and in the cache's `dropped`);
+ *   4. reads each reserved expert's six tensors from host memory into its
+ *      slot, then runs the layer's expert kernels on the slots (k3moe_forward
+ *      semantics: router-order sum, shared expert; `out` written).
+ * The result is bit-identical to k3moe_forward on the same inputs when no
+ * request is dropped. Calls on one cache must be serialised on one stream
+ * (the slot table lives on the device and each call updates it). */
+typedef struct k3moe_cache k3moe_cache;
+
+typedef struct {
+    uint64_t steps;          /* k3moe_cache_forward calls with T > 0        */
+    uint64_t requests;       /* distinct experts asked for, summed          */
+    uint64_t resident_hits;  /* of those, in a slot when the call began     */
+    uint64_t misses;         /* of those, read from host memory             */
+    uint64_t evictions;      /* misses that displaced a resident expert     */
+    uint64_t dropped;        /* requests left without a slot                */
+    uint64_t bytes_read;     /* host -> HBM expert bytes                    */
+} k3moe_cache_stats;
+
+/* n_slots in [1, n_experts]. Allocates the arena (n_slots times the
+ * expert's six tensors, each 256-byte aligned) and the slot table; every
+ * slot starts empty. The layer must outlive the cache. Returns
+ * K3MOE_E_INVALID_ARG if an expert tensor is in host memory the device
+ * cannot read (pageable memory), K3MOE_E_OUT_OF_MEMORY if the arena does
+ * not fit. */
+k3moe_status k3moe_cache_create(const k3moe_layer *layer, int32_t n_slots, k3moe_cache **out);
+
+/* Workspace bytes of k3moe_cache_forward for up to max_tokens tokens. */
+k3moe_status k3moe_cache_workspace_size(const k3moe_cache *cache, int32_t max_tokens, size_t *bytes);
+
+/* The layer's expert forward through the cache (steps above).
+ *   x bf16 [T][hidden], idx int32 [T][topk] (expert ids), w fp32 [T][topk],
+ *   out fp32 [T][hidden] (16-byte aligned), written. T == 0 does nothing. */
+k3moe_status k3moe_cache_forward(k3moe_cache *cache, const uint16_t *x, int32_t T,
+                                 const int32_t *idx, const float *w, float *out,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Counters since create or the last reset. Synchronises the stream. */
+k3moe_status k3moe_cache_stats_read(const k3moe_cache *cache, k3moe_cache_stats *stats, void *stream);
+
+/* Which expert each slot holds (-1: empty), host int32 [n_slots].
+ * Synchronises the stream. */
+k3moe_status k3moe_cache_slots(const k3moe_cache *cache, int32_t *slots, void *stream);
+
+/* Empties every slot and zeroes the counters (a kernel on the stream). */
+k3moe_status k3moe_cache_reset(k3moe_cache *cache, void *stream);
+
+/* Frees the arena and table (synchronises the device first). NULL is
+ * accepted. */
+void k3moe_cache_destroy(k3moe_cache *cache);
 
 /* Frees the handle and its error counter (synchronises the device first).
  * NULL is accepted. */

@@ -54,12 +54,19 @@ class Weights(ctypes.Structure):
                 ("lat_up", ctypes.c_void_p), ("lat_norm", ctypes.c_void_p)]
 
 
+class CacheStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in ("steps", "requests", "resident_hits", "misses",
+                                                "evictions", "dropped", "bytes_read")]
+
+
 _lib = None
 EXPORTS = ("k3moe_layer_create", "k3moe_workspace_size", "k3moe_route", "k3moe_forward",
-           "k3moe_step", "k3moe_error_count", "k3moe_error_reset", "k3moe_profile_enable",
+           "k3moe_step", "k3moe_cache_create", "k3moe_cache_workspace_size", "k3moe_cache_forward",
+           "k3moe_cache_stats_read", "k3moe_cache_slots", "k3moe_cache_reset", "k3moe_cache_destroy",
+           "k3moe_error_count", "k3moe_error_reset", "k3moe_profile_enable",
            "k3moe_profile_read", "k3moe_layer_destroy", "k3moe_status_string")
 STAGES = ("router", "topk", "xsplit", "perm", "gateup", "shared_gateup", "down", "combine",
-          "latent_in", "latent_out", "prenorm")
+          "latent_in", "latent_out", "prenorm", "cache_plan", "cache_fill")
 
 
 def lib():
@@ -80,6 +87,20 @@ def lib():
         L.k3moe_forward.argtypes = [P, P, i32, P, P, P, P, ctypes.c_size_t, P]
         L.k3moe_step.restype = st
         L.k3moe_step.argtypes = [P, P, i32, P, ctypes.c_float, P, P, P, P, P, ctypes.c_size_t, P]
+        L.k3moe_cache_create.restype = st
+        L.k3moe_cache_create.argtypes = [P, i32, ctypes.POINTER(P)]
+        L.k3moe_cache_workspace_size.restype = st
+        L.k3moe_cache_workspace_size.argtypes = [P, i32, ctypes.POINTER(ctypes.c_size_t)]
+        L.k3moe_cache_forward.restype = st
+        L.k3moe_cache_forward.argtypes = [P, P, i32, P, P, P, P, ctypes.c_size_t, P]
+        L.k3moe_cache_stats_read.restype = st
+        L.k3moe_cache_stats_read.argtypes = [P, ctypes.POINTER(CacheStats), P]
+        L.k3moe_cache_slots.restype = st
+        L.k3moe_cache_slots.argtypes = [P, P, P]
+        L.k3moe_cache_reset.restype = st
+        L.k3moe_cache_reset.argtypes = [P, P]
+        L.k3moe_cache_destroy.restype = None
+        L.k3moe_cache_destroy.argtypes = [P]
         L.k3moe_error_count.restype = st
         L.k3moe_error_count.argtypes = [P, ctypes.POINTER(ctypes.c_uint64), P]
         L.k3moe_error_reset.restype = st
@@ -118,11 +139,11 @@ def _check(status, what):
         raise K3MoeError(status, what)
 
 
-def _dev(t, dtype_sizes, name):
+def _dev(t, dtype_sizes, name, pinned_ok=False):
     if t is None:
         return
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+    if not (t.is_cuda or (pinned_ok and t.is_pinned())):
+        raise ValueError(f"{name} must be a device tensor" + (" or pinned host memory" if pinned_ok else ""))
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if t.element_size() not in dtype_sizes:
@@ -139,6 +160,8 @@ class Layer:
     Latent layer (cfg.latent = L > 0): the experts are [E][I][L/2] (gate, up)
     and [E][L][I/2] (down), lat_down bf16 [L][H], lat_up bf16 [H][L],
     lat_norm fp32 [L] (None without the norm).
+    The routed expert tensors may instead be pinned host tensors
+    (pin_memory=True) for a layer served through a ``Cache``.
     The handle keeps references to the tensors so they outlive it.
     """
 
@@ -153,7 +176,7 @@ class Layer:
         for t, n in ((gate_packed, "gate_packed"), (gate_scales, "gate_scales"),
                      (up_packed, "up_packed"), (up_scales, "up_scales"),
                      (down_packed, "down_packed"), (down_scales, "down_scales")):
-            _dev(t, (1,), n)
+            _dev(t, (1,), n, pinned_ok=True)
         self.cfg = cfg
         self.device = router_w.device
         self._keep = (router_w, router_bias, gate_packed, gate_scales, up_packed, up_scales,
@@ -255,3 +278,65 @@ class Layer:
     def error_reset(self, stream=None):
         _check(lib().k3moe_error_reset(self.handle, _stream(stream, self.device)),
                "k3moe_error_reset")
+
+
+class Cache:
+    """An HBM arena of n_slots expert slots in front of a layer whose routed
+    experts live in pinned host memory (k3moe_cache_*). Keeps the layer alive."""
+
+    def __init__(self, layer: Layer, n_slots: int):
+        self.layer = layer
+        self.device = layer.device
+        self.n_slots = int(n_slots)
+        h = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            _check(lib().k3moe_cache_create(layer.handle, self.n_slots, ctypes.byref(h)),
+                   "k3moe_cache_create")
+        self.handle = h
+
+    def workspace_size(self, max_tokens: int) -> int:
+        n = ctypes.c_size_t()
+        _check(lib().k3moe_cache_workspace_size(self.handle, int(max_tokens), ctypes.byref(n)),
+               "k3moe_cache_workspace_size")
+        return n.value
+
+    def workspace(self, max_tokens: int):
+        return torch.empty(self.workspace_size(max_tokens) + 256, dtype=torch.uint8,
+                           device=self.device)
+
+    def forward(self, x, idx, w, out, workspace=None, stream=None):
+        """k3moe_cache_forward: out fp32 [T][H] (written) through the slots."""
+        T = x.shape[0]
+        _dev(x, (2,), "x"), _dev(idx, (4,), "idx"), _dev(w, (4,), "w"), _dev(out, (4,), "out")
+        ws = workspace if workspace is not None else self.workspace(T)
+        p, n = Layer._ws(ws)
+        _check(lib().k3moe_cache_forward(self.handle, x.data_ptr(), T, idx.data_ptr(), w.data_ptr(),
+                                         out.data_ptr(), p, n, _stream(stream, self.device)),
+               "k3moe_cache_forward")
+
+    def stats(self, stream=None) -> dict:
+        st = CacheStats()
+        _check(lib().k3moe_cache_stats_read(self.handle, ctypes.byref(st), _stream(stream, self.device)),
+               "k3moe_cache_stats_read")
+        return {n: getattr(st, n) for n, _ in CacheStats._fields_}
+
+    def slots(self, stream=None):
+        """Expert held by each slot (-1: empty), as a list."""
+        buf = (ctypes.c_int32 * self.n_slots)()
+        _check(lib().k3moe_cache_slots(self.handle, buf, _stream(stream, self.device)),
+               "k3moe_cache_slots")
+        return list(buf)
+
+    def reset(self, stream=None):
+        _check(lib().k3moe_cache_reset(self.handle, _stream(stream, self.device)), "k3moe_cache_reset")
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().k3moe_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -9,7 +9,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libk3moe.so")
 SOURCES = [os.path.join(CSRC, "k3moe_api.cpp"), os.path.join(CSRC, "k3moe_kernels.hip"),
            os.path.join(CSRC, "k3moe_grouped.hip"), os.path.join(CSRC, "k3moe_stream.hip"),
-           os.path.join(CSRC, "k3moe_latent.hip"), os.path.join(CSRC, "k3moe_step.hip")]
+           os.path.join(CSRC, "k3moe_latent.hip"), os.path.join(CSRC, "k3moe_step.hip"),
+           os.path.join(CSRC, "k3moe_cache.hip")]
 HEADERS = [os.path.join(CSRC, "k3moe_internal.h"), os.path.join(ROOT, "include", "k3moe.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

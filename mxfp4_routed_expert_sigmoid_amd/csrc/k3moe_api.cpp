@@ -17,6 +17,21 @@ struct k3moe_layer {
     k3moe::Profiler *prof;       // per-stage event timing (k3moe_profile_*)
 };
 
+struct k3moe_cache {
+    const k3moe_layer *layer;
+    int S;                       // slots
+    int device;
+    const uint8_t *src[6];       // device-visible expert tensors: gate, up, down (packed, scales)
+    int64_t src_stride[6];
+    int64_t seg_len[6], seg_off[6];
+    int64_t slot_bytes, expert_bytes;
+    uint8_t *arena;              // [S][slot_bytes]
+    char *table;                 // counters, slot_of [E], key_of [S], used_at [S]
+    unsigned long long *ctr;
+    int32_t *slot_of, *key_of;
+    long long *used_at;
+};
+
 namespace k3moe {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -234,6 +249,39 @@ static k3moe_status check_call(const k3moe_layer *l, int32_t T, void *ws, size_t
     return K3MOE_OK;
 }
 
+// The layer as the expert kernels see it through a cache: S "experts" (the
+// slots), each tensor at its offset in slot 0 with the slot stride.
+static LayerView cache_view(const k3moe_cache *c)
+{
+    LayerView v = view(c->layer);
+    v.E = c->S;
+    const uint8_t **dst[6] = {&v.gp, &v.gs, &v.up, &v.us, &v.dp, &v.ds};
+    for (int i = 0; i < 6; ++i) *dst[i] = c->arena + c->seg_off[i];
+    v.g_sp = v.g_ss = v.u_sp = v.u_ss = v.d_sp = v.d_ss = c->slot_bytes;
+    return v;
+}
+
+struct CacheWs {
+    WsLayout lay;          // the layer's workspace at S experts
+    size_t remap, fill, nfill, total;
+};
+
+static CacheWs cache_ws(const k3moe_cache *c, int64_t T)
+{
+    k3moe_config cs = c->layer->cfg;
+    cs.n_experts = c->S;
+    CacheWs w;
+    w.lay = ws_layout(cs, T);
+    size_t o = align256(w.lay.total);
+    w.remap = o;
+    o = align256(o + std::max<size_t>(sizeof(int32_t) * T * cs.topk, 1));
+    w.fill = o;
+    o = align256(o + sizeof(int2) * c->S);
+    w.nfill = o;
+    w.total = align256(o + sizeof(int32_t));
+    return w;
+}
+
 }  // namespace k3moe
 
 using namespace k3moe;
@@ -398,6 +446,187 @@ k3moe_status k3moe_profile_read(k3moe_layer *l, double *ms, int64_t *launches, i
     }
     p.recs.clear();
     return st;
+}
+
+k3moe_status k3moe_cache_create(const k3moe_layer *l, int32_t n_slots, k3moe_cache **out)
+{
+    if (!out) return K3MOE_E_INVALID_ARG;
+    *out = nullptr;
+    if (!l || n_slots < 1 || n_slots > l->cfg.n_experts) return K3MOE_E_INVALID_ARG;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return K3MOE_E_HIP;
+    if (dev != l->device) return K3MOE_E_INVALID_ARG;
+    const k3moe_config &c = l->cfg;
+    const int64_t I = c.inter, EK = c.latent ? c.latent : c.hidden, E = c.n_experts;
+    const k3moe_mxfp4 *m[3] = {&l->w.gate, &l->w.up, &l->w.down};
+    const int64_t elems = I * EK;  // every expert matrix has I * EK weights
+    k3moe_cache tmp{};
+    tmp.layer = l;
+    tmp.S = n_slots;
+    tmp.device = dev;
+    int64_t off = 0;
+    for (int i = 0; i < 6; ++i) {
+        const void *p = (i & 1) ? (const void *)m[i / 2]->scales : (const void *)m[i / 2]->packed;
+        hipPointerAttribute_t a{};
+        if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+            (void)hipGetLastError();
+            return K3MOE_E_INVALID_ARG;  // pageable host memory: the device cannot read it
+        }
+        void *dp = nullptr;
+        if (a.type == hipMemoryTypeHost) {  // pinned host pages: their address on the device
+            if (hipHostGetDevicePointer(&dp, const_cast<void *>(p), 0) != hipSuccess) {
+                (void)hipGetLastError();
+                return K3MOE_E_INVALID_ARG;
+            }
+        } else if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) {
+            dp = const_cast<void *>(p);
+        }
+        if (!dp || !aligned(dp, 16)) return K3MOE_E_INVALID_ARG;
+        tmp.src[i] = static_cast<const uint8_t *>(dp);
+        tmp.src_stride[i] = (i & 1) ? m[i / 2]->expert_stride_scales : m[i / 2]->expert_stride_packed;
+        tmp.seg_len[i] = (i & 1) ? elems / 32 : elems / 2;
+        tmp.seg_off[i] = off;
+        off = (int64_t)align256((size_t)(off + tmp.seg_len[i]));
+    }
+    tmp.slot_bytes = off;
+    tmp.expert_bytes = 0;
+    for (int i = 0; i < 6; ++i) tmp.expert_bytes += tmp.seg_len[i];
+    const size_t table = align256(sizeof(unsigned long long) * kCtrCount) + align256(sizeof(int32_t) * E) +
+                         align256(sizeof(int32_t) * n_slots) + align256(sizeof(long long) * n_slots);
+    size_t free_b = 0, total_b = 0;
+    if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) return K3MOE_E_HIP;
+    if ((size_t)tmp.slot_bytes * n_slots + table + ((size_t)1 << 20) > free_b) return K3MOE_E_OUT_OF_MEMORY;
+    k3moe_cache *cc = new (std::nothrow) k3moe_cache(tmp);
+    if (!cc) return K3MOE_E_OUT_OF_MEMORY;
+    if (hipMalloc(&cc->arena, (size_t)cc->slot_bytes * n_slots) != hipSuccess) {
+        delete cc;
+        return K3MOE_E_OUT_OF_MEMORY;
+    }
+    if (hipMalloc(&cc->table, table) != hipSuccess) {
+        (void)hipFree(cc->arena);
+        delete cc;
+        return K3MOE_E_OUT_OF_MEMORY;
+    }
+    size_t o = 0;
+    cc->ctr = reinterpret_cast<unsigned long long *>(cc->table + o);
+    o += align256(sizeof(unsigned long long) * kCtrCount);
+    cc->slot_of = reinterpret_cast<int32_t *>(cc->table + o);
+    o += align256(sizeof(int32_t) * E);
+    cc->key_of = reinterpret_cast<int32_t *>(cc->table + o);
+    o += align256(sizeof(int32_t) * n_slots);
+    cc->used_at = reinterpret_cast<long long *>(cc->table + o);
+    if (launch_cache_init(cc->ctr, cc->slot_of, (int)E, cc->key_of, cc->used_at, n_slots, nullptr) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(cc->table);
+        (void)hipFree(cc->arena);
+        delete cc;
+        return K3MOE_E_HIP;
+    }
+    *out = cc;
+    return K3MOE_OK;
+}
+
+k3moe_status k3moe_cache_workspace_size(const k3moe_cache *c, int32_t max_tokens, size_t *bytes)
+{
+    if (!c || !bytes || max_tokens < 0) return K3MOE_E_INVALID_ARG;
+    if (!batch_fits(c->layer->cfg, max_tokens)) return K3MOE_E_UNSUPPORTED_SHAPE;
+    *bytes = cache_ws(c, max_tokens).total;
+    return K3MOE_OK;
+}
+
+k3moe_status k3moe_cache_forward(k3moe_cache *c, const uint16_t *x, int32_t T, const int32_t *idx,
+                                 const float *w, float *out, void *ws, size_t ws_bytes, void *stream)
+{
+    if (!c || T < 0) return K3MOE_E_INVALID_ARG;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return K3MOE_E_HIP;
+    if (dev != c->device) return K3MOE_E_INVALID_ARG;
+    if (T == 0) return K3MOE_OK;
+    const k3moe_config &cfg = c->layer->cfg;
+    if (!batch_fits(cfg, T)) return K3MOE_E_UNSUPPORTED_SHAPE;
+    if (!x || !idx || !w || !out) return K3MOE_E_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(idx, 4) || !aligned(w, 4) || !aligned(out, 16)) return K3MOE_E_ALIGNMENT;
+    const CacheWs cw = cache_ws(c, T);
+    if (!ws || !aligned(ws, 256) || ws_bytes < cw.total) return K3MOE_E_WORKSPACE;
+    char *wsc = static_cast<char *>(ws);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t n = (int64_t)T * cfg.topk;
+    CachePlanParams pp{};
+    pp.idx = idx;
+    pp.n = n;
+    pp.E = cfg.n_experts;
+    pp.S = c->S;
+    pp.expert_bytes = c->expert_bytes;
+    pp.slot_of = c->slot_of;
+    pp.key_of = c->key_of;
+    pp.used_at = c->used_at;
+    pp.ctr = c->ctr;
+    pp.remap = reinterpret_cast<int32_t *>(wsc + cw.remap);
+    pp.fill = reinterpret_cast<int2 *>(wsc + cw.fill);
+    pp.nfill = reinterpret_cast<int32_t *>(wsc + cw.nfill);
+    CacheFillParams fp{};
+    fp.fill = pp.fill;
+    fp.nfill = pp.nfill;
+    for (int i = 0; i < 6; ++i) {
+        fp.src[i] = c->src[i];
+        fp.src_stride[i] = c->src_stride[i];
+        fp.seg_len[i] = c->seg_len[i];
+        fp.seg_off[i] = c->seg_off[i];
+    }
+    fp.arena = c->arena;
+    fp.slot_bytes = c->slot_bytes;
+    fp.expert_bytes = c->expert_bytes;
+    fp.nchunk = (int)((c->expert_bytes + kFillChunk - 1) / kFillChunk);
+    const int max_fill = (int)std::min<int64_t>(c->S, std::min<int64_t>(cfg.n_experts, n));
+    if (launch_cache_plan_fill(pp, fp, max_fill, st, c->layer->prof) != hipSuccess) return K3MOE_E_HIP;
+    if (launch_forward(cache_view(c), x, T, pp.remap, w, out, wsc, cw.lay, st, c->layer->prof) != hipSuccess)
+        return K3MOE_E_HIP;
+    return K3MOE_OK;
+}
+
+k3moe_status k3moe_cache_stats_read(const k3moe_cache *c, k3moe_cache_stats *out, void *stream)
+{
+    if (!c || !out) return K3MOE_E_INVALID_ARG;
+    unsigned long long v[kCtrCount];
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(v, c->ctr, sizeof v, hipMemcpyDeviceToHost, st) != hipSuccess) return K3MOE_E_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return K3MOE_E_HIP;
+    out->steps = v[kCtrSteps];
+    out->requests = v[kCtrRequests];
+    out->resident_hits = v[kCtrHits];
+    out->misses = v[kCtrMisses];
+    out->evictions = v[kCtrEvictions];
+    out->dropped = v[kCtrDropped];
+    out->bytes_read = v[kCtrBytes];
+    return K3MOE_OK;
+}
+
+k3moe_status k3moe_cache_slots(const k3moe_cache *c, int32_t *slots, void *stream)
+{
+    if (!c || !slots) return K3MOE_E_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(slots, c->key_of, sizeof(int32_t) * c->S, hipMemcpyDeviceToHost, st) != hipSuccess)
+        return K3MOE_E_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return K3MOE_E_HIP;
+    return K3MOE_OK;
+}
+
+k3moe_status k3moe_cache_reset(k3moe_cache *c, void *stream)
+{
+    if (!c) return K3MOE_E_INVALID_ARG;
+    if (launch_cache_init(c->ctr, c->slot_of, c->layer->cfg.n_experts, c->key_of, c->used_at, c->S,
+                          static_cast<hipStream_t>(stream)) != hipSuccess)
+        return K3MOE_E_HIP;
+    return K3MOE_OK;
+}
+
+void k3moe_cache_destroy(k3moe_cache *c)
+{
+    if (!c) return;
+    (void)hipDeviceSynchronize();
+    (void)hipFree(c->table);
+    (void)hipFree(c->arena);
+    delete c;
 }
 
 void k3moe_layer_destroy(k3moe_layer *l)

@@ -134,6 +134,51 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T,
                           const int32_t *idx, const float *w, float *out, char *ws,
                           const WsLayout &lay, hipStream_t s, Profiler *prof, const OutEpi &epi = OutEpi());
 
+// Expert slot cache (k3moe_cache.hip). Device counters, in this order:
+enum {
+    kCtrTick = 0,      // last use stamp handed out
+    kCtrSteps,         // plans run
+    kCtrRequests,      // distinct experts asked for
+    kCtrHits,          // of those, resident when the plan began
+    kCtrMisses,        // read into a slot
+    kCtrEvictions,     // misses that displaced a resident expert
+    kCtrDropped,       // requests that found no slot
+    kCtrBytes,         // bytes read from host memory
+    kCtrCount = 16
+};
+constexpr int kCacheSlotBits = 13;           // slot index bits of a victim key (slots <= 4096)
+constexpr int64_t kFillChunk = 256 * 1024;   // bytes per fill block
+
+struct CachePlanParams {
+    const int32_t *idx;  // assignments [n] (expert ids)
+    int64_t n;
+    int E, S;
+    int64_t expert_bytes;
+    int32_t *slot_of;    // [E] device table
+    int32_t *key_of;     // [S]
+    long long *used_at;  // [S]
+    unsigned long long *ctr;
+    int32_t *remap;      // [n] out: slot ids
+    int2 *fill;          // [S] out: (expert, slot)
+    int32_t *nfill;      // out
+};
+struct CacheFillParams {
+    const int2 *fill;
+    const int32_t *nfill;
+    const uint8_t *src[6];     // device-visible base of each tensor (expert 0)
+    int64_t src_stride[6];     // bytes between experts
+    int64_t seg_len[6];        // bytes per expert
+    int64_t seg_off[6];        // offset in a slot
+    uint8_t *arena;
+    int64_t slot_bytes, expert_bytes;
+    int nchunk;
+};
+size_t cache_plan_lds_bytes(int E, int S);
+hipError_t launch_cache_init(unsigned long long *ctr, int32_t *slot_of, int E, int32_t *key_of, long long *used_at,
+                             int S, hipStream_t s);
+hipError_t launch_cache_plan_fill(const CachePlanParams &pp, const CacheFillParams &fp, int max_fill,
+                                  hipStream_t s, Profiler *prof);
+
 // Pre-MoE norm (k3moe_step.hip): x[t] = bf16_RNE(RMSNorm(h[t]) * gamma).
 hipError_t launch_prenorm(const float *h, int T, int H, const float *gamma, float eps, uint16_t *x, hipStream_t s);
 
