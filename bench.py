@@ -19,6 +19,10 @@ shared expert of inter 1536, bias N(0, 0.01)):
   step     T = 1 through k3moe_step on the full shape: the decoder layer's
            pre-MoE RMSNorm of an fp32 residual stream into bf16 tokens, route,
            experts, the residual add fused into the last kernel
+  cache    T = 1 on the full shape with the 896 experts in pinned host memory
+           and --slots of them in an HBM slot arena (k3moe_cache_forward):
+           misses are read over the host link each step; --routing picks
+           flat (normal) or Zipf(1.1) routes; reports the resident hit rate
 Steps rotate over a pool of token batches so consecutive steps select
 different experts (the 281 MB a decode step touches is not left in the
 256 MB last-level cache by the previous step).
@@ -44,6 +48,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "routed-expert HBM GB/s (decode) and tokens/s per MoE layer, % of roofline"
 HBM_PEAK_GBPS = 8000.0
+HOST_LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction
 STEP_EPS = 1e-5  # the pre-MoE norm's epsilon (the pages' rms_eps)
 EXPERT_MATRIX_BYTES = None  # filled from the spec
 
@@ -61,10 +66,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", choices=("decode", "batched", "prefill", "latent", "step"), default="decode")
+    ap.add_argument("--workload", choices=("decode", "batched", "prefill", "latent", "step", "cache"), default="decode")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--slots", type=int, default=224, help="cache: HBM expert slots")
+    ap.add_argument("--routing", choices=("normal", "zipf"), default=None,
+                    help="cache: routing of the token pool (default normal)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the layer is measured "
@@ -83,7 +91,9 @@ def main():
     torch.cuda.set_device(0)
     T, routing, pool = {"decode": (1, "normal", 64), "batched": (64, "normal", 8),
                         "prefill": (2048, "zipf", 2), "latent": (1, "normal", 64),
-                        "step": (1, "normal", 64)}[args.workload]
+                        "step": (1, "normal", 64), "cache": (1, "normal", 256)}[args.workload]
+    if args.workload == "cache" and args.routing:
+        routing = args.routing
     if args.workload == "latent":
         spec = synth.pages_latent_spec(seed=0, routing=routing)
     else:
@@ -93,9 +103,25 @@ def main():
     log(f"[bench] building layer: {E} experts x {spec.expert_bytes} B resident")
     tens = sd.layer_tensors(spec, 0, dev)
     layer = sd.make_layer(spec, tens)
+    cache = None
+    if args.workload == "cache":
+        # the routed experts move to pinned host memory; HBM keeps --slots of them
+        host = dict(tens)
+        for k in ("gate_packed", "gate_scales", "up_packed", "up_scales", "down_packed", "down_scales"):
+            h = torch.empty(tens[k].shape, dtype=tens[k].dtype, pin_memory=True)
+            h.copy_(tens[k])
+            host[k] = h
+        torch.cuda.synchronize()
+        layer.close()
+        del layer
+        tens = host
+        torch.cuda.empty_cache()
+        layer = sd.make_layer(spec, tens)
+        cache = k3.Cache(layer, args.slots)
+        log(f"[bench] experts in pinned host memory, {args.slots} HBM slots")
     xs_np = [synth.make_x(spec, T, attempt=100 + p) for p in range(pool)]
     xs = [sd.bf16_tensor(x, dev) for x in xs_np]
-    ws = layer.workspace(T)
+    ws = layer.workspace(T) if cache is None else cache.workspace(T)
     idx = torch.empty((T, K), dtype=torch.int32, device=dev)
     w = torch.empty((T, K), dtype=torch.float32, device=dev)
     out = torch.empty((T, H), dtype=torch.float32, device=dev)
@@ -119,6 +145,9 @@ def main():
             return
         x = xs[i % pool]
         layer.route(x, idx, w, workspace=ws, stream=stream)
+        if cache is not None:
+            cache.forward(x, idx, w, out, workspace=ws, stream=stream)
+            return
         layer.forward(x, idx, w, out, workspace=ws, stream=stream)
 
     # distinct experts per pool entry (for the algorithmic byte counts)
@@ -129,8 +158,15 @@ def main():
         distinct.append(len(set(idx.cpu().numpy().ravel().tolist())))
     assert layer.error_count() == 0
 
-    for i in range(args.warmup):
-        step(i)
+    if cache is not None:
+        # fill the arena and reach the steady state before timing
+        for i in range(max(args.warmup, 4 * E // K)):
+            step(i)
+        torch.cuda.synchronize()
+        c0 = cache.stats()
+    else:
+        for i in range(args.warmup):
+            step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -139,6 +175,9 @@ def main():
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
     log(f"[bench] timed {args.steps} steps: {ms:.4f} ms/step")
+    if cache is not None:
+        c1 = cache.stats()
+        cd = {k: c1[k] - c0[k] for k in c1}
 
     # second pass with per-stage events (same steps)
     layer.profile(True)
@@ -170,6 +209,8 @@ def main():
     }
     if args.workload == "step":
         stage_bytes["prenorm"] = T * H * 4 + H * 4 + T * H * 2
+    if cache is not None:
+        stage_bytes = {"cache_fill": cd["bytes_read"] / max(1, cd["steps"])}
     if Lt:
         stage_bytes["latent_in"] = Lt * H * 2 + T * H * 2 + T * Lt * 4
         stage_bytes["latent_out"] = H * Lt * 2 + Lt * 4 + T * Lt * 12 + T * H * 8
@@ -178,9 +219,11 @@ def main():
                "prefill": {"gateup": "k_gu_gemm + k_gu_stream", "down": "k_dn_gemm + k_dn_stream"},
                "latent": {"gateup": "k_gu_stream", "down": "k_dn_stream", "latent_in": "k_proj",
                           "latent_out": "k_proj + k_rms_split"},
-               "step": {"gateup": "k_gateup_dec", "down": "k_down_dec", "prenorm": "k_prenorm"}}[args.workload]
+               "step": {"gateup": "k_gateup_dec", "down": "k_down_dec", "prenorm": "k_prenorm"},
+               "cache": {"cache_fill": "k_cache_fill"}}[args.workload]
     dom = max(stage_bytes, key=lambda s: stage_us[s])
-    achieved = stage_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9
+    achieved = stage_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9 if stage_us[dom] > 0 else 0.0
+    peak = HBM_PEAK_GBPS if cache is None else HOST_LINK_PEAK_GBPS
     traffic = measured_traffic(kernels[dom])
     value = routed_bytes / (ms * 1e-3) / 1e9
     layer_bytes = routed_bytes + router_bytes + shared_bytes + proj_bytes + T * H * 2 + T * H * 4
@@ -216,16 +259,27 @@ def main():
         "stage_us": {k: round(v, 3) for k, v in stage_us.items()},
         "roofline": {
             "kernel": kernels[dom],
-            "bound": "hbm",
+            "bound": "hbm" if cache is None else "host link (PCIe 5.0 x16)",
             "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBPS,
+            "peak": peak,
             "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "frac": round(achieved / peak, 4),
             "bytes_per_launch": round(stage_bytes[dom]),
             "traffic": traffic,
         },
     }
 
+    if cache is not None:
+        result["config"]["workload"] += f", experts in pinned host memory, {args.slots} HBM slots"
+        result["cache"] = {
+            "slots": args.slots,
+            "requests_per_step": round(cd["requests"] / cd["steps"], 3),
+            "resident_hit_rate": round(cd["resident_hits"] / max(1, cd["requests"]), 4),
+            "retention": round(1 - cd["evictions"] / max(1, cd["requests"]), 4),
+            "host_bytes_per_step": round(cd["bytes_read"] / cd["steps"]),
+            "dropped": cd["dropped"],
+            "slots_over_experts": round(args.slots / E, 4),
+        }
     if not args.no_cpu_baseline:
         if args.workload == "step":
             result["cpu_baseline"] = cpu_baseline(spec, hs_np, T, args.cpu_seconds, expert_b,

@@ -278,7 +278,8 @@ typedef struct {
  * not fit. */
 k3moe_status k3moe_cache_create(const k3moe_layer *layer, int32_t n_slots, k3moe_cache **out);
 
-/* Workspace bytes of k3moe_cache_forward for up to max_tokens tokens. */
+/* Workspace bytes of k3moe_cache_forward for up to max_tokens tokens (also
+ * enough for k3moe_route and k3moe_forward of the cache's layer). */
 k3moe_status k3moe_cache_workspace_size(const k3moe_cache *cache, int32_t max_tokens, size_t *bytes);
 
 /* The layer's expert forward through the cache (steps above).

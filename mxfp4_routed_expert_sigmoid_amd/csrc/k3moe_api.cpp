@@ -530,7 +530,8 @@ k3moe_status k3moe_cache_workspace_size(const k3moe_cache *c, int32_t max_tokens
 {
     if (!c || !bytes || max_tokens < 0) return K3MOE_E_INVALID_ARG;
     if (!batch_fits(c->layer->cfg, max_tokens)) return K3MOE_E_UNSUPPORTED_SHAPE;
-    *bytes = cache_ws(c, max_tokens).total;
+    // enough for the layer's own route/forward too, so one workspace serves a step
+    *bytes = std::max(cache_ws(c, max_tokens).total, ws_layout(c->layer->cfg, max_tokens).total);
     return K3MOE_OK;
 }
 
