@@ -246,6 +246,176 @@ __global__ __launch_bounds__(256) void k_rms_split(const float *__restrict__ acc
     }
 }
 
+// ---------------------------------------------------------------------------
+// One token: both projections as streaming matrix-vector products with fp32
+// FMA (a one-column product leaves the MFMA nothing to gain). A wave owns RW
+// consecutive weight rows over the whole K range, walked in slices of 512
+// (16 bytes = 8 weights of each row per lane), kGvDepth slices in flight;
+// the per-lane sums are reduced across the wave at the end. The token side
+// (the bf16 x, or the normed fp32 aggregate) is read per slice and stays in
+// the caches.
+constexpr int kGvWaves = 4;
+constexpr int kGvDepth = 4;    // slices in flight per wave
+constexpr int kGvSlice = 512;  // K per slice (64 lanes x 8)
+
+__device__ __forceinline__ float gv_wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Rows row0 .. row0 + RW - 1 (clamped to R) of W [R][K] times the token:
+// NORMED = false: bf16 x [K]; NORMED = true: fp32 a[k] * inv * gamma[k]
+// (gamma null: a[k] * inv). inv is computed by the block (fp64 sum of
+// squares, epsilon inside the root) after the first weight slices are in
+// flight, when want_norm is set; every block computes the same value.
+template <int RW, bool NORMED>
+__device__ __forceinline__ void gv_rows(const uint16_t *__restrict__ W, int R, int K, int row0,
+                                        const uint16_t *__restrict__ x, const float *__restrict__ a,
+                                        const float *__restrict__ gamma, bool want_norm, float eps,
+                                        float (&acc)[RW])
+{
+    __shared__ double red[kGvWaves];
+    __shared__ float inv_sh;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int NS = (K + kGvSlice - 1) / kGvSlice;
+    const uint16_t *wr[RW];
+#pragma unroll
+    for (int q = 0; q < RW; ++q) {
+        wr[q] = W + (size_t)min(row0 + q, R - 1) * K;
+        acc[q] = 0.0f;
+    }
+    u4 buf[kGvDepth][RW];
+    auto load = [&](int sl, u4(&b)[RW]) {
+        const int i = min(sl * kGvSlice + lane * 8, K - 8);
+#pragma unroll
+        for (int q = 0; q < RW; ++q) b[q] = *reinterpret_cast<const u4 *>(wr[q] + i);
+    };
+#pragma unroll
+    for (int d = 0; d < kGvDepth; ++d) load(min(d, NS - 1), buf[d]);
+
+    float inv = 1.0f;
+    if constexpr (NORMED) {
+        if (want_norm) {
+            double ss = 0.0;
+            for (int l4 = tid; l4 < K / 4; l4 += 64 * kGvWaves) {
+                const float4 v = reinterpret_cast<const float4 *>(a)[l4];
+                ss = fma((double)v.x, (double)v.x, ss);
+                ss = fma((double)v.y, (double)v.y, ss);
+                ss = fma((double)v.z, (double)v.z, ss);
+                ss = fma((double)v.w, (double)v.w, ss);
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+            if (lane == 0) red[tid >> 6] = ss;
+            __syncthreads();
+            if (tid == 0) {
+                double t = 0.0;
+#pragma unroll
+                for (int w = 0; w < kGvWaves; ++w) t += red[w];
+                inv_sh = (float)(1.0 / sqrt(t / (double)K + (double)eps));
+            }
+            __syncthreads();
+            inv = inv_sh;
+        }
+    }
+
+    for (int s0 = 0; s0 < NS; s0 += kGvDepth) {
+#pragma unroll
+        for (int d = 0; d < kGvDepth; ++d) {
+            const int sl = s0 + d;
+            if (sl < NS) {
+                const int i = sl * kGvSlice + lane * 8;
+                const int ic = min(i, K - 8);
+                float xv[8];
+                if constexpr (NORMED) {
+                    const float4 a0 = *reinterpret_cast<const float4 *>(a + ic);
+                    const float4 a1 = *reinterpret_cast<const float4 *>(a + ic + 4);
+                    xv[0] = a0.x * inv; xv[1] = a0.y * inv; xv[2] = a0.z * inv; xv[3] = a0.w * inv;
+                    xv[4] = a1.x * inv; xv[5] = a1.y * inv; xv[6] = a1.z * inv; xv[7] = a1.w * inv;
+                    if (gamma) {
+                        const float4 g0 = *reinterpret_cast<const float4 *>(gamma + ic);
+                        const float4 g1 = *reinterpret_cast<const float4 *>(gamma + ic + 4);
+                        xv[0] *= g0.x; xv[1] *= g0.y; xv[2] *= g0.z; xv[3] *= g0.w;
+                        xv[4] *= g1.x; xv[5] *= g1.y; xv[6] *= g1.z; xv[7] *= g1.w;
+                    }
+                } else {
+                    const u4 xb = *reinterpret_cast<const u4 *>(x + ic);
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        xv[2 * h] = bf16f(xb[h] & 0xffffu);
+                        xv[2 * h + 1] = bf16f(xb[h] >> 16);
+                    }
+                }
+                if (i >= K)  // a clamped copy past the row end adds nothing
+#pragma unroll
+                    for (int h = 0; h < 8; ++h) xv[h] = 0.0f;
+#pragma unroll
+                for (int q = 0; q < RW; ++q)
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        acc[q] = fmaf(bf16f(buf[d][q][h] & 0xffffu), xv[2 * h], acc[q]);
+                        acc[q] = fmaf(bf16f(buf[d][q][h] >> 16), xv[2 * h + 1], acc[q]);
+                    }
+            }
+            load(min(sl + kGvDepth, NS - 1), buf[d]);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < RW; ++q) acc[q] = gv_wave_sum(acc[q]);
+}
+
+// z = W_d x for one token, written as the bf16 hi and lo planes the experts read.
+template <int RW>
+__global__ __launch_bounds__(64 * kGvWaves) void k_gv_down(const uint16_t *__restrict__ W, const uint16_t *__restrict__ x,
+                                                           int R, int K, uint16_t *__restrict__ hi,
+                                                           uint16_t *__restrict__ lo)
+{
+    const int lane = threadIdx.x & 63, row0 = (blockIdx.x * kGvWaves + (threadIdx.x >> 6)) * RW;
+    float acc[RW];
+    gv_rows<RW, false>(W, R, K, row0, x, nullptr, nullptr, false, 0.0f, acc);
+#pragma unroll
+    for (int q = 0; q < RW; ++q)
+        if (lane == q && row0 + q < R) {
+            const uint16_t h = bf16_rne(acc[q]);
+            hi[row0 + q] = h;
+            lo[row0 + q] = bf16_rne(acc[q] - bf16f(h));
+        }
+}
+
+// out = W_u (RMSNorm(acc) or acc) for one token, then the addend's AS slices
+// in order (the shared expert's K-slice partials, stride astride), then the
+// epilogue (residual add, bf16 copy) as in k_proj_finish.
+template <int RW>
+__global__ __launch_bounds__(64 * kGvWaves) void k_gv_up(const uint16_t *__restrict__ W, const float *__restrict__ a,
+                                                         const float *__restrict__ gamma, int norm, float eps, int R,
+                                                         int K, const float *__restrict__ addend, int AS,
+                                                         int64_t astride, float *__restrict__ out, int resid,
+                                                         uint16_t *__restrict__ ob)
+{
+    const int lane = threadIdx.x & 63, row0 = (blockIdx.x * kGvWaves + (threadIdx.x >> 6)) * RW;
+    float acc[RW];
+    gv_rows<RW, true>(W, R, K, row0, nullptr, a, norm ? gamma : nullptr, norm != 0, eps, acc);
+#pragma unroll
+    for (int q = 0; q < RW; ++q)
+        if (lane == q && row0 + q < R) {
+            const int r = row0 + q;
+            float v = acc[q];
+            if (addend) {
+                float ad = addend[r];
+                for (int s = 1; s < AS; ++s) ad += addend[(size_t)s * astride + r];
+                v += ad;
+            }
+            if (resid) v = out[r] + v;
+            out[r] = v;
+            if (ob) ob[r] = bf16_rne(v);
+        }
+}
+
+constexpr int kGvDownRows = 2;  // rows per wave: R = 3584 gives 448 blocks
+constexpr int kGvUpRows = 4;    // R = 7168 gives 448 blocks
+
 // out = W (planes) as fp32 [T][R] (+ addend), or as bf16 hi/lo planes.
 static hipError_t launch_proj(const uint16_t *W, const uint16_t *p0, const uint16_t *p1, int T, int R, int Kd,
                               float *part, const float *addend, int AS, float *out, uint16_t *hi, uint16_t *lo,
@@ -299,10 +469,17 @@ hipError_t launch_latent_forward(const LayerView &L, const uint16_t *x, int T, c
     float *part = reinterpret_cast<float *>(ws + lay.lat_part);
     float *ys = reinterpret_cast<float *>(ws + lay.ys);
     hipError_t e;
+    const bool one = T == 1;  // one token: the projections as streaming GEMVs
     {
         StageMark m(prof, K3MOE_STAGE_LATENT_IN, s);  // z = Wd x, as bf16 hi and lo
-        if ((e = launch_proj(L.lat_down, x, nullptr, T, Lt, L.H, part, nullptr, 1, nullptr, zh, zl, s)) != hipSuccess)
+        if (one) {
+            const int rpb = kGvWaves * kGvDownRows;
+            k_gv_down<kGvDownRows><<<(unsigned)((Lt + rpb - 1) / rpb), 64 * kGvWaves, 0, s>>>(L.lat_down, x, Lt,
+                                                                                            L.H, zh, zl);
+        } else if ((e = launch_proj(L.lat_down, x, nullptr, T, Lt, L.H, part, nullptr, 1, nullptr, zh, zl, s)) !=
+                   hipSuccess) {
             return e;
+        }
     }
     launch_perm(L, idx, T, ws, lay, s, prof);
     uint16_t *act_hi = reinterpret_cast<uint16_t *>(ws + lay.act);
@@ -322,6 +499,13 @@ hipError_t launch_latent_forward(const LayerView &L, const uint16_t *x, int T, c
     }
     {
         StageMark m(prof, K3MOE_STAGE_LATENT_OUT, s);  // norm, then out = Wu acc (+ shared)
+        if (one) {
+            const int rpb = kGvWaves * kGvUpRows;
+            k_gv_up<kGvUpRows><<<(unsigned)((L.H + rpb - 1) / rpb), 64 * kGvWaves, 0, s>>>(
+                L.lat_up, acc, L.lat_norm, L.lat_norm_on, L.lat_eps, L.H, Lt, ysh, ysh_slices, (int64_t)L.H, out,
+                epi.resid, epi.ob);
+            return hipGetLastError();
+        }
         if (L.lat_norm_on)
             k_rms_split<true><<<(unsigned)T, 256, 0, s>>>(acc, Lt, L.lat_norm, L.lat_eps, nh, nl);
         else

@@ -85,6 +85,34 @@ __device__ __forceinline__ float act_fn(float g, float u, int kind, float b1, fl
     return g * sg * u;
 }
 
+// An item's LDS header: per column c < 16 its token (key), the row its
+// operand comes from (val), its output row (out), its staged row (cmap); per
+// staged row r its source row (src); the staged row count. Columns with the
+// same token share one staged row: a token naming an expert twice gets the
+// same activations twice, so one staged row per distinct token is exact and
+// an item never needs more than min(T, 16) of them.
+constexpr int kHdrKey = 0, kHdrVal = 16, kHdrOut = 32, kHdrMap = 48, kHdrSrc = 64, kHdrN = 80;
+constexpr int kHdrBytes = 96 * 4;
+
+// Wave 0 (call between barriers): the staged rows of an item whose n
+// columns carry non-decreasing keys (the stable sort keeps an expert's
+// assignments in token order; a shared item's tokens are consecutive).
+__device__ __forceinline__ void item_rows(int *hdr, int n)
+{
+    if (threadIdx.x < 64) {
+        const int c = threadIdx.x;
+        const bool in = c < n;
+        const bool head = in && (c == 0 || hdr[kHdrKey + c] != hdr[kHdrKey + c - 1]);
+        const uint64_t m = __ballot(head);
+        if (in) {
+            const int r = __popcll(m & ((2ull << c) - 1ull)) - 1;
+            hdr[kHdrMap + c] = r;
+            if (head) hdr[kHdrSrc + r] = hdr[kHdrVal + c];
+        }
+        if (c == 0) hdr[kHdrN] = __popcll(m);
+    }
+}
+
 // K elements per group and token-row bytes per group.
 template <bool FP4> constexpr int group_k() { return FP4 ? 128 * kSChunks : 8 * 4 * kSChunks; }
 template <bool FP4> constexpr int brow_bytes() { return group_k<FP4>() * 2 + kSPad; }
@@ -106,13 +134,17 @@ struct GuStreamParams {
     int sh_slices;            // hidden-dimension slices of a shared block (1: whole K)
     float *sh_part;           // sh_slices > 1: fp32 partial sums [slice][T][gate, up][I_s]
     uint16_t *act_hi, *act_lo, *ash_hi, *ash_lo;
+    int stg;                  // token rows per plane and buffer in LDS (min(16, T): no item has more)
 };
 
-// np: token planes (1, or 2 when the routed tokens come as bf16 hi and lo)
-constexpr int gu_stream_lds_bytes(int np) { return 2 * np * kSTok * brow_bytes<true>() + kSTok * 4; }
+// np: token planes (1, or 2 when the routed tokens come as bf16 hi and lo);
+// stg: token rows staged per plane and buffer
+constexpr int gu_stream_lds_bytes(int np, int stg) { return 2 * np * stg * brow_bytes<true>() + kHdrBytes; }
 
 // The wave's part of one block: gate and up rows row0 + 16 rf + l16 (rf = 0, 1)
-// of an item with token rows tok_l[0..15] (clamped to the item's tokens),
+// of an item of n columns whose distinct tokens hdr[kHdrSrc + r] (r <
+// hdr[kHdrN] <= p.stg) are staged; column c reads staged row hdr[kHdrMap +
+// c] (columns past n read the last column's and are never stored),
 // over the K groups [g0, g1). The tokens are NP bf16 planes of width KW
 // (xp[0], xp[1]: hi and lo of an fp32 input, multiplied into one
 // accumulator). part == null: the activation goes to ohi/olo rows orow0 +
@@ -121,7 +153,7 @@ constexpr int gu_stream_lds_bytes(int np) { return 2 * np * kSTok * brow_bytes<t
 template <bool FP4, int NP>
 __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const uint8_t *wg, const uint8_t *wu,
                                                 const uint8_t *sg, const uint8_t *su, int rows, int row0,
-                                                const int *tok_l, int n, uint8_t *B_l, uint16_t *ohi,
+                                                const int *hdr, int n, uint8_t *B_l, uint16_t *ohi,
                                                 uint16_t *olo, int64_t orow0, int ostride, int g0, int g1,
                                                 float *part, const uint16_t *x0, const uint16_t *x1, int KW)
 {
@@ -130,6 +162,8 @@ __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const u
     constexpr int BU4 = GK * 2 / 16;                           // u4 per token row per group
     constexpr int NB = (kSTok * BU4 + 64 * kSWaves - 1) / (64 * kSWaves);  // staging u4 per thread and plane
     const int H = KW, tid = threadIdx.x, lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+    const int stg = p.stg, nv = hdr[kHdrN] * BU4;  // staged rows per plane; u4 of the staged rows
+    const int brow = hdr[kHdrMap + min(l16, n - 1)];  // the staged row of this lane's B column
     const size_t rowb = FP4 ? (size_t)H / 2 : (size_t)H * 2;
     const uint8_t *wr[2][2];
     const uint8_t *sr[2][2] = {{nullptr, nullptr}, {nullptr, nullptr}};
@@ -167,11 +201,11 @@ __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const u
 #pragma unroll
         for (int pl = 0; pl < NP; ++pl)
 #pragma unroll
-            for (int q = 0; q < NB; ++q) {
-                const int v = min(tid + 64 * kSWaves * q, kSTok * BU4 - 1);
+            for (int q = 0; q < NB; ++q) {  // unconditional (clamped) loads keep the wait counts exact
+                const int v = min(tid + 64 * kSWaves * q, nv - 1);
                 const int col = v / BU4, seg = v - col * BU4;
-                xs[pl][q] = *reinterpret_cast<const u4 *>(xb[pl] + ((size_t)tok_l[col] * H + (size_t)gc * GK) * 2 +
-                                                           16 * seg);
+                xs[pl][q] = *reinterpret_cast<const u4 *>(
+                    xb[pl] + ((size_t)hdr[kHdrSrc + col] * H + (size_t)gc * GK) * 2 + 16 * seg);
             }
     };
     auto xstore = [&](int buf) {
@@ -180,9 +214,9 @@ __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const u
 #pragma unroll
             for (int q = 0; q < NB; ++q) {
                 const int v = tid + 64 * kSWaves * q;
-                if (v < kSTok * BU4) {
+                if (v < nv) {
                     const int col = v / BU4, seg = v - col * BU4;
-                    *reinterpret_cast<u4 *>(B_l + ((buf * NP + pl) * kSTok + col) * BROW + 16 * seg) = xs[pl][q];
+                    *reinterpret_cast<u4 *>(B_l + ((buf * NP + pl) * stg + col) * BROW + 16 * seg) = xs[pl][q];
                 }
             }
     };
@@ -194,7 +228,7 @@ __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const u
         for (int rf = 0; rf < 2; ++rf) acc[m][rf] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
     auto compute = [&](const Grp &b, int buf) {
-        const uint8_t *Bb = B_l + (buf * NP * kSTok + l16) * BROW;
+        const uint8_t *Bb = B_l + (buf * NP * stg + brow) * BROW;
 #pragma unroll
         for (int c = 0; c < kSChunks; ++c) {
             float sc[2][2];
@@ -211,7 +245,7 @@ __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const u
                 bf8 bv[NP];
 #pragma unroll
                 for (int pl = 0; pl < NP; ++pl)
-                    bv[pl] = as_bf8(*reinterpret_cast<const u4 *>(Bb + pl * kSTok * BROW + 2 * kb));
+                    bv[pl] = as_bf8(*reinterpret_cast<const u4 *>(Bb + pl * stg * BROW + 2 * kb));
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -290,8 +324,8 @@ __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const u
 __global__ __launch_bounds__(64 * kSWaves) void k_gu_stream(GuStreamParams p)
 {
     extern __shared__ __align__(16) uint8_t lds[];
-    int *tok_l = reinterpret_cast<int *>(lds);
-    uint8_t *B_l = lds + kSTok * 4;
+    int *hdr = reinterpret_cast<int *>(lds);
+    uint8_t *B_l = lds + kHdrBytes;
     const int wave = threadIdx.x >> 6;
     int b = blockIdx.x;
     if (b < p.sh_blocks) {  // shared expert: token group tg, rows [rb*128, rb*128 + 128) of I_s, slice ks
@@ -300,11 +334,13 @@ __global__ __launch_bounds__(64 * kSWaves) void k_gu_stream(GuStreamParams p)
         const int tg = tb / RB, rb = tb - tg * RB;
         const int t0 = tg * kSTok, n = min(kSTok, p.T - t0);
         const int NG = p.H / group_k<false>();
-        if (threadIdx.x < kSTok) tok_l[threadIdx.x] = t0 + min((int)threadIdx.x, n - 1);
+        if (threadIdx.x < kSTok) hdr[kHdrKey + threadIdx.x] = hdr[kHdrVal + threadIdx.x] = t0 + min((int)threadIdx.x, n - 1);
+        __syncthreads();
+        item_rows(hdr, n);
         __syncthreads();
         gu_stream_block<false, 1>(p, reinterpret_cast<const uint8_t *>(p.sh_gate),
                                   reinterpret_cast<const uint8_t *>(p.sh_up), nullptr, nullptr, p.Is,
-                                  rb * kSBlkRows + wave * kSRows, tok_l, n, B_l, p.ash_hi, p.ash_lo, t0, p.Is,
+                                  rb * kSBlkRows + wave * kSRows, hdr, n, B_l, p.ash_hi, p.ash_lo, t0, p.Is,
                                   NG * ks / S, NG * (ks + 1) / S,
                                   S > 1 ? p.sh_part + (size_t)ks * p.T * 2 * p.Is : nullptr, p.x, nullptr, p.H);
         return;
@@ -315,15 +351,18 @@ __global__ __launch_bounds__(64 * kSWaves) void k_gu_stream(GuStreamParams p)
     if (li >= *p.light_n) return;
     const int q = p.light[li], e = p.active_e[q];
     const int off = p.active_off[q], n = p.active_off[q + 1] - off;
-    if (threadIdx.x < kSTok) tok_l[threadIdx.x] = p.sorted[off + min((int)threadIdx.x, n - 1)] / p.K;
+    if (threadIdx.x < kSTok)
+        hdr[kHdrKey + threadIdx.x] = hdr[kHdrVal + threadIdx.x] = p.sorted[off + min((int)threadIdx.x, n - 1)] / p.K;
+    __syncthreads();
+    item_rows(hdr, n);
     __syncthreads();
     if (p.xr_lo)
         gu_stream_block<true, 2>(p, p.gp + e * p.g_sp, p.up + e * p.u_sp, p.gs + e * p.g_ss, p.us + e * p.u_ss,
-                                 p.I, rb * kSBlkRows + wave * kSRows, tok_l, n, B_l, p.act_hi, p.act_lo, off, p.I,
+                                 p.I, rb * kSBlkRows + wave * kSRows, hdr, n, B_l, p.act_hi, p.act_lo, off, p.I,
                                  0, p.Kr / group_k<true>(), nullptr, p.xr, p.xr_lo, p.Kr);
     else
         gu_stream_block<true, 1>(p, p.gp + e * p.g_sp, p.up + e * p.u_sp, p.gs + e * p.g_ss, p.us + e * p.u_ss,
-                                 p.I, rb * kSBlkRows + wave * kSRows, tok_l, n, B_l, p.act_hi, p.act_lo, off, p.I,
+                                 p.I, rb * kSBlkRows + wave * kSRows, hdr, n, B_l, p.act_hi, p.act_lo, off, p.I,
                                  0, p.Kr / group_k<true>(), nullptr, p.xr, nullptr, p.Kr);
 }
 
@@ -380,14 +419,14 @@ struct DnStreamParams {
 // LDS of a down block: both planes of stg staged token rows of width KD
 __host__ __device__ constexpr int dn_stream_lds_bytes(int KD, int stg)
 {
-    return 2 * stg * (2 * KD + kSPad) + kSTok * 8;
+    return 2 * stg * (2 * KD + kSPad) + kHdrBytes;
 }
 
 // Rows [rb0, rb1) x 256 of an R-row matrix, K columns [k0, k0 + KD) of rows
 // KW long (weights and activations), into yout rows orow * R.
 template <bool FP4>
 __device__ __forceinline__ void dn_stream_run(const DnStreamParams &p, const uint8_t *wd, const uint8_t *sd, int KD,
-                                              int rb0, int rb1, const int *arow_l, const int *orow_l, int n,
+                                              int rb0, int rb1, const int *hdr, int n,
                                               const uint16_t *ahi, const uint16_t *alo, uint8_t *B_l, int R,
                                               float *yout, int KW, int k0)
 {
@@ -399,17 +438,17 @@ __device__ __forceinline__ void dn_stream_run(const DnStreamParams &p, const uin
     wd += FP4 ? k0 / 2 : (size_t)k0 * 2;
     if (FP4) sd += k0 / 32;
 
-    // stage both activation planes of the item's tokens (stg rows: every
-    // item has at most that many), whole K range
-    const int stg = p.stg;
+    // stage both activation planes of the item's staged rows (one per
+    // distinct token, at most stg), whole K range
+    const int stg = p.stg, nr = hdr[kHdrN];
     {
         const int ru4 = KD * 2 / 16;  // u4 per token row
-        for (int v = tid; v < 2 * stg * ru4; v += 64 * kDWaves) {
-            const int half = v / (stg * ru4), vv = v - half * (stg * ru4);
+        for (int v = tid; v < 2 * nr * ru4; v += 64 * kDWaves) {
+            const int half = v / (nr * ru4), vv = v - half * (nr * ru4);
             const int col = vv / ru4, seg = vv - col * ru4;
             const uint16_t *src = half ? alo : ahi;
             *reinterpret_cast<u4 *>(B_l + (half * stg + col) * BROW + 16 * seg) =
-                *reinterpret_cast<const u4 *>(src + (size_t)arow_l[col] * KW + k0 + 8 * seg);
+                *reinterpret_cast<const u4 *>(src + (size_t)hdr[kHdrSrc + col] * KW + k0 + 8 * seg);
         }
     }
     __syncthreads();
@@ -432,10 +471,11 @@ __device__ __forceinline__ void dn_stream_run(const DnStreamParams &p, const uin
     };
 
     v4f acc[2] = {v4f{0.0f, 0.0f, 0.0f, 0.0f}, v4f{0.0f, 0.0f, 0.0f, 0.0f}};
-    // B column l16 reads a staged row (columns past stg repeat the last one,
-    // never stored)
-    const uint8_t *Bh = B_l + min(l16, stg - 1) * BROW;
-    const uint8_t *Bl = B_l + (stg + min(l16, stg - 1)) * BROW;
+    // B column l16 reads its staged row (columns past n repeat the last
+    // column's, never stored)
+    const int brow = hdr[kHdrMap + min(l16, n - 1)];
+    const uint8_t *Bh = B_l + brow * BROW;
+    const uint8_t *Bl = B_l + (stg + brow) * BROW;
     auto compute = [&](const Grp &b, int it) {
         const int rb = rb0 + it / NG, gi = it - (it / NG) * NG;
         const int kg = gi * GK;
@@ -466,7 +506,7 @@ __device__ __forceinline__ void dn_stream_run(const DnStreamParams &p, const uin
         }
         if (gi == NG - 1) {  // row block done: lane holds rows 4g + i of token column l16
             if (l16 < n) {
-                float *yr = yout + (size_t)orow_l[l16] * H;
+                float *yr = yout + (size_t)hdr[kHdrOut + l16] * H;
 #pragma unroll
                 for (int rf = 0; rf < 2; ++rf) {
                     const int row = rb * kDBlkRows + wave * kSRows + 16 * rf + 4 * g;
@@ -492,9 +532,8 @@ __device__ __forceinline__ void dn_stream_run(const DnStreamParams &p, const uin
 __global__ __launch_bounds__(64 * kDWaves) void k_dn_stream(DnStreamParams p)
 {
     extern __shared__ __align__(16) uint8_t lds[];
-    int *arow_l = reinterpret_cast<int *>(lds);
-    int *orow_l = arow_l + kSTok;
-    uint8_t *B_l = lds + kSTok * 8;
+    int *hdr = reinterpret_cast<int *>(lds);
+    uint8_t *B_l = lds + kHdrBytes;
     const int item = blockIdx.x / p.runs, run = blockIdx.x - item * p.runs;
     const int R = item < p.sh_items ? p.H : p.Hr;  // output rows of this item
     const int RBT = (R + kDBlkRows - 1) / kDBlkRows;
@@ -505,13 +544,15 @@ __global__ __launch_bounds__(64 * kDWaves) void k_dn_stream(DnStreamParams p)
         const int t0 = tg * kSTok, n = min(kSTok, p.T - t0);
         if (threadIdx.x < kSTok) {
             const int t = t0 + min((int)threadIdx.x, n - 1);
-            arow_l[threadIdx.x] = t;
-            orow_l[threadIdx.x] = p.ysh ? t : t * (p.K + 1) + p.K;
+            hdr[kHdrKey + threadIdx.x] = hdr[kHdrVal + threadIdx.x] = t;
+            hdr[kHdrOut + threadIdx.x] = p.ysh ? t : t * (p.K + 1) + p.K;
         }
         __syncthreads();
+        item_rows(hdr, n);
+        __syncthreads();
         const int KS = p.Is / p.sh_ks;
-        dn_stream_run<false>(p, reinterpret_cast<const uint8_t *>(p.sh_down), nullptr, KS, rb0, rb1, arow_l,
-                             orow_l, n, p.ash_hi, p.ash_lo, B_l, p.H,
+        dn_stream_run<false>(p, reinterpret_cast<const uint8_t *>(p.sh_down), nullptr, KS, rb0, rb1, hdr, n,
+                             p.ash_hi, p.ash_lo, B_l, p.H,
                              p.ysh ? p.ysh + (size_t)ks * p.T * p.H : p.ys, p.Is, ks * KS);
         return;
     }
@@ -522,12 +563,15 @@ __global__ __launch_bounds__(64 * kDWaves) void k_dn_stream(DnStreamParams p)
     if (threadIdx.x < kSTok) {
         const int c = min((int)threadIdx.x, n - 1);
         const int a = p.sorted[off + c];
-        arow_l[threadIdx.x] = off + c;
-        orow_l[threadIdx.x] = (a / p.K) * (p.K + 1) + a % p.K;
+        hdr[kHdrKey + threadIdx.x] = a / p.K;  // the token
+        hdr[kHdrVal + threadIdx.x] = off + c;  // its activation row
+        hdr[kHdrOut + threadIdx.x] = (a / p.K) * (p.K + 1) + a % p.K;
     }
     __syncthreads();
-    dn_stream_run<true>(p, p.dp + e * p.d_sp, p.ds + e * p.d_ss, p.I, rb0, rb1, arow_l, orow_l, n, p.act_hi,
-                        p.act_lo, B_l, p.Hr, p.ys, p.I, 0);
+    item_rows(hdr, n);
+    __syncthreads();
+    dn_stream_run<true>(p, p.dp + e * p.d_sp, p.ds + e * p.d_ss, p.I, rb0, rb1, hdr, n, p.act_hi, p.act_lo, B_l,
+                        p.Hr, p.ys, p.I, 0);
 }
 
 }  // namespace
@@ -575,7 +619,7 @@ hipError_t launch_stream_gu(const LayerView &L, const uint16_t *x, const uint16_
 {
     static const bool lds_set = [] {
         (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gu_stream),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, gu_stream_lds_bytes(2));
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, gu_stream_lds_bytes(2, kSTok));
         return true;
     }();
     (void)lds_set;
@@ -607,6 +651,7 @@ hipError_t launch_stream_gu(const LayerView &L, const uint16_t *x, const uint16_
     p.sorted = sorted;
     p.light = light;
     p.light_n = light_n;
+    p.stg = std::min(T, kSTok);
     p.sh_slices = with_shared ? std::min(stream_shared_slices(T), L.H / group_k<false>()) : 1;  // no empty slice
     p.sh_part = sh_part;
     p.sh_blocks = with_shared ? ((T + kSTok - 1) / kSTok) * (L.Is / kSBlkRows) * p.sh_slices : 0;
@@ -616,7 +661,7 @@ hipError_t launch_stream_gu(const LayerView &L, const uint16_t *x, const uint16_
     p.ash_lo = ash_lo;
     const int64_t cap = std::min<int64_t>(L.E, (int64_t)T * L.K);
     const unsigned nblk = (unsigned)(p.sh_blocks + cap * (L.I / kSBlkRows));
-    k_gu_stream<<<nblk, 64 * kSWaves, gu_stream_lds_bytes(xr_lo ? 2 : 1), s>>>(p);
+    k_gu_stream<<<nblk, 64 * kSWaves, gu_stream_lds_bytes(xr_lo ? 2 : 1, p.stg), s>>>(p);
     if (with_shared && p.sh_slices > 1) {
         const int64_t n = (int64_t)T * L.Is;
         k_sh_act<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(sh_part, p.sh_slices, T, L.Is, L.act, L.b1, L.b2,

@@ -59,11 +59,13 @@ def test_tiny_latent(T):
     _run(spec, layer, T)
 
 
-def test_tiny_latent_without_norm_or_shared():
+@pytest.mark.parametrize("T", [1, 7])
+def test_tiny_latent_without_norm_or_shared(T):
+    # T = 1 takes the one-token projections (no norm: the aggregate as is)
     spec = synth.LayerSpec(hidden=256, inter=128, n_experts=8, topk=2, shared_inter=0,
                            bias_std=0.05, seed=97, latent=256, latent_norm=0)
     _, layer = _layer(spec)
-    _run(spec, layer, 7)
+    _run(spec, layer, T)
 
 
 @pytest.mark.parametrize("T,routing", [(1, "normal"), (5, "normal"), (40, "normal"), (129, "zipf"),

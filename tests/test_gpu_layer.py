@@ -405,3 +405,28 @@ def test_full_prefill_T2048_zipf_sampled():
     ref, denom, _ = oracle_forward(spec, x_np, idx_in, w_in, tokens=few)
     assert rel_err(out[few], ref, denom) <= REL_TOL
     assert layer.error_count() == 0
+
+
+@pytest.mark.parametrize("latent", [0, 256])
+def test_repeated_ids_within_a_token(latent):
+    # a token may name an expert more than once (the layer sums every
+    # assignment): an expert's item then holds more assignments than there
+    # are tokens, which the streaming kernels stage once per distinct token
+    spec = synth.LayerSpec(hidden=512, inter=512, n_experts=16, topk=4, shared_inter=256,
+                           bias_std=0.05, seed=77, latent=latent)
+    sd = _dev()
+    t = sd.layer_tensors(spec, 0, DEV)
+    layer = sd.make_layer(spec, t)
+    rng = np.random.default_rng(7)
+    cases = [np.array([[5, 5, 5, 5]]),
+             np.array([[5, 5, 5, 2], [5, 7, 7, 1], [5, 3, 9, 9]]),
+             np.array([[1, 1, 4, 4], [4, 4, 1, 1]])]
+    for idx in cases:
+        T = idx.shape[0]
+        idx = idx.astype(np.int32)
+        w = rng.uniform(0.05, 1.0, idx.shape).astype(np.float32)
+        x_np = synth.make_x(spec, T, attempt=T)
+        out = _forward_gpu(layer, _x_dev(x_np), idx, w)
+        ref, denom, drops = oracle_forward(spec, x_np, idx, w)
+        assert drops == 0
+        assert rel_err(out, ref, denom) <= REL_TOL, idx.tolist()
