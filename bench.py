@@ -179,6 +179,19 @@ def main():
         c1 = cache.stats()
         cd = {k: c1[k] - c0[k] for k in c1}
 
+    # per-step spread: an event pair around every step (same steps), so the
+    # median and the 10th / 90th percentiles of the step time can be reported
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    step_us = np.sort(np.array([a.elapsed_time(b) * 1e3 for a, b in evs]))
+    pct = {q: float(np.percentile(step_us, q)) for q in (10, 50, 90)}
+    log(f"[bench] step us p10 {pct[10]:.2f} p50 {pct[50]:.2f} p90 {pct[90]:.2f}")
+
     # second pass with per-stage events (same steps)
     layer.profile(True)
     layer.profile_read(stream)
@@ -254,6 +267,7 @@ def main():
             "distinct_experts_per_step": round(nd, 2),
         },
         "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "step_us_p10_p50_p90": [round(pct[10], 2), round(pct[50], 2), round(pct[90], 2)],
         "layer_GBps": round(layer_bytes / (ms * 1e-3) / 1e9, 2),
         "routed_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "stage_us": {k: round(v, 3) for k, v in stage_us.items()},
