@@ -50,6 +50,9 @@ METRIC = "routed-expert HBM GB/s (decode) and tokens/s per MoE layer, % of roofl
 HBM_PEAK_GBPS = 8000.0
 HOST_LINK_PEAK_GBPS = 64.0  # PCIe 5.0 x16, one direction
 STEP_EPS = 1e-5  # the pre-MoE norm's epsilon (the pages' rms_eps)
+STREAM_MAX_TOKENS = 16  # experts with more assignments go to the tile GEMMs
+BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA
+MXFP4_PEAK_TFLOPS = 10100.0  # dense MXFP4 MFMA
 EXPERT_MATRIX_BYTES = None  # filled from the spec
 
 
@@ -151,11 +154,14 @@ def main():
         layer.forward(x, idx, w, out, workspace=ws, stream=stream)
 
     # distinct experts per pool entry (for the algorithmic byte counts)
-    distinct = []
+    distinct, heavy = [], []
     for p in range(pool):
         step(p)
         torch.cuda.synchronize()
-        distinct.append(len(set(idx.cpu().numpy().ravel().tolist())))
+        ids = idx.cpu().numpy().ravel()
+        distinct.append(len(set(ids.tolist())))
+        cnt = np.bincount(ids[(ids >= 0) & (ids < E)], minlength=E)
+        heavy.append(cnt[cnt > STREAM_MAX_TOKENS])   # experts the tile GEMMs take
     assert layer.error_count() == 0
 
     if cache is not None:
@@ -234,6 +240,18 @@ def main():
                           "latent_out": "k_proj + k_rms_split"},
                "step": {"gateup": "k_gateup_dec", "down": "k_down_dec", "prenorm": "k_prenorm"},
                "cache": {"cache_fill": "k_cache_fill"}}[args.workload]
+    # the hot experts' tile GEMMs: algorithmic flops (2 per multiply-add,
+    # gate and up, per assignment) and issued flops (whole token tiles; the
+    # down tiles multiply the activation's hi and lo planes)
+    tile_tok_gu = 64 if Lt else 128
+    mf = {"alg_gu": 0.0, "iss_gu": 0.0, "alg_dn": 0.0, "iss_dn": 0.0}
+    for i in range(args.steps):
+        c = heavy[i % pool]
+        mf["alg_gu"] += c.sum() * 2 * 2 * I * EKw
+        mf["iss_gu"] += (np.ceil(c / tile_tok_gu) * tile_tok_gu).sum() * 2 * 2 * I * EKw * (2 if Lt else 1)
+        mf["alg_dn"] += c.sum() * 2 * EKw * I
+        mf["iss_dn"] += (np.ceil(c / 64) * 64).sum() * 2 * EKw * I * 2
+    mf = {k: v / args.steps for k, v in mf.items()}
     dom = max(stage_bytes, key=lambda s: stage_us[s])
     achieved = stage_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9 if stage_us[dom] > 0 else 0.0
     peak = HBM_PEAK_GBPS if cache is None else HOST_LINK_PEAK_GBPS
@@ -283,6 +301,24 @@ def main():
         },
     }
 
+    if mf["alg_gu"] > 0 and stage_us.get("gateup_tiles", 0) > 0:
+        tu, td = stage_us["gateup_tiles"] * 1e-6, max(stage_us.get("down_tiles", 0), 1e-9) * 1e-6
+        result["mfma"] = {
+            "kernel": "k_gemm gate/up tiles (experts with > 16 assignments)",
+            "alg_TFLOPs": round(mf["alg_gu"] / tu / 1e12, 2),
+            "issued_TFLOPs": round(mf["iss_gu"] / tu / 1e12, 2),
+            "alg_frac_of_mxfp4_peak": round(mf["alg_gu"] / tu / 1e12 / MXFP4_PEAK_TFLOPS, 4),
+            "issued_frac_of_bf16_peak": round(mf["iss_gu"] / tu / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "down_alg_TFLOPs": round(mf["alg_dn"] / td / 1e12, 2),
+            "down_issued_frac_of_bf16_peak": round(mf["iss_dn"] / td / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "tile_us": [round(stage_us["gateup_tiles"], 2), round(stage_us.get("down_tiles", 0.0), 2)],
+        }
+        if args.workload == "prefill":   # the dominant kernel is the hot experts' gate/up tiles
+            a = mf["alg_gu"] / tu / 1e12
+            result["roofline"] = {"kernel": "k_gemm<0> (gate/up tiles)", "bound": "mfma",
+                                  "achieved": round(a, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(a / BF16_PEAK_TFLOPS, 4),
+                                  "flops_per_launch": round(mf["alg_gu"]), "traffic": None}
     if cache is not None:
         result["config"]["workload"] += f", experts in pinned host memory, {args.slots} HBM slots"
         result["cache"] = {

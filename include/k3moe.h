@@ -229,7 +229,9 @@ typedef enum {
     K3MOE_STAGE_PRENORM = 10,       /* step: norm of the residual stream  */
     K3MOE_STAGE_CACHE_PLAN = 11,    /* cache: hits, victims, slot ids     */
     K3MOE_STAGE_CACHE_FILL = 12,    /* cache: host -> HBM expert reads    */
-    K3MOE_N_STAGES = 13
+    K3MOE_STAGE_GATEUP_TILES = 13,  /* the routed gate/up tile GEMMs only (within GATEUP) */
+    K3MOE_STAGE_DOWN_TILES = 14,    /* the routed down tile GEMMs only (within DOWN)      */
+    K3MOE_N_STAGES = 15
 } k3moe_stage;
 
 k3moe_status k3moe_profile_enable(k3moe_layer *layer, int enable);

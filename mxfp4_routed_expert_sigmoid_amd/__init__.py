@@ -66,7 +66,8 @@ EXPORTS = ("k3moe_layer_create", "k3moe_workspace_size", "k3moe_route", "k3moe_f
            "k3moe_error_count", "k3moe_error_reset", "k3moe_profile_enable",
            "k3moe_profile_read", "k3moe_layer_destroy", "k3moe_status_string")
 STAGES = ("router", "topk", "xsplit", "perm", "gateup", "shared_gateup", "down", "combine",
-          "latent_in", "latent_out", "prenorm", "cache_plan", "cache_fill")
+          "latent_in", "latent_out", "prenorm", "cache_plan", "cache_fill", "gateup_tiles",
+          "down_tiles")
 
 
 def lib():

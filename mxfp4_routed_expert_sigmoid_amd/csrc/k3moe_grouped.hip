@@ -538,10 +538,13 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t 
         gp.tile_n = counts;
         gp.ohi = act_hi;
         gp.olo = act_lo;
-        if (gemm_gu && two)
-            k_gemm<kGU2><<<(unsigned)(cap_gu * rb_i), 64 * GemmShape<kGU2>::WAVES, gemm_lds_bytes<kGU2>(), s>>>(gp);
-        else if (gemm_gu)
-            k_gemm<kGU><<<(unsigned)(cap_gu * rb_i), 64 * GemmShape<kGU>::WAVES, gemm_lds_bytes<kGU>(), s>>>(gp);
+        if (gemm_gu) {
+            StageMark mt(prof, K3MOE_STAGE_GATEUP_TILES, s);
+            if (two)
+                k_gemm<kGU2><<<(unsigned)(cap_gu * rb_i), 64 * GemmShape<kGU2>::WAVES, gemm_lds_bytes<kGU2>(), s>>>(gp);
+            else
+                k_gemm<kGU><<<(unsigned)(cap_gu * rb_i), 64 * GemmShape<kGU>::WAVES, gemm_lds_bytes<kGU>(), s>>>(gp);
+        }
         if (L.Is > 0 && !sh_stream) {
             StageMark m2(prof, K3MOE_STAGE_SHARED_GATEUP, s);
             GemmParams sp = gp;
@@ -580,8 +583,10 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t 
         dp.tiles = tiles_dn;
         dp.tile_n = counts + 1;
         dp.ys = ys;
-        if (gemm_dn)
+        if (gemm_dn) {
+            StageMark mt(prof, K3MOE_STAGE_DOWN_TILES, s);
             k_gemm<kDN><<<(unsigned)(cap_dn * rb_r), 64 * GemmShape<kDN>::WAVES, gemm_lds_bytes<kDN>(), s>>>(dp);
+        }
         if (L.Is > 0 && !sh_stream) {
             // shared rows of H: to slot k of ys (flat), or to ysh [T][H] (K = 0 makes the row t)
             GemmParams sp = dp;
