@@ -19,6 +19,12 @@ shared expert of inter 1536, bias N(0, 0.01)):
   step     T = 1 through k3moe_step on the full shape: the decoder layer's
            pre-MoE RMSNorm of an fp32 residual stream into bf16 tokens, route,
            experts, the residual add fused into the last kernel
+  stack    --layers (8) full-shape layers resident (126 GB), --tokens (1) per
+           step through all of them on an fp32 residual stream, each layer a
+           decoder-layer MoE step (k3moe_step: the pre-MoE RMSNorm with the
+           layer's own gain, route with its own router, experts, the residual
+           add in the last kernel); the norm keeps every layer's routes
+           spread (a plain residual grows until the sigmoid scores saturate)
   cache    T = 1 on the full shape with the 896 experts in pinned host memory
            and --slots of them in an HBM slot arena (k3moe_cache_forward):
            misses are read over the host link each step; --routing picks
@@ -69,11 +75,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", choices=("decode", "batched", "prefill", "latent", "step", "cache"), default="decode")
+    ap.add_argument("--workload", choices=("decode", "batched", "prefill", "latent", "step", "cache", "stack"), default="decode")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--slots", type=int, default=224, help="cache: HBM expert slots")
+    ap.add_argument("--layers", type=int, default=8, help="stack: resident layers")
+    ap.add_argument("--tokens", type=int, default=1, help="stack: tokens per step")
     ap.add_argument("--routing", choices=("normal", "zipf"), default=None,
                     help="cache: routing of the token pool (default normal)")
     args = ap.parse_args()
@@ -94,7 +102,9 @@ def main():
     torch.cuda.set_device(0)
     T, routing, pool = {"decode": (1, "normal", 64), "batched": (64, "normal", 8),
                         "prefill": (2048, "zipf", 2), "latent": (1, "normal", 64),
-                        "step": (1, "normal", 64), "cache": (1, "normal", 256)}[args.workload]
+                        "step": (1, "normal", 64), "cache": (1, "normal", 256),
+                        "stack": (args.tokens, "normal", 8)}[args.workload]
+    nl = args.layers if args.workload == "stack" else 1
     if args.workload == "cache" and args.routing:
         routing = args.routing
     if args.workload == "latent":
@@ -122,11 +132,16 @@ def main():
         layer = sd.make_layer(spec, tens)
         cache = k3.Cache(layer, args.slots)
         log(f"[bench] experts in pinned host memory, {args.slots} HBM slots")
+    layers = [layer]
+    for l in range(1, nl):
+        log(f"[bench] building layer {l}")
+        layers.append(sd.make_layer(spec, sd.layer_tensors(spec, l, dev)))
     xs_np = [synth.make_x(spec, T, attempt=100 + p) for p in range(pool)]
     xs = [sd.bf16_tensor(x, dev) for x in xs_np]
     ws = layer.workspace(T) if cache is None else cache.workspace(T)
-    idx = torch.empty((T, K), dtype=torch.int32, device=dev)
-    w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    idxs = [torch.empty((T, K), dtype=torch.int32, device=dev) for _ in range(nl)]
+    ws_l = [torch.empty((T, K), dtype=torch.float32, device=dev) for _ in range(nl)]
+    idx, w = idxs[0], ws_l[0]
     out = torch.empty((T, H), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     if args.workload == "step":
@@ -135,6 +150,11 @@ def main():
         hs = [torch.from_numpy(h).to(dev) for h in hs_np]
         gamma_np = synth.make_post_norm(spec)
         gamma = torch.from_numpy(gamma_np).to(dev)
+    if args.workload == "stack":
+        hs_np = [synth.make_residual(spec, T, attempt=100 + p) for p in range(pool)]
+        hs = [torch.from_numpy(h).to(dev) for h in hs_np]
+        gammas = [torch.from_numpy(synth.make_post_norm(spec, l)).to(dev) for l in range(nl)]
+        gamma_np = synth.make_post_norm(spec, 0)
 
     # calibration read of known size (256 MiB) for hardware byte counters
     cal = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -143,6 +163,11 @@ def main():
     del cal
 
     def step(i):
+        if args.workload == "stack":
+            h = hs[i % pool]
+            for l, lay in enumerate(layers):
+                lay.step(h, gammas[l], STEP_EPS, idxs[l], ws_l[l], workspace=ws, stream=stream)
+            return
         if args.workload == "step":
             layer.step(hs[i % pool], gamma, STEP_EPS, idx, w, workspace=ws, stream=stream)
             return
@@ -158,10 +183,14 @@ def main():
     for p in range(pool):
         step(p)
         torch.cuda.synchronize()
-        ids = idx.cpu().numpy().ravel()
-        distinct.append(len(set(ids.tolist())))
-        cnt = np.bincount(ids[(ids >= 0) & (ids < E)], minlength=E)
-        heavy.append(cnt[cnt > STREAM_MAX_TOKENS])   # experts the tile GEMMs take
+        dl, hl = [], []
+        for l in range(nl):   # per layer; a stack's figures are per-layer means
+            ids = idxs[l].cpu().numpy().ravel()
+            dl.append(len(set(ids.tolist())))
+            cnt = np.bincount(ids[(ids >= 0) & (ids < E)], minlength=E)
+            hl.append(cnt[cnt > STREAM_MAX_TOKENS])   # experts the tile GEMMs take
+        distinct.append(sum(dl) / nl)
+        heavy.append(np.concatenate(hl) if nl > 1 else hl[0])
     assert layer.error_count() == 0
 
     if cache is not None:
@@ -226,7 +255,7 @@ def main():
         "gateup": nd * 2 * gu + (2 * Is * H * 2 if shared_in_gateup else 0) + x_read + act_b,
         "down": nd * dn + Is * H * 2 + act_b + T * (K + 1) * EKw * 4 + (T * H * 4 if Lt else 0),
     }
-    if args.workload == "step":
+    if args.workload in ("step", "stack"):
         stage_bytes["prenorm"] = T * H * 4 + H * 4 + T * H * 2
     if cache is not None:
         stage_bytes = {"cache_fill": cd["bytes_read"] / max(1, cd["steps"])}
@@ -239,7 +268,9 @@ def main():
                "latent": {"gateup": "k_gu_stream", "down": "k_dn_stream", "latent_in": "k_proj",
                           "latent_out": "k_proj + k_rms_split"},
                "step": {"gateup": "k_gateup_dec", "down": "k_down_dec", "prenorm": "k_prenorm"},
-               "cache": {"cache_fill": "k_cache_fill"}}[args.workload]
+               "cache": {"cache_fill": "k_cache_fill"},
+               "stack": ({"gateup": "k_gateup_dec", "down": "k_down_dec", "prenorm": "k_prenorm"} if T == 1
+                         else {"gateup": "k_gu_stream", "down": "k_dn_stream", "prenorm": "k_prenorm"})}[args.workload]
     # the hot experts' tile GEMMs: algorithmic flops (2 per multiply-add,
     # gate and up, per assignment) and issued flops (whole token tiles; the
     # down tiles multiply the activation's hi and lo planes)
@@ -251,13 +282,15 @@ def main():
         mf["iss_gu"] += (np.ceil(c / tile_tok_gu) * tile_tok_gu).sum() * 2 * 2 * I * EKw * (2 if Lt else 1)
         mf["alg_dn"] += c.sum() * 2 * EKw * I
         mf["iss_dn"] += (np.ceil(c / 64) * 64).sum() * 2 * EKw * I * 2
-    mf = {k: v / args.steps for k, v in mf.items()}
+    mf = {k: v / args.steps / nl for k, v in mf.items()}
     dom = max(stage_bytes, key=lambda s: stage_us[s])
     achieved = stage_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9 if stage_us[dom] > 0 else 0.0
     peak = HBM_PEAK_GBPS if cache is None else HOST_LINK_PEAK_GBPS
     traffic = measured_traffic(kernels[dom])
-    value = routed_bytes / (ms * 1e-3) / 1e9
+    value = nl * routed_bytes / (ms * 1e-3) / 1e9
     layer_bytes = routed_bytes + router_bytes + shared_bytes + proj_bytes + T * H * 2 + T * H * 4
+    if args.workload == "stack":
+        layer_bytes += T * H * 16 + H * 4   # the stream: norm read, add read + write; the gain
     if args.workload == "step":
         layer_bytes += T * H * 8 + H * 4   # the stream read twice (norm, add) and the gain
     result = {
@@ -274,7 +307,10 @@ def main():
         "dtype": "mxfp4",
         "data": "synthetic",
         "config": {
-            "workload": f"{args.workload}: T={T} tokens/step, hidden {H}, {E} experts top-{K}, "
+            "workload": f"{args.workload}: T={T} tokens/step, "
+                        + (f"{nl} resident layers, each a decoder-layer step (pre-MoE RMSNorm, its own "
+                           f"router, residual add; k3moe_step), " if args.workload == "stack" else "")
+                        + f"hidden {H}, {E} experts top-{K}, "
                         + ("pre-MoE RMSNorm of an fp32 residual stream into bf16 tokens and the "
                            "residual add (k3moe_step), " if args.workload == "step" else "")
                         + (f"experts in a {Lt} latent (bf16 down/up projections, RMSNorm of the "
@@ -286,7 +322,9 @@ def main():
         },
         "tokens_per_s": round(T / (ms * 1e-3), 1),
         "step_us_p10_p50_p90": [round(pct[10], 2), round(pct[50], 2), round(pct[90], 2)],
-        "layer_GBps": round(layer_bytes / (ms * 1e-3) / 1e9, 2),
+        "layer_GBps": round(nl * layer_bytes / (ms * 1e-3) / 1e9, 2),
+        "layers_per_step": nl,
+        "tokens_per_s_per_layer": round(T * nl / (ms * 1e-3), 1),
         "routed_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "stage_us": {k: round(v, 3) for k, v in stage_us.items()},
         "roofline": {
@@ -331,7 +369,7 @@ def main():
             "slots_over_experts": round(args.slots / E, 4),
         }
     if not args.no_cpu_baseline:
-        if args.workload == "step":
+        if args.workload in ("step", "stack"):
             result["cpu_baseline"] = cpu_baseline(spec, hs_np, T, args.cpu_seconds, expert_b,
                                                   gamma=gamma_np)
         else:

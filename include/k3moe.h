@@ -180,6 +180,19 @@ k3moe_status k3moe_forward(const k3moe_layer *layer, const uint16_t *x, int32_t 
                            const int32_t *idx, const float *w, float *out,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* k3moe_forward with the residual add fused into its last kernel, for a
+ * stack of layers on an fp32 residual stream (each layer's output added to
+ * the stream, the next layer reading it rounded to bf16):
+ *   h  fp32 [T][hidden]  in/out, 16-byte aligned: h += forward(x, idx, w),
+ *                        the complete layer output added once
+ *   hb bf16 [T][hidden]  out (optional, NULL = not written): bf16_RNE of
+ *                        the updated h; may be x itself (x is read before
+ *                        the last kernel writes hb)
+ * Other arguments and errors as k3moe_forward. */
+k3moe_status k3moe_forward_residual(const k3moe_layer *layer, const uint16_t *x, int32_t T,
+                                    const int32_t *idx, const float *w, float *h, uint16_t *hb,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
 /* One decoder layer's MoE on the residual stream (README, the decoder-layer
  * listing after "Aggregate, attend, aggregate again": the layer input is
  * k3_rmsnorm of h with the post-attention gain, then k3_moe; the output is

@@ -61,7 +61,7 @@ class CacheStats(ctypes.Structure):
 
 _lib = None
 EXPORTS = ("k3moe_layer_create", "k3moe_workspace_size", "k3moe_route", "k3moe_forward",
-           "k3moe_step", "k3moe_cache_create", "k3moe_cache_workspace_size", "k3moe_cache_forward",
+           "k3moe_forward_residual", "k3moe_step", "k3moe_cache_create", "k3moe_cache_workspace_size", "k3moe_cache_forward",
            "k3moe_cache_stats_read", "k3moe_cache_slots", "k3moe_cache_reset", "k3moe_cache_destroy",
            "k3moe_error_count", "k3moe_error_reset", "k3moe_profile_enable",
            "k3moe_profile_read", "k3moe_layer_destroy", "k3moe_status_string")
@@ -86,6 +86,8 @@ def lib():
         L.k3moe_route.argtypes = [P, P, i32, P, P, P, P, ctypes.c_size_t, P]
         L.k3moe_forward.restype = st
         L.k3moe_forward.argtypes = [P, P, i32, P, P, P, P, ctypes.c_size_t, P]
+        L.k3moe_forward_residual.restype = st
+        L.k3moe_forward_residual.argtypes = [P, P, i32, P, P, P, P, P, ctypes.c_size_t, P]
         L.k3moe_step.restype = st
         L.k3moe_step.argtypes = [P, P, i32, P, ctypes.c_float, P, P, P, P, P, ctypes.c_size_t, P]
         L.k3moe_cache_create.restype = st
@@ -243,6 +245,17 @@ class Layer:
         _check(lib().k3moe_forward(self.handle, x.data_ptr(), T, idx.data_ptr(), w.data_ptr(),
                                    out.data_ptr(), p, n, _stream(stream, self.device)),
                "k3moe_forward")
+
+    def forward_residual(self, x, idx, w, h, hb=None, workspace=None, stream=None):
+        """k3moe_forward_residual: h fp32 [T][H] += forward(x, idx, w), in place;
+        hb (bf16 [T][H], optional, may be x) receives bf16 of the updated h."""
+        T = x.shape[0]
+        _dev(x, (2,), "x"), _dev(idx, (4,), "idx"), _dev(w, (4,), "w"), _dev(h, (4,), "h"), _dev(hb, (2,), "hb")
+        ws = workspace if workspace is not None else self.workspace(T)
+        p, n = self._ws(ws)
+        _check(lib().k3moe_forward_residual(self.handle, x.data_ptr(), T, idx.data_ptr(), w.data_ptr(),
+                                            h.data_ptr(), _ptr(hb), p, n, _stream(stream, self.device)),
+               "k3moe_forward_residual")
 
     def step(self, h, gamma, eps, idx, w, x_out=None, hb=None, workspace=None, stream=None):
         """k3moe_step: h fp32 [T][H] += layer(bf16(RMSNorm(h) * gamma)), in place;

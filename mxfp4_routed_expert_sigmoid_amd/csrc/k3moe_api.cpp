@@ -366,6 +366,26 @@ k3moe_status k3moe_forward(const k3moe_layer *l, const uint16_t *x, int32_t T, c
     return K3MOE_OK;
 }
 
+k3moe_status k3moe_forward_residual(const k3moe_layer *l, const uint16_t *x, int32_t T, const int32_t *idx,
+                                    const float *w, float *h, uint16_t *hb, void *ws, size_t ws_bytes,
+                                    void *stream)
+{
+    bool nothing;
+    k3moe_status s = check_call(l, T, ws, ws_bytes, &nothing);
+    if (s != K3MOE_OK || nothing) return s;
+    if (!x || !idx || !w || !h) return K3MOE_E_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(idx, 4) || !aligned(w, 4) || !aligned(h, 16) || (hb && !aligned(hb, 16)))
+        return K3MOE_E_ALIGNMENT;
+    const WsLayout lay = ws_layout(l->cfg, T);
+    OutEpi epi;
+    epi.resid = true;
+    epi.ob = hb;
+    if (launch_forward(view(l), x, T, idx, w, h, static_cast<char *>(ws), lay, static_cast<hipStream_t>(stream),
+                       l->prof, epi) != hipSuccess)
+        return K3MOE_E_HIP;
+    return K3MOE_OK;
+}
+
 k3moe_status k3moe_step(const k3moe_layer *l, float *h, int32_t T, const float *gamma, float eps,
                         uint16_t *x_out, int32_t *idx, float *w, uint16_t *hb, void *ws, size_t ws_bytes,
                         void *stream)

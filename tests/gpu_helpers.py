@@ -74,3 +74,16 @@ def oracle_forward(spec, x, idx, w, layer=0, tokens=None):
     out, denom, drops = oracle.forward(xs, ids, ws, es, spec.hidden, spec.inter, shared=shared,
                                        act_kind=spec.act, b1=spec.situ_b1, b2=spec.situ_b2)
     return out, denom, drops
+
+
+def bf16_rne_np(v):
+    """bf16 bits of fp32 values by the definition (nearer neighbour, ties to
+    the even one), vectorised."""
+    v = np.asarray(v, np.float32)
+    toward = (v.view(np.uint32) >> 16).astype(np.uint32)
+    away = toward + 1
+    f = lambda b: (b << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    dt = np.abs(v.astype(np.float64) - f(toward))
+    da = np.abs(f(away) - v.astype(np.float64))
+    pick_away = (da < dt) | ((da == dt) & ((toward & 1) == 1))
+    return np.where(pick_away, away, toward).astype(np.uint16)

@@ -17,7 +17,7 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import REL_TOL, check_route, oracle_forward
+from gpu_helpers import REL_TOL, bf16_rne_np, check_route, oracle_forward
 
 pytestmark = pytest.mark.gpu
 
@@ -49,19 +49,6 @@ def _inv_certified(h, eps):
     return ok
 
 
-def _bf16_rne_np(v):
-    """bf16 bits of fp32 values by the definition (nearer neighbour, ties to
-    the even one), vectorised for the checks below."""
-    v = np.asarray(v, np.float32)
-    toward = (v.view(np.uint32) >> 16).astype(np.uint32)
-    away = toward + 1
-    f = lambda b: (b << 16).astype(np.uint32).view(np.float32).astype(np.float64)
-    dt = np.abs(v.astype(np.float64) - f(toward))
-    da = np.abs(f(away) - v.astype(np.float64))
-    pick_away = (da < dt) | ((da == dt) & ((toward & 1) == 1))
-    return np.where(pick_away, away, toward).astype(np.uint16)
-
-
 def _step(spec, layer, T, scale=4.0, tokens=None, with_outputs=True, attempt=0):
     h_np = synth.make_residual(spec, T, scale=scale, attempt=attempt)
     gamma_np = synth.make_post_norm(spec)
@@ -81,7 +68,7 @@ def _step(spec, layer, T, scale=4.0, tokens=None, with_outputs=True, attempt=0):
     assert _inv_certified(h_np, EPS).all()
     if with_outputs:
         assert np.array_equal(x.cpu().numpy().view(np.uint16), x_ref)
-        assert np.array_equal(hb.cpu().numpy().view(np.uint16), _bf16_rne_np(h_new))
+        assert np.array_equal(hb.cpu().numpy().view(np.uint16), bf16_rne_np(h_new))
     tokens = np.arange(T) if tokens is None else np.asarray(tokens)
     idx_r, w_r, _, ch = oracle.route(x_ref[tokens], synth.make_router(spec), synth.make_bias(spec),
                                      spec.topk, renorm=spec.renorm, routed_scale=spec.routed_scale,
@@ -163,3 +150,34 @@ def test_full_step_T64_sampled():
     spec, _, layer = _full()
     _step(spec, layer, 64, tokens=[0, 21, 42, 63])
     _FULL.clear()
+
+
+@pytest.mark.parametrize("T,latent", [(1, 0), (5, 0), (1, 512), (5, 512)])
+def test_forward_residual_is_forward_plus_the_stream(T, latent):
+    # h += forward(x) fused into the last kernel: bit-identical to forward
+    # followed by one fp32 add; the bf16 copy is the nearest-even rounding;
+    # writing the copy over x itself gives the same bits
+    import synth.device as sd
+    spec = synth.LayerSpec(hidden=1024, inter=512, n_experts=16, topk=4, shared_inter=512,
+                           bias_std=0.05, seed=160 + T, latent=latent)
+    _, layer = _layer(spec)
+    x_np = synth.make_x(spec, T)
+    x = sd.bf16_tensor(x_np, DEV)
+    idx = torch.empty((T, spec.topk), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, spec.topk), dtype=torch.float32, device=DEV)
+    layer.route(x, idx, w)
+    out = torch.empty((T, spec.hidden), dtype=torch.float32, device=DEV)
+    layer.forward(x, idx, w, out)
+    h0 = synth.make_residual(spec, T)
+    h = torch.from_numpy(h0).to(DEV)
+    hb = torch.empty((T, spec.hidden), dtype=torch.int16, device=DEV)
+    layer.forward_residual(x, idx, w, h, hb=hb)
+    h2 = torch.from_numpy(h0).to(DEV)
+    x2 = x.clone()
+    layer.forward_residual(x2, idx, w, h2, hb=x2)
+    torch.cuda.synchronize()
+    want = (h0 + out.cpu().numpy()).astype(np.float32)
+    assert np.array_equal(h.cpu().numpy(), want)
+    assert np.array_equal(hb.cpu().numpy().view(np.uint16), bf16_rne_np(want))
+    assert np.array_equal(h2.cpu().numpy(), want)
+    assert np.array_equal(x2.view(torch.int16).cpu().numpy().view(np.uint16), bf16_rne_np(want))
