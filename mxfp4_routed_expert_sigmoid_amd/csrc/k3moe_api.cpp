@@ -401,7 +401,8 @@ k3moe_status k3moe_step(const k3moe_layer *l, float *h, int32_t T, const float *
     char *wsc = static_cast<char *>(ws);
     uint16_t *x = x_out ? x_out : reinterpret_cast<uint16_t *>(wsc + lay.step_x);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const LayerView v = view(l);
+    LayerView v = view(l);
+    v.routes_distinct = true;  // the routes below come from the router
     {
         StageMark m(l->prof, K3MOE_STAGE_PRENORM, st);
         if (launch_prenorm(h, T, v.H, gamma, eps, x, st) != hipSuccess) return K3MOE_E_HIP;

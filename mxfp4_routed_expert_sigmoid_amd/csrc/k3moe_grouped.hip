@@ -496,10 +496,10 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t 
     // grids cover the most tiles the split can produce (most blocks exit at once)
     const size_t cap_gu = grouped_tile_cap(T, L.K, L.E, TG, smax_gu), cap_dn = grouped_tile_cap(T, L.K, L.E, TD, smax_dn);
     int32_t *light_gu = light, *light_dn = light + L.E;
-    // no expert can hold more than T * K assignments (ids may repeat within a
-    // token): when that fits the streamed limit, no tile is heavy and the
-    // tile GEMMs would only exit
-    const int64_t most = (int64_t)T * L.K;
+    // no expert can hold more than T * K assignments (T when the ids come
+    // from the router: no expert twice in a token): when that fits the
+    // streamed limit, no tile is heavy and the tile GEMMs would only exit
+    const int64_t most = L.routes_distinct ? (int64_t)T : (int64_t)T * L.K;
     const bool gemm_gu = !(stream && most <= smax_gu), gemm_dn = !(stream_dn && most <= smax_dn);
     k_tiles<<<1, 1024, 0, s>>>(active_n, active_off, TG, TD, smax_gu, smax_dn, tiles_gu, tiles_dn, light_gu, light_dn,
                                counts);

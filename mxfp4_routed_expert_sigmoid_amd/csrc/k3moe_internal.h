@@ -65,6 +65,7 @@ struct LayerView {
     const uint16_t *lat_down, *lat_up;
     const float *lat_norm;
     unsigned long long *errors;
+    bool routes_distinct = false;  // the ids come from the router (no expert twice in a token)
 };
 
 // Event pairs around kernel launches, per stage (k3moe_profile_*).
