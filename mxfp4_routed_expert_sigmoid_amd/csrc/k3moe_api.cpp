@@ -636,6 +636,9 @@ k3moe_status k3moe_cache_slots(const k3moe_cache *c, int32_t *slots, void *strea
 k3moe_status k3moe_cache_reset(k3moe_cache *c, void *stream)
 {
     if (!c) return K3MOE_E_INVALID_ARG;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return K3MOE_E_HIP;
+    if (dev != c->device) return K3MOE_E_INVALID_ARG;  // the table lives on the cache's device
     if (launch_cache_init(c->ctr, c->slot_of, c->layer->cfg.n_experts, c->key_of, c->used_at, c->S,
                           static_cast<hipStream_t>(stream)) != hipSuccess)
         return K3MOE_E_HIP;
