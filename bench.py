@@ -265,8 +265,10 @@ def main():
     kernels = {"decode": {"gateup": "k_gateup_dec", "down": "k_down_dec"},
                "batched": {"gateup": "k_gu_stream", "down": "k_dn_stream"},
                "prefill": {"gateup": "k_gu_gemm + k_gu_stream", "down": "k_dn_gemm + k_dn_stream"},
-               "latent": {"gateup": "k_gu_stream", "down": "k_dn_stream", "latent_in": "k_proj",
-                          "latent_out": "k_proj + k_rms_split"},
+               "latent": ({"gateup": "k_gateup_dec", "down": "k_down_dec", "latent_in": "k_gv_down",
+                           "latent_out": "k_gv_up"} if T == 1 else
+                          {"gateup": "k_gu_stream", "down": "k_dn_stream", "latent_in": "k_proj",
+                           "latent_out": "k_proj + k_rms_split"}),
                "step": {"gateup": "k_gateup_dec", "down": "k_down_dec", "prenorm": "k_prenorm"},
                "cache": {"cache_fill": "k_cache_fill"},
                "stack": ({"gateup": "k_gateup_dec", "down": "k_down_dec", "prenorm": "k_prenorm"} if T == 1

@@ -183,6 +183,14 @@ hipError_t launch_cache_plan_fill(const CachePlanParams &pp, const CacheFillPara
 // Pre-MoE norm (k3moe_step.hip): x[t] = bf16_RNE(RMSNorm(h[t]) * gamma).
 hipError_t launch_prenorm(const float *h, int T, int H, const float *gamma, float eps, uint16_t *x, hipStream_t s);
 
+// A latent layer's experts for one token on the single-token kernels
+// (k3moe_kernels.hip): routed rows (width EK) to the staging rows ys, the
+// shared expert's rows to ysh [H].
+bool latent_t1_ok(const LayerView &L);
+hipError_t launch_latent_t1(const LayerView &L, const uint16_t *x, const uint16_t *zh, const uint16_t *zl,
+                            const int32_t *idx, float *act, float *ash, char *ys_base, float *ysh, hipStream_t s,
+                            Profiler *prof);
+
 // Latent layer (k3moe_latent.hip): projections with bf16 weights, the norm.
 int proj_splits(int64_t T, int R, int Kd);
 hipError_t launch_latent_forward(const LayerView &L, const uint16_t *x, int T, const int32_t *idx,

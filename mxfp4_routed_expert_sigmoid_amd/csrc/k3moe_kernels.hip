@@ -703,7 +703,10 @@ struct GateUpParams {
     int64_t g_sp, g_ss, u_sp, u_ss;
     int H, I, K, E, act, Is;
     float b1, b2;
-    const uint16_t *x;
+    const uint16_t *x;      // the token, bf16 [H] (the shared expert's input)
+    const uint16_t *xr;     // the routed experts' input, bf16 [Kr] (x for a flat layer; hi of z)
+    const uint16_t *xr_lo;  // its lo plane (latent z) or null
+    int Kr;                 // routed input width (H, or the latent)
     const int32_t *idx;
     float *act_f;  // fp32 activations [k][I]
     const uint16_t *sh_gate, *sh_up;
@@ -728,7 +731,7 @@ struct GateUpParams {
 // 4 steps, double-buffered in registers. The activation is written in fp32
 // (act_f[slot][I]); the down kernel expands it into e4m3 terms.
 constexpr int kGuDecWaves = 4;                 // waves per block
-constexpr int kGuDecUnits = 3;                 // routed units per block (waves 0..2)
+constexpr int kGuDecMaxUnits = 3;              // routed units per block (waves 0..UNITS-1), at most
 constexpr int kGuUnitRows = 16;                // rows per routed unit
 constexpr int kGuShMaxRows = 4;                // shared rows per pass of wave 3
 constexpr int kXqPad = 64;                     // LDS term-row padding (banks)
@@ -736,9 +739,10 @@ constexpr int kScPad = 16;                     // LDS scale-row padding (banks)
 constexpr int kGuStgQ = 8;                     // token staging copies per thread (16 B of bf16)
 constexpr int kGuStgS = 6;                     // scale-row staging copies per thread
 
-__host__ __device__ constexpr int gu_dec_lds_bytes(int H)
+// the routed input (np planes of Kr bf16) and the units' scale rows
+__host__ __device__ constexpr int gu_dec_lds_bytes(int Kr, int np)
 {
-    return 2 * H + kGuDecUnits * 2 * kGuUnitRows * (H / 32 + kScPad);
+    return 2 * Kr * np + kGuDecMaxUnits * 2 * kGuUnitRows * (Kr / 32 + kScPad);
 }
 
 // Wave 3 of a gate/up block: shared rows [r0, r1) of gate and up (bf16,
@@ -802,25 +806,31 @@ __device__ void shared_gateup_rows(const GateUpParams &p, int r0, int r1)
     }
 }
 
-template <bool WIDE>
+// UNITS: routed waves per block (the other waves run shared rows), chosen
+// so both kinds of wave move about the same bytes. P2: the routed input comes
+// as bf16 hi and lo planes (a latent z); MFMA column c reads plane c & 1 and
+// the two columns' sums are added at the end, so the second plane costs no
+// extra MFMA.
+template <bool WIDE, int UNITS, bool P2>
 __global__ __launch_bounds__(64 * kGuDecWaves) void k_gateup_dec(GateUpParams p)
 {
+    constexpr int NP = P2 ? 2 : 1;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int grp = lane >> 4, col = lane & 15;
-    const int H = p.H, KS = H >> 7, SR = H >> 5, NCH = (KS + 3) >> 2;
+    const int H = p.Kr, KS = H >> 7, SR = H >> 5, NCH = (KS + 3) >> 2;  // H: the routed input width
     const int SRP = SR + kScPad;
     const int RT = p.I / kGuUnitRows;
     const int nunits = p.K * RT;
     const int b = blockIdx.x;
 
     extern __shared__ __align__(16) uint8_t lds[];
-    uint8_t *x_l = lds;                   // [H]           the token, bf16
-    uint8_t *sc_l = x_l + 2 * H;          // [3][2][16][H/32 + pad] unit scale rows
+    uint8_t *x_l = lds;                   // [NP][H]       the routed input, bf16
+    uint8_t *sc_l = x_l + 2 * H * NP;     // [UNITS][2][16][H/32 + pad] unit scale rows
 
-    // this wave's routed unit (waves 0..2) and its expert
-    const int u = kGuDecUnits * b + wave;
-    const bool routed = wave < kGuDecUnits && u < nunits;
+    // this wave's routed unit (waves 0..UNITS-1) and its expert
+    const int u = UNITS * b + wave;
+    const bool routed = wave < UNITS && u < nunits;
     const int slot = routed ? u / RT : 0, rt = routed ? u - (u / RT) * RT : 0;
     int e = routed ? p.idx[slot] : 0;
     const bool active = routed && e >= 0 && e < p.E;  // an invalid id: nothing (the combine counts it)
@@ -846,20 +856,21 @@ __global__ __launch_bounds__(64 * kGuDecWaves) void k_gateup_dec(GateUpParams p)
     // loads). A unit's scale rows are 16 consecutive rows, contiguous.
     Chunk b0, b1;
     if constexpr (WIDE) {  // SR % 16 == 0
-        const int nxq = H >> 3;  // u4 count of the bf16 token
-        const int nrow = SR >> 4, nsc = kGuDecUnits * 2 * kGuUnitRows * nrow;
+        const int nxq = (H >> 3) * NP;  // u4 count of the bf16 input planes
+        const int nrow = SR >> 4, nsc = UNITS * 2 * kGuUnitRows * nrow;
         u4 tq[kGuStgQ], ts[kGuStgS];
 #pragma unroll
         for (int q = 0; q < kGuStgQ; ++q) {
             const int i = min((int)threadIdx.x + q * 64 * kGuDecWaves, nxq - 1);
-            tq[q] = *reinterpret_cast<const u4 *>(p.x + 8 * i);
+            const int pl = P2 ? i / (H >> 3) : 0, ii = i - pl * (H >> 3);
+            tq[q] = *reinterpret_cast<const u4 *>((pl ? p.xr_lo : p.xr) + 8 * ii);
         }
 #pragma unroll
         for (int q = 0; q < kGuStgS; ++q) {
             const int i = min((int)threadIdx.x + q * 64 * kGuDecWaves, nsc - 1);
             const int un = i / (2 * kGuUnitRows * nrow), rem = i - un * (2 * kGuUnitRows * nrow);
             const int mat = rem / (kGuUnitRows * nrow), rem2 = rem - mat * (kGuUnitRows * nrow);
-            const int uu = min(kGuDecUnits * b + un, nunits - 1);
+            const int uu = min(UNITS * b + un, nunits - 1);
             const int su = uu / RT, srt = uu - su * RT;
             int se = p.idx[su];
             se = (se >= 0 && se < p.E) ? se : 0;
@@ -886,11 +897,12 @@ __global__ __launch_bounds__(64 * kGuDecWaves) void k_gateup_dec(GateUpParams p)
             }
         }
     } else {  // short rows (small layers): byte copies
-        for (int i = threadIdx.x; i < H; i += blockDim.x) reinterpret_cast<uint16_t *>(x_l)[i] = p.x[i];
-        for (int i = threadIdx.x; i < kGuDecUnits * 2 * kGuUnitRows * SR; i += blockDim.x) {
+        for (int i = threadIdx.x; i < H * NP; i += blockDim.x)
+            reinterpret_cast<uint16_t *>(x_l)[i] = (P2 && i >= H) ? p.xr_lo[i - H] : p.xr[i];
+        for (int i = threadIdx.x; i < UNITS * 2 * kGuUnitRows * SR; i += blockDim.x) {
             const int row = i / SR, o = i - row * SR;
             const int un = row / (2 * kGuUnitRows), mat = (row / kGuUnitRows) & 1, r = row % kGuUnitRows;
-            const int uu = min(kGuDecUnits * b + un, nunits - 1);
+            const int uu = min(UNITS * b + un, nunits - 1);
             const int su = uu / RT, srt = uu - su * RT;
             int se = p.idx[su];
             se = (se >= 0 && se < p.E) ? se : 0;
@@ -904,10 +916,10 @@ __global__ __launch_bounds__(64 * kGuDecWaves) void k_gateup_dec(GateUpParams p)
     }
     __syncthreads();
 
-    if (wave == kGuDecUnits) {  // the shared expert's slice of rows
+    if (wave >= UNITS) {  // the shared expert's slice of rows, split over the shared waves
         if (p.Is > 0) {
-            const int nb = gridDim.x;
-            shared_gateup_rows(p, (int)((int64_t)p.Is * b / nb), (int)((int64_t)p.Is * (b + 1) / nb));
+            const int64_t ns = (int64_t)gridDim.x * (kGuDecWaves - UNITS), si = (int64_t)b * (kGuDecWaves - UNITS) + (wave - UNITS);
+            shared_gateup_rows(p, (int)(p.Is * si / ns), (int)(p.Is * (si + 1) / ns));
         }
         return;
     }
@@ -917,7 +929,7 @@ __global__ __launch_bounds__(64 * kGuDecWaves) void k_gateup_dec(GateUpParams p)
     // copies). Lane group grp's 16-byte weight load of 128-K step k holds
     // K = 128k + 32 grp + [0, 32); MFMA sub-step ss takes K = 128k + 32 grp +
     // 8 ss + [0, 8) on both sides.
-    const uint8_t *xb = x_l + 64 * grp;
+    const uint8_t *xb = x_l + (P2 ? (col & 1) * 2 * H : 0) + 64 * grp;  // P2: column c reads plane c & 1
     const uint8_t *s_g = sc_l + (wave * 2 * kGuUnitRows + (lane & 15)) * SRP;  // this lane's gate row
     const uint8_t *s_u = s_g + kGuUnitRows * SRP;
     v4f accg = v4f{0.0f, 0.0f, 0.0f, 0.0f}, accu = accg;
@@ -956,7 +968,15 @@ __global__ __launch_bounds__(64 * kGuDecWaves) void k_gateup_dec(GateUpParams p)
         load(min(c + 3, NCH - 1), b1);
     }
 
-    // every column holds the token's result: lane 16g (column 0) has rows 4g..4g+3
+    // every column holds the token's result (P2: columns 0 and 1 its hi and
+    // lo parts, added here): lane 16g (column 0) has rows 4g..4g+3
+    if constexpr (P2) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            accg[r] += __shfl_xor(accg[r], 1);
+            accu[r] += __shfl_xor(accu[r], 1);
+        }
+    }
     if (col == 0) {
         float4 a4;
         a4.x = act_fn(accg[0], accu[0], p.act, p.b1, p.b2);
@@ -981,6 +1001,8 @@ struct DownDecParams {
     const uint8_t *dp, *ds;
     int64_t d_sp, d_ss;
     int H, I, E, K, Is, M;
+    int Hr;     // routed output rows (H, or the latent)
+    float *ysh; // the shared expert's rows fp32 [H], or null: ys slot k
     const int32_t *idx;
     const float *act_f;  // fp32 activations [k][I]
     const uint16_t *sh_down;
@@ -991,8 +1013,8 @@ struct DownDecParams {
 constexpr int kDnDecWaves = 4;
 constexpr int kDnMaxTiles = 16;      // tiles per block (LDS sizing)
 constexpr int kDnShPerWave = 4;      // shared rows per wave (at most)
-constexpr int kDnShSl = 3;           // shared slices of 512 prefetched (I_s <= 1536)
-constexpr int kDnStgQ = 2;           // activation float4s per thread (I <= 2048)
+constexpr int kDnShSl = 3;           // shared slices of 512 per load group (the first prefetched)
+constexpr int kDnStgQ = 3;           // activation float4s per thread (I <= 3072)
 constexpr int kDnStgS = 4;           // scale-row staging copies per thread
 
 __host__ __device__ constexpr int dn_dec_lds_bytes(int I)
@@ -1010,7 +1032,7 @@ __global__ __launch_bounds__(64 * kDnDecWaves) void k_down_dec(DownDecParams p)
     const int grp = lane >> 4, col = lane & 15;
     const int I = p.I, KS = I >> 7, SR = I >> 5, NCH = (KS + 3) >> 2;
     const int AQS = I + kXqPad, SRP = SR + kScPad;
-    const int T16 = p.H >> 4, M = p.M;
+    const int T16 = p.Hr >> 4, M = p.M;
     const int j = blockIdx.x / M, i = blockIdx.x - j * M;
     const int t0 = T16 * i / M, t1 = T16 * (i + 1) / M, nt = t1 - t0;
     const int nblk = p.K * M;
@@ -1039,7 +1061,7 @@ __global__ __launch_bounds__(64 * kDnDecWaves) void k_down_dec(DownDecParams p)
     const int Is = p.Is;
     u4 shw[kDnShPerWave][kDnShSl];
     float4 shx[kDnShSl][2];
-    const bool sh_pf = Is > 0 && Is <= 512 * kDnShSl && nsr <= kDnShPerWave;
+    const bool sh_pf = Is > 0 && nsr <= kDnShPerWave;  // the first kDnShSl slices of the shared rows
     if (sh_pf) {
 #pragma unroll
         for (int c = 0; c < kDnShSl; ++c) {
@@ -1206,15 +1228,30 @@ __global__ __launch_bounds__(64 * kDnDecWaves) void k_down_dec(DownDecParams p)
             v = fmaf(bf16f(w4[3] >> 16), x1.w, v);
             a = v;
         };
-        if (sh_pf) {
+        if (sh_pf) {  // slices of 512 in groups of kDnShSl, all the wave's rows at once
             float a4[kDnShPerWave];
 #pragma unroll
             for (int q = 0; q < kDnShPerWave; ++q) a4[q] = 0.0f;
+            for (int c0 = 0; c0 < Is; c0 += 512 * kDnShSl) {
+                if (c0 > 0) {  // the first group was loaded before the routed stream
 #pragma unroll
-            for (int c = 0; c < kDnShSl; ++c)
-                if (c * 512 + lane * 8 < Is)
+                    for (int c = 0; c < kDnShSl; ++c) {
+                        const int ic = min(c0 + c * 512 + lane * 8, Is - 8);
 #pragma unroll
-                    for (int q = 0; q < kDnShPerWave; ++q) dot8(a4[q], shw[q][c], shx[c][0], shx[c][1]);
+                        for (int q = 0; q < kDnShPerWave; ++q) {
+                            const int r = r0 + wave + kDnDecWaves * min(q, max(nsr - 1, 0));
+                            shw[q][c] = *reinterpret_cast<const u4 *>(p.sh_down + (size_t)min(r, p.H - 1) * Is + ic);
+                        }
+                        shx[c][0] = *reinterpret_cast<const float4 *>(p.ash + ic);
+                        shx[c][1] = *reinterpret_cast<const float4 *>(p.ash + ic + 4);
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < kDnShSl; ++c)
+                    if (c0 + c * 512 + lane * 8 < Is)
+#pragma unroll
+                        for (int q = 0; q < kDnShPerWave; ++q) dot8(a4[q], shw[q][c], shx[c][0], shx[c][1]);
+            }
 #pragma unroll
             for (int q = 0; q < kDnShPerWave; ++q) {
 #pragma unroll
@@ -1238,9 +1275,11 @@ __global__ __launch_bounds__(64 * kDnDecWaves) void k_down_dec(DownDecParams p)
     }
     __syncthreads();
     for (int ii = threadIdx.x; ii < nt * 16; ii += blockDim.x)
-        p.ys[(size_t)j * p.H + (size_t)t0 * 16 + ii] = ok ? y_l[ii] : 0.0f;
-    if (Is > 0)
-        for (int ii = threadIdx.x; ii < r1 - r0; ii += blockDim.x) p.ys[(size_t)p.K * p.H + r0 + ii] = sh_l[ii];
+        p.ys[(size_t)j * p.Hr + (size_t)t0 * 16 + ii] = ok ? y_l[ii] : 0.0f;
+    if (Is > 0) {
+        float *yshr = p.ysh ? p.ysh : p.ys + (size_t)p.K * p.Hr;
+        for (int ii = threadIdx.x; ii < r1 - r0; ii += blockDim.x) yshr[r0 + ii] = sh_l[ii];
+    }
 }
 
 // Router-order combine: out[t][o] = sum_j w[t][j] * ys[t][j][o] (j = 0..k-1
@@ -1374,28 +1413,53 @@ hipError_t launch_route(const LayerView &L, const uint16_t *x, int T, int32_t *i
 // thread; row tiles dividing I and H; a down block's tiles fit its LDS).
 static int down_blocks_per_slot(const LayerView &L, int ncu)
 {
-    const int T16 = L.H / 16;
+    const int T16 = L.EK / 16;  // routed output tiles
     int M = std::max(1, (2 * ncu + L.K - 1) / L.K);
     M = std::min(M, T16);
-    while ((T16 + M - 1) / M > kDnMaxTiles) ++M;  // tiles per block fit the LDS staging
+    // tiles per block fit the LDS staging, and their scale rows one pass of
+    // the staging copies (wide rows)
+    auto fits = [&](int m) {
+        const int nt = (T16 + m - 1) / m;
+        return nt <= kDnMaxTiles && (L.I % 512 != 0 || nt * 16 * (L.I / 512) <= 64 * kDnDecWaves * kDnStgS);
+    };
+    while (M < T16 && !fits(M)) ++M;
     return M;
+}
+
+// Routed waves per gate/up block: both kinds of wave should move about the
+// same bytes (a routed unit: 16 rows of gate and up; the shared rows shared
+// out over the other waves of every block).
+static int gu_dec_units(const LayerView &L)
+{
+    const double routed = (double)L.K * L.I * L.EK * 2 * (0.5 + 1.0 / 32), shared = (double)L.Is * L.H * 4;
+    const int u = (int)(4.0 * routed / (routed + shared) + 0.5);
+    return u <= 2 ? 2 : 3;
 }
 
 static bool decode_path_ok(const LayerView &L)
 {
-    if (L.Lt > 0) return false;  // a latent layer takes the grouped path at every T
-    const bool gu = L.H % 512 != 0 || L.H / 8 <= 64 * kGuDecWaves * kGuStgQ;
-    const bool gu_sc = L.H % 512 != 0 || kGuDecUnits * 2 * kGuUnitRows * (L.H / 512) <= 64 * kGuDecWaves * kGuStgS;
-    const bool dn = L.I <= 4 * 64 * kDnDecWaves * kDnStgQ &&  // the activation staging, both row forms
-                    (L.I % 512 != 0 || kDnMaxTiles * 16 * (L.I / 512) <= 64 * kDnDecWaves * kDnStgS);
-    return gu && gu_sc && dn && L.I % kGuUnitRows == 0 && L.H % 16 == 0 && L.H >= 16 * kDnDecWaves;
+    // a latent layer: whole 512-groups (the two-plane staging takes the wide form)
+    if (L.Lt > 0 && (L.EK % 512 != 0 || L.H % 512 != 0)) return false;
+    const int np = L.Lt > 0 ? 2 : 1;
+    const bool gu = L.EK % 512 != 0 || np * L.EK / 8 <= 64 * kGuDecWaves * kGuStgQ;
+    const bool gu_sc = L.EK % 512 != 0 || kGuDecMaxUnits * 2 * kGuUnitRows * (L.EK / 512) <= 64 * kGuDecWaves * kGuStgS;
+    // the activation staging; one tile's scale rows per staging pass at least
+    // (down_blocks_per_slot takes enough blocks for the rest)
+    const bool dn = L.I <= 4 * 64 * kDnDecWaves * kDnStgQ &&
+                    (L.I % 512 != 0 || 16 * (L.I / 512) <= 64 * kDnDecWaves * kDnStgS);
+    return gu && gu_sc && dn && L.I % kGuUnitRows == 0 && L.EK % 16 == 0 && L.EK >= 16 * kDnDecWaves &&
+           L.H >= 16 * kDnDecWaves;
 }
 
 // T = 1: token fp8 expansion, gate/up, down, router-order combine. The
 // router slots are the assignment list (no permutation).
-static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const int32_t *idx,
-                                    const float *w, float *out, float *act, float *ash, char *ys_base,
-                                    hipStream_t s, Profiler *prof, const OutEpi &epi)
+// xr, xr_lo: the routed input (x, or a latent z as hi and lo planes); ysh:
+// the shared rows' own buffer (latent) or null (slot k of the staging rows);
+// out null: no combine (the latent layer combines at its own width).
+static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const uint16_t *xr,
+                                    const uint16_t *xr_lo, const int32_t *idx, const float *w, float *out,
+                                    float *act, float *ash, char *ys_base, float *ysh, hipStream_t s,
+                                    Profiler *prof, const OutEpi &epi)
 {
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1417,6 +1481,9 @@ static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const
     gp.b1 = L.b1;
     gp.b2 = L.b2;
     gp.x = x;
+    gp.xr = xr;
+    gp.xr_lo = xr_lo;
+    gp.Kr = L.EK;
     gp.idx = idx;
     gp.act_f = act;
     gp.sh_gate = L.sh_gate;
@@ -1424,13 +1491,19 @@ static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const
     gp.ash = ash;
     {
         StageMark m(prof, K3MOE_STAGE_GATEUP, s);
-        const int nunits = L.K * (L.I / kGuUnitRows);
-        const unsigned nblk = (unsigned)((nunits + kGuDecUnits - 1) / kGuDecUnits);
-        const size_t lds = gu_dec_lds_bytes(L.H);
-        if (L.H % 512 == 0)
-            k_gateup_dec<true><<<nblk, 64 * kGuDecWaves, lds, s>>>(gp);
+        const int nunits = L.K * (L.I / kGuUnitRows), units = gu_dec_units(L);
+        const unsigned nblk = (unsigned)((nunits + units - 1) / units);
+        const size_t lds = gu_dec_lds_bytes(L.EK, xr_lo ? 2 : 1);
+        if (xr_lo)  // two planes: the wide form only (decode_path_ok)
+            k_gateup_dec<true, 2, true><<<nblk, 64 * kGuDecWaves, lds, s>>>(gp);
+        else if (L.EK % 512 == 0 && units == 2)
+            k_gateup_dec<true, 2, false><<<nblk, 64 * kGuDecWaves, lds, s>>>(gp);
+        else if (L.EK % 512 == 0)
+            k_gateup_dec<true, 3, false><<<nblk, 64 * kGuDecWaves, lds, s>>>(gp);
+        else if (units == 2)
+            k_gateup_dec<false, 2, false><<<nblk, 64 * kGuDecWaves, lds, s>>>(gp);
         else
-            k_gateup_dec<false><<<nblk, 64 * kGuDecWaves, lds, s>>>(gp);
+            k_gateup_dec<false, 3, false><<<nblk, 64 * kGuDecWaves, lds, s>>>(gp);
     }
     float *ys = reinterpret_cast<float *>(ys_base);
     DownDecParams dp{};
@@ -1439,6 +1512,8 @@ static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const
     dp.d_sp = L.d_sp;
     dp.d_ss = L.d_ss;
     dp.H = L.H;
+    dp.Hr = L.EK;
+    dp.ysh = ysh;
     dp.I = L.I;
     dp.E = L.E;
     dp.K = L.K;
@@ -1452,19 +1527,31 @@ static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const
     {
         StageMark m(prof, K3MOE_STAGE_DOWN, s);
         const unsigned nblk = (unsigned)(L.K * dp.M);
-        const size_t lds = dn_dec_lds_bytes(L.I) + 4 * (L.H / nblk + 1);
+        const size_t lds = dn_dec_lds_bytes(L.I) + 4 * (L.H / nblk + 1);  // + the block's shared rows
         if (L.I % 512 == 0)
             k_down_dec<true><<<nblk, 64 * kDnDecWaves, lds, s>>>(dp);
         else
             k_down_dec<false><<<nblk, 64 * kDnDecWaves, lds, s>>>(dp);
     }
-    {
+    if (out) {
         StageMark m(prof, K3MOE_STAGE_COMBINE, s);
         k_combine<<<(unsigned)((L.H / 4 + kCombineThreads - 1) / kCombineThreads), kCombineThreads, 0, s>>>(
             ys, w, idx, 1, L.K, L.H, L.E, L.Is > 0, out, L.errors, epi.resid, epi.ob);
     }
     return hipGetLastError();
 }
+
+// One token of a latent layer on the single-token kernels: the routed
+// experts read z's planes and write their rows (width EK) to the staging
+// rows, the shared expert reads x and writes ysh [H].
+hipError_t launch_latent_t1(const LayerView &L, const uint16_t *x, const uint16_t *zh, const uint16_t *zl,
+                            const int32_t *idx, float *act, float *ash, char *ys_base, float *ysh, hipStream_t s,
+                            Profiler *prof)
+{
+    return launch_forward_t1(L, x, zh, zl, idx, nullptr, nullptr, act, ash, ys_base, ysh, s, prof, OutEpi());
+}
+
+bool latent_t1_ok(const LayerView &L) { return decode_path_ok(L); }
 
 // T > 1 (or shapes the single-token kernels do not take): token -> expert
 // permutation, grouped GEMMs, router-order combine.
@@ -1509,8 +1596,8 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const in
     float *ys = reinterpret_cast<float *>(ws + lay.ys);
 
     if (T == 1 && decode_path_ok(L))
-        return launch_forward_t1(L, x, idx, w, out, reinterpret_cast<float *>(ws + lay.act),
-                                 reinterpret_cast<float *>(ws + lay.ash), ws + lay.ys, s, prof, epi);
+        return launch_forward_t1(L, x, x, nullptr, idx, w, out, reinterpret_cast<float *>(ws + lay.act),
+                                 reinterpret_cast<float *>(ws + lay.ash), ws + lay.ys, nullptr, s, prof, epi);
     launch_perm(L, idx, T, ws, lay, s, prof);
     // activations: routed bf16 hi and lo [T*k][I] in the fp8-term region
     // (4 bytes per element either way); shared bf16 hi and lo [T][Is] in the

@@ -464,8 +464,6 @@ hipError_t launch_latent_forward(const LayerView &L, const uint16_t *x, int T, c
     float *acc = reinterpret_cast<float *>(ws + lay.lat_acc);
     uint16_t *nh = reinterpret_cast<uint16_t *>(ws + lay.lat_n), *nl = nh + (size_t)T * Lt;
     float *ysh = L.Is > 0 ? reinterpret_cast<float *>(ws + lay.lat_ysh) : nullptr;
-    // the streamed shared down rows leave K-slice partials (the grouped GEMM one sum)
-    const int ysh_slices = stream_shared_ok(L, T) ? stream_shared_down_slices(L.Lt, L.Is, T) : 1;
     float *part = reinterpret_cast<float *>(ws + lay.lat_part);
     float *ys = reinterpret_cast<float *>(ws + lay.ys);
     hipError_t e;
@@ -481,17 +479,26 @@ hipError_t launch_latent_forward(const LayerView &L, const uint16_t *x, int T, c
             return e;
         }
     }
-    launch_perm(L, idx, T, ws, lay, s, prof);
-    uint16_t *act_hi = reinterpret_cast<uint16_t *>(ws + lay.act);
-    uint16_t *act_lo = act_hi + (size_t)T * L.K * L.I;
-    uint16_t *ash_hi = reinterpret_cast<uint16_t *>(ws + lay.ash);
-    uint16_t *ash_lo = ash_hi + (size_t)T * L.Is;
-    e = launch_grouped(L, x, zh, zl, T, reinterpret_cast<int32_t *>(ws + lay.active_n),
-                       reinterpret_cast<int32_t *>(ws + lay.active_e), reinterpret_cast<int32_t *>(ws + lay.active_off),
-                       reinterpret_cast<int32_t *>(ws + lay.sorted), act_hi, act_lo, ash_hi, ash_lo,
-                       reinterpret_cast<float *>(ws + lay.sh_part), reinterpret_cast<int2 *>(ws + lay.tiles_gu),
-                       reinterpret_cast<int2 *>(ws + lay.tiles_dn), reinterpret_cast<int32_t *>(ws + lay.light),
-                       reinterpret_cast<int32_t *>(ws + lay.tile_n), ys, ysh, s, prof);
+    int ysh_slices = 1;  // the shared rows' K-slice partials (the streamed form only)
+    if (one && latent_t1_ok(L)) {
+        // the router slots are the assignments: no permutation, the single-token kernels
+        e = launch_latent_t1(L, x, zh, zl, idx, reinterpret_cast<float *>(ws + lay.act),
+                             reinterpret_cast<float *>(ws + lay.ash), ws + lay.ys, ysh, s, prof);
+    } else {
+        launch_perm(L, idx, T, ws, lay, s, prof);
+        uint16_t *act_hi = reinterpret_cast<uint16_t *>(ws + lay.act);
+        uint16_t *act_lo = act_hi + (size_t)T * L.K * L.I;
+        uint16_t *ash_hi = reinterpret_cast<uint16_t *>(ws + lay.ash);
+        uint16_t *ash_lo = ash_hi + (size_t)T * L.Is;
+        e = launch_grouped(L, x, zh, zl, T, reinterpret_cast<int32_t *>(ws + lay.active_n),
+                           reinterpret_cast<int32_t *>(ws + lay.active_e),
+                           reinterpret_cast<int32_t *>(ws + lay.active_off), reinterpret_cast<int32_t *>(ws + lay.sorted),
+                           act_hi, act_lo, ash_hi, ash_lo, reinterpret_cast<float *>(ws + lay.sh_part),
+                           reinterpret_cast<int2 *>(ws + lay.tiles_gu), reinterpret_cast<int2 *>(ws + lay.tiles_dn),
+                           reinterpret_cast<int32_t *>(ws + lay.light), reinterpret_cast<int32_t *>(ws + lay.tile_n),
+                           ys, ysh, s, prof);
+        ysh_slices = stream_shared_ok(L, T) ? stream_shared_down_slices(L.Lt, L.Is, T) : 1;
+    }
     if (e != hipSuccess) return e;
     {
         StageMark m(prof, K3MOE_STAGE_COMBINE, s);  // the routed aggregate [T][L], router order

@@ -289,11 +289,12 @@ def test_pages_expert_shape(T, shared):
     assert rel_err(out, ref, denom) <= REL_TOL
 
 
-@pytest.mark.parametrize("T,inter,hidden", [(1, 2176, 256), (1, 1664, 256), (2, 2176, 256), (1, 2560, 512)])
+@pytest.mark.parametrize("T,inter,hidden", [(1, 3200, 256), (1, 2176, 256), (1, 1664, 256), (2, 3200, 256),
+                                           (1, 3584, 512)])
 def test_inter_widths_past_and_below_decode_staging(T, inter, hidden):
     # intermediate widths that are not multiples of 512, one past the
-    # single-token down kernel's activation staging (2048 elements: such a
-    # layer takes the grouped path) and one within it; and 2560 at hidden
+    # single-token down kernel's activation staging (3072 elements: such a
+    # layer takes the grouped path) and two within it; and 3584 at hidden
     # 512, where one token takes the streaming kernels with the shared
     # expert cut into hidden-dimension slices (their partials need room in
     # the workspace at T = 1 too)
