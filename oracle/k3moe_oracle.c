@@ -41,8 +41,9 @@
  * value of the sigmoid of the fp32 logit, evaluated in fp64 and rounded once.
  *
  * The SwiGLU activation (g * sigmoid(g) * u) is a second activation kind the
- * layer can be configured with; the pages use SiTU-GLU. SwiGLU is pinned only
- * through the SiTU limit of large betas (parity unpinned beyond that).
+ * layer can be configured with; the pages use SiTU-GLU. SwiGLU is pinned by
+ * closed forms (the sigmoid is exactly 3/4 and 1/4 at +-ln 3, zero gate or
+ * up, the large-gate limits) and by the SiTU limit of large betas.
  */
 #include <math.h>
 #include <stdint.h>

@@ -3,6 +3,7 @@
 Source: "kimi-k3-in-c" README §9 (k3_situ_glu: SiTU-GLU with betas 4 and 25,
 the sigmoid on the raw gate, the bound b1*b2 = 100)."""
 import json
+import math
 import os
 
 import numpy as np
@@ -69,3 +70,17 @@ def test_swiglu_kind_is_silu_glu():
             got = oracle.act(g, u, oracle.ACT_SWIGLU)
             ref = silu_glu(g, u)
             assert abs(got - ref) <= 1e-14 * max(1.0, abs(ref))
+
+
+def test_swiglu_closed_forms():
+    # sigmoid(ln 3) = 3/4 and sigmoid(-ln 3) = 1/4 exactly, so
+    # g * sigmoid(g) * u is known in closed form there; g = 0 or u = 0 give 0;
+    # a large gate passes g * u, a very negative one gives 0
+    l3 = math.log(3.0)
+    for u in (-2.0, 0.5, 3.0):
+        assert abs(oracle.act(l3, u, oracle.ACT_SWIGLU) - 0.75 * l3 * u) <= 1e-15 * abs(u) * 2
+        assert abs(oracle.act(-l3, u, oracle.ACT_SWIGLU) - (-0.25 * l3 * u)) <= 1e-15 * abs(u) * 2
+        assert oracle.act(0.0, u, oracle.ACT_SWIGLU) == 0.0
+        assert abs(oracle.act(60.0, u, oracle.ACT_SWIGLU) - 60.0 * u) <= 1e-12 * abs(60.0 * u)
+        assert abs(oracle.act(-60.0, u, oracle.ACT_SWIGLU)) <= 60.0 * abs(u) * math.exp(-60.0)  # sigmoid(-60) < e^-60
+    assert oracle.act(1.3, 0.0, oracle.ACT_SWIGLU) == 0.0
