@@ -62,7 +62,7 @@ typedef enum {
     K3MOE_OK = 0,
     K3MOE_E_INVALID_ARG = 1,       /* NULL pointer, negative size, ...       */
     K3MOE_E_CONFIG = 2,            /* config field missing or out of range   */
-    K3MOE_E_UNSUPPORTED_SHAPE = 3, /* a size this build's kernels refuse     */
+    K3MOE_E_UNSUPPORTED_SHAPE = 3, /* a size the library's kernels refuse  */
     K3MOE_E_ALIGNMENT = 4,         /* a pointer or stride not 16-byte aligned */
     K3MOE_E_WORKSPACE = 5,         /* workspace NULL, too small or misaligned */
     K3MOE_E_OUT_OF_MEMORY = 6,     /* device memory could not be had         */
