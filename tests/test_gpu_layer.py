@@ -431,3 +431,54 @@ def test_repeated_ids_within_a_token(latent):
         ref, denom, drops = oracle_forward(spec, x_np, idx, w)
         assert drops == 0
         assert rel_err(out, ref, denom) <= REL_TOL, idx.tolist()
+
+
+@pytest.mark.parametrize("n_experts,topk", [(8, 8), (8, 1), (1, 1), (4, 4)])
+def test_degenerate_routing(n_experts, topk):
+    # every expert selected (top-k = E), a single expert per token, a single
+    # expert in the layer: routes and outputs against the oracle
+    spec = synth.LayerSpec(hidden=256, inter=128, n_experts=n_experts, topk=topk, shared_inter=128,
+                           bias_std=0.05, seed=300 + 10 * n_experts + topk)
+    sd = _dev()
+    t = sd.layer_tensors(spec, 0, DEV)
+    layer = sd.make_layer(spec, t)
+    for T in (1, 7):
+        Wr, bias = synth.make_router(spec), synth.make_bias(spec)
+        x_np = synth.make_x(spec, T)
+        idx_r, w_r, _, ch = oracle.route(x_np, Wr, bias, spec.topk, want_detail=True)
+        x, idx, w, _ = _route_gpu(layer, x_np, T, spec.topk)
+        check_route(idx.cpu().numpy(), w.cpu().numpy(), idx_r, w_r, ch, spec.topk)
+        if topk == n_experts:  # every expert, in descending selection score
+            assert all(sorted(r) == list(range(n_experts)) for r in idx.cpu().numpy().tolist())
+        out = _forward_gpu(layer, x, idx_r, w_r)
+        ref, denom, _ = oracle_forward(spec, x_np, idx_r, w_r)
+        assert rel_err(out, ref, denom) <= REL_TOL
+
+
+def test_full_largest_batch_and_one_past_it():
+    # the largest batch the 32-bit batch offsets take at this shape
+    # (T * topk * inter * 2 bytes below 2 GiB: T = 43,690), sampled tokens
+    # against the oracle; one token more is refused before any launch
+    import mxfp4_routed_expert_sigmoid_amd as k3
+    spec, t, layer = _full()
+    T = 43690
+    x_np = synth.make_x(spec, T, attempt=3)
+    x, idx, w, _ = _route_gpu(layer, x_np, T, spec.topk)
+    idx_g, w_g = idx.cpu().numpy(), w.cpu().numpy()
+    sample = [0, 12345, 30001, T - 1]
+    Wr, bias = synth.make_router(spec), synth.make_bias(spec)
+    idx_r, w_r, _, ch = oracle.route(x_np[sample], Wr, bias, spec.topk, want_detail=True)
+    check_route(idx_g[sample], w_g[sample], idx_r, w_r, ch, spec.topk)
+    out = _forward_gpu(layer, x, idx_g, w_g)
+    ref, denom, _ = oracle_forward(spec, x_np, idx_g, w_g, tokens=sample)
+    assert rel_err(out[sample], ref, denom) <= REL_TOL
+    del out
+    with pytest.raises(k3.K3MoeError):
+        layer.workspace_size(T + 1)
+    big = torch.empty((T + 1, spec.hidden), dtype=torch.bfloat16, device=DEV)
+    i1 = torch.empty((T + 1, spec.topk), dtype=torch.int32, device=DEV)
+    w1 = torch.empty((T + 1, spec.topk), dtype=torch.float32, device=DEV)
+    ws = layer.workspace(T)
+    with pytest.raises(k3.K3MoeError):
+        layer.route(big, i1, w1, workspace=ws)
+    torch.cuda.synchronize()
