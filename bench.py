@@ -12,7 +12,7 @@ shared expert of inter 1536, bias N(0, 0.01)):
   decode   T = 1 token per step (default; the metric's configuration)
   batched  T = 64, uniformly random routing
   prefill  T = 2048, Zipf(1.1)-skewed routing
-  latent   T = 1 on the pages' latent layer: hidden 7168, experts in a 3584
+  latent   T = 1 (or --tokens) on the pages' latent layer: hidden 7168, experts in a 3584
            latent with inter 3072 (the same 17,547,264 B per expert), two
            shared experts of 3072 (one of 6144) on x, bf16 down- and
            up-projections, RMSNorm of the aggregate
@@ -25,7 +25,7 @@ shared expert of inter 1536, bias N(0, 0.01)):
            layer's own gain, route with its own router, experts, the residual
            add in the last kernel); the norm keeps every layer's routes
            spread (a plain residual grows until the sigmoid scores saturate)
-  cache    T = 1 on the full shape with the 896 experts in pinned host memory
+  cache    T = 1 (or --tokens) on the full shape with the 896 experts in pinned host memory
            and --slots of them in an HBM slot arena (k3moe_cache_forward):
            misses are read over the host link each step; --routing picks
            flat (normal) or Zipf(1.1) routes; reports the resident hit rate
@@ -81,7 +81,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--slots", type=int, default=224, help="cache: HBM expert slots")
     ap.add_argument("--layers", type=int, default=8, help="stack: resident layers")
-    ap.add_argument("--tokens", type=int, default=1, help="stack: tokens per step")
+    ap.add_argument("--tokens", type=int, default=1, help="stack, latent, cache: tokens per step")
     ap.add_argument("--routing", choices=("normal", "zipf"), default=None,
                     help="cache: routing of the token pool (default normal)")
     args = ap.parse_args()
@@ -101,8 +101,8 @@ def main():
     dev = "cuda:0"
     torch.cuda.set_device(0)
     T, routing, pool = {"decode": (1, "normal", 64), "batched": (64, "normal", 8),
-                        "prefill": (2048, "zipf", 2), "latent": (1, "normal", 64),
-                        "step": (1, "normal", 64), "cache": (1, "normal", 256),
+                        "prefill": (2048, "zipf", 2), "latent": (args.tokens, "normal", 64 if args.tokens == 1 else 8),
+                        "step": (1, "normal", 64), "cache": (args.tokens, "normal", 256 if args.tokens == 1 else 32),
                         "stack": (args.tokens, "normal", 8)}[args.workload]
     nl = args.layers if args.workload == "stack" else 1
     if args.workload == "cache" and args.routing:

@@ -88,8 +88,8 @@ WsLayout ws_layout(const k3moe_config &c, int64_t T)
         L.lat_n = take((size_t)T * Lt * 4);
         // the shared expert's output, in K-slice partial sums for a few tokens
         size_t ysh = sizeof(float) * T * H;
-        for (int64_t t = 1; t <= std::min<int64_t>(T, 64); ++t)
-            ysh = std::max(ysh, sizeof(float) * stream_shared_down_slices((int)Lt, (int)Is, (int)t) * t * H);
+        for (int64_t t = 1; t <= std::min<int64_t>(T, 128); ++t)  // the streamed shared expert: T <= 128
+            ysh = std::max(ysh, sizeof(float) * stream_shared_down_slices((int)Lt, (int)Is, (int)t, (int)I) * t * H);
         L.lat_ysh = take(ysh);
         // projection partial sums: the largest over T' <= T of either projection
         // (one slice at least: the projections always sum through them)

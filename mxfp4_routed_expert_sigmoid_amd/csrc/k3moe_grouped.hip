@@ -492,7 +492,7 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t 
     const int rb_s = (L.Is + kTileRows - 1) / kTileRows;
     const bool stream = stream_path_ok(L), stream_dn = stream_down_ok(L, T);
     const bool sh_stream = stream_shared_ok(L, T);
-    const int smax_gu = stream ? stream_max_tokens() : 0, smax_dn = stream_dn ? stream_max_tokens() : 0;
+    const int smax_gu = stream ? stream_max_tokens() : 0, smax_dn = stream_dn ? stream_down_rows(L, T) : 0;
     // grids cover the most tiles the split can produce (most blocks exit at once)
     const size_t cap_gu = grouped_tile_cap(T, L.K, L.E, TG, smax_gu), cap_dn = grouped_tile_cap(T, L.K, L.E, TD, smax_dn);
     int32_t *light_gu = light, *light_dn = light + L.E;

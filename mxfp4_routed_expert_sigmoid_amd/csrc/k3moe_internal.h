@@ -216,7 +216,8 @@ bool stream_down_ok(const LayerView &L, int T);
 int stream_max_tokens();
 int stream_shared_slices(int T);
 bool stream_shared_ok(const LayerView &L, int T);
-int stream_shared_down_slices(int Lt, int Is, int T);
+int stream_shared_down_slices(int Lt, int Is, int T, int I);
+int stream_down_rows(const LayerView &L, int T);
 hipError_t launch_stream_gu(const LayerView &L, const uint16_t *x, const uint16_t *xr, const uint16_t *xr_lo,
                             int T, const int32_t *active_e, const int32_t *active_off, const int32_t *sorted,
                             const int32_t *light, const int32_t *light_n, bool with_shared, uint16_t *act_hi,

@@ -497,7 +497,7 @@ hipError_t launch_latent_forward(const LayerView &L, const uint16_t *x, int T, c
                            reinterpret_cast<int2 *>(ws + lay.tiles_gu), reinterpret_cast<int2 *>(ws + lay.tiles_dn),
                            reinterpret_cast<int32_t *>(ws + lay.light), reinterpret_cast<int32_t *>(ws + lay.tile_n),
                            ys, ysh, s, prof);
-        ysh_slices = stream_shared_ok(L, T) ? stream_shared_down_slices(L.Lt, L.Is, T) : 1;
+        ysh_slices = stream_shared_ok(L, T) ? stream_shared_down_slices(L.Lt, L.Is, T, L.I) : 1;
     }
     if (e != hipSuccess) return e;
     {

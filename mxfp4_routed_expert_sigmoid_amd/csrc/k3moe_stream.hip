@@ -539,9 +539,9 @@ __global__ __launch_bounds__(64 * kDWaves) void k_dn_stream(DnStreamParams p)
     const int RBT = (R + kDBlkRows - 1) / kDBlkRows;
     const int rb0 = run * p.run_rb, rb1 = min(RBT, rb0 + p.run_rb);
     if (rb0 >= rb1) return;
-    if (item < p.sh_items) {  // shared expert: token group tg, K slice ks
+    if (item < p.sh_items) {  // shared expert: token group tg (p.stg tokens), K slice ks
         const int tg = item / p.sh_ks, ks = item - tg * p.sh_ks;
-        const int t0 = tg * kSTok, n = min(kSTok, p.T - t0);
+        const int t0 = tg * p.stg, n = min(p.stg, p.T - t0);
         if (threadIdx.x < kSTok) {
             const int t = t0 + min((int)threadIdx.x, n - 1);
             hdr[kHdrKey + threadIdx.x] = hdr[kHdrVal + threadIdx.x] = t;
@@ -582,30 +582,46 @@ bool stream_path_ok(const LayerView &L)
            L.I % kSBlkRows == 0 && L.H % kSBlkRows == 0 && L.EK % kSBlkRows == 0 && L.Is % kSBlkRows == 0;
 }
 
-// The down kernel stages a whole item's activations (at most min(16, T)
-// token rows): it takes the routed light experts when they fit in LDS (and
-// the shared expert likewise).
-bool stream_down_ok(const LayerView &L, int T)
-{
-    return stream_path_ok(L) && dn_stream_lds_bytes(std::max(L.I, L.Is), std::min(T, kSTok)) <= 160 * 1024 &&
-           (L.Is == 0 || L.Is % group_k<true>() == 0);
-}
-
 int stream_max_tokens() { return kSTok; }
 
-bool stream_shared_ok(const LayerView &L, int T) { return L.Is > 0 && T <= 8 * kSTok && stream_down_ok(L, T); }
-
 // K slices of the shared expert's down rows when its output goes to a
-// buffer of its own (fp32 partials summed in order by the consumer): for one
-// token group, so its few row blocks (one per 256 rows of H) do not outlast
-// the routed experts' blocks. Each slice a multiple of the bf16 K group.
-int stream_shared_down_slices(int Lt, int Is, int T)
+// buffer of its own (a latent layer: fp32 partials summed in order by the
+// consumer). For one token group, 8 (or 4, 2) slices so its few row blocks
+// (one per 256 rows of H) do not outlast the routed experts' blocks; for
+// more tokens, the fewest that keep a slice no wider than the routed K, so
+// the shared rows never need more LDS than the routed ones. Each slice a
+// multiple of the bf16 K group.
+int stream_shared_down_slices(int Lt, int Is, int T, int I)
 {
-    if (Lt == 0 || Is == 0 || T > kSTok) return 1;
-    for (int S = 8; S > 1; S /= 2)
-        if (Is % (S * group_k<false>()) == 0) return S;
+    if (Lt == 0 || Is == 0) return 1;
+    if (T <= kSTok) {
+        for (int S = 8; S > 1; S /= 2)
+            if (Is % (S * group_k<false>()) == 0) return S;
+        return 1;
+    }
+    for (int S = 1; S <= 8; S *= 2)
+        if (Is / S <= I && Is % (S * group_k<false>()) == 0) return S;
     return 1;
 }
+
+// Token rows the down kernel stages per item: min(16, T), fewer when both
+// activation planes of that many rows at the widest K it stages (the routed
+// I, or the shared rows' slice) would not fit in LDS. It is also the light
+// limit of the down stage (an item never has more distinct tokens than
+// assignments) and the shared expert's token-group size. 0: nothing fits.
+int stream_down_rows(const LayerView &L, int T)
+{
+    const int KD = std::max(L.I, L.Is / stream_shared_down_slices(L.Lt, L.Is, T, L.I));
+    const int fit = (160 * 1024 - kHdrBytes) / (2 * (2 * KD + kSPad));
+    return std::min(std::min(T, kSTok), fit);
+}
+
+bool stream_down_ok(const LayerView &L, int T)
+{
+    return stream_path_ok(L) && stream_down_rows(L, T) >= 1 && (L.Is == 0 || L.Is % group_k<true>() == 0);
+}
+
+bool stream_shared_ok(const LayerView &L, int T) { return L.Is > 0 && T <= 8 * kSTok && stream_down_ok(L, T); }
 
 // Slices of the shared expert's hidden dimension for small batches, where
 // its few gate/up blocks (one per 128 rows and token group) would otherwise
@@ -703,9 +719,9 @@ hipError_t launch_stream_dn(const LayerView &L, int T, const int32_t *active_e, 
     p.sorted = sorted;
     p.light = light;
     p.light_n = light_n;
-    p.sh_ks = ysh ? stream_shared_down_slices(L.Lt, L.Is, T) : 1;
-    p.sh_items = with_shared ? (T + kSTok - 1) / kSTok * p.sh_ks : 0;
-    p.stg = std::min(T, kSTok);
+    p.sh_ks = ysh ? stream_shared_down_slices(L.Lt, L.Is, T, L.I) : 1;
+    p.stg = stream_down_rows(L, T);
+    p.sh_items = with_shared ? (T + p.stg - 1) / p.stg * p.sh_ks : 0;
     // each item's rows in `runs` blocks of run_rb 256-row blocks: about 7 row
     // blocks per run, fewer when there are few items (about 512 blocks)
     const int64_t cap = std::min<int64_t>(L.E, (int64_t)T * L.K);
