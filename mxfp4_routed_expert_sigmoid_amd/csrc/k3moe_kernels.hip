@@ -364,7 +364,10 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v)
 // among the candidates {key >= tau}. When there are at most 64 candidates
 // (the usual case: about k of them), they are gathered in LDS, each takes
 // its rank in the order above by comparing against all of them, and the
-// first k ranks are the picks. With more candidates (heavy ties) the wave
+// first k ranks are the picks. A candidate is held as one 64-bit word, key in
+// the high half and the complement of its expert index in the low half, so
+// that order is a single unsigned comparison; the 64 slots are prefilled with
+// 0, which no candidate is below. With more candidates (heavy ties) the wave
 // falls back to k rounds of a wave-wide maximum, the lowest lane holding it
 // winning and rescanning its keys.
 //
@@ -377,14 +380,13 @@ __device__ __forceinline__ uint32_t order_key(float v)
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // > 0 for every float
 }
 
-template <int NQ>
+template <int NQ, bool V4>
 __global__ __launch_bounds__(64) void k_topk(const float *__restrict__ sc, const float *__restrict__ ch,
                                              int E, int K, int renorm, float rscale,
                                              int32_t *__restrict__ idx, float *__restrict__ w)
 {
     __shared__ uint32_t lmax_l[64];
-    __shared__ uint32_t ck_l[64];  // candidates: key, expert, score
-    __shared__ int ci_l[64];
+    __shared__ uint64_t cc_l[64];  // candidates: key << 32 | ~expert, score
     __shared__ float cs_l[64];
     __shared__ int pi_l[kMaxTopk];  // picks in router order: expert, score
     __shared__ float ps_l[kMaxTopk];
@@ -394,12 +396,24 @@ __global__ __launch_bounds__(64) void k_topk(const float *__restrict__ sc, const
     const float *sr = sc + (size_t)t * E;
     const int e0 = lane * NQ;
     // the selection scores and the scores are loaded together, every load
-    // issued before the first is used (clamped index, no branch)
+    // issued before the first is used (clamped index, no branch); V4 (E a
+    // multiple of 4, rows 16-byte aligned): 16-byte loads, whole or clamped
     float raw[NQ], sv[NQ];
+    if constexpr (V4) {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        raw[q] = c[min(e0 + q, E - 1)];
-        sv[q] = sr[min(e0 + q, E - 1)];
+        for (int q = 0; q < NQ; q += 4) {
+            const int b = min(e0 + q, E - 4);
+            const float4 a = *reinterpret_cast<const float4 *>(c + b);
+            const float4 d = *reinterpret_cast<const float4 *>(sr + b);
+            raw[q] = a.x, raw[q + 1] = a.y, raw[q + 2] = a.z, raw[q + 3] = a.w;
+            sv[q] = d.x, sv[q + 1] = d.y, sv[q + 2] = d.z, sv[q + 3] = d.w;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            raw[q] = c[min(e0 + q, E - 1)];
+            sv[q] = sr[min(e0 + q, E - 1)];
+        }
     }
     uint32_t v[NQ];
 #pragma unroll
@@ -411,6 +425,7 @@ __global__ __launch_bounds__(64) void k_topk(const float *__restrict__ sc, const
     // tau: the lane maximum of rank k-1 (ranks 0..63 distinct: equal maxima
     // by lane)
     lmax_l[lane] = lm;
+    cc_l[lane] = 0ull;
     __syncthreads();
     int rank = 0;
 #pragma unroll 16
@@ -429,8 +444,7 @@ __global__ __launch_bounds__(64) void k_topk(const float *__restrict__ sc, const
         const uint64_t m = __ballot(in);
         const int pos = C + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
         if (in && pos < 64) {
-            ck_l[pos] = v[q];
-            ci_l[pos] = e0 + q;
+            cc_l[pos] = ((uint64_t)v[q] << 32) | (uint32_t)~(uint32_t)(e0 + q);
             cs_l[pos] = sv[q];
         }
         C += __popcll(m);
@@ -440,18 +454,13 @@ __global__ __launch_bounds__(64) void k_topk(const float *__restrict__ sc, const
     int mine = 0;
     float mine_s = 0.0f;  // score of pick j, held by lane j
     if (C <= 64) {
-        if (lane < C) {
-            const uint32_t k0 = ck_l[lane];
-            const int i0 = ci_l[lane];
-            int r = 0;
-            for (int j = 0; j < C; ++j) {
-                const uint32_t kj = ck_l[j];
-                r += (kj > k0 || (kj == k0 && ci_l[j] < i0)) ? 1 : 0;
-            }
-            if (r < K) {
-                pi_l[r] = i0;
-                ps_l[r] = cs_l[lane];
-            }
+        const uint64_t k0 = cc_l[lane];
+        int r = 0;
+#pragma unroll
+        for (int j = 0; j < 64; ++j) r += cc_l[j] > k0 ? 1 : 0;
+        if (lane < C && r < K) {
+            pi_l[r] = (int)~(uint32_t)k0;
+            ps_l[r] = cs_l[lane];
         }
         __syncthreads();
         if (lane < K) {
@@ -1368,7 +1377,12 @@ template <int NQ>
 static void topk_launch(int T, hipStream_t s, const float *sc, const float *ch, const LayerView &L,
                         int32_t *idx, float *w)
 {
-    k_topk<NQ><<<T, 64, 0, s>>>(sc, ch, L.E, L.K, L.renorm, L.routed_scale, idx, w);
+    // 16-byte loads need whole quads of experts per lane and 16-byte aligned
+    // rows (the workspace regions are 256-aligned)
+    if (NQ % 4 == 0 && L.E % 4 == 0)
+        k_topk<NQ, (NQ % 4 == 0)><<<T, 64, 0, s>>>(sc, ch, L.E, L.K, L.renorm, L.routed_scale, idx, w);
+    else
+        k_topk<NQ, false><<<T, 64, 0, s>>>(sc, ch, L.E, L.K, L.renorm, L.routed_scale, idx, w);
 }
 
 hipError_t launch_route(const LayerView &L, const uint16_t *x, int T, int32_t *idx, float *w,
