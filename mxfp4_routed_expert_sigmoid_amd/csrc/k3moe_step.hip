@@ -20,7 +20,10 @@ __device__ __forceinline__ uint32_t pn_bf16(float f)
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// One block per token; n % 4 == 0.
+// One block per token; n % 4 == 0. A row of at most kPnThreads * kPnV float4
+// (n <= 8192) is read once: the gain is loaded beside it and both stay in
+// registers across the reduction, so the only memory latency before the
+// stores is the first one.
 __global__ __launch_bounds__(kPnThreads) void k_prenorm(const float *__restrict__ h, int n,
                                                         const float *__restrict__ gamma, float eps,
                                                         uint16_t *__restrict__ x)
@@ -29,8 +32,27 @@ __global__ __launch_bounds__(kPnThreads) void k_prenorm(const float *__restrict_
     __shared__ float inv_sh;
     const int t = blockIdx.x, tid = threadIdx.x, nv = n / 4;
     const float4 *a = reinterpret_cast<const float4 *>(h + (size_t)t * n);
+    const float4 *gm = reinterpret_cast<const float4 *>(gamma);
+    const bool one = nv <= kPnThreads * kPnV;
+    float4 v1[kPnV], g1[kPnV];
     double ss = 0.0;
-    for (int c0 = 0; c0 < nv; c0 += kPnThreads * kPnV) {
+    if (one) {
+#pragma unroll
+        for (int j = 0; j < kPnV; ++j) {
+            const int i = min(tid + kPnThreads * j, nv - 1);
+            v1[j] = a[i];
+            g1[j] = gm[i];
+        }
+#pragma unroll
+        for (int j = 0; j < kPnV; ++j) {
+            if (tid + kPnThreads * j >= nv) v1[j] = float4{0.0f, 0.0f, 0.0f, 0.0f};
+            ss = fma((double)v1[j].x, (double)v1[j].x, ss);
+            ss = fma((double)v1[j].y, (double)v1[j].y, ss);
+            ss = fma((double)v1[j].z, (double)v1[j].z, ss);
+            ss = fma((double)v1[j].w, (double)v1[j].w, ss);
+        }
+    }
+    for (int c0 = 0; !one && c0 < nv; c0 += kPnThreads * kPnV) {
         float4 v[kPnV];
 #pragma unroll
         for (int j = 0; j < kPnV; ++j) {
@@ -57,9 +79,17 @@ __global__ __launch_bounds__(kPnThreads) void k_prenorm(const float *__restrict_
     }
     __syncthreads();
     const float inv = inv_sh;
-    const float4 *gm = reinterpret_cast<const float4 *>(gamma);
     uint2 *xo = reinterpret_cast<uint2 *>(x + (size_t)t * n);
-    for (int c0 = 0; c0 < nv; c0 += kPnThreads * kPnV) {
+    if (one) {
+#pragma unroll
+        for (int j = 0; j < kPnV; ++j) {
+            const int i = tid + kPnThreads * j;
+            if (i < nv)
+                xo[i] = uint2{pn_bf16(v1[j].x * inv * g1[j].x) | (pn_bf16(v1[j].y * inv * g1[j].y) << 16),
+                              pn_bf16(v1[j].z * inv * g1[j].z) | (pn_bf16(v1[j].w * inv * g1[j].w) << 16)};
+        }
+    }
+    for (int c0 = 0; !one && c0 < nv; c0 += kPnThreads * kPnV) {
         float4 v[kPnV], g[kPnV];
 #pragma unroll
         for (int j = 0; j < kPnV; ++j) {

@@ -110,6 +110,16 @@ def test_mid_latent_step(T):
     _step(spec, layer, T)
 
 
+@pytest.mark.parametrize("hidden", [8192, 8704])
+def test_wide_row_step(hidden):
+    # rows up to 8192 are normed from registers in one read, wider ones in two
+    # passes over the row
+    spec = synth.LayerSpec(hidden=hidden, inter=128, n_experts=8, topk=2, shared_inter=128,
+                           bias_std=0.05, seed=160 + hidden % 7)
+    _, layer = _layer(spec)
+    _step(spec, layer, 3)
+
+
 def test_step_refusals():
     import mxfp4_routed_expert_sigmoid_amd as k3
     spec = synth.LayerSpec(hidden=256, inter=128, n_experts=8, topk=2, shared_inter=0,
