@@ -372,6 +372,21 @@ def test_full_decode_T1():
     assert np.array_equal(out, _forward_gpu(layer, x, idx_r, w_r))
 
 
+@pytest.mark.parametrize("T", [3, 4])
+def test_full_small_batch_per_token(T):
+    # batches of a few tokens run the single-token kernels once per token,
+    # sharing one token's workspace rows in stream order
+    spec, t, layer = _full()
+    Wr, bias = synth.make_router(spec), synth.make_bias(spec)
+    x_np, idx_r, w_r, logits, ch, _ = _certified_x(spec, T, Wr, bias)
+    x, idx, w, _ = _route_gpu(layer, x_np, T, spec.topk)
+    check_route(idx.cpu().numpy(), w.cpu().numpy(), idx_r, w_r, ch, spec.topk)
+    out = _forward_gpu(layer, x, idx_r, w_r)
+    ref, denom, _ = oracle_forward(spec, x_np, idx_r, w_r)
+    assert rel_err(out, ref, denom) <= REL_TOL
+    assert np.array_equal(out, _forward_gpu(layer, x, idx_r, w_r))
+
+
 def test_full_batched_decode_T64_sampled():
     spec, t, layer = _full()
     T = 64
