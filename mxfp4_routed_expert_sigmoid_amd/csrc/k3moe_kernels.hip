@@ -1600,7 +1600,7 @@ void launch_combine(const LayerView &L, const float *ys, const float *w, const i
 
 // Batches up to this size take the single-token kernels once per token: at
 // T <= 4 that beats one weight-streaming pass over the union of their experts
-// (full flat shape: T = 2 169 us against 216, T = 4 322 against 354); from
+// (full flat shape: T = 2 165 us against 216, T = 4 310 against 354); from
 // about 5 tokens on, streaming each distinct expert once wins.
 constexpr int kT1LoopMax = 4;
 
@@ -1615,21 +1615,26 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const in
     int32_t *sorted = reinterpret_cast<int32_t *>(ws + lay.sorted);
     float *ys = reinterpret_cast<float *>(ws + lay.ys);
 
+    if (T == 1 && decode_path_ok(L))
+        return launch_forward_t1(L, x, x, nullptr, idx, w, out, reinterpret_cast<float *>(ws + lay.act),
+                                 reinterpret_cast<float *>(ws + lay.ash), ws + lay.ys, nullptr, s, prof, epi);
     // up to kT1LoopMax tokens: the single-token kernels once per token, in
-    // token order, reusing the first token's workspace rows (stream order
-    // keeps the passes apart)
+    // token order, each writing its token's staging rows of ys (the
+    // activation rows are reused: stream order keeps the passes apart), then
+    // one combine over the batch
     if (T <= kT1LoopMax && decode_path_ok(L)) {
         for (int t = 0; t < T; ++t) {
-            OutEpi et = epi;
-            if (et.ob) et.ob += (size_t)t * L.H;
             const uint16_t *xt = x + (size_t)t * L.H;
-            const hipError_t e = launch_forward_t1(L, xt, xt, nullptr, idx + (size_t)t * L.K, w + (size_t)t * L.K,
-                                                   out + (size_t)t * L.H, reinterpret_cast<float *>(ws + lay.act),
-                                                   reinterpret_cast<float *>(ws + lay.ash), ws + lay.ys, nullptr, s,
-                                                   prof, et);
+            const hipError_t e = launch_forward_t1(L, xt, xt, nullptr, idx + (size_t)t * L.K, nullptr, nullptr,
+                                                   reinterpret_cast<float *>(ws + lay.act),
+                                                   reinterpret_cast<float *>(ws + lay.ash),
+                                                   reinterpret_cast<char *>(ys + (size_t)t * (L.K + 1) * L.H),
+                                                   nullptr, s, prof, OutEpi());
             if (e != hipSuccess) return e;
         }
-        return hipSuccess;
+        StageMark m(prof, K3MOE_STAGE_COMBINE, s);
+        launch_combine(L, ys, w, idx, T, L.H, L.Is > 0, out, s, epi);
+        return hipGetLastError();
     }
     launch_perm(L, idx, T, ws, lay, s, prof);
     // activations: routed bf16 hi and lo [T*k][I] in the fp8-term region
