@@ -156,12 +156,28 @@ double k3o_act(double g, double u, int kind, double b1, double b2)
     return NAN;
 }
 
+/* One expert's selection score, and the order the router takes experts in:
+ * the larger score first, equal scores by the lower expert index. */
+struct choice {
+    float ch;
+    int32_t e;
+};
+
+static int by_choice(const void *pa, const void *pb)
+{
+    const struct choice *a = (const struct choice *)pa, *b = (const struct choice *)pb;
+    if (a->ch > b->ch) return -1;
+    if (a->ch < b->ch) return 1;
+    return (a->e > b->e) - (a->e < b->e);
+}
+
 /* Router for T tokens (§9, k3_router).
  *   logit[e] = sum_i x[i] * Wr[e][i]            fp64 over exact bf16 products
  *   sc[e]    = fp32 of sigmoid(fp32 logit)      unbiased score
  *   ch[e]    = sc[e] + bias[e]  (fp32 add)      selection score
- *   for j in 0..topk-1: the untaken e with the largest ch, scanning e upward
- *     and replacing only on a strictly larger value (ties -> lowest index)
+ *   selection: the experts ordered by ch, larger first, and among equal ch
+ *     the lower expert index first (the order in which a repeated strict
+ *     maximum takes them); the first topk of that order, in order
  *   w[j] = sc[idx[j]]; if renorm: s = sum_j w[j] (fp32, j order) and, if
  *   s > 0, w[j] /= s; finally w[j] *= routed_scale.
  * Outputs idx [T][topk], w [T][topk]; optional logits [T][E] (fp64) and
@@ -176,9 +192,9 @@ int k3o_route(int32_t *idx, float *w, double *logits_out, float *ch_out,
     double *logit = (double *)malloc(sizeof(double) * E);
     float *sc = (float *)malloc(sizeof(float) * E);
     float *ch = (float *)malloc(sizeof(float) * E);
-    char *taken = (char *)malloc(E);
-    if (!xd || !logit || !sc || !ch || !taken) {
-        free(xd); free(logit); free(sc); free(ch); free(taken);
+    struct choice *order = (struct choice *)malloc(sizeof(struct choice) * E);
+    if (!xd || !logit || !sc || !ch || !order) {
+        free(xd); free(logit); free(sc); free(ch); free(order);
         return -1;
     }
     for (int64_t t = 0; t < T; t++) {
@@ -189,16 +205,13 @@ int k3o_route(int32_t *idx, float *w, double *logits_out, float *ch_out,
             sc[e] = (float)sigmoid((double)l32);
             ch[e] = sc[e] + (bias ? bias[e] : 0.0f);
         }
-        memset(taken, 0, E);
+        for (int64_t e = 0; e < E; e++) { order[e].ch = ch[e]; order[e].e = (int32_t)e; }
+        qsort(order, (size_t)E, sizeof *order, by_choice);
         int32_t *it = idx + t * topk;
         float *wt = w + t * topk;
         for (int64_t j = 0; j < topk; j++) {
-            int64_t best = -1;
-            for (int64_t e = 0; e < E; e++)
-                if (!taken[e] && (best < 0 || ch[e] > ch[best])) best = e;
-            taken[best] = 1;
-            it[j] = (int32_t)best;
-            wt[j] = sc[best];
+            it[j] = order[j].e;
+            wt[j] = sc[order[j].e];
         }
         if (renorm) {
             float s = 0.0f;
@@ -210,7 +223,7 @@ int k3o_route(int32_t *idx, float *w, double *logits_out, float *ch_out,
         if (logits_out) memcpy(logits_out + t * E, logit, sizeof(double) * E);
         if (ch_out) memcpy(ch_out + t * E, ch, sizeof(float) * E);
     }
-    free(xd); free(logit); free(sc); free(ch); free(taken);
+    free(xd); free(logit); free(sc); free(ch); free(order);
     return 0;
 }
 

@@ -84,3 +84,16 @@ def test_swiglu_closed_forms():
         assert abs(oracle.act(60.0, u, oracle.ACT_SWIGLU) - 60.0 * u) <= 1e-12 * abs(60.0 * u)
         assert abs(oracle.act(-60.0, u, oracle.ACT_SWIGLU)) <= 60.0 * abs(u) * math.exp(-60.0)  # sigmoid(-60) < e^-60
     assert oracle.act(1.3, 0.0, oracle.ACT_SWIGLU) == 0.0
+
+
+def test_raw_gate_sigmoid_worked_value():
+    # g = 8, u = 25: 4 tanh(2) = 3.856110, sigmoid(8) = 0.999665,
+    # 25 tanh(1) = 19.039854, so the unit gives 73.3952 (73.39 to two
+    # places, truncated). Feeding the sigmoid the capped gate instead
+    # (sigmoid(3.856110) = 0.979332) would give 71.8991: the README's
+    # warning that the sigmoid takes the uncapped gate (§9, k3_situ_glu).
+    v = oracle.act(8.0, 25.0, oracle.ACT_SITU, B1, B2)
+    assert abs(v - 73.3952) < 1e-4
+    assert abs(v - 71.8991) > 1.4
+    # and the sign follows the up half
+    assert abs(oracle.act(8.0, -25.0, oracle.ACT_SITU, B1, B2) + 73.3952) < 1e-4

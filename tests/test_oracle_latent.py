@@ -132,3 +132,108 @@ def test_drops_counted_and_denominator_bounds_the_output():
     assert drops == 1
     assert np.all(den >= np.abs(out))
     assert np.all(den > 0)
+
+
+# ---------------------------------------------------------------------------
+# A dense numpy statement of the latent layer, written from README §9 k3_moe
+# steps 2-6 with its own MXFP4 decode (from the golden E2M1 table) and its
+# own activation: a check of the oracle that shares none of its code.
+import json
+import math
+import os
+
+from conftest import GOLDEN
+
+_TABLE = np.array(json.load(open(os.path.join(GOLDEN, "e2m1_table.json")))["values"])
+
+
+def _dense(packed, scales):
+    rows, half = packed.shape
+    codes = np.empty((rows, 2 * half), np.int64)
+    codes[:, 0::2] = packed & 15
+    codes[:, 1::2] = packed >> 4
+    s = np.array([0.0 if b == 255 else math.ldexp(1.0, b - 127) for b in range(256)])
+    return _TABLE[codes] * np.repeat(s[scales], 32, axis=1)
+
+
+def _situ(g, u, b1=4.0, b2=25.0):
+    return b1 * np.tanh(g / b1) / (1.0 + np.exp(-g)) * (b2 * np.tanh(u / b2))
+
+
+def _dense_latent(x, idx, w, h, Wd, Wu, gamma, eps, S, perturb=None):
+    """Per token: z = Wd x; acc = sum_j w_j W2_e act(W1_e z, W3_e z) in router
+    order; acc <- RMSNorm(acc) * gamma; out = Wu acc + S2 act(S1 x, S3 x).
+    perturb(t, j, y, yabs) may replace an expert's output (error-bound check)."""
+    bf = lambda a: synth.bf16_to_f32(a).astype(np.float64)
+    xf, Wdf, Wuf = bf(x), bf(Wd), bf(Wu)
+    S1, S3, S2 = (bf(m) for m in S)
+    out = np.zeros((x.shape[0], Wuf.shape[0]))
+    for t in range(x.shape[0]):
+        z = Wdf @ xf[t]
+        acc = np.zeros(Wdf.shape[0])
+        for j in range(idx.shape[1]):
+            e = idx[t, j]
+            g = _dense(h["gate_packed"][e], h["gate_scales"][e]) @ z
+            u = _dense(h["up_packed"][e], h["up_scales"][e]) @ z
+            a = _situ(g, u)
+            D2 = _dense(h["down_packed"][e], h["down_scales"][e])
+            y = D2 @ a
+            if perturb is not None:
+                y = perturb(t, j, y, np.abs(D2) @ np.abs(a))
+            acc += np.float64(w[t, j]) * y
+        acc = acc / np.sqrt(np.mean(acc ** 2) + eps) * gamma.astype(np.float64)
+        out[t] = Wuf @ acc + S2 @ _situ(S1 @ xf[t], S3 @ xf[t])
+    return out
+
+
+def _general_latent_case():
+    # L != H, general (random) projections, the norm on with a non-trivial
+    # gain, a shared expert, a positive epsilon
+    spec = _spec(hidden=256, latent=128, inter=96, n_experts=6, topk=3, shared_inter=64, seed=11)
+    x, idx, w, es = _setup(spec, 3)
+    h = synth.expert_host(spec, list(range(spec.n_experts)))
+    Wd, Wu, g = synth.make_latent(spec)
+    S = synth.make_shared(spec)
+    return spec, x, idx, w, es, h, Wd, Wu, g, S
+
+
+def test_latent_matches_dense_numpy_general_projections():
+    spec, x, idx, w, es, h, Wd, Wu, g, S = _general_latent_case()
+    assert Wd.shape == (128, 256) and Wu.shape == (256, 128)
+    eps = 1e-5
+    out, den, drops = oracle.forward_latent(x, idx, w, es, 256, 128, 96, Wd, Wu, gamma=g, eps=eps,
+                                            shared=S)
+    assert drops == 0
+    ref = _dense_latent(x, idx, w, h, Wd, Wu, g, eps, S)
+    assert np.all(np.abs(out - ref) <= 1e-11 * den)
+    # the routed part matters: dropping one slot's weight changes the result
+    w2 = w.copy()
+    w2[:, 0] = 0.0
+    ref2 = _dense_latent(x, idx, w2, h, Wd, Wu, g, eps, S)
+    assert np.max(np.abs(ref2 - ref) / den) > 1e-3
+
+
+def test_latent_denominator_bounds_first_order_error():
+    # D is the error denominator: a relative perturbation of at most r in
+    # every expert product (each y_j[l] moved by up to r * sum_n |W2[l][n] a[n]|)
+    # moves each output by at most r * D, to first order (the norm included)
+    spec, x, idx, w, es, h, Wd, Wu, g, S = _general_latent_case()
+    eps = 1e-5
+    out, den, _ = oracle.forward_latent(x, idx, w, es, 256, 128, 96, Wd, Wu, gamma=g, eps=eps, shared=S)
+    base = _dense_latent(x, idx, w, h, Wd, Wu, g, eps, S)
+    r = 1e-7
+    worst = 0.0
+    for trial in range(6):
+        rng = np.random.default_rng(100 + trial)
+        signs = {}
+
+        def perturb(t, j, y, yabs):
+            s = signs.setdefault((t, j), rng.choice([-1.0, 1.0], size=y.shape) if trial < 4
+                                 else np.sign(y + 1e-300))
+            return y + r * s * yabs
+        moved = _dense_latent(x, idx, w, h, Wd, Wu, g, eps, S, perturb=perturb)
+        ratio = np.abs(moved - base) / (r * den)
+        worst = max(worst, float(ratio.max()))
+    assert worst <= 1.0 + 1e-3
+    # and D is not loose by orders of magnitude
+    assert worst >= 1e-2
