@@ -180,6 +180,24 @@ k3moe_status k3moe_forward(const k3moe_layer *layer, const uint16_t *x, int32_t 
                            const int32_t *idx, const float *w, float *out,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* k3moe_forward for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels and results, bit for bit, with a fixed 64 MiB device array of the
+ * library standing in for the workspace. Each GPU holds its own copy from the
+ * moment the library is loaded there until the process ends. The call
+ * allocates nothing (no hipMalloc, no event, no library allocation) and
+ * takes no workspace argument.
+ *   T whose workspace (k3moe_workspace_size) exceeds 64 MiB is refused with
+ *   K3MOE_E_WORKSPACE before any launch (about 100 tokens at hidden 7168,
+ *   top-16, inter 1536).
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (on different streams, or from different threads or layers) race.
+ *   Serialise them on one stream. No part of the array has to start at zero.
+ *   Per-stage profiling (k3moe_profile_enable) does not record these calls.
+ * Other arguments and errors as k3moe_forward. */
+k3moe_status k3moe_forward_noalloc(const k3moe_layer *layer, const uint16_t *x, int32_t T,
+                                   const int32_t *idx, const float *w, float *out, void *stream);
+
 /* k3moe_forward with the residual add fused into its last kernel, for a
  * stack of layers on an fp32 residual stream (each layer's output added to
  * the stream, the next layer reading it rounded to bf16):

@@ -61,7 +61,7 @@ class CacheStats(ctypes.Structure):
 
 _lib = None
 EXPORTS = ("k3moe_layer_create", "k3moe_workspace_size", "k3moe_route", "k3moe_forward",
-           "k3moe_forward_residual", "k3moe_step", "k3moe_cache_create", "k3moe_cache_workspace_size", "k3moe_cache_forward",
+           "k3moe_forward_noalloc", "k3moe_forward_residual", "k3moe_step", "k3moe_cache_create", "k3moe_cache_workspace_size", "k3moe_cache_forward",
            "k3moe_cache_stats_read", "k3moe_cache_slots", "k3moe_cache_reset", "k3moe_cache_destroy",
            "k3moe_error_count", "k3moe_error_reset", "k3moe_profile_enable",
            "k3moe_profile_read", "k3moe_layer_destroy", "k3moe_status_string")
@@ -86,6 +86,8 @@ def lib():
         L.k3moe_route.argtypes = [P, P, i32, P, P, P, P, ctypes.c_size_t, P]
         L.k3moe_forward.restype = st
         L.k3moe_forward.argtypes = [P, P, i32, P, P, P, P, ctypes.c_size_t, P]
+        L.k3moe_forward_noalloc.restype = st
+        L.k3moe_forward_noalloc.argtypes = [P, P, i32, P, P, P, P]
         L.k3moe_forward_residual.restype = st
         L.k3moe_forward_residual.argtypes = [P, P, i32, P, P, P, P, P, ctypes.c_size_t, P]
         L.k3moe_step.restype = st
@@ -245,6 +247,16 @@ class Layer:
         _check(lib().k3moe_forward(self.handle, x.data_ptr(), T, idx.data_ptr(), w.data_ptr(),
                                    out.data_ptr(), p, n, _stream(stream, self.device)),
                "k3moe_forward")
+
+    def forward_noalloc(self, x, idx, w, out, stream=None):
+        """k3moe_forward_noalloc: k3moe_forward on the library's fixed per-GPU
+        scratch array (no workspace, nothing allocated); calls on one GPU must
+        not overlap."""
+        T = x.shape[0]
+        _dev(x, (2,), "x"), _dev(idx, (4,), "idx"), _dev(w, (4,), "w"), _dev(out, (4,), "out")
+        _check(lib().k3moe_forward_noalloc(self.handle, x.data_ptr(), T, idx.data_ptr(), w.data_ptr(),
+                                           out.data_ptr(), _stream(stream, self.device)),
+               "k3moe_forward_noalloc")
 
     def forward_residual(self, x, idx, w, h, hb=None, workspace=None, stream=None):
         """k3moe_forward_residual: h fp32 [T][H] += forward(x, idx, w), in place;

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <new>
 
 #include "k3moe_internal.h"
@@ -282,6 +283,39 @@ static CacheWs cache_ws(const k3moe_cache *c, int64_t T)
     return w;
 }
 
+// Allocation-free forward (k3moe_forward_noalloc): a fixed device array
+// stands in for the caller's workspace. Each GPU the library runs on holds
+// its own copy (a module global), so its address is looked up once per
+// device, with that device current, when the first layer is created there.
+// In host code the array's name is only a stand-in for the device symbol:
+// kernels and copies take the looked-up address, never the name.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxScratchDevices = 64;
+static std::mutex g_scratch_mu;
+static char *g_scratch_ptr[kMaxScratchDevices];
+
+static k3moe_status resolve_scratch(int dev)
+{
+    if (dev < 0 || dev >= kMaxScratchDevices) return K3MOE_E_UNSUPPORTED_SHAPE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev]) return K3MOE_OK;
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        (void)hipGetLastError();
+        return K3MOE_E_HIP;
+    }
+    g_scratch_ptr[dev] = static_cast<char *>(p);
+    return K3MOE_OK;
+}
+
+static char *scratch_of(int dev)
+{
+    if (dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace k3moe
 
 using namespace k3moe;
@@ -297,6 +331,7 @@ k3moe_status k3moe_layer_create(const k3moe_config *cfg, const k3moe_weights *w,
     if ((s = check_weights(cfg, w)) != K3MOE_OK) return s;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return K3MOE_E_HIP;
+    if ((s = resolve_scratch(dev)) != K3MOE_OK) return s;  // this device's k3moe_forward_noalloc scratch
     size_t free_b = 0, total_b = 0;
     if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) return K3MOE_E_HIP;
     if (free_b < (size_t)1 << 20) return K3MOE_E_OUT_OF_MEMORY;
@@ -362,6 +397,26 @@ k3moe_status k3moe_forward(const k3moe_layer *l, const uint16_t *x, int32_t T, c
     const WsLayout lay = ws_layout(l->cfg, T);
     if (launch_forward(view(l), x, T, idx, w, out, static_cast<char *>(ws), lay,
                        static_cast<hipStream_t>(stream), l->prof) != hipSuccess)
+        return K3MOE_E_HIP;
+    return K3MOE_OK;
+}
+
+k3moe_status k3moe_forward_noalloc(const k3moe_layer *l, const uint16_t *x, int32_t T, const int32_t *idx,
+                                   const float *w, float *out, void *stream)
+{
+    if (!l) return K3MOE_E_INVALID_ARG;
+    char *ws = scratch_of(l->device);
+    if (!ws) return K3MOE_E_HIP;  // the layer's device has no resolved scratch
+    bool nothing;
+    k3moe_status s = check_call(l, T, ws, kScratchBytes, &nothing);  // T beyond the scratch: E_WORKSPACE
+    if (s != K3MOE_OK || nothing) return s;
+    if (!x || !idx || !w || !out) return K3MOE_E_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(idx, 4) || !aligned(w, 4) || !aligned(out, 16))
+        return K3MOE_E_ALIGNMENT;
+    const WsLayout lay = ws_layout(l->cfg, T);
+    // no profiler: its event records could create events
+    if (launch_forward(view(l), x, T, idx, w, out, ws, lay, static_cast<hipStream_t>(stream), nullptr) !=
+        hipSuccess)
         return K3MOE_E_HIP;
     return K3MOE_OK;
 }
