@@ -172,11 +172,11 @@ def main():
             layer.step(hs[i % pool], gamma, STEP_EPS, idx, w, workspace=ws, stream=stream)
             return
         x = xs[i % pool]
-        layer.route(x, idx, w, workspace=ws, stream=stream)
         if cache is not None:
+            layer.route(x, idx, w, workspace=ws, stream=stream)
             cache.forward(x, idx, w, out, workspace=ws, stream=stream)
             return
-        layer.forward(x, idx, w, out, workspace=ws, stream=stream)
+        layer.route_forward(x, idx, w, out, workspace=ws, stream=stream)
 
     # distinct experts per pool entry (for the algorithmic byte counts)
     distinct, heavy = [], []
@@ -227,15 +227,19 @@ def main():
     pct = {q: float(np.percentile(step_us, q)) for q in (10, 50, 90)}
     log(f"[bench] step us p10 {pct[10]:.2f} p50 {pct[50]:.2f} p90 {pct[90]:.2f}")
 
-    # second pass with per-stage events (same steps)
+    # second pass with per-stage events (same steps): an event pair around
+    # each stage's launches on the launch stream; a stage's time is summed
+    # over its launches in a step (a batch of 2-4 tokens runs the one-token
+    # kernels once per token) and averaged over the steps
     layer.profile(True)
     layer.profile_read(stream)
     for i in range(args.steps):
         step(i)
     stages = layer.profile_read(stream)
     layer.profile(False)
-    stage_us = {k: (v[0] * 1e3 / v[1] if v[1] else 0.0) for k, v in stages.items()}
-    log(f"[bench] stage us/launch: " + ", ".join(f"{k} {v:.2f}" for k, v in stage_us.items()))
+    stage_us = {k: v[0] * 1e3 / args.steps for k, v in stages.items() if v[1]}
+    launches = {k: v[1] / args.steps for k, v in stages.items() if v[1]}
+    log(f"[bench] stage us/step: " + ", ".join(f"{k} {v:.2f}" for k, v in stage_us.items()))
 
     # algorithmic bytes, averaged over the rotation actually timed
     nd = sum(distinct[i % pool] for i in range(args.steps)) / args.steps
@@ -250,11 +254,23 @@ def main():
     # (4 B per element: fp32, or bf16 hi + lo), expert outputs staged in fp32
     x_read = T * H * 2 + (T * Lt * 4 if Lt else 0)   # the bf16 tokens (+ the latent's hi/lo planes)
     act_b = T * K * I * 4 + T * Is * 4
-    shared_in_gateup = stages["shared_gateup"][1] == 0  # no separate shared gate/up launch
-    stage_bytes = {
-        "gateup": nd * 2 * gu + (2 * Is * H * 2 if shared_in_gateup else 0) + x_read + act_b,
-        "down": nd * dn + Is * H * 2 + act_b + T * (K + 1) * EKw * 4 + (T * H * 4 if Lt else 0),
-    }
+    # the one-token fused path (a flat layer, one token, through route_forward
+    # or step): router | shared gate/up + top-k + routed gate/up | shared
+    # down + routed down + router-order sum (no separate combine)
+    fused = "combine" not in stage_us and not Lt and T == 1 and cache is None
+    if fused:
+        terms = K * 4 * I + K * 4 * (I // 32)   # the activations as e4m3 terms and their scales
+        stage_bytes = {
+            "router": router_bytes + H * 2 + E * 8,
+            "gateup": nd * 2 * gu + 2 * Is * H * 2 + H * 2 + E * 8 + terms + Is * 4 + K * 8,
+            "down": nd * dn + Is * H * 2 + terms + Is * 4 + K * 8 + H * 4 * (2 if args.workload in ("step", "stack") else 1),
+        }
+    else:
+        shared_in_gateup = "shared_gateup" not in stage_us  # no separate shared gate/up launch
+        stage_bytes = {
+            "gateup": nd * 2 * gu + (2 * Is * H * 2 if shared_in_gateup else 0) + x_read + act_b,
+            "down": nd * dn + Is * H * 2 + act_b + T * (K + 1) * EKw * 4 + (T * H * 4 if Lt else 0),
+        }
     if args.workload in ("step", "stack"):
         stage_bytes["prenorm"] = T * H * 4 + H * 4 + T * H * 2
     if cache is not None:
@@ -262,16 +278,19 @@ def main():
     if Lt:
         stage_bytes["latent_in"] = Lt * H * 2 + T * H * 2 + T * Lt * 4
         stage_bytes["latent_out"] = H * Lt * 2 + Lt * 4 + T * Lt * 12 + T * H * 8
-    kernels = {"decode": {"gateup": "k_gateup_dec", "down": "k_down_dec"},
+    kernels = {"decode": ({"router": "k_router", "gateup": "k_dec_gateup", "down": "k_dec_down"} if fused
+                          else {"gateup": "k_gateup_dec", "down": "k_down_dec"}),
                "batched": {"gateup": "k_gu_stream", "down": "k_dn_stream"},
                "prefill": {"gateup": "k_gu_gemm + k_gu_stream", "down": "k_dn_gemm + k_dn_stream"},
                "latent": ({"gateup": "k_gateup_dec", "down": "k_down_dec", "latent_in": "k_gv_down",
                            "latent_out": "k_gv_up"} if T == 1 else
                           {"gateup": "k_gu_stream", "down": "k_dn_stream", "latent_in": "k_proj",
                            "latent_out": "k_proj + k_rms_split"}),
-               "step": {"gateup": "k_gateup_dec", "down": "k_down_dec", "prenorm": "k_prenorm"},
+               "step": {"router": "k_router", "gateup": "k_dec_gateup", "down": "k_dec_down",
+                        "prenorm": "k_prenorm"},
                "cache": {"cache_fill": "k_cache_fill"},
-               "stack": ({"gateup": "k_gateup_dec", "down": "k_down_dec", "prenorm": "k_prenorm"} if T == 1
+               "stack": ({"router": "k_router", "gateup": "k_dec_gateup", "down": "k_dec_down",
+                          "prenorm": "k_prenorm"} if T == 1
                          else {"gateup": "k_gu_stream", "down": "k_dn_stream", "prenorm": "k_prenorm"})}[args.workload]
     # the hot experts' tile GEMMs: algorithmic flops (2 per multiply-add,
     # gate and up, per assignment) and issued flops (whole token tiles; the
@@ -285,8 +304,9 @@ def main():
         mf["alg_dn"] += c.sum() * 2 * EKw * I
         mf["iss_dn"] += (np.ceil(c / 64) * 64).sum() * 2 * EKw * I * 2
     mf = {k: v / args.steps / nl for k, v in mf.items()}
-    dom = max(stage_bytes, key=lambda s: stage_us[s])
-    achieved = stage_bytes[dom] / (stage_us[dom] * 1e-6) / 1e9 if stage_us[dom] > 0 else 0.0
+    dom = max(stage_bytes, key=lambda s: stage_us.get(s, 0.0))
+    dom_us = stage_us.get(dom, 0.0)
+    achieved = stage_bytes[dom] / (dom_us * 1e-6) / 1e9 if dom_us > 0 else 0.0
     peak = HBM_PEAK_GBPS if cache is None else HOST_LINK_PEAK_GBPS
     traffic = measured_traffic(kernels[dom])
     value = nl * routed_bytes / (ms * 1e-3) / 1e9
@@ -328,7 +348,7 @@ def main():
         "layers_per_step": nl,
         "tokens_per_s_per_layer": round(T * nl / (ms * 1e-3), 1),
         "routed_frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
-        "stage_us": {k: round(v, 3) for k, v in stage_us.items()},
+        "stage_us_per_step": {k: round(v, 3) for k, v in stage_us.items()},
         "roofline": {
             "kernel": kernels[dom],
             "bound": "hbm" if cache is None else "host link (PCIe 5.0 x16)",
@@ -336,7 +356,10 @@ def main():
             "peak": peak,
             "unit": "GB/s",
             "frac": round(achieved / peak, 4),
-            "bytes_per_launch": round(stage_bytes[dom]),
+            "bytes_per_step": round(stage_bytes[dom]),
+            "us_per_step": round(dom_us, 3),
+            "launches_per_step": round(launches.get(dom, 0.0), 3),
+            "timing": "HIP events around the stage's launches on the launch stream, summed per step",
             "traffic": traffic,
         },
     }
@@ -445,11 +468,22 @@ def cpu_baseline(spec, xs_np, T, budget_s, expert_b, gamma=None):
         log(f"[bench] cpu baseline: {tokens} tokens, {spent:.1f} s")
         if spent >= budget_s:
             break
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {
         "value": round(routed / spent / 1e9, 4),
         "unit": "GB/s",
         "tokens_per_s": round(tokens / spent, 4),
         "cores": oracle.threads(),
+        "cpu_model": model,
+        "nproc": os.cpu_count(),
         "kind": "oracle",
         "sample": f"{tokens} whole tokens (route + 16 experts + shared expert) of this workload, "
                   f"one token per oracle call, {spent:.1f} s of oracle time",

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define K3MOE_ABI_VERSION 2u
+#define K3MOE_ABI_VERSION 3u
 
 typedef enum {
     K3MOE_OK = 0,
@@ -180,6 +180,20 @@ k3moe_status k3moe_forward(const k3moe_layer *layer, const uint16_t *x, int32_t 
                            const int32_t *idx, const float *w, float *out,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* Route and forward in one call: k3moe_route followed by k3moe_forward on
+ * its routes (README §9: k3_router, then k3_moe), with the same arguments,
+ * outputs and workspace. For one token of a flat layer (hidden <= 8192,
+ * inter <= 2048, shared_inter <= 4096, topk <= 16) the whole layer runs in
+ * three launches (router and shared gate/up; top-k, routed gate/up and
+ * shared down; routed down and the router-order sum); other batches and
+ * layers run route then forward. idx, w and out are written; logits as in
+ * k3moe_route. Ids come from the router, so no drop can occur. The output
+ * agrees with k3moe_forward on the same routes to the layer's error bound,
+ * not bit for bit (the one-token kernels sum in another order). */
+k3moe_status k3moe_route_forward(const k3moe_layer *layer, const uint16_t *x, int32_t T,
+                                 int32_t *idx, float *w, float *logits, float *out,
+                                 void *workspace, size_t workspace_bytes, void *stream);
+
 /* k3moe_forward for callers that cannot allocate (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * kernels and results, bit for bit, with a fixed 64 MiB device array of the
@@ -247,22 +261,22 @@ k3moe_status k3moe_error_reset(k3moe_layer *layer, void *stream);
  * read, and clears the record. Recording adds two event records per launch
  * to the stream, so time the layer itself with profiling off. */
 typedef enum {
-    K3MOE_STAGE_ROUTER = 0,         /* router logits, scores              */
-    K3MOE_STAGE_TOPK = 1,           /* top-k, weights                     */
-    K3MOE_STAGE_XSPLIT = 2,         /* reserved: no kernel records it     */
-    K3MOE_STAGE_PERM = 3,           /* token -> expert permutation        */
-    K3MOE_STAGE_GATEUP = 4,         /* routed gate/up MXFP4 + activation  */
-    K3MOE_STAGE_SHARED_GATEUP = 5,  /* shared expert gate/up + activation */
-    K3MOE_STAGE_DOWN = 6,           /* down MXFP4 (+ shared down)         */
-    K3MOE_STAGE_COMBINE = 7,        /* router-order weighted sum + shared */
-    K3MOE_STAGE_LATENT_IN = 8,      /* latent: down-projection of x       */
-    K3MOE_STAGE_LATENT_OUT = 9,     /* latent: norm and up-projection     */
-    K3MOE_STAGE_PRENORM = 10,       /* step: norm of the residual stream  */
-    K3MOE_STAGE_CACHE_PLAN = 11,    /* cache: hits, victims, slot ids     */
-    K3MOE_STAGE_CACHE_FILL = 12,    /* cache: host -> HBM expert reads    */
-    K3MOE_STAGE_GATEUP_TILES = 13,  /* the routed gate/up tile GEMMs only (within GATEUP) */
-    K3MOE_STAGE_DOWN_TILES = 14,    /* the routed down tile GEMMs only (within DOWN)      */
-    K3MOE_N_STAGES = 15
+    K3MOE_STAGE_ROUTER = 0,         /* router logits, scores (one token of a flat layer:
+                                       with the shared expert's gate/up rows) */
+    K3MOE_STAGE_TOPK = 1,           /* top-k, weights (one token: inside GATEUP) */
+    K3MOE_STAGE_PERM = 2,           /* token -> expert permutation        */
+    K3MOE_STAGE_GATEUP = 3,         /* routed gate/up MXFP4 + activation  */
+    K3MOE_STAGE_SHARED_GATEUP = 4,  /* shared expert gate/up + activation */
+    K3MOE_STAGE_DOWN = 5,           /* down MXFP4 (+ shared down; one token: + the sum) */
+    K3MOE_STAGE_COMBINE = 6,        /* router-order weighted sum + shared */
+    K3MOE_STAGE_LATENT_IN = 7,      /* latent: down-projection of x       */
+    K3MOE_STAGE_LATENT_OUT = 8,     /* latent: norm and up-projection     */
+    K3MOE_STAGE_PRENORM = 9,        /* step: norm of the residual stream  */
+    K3MOE_STAGE_CACHE_PLAN = 10,    /* cache: hits, victims, slot ids     */
+    K3MOE_STAGE_CACHE_FILL = 11,    /* cache: host -> HBM expert reads    */
+    K3MOE_STAGE_GATEUP_TILES = 12,  /* the routed gate/up tile GEMMs only (within GATEUP) */
+    K3MOE_STAGE_DOWN_TILES = 13,    /* the routed down tile GEMMs only (within DOWN)      */
+    K3MOE_N_STAGES = 14
 } k3moe_stage;
 
 k3moe_status k3moe_profile_enable(k3moe_layer *layer, int enable);

@@ -14,7 +14,7 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libk3moe.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 ACT_SITU, ACT_SWIGLU = 1, 2
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "invalid or incomplete config",
@@ -61,11 +61,11 @@ class CacheStats(ctypes.Structure):
 
 _lib = None
 EXPORTS = ("k3moe_layer_create", "k3moe_workspace_size", "k3moe_route", "k3moe_forward",
-           "k3moe_forward_noalloc", "k3moe_forward_residual", "k3moe_step", "k3moe_cache_create", "k3moe_cache_workspace_size", "k3moe_cache_forward",
+           "k3moe_route_forward", "k3moe_forward_noalloc", "k3moe_forward_residual", "k3moe_step", "k3moe_cache_create", "k3moe_cache_workspace_size", "k3moe_cache_forward",
            "k3moe_cache_stats_read", "k3moe_cache_slots", "k3moe_cache_reset", "k3moe_cache_destroy",
            "k3moe_error_count", "k3moe_error_reset", "k3moe_profile_enable",
            "k3moe_profile_read", "k3moe_layer_destroy", "k3moe_status_string")
-STAGES = ("router", "topk", "xsplit", "perm", "gateup", "shared_gateup", "down", "combine",
+STAGES = ("router", "topk", "perm", "gateup", "shared_gateup", "down", "combine",
           "latent_in", "latent_out", "prenorm", "cache_plan", "cache_fill", "gateup_tiles",
           "down_tiles")
 
@@ -86,6 +86,8 @@ def lib():
         L.k3moe_route.argtypes = [P, P, i32, P, P, P, P, ctypes.c_size_t, P]
         L.k3moe_forward.restype = st
         L.k3moe_forward.argtypes = [P, P, i32, P, P, P, P, ctypes.c_size_t, P]
+        L.k3moe_route_forward.restype = st
+        L.k3moe_route_forward.argtypes = [P, P, i32, P, P, P, P, P, ctypes.c_size_t, P]
         L.k3moe_forward_noalloc.restype = st
         L.k3moe_forward_noalloc.argtypes = [P, P, i32, P, P, P, P]
         L.k3moe_forward_residual.restype = st
@@ -142,6 +144,23 @@ def _stream(stream, device):
 def _check(status, what):
     if status != 0:
         raise K3MoeError(status, what)
+
+
+def _shape(t, shape, name):
+    """Refuse a tensor whose shape is not `shape` (None: absent, accepted).
+    The C ABI takes raw pointers, so a mis-shaped tensor would become an
+    out-of-bounds device access; it is refused here before any call."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _rows(x, width, name="x"):
+    """Token count of a [T][width] tensor (refused otherwise)."""
+    if x.dim() != 2 or x.shape[1] != width:
+        raise ValueError(f"{name}: shape {tuple(x.shape)}, expected [T][{width}]")
+    return x.shape[0]
 
 
 def _dev(t, dtype_sizes, name, pinned_ok=False):
@@ -229,30 +248,65 @@ class Layer:
         off = (-base) % 256
         return ctypes.c_void_p(base + off), ws.numel() - off
 
+    def _call_ws(self, workspace, T, stream):
+        """The caller's workspace, or a new one for T tokens. A new one is
+        allocated on the current stream; when the call runs on another
+        stream it is marked as used there, so the caching allocator does not
+        hand its memory out again while the queued kernels still use it."""
+        if workspace is not None:
+            return workspace
+        ws = self.workspace(T)
+        if stream is not None and stream != torch.cuda.current_stream(self.device):
+            ws.record_stream(stream)
+        return ws
+
+    def _check_tokens(self, T, **t):
+        H, K, E = self.cfg.hidden, self.cfg.topk, self.cfg.n_experts
+        shapes = {"idx": (T, K), "w": (T, K), "out": (T, H), "h": (T, H), "hb": (T, H),
+                  "x_out": (T, H), "logits": (T, E), "gamma": (H,)}
+        for name, tensor in t.items():
+            _shape(tensor, shapes[name], name)
+
     def route(self, x, idx, w, logits=None, workspace=None, stream=None):
         """k3moe_route: x bf16 [T][H] -> idx int32 [T][k], w fp32 [T][k] (written)."""
-        T = x.shape[0]
+        T = _rows(x, self.cfg.hidden)
+        self._check_tokens(T, idx=idx, w=w, logits=logits)
         _dev(x, (2,), "x"), _dev(idx, (4,), "idx"), _dev(w, (4,), "w"), _dev(logits, (4,), "logits")
-        ws = workspace if workspace is not None else self.workspace(T)
+        ws = self._call_ws(workspace, T, stream)
         p, n = self._ws(ws)
         _check(lib().k3moe_route(self.handle, x.data_ptr(), T, idx.data_ptr(), w.data_ptr(),
                                  _ptr(logits), p, n, _stream(stream, self.device)), "k3moe_route")
 
     def forward(self, x, idx, w, out, workspace=None, stream=None):
         """k3moe_forward: out fp32 [T][H] (written) from x, idx, w."""
-        T = x.shape[0]
+        T = _rows(x, self.cfg.hidden)
+        self._check_tokens(T, idx=idx, w=w, out=out)
         _dev(x, (2,), "x"), _dev(idx, (4,), "idx"), _dev(w, (4,), "w"), _dev(out, (4,), "out")
-        ws = workspace if workspace is not None else self.workspace(T)
+        ws = self._call_ws(workspace, T, stream)
         p, n = self._ws(ws)
         _check(lib().k3moe_forward(self.handle, x.data_ptr(), T, idx.data_ptr(), w.data_ptr(),
                                    out.data_ptr(), p, n, _stream(stream, self.device)),
                "k3moe_forward")
 
+    def route_forward(self, x, idx, w, out, logits=None, workspace=None, stream=None):
+        """k3moe_route_forward: route x, then the expert layer on those routes;
+        idx int32 [T][k], w fp32 [T][k] and out fp32 [T][H] written."""
+        T = _rows(x, self.cfg.hidden)
+        self._check_tokens(T, idx=idx, w=w, out=out, logits=logits)
+        _dev(x, (2,), "x"), _dev(idx, (4,), "idx"), _dev(w, (4,), "w"), _dev(out, (4,), "out")
+        _dev(logits, (4,), "logits")
+        ws = self._call_ws(workspace, T, stream)
+        p, n = self._ws(ws)
+        _check(lib().k3moe_route_forward(self.handle, x.data_ptr(), T, idx.data_ptr(), w.data_ptr(),
+                                         _ptr(logits), out.data_ptr(), p, n, _stream(stream, self.device)),
+               "k3moe_route_forward")
+
     def forward_noalloc(self, x, idx, w, out, stream=None):
         """k3moe_forward_noalloc: k3moe_forward on the library's fixed per-GPU
         scratch array (no workspace, nothing allocated); calls on one GPU must
         not overlap."""
-        T = x.shape[0]
+        T = _rows(x, self.cfg.hidden)
+        self._check_tokens(T, idx=idx, w=w, out=out)
         _dev(x, (2,), "x"), _dev(idx, (4,), "idx"), _dev(w, (4,), "w"), _dev(out, (4,), "out")
         _check(lib().k3moe_forward_noalloc(self.handle, x.data_ptr(), T, idx.data_ptr(), w.data_ptr(),
                                            out.data_ptr(), _stream(stream, self.device)),
@@ -261,9 +315,10 @@ class Layer:
     def forward_residual(self, x, idx, w, h, hb=None, workspace=None, stream=None):
         """k3moe_forward_residual: h fp32 [T][H] += forward(x, idx, w), in place;
         hb (bf16 [T][H], optional, may be x) receives bf16 of the updated h."""
-        T = x.shape[0]
+        T = _rows(x, self.cfg.hidden)
+        self._check_tokens(T, idx=idx, w=w, h=h, hb=hb)
         _dev(x, (2,), "x"), _dev(idx, (4,), "idx"), _dev(w, (4,), "w"), _dev(h, (4,), "h"), _dev(hb, (2,), "hb")
-        ws = workspace if workspace is not None else self.workspace(T)
+        ws = self._call_ws(workspace, T, stream)
         p, n = self._ws(ws)
         _check(lib().k3moe_forward_residual(self.handle, x.data_ptr(), T, idx.data_ptr(), w.data_ptr(),
                                             h.data_ptr(), _ptr(hb), p, n, _stream(stream, self.device)),
@@ -273,10 +328,11 @@ class Layer:
         """k3moe_step: h fp32 [T][H] += layer(bf16(RMSNorm(h) * gamma)), in place;
         idx int32 [T][k] and w fp32 [T][k] written; x_out / hb (bf16 [T][H],
         optional) receive the normed input and bf16 of the updated h."""
-        T = h.shape[0]
+        T = _rows(h, self.cfg.hidden, "h")
+        self._check_tokens(T, gamma=gamma, idx=idx, w=w, x_out=x_out, hb=hb)
         _dev(h, (4,), "h"), _dev(gamma, (4,), "gamma"), _dev(idx, (4,), "idx"), _dev(w, (4,), "w")
         _dev(x_out, (2,), "x_out"), _dev(hb, (2,), "hb")
-        ws = workspace if workspace is not None else self.workspace(T)
+        ws = self._call_ws(workspace, T, stream)
         p, n = self._ws(ws)
         _check(lib().k3moe_step(self.handle, h.data_ptr(), T, gamma.data_ptr(), float(eps),
                                 _ptr(x_out), idx.data_ptr(), w.data_ptr(), _ptr(hb), p, n,
@@ -332,9 +388,14 @@ class Cache:
 
     def forward(self, x, idx, w, out, workspace=None, stream=None):
         """k3moe_cache_forward: out fp32 [T][H] (written) through the slots."""
-        T = x.shape[0]
+        T = _rows(x, self.layer.cfg.hidden)
+        self.layer._check_tokens(T, idx=idx, w=w, out=out)
         _dev(x, (2,), "x"), _dev(idx, (4,), "idx"), _dev(w, (4,), "w"), _dev(out, (4,), "out")
-        ws = workspace if workspace is not None else self.workspace(T)
+        ws = workspace
+        if ws is None:
+            ws = self.workspace(T)
+            if stream is not None and stream != torch.cuda.current_stream(self.device):
+                ws.record_stream(stream)
         p, n = Layer._ws(ws)
         _check(lib().k3moe_cache_forward(self.handle, x.data_ptr(), T, idx.data_ptr(), w.data_ptr(),
                                          out.data_ptr(), p, n, _stream(stream, self.device)),

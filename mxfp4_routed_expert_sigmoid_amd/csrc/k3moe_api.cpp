@@ -401,6 +401,31 @@ k3moe_status k3moe_forward(const k3moe_layer *l, const uint16_t *x, int32_t T, c
     return K3MOE_OK;
 }
 
+k3moe_status k3moe_route_forward(const k3moe_layer *l, const uint16_t *x, int32_t T, int32_t *idx, float *w,
+                                 float *logits, float *out, void *ws, size_t ws_bytes, void *stream)
+{
+    bool nothing;
+    k3moe_status s = check_call(l, T, ws, ws_bytes, &nothing);
+    if (s != K3MOE_OK || nothing) return s;
+    if (!x || !idx || !w || !out) return K3MOE_E_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(idx, 4) || !aligned(w, 4) || (logits && !aligned(logits, 4)) ||
+        !aligned(out, 16))
+        return K3MOE_E_ALIGNMENT;
+    const WsLayout lay = ws_layout(l->cfg, T);
+    char *wsc = static_cast<char *>(ws);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    LayerView v = view(l);
+    if (T == 1 && decode_fused_ok(v)) {
+        if (launch_decode_fused(v, x, idx, w, logits, true, out, wsc, lay, st, l->prof) != hipSuccess)
+            return K3MOE_E_HIP;
+        return K3MOE_OK;
+    }
+    v.routes_distinct = true;  // the routes below come from the router
+    if (launch_route(v, x, T, idx, w, logits, wsc, lay, st, l->prof) != hipSuccess) return K3MOE_E_HIP;
+    if (launch_forward(v, x, T, idx, w, out, wsc, lay, st, l->prof) != hipSuccess) return K3MOE_E_HIP;
+    return K3MOE_OK;
+}
+
 k3moe_status k3moe_forward_noalloc(const k3moe_layer *l, const uint16_t *x, int32_t T, const int32_t *idx,
                                    const float *w, float *out, void *stream)
 {
@@ -462,10 +487,15 @@ k3moe_status k3moe_step(const k3moe_layer *l, float *h, int32_t T, const float *
         StageMark m(l->prof, K3MOE_STAGE_PRENORM, st);
         if (launch_prenorm(h, T, v.H, gamma, eps, x, st) != hipSuccess) return K3MOE_E_HIP;
     }
-    if (launch_route(v, x, T, idx, w, nullptr, wsc, lay, st, l->prof) != hipSuccess) return K3MOE_E_HIP;
     OutEpi epi;
     epi.resid = true;
     epi.ob = hb;
+    if (T == 1 && decode_fused_ok(v)) {
+        if (launch_decode_fused(v, x, idx, w, nullptr, true, h, wsc, lay, st, l->prof, epi) != hipSuccess)
+            return K3MOE_E_HIP;
+        return K3MOE_OK;
+    }
+    if (launch_route(v, x, T, idx, w, nullptr, wsc, lay, st, l->prof) != hipSuccess) return K3MOE_E_HIP;
     if (launch_forward(v, x, T, idx, w, h, wsc, lay, st, l->prof, epi) != hipSuccess) return K3MOE_E_HIP;
     return K3MOE_OK;
 }

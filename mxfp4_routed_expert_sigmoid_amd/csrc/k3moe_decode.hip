@@ -1,0 +1,645 @@
+// The one-token layer of a flat layer in three launches: route + experts +
+// router-order combine ("kimi-k3-in-c" README §9 "Picking 16 experts of
+// 896": k3_router, k3_moe steps 3 and 6, k3_situ_glu; §4 "Reduction one: the
+// experts already ship at half a byte": the MXFP4 format).
+//
+//   R  (k_router)            the router rows (logits, scores)
+//   G  (k_dec_gateup)        the shared expert's gate/up rows (blocks that
+//                            need no routes, first in the grid), then the
+//                            top-k and the routed experts' gate/up rows and
+//                            activations (written as e4m3 terms)
+//   D  (k_dec_down)          the shared expert's down rows, the routed
+//                            experts' down rows, the router-order weighted
+//                            sum, the output
+//
+// Decode is a stream of weights from HBM: the design aims at the access
+// pattern a plain streaming read runs fastest with on MI355X, one wave
+// instruction = one contiguous kilobyte of one weight row, and at as few
+// launches as the data dependencies allow (route -> gate/up -> down).
+//
+// MFMA with row-contiguous loads. A wave's 64 lanes hold 64 consecutive
+// 16-byte pieces of ONE weight row (one 32-weight group each), not the
+// 16 rows x 64 bytes the MFMA operand layout asks for. The MFMA still does
+// the dot products: each lane also holds, as its B fragment, the other
+// operand at the same K positions as its own A fragment, so the product of a
+// lane's A with its own B sits on the diagonal of the 16 x 16 result
+// (C[i][i] sums lanes i, i+16, i+32, i+48), and the row's dot product is
+// the sum of the diagonal. Off-diagonal entries are never read.
+//  * bf16 MFMA (v_mfma_f32_16x16x32_bf16, gate/up): A and B take the same K
+//    positions in the same lane, so a lane's B is simply the token at its
+//    weights' positions, kept in registers for every row.
+//  * Scaled MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, down): the fp4 A of
+//    lane (i, g) = lane i + 16 g is the 32 K positions [32g, 32g + 32) of
+//    MFMA row i, while the fp8 B of lane (i, g') holds K positions
+//    [16g', 16g' + 16) in bytes 0..15 and [64 + 16g', 80 + 16g') in bytes
+//    16..31 of column i. So lane (i, g') loads, for its B, half g' & 1 of
+//    the activation pieces that lanes (i, g'/2) and (i, 2 + g'/2) multiply;
+//    the scale of B's K-block g comes from lane (i, g), which holds exactly
+//    that block's term scale.
+#include "k3moe_device.h"
+#include "k3moe_internal.h"
+
+namespace k3moe {
+namespace {
+
+// Loads in the streaming loops are plain loads from clamped (always valid)
+// addresses: a lane past a row's end reads real weights that meet a zero
+// operand on the other side (or a zero scale), so nothing is masked after
+// the load. Operands that stay in registers (the token, the activations, the
+// e4m3 terms) are masked once, when they are loaded, with a mask the
+// compiler cannot see through: a select on a loaded value may otherwise be
+// turned into a branch around the load, and a branch around a load makes the
+// wait-count pass drain every load in flight at the join.
+__device__ __forceinline__ uint32_t lane_mask(bool on)
+{
+    uint32_t m = on ? 0xffffffffu : 0u;
+    asm volatile("" : "+v"(m));
+    return m;
+}
+__device__ __forceinline__ u4 ld16m(const void *p, uint32_t m)
+{
+    const u4 v = *reinterpret_cast<const u4 *>(p);
+    return u4{v.x & m, v.y & m, v.z & m, v.w & m};
+}
+__device__ __forceinline__ u4 ld16(const void *p) { return *reinterpret_cast<const u4 *>(p); }
+
+// Sum over the wave, fixed order, through DPP (quad steps, half-row and row
+// mirrors, then the row broadcasts into lane 63), read back from lane 63.
+__device__ __forceinline__ float wave_sum(float v)
+{
+#define K3_DPP(x, ctrl, rmask) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, rmask, 0xf, false))
+    v += K3_DPP(v, 0xb1, 0xf);   // quad [1,0,3,2]
+    v += K3_DPP(v, 0x4e, 0xf);   // quad [2,3,0,1]
+    v += K3_DPP(v, 0x141, 0xf);  // row_half_mirror
+    v += K3_DPP(v, 0x140, 0xf);  // row_mirror
+    v += K3_DPP(v, 0x142, 0xa);  // row_bcast15 into rows 1, 3
+    v += K3_DPP(v, 0x143, 0xc);  // row_bcast31 into rows 2, 3
+#undef K3_DPP
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Diagonal of a 16 x 16 MFMA result, summed: lane L holds
+// C[4 (L / 16) + r][L % 16] in acc[r], so C[i][i] sits in the lanes with
+// (L % 16) / 4 == L / 16, register L % 4.
+__device__ __forceinline__ float diag_sum(const v4f acc)
+{
+    const int L = threadIdx.x & 63, r = L & 3;
+    const float v = r == 0 ? acc[0] : r == 1 ? acc[1] : r == 2 ? acc[2] : acc[3];
+    return wave_sum((((L & 15) >> 2) == (L >> 4)) ? v : 0.0f);
+}
+
+// ---------------------------------------------------------------------------
+// G: the routed experts' gate/up rows, one E8M0 block of a slot's activation
+// per 4-wave block: block q of slot j takes rows [32 q', 32 q' + 32) of gate
+// and up (q' = q mod I/32). Wave w streams ONE matrix (w & 1: gate, up) over
+// 16 rows (w >> 1: the first or second half), one weight stream per wave: on
+// MI355X a wave with one contiguous stream and two rows in flight keeps HBM
+// busier than one interleaving two streams. Each wave
+//  1. loads the token into registers at its lanes' K positions (lane l of
+//     row piece s: elements 2048 s + 32 l + [0, 32)),
+//  2. reads the slot's expert from the top-k that wave 0 takes from the
+//     router's scores (or from the ids given),
+//  3. stages its 16 E8M0 rows (contiguous) in LDS,
+//  4. streams its 16 rows, two in flight, each row piece as 4 bf16 MFMAs
+//     after an exact fp4 -> bf16 expansion (the diagonal dot product),
+//  5. parks its 16 sums in LDS; after the block barrier wave 0 takes the
+//     32 activations and splits them into 4 e4m3 terms with one E8M0 scale
+//     per term (the form the down kernel's scaled MFMA takes).
+constexpr int kDecGuPieces = 4;    // 1 KB pieces per row: H <= 8192
+constexpr int kDecUnitRows = 16;   // rows per wave
+
+struct DecGuParams {
+    const uint8_t *gp, *gs, *up, *us;
+    int64_t g_sp, g_ss, u_sp, u_ss;
+    int H, I, E, K, act;
+    float b1, b2;
+    int renorm;
+    float rscale;
+    const uint16_t *x;          // bf16 [H]
+    const float *sc, *ch;       // router scores [E] (fused top-k)
+    int32_t *idx;               // [K]: written by block 0 (fused top-k) or read
+    float *w;                   // [K]: written by block 0 (fused top-k)
+    uint8_t *aq;                // e4m3 terms [K][4][I]
+    uint8_t *as;                // their E8M0 scales [K][4][I / 32]
+    const uint16_t *sh_gate, *sh_up;  // bf16 [Is][H]
+    float *ash;                 // [Is] out: the shared expert's activation
+    int Is, nsh;                // shared row pairs; blocks given to them (first in the grid)
+};
+
+// LDS: the 4 waves' E8M0 rows (16 x H/32 bytes each), the top-k scratch,
+// the expert id, the parked sums [4][16].
+__host__ __device__ constexpr int dec_gu_lds_bytes(int H) { return 4 * (H / 2) + (int)sizeof(TopkLds) + 16 + 4 * 16 * 4; }
+
+// A shared gate/up block: wave w takes row pair n = 4 b + w (gate row n, up
+// row n), both rows' loads issued together, the token read from LDS at the
+// same slice positions (lane l: elements 512 s + 8 l + [0, 8) of slice s);
+// fp32 products in slice order, one wave-wide sum per row, the activation
+// into ash.
+template <int NS>
+__device__ void dec_shared_gateup(const DecGuParams &p, int b, uint8_t *lds)
+{
+    u4 *x_l = reinterpret_cast<u4 *>(lds);  // [NS][64]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = p.H;
+    const int n = 4 * b + wave;
+    const bool live = n < p.Is;
+    const uint16_t *r0 = p.sh_gate + (size_t)(live ? n : 0) * H, *r1 = p.sh_up + (size_t)(live ? n : 0) * H;
+    u4 w0[NS], w1[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {  // the rows first: they are the block's bytes
+        const int i = 512 * s + 8 * lane;
+        const int ic = i < H ? i : 0;  // off lanes meet a zero token
+        w0[s] = ld16(r0 + ic);
+        w1[s] = ld16(r1 + ic);
+    }
+    constexpr int XQ = (NS * 64 + 255) / 256;
+    u4 xs[XQ];
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+        const int i = threadIdx.x + 256 * q;
+        const bool on = i < NS * 64 && 8 * i < H;
+        xs[q] = ld16m(p.x + (on ? 8 * i : 0), lane_mask(on));
+    }
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+        const int i = threadIdx.x + 256 * q;
+        if (i < NS * 64) x_l[i] = xs[q];
+    }
+    __syncthreads();
+    if (!live) return;
+    float g = 0.0f, u = 0.0f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+        const u4 xv = x_l[s * 64 + lane];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float xl = bf16f(xv[q] & 0xffffu), xh = bf16f(xv[q] >> 16);
+            g = fmaf(bf16f(w0[s][q] & 0xffffu), xl, g);
+            g = fmaf(bf16f(w0[s][q] >> 16), xh, g);
+            u = fmaf(bf16f(w1[s][q] & 0xffffu), xl, u);
+            u = fmaf(bf16f(w1[s][q] >> 16), xh, u);
+        }
+    }
+    g = wave_sum(g);
+    u = wave_sum(u);
+    if (lane == 0) p.ash[n] = act_fn(g, u, p.act, p.b1, p.b2);
+}
+
+// Split the activations held by lanes 0..31 (one E8M0 block) into 4 e4m3
+// terms: per term, the scale puts the block's largest remainder in
+// [224, 448], the term takes only the elements within 6 binades of that
+// maximum (the scaled MFMA sums 16-product runs to about 14 bits below the
+// run's largest product) and its rounding error is carried exactly into the
+// next term.
+__device__ __forceinline__ void split_terms_32(float r, uint8_t *term, size_t term_stride, uint8_t *sc,
+                                               size_t sc_stride)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int t = 0; t < kATerms; ++t) {
+        float m = fabsf(r);
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));  // within lanes 0..31
+        int S = 0;
+        float keep_min = INFINITY;
+        if (m > 0.0f) {
+            int ex;
+            frexpf(m, &ex);
+            S = ex - 9;
+            if (ldexpf(m, -S) > 448.0f) S += 1;
+            if (S < -127) S = -127;
+            frexpf(ldexpf(m, -S), &ex);
+            keep_min = ldexpf(1.0f, ex - 7);
+        }
+        const float q = ldexpf(r, -S);
+        uint32_t c = 0;
+        if (fabsf(q) >= keep_min) {
+            c = __builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xffu;
+            r -= ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)c, 0), S);
+        }
+        if (lane < 32) term[t * term_stride + lane] = (uint8_t)c;
+        if (lane == 0) sc[t * sc_stride] = (uint8_t)(S + 127);
+    }
+}
+
+// NQ > 0: wave 0 takes the top-k here (16-byte score loads, NQ experts per
+// lane); NQ == 0: the ids are read from p.idx.
+template <int NQ, int NS>
+__global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    if ((int)blockIdx.x < p.nsh) {
+        dec_shared_gateup<NS>(p, blockIdx.x, lds);
+        return;
+    }
+    const int bid = blockIdx.x - p.nsh;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int H = p.H, HB = H >> 1, HG = H >> 5;  // packed bytes and E8M0 groups per row
+    const int NG = p.I >> 5;                      // E8M0 blocks per slot activation
+    const int j = bid / NG, qb = bid - j * NG;
+    const int mat = wave & 1, half = wave >> 1;
+    uint8_t *sc_l = lds + wave * (H / 2);
+    TopkLds &tl = *reinterpret_cast<TopkLds *>(lds + 2 * H);
+    int *e_l = reinterpret_cast<int *>(lds + 2 * H + sizeof(TopkLds));
+    float *sum_l = reinterpret_cast<float *>(lds + 2 * H + sizeof(TopkLds) + 16);  // [4][16]
+
+    // 1. the token at this lane's K positions
+    u4 xv[kDecGuPieces][4];
+#pragma unroll
+    for (int s = 0; s < kDecGuPieces; ++s)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int i = 2048 * s + 32 * lane + 8 * c;
+            xv[s][c] = ld16m(p.x + (i < H ? i : 0), lane_mask(i < H));
+        }
+
+    // 2. the slot's expert
+    if constexpr (NQ > 0) {
+        if (wave == 0) {
+            int pick;
+            float wt;
+            topk_wave<NQ, true>(p.sc, p.ch, p.E, p.K, p.renorm, p.rscale, tl, &pick, &wt);
+            if (bid == 0 && lane < p.K) {
+                p.idx[lane] = pick;
+                p.w[lane] = wt;
+            }
+            if (lane == 0) e_l[0] = __builtin_amdgcn_readlane(pick, j);
+        }
+        __syncthreads();
+    } else {
+        if (threadIdx.x == 0) e_l[0] = p.idx[j];
+        __syncthreads();
+    }
+    int e = e_l[0];
+    const bool ok = e >= 0 && e < p.E;  // an invalid id: zero activations (the down kernel drops it)
+    e = ok ? e : 0;
+
+    // 3. this wave's 16 E8M0 rows (contiguous: 16 x H/32 bytes)
+    const int row0 = 32 * qb + kDecUnitRows * half;
+    const uint8_t *sbase = (mat ? p.us + (int64_t)e * p.u_ss : p.gs + (int64_t)e * p.g_ss) + (size_t)row0 * HG;
+    const uint8_t *wbase = (mat ? p.up + (int64_t)e * p.u_sp : p.gp + (int64_t)e * p.g_sp) + (size_t)row0 * HB;
+    constexpr int SQ = 8192 / 2 / 1024;  // 16-byte pieces per lane (H <= 8192)
+    u4 scv[SQ];
+#pragma unroll
+    for (int k = 0; k < SQ; ++k) {
+        const int i = 16 * lane + 1024 * k;
+        scv[k] = ld16(sbase + (i < H / 2 ? i : 0));
+    }
+
+    // 4. the rows, two in flight (named buffers, so the compiler's wait
+    // counts follow the rotation); row r's sum is parked in lane r
+    int soff[kDecGuPieces];        // this lane's offset in a row piece (off lanes: 0)
+    int gidx[kDecGuPieces];        // this lane's E8M0 group (off lanes: 0)
+    uint32_t smask[kDecGuPieces];  // off lanes scale their weights by 0
+#pragma unroll
+    for (int s = 0; s < kDecGuPieces; ++s) {
+        const bool on = 64 * s + lane < HG;
+        soff[s] = on ? 1024 * s + 16 * lane : 0;
+        gidx[s] = on ? 64 * s + lane : 0;
+        smask[s] = lane_mask(on);
+    }
+    struct Row {
+        u4 a[kDecGuPieces];
+    };
+    auto load = [&](int r, Row &b) {
+        const size_t ro = (size_t)min(r, kDecUnitRows - 1) * HB;
+#pragma unroll
+        for (int s = 0; s < kDecGuPieces; ++s) b.a[s] = ld16(wbase + ro + soff[s]);
+    };
+    float mine = 0.0f;
+    auto compute = [&](int r, const Row &b) {
+        v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < kDecGuPieces; ++s) {
+            const float f = __uint_as_float(__float_as_uint(e8m0_to_f32(sc_l[r * HG + gidx[s]])) & smask[s]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc = mfma_bf16(dequant8_bf16(b.a[s][c], f), as_bf8(xv[s][c]), acc);
+        }
+        const float v = diag_sum(acc);
+        mine = lane == r ? v : mine;
+    };
+    Row b0, b1;
+    load(0, b0);
+    load(1, b1);
+#pragma unroll
+    for (int k = 0; k < SQ; ++k) {
+        const int i = 16 * lane + 1024 * k;
+        if (i < H / 2) *reinterpret_cast<u4 *>(sc_l + i) = scv[k];
+    }
+    wave_lds_sync();  // the E8M0 rows are in LDS
+    for (int r = 0; r < kDecUnitRows; r += 2) {
+        compute(r, b0);
+        load(r + 2, b0);
+        compute(r + 1, b1);
+        load(r + 3, b1);
+    }
+    if (lane < kDecUnitRows) sum_l[wave * kDecUnitRows + lane] = mine;
+    __syncthreads();
+
+    // 5. wave 0: the 32 activations (lane l: row 32 qb + l) as e4m3 terms
+    if (wave == 0) {
+        const int hl = (lane >> 4) & 1, rl = lane & 15;  // lanes 32..63 repeat 0..31 (unused)
+        const float g = sum_l[(2 * hl) * kDecUnitRows + rl], u = sum_l[(2 * hl + 1) * kDecUnitRows + rl];
+        const float a = ok ? act_fn(g, u, p.act, p.b1, p.b2) : 0.0f;
+        split_terms_32(lane < 32 ? a : 0.0f, p.aq + ((size_t)j * kATerms) * p.I + (size_t)qb * 32, p.I,
+                       p.as + ((size_t)j * kATerms) * NG + qb, NG);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// D: the routed experts' down rows, the router-order sum and the shared rows.
+// Block b owns output rows [b RB, b RB + RB) for every slot; wave w takes
+// slots w and w + 8. A slot's B operands (4 e4m3 terms of its activation,
+// arranged for the diagonal) and their scales stay in registers for all the
+// block's rows; a row of W2 is one wave instruction (lane l: group l, I/32
+// lanes). The per-slot results go to LDS and one pass sums them in router
+// order, adds the shared row and applies the epilogue.
+constexpr int kDecDnWaves = 8;
+constexpr int kDecDnDepth = 4;     // rows (two slots each) in flight per wave
+constexpr int kDecShRows = 4;      // shared rows per wave: a block owns at most 32 rows
+constexpr int kDecShSl = 4;        // 512-element slices of a shared row (I_s <= 2048)
+
+struct DecDnParams {
+    const uint8_t *dp, *ds;
+    int64_t d_sp, d_ss;
+    int H, I, E, K, RB;
+    const int32_t *idx;
+    const float *w;
+    const uint8_t *aq, *as;
+    const uint16_t *sh_down;    // bf16 [H][Is] (Is == 0: none)
+    const float *ash;           // [Is]
+    int Is;
+    float *out;
+    int resid;
+    uint16_t *ob;
+    unsigned long long *errors;
+};
+
+__global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
+{
+    extern __shared__ __align__(16) float y_l[];  // [K][RB]
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int I = p.I, NG = I >> 5, IB = I >> 1;
+    const int r0 = blockIdx.x * p.RB, nr = min(p.RB, p.H - r0);
+    const int ns = (p.K - wave + kDecDnWaves - 1) / kDecDnWaves;  // slots of this wave (0..2)
+
+    // the shared expert's rows of this block first (they need no routes):
+    // wave w takes rows r0 + w + 8 k, all its loads issued together
+    __shared__ float sh_l[kDecShRows * kDecDnWaves];
+    const int NSS = (p.Is + 511) >> 9;
+    u4 shw[kDecShRows][kDecShSl];
+    float4 sha[kDecShSl][2];
+    if (p.Is > 0) {
+#pragma unroll
+        for (int k = 0; k < kDecShRows; ++k) {
+            const int r = r0 + min(wave + kDecDnWaves * k, nr - 1);
+#pragma unroll
+            for (int sl = 0; sl < kDecShSl; ++sl) {
+                const bool on = sl < NSS && 512 * sl + 8 * lane < p.Is;
+                shw[k][sl] = ld16(p.sh_down + (size_t)r * p.Is + (on ? 512 * sl + 8 * lane : 0));
+            }
+        }
+#pragma unroll
+        for (int sl = 0; sl < kDecShSl; ++sl) {
+            const bool on = sl < NSS && 512 * sl + 8 * lane < p.Is;
+            const int i = on ? 512 * sl + 8 * lane : 0;
+            const uint32_t m = lane_mask(on);  // off lanes: a zero activation
+            const u4 a0 = ld16m(p.ash + i, m), a1 = ld16m(p.ash + i + 4, m);
+            sha[sl][0] = float4{__uint_as_float(a0.x), __uint_as_float(a0.y), __uint_as_float(a0.z), __uint_as_float(a0.w)};
+            sha[sl][1] = float4{__uint_as_float(a1.x), __uint_as_float(a1.y), __uint_as_float(a1.z), __uint_as_float(a1.w)};
+        }
+    }
+
+    // the routing weights, zero for an id outside [0, E) (its slot adds
+    // nothing), loaded once
+    float wk[2 * kDecDnWaves];
+#pragma unroll
+    for (int j = 0; j < 2 * kDecDnWaves; ++j) {
+        const int jc = min(j, p.K - 1);
+        const int e = p.idx[jc];
+        const float wv = p.w[jc];
+        wk[j] = (j < p.K && e >= 0 && e < p.E) ? wv : 0.0f;
+    }
+    int ej[2];
+    v8i bt[2][kATerms];
+    int bs[2][kATerms];
+    const int i16 = lane & 15, g4 = lane >> 4;
+    const int p0 = 32 * (i16 + 16 * (g4 >> 1)) + 16 * (g4 & 1);
+    const int p1 = 32 * (i16 + 16 * (2 + (g4 >> 1))) + 16 * (g4 & 1);
+    const bool on = lane < NG;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int j = wave + kDecDnWaves * m;
+        const int jj = m < ns ? j : 0;
+        const int e = p.idx[jj];
+        ej[m] = (m < ns && e >= 0 && e < p.E) ? e : -1;
+#pragma unroll
+        for (int t = 0; t < kATerms; ++t) {
+            const uint8_t *tr = p.aq + ((size_t)jj * kATerms + t) * I;
+            const u4 l2 = ld16m(tr + (p0 < I ? p0 : 0), lane_mask(p0 < I));
+            const u4 h2 = ld16m(tr + (p1 < I ? p1 : 0), lane_mask(p1 < I));
+            bt[m][t] = v8i{(int)l2.x, (int)l2.y, (int)l2.z, (int)l2.w, (int)h2.x, (int)h2.y, (int)h2.z, (int)h2.w};
+            bs[m][t] = on ? (int)p.as[((size_t)jj * kATerms + t) * NG + lane] : 127;
+        }
+    }
+
+    // the block's rows, both slots of the wave per row (a wave with one slot
+    // computes the second on its first slot's data and drops it); loads past
+    // the last row re-read it (never used). Lanes past I/32 read group 0 of
+    // the row and meet a zero B operand.
+    const int nrow = max(nr, 1);
+    const int e0 = max(ej[0], 0), e1 = max(ns > 1 ? ej[1] : ej[0], 0);
+    const uint8_t *pa0 = p.dp + (int64_t)e0 * p.d_sp + (on ? 16 * lane : 0);
+    const uint8_t *pa1 = p.dp + (int64_t)e1 * p.d_sp + (on ? 16 * lane : 0);
+    const uint8_t *ps0 = p.ds + (int64_t)e0 * p.d_ss + (on ? lane : 0);
+    const uint8_t *ps1 = p.ds + (int64_t)e1 * p.d_ss + (on ? lane : 0);
+    struct Row {
+        u4 a0, a1;
+        uint32_t s0, s1;
+    };
+    auto load = [&](int rr, Row &b) {
+        const size_t r = (size_t)(r0 + min(rr, nrow - 1));
+        b.a0 = ld16(pa0 + r * IB);
+        b.a1 = ld16(pa1 + r * IB);
+        b.s0 = ps0[r * NG];
+        b.s1 = ps1[r * NG];
+    };
+    auto mma = [&](const u4 a, uint32_t sb, const v8i (&B)[kATerms], const int (&S)[kATerms]) {
+        const bool drop = sb == 255u;  // E8M0 255: the group contributes nothing
+        const u4 av = drop ? u4{0u, 0u, 0u, 0u} : a;
+        const int sa = drop ? 127 : (int)sb;
+        const v8i A = v8i{(int)av.x, (int)av.y, (int)av.z, (int)av.w, 0, 0, 0, 0};
+        v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int t = 0; t < kATerms; ++t) acc = mfma_fp4_fp8(A, B[t], acc, sa, S[t]);
+        return acc;
+    };
+    Row buf[kDecDnDepth];
+#pragma unroll
+    for (int d = 0; d < kDecDnDepth; ++d) load(d, buf[d]);
+    if (p.Is > 0) {  // the shared rows: fp32 products in slice order, one wave-wide sum per row
+#pragma unroll
+        for (int k = 0; k < kDecShRows; ++k) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int sl = 0; sl < kDecShSl; ++sl) {
+                const u4 w = shw[k][sl];
+                const float4 x0 = sha[sl][0], x1 = sha[sl][1];
+                acc = fmaf(bf16f(w[0] & 0xffffu), x0.x, acc);
+                acc = fmaf(bf16f(w[0] >> 16), x0.y, acc);
+                acc = fmaf(bf16f(w[1] & 0xffffu), x0.z, acc);
+                acc = fmaf(bf16f(w[1] >> 16), x0.w, acc);
+                acc = fmaf(bf16f(w[2] & 0xffffu), x1.x, acc);
+                acc = fmaf(bf16f(w[2] >> 16), x1.y, acc);
+                acc = fmaf(bf16f(w[3] & 0xffffu), x1.z, acc);
+                acc = fmaf(bf16f(w[3] >> 16), x1.w, acc);
+            }
+            acc = wave_sum(acc);
+            if (lane == 0) sh_l[wave + kDecDnWaves * k] = acc;
+        }
+    }
+    for (int r = 0; r < nrow; r += kDecDnDepth) {
+#pragma unroll
+        for (int d = 0; d < kDecDnDepth; ++d) {
+            const v4f c0 = mma(buf[d].a0, buf[d].s0, bt[0], bs[0]);
+            const v4f c1 = mma(buf[d].a1, buf[d].s1, bt[1], bs[1]);
+            load(r + d + kDecDnDepth, buf[d]);
+            const float y0 = diag_sum(c0), y1 = diag_sum(c1);
+            if (lane == 0 && r + d < nr) {
+                if (ns > 0) y_l[wave * p.RB + r + d] = ej[0] >= 0 ? y0 : 0.0f;
+                if (ns > 1) y_l[(wave + kDecDnWaves) * p.RB + r + d] = ej[1] >= 0 ? y1 : 0.0f;
+            }
+        }
+    }
+    __syncthreads();
+
+    // router-order sum (ids outside [0, E) add nothing), the shared row, the epilogue
+    for (int r = threadIdx.x; r < nr; r += blockDim.x) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 2 * kDecDnWaves; ++j)
+            if (j < p.K) acc = fmaf(wk[j], y_l[j * p.RB + r], acc);  // a dropped slot: 0 * 0
+        if (p.Is > 0) acc += sh_l[r];  // row r0 + r: wave r % 8, k = r / 8
+        float *op = p.out + r0 + r;
+        if (p.resid) acc = *op + acc;
+        *op = acc;
+        if (p.ob) p.ob[r0 + r] = bf16_rne(acc);
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        for (int j = 0; j < p.K; ++j)
+            if (p.idx[j] < 0 || p.idx[j] >= p.E) atomicAdd(p.errors, 1ull);
+}
+
+}  // namespace
+
+// The shapes the three kernels take: a flat layer, H <= 8192 (four 1 KB
+// pieces per gate/up row, sixteen 512-element router slices), I <= 2048 (a
+// down row in one wave instruction), I_s <= 2048, top-k <= 16 (two slots per
+// down wave).
+bool decode_fused_ok(const LayerView &L)
+{
+    return L.Lt == 0 && L.H <= 8192 && L.H % 128 == 0 && L.I <= 2048 && L.I % 128 == 0 && L.Is <= 2048 &&
+           L.K <= 2 * kDecDnWaves && L.E <= kMaxExperts && 32 * L.H >= L.I;
+}
+
+// Workspace use (the T = 1 layout): sc, ch; ash; the e4m3 terms in act
+// (k * 4 * I bytes); their E8M0 scales in ys.
+hipError_t launch_decode_fused(const LayerView &L, const uint16_t *x, int32_t *idx, float *w, float *logits,
+                               bool route, float *out, char *ws, const WsLayout &lay, hipStream_t s,
+                               Profiler *prof, const OutEpi &epi)
+{
+    int dev = 0, ncu = 256;
+    if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    float *sc = reinterpret_cast<float *>(ws + lay.sc);
+    float *ch = reinterpret_cast<float *>(ws + lay.ch);
+    float *ash = reinterpret_cast<float *>(ws + lay.ash);
+    uint8_t *aq = reinterpret_cast<uint8_t *>(ws + lay.act);
+    uint8_t *as = reinterpret_cast<uint8_t *>(ws + lay.ys);
+
+    // R: the router rows (logits, scores)
+    if (route) {
+        StageMark m(prof, K3MOE_STAGE_ROUTER, s);
+        if (launch_router_t1(L, x, sc, ch, logits, s) != hipSuccess) return hipGetLastError();
+    }
+    // the top-k in G (16 experts per lane, 16-byte loads) or on its own
+    const bool fused_topk = route && L.E > 512 && L.E <= 1024 && L.E % 4 == 0;
+    if (route && !fused_topk) {
+        StageMark m(prof, K3MOE_STAGE_TOPK, s);
+        if (launch_topk(L, 1, sc, ch, idx, w, s) != hipSuccess) return hipGetLastError();
+    }
+    // G: top-k, routed gate/up
+    {
+        StageMark m(prof, K3MOE_STAGE_GATEUP, s);
+        DecGuParams gp{};
+        gp.gp = L.gp;
+        gp.gs = L.gs;
+        gp.up = L.up;
+        gp.us = L.us;
+        gp.g_sp = L.g_sp;
+        gp.g_ss = L.g_ss;
+        gp.u_sp = L.u_sp;
+        gp.u_ss = L.u_ss;
+        gp.H = L.H;
+        gp.I = L.I;
+        gp.E = L.E;
+        gp.K = L.K;
+        gp.act = L.act;
+        gp.b1 = L.b1;
+        gp.b2 = L.b2;
+        gp.renorm = L.renorm;
+        gp.rscale = L.routed_scale;
+        gp.x = x;
+        gp.sc = sc;
+        gp.ch = ch;
+        gp.idx = idx;
+        gp.w = w;
+        gp.aq = aq;
+        gp.as = as;
+        gp.sh_gate = L.sh_gate;
+        gp.sh_up = L.sh_up;
+        gp.ash = ash;
+        gp.Is = L.Is;
+        gp.nsh = (L.Is + 3) / 4;
+        const unsigned nb = (unsigned)(gp.nsh + L.K * (L.I / 32));
+        const int NS = L.H <= 2048 ? 4 : L.H <= 4096 ? 8 : L.H <= 7168 ? 14 : 16;
+        const size_t lds = std::max<size_t>(dec_gu_lds_bytes(L.H), (size_t)NS * 64 * 16);
+#define K3_GU(NQ, NSL) k_dec_gateup<NQ, NSL><<<nb, 256, lds, s>>>(gp)
+        if (fused_topk) {
+            if (NS == 4) K3_GU(16, 4); else if (NS == 8) K3_GU(16, 8); else if (NS == 14) K3_GU(16, 14); else K3_GU(16, 16);
+        } else {
+            if (NS == 4) K3_GU(0, 4); else if (NS == 8) K3_GU(0, 8); else if (NS == 14) K3_GU(0, 14); else K3_GU(0, 16);
+        }
+#undef K3_GU
+    }
+    // D: shared down, routed down, router-order sum, epilogue
+    {
+        StageMark m(prof, K3MOE_STAGE_DOWN, s);
+        DecDnParams dp{};
+        dp.dp = L.dp;
+        dp.ds = L.ds;
+        dp.d_sp = L.d_sp;
+        dp.d_ss = L.d_ss;
+        dp.H = L.H;
+        dp.I = L.I;
+        dp.E = L.E;
+        dp.K = L.K;
+        // one block per CU, at most kDecShRows rows per wave
+        const int nb = std::max(std::min(ncu, L.H), (L.H + kDecShRows * kDecDnWaves - 1) / (kDecShRows * kDecDnWaves));
+        dp.RB = (L.H + nb - 1) / nb;
+        dp.idx = idx;
+        dp.w = w;
+        dp.aq = aq;
+        dp.as = as;
+        dp.sh_down = L.sh_down;
+        dp.ash = ash;
+        dp.Is = L.Is;
+        dp.out = out;
+        dp.resid = epi.resid;
+        dp.ob = epi.ob;
+        dp.errors = L.errors;
+        const unsigned grid = (unsigned)((L.H + dp.RB - 1) / dp.RB);
+        k_dec_down<<<grid, 64 * kDecDnWaves, sizeof(float) * L.K * dp.RB, s>>>(dp);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace k3moe

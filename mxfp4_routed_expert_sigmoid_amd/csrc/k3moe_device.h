@@ -1,0 +1,274 @@
+// Device helpers shared by the gfx950 kernel files: vector types, bf16 and
+// E8M0 conversions, the fp4 -> bf16 expansion, MFMA wrappers, the gated
+// activation, wave-level reductions and the top-k of one token.
+#pragma once
+
+#include <math.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include <hip/hip_runtime.h>
+
+#include "k3moe.h"
+
+namespace k3moe {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned u4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+
+// bf16 bit pattern (low 16 bits of h) -> fp32, exactly.
+__device__ __forceinline__ float bf16f(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite values).
+__device__ __forceinline__ uint32_t bf16_rne_u32(float f)
+{
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint16_t bf16_rne(float f) { return (uint16_t)bf16_rne_u32(f); }
+
+// E8M0 byte -> the fp32 factor 2^(s-127) for the scaled converters; byte 0 is
+// the subnormal 2^-127, byte 255 drops its group (factor 0).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s)
+{
+    return s == 255u ? 0.0f : __uint_as_float(s == 0u ? 0x00400000u : s << 23);
+}
+
+// 8 fp4 weights (one 32-bit word, low nibble first) -> 8 bf16, scaled
+// exactly (every fp4 value times a power of two is a bf16).
+__device__ __forceinline__ bf8 dequant8_bf16(uint32_t w, float scale)
+{
+    const bf2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+    const bf2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+    const bf2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+    const bf2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+    return bf8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+__device__ __forceinline__ bf8 as_bf8(u4 v)
+{
+    bf8 r;
+    __builtin_memcpy(&r, &v, 16);
+    return r;
+}
+
+__device__ __forceinline__ v4f mfma_bf16(const bf8 &a, const bf8 &b, v4f c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Scaled MFMA, A in fp4 (format 4), B in fp8 e4m3 (format 0); the scale
+// bytes are taken from byte S of the packed scale words.
+template <int S = 0>
+__device__ __forceinline__ v4f mfma_fp4_fp8(const v8i &a, const v8i &b, v4f c, int sa, int sb)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, S, sa, S, sb);
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
+// Gated activation (README §9, k3_situ_glu): SiTU-GLU (the sigmoid on the
+// raw gate) or SwiGLU, fp32.
+__device__ __forceinline__ float act_fn(float g, float u, int kind, float b1, float b2)
+{
+    const float sg = 1.0f / (1.0f + expf(-g));
+    if (kind == K3MOE_ACT_SITU) return (b1 * tanhf(g / b1) * sg) * (b2 * tanhf(u / b2));
+    return g * sg * u;
+}
+
+// Orders LDS traffic of one wave: its earlier LDS stores are complete and
+// visible to every lane of the wave before its later LDS loads (the wave's
+// LDS operations complete in order; the clobber stops the compiler moving
+// memory operations across).
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Wave-wide max / min of a uint32 through DPP (row-local steps, then the
+// row broadcasts), read back from lane 63: the same value in every lane.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v)
+{
+    auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xb1, 0xf, 0xf, false));   // quad [1,0,3,2]
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4e, 0xf, 0xf, false));   // quad [2,3,0,1]
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xf, 0xf, false));  // row_mirror
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast15
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Order-preserving uint32 key of a selection score (> 0 for every float;
+// NaN ranks as -inf).
+__device__ __forceinline__ uint32_t order_key(float v)
+{
+    if (v != v) v = -INFINITY;
+    const uint32_t b = __float_as_uint(v);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// LDS a wave's top-k works in.
+struct TopkLds {
+    uint32_t lmax[64];
+    uint64_t cc[64];   // candidates: key << 32 | ~expert
+    float cs[64];      // their unbiased scores
+    int pi[64];        // picks in router order: expert, score
+    float ps[64];
+};
+
+// Top-k of one token (README §9, k3_router): the k largest selection scores
+// ch, in descending order, equal scores by ascending expert index (the order
+// of a repeated strict maximum); weights are the unbiased scores sc of the
+// picks, renormalised in router order when renorm is set, then scaled.
+// One wave; lane l holds the scores of experts l*NQ .. l*NQ+NQ-1 (a
+// contiguous range, so a lower lane always holds lower expert indices) as
+// order-preserving keys.
+//
+// Threshold and rank: tau = the k-th largest of the 64 lane maxima. k lanes
+// hold a key >= tau, so the k-th largest key is >= tau and every pick is
+// among the candidates {key >= tau}. When there are at most 64 candidates
+// (the usual case: about k of them), they are gathered in LDS, each takes
+// its rank in the order above by comparing against all of them, and the
+// first k ranks are the picks. A candidate is one 64-bit word, key in the
+// high half and the complement of its expert index in the low half, so that
+// order is a single unsigned comparison; the 64 slots are prefilled with 0,
+// which no candidate is below. With more candidates (heavy ties) the wave
+// falls back to k rounds of a wave-wide maximum, the lowest lane holding it
+// winning and rescanning its keys.
+//
+// Returns, in lane j < k, pick j's expert (*pick) and weight (*wt). V4:
+// E a multiple of 4 and rows 16-byte aligned (16-byte loads).
+template <int NQ, bool V4>
+__device__ __forceinline__ void topk_wave(const float *__restrict__ sc, const float *__restrict__ ch, int E, int K,
+                                          int renorm, float rscale, TopkLds &L, int *pick, float *wt)
+{
+    const int lane = threadIdx.x & 63;
+    const int e0 = lane * NQ;
+    // the selection scores and the scores are loaded together, every load
+    // issued before the first is used (clamped index, no branch)
+    float raw[NQ], sv[NQ];
+    if constexpr (V4) {
+#pragma unroll
+        for (int q = 0; q < NQ; q += 4) {
+            const int b = min(e0 + q, E - 4);
+            const float4 a = *reinterpret_cast<const float4 *>(ch + b);
+            const float4 d = *reinterpret_cast<const float4 *>(sc + b);
+            raw[q] = a.x, raw[q + 1] = a.y, raw[q + 2] = a.z, raw[q + 3] = a.w;
+            sv[q] = d.x, sv[q + 1] = d.y, sv[q + 2] = d.z, sv[q + 3] = d.w;
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+            raw[q] = ch[min(e0 + q, E - 1)];
+            sv[q] = sc[min(e0 + q, E - 1)];
+        }
+    }
+    uint32_t v[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) v[q] = e0 + q < E ? order_key(raw[q]) : 0u;  // 0: none / taken
+    uint32_t lm = 0u;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) lm = v[q] > lm ? v[q] : lm;
+
+    // tau: the lane maximum of rank k-1 (ranks 0..63 distinct: equal maxima
+    // by lane)
+    L.lmax[lane] = lm;
+    L.cc[lane] = 0ull;
+    wave_lds_sync();
+    int rank = 0;
+#pragma unroll 16
+    for (int j = 0; j < 64; ++j) {
+        const uint32_t u = L.lmax[j];
+        rank += (u > lm || (u == lm && j < lane)) ? 1 : 0;
+    }
+    const uint64_t at = __ballot(rank == K - 1);
+    const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)lm, (int)__builtin_ctzll(at));
+
+    // gather the candidates (key >= tau; a key of 0 is no expert)
+    int C = 0;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+        const bool in = v[q] >= tau && v[q] != 0u;
+        const uint64_t m = __ballot(in);
+        const int pos = C + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (in && pos < 64) {
+            L.cc[pos] = ((uint64_t)v[q] << 32) | (uint32_t)~(uint32_t)(e0 + q);
+            L.cs[pos] = sv[q];
+        }
+        C += __popcll(m);
+    }
+    wave_lds_sync();
+
+    int mine = 0;
+    float mine_s = 0.0f;  // score of pick j, held by lane j
+    if (C <= 64) {
+        const uint64_t k0 = L.cc[lane];
+        int r = 0;
+#pragma unroll
+        for (int j = 0; j < 64; ++j) r += L.cc[j] > k0 ? 1 : 0;
+        if (lane < C && r < K) {
+            L.pi[r] = (int)~(uint32_t)k0;
+            L.ps[r] = L.cs[lane];
+        }
+        wave_lds_sync();
+        if (lane < K) {
+            mine = L.pi[lane];
+            mine_s = L.ps[lane];
+        }
+    } else {
+        uint32_t bk;  // best remaining key of this lane (0: none)
+        int bq;       // its position
+        auto rescan = [&]() {
+            bk = 0u;
+            bq = 0;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                const bool gt = v[q] > bk;
+                bk = gt ? v[q] : bk;
+                bq = gt ? q : bq;
+            }
+        };
+        rescan();
+        for (int j = 0; j < K; ++j) {
+            const uint32_t m = wave_reduce_u32<true>(bk);
+            const uint64_t holders = __ballot(bk == m);
+            const int wl = (int)__builtin_ctzll(holders);  // lowest lane holding the maximum
+            const int win = wl * NQ + __builtin_amdgcn_readlane(bq, wl);
+            float ws = 0.0f;
+            if (lane == wl) {
+#pragma unroll
+                for (int q = 0; q < NQ; ++q)
+                    if (q == bq) {
+                        ws = sv[q];
+                        v[q] = 0u;
+                    }
+                rescan();
+            }
+            ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ws), wl));
+            if (lane == j) {
+                mine = win;
+                mine_s = ws;
+            }
+        }
+    }
+    // renormalisation: the sum runs over the picks in router order
+    float s = 0.0f;
+    for (int j = 0; j < K; ++j) s += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine_s), j));
+    float v0 = mine_s;
+    if (renorm && s > 0.0f) v0 /= s;
+    *pick = mine;
+    *wt = v0 * rscale;
+}
+
+}  // namespace k3moe

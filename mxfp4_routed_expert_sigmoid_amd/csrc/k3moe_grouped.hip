@@ -26,62 +26,13 @@
 // the shared expert); the combine sums them in router order.
 #include <type_traits>
 
+#include "k3moe_device.h"
 #include "k3moe_internal.h"
 
 namespace k3moe {
 namespace {
 
-typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef unsigned u4 __attribute__((ext_vector_type(4)));
-
 constexpr int kBPad = 16;       // LDS padding per token row
-
-__device__ __forceinline__ float bf16f(uint32_t h) { return __uint_as_float(h << 16); }
-
-__device__ __forceinline__ uint16_t bf16_rne(float f)
-{
-    const uint32_t u = __float_as_uint(f);
-    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
-
-// E8M0 byte -> fp32 scale for the converter: 2^(s-127); byte 0 is the
-// subnormal 2^-127; byte 255 drops its group (scale 0).
-__device__ __forceinline__ float e8m0_scale(uint32_t s)
-{
-    return s == 255u ? 0.0f : __uint_as_float(s == 0u ? 0x00400000u : s << 23);
-}
-
-// 8 fp4 weights (one 32-bit word, low nibble first) -> 8 bf16, scaled.
-__device__ __forceinline__ bf8 dequant8(uint32_t w, float scale)
-{
-    const bf2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
-    const bf2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
-    const bf2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
-    const bf2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
-    return bf8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
-__device__ __forceinline__ bf8 as_bf8(u4 v)
-{
-    bf8 r;
-    __builtin_memcpy(&r, &v, 16);
-    return r;
-}
-
-__device__ __forceinline__ v4f mfma_bf16(const bf8 &a, const bf8 &b, v4f c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// Gated activation (README §9, k3_situ_glu): SiTU-GLU or SwiGLU, fp32.
-__device__ __forceinline__ float act_fn(float g, float u, int kind, float b1, float b2)
-{
-    const float sg = 1.0f / (1.0f + expf(-g));
-    if (kind == K3MOE_ACT_SITU) return (b1 * tanhf(g / b1) * sg) * (b2 * tanhf(u / b2));
-    return g * sg * u;
-}
 
 // ---------------------------------------------------------------------------
 // Work lists. Active expert q (ascending id) with n_q assignments goes to the
@@ -311,7 +262,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &p, int e, int rb, in
 #pragma unroll
             for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-                for (int rf = 0; rf < RF; ++rf) sc[m][rf] = e8m0_scale((b.s[m][rf] >> (8 * g)) & 0xffu);
+                for (int rf = 0; rf < RF; ++rf) sc[m][rf] = e8m0_to_f32((b.s[m][rf] >> (8 * g)) & 0xffu);
         }
 #pragma unroll
         for (int st = 0; st < SPC; ++st) {
@@ -321,7 +272,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &p, int e, int rb, in
 #pragma unroll
                 for (int rf = 0; rf < RF; ++rf) {
                     if constexpr (FP4)
-                        a[m][rf] = dequant8(b.a[m][rf][st], sc[m][rf]);
+                        a[m][rf] = dequant8_bf16(b.a[m][rf][st], sc[m][rf]);
                     else
                         a[m][rf] = as_bf8(b.a[m][rf]);
                 }

@@ -123,6 +123,10 @@ int router_kspan(int H, int S);
 hipError_t launch_route(const LayerView &L, const uint16_t *x, int T, int32_t *idx,
                         float *w, float *logits, char *ws, const WsLayout &lay,
                         hipStream_t s, Profiler *prof);
+hipError_t launch_topk(const LayerView &L, int T, const float *sc, const float *ch, int32_t *idx, float *w,
+                       hipStream_t s);
+hipError_t launch_router_t1(const LayerView &L, const uint16_t *x, float *sc, float *ch, float *logits,
+                            hipStream_t s);
 // What the layer's last kernel does with a result v of out[t][o]: store it
 // (resid = false) or add it to the value already there (out += v, fp32, the
 // residual stream); ob, when set, also receives bf16_RNE of the stored value.
@@ -134,6 +138,14 @@ struct OutEpi {
 hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T,
                           const int32_t *idx, const float *w, float *out, char *ws,
                           const WsLayout &lay, hipStream_t s, Profiler *prof, const OutEpi &epi = OutEpi());
+
+// The one-token layer in three launches (k3moe_decode.hip): route (when
+// `route`; else idx/w are read) + experts + router-order combine into out
+// with the epilogue. decode_fused_ok: the shapes it takes.
+bool decode_fused_ok(const LayerView &L);
+hipError_t launch_decode_fused(const LayerView &L, const uint16_t *x, int32_t *idx, float *w, float *logits,
+                               bool route, float *out, char *ws, const WsLayout &lay, hipStream_t s,
+                               Profiler *prof, const OutEpi &epi = OutEpi());
 
 // Expert slot cache (k3moe_cache.hip). Device counters, in this order:
 enum {

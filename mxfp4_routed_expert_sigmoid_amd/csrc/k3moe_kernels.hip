@@ -34,77 +34,11 @@
 
 #include <type_traits>
 
+#include "k3moe_device.h"
 #include "k3moe_internal.h"
 
 namespace k3moe {
 namespace {
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef unsigned u4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float bf16f(uint32_t h) { return __uint_as_float(h << 16); }
-
-// fp32 -> bf16 bits, round to nearest even (finite values)
-__device__ __forceinline__ uint32_t bf16_rne_u32(float f)
-{
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
-// E8M0 byte -> the fp32 factor 2^(s-127) for the scaled converter; byte 0 is
-// the subnormal 2^-127, byte 255 drops its group (factor 0).
-__device__ __forceinline__ float e8m0_to_f32(uint32_t s)
-{
-    return s == 255u ? 0.0f : __uint_as_float(s == 0u ? 0x00400000u : s << 23);
-}
-
-// 8 fp4 weights (one 32-bit word, low nibble first) -> 8 bf16, scaled exactly.
-__device__ __forceinline__ bf8 dequant8_bf16(uint32_t w, float scale)
-{
-    const bf2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
-    const bf2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
-    const bf2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
-    const bf2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
-    return bf8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
-__device__ __forceinline__ bf8 as_bf8(u4 v)
-{
-    bf8 r;
-    __builtin_memcpy(&r, &v, 16);
-    return r;
-}
-
-__device__ __forceinline__ v4f mfma_bf16_32(const bf8 &a, const bf8 &b, v4f c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ v4f mfma_fp4_fp8(const v8i &a, const v8i &b, v4f c, int sa, int sb)
-{
-    // A format 4 = fp4 (e2m1), B format 0 = fp8 (e4m3); scale bytes in byte 0.
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, sa, 0, sb);
-}
-
-// Same, with the scale bytes taken from byte S of packed scale words.
-template <int S>
-__device__ __forceinline__ v4f mfma_fp4_fp8_sel(const v8i &a, const v8i &b, v4f c, int sa, int sb)
-{
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, S, sa, S, sb);
-}
-
-// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F &&f)
-{
-    if constexpr (B < E) {
-        f(std::integral_constant<int, B>{});
-        static_for<B + 1, E>(f);
-    }
-}
 
 // A lane's scale bytes for 4 consecutive K steps: from the 16 bytes holding
 // K-blocks 4s+g (step s, lane group g) of a row, byte g of each dword.
@@ -127,14 +61,6 @@ __device__ __forceinline__ v8i a_operand(u4 v) { return v8i{(int)v.x, (int)v.y, 
 __device__ __forceinline__ v8i b_operand(u4 lo, u4 hi)
 {
     return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-}
-
-// Gated activation (README §9, k3_situ_glu): SiTU-GLU or SwiGLU, fp32.
-__device__ __forceinline__ float act_fn(float g, float u, int kind, float b1, float b2)
-{
-    const float sg = 1.0f / (1.0f + expf(-g));
-    if (kind == K3MOE_ACT_SITU) return (b1 * tanhf(g / b1) * sg) * (b2 * tanhf(u / b2));
-    return g * sg * u;
 }
 
 // Maximum over the 8 lanes of each aligned lane octet (DPP: swap neighbours,
@@ -338,179 +264,20 @@ __global__ __launch_bounds__(256) void k_router_reduce(const double *__restrict_
     router_finish(acc, t, (int)(i - (int64_t)t * E), E, bias, sc, ch, logits);
 }
 
-// Wave-wide max / min of a uint32 through DPP (row-local steps, then the
-// row broadcasts), read back from lane 63: the same value in every lane.
-template <bool MAX>
-__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v)
-{
-    auto op = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
-    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xb1, 0xf, 0xf, false));   // quad [1,0,3,2]
-    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4e, 0xf, 0xf, false));   // quad [2,3,0,1]
-    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xf, 0xf, false));  // row_half_mirror
-    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xf, 0xf, false));  // row_mirror
-    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast15
-    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast31
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
-}
-
-// Top-k (README §9): the k largest selection scores, in descending order,
-// equal scores by ascending expert index (the order of a repeated strict
-// maximum). One wave per token; lane l holds the selection scores of experts
-// l*NQ .. l*NQ+NQ-1 (a contiguous range, so a lower lane always holds lower
-// expert indices) as order-preserving uint32 keys; NaN ranks as -inf.
-//
-// Threshold and rank: tau = the k-th largest of the 64 lane maxima. k lanes
-// hold a key >= tau, so the k-th largest key is >= tau and every pick is
-// among the candidates {key >= tau}. When there are at most 64 candidates
-// (the usual case: about k of them), they are gathered in LDS, each takes
-// its rank in the order above by comparing against all of them, and the
-// first k ranks are the picks. A candidate is held as one 64-bit word, key in
-// the high half and the complement of its expert index in the low half, so
-// that order is a single unsigned comparison; the 64 slots are prefilled with
-// 0, which no candidate is below. With more candidates (heavy ties) the wave
-// falls back to k rounds of a wave-wide maximum, the lowest lane holding it
-// winning and rescanning its keys.
-//
-// Weights are the unbiased scores of the picks, renormalised in router
-// order, then scaled.
-__device__ __forceinline__ uint32_t order_key(float v)
-{
-    if (v != v) v = -INFINITY;
-    const uint32_t b = __float_as_uint(v);
-    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // > 0 for every float
-}
-
+// Top-k (README §9): one wave per token (topk_wave).
 template <int NQ, bool V4>
 __global__ __launch_bounds__(64) void k_topk(const float *__restrict__ sc, const float *__restrict__ ch,
                                              int E, int K, int renorm, float rscale,
                                              int32_t *__restrict__ idx, float *__restrict__ w)
 {
-    __shared__ uint32_t lmax_l[64];
-    __shared__ uint64_t cc_l[64];  // candidates: key << 32 | ~expert, score
-    __shared__ float cs_l[64];
-    __shared__ int pi_l[kMaxTopk];  // picks in router order: expert, score
-    __shared__ float ps_l[kMaxTopk];
-    const int t = blockIdx.x;
-    const int lane = threadIdx.x;
-    const float *c = ch + (size_t)t * E;
-    const float *sr = sc + (size_t)t * E;
-    const int e0 = lane * NQ;
-    // the selection scores and the scores are loaded together, every load
-    // issued before the first is used (clamped index, no branch); V4 (E a
-    // multiple of 4, rows 16-byte aligned): 16-byte loads, whole or clamped
-    float raw[NQ], sv[NQ];
-    if constexpr (V4) {
-#pragma unroll
-        for (int q = 0; q < NQ; q += 4) {
-            const int b = min(e0 + q, E - 4);
-            const float4 a = *reinterpret_cast<const float4 *>(c + b);
-            const float4 d = *reinterpret_cast<const float4 *>(sr + b);
-            raw[q] = a.x, raw[q + 1] = a.y, raw[q + 2] = a.z, raw[q + 3] = a.w;
-            sv[q] = d.x, sv[q + 1] = d.y, sv[q + 2] = d.z, sv[q + 3] = d.w;
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-            raw[q] = c[min(e0 + q, E - 1)];
-            sv[q] = sr[min(e0 + q, E - 1)];
-        }
-    }
-    uint32_t v[NQ];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) v[q] = e0 + q < E ? order_key(raw[q]) : 0u;  // 0: none / taken
-    uint32_t lm = 0u;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) lm = v[q] > lm ? v[q] : lm;
-
-    // tau: the lane maximum of rank k-1 (ranks 0..63 distinct: equal maxima
-    // by lane)
-    lmax_l[lane] = lm;
-    cc_l[lane] = 0ull;
-    __syncthreads();
-    int rank = 0;
-#pragma unroll 16
-    for (int j = 0; j < 64; ++j) {
-        const uint32_t u = lmax_l[j];
-        rank += (u > lm || (u == lm && j < lane)) ? 1 : 0;
-    }
-    const uint64_t at = __ballot(rank == K - 1);
-    const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)lm, (int)__builtin_ctzll(at));
-
-    // gather the candidates (key >= tau; a key of 0 is no expert)
-    int C = 0;
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        const bool in = v[q] >= tau && v[q] != 0u;
-        const uint64_t m = __ballot(in);
-        const int pos = C + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        if (in && pos < 64) {
-            cc_l[pos] = ((uint64_t)v[q] << 32) | (uint32_t)~(uint32_t)(e0 + q);
-            cs_l[pos] = sv[q];
-        }
-        C += __popcll(m);
-    }
-    __syncthreads();
-
-    int mine = 0;
-    float mine_s = 0.0f;  // score of pick j, held by lane j
-    if (C <= 64) {
-        const uint64_t k0 = cc_l[lane];
-        int r = 0;
-#pragma unroll
-        for (int j = 0; j < 64; ++j) r += cc_l[j] > k0 ? 1 : 0;
-        if (lane < C && r < K) {
-            pi_l[r] = (int)~(uint32_t)k0;
-            ps_l[r] = cs_l[lane];
-        }
-        __syncthreads();
-        if (lane < K) {
-            mine = pi_l[lane];
-            mine_s = ps_l[lane];
-        }
-    } else {
-        uint32_t bk;  // best remaining key of this lane (0: none)
-        int bq;       // its position
-        auto rescan = [&]() {
-            bk = 0u;
-            bq = 0;
-#pragma unroll
-            for (int q = 0; q < NQ; ++q) {
-                const bool gt = v[q] > bk;
-                bk = gt ? v[q] : bk;
-                bq = gt ? q : bq;
-            }
-        };
-        rescan();
-        for (int j = 0; j < K; ++j) {
-            const uint32_t m = wave_reduce_u32<true>(bk);
-            const uint64_t holders = __ballot(bk == m);
-            const int wl = (int)__builtin_ctzll(holders);  // lowest lane holding the maximum
-            const int win = wl * NQ + __builtin_amdgcn_readlane(bq, wl);
-            float ws = 0.0f;
-            if (lane == wl) {
-#pragma unroll
-                for (int q = 0; q < NQ; ++q)
-                    if (q == bq) {
-                        ws = sv[q];
-                        v[q] = 0u;
-                    }
-                rescan();
-            }
-            ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ws), wl));
-            if (lane == j) {
-                mine = win;
-                mine_s = ws;
-            }
-        }
-    }
-    // renormalisation: the sum runs over the picks in router order
-    float s = 0.0f;
-    for (int j = 0; j < K; ++j) s += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine_s), j));
+    __shared__ TopkLds lds;
+    const int t = blockIdx.x, lane = threadIdx.x;
+    int pick;
+    float wt;
+    topk_wave<NQ, V4>(sc + (size_t)t * E, ch + (size_t)t * E, E, K, renorm, rscale, lds, &pick, &wt);
     if (lane < K) {
-        float v0 = mine_s;
-        if (renorm && s > 0.0f) v0 /= s;
-        w[(size_t)t * K + lane] = v0 * rscale;
-        idx[(size_t)t * K + lane] = mine;
+        w[(size_t)t * K + lane] = wt;
+        idx[(size_t)t * K + lane] = pick;
     }
 }
 
@@ -964,8 +731,8 @@ __global__ __launch_bounds__(64 * kGuDecWaves) void k_gateup_dec(GateUpParams p)
 #pragma unroll
                 for (int ss = 0; ss < 4; ++ss) {
                     const bf8 B = as_bf8(*reinterpret_cast<const u4 *>(xb + k * 256 + 16 * ss));
-                    accg = mfma_bf16_32(dequant8_bf16(bf.a[st][0][ss], fg), B, accg);
-                    accu = mfma_bf16_32(dequant8_bf16(bf.a[st][1][ss], fu), B, accu);
+                    accg = mfma_bf16(dequant8_bf16(bf.a[st][0][ss], fg), B, accg);
+                    accu = mfma_bf16(dequant8_bf16(bf.a[st][1][ss], fu), B, accu);
                 }
             }
         });
@@ -1196,7 +963,7 @@ __global__ __launch_bounds__(64 * kDnDecWaves) void k_down_dec(DownDecParams p)
                 const v8i B = b_operand(*reinterpret_cast<const u4 *>(bb + k * 128),
                                         *reinterpret_cast<const u4 *>(bb + k * 128 + 64));
                 const u4 av = ((drop >> (8 * st + 7)) & 1u) ? u4{0u, 0u, 0u, 0u} : bf.a[st];
-                acc = mfma_fp4_fp8_sel<st>(a_operand(av), B, acc, (int)sa, (int)sb);
+                acc = mfma_fp4_fp8<st>(a_operand(av), B, acc, (int)sa, (int)sb);
             }
         });
         if (c == NCH - 1) {
@@ -1411,15 +1178,31 @@ hipError_t launch_route(const LayerView &L, const uint16_t *x, int T, int32_t *i
     }
     {
         StageMark m(prof, K3MOE_STAGE_TOPK, s);
-        const int nq = (L.E + 63) / 64;
-        if (nq <= 1) topk_launch<1>(T, s, sc, ch, L, idx, w);
-        else if (nq <= 2) topk_launch<2>(T, s, sc, ch, L, idx, w);
-        else if (nq <= 4) topk_launch<4>(T, s, sc, ch, L, idx, w);
-        else if (nq <= 8) topk_launch<8>(T, s, sc, ch, L, idx, w);
-        else if (nq <= 16) topk_launch<16>(T, s, sc, ch, L, idx, w);
-        else if (nq <= 32) topk_launch<32>(T, s, sc, ch, L, idx, w);
-        else topk_launch<64>(T, s, sc, ch, L, idx, w);
+        (void)launch_topk(L, T, sc, ch, idx, w, s);
     }
+    return hipGetLastError();
+}
+
+// The router rows of one token (one wave per expert): scores and selection
+// scores into sc, ch; fp32 logits when asked.
+hipError_t launch_router_t1(const LayerView &L, const uint16_t *x, float *sc, float *ch, float *logits,
+                            hipStream_t s)
+{
+    k_router<<<dim3((L.E + 3) / 4, 1), 256, 0, s>>>(x, L.router_w, L.router_bias, L.H, L.E, sc, ch, logits);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const LayerView &L, int T, const float *sc, const float *ch, int32_t *idx, float *w,
+                       hipStream_t s)
+{
+    const int nq = (L.E + 63) / 64;
+    if (nq <= 1) topk_launch<1>(T, s, sc, ch, L, idx, w);
+    else if (nq <= 2) topk_launch<2>(T, s, sc, ch, L, idx, w);
+    else if (nq <= 4) topk_launch<4>(T, s, sc, ch, L, idx, w);
+    else if (nq <= 8) topk_launch<8>(T, s, sc, ch, L, idx, w);
+    else if (nq <= 16) topk_launch<16>(T, s, sc, ch, L, idx, w);
+    else if (nq <= 32) topk_launch<32>(T, s, sc, ch, L, idx, w);
+    else topk_launch<64>(T, s, sc, ch, L, idx, w);
     return hipGetLastError();
 }
 

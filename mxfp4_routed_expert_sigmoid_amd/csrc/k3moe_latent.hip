@@ -6,29 +6,12 @@
 // router-order sum are the flat layer's kernels.
 #include <algorithm>
 
+#include "k3moe_device.h"
 #include "k3moe_internal.h"
 
 namespace k3moe {
 namespace {
 
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef unsigned u4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ float bf16f(uint32_t h) { return __uint_as_float(h << 16); }
-
-__device__ __forceinline__ uint16_t bf16_rne(float f)
-{
-    const uint32_t u = __float_as_uint(f);
-    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
-
-__device__ __forceinline__ bf8 as_bf8(u4 v)
-{
-    bf8 r;
-    __builtin_memcpy(&r, &v, 16);
-    return r;
-}
 
 // ---------------------------------------------------------------------------
 // Projection with bf16 weights W [R][Kd] of NP token planes [T][Kd] (bf16; two

@@ -27,15 +27,11 @@
 // The same launches also run the shared expert for small batches: its blocks
 // come first in the grid (token groups of 16, bf16 weights), so they stream
 // alongside the routed blocks.
+#include "k3moe_device.h"
 #include "k3moe_internal.h"
 
 namespace k3moe {
 namespace {
-
-typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-typedef unsigned u4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSWaves = 4;                 // waves per block
 constexpr int kSRows = 32;                 // weight rows per wave
@@ -43,47 +39,6 @@ constexpr int kSBlkRows = kSWaves * kSRows;
 constexpr int kSTok = 16;                  // tokens per stream item (one B tile)
 constexpr int kSChunks = 4;                // 16-byte weight loads per row per K group
 constexpr int kSPad = 16;                  // LDS padding per token row
-
-__device__ __forceinline__ float bf16f(uint32_t h) { return __uint_as_float(h << 16); }
-
-__device__ __forceinline__ uint16_t bf16_rne(float f)
-{
-    const uint32_t u = __float_as_uint(f);
-    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-}
-
-__device__ __forceinline__ float e8m0_scale(uint32_t s)
-{
-    return s == 255u ? 0.0f : __uint_as_float(s == 0u ? 0x00400000u : s << 23);
-}
-
-__device__ __forceinline__ bf8 dequant8(uint32_t w, float scale)
-{
-    const bf2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
-    const bf2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
-    const bf2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
-    const bf2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
-    return bf8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
-__device__ __forceinline__ bf8 as_bf8(u4 v)
-{
-    bf8 r;
-    __builtin_memcpy(&r, &v, 16);
-    return r;
-}
-
-__device__ __forceinline__ v4f mfma_bf16(const bf8 &a, const bf8 &b, v4f c)
-{
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ float act_fn(float g, float u, int kind, float b1, float b2)
-{
-    const float sg = 1.0f / (1.0f + expf(-g));
-    if (kind == K3MOE_ACT_SITU) return (b1 * tanhf(g / b1) * sg) * (b2 * tanhf(u / b2));
-    return g * sg * u;
-}
 
 // An item's LDS header: per column c < 16 its token (key), the row its
 // operand comes from (val), its output row (out), its staged row (cmap); per
@@ -236,7 +191,7 @@ __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const u
 #pragma unroll
                 for (int m = 0; m < 2; ++m)
 #pragma unroll
-                    for (int rf = 0; rf < 2; ++rf) sc[m][rf] = e8m0_scale((b.s[m][rf][c] >> (8 * g)) & 0xffu);
+                    for (int rf = 0; rf < 2; ++rf) sc[m][rf] = e8m0_to_f32((b.s[m][rf][c] >> (8 * g)) & 0xffu);
             }
             constexpr int SPC = FP4 ? 4 : 1;  // MFMA steps per 16-byte load
 #pragma unroll
@@ -252,7 +207,7 @@ __device__ __forceinline__ void gu_stream_block(const GuStreamParams &p, const u
                     for (int rf = 0; rf < 2; ++rf) {
                         bf8 a;
                         if constexpr (FP4)
-                            a = dequant8(b.a[m][rf][c][st], sc[m][rf]);
+                            a = dequant8_bf16(b.a[m][rf][c][st], sc[m][rf]);
                         else
                             a = as_bf8(b.a[m][rf][c]);
 #pragma unroll
@@ -484,7 +439,7 @@ __device__ __forceinline__ void dn_stream_run(const DnStreamParams &p, const uin
             float sc[2];
             if constexpr (FP4) {
 #pragma unroll
-                for (int rf = 0; rf < 2; ++rf) sc[rf] = e8m0_scale((b.s[rf][c] >> (8 * g)) & 0xffu);
+                for (int rf = 0; rf < 2; ++rf) sc[rf] = e8m0_to_f32((b.s[rf][c] >> (8 * g)) & 0xffu);
             }
             constexpr int SPC = FP4 ? 4 : 1;
 #pragma unroll
@@ -496,7 +451,7 @@ __device__ __forceinline__ void dn_stream_run(const DnStreamParams &p, const uin
                 for (int rf = 0; rf < 2; ++rf) {
                     bf8 a;
                     if constexpr (FP4)
-                        a = dequant8(b.a[rf][c][st], sc[rf]);
+                        a = dequant8_bf16(b.a[rf][c][st], sc[rf]);
                     else
                         a = as_bf8(b.a[rf][c]);
                     acc[rf] = mfma_bf16(a, bh, acc[rf]);

@@ -105,3 +105,59 @@ def test_latent_weight_refusals():
     w3 = _weights(8)
     w3.lat_down, w3.lat_up, w3.lat_norm = base, base + 0x100000, base + 0x200000
     assert _create(nonorm, w3) == 1                   # gamma without the norm
+
+
+def test_stage_list_matches_header():
+    src = open(os.path.join(ROOT, "include", "k3moe.h")).read()
+    n = int(re.search(r"K3MOE_N_STAGES\s*=\s*(\d+)", src).group(1))
+    names = re.findall(r"K3MOE_STAGE_([A-Z_]+)\s*=\s*(\d+)", src)
+    assert len(k3.STAGES) == n == len(names)
+    for name, i in names:
+        assert k3.STAGES[int(i)] == name.lower()
+    abi = int(re.search(r"#define K3MOE_ABI_VERSION (\d+)u", src).group(1))
+    assert k3.ABI_VERSION == abi
+
+
+# ---------------------------------------------------------------------------
+# The binding refuses mis-shaped tensors before any library call (the C ABI
+# takes raw pointers, so a wrong shape would become an out-of-bounds device
+# access). These run on the CPU: the shape checks come before the device
+# checks, and nothing reaches the library.
+
+def _fake_layer(hidden=256, inter=128, n_experts=8, topk=2):
+    import torch
+    L = k3.Layer.__new__(k3.Layer)
+    L.cfg = k3.make_config(hidden, inter, n_experts, topk)
+    L.device = torch.device("cpu")
+    L.handle = None
+    return L
+
+
+@pytest.mark.parametrize("call", ["route", "forward", "route_forward", "forward_noalloc",
+                                  "forward_residual", "step"])
+def test_binding_refuses_mis_shaped_tensors(call):
+    import torch
+    L = _fake_layer()
+    T, H, K, E = 3, 256, 2, 8
+    good = dict(x=torch.zeros(T, H, dtype=torch.int16), idx=torch.zeros(T, K, dtype=torch.int32),
+                w=torch.zeros(T, K), out=torch.zeros(T, H), h=torch.zeros(T, H),
+                gamma=torch.zeros(H), logits=torch.zeros(T, E))
+    bad = {"x": torch.zeros(T, H + 128, dtype=torch.int16), "idx": torch.zeros(T, K + 1, dtype=torch.int32),
+           "w": torch.zeros(T + 1, K), "out": torch.zeros(T, H - 128), "h": torch.zeros(T, 2 * H),
+           "gamma": torch.zeros(H + 1), "logits": torch.zeros(T, E + 1)}
+    args = {"route": ("x", "idx", "w"), "forward": ("x", "idx", "w", "out"),
+            "route_forward": ("x", "idx", "w", "out"), "forward_noalloc": ("x", "idx", "w", "out"),
+            "forward_residual": ("x", "idx", "w", "h"), "step": ("h", "gamma", None, "idx", "w")}[call]
+    for wrong in [a for a in args if a]:
+        vals = []
+        for a in args:
+            if a is None:
+                vals.append(1e-5)  # step's eps
+            else:
+                vals.append(bad[a] if a == wrong else good[a])
+        with pytest.raises(ValueError, match="shape"):
+            getattr(L, call)(*vals)
+    if call in ("route", "route_forward"):
+        vals = [good[a] for a in args]
+        with pytest.raises(ValueError, match="logits"):
+            getattr(L, call)(*vals, logits=bad["logits"])
