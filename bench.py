@@ -258,12 +258,21 @@ def main():
     # or step): router | shared gate/up + top-k + routed gate/up | shared
     # down + routed down + router-order sum (no separate combine)
     fused = "combine" not in stage_us and not Lt and T == 1 and cache is None
+    # flat layers at 2..4 tokens run the single-token kernels once per token
+    per_token = not fused and not Lt and T <= 4 and cache is None
     if fused:
         terms = K * 4 * I + K * 4 * (I // 32)   # the activations as e4m3 terms and their scales
         stage_bytes = {
             "router": router_bytes + H * 2 + E * 8,
             "gateup": nd * 2 * gu + 2 * Is * H * 2 + H * 2 + E * 8 + terms + Is * 4 + K * 8,
             "down": nd * dn + Is * H * 2 + terms + Is * 4 + K * 8 + H * 4 * (2 if args.workload in ("step", "stack") else 1),
+        }
+    elif per_token:
+        # a few tokens (2..4) on the single-token kernels, one pass per token:
+        # each pass reads its token's experts and the shared expert again
+        stage_bytes = {
+            "gateup": T * (K * 2 * gu + 2 * Is * H * 2 + H * 2 + K * I * 4 + Is * 4),
+            "down": T * (K * dn + Is * H * 2 + K * I * 4 + Is * 4 + (K + 1) * H * 4),
         }
     else:
         shared_in_gateup = "shared_gateup" not in stage_us  # no separate shared gate/up launch
@@ -278,19 +287,23 @@ def main():
     if Lt:
         stage_bytes["latent_in"] = Lt * H * 2 + T * H * 2 + T * Lt * 4
         stage_bytes["latent_out"] = H * Lt * 2 + Lt * 4 + T * Lt * 12 + T * H * 8
+    one_tok = {"gateup": "k_gateup_dec", "down": "k_down_dec"}   # the per-token loop's kernels
     kernels = {"decode": ({"router": "k_router", "gateup": "k_dec_gateup", "down": "k_dec_down"} if fused
-                          else {"gateup": "k_gateup_dec", "down": "k_down_dec"}),
-               "batched": {"gateup": "k_gu_stream", "down": "k_dn_stream"},
+                          else one_tok),
+               "batched": one_tok if per_token else {"gateup": "k_gu_stream", "down": "k_dn_stream"},
                "prefill": {"gateup": "k_gu_gemm + k_gu_stream", "down": "k_dn_gemm + k_dn_stream"},
                "latent": ({"gateup": "k_gateup_dec", "down": "k_down_dec", "latent_in": "k_gv_down",
                            "latent_out": "k_gv_up"} if T == 1 else
                           {"gateup": "k_gu_stream", "down": "k_dn_stream", "latent_in": "k_proj",
                            "latent_out": "k_proj + k_rms_split"}),
-               "step": {"router": "k_router", "gateup": "k_dec_gateup", "down": "k_dec_down",
-                        "prenorm": "k_prenorm"},
+               "step": ({"router": "k_router", "gateup": "k_dec_gateup", "down": "k_dec_down",
+                         "prenorm": "k_prenorm"} if T == 1
+                        else dict(one_tok, prenorm="k_prenorm") if per_token
+                        else {"gateup": "k_gu_stream", "down": "k_dn_stream", "prenorm": "k_prenorm"}),
                "cache": {"cache_fill": "k_cache_fill"},
                "stack": ({"router": "k_router", "gateup": "k_dec_gateup", "down": "k_dec_down",
                           "prenorm": "k_prenorm"} if T == 1
+                         else dict(one_tok, prenorm="k_prenorm") if per_token
                          else {"gateup": "k_gu_stream", "down": "k_dn_stream", "prenorm": "k_prenorm"})}[args.workload]
     # the hot experts' tile GEMMs: algorithmic flops (2 per multiply-add,
     # gate and up, per assignment) and issued flops (whole token tiles; the

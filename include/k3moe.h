@@ -139,7 +139,16 @@ typedef struct k3moe_layer k3moe_layer;
 /* Validate the config and weight descriptors and make a layer handle on the
  * current HIP device. The handle references the weights (it never copies or
  * repacks them) and owns one 8-byte device error counter. Checks that the
- * device has room for that counter before allocating. */
+ * device has room for that counter plus a 1 MiB margin before allocating
+ * (K3MOE_E_OUT_OF_MEMORY otherwise).
+ *
+ * Free device memory, here and in k3moe_cache_create, is hipMemGetInfo's
+ * free bytes capped by the environment variable K3MOE_HBM_BUDGET (decimal
+ * bytes) when it is set and non-empty: a process can hold the library to a
+ * share of the device. A value that is not a plain decimal number (digits
+ * only, below 2^64) gives K3MOE_E_INVALID_ARG. The kimi-k3-in-c README
+ * (§11, streaming the trunk) adds up every allocation before making any;
+ * both create calls do. */
 k3moe_status k3moe_layer_create(const k3moe_config *cfg, const k3moe_weights *w,
                                 k3moe_layer **out);
 
@@ -321,9 +330,18 @@ typedef struct {
  * expert's six tensors, each 256-byte aligned) and the slot table; every
  * slot starts empty. The layer must outlive the cache. Returns
  * K3MOE_E_INVALID_ARG if an expert tensor is in host memory the device
- * cannot read (pageable memory), K3MOE_E_OUT_OF_MEMORY if the arena does
- * not fit. */
+ * cannot read (pageable memory), K3MOE_E_OUT_OF_MEMORY if the arena and
+ * table (k3moe_cache_device_bytes) plus 1 MiB exceed the free device memory
+ * (capped by K3MOE_HBM_BUDGET, see k3moe_layer_create); nothing is
+ * allocated then. */
 k3moe_status k3moe_cache_create(const k3moe_layer *layer, int32_t n_slots, k3moe_cache **out);
+
+/* Device bytes k3moe_cache_create allocates for a layer of this config and
+ * n_slots slots (the arena and the slot table), from the config alone (no
+ * device call): what to budget before creating the cache. The create call
+ * also keeps a 1 MiB margin free. Returns the config's refusal, or
+ * K3MOE_E_INVALID_ARG for n_slots outside [1, n_experts]. */
+k3moe_status k3moe_cache_device_bytes(const k3moe_config *cfg, int32_t n_slots, size_t *bytes);
 
 /* Workspace bytes of k3moe_cache_forward for up to max_tokens tokens (also
  * enough for k3moe_route and k3moe_forward of the cache's layer). */

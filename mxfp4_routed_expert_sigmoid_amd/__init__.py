@@ -61,8 +61,9 @@ class CacheStats(ctypes.Structure):
 
 _lib = None
 EXPORTS = ("k3moe_layer_create", "k3moe_workspace_size", "k3moe_route", "k3moe_forward",
-           "k3moe_route_forward", "k3moe_forward_noalloc", "k3moe_forward_residual", "k3moe_step", "k3moe_cache_create", "k3moe_cache_workspace_size", "k3moe_cache_forward",
-           "k3moe_cache_stats_read", "k3moe_cache_slots", "k3moe_cache_reset", "k3moe_cache_destroy",
+           "k3moe_route_forward", "k3moe_forward_noalloc", "k3moe_forward_residual", "k3moe_step",
+           "k3moe_cache_create", "k3moe_cache_device_bytes", "k3moe_cache_workspace_size",
+           "k3moe_cache_forward", "k3moe_cache_stats_read", "k3moe_cache_slots", "k3moe_cache_reset", "k3moe_cache_destroy",
            "k3moe_error_count", "k3moe_error_reset", "k3moe_profile_enable",
            "k3moe_profile_read", "k3moe_layer_destroy", "k3moe_status_string")
 STAGES = ("router", "topk", "perm", "gateup", "shared_gateup", "down", "combine",
@@ -96,6 +97,8 @@ def lib():
         L.k3moe_step.argtypes = [P, P, i32, P, ctypes.c_float, P, P, P, P, P, ctypes.c_size_t, P]
         L.k3moe_cache_create.restype = st
         L.k3moe_cache_create.argtypes = [P, i32, ctypes.POINTER(P)]
+        L.k3moe_cache_device_bytes.restype = st
+        L.k3moe_cache_device_bytes.argtypes = [P, i32, ctypes.POINTER(ctypes.c_size_t)]
         L.k3moe_cache_workspace_size.restype = st
         L.k3moe_cache_workspace_size.argtypes = [P, i32, ctypes.POINTER(ctypes.c_size_t)]
         L.k3moe_cache_forward.restype = st
@@ -360,6 +363,15 @@ class Layer:
     def error_reset(self, stream=None):
         _check(lib().k3moe_error_reset(self.handle, _stream(stream, self.device)),
                "k3moe_error_reset")
+
+
+def cache_device_bytes(cfg: Config, n_slots: int) -> int:
+    """Device bytes a cache of n_slots slots allocates for a layer of this
+    config (k3moe_cache_device_bytes; no device call)."""
+    n = ctypes.c_size_t()
+    _check(lib().k3moe_cache_device_bytes(ctypes.byref(cfg), int(n_slots), ctypes.byref(n)),
+           "k3moe_cache_device_bytes")
+    return n.value
 
 
 class Cache:

@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <mutex>
 #include <new>
 
@@ -231,6 +232,63 @@ static bool batch_fits(const k3moe_config &c, int64_t T)
     return T * c.hidden * 2 < lim && T * c.topk * I * 2 < lim;
 }
 
+// Free HBM as the library plans against it: hipMemGetInfo's free bytes,
+// capped by K3MOE_HBM_BUDGET (decimal bytes) when that is set, so a process
+// can keep the library inside a share of the device (and a test can stand in
+// a shortfall). An unparsable value is refused.
+static k3moe_status free_hbm(size_t *free_b)
+{
+    size_t total_b = 0;
+    if (hipMemGetInfo(free_b, &total_b) != hipSuccess) return K3MOE_E_HIP;
+    const char *env = std::getenv("K3MOE_HBM_BUDGET");
+    if (env && *env) {
+        // digits only (no sign, space or exponent), at most 2^64 - 1
+        unsigned long long v = 0;
+        for (const char *c = env; *c; ++c) {
+            if (*c < '0' || *c > '9') return K3MOE_E_INVALID_ARG;
+            const unsigned d = (unsigned)(*c - '0');
+            if (v > (~0ull - d) / 10) return K3MOE_E_INVALID_ARG;
+            v = v * 10 + d;
+        }
+        if (v < *free_b) *free_b = (size_t)v;
+    }
+    return K3MOE_OK;
+}
+
+// Device bytes a layer handle allocates (the error counter), and the margin
+// every create call keeps free beyond its own allocations.
+constexpr size_t kLayerDeviceBytes = sizeof(unsigned long long);
+constexpr size_t kCreateMarginBytes = (size_t)1 << 20;
+
+// The cache's device allocations, from the layer's config alone: per slot
+// the expert's six tensors (gate, up, down; packed then scales), each
+// 256-byte aligned, in that order; the table holds the counters, the expert
+// -> slot map and the per-slot key and last use.
+struct CachePlan {
+    int64_t seg_len[6], seg_off[6];
+    int64_t slot_bytes, expert_bytes;
+    size_t arena, table;
+};
+
+static CachePlan cache_plan(const k3moe_config &c, int32_t n_slots)
+{
+    CachePlan p{};
+    const int64_t EK = c.latent ? c.latent : c.hidden;
+    const int64_t elems = (int64_t)c.inter * EK;  // every expert matrix has I * EK weights
+    int64_t off = 0;
+    for (int i = 0; i < 6; ++i) {
+        p.seg_len[i] = (i & 1) ? elems / 32 : elems / 2;
+        p.seg_off[i] = off;
+        off = (int64_t)align256((size_t)(off + p.seg_len[i]));
+        p.expert_bytes += p.seg_len[i];
+    }
+    p.slot_bytes = off;
+    p.arena = (size_t)p.slot_bytes * (size_t)n_slots;
+    p.table = align256(sizeof(unsigned long long) * kCtrCount) + align256(sizeof(int32_t) * c.n_experts) +
+              align256(sizeof(int32_t) * n_slots) + align256(sizeof(long long) * n_slots);
+    return p;
+}
+
 // Common checks of a route/forward call; T == 0 is reported as "nothing to do".
 static k3moe_status check_call(const k3moe_layer *l, int32_t T, void *ws, size_t ws_bytes,
                                bool *nothing)
@@ -332,9 +390,9 @@ k3moe_status k3moe_layer_create(const k3moe_config *cfg, const k3moe_weights *w,
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess) return K3MOE_E_HIP;
     if ((s = resolve_scratch(dev)) != K3MOE_OK) return s;  // this device's k3moe_forward_noalloc scratch
-    size_t free_b = 0, total_b = 0;
-    if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) return K3MOE_E_HIP;
-    if (free_b < (size_t)1 << 20) return K3MOE_E_OUT_OF_MEMORY;
+    size_t free_b = 0;
+    if ((s = free_hbm(&free_b)) != K3MOE_OK) return s;
+    if (free_b < kLayerDeviceBytes + kCreateMarginBytes) return K3MOE_E_OUT_OF_MEMORY;
     k3moe_layer *l = new (std::nothrow) k3moe_layer;
     if (!l) return K3MOE_E_OUT_OF_MEMORY;
     l->cfg = *cfg;
@@ -563,14 +621,13 @@ k3moe_status k3moe_cache_create(const k3moe_layer *l, int32_t n_slots, k3moe_cac
     if (hipGetDevice(&dev) != hipSuccess) return K3MOE_E_HIP;
     if (dev != l->device) return K3MOE_E_INVALID_ARG;
     const k3moe_config &c = l->cfg;
-    const int64_t I = c.inter, EK = c.latent ? c.latent : c.hidden, E = c.n_experts;
+    const int64_t E = c.n_experts;
     const k3moe_mxfp4 *m[3] = {&l->w.gate, &l->w.up, &l->w.down};
-    const int64_t elems = I * EK;  // every expert matrix has I * EK weights
+    const CachePlan plan = cache_plan(c, n_slots);
     k3moe_cache tmp{};
     tmp.layer = l;
     tmp.S = n_slots;
     tmp.device = dev;
-    int64_t off = 0;
     for (int i = 0; i < 6; ++i) {
         const void *p = (i & 1) ? (const void *)m[i / 2]->scales : (const void *)m[i / 2]->packed;
         hipPointerAttribute_t a{};
@@ -590,18 +647,17 @@ k3moe_status k3moe_cache_create(const k3moe_layer *l, int32_t n_slots, k3moe_cac
         if (!dp || !aligned(dp, 16)) return K3MOE_E_INVALID_ARG;
         tmp.src[i] = static_cast<const uint8_t *>(dp);
         tmp.src_stride[i] = (i & 1) ? m[i / 2]->expert_stride_scales : m[i / 2]->expert_stride_packed;
-        tmp.seg_len[i] = (i & 1) ? elems / 32 : elems / 2;
-        tmp.seg_off[i] = off;
-        off = (int64_t)align256((size_t)(off + tmp.seg_len[i]));
+        tmp.seg_len[i] = plan.seg_len[i];
+        tmp.seg_off[i] = plan.seg_off[i];
     }
-    tmp.slot_bytes = off;
-    tmp.expert_bytes = 0;
-    for (int i = 0; i < 6; ++i) tmp.expert_bytes += tmp.seg_len[i];
-    const size_t table = align256(sizeof(unsigned long long) * kCtrCount) + align256(sizeof(int32_t) * E) +
-                         align256(sizeof(int32_t) * n_slots) + align256(sizeof(long long) * n_slots);
-    size_t free_b = 0, total_b = 0;
-    if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) return K3MOE_E_HIP;
-    if ((size_t)tmp.slot_bytes * n_slots + table + ((size_t)1 << 20) > free_b) return K3MOE_E_OUT_OF_MEMORY;
+    tmp.slot_bytes = plan.slot_bytes;
+    tmp.expert_bytes = plan.expert_bytes;
+    const size_t table = plan.table;
+    // everything the cache allocates is added up before anything is allocated
+    size_t free_b = 0;
+    const k3moe_status fs = free_hbm(&free_b);
+    if (fs != K3MOE_OK) return fs;
+    if (plan.arena + table + kCreateMarginBytes > free_b) return K3MOE_E_OUT_OF_MEMORY;
     k3moe_cache *cc = new (std::nothrow) k3moe_cache(tmp);
     if (!cc) return K3MOE_E_OUT_OF_MEMORY;
     if (hipMalloc(&cc->arena, (size_t)cc->slot_bytes * n_slots) != hipSuccess) {
@@ -629,6 +685,17 @@ k3moe_status k3moe_cache_create(const k3moe_layer *l, int32_t n_slots, k3moe_cac
         return K3MOE_E_HIP;
     }
     *out = cc;
+    return K3MOE_OK;
+}
+
+k3moe_status k3moe_cache_device_bytes(const k3moe_config *cfg, int32_t n_slots, size_t *bytes)
+{
+    if (!bytes) return K3MOE_E_INVALID_ARG;
+    const k3moe_status s = check_config(cfg);
+    if (s != K3MOE_OK) return s;
+    if (n_slots < 1 || n_slots > cfg->n_experts) return K3MOE_E_INVALID_ARG;
+    const CachePlan p = cache_plan(*cfg, n_slots);
+    *bytes = p.arena + p.table;
     return K3MOE_OK;
 }
 

@@ -14,7 +14,7 @@ LIB = os.path.join(HERE, "libk3oracle.so")
 
 def build(verbose: bool = False) -> str:
     cmd = ["gcc", "-std=c99", "-O2", "-fPIC", "-shared", "-fopenmp",
-           "-ffp-contract=off", "-Wall", "-Wextra", "-o", LIB, SRC, "-lm"]
+           "-ffp-contract=off", "-fno-semantic-interposition", "-Wall", "-Wextra", "-o", LIB, SRC, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

@@ -54,13 +54,15 @@
 #define K3O_ACT_SWIGLU 2
 
 /* E2M1 code -> value. Bit 3 is the sign; the 3 low bits index the eight
- * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (§4, the 16-entry table). Code 8 is -0. */
-double k3o_e2m1(int code)
-{
-    static const double magnitude[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
-    const double v = magnitude[code & 7];
-    return (code & 8) ? -v : v;
-}
+ * magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (§4, the 16-entry table). Code 8 is
+ * -0. Written out as the 16 signed values so the decode has no branch on the
+ * (random) sign bit. */
+static const double e2m1_value[16] = {
+    0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+    -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0,
+};
+
+double k3o_e2m1(int code) { return e2m1_value[code & 15]; }
 
 /* E8M0 byte -> 2^(b - 127); byte 255 (NaN in the MX specification) maps to 0
  * so its whole 32-group contributes nothing (§4). Byte 0 is 2^-127. */

@@ -55,17 +55,84 @@ def rel_err(out_gpu, out_ref, denom):
     return float((err / d).max())
 
 
-def oracle_forward(spec, x, idx, w, layer=0, tokens=None):
-    """Oracle output/denominators for the listed tokens (all by default)."""
+# attempt numbers of redrawn tokens: row t, redraw a -> _REDRAW + t * 64 + a
+_REDRAW = 1 << 24
+_REDRAW_MAX = 64
+
+
+def certify_rows(spec, x, Wr, bias, rows=None, layer=0):
+    """Redraw, in place, every listed token of x (bf16 patterns [T][H]) whose
+    oracle route is not certified: row t takes the single token
+    synth.make_x(spec, 1, layer, attempt=_REDRAW + 64 t + a) for the next a
+    until its route is. Returns the oracle's (idx, w, logits, ch) of the
+    listed rows (all rows by default), every one certified, so the GPU's ids
+    must equal the oracle's exactly on them."""
+    rows = np.arange(x.shape[0]) if rows is None else np.asarray(rows)
+    kw = dict(renorm=spec.renorm, routed_scale=spec.routed_scale, want_detail=True)
+    res = list(oracle.route(x[rows], Wr, bias, spec.topk, **kw))
+    for a in range(_REDRAW_MAX):
+        bad = np.nonzero(~route_certificate(res[3], spec.topk))[0]
+        if bad.size == 0:
+            return tuple(res)
+        for i in bad:
+            t = int(rows[i])
+            x[t] = synth.make_x(spec, 1, layer=layer, attempt=_REDRAW + t * _REDRAW_MAX + a)[0]
+        for arr, new in zip(res, oracle.route(x[rows[bad]], Wr, bias, spec.topk, **kw)):
+            arr[bad] = new
+    raise AssertionError("a token stayed uncertified")
+
+
+def tile_edge_tokens(idx, n_experts, smax, tile_sizes, experts=None):
+    """Tokens on the edges of the grouped-GEMM tiles. The permutation lists an
+    expert's assignments in token order; an expert with more than smax of
+    them runs on tiles of each listed size. For each such expert (or each
+    listed one): the tokens in the first and last row of its first tile, the
+    first row of its second tile, and the first and last row of its last
+    (possibly partial) tile."""
+    out = set()
+    for e in (range(n_experts) if experts is None else experts):
+        toks = np.nonzero((idx == e).any(1))[0]
+        n = toks.size
+        if n <= smax:
+            continue
+        for ts in tile_sizes:
+            rows = {0, min(ts, n) - 1, ts * ((n - 1) // ts), n - 1}
+            if n > ts:
+                rows.add(ts)
+            out.update(int(toks[r]) for r in rows)
+    return sorted(out)
+
+
+_SHARED = {}
+
+
+def _shared(spec, layer):
+    """synth.make_shared, kept for the last few (spec, layer) pairs."""
+    key = (repr(spec), layer)
+    if key not in _SHARED:
+        if len(_SHARED) >= 4:
+            _SHARED.pop(next(iter(_SHARED)))
+        _SHARED[key] = synth.make_shared(spec, layer)
+    return _SHARED[key]
+
+
+def oracle_forward(spec, x, idx, w, layer=0, tokens=None, chunk=48):
+    """Oracle output/denominators for the listed tokens (all by default), in
+    chunks of tokens (the host copies of one chunk's experts at a time)."""
     if tokens is None:
         tokens = np.arange(x.shape[0])
     tokens = np.asarray(tokens)
+    if tokens.size > chunk:
+        parts = [oracle_forward(spec, x, idx, w, layer, tokens[i:i + chunk], chunk)
+                 for i in range(0, tokens.size, chunk)]
+        return (np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]),
+                sum(p[2] for p in parts))
     xs, ids, ws = x[tokens], idx[tokens], w[tokens]
     used = sorted({int(e) for e in ids.ravel() if 0 <= e < spec.n_experts})
     h = synth.expert_host(spec, used, layer)
     es = oracle.ExpertSet(used, spec.n_experts, h["gate_packed"], h["gate_scales"],
                           h["up_packed"], h["up_scales"], h["down_packed"], h["down_scales"])
-    shared = synth.make_shared(spec, layer)
+    shared = _shared(spec, layer)
     if spec.latent:
         wd, wu, gamma = synth.make_latent(spec, layer)
         return oracle.forward_latent(xs, ids, ws, es, spec.hidden, spec.latent, spec.inter, wd, wu,

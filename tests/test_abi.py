@@ -161,3 +161,30 @@ def test_binding_refuses_mis_shaped_tensors(call):
         vals = [good[a] for a in args]
         with pytest.raises(ValueError, match="logits"):
             getattr(L, call)(*vals, logits=bad["logits"])
+
+
+def test_cache_device_bytes_plan_on_the_host():
+    # the cache's device allocations from the config alone (no device call):
+    # the arena is n_slots slots of the expert's six tensors, each padded to
+    # 256 bytes; the slot table adds a little per expert and per slot
+    import mxfp4_routed_expert_sigmoid_amd as k3
+    cfg = k3.make_config(7168, 1536, 896, 16, 1536)
+    slot = 3 * (1536 * 7168 // 2 + 1536 * 7168 // 32)
+    assert slot == 17547264
+    for S in (1, 24, 224, 896):
+        n = k3.cache_device_bytes(cfg, S)
+        assert S * slot < n <= S * slot + 256 + 4 * 896 + 12 * S + 3 * 256
+    # padding: hidden 384, inter 128 -> packed 24,576 B (aligned), scales 1,536 B (aligned);
+    # latent 256, inter 384 -> scales 3,072 B; inter 128, hidden 128 -> scales 512 B
+    cfg2 = k3.make_config(128, 128, 4, 2, 0)
+    one = k3.cache_device_bytes(cfg2, 1)
+    two = k3.cache_device_bytes(cfg2, 2)
+    per = 3 * (8192 + 512)
+    assert per <= two - one <= per + 3 * 256
+    for bad in (0, -1, 5):
+        with pytest.raises(k3.K3MoeError) as ei:
+            k3.cache_device_bytes(cfg2, bad)
+        assert ei.value.status == 1
+    with pytest.raises(k3.K3MoeError) as ei:
+        k3.cache_device_bytes(k3.make_config(100, 128, 4, 2, 0), 1)   # hidden not a multiple of 128
+    assert ei.value.status == 3

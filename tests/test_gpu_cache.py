@@ -7,13 +7,17 @@ Bars (integer work bit-exact, the expert arithmetic unchanged):
   - the output is bit-identical to k3moe_forward of the same layer with its
     experts resident in HBM, on the same routes with every assignment the
     model drops replaced by an out-of-range id (which contributes nothing);
+  - the output is within the layer's error bound of the fp64 oracle's on
+    those routes (every call, every token);
   - dropped assignments are counted by the layer's error counter.
-Every input is seeded and synthetic."""
+Every input is seeded and synthetic; expected values come only from
+``oracle``."""
 import numpy as np
 import pytest
 import torch
 
 import synth
+from gpu_helpers import REL_TOL, oracle_forward, rel_err
 from oracle.cache_policy import SlotCache
 
 pytestmark = pytest.mark.gpu
@@ -54,7 +58,8 @@ def _routes(rng, spec, T):
 def _call(spec, cache, model, resident, host, T, rng, attempt):
     import synth.device as sd
     idx, w = _routes(rng, spec, T)
-    x = sd.bf16_tensor(synth.make_x(spec, T, attempt=attempt), DEV)
+    x_np = synth.make_x(spec, T, attempt=attempt)
+    x = sd.bf16_tensor(x_np, DEV)
     idx_d, w_d = torch.from_numpy(idx).to(DEV), torch.from_numpy(w).to(DEV)
     err0 = host.error_count()
     out_c = torch.empty((T, spec.hidden), dtype=torch.float32, device=DEV)
@@ -70,6 +75,9 @@ def _call(spec, cache, model, resident, host, T, rng, attempt):
     resident.forward(x, torch.from_numpy(idx_ref).to(DEV), w_d, out_r)
     torch.cuda.synchronize()
     assert np.array_equal(out_c.cpu().numpy(), out_r.cpu().numpy())
+    ref, denom, drops = oracle_forward(spec, x_np, idx_ref, w)
+    assert drops == int(dropped.sum())
+    assert rel_err(out_c.cpu().numpy(), ref, denom) <= REL_TOL
     assert host.error_count() - err0 == int(dropped.sum())
     assert resident.error_count() - err1 == int(dropped.sum())
     return reads, int(dropped.sum())

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import REL_TOL, check_route, oracle_forward, rel_err
+from gpu_helpers import REL_TOL, certify_rows, check_route, oracle_forward, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -29,14 +29,13 @@ def _run(spec, layer, T, tokens=None):
     import synth.device as sd
     x_np = synth.make_x(spec, T)
     Wr, bias = synth.make_router(spec), synth.make_bias(spec)
-    idx_r, w_r, _, ch = oracle.route(x_np, Wr, bias, spec.topk, renorm=spec.renorm,
-                                     routed_scale=spec.routed_scale, want_detail=True)
+    idx_r, w_r, _, ch = certify_rows(spec, x_np, Wr, bias)
     x = sd.bf16_tensor(x_np, DEV)
     idx = torch.empty((T, spec.topk), dtype=torch.int32, device=DEV)
     w = torch.empty((T, spec.topk), dtype=torch.float32, device=DEV)
     layer.route(x, idx, w)
     torch.cuda.synchronize()
-    check_route(idx.cpu().numpy(), w.cpu().numpy(), idx_r, w_r, ch, spec.topk)
+    assert check_route(idx.cpu().numpy(), w.cpu().numpy(), idx_r, w_r, ch, spec.topk) == T
     out = torch.empty((T, spec.hidden), dtype=torch.float32, device=DEV)
     layer.forward(x, torch.from_numpy(idx_r).to(DEV), torch.from_numpy(w_r).to(DEV), out)
     torch.cuda.synchronize()
@@ -47,7 +46,7 @@ def _run(spec, layer, T, tokens=None):
     err = rel_err(o[tokens], ref, denom)
     print(f"[latent] T={T} max rel err {err:.3g}", flush=True)
     assert err <= REL_TOL
-    return o
+    return o, x_np, idx_r, w_r
 
 
 @pytest.mark.parametrize("T", [1, 2, 5, 17, 40, 129])
@@ -75,13 +74,11 @@ def test_mid_latent_stream_and_gemm(T, routing):
     spec = synth.LayerSpec(hidden=1024, inter=512, n_experts=16, topk=4, shared_inter=512,
                            bias_std=0.05, routing=routing, seed=100 + T, latent=512)
     _, layer = _layer(spec)
-    o = _run(spec, layer, T)
+    o, x_np, idx_r, w_r = _run(spec, layer, T)
     if T >= 129:
         # deterministic: a second call gives the same bits
         import synth.device as sd
-        x = sd.bf16_tensor(synth.make_x(spec, T), DEV)
-        idx_r, w_r = oracle.route(synth.make_x(spec, T), synth.make_router(spec), synth.make_bias(spec),
-                                  spec.topk)
+        x = sd.bf16_tensor(x_np, DEV)
         out = torch.empty((T, spec.hidden), dtype=torch.float32, device=DEV)
         layer.forward(x, torch.from_numpy(idx_r).to(DEV), torch.from_numpy(w_r).to(DEV), out)
         torch.cuda.synchronize()
@@ -106,9 +103,9 @@ def test_pages_latent_decode_T1():
     _run(spec, layer, 1)
 
 
-def test_pages_latent_T64_sampled():
+def test_pages_latent_T64_all_tokens():
     spec, _, layer = _pages()
-    _run(spec, layer, 64, tokens=[0, 21, 63])
+    _run(spec, layer, 64)
 
 
 def test_pages_latent_release():

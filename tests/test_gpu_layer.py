@@ -8,7 +8,8 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import REL_TOL, check_route, oracle_forward, rel_err, route_certificate
+from gpu_helpers import (REL_TOL, certify_rows, check_route, oracle_forward, rel_err, route_certificate,
+                         tile_edge_tokens)
 
 pytestmark = pytest.mark.gpu
 
@@ -362,7 +363,7 @@ def test_full_decode_T1():
     Wr, bias = synth.make_router(spec), synth.make_bias(spec)
     x_np, idx_r, w_r, logits, ch, _ = _certified_x(spec, 1, Wr, bias)
     x, idx, w, lg = _route_gpu(layer, x_np, 1, spec.topk, logits=True)
-    check_route(idx.cpu().numpy(), w.cpu().numpy(), idx_r, w_r, ch, spec.topk)
+    assert check_route(idx.cpu().numpy(), w.cpu().numpy(), idx_r, w_r, ch, spec.topk) == 1
     l32 = logits.astype(np.float32)
     assert np.max(np.abs(lg.cpu().numpy() - l32) / np.maximum(np.abs(l32), 1e-30)) <= 2.0 ** -23
     out = _forward_gpu(layer, x, idx_r, w_r)
@@ -380,47 +381,65 @@ def test_full_small_batch_per_token(T):
     Wr, bias = synth.make_router(spec), synth.make_bias(spec)
     x_np, idx_r, w_r, logits, ch, _ = _certified_x(spec, T, Wr, bias)
     x, idx, w, _ = _route_gpu(layer, x_np, T, spec.topk)
-    check_route(idx.cpu().numpy(), w.cpu().numpy(), idx_r, w_r, ch, spec.topk)
+    assert check_route(idx.cpu().numpy(), w.cpu().numpy(), idx_r, w_r, ch, spec.topk) == T
     out = _forward_gpu(layer, x, idx_r, w_r)
     ref, denom, _ = oracle_forward(spec, x_np, idx_r, w_r)
     assert rel_err(out, ref, denom) <= REL_TOL
     assert np.array_equal(out, _forward_gpu(layer, x, idx_r, w_r))
 
 
-def test_full_batched_decode_T64_sampled():
+def test_full_batched_decode_T64_all_tokens():
+    # every token of the batch certified (uncertified ones redrawn), so the
+    # GPU's ids equal the oracle's on all 64; every output compared
     spec, t, layer = _full()
     T = 64
     Wr, bias = synth.make_router(spec), synth.make_bias(spec)
     x_np = synth.make_x(spec, T, attempt=1)
-    idx_r, w_r, logits, ch = oracle.route(x_np, Wr, bias, spec.topk, want_detail=True)
+    idx_r, w_r, logits, ch = certify_rows(spec, x_np, Wr, bias)
     x, idx, w, _ = _route_gpu(layer, x_np, T, spec.topk)
-    ncert = check_route(idx.cpu().numpy(), w.cpu().numpy(), idx_r, w_r, ch, spec.topk)
-    assert ncert >= T - 4
+    assert check_route(idx.cpu().numpy(), w.cpu().numpy(), idx_r, w_r, ch, spec.topk) == T
     out = _forward_gpu(layer, x, idx_r, w_r)
-    sample = [0, 13, 37, 63]
-    ref, denom, _ = oracle_forward(spec, x_np, idx_r, w_r, tokens=sample)
-    assert rel_err(out[sample], ref, denom) <= REL_TOL
+    ref, denom, drops = oracle_forward(spec, x_np, idx_r, w_r)
+    assert drops == 0
+    err = rel_err(out, ref, denom)
+    print(f"[full T=64] max rel err {err:.3g} over {T} tokens", flush=True)
+    assert err <= REL_TOL
+    assert layer.error_count() == 0
 
 
-def test_full_prefill_T2048_zipf_sampled():
+# Tile geometry of the multi-token path at this shape (a flat layer, one bf16
+# plane): experts with more than 16 assignments run on 128-token gate/up tiles
+# and 64-token down tiles; the others stream.
+_SMAX, _TILE_GU, _TILE_DN = 16, 128, 64
+
+
+def test_full_prefill_T2048_zipf_tile_edges():
+    # 2048 Zipf-routed tokens, all certified (so the GPU's ids equal the
+    # oracle's on every token and the tiles are the ones the oracle's ids
+    # give); compared: every token on a tile edge of every expert that runs on
+    # tiles (first/last row of its first and last gate/up and down tile, the
+    # first row of its second), plus 32 drawn at random
     spec, t, layer = _full("zipf")
     T = 2048
     Wr, bias = synth.make_router(spec), synth.make_bias(spec)
     x_np = synth.make_x(spec, T)
+    idx_r, w_r, logits, ch = certify_rows(spec, x_np, Wr, bias)
     x, idx, w, _ = _route_gpu(layer, x_np, T, spec.topk)
-    idx_g, w_g = idx.cpu().numpy(), w.cpu().numpy()
-    rng = np.random.default_rng(0)
-    sample = np.sort(rng.choice(T, 24, replace=False))
-    idx_r, w_r, logits, ch = oracle.route(x_np[sample], Wr, bias, spec.topk, want_detail=True)
-    check_route(idx_g[sample], w_g[sample], idx_r, w_r, ch, spec.topk)
-    # forward with the oracle's routes on the sampled tokens
-    idx_in, w_in = idx_g.copy(), w_g.copy()
-    idx_in[sample], w_in[sample] = idx_r, w_r
-    out = _forward_gpu(layer, x, idx_in, w_in)
-    few = sample[:3]
-    ref, denom, _ = oracle_forward(spec, x_np, idx_in, w_in, tokens=few)
-    assert rel_err(out[few], ref, denom) <= REL_TOL
+    assert check_route(idx.cpu().numpy(), w.cpu().numpy(), idx_r, w_r, ch, spec.topk) == T
+    out = _forward_gpu(layer, x, idx_r, w_r)
     assert layer.error_count() == 0
+    edges = tile_edge_tokens(idx_r, spec.n_experts, _SMAX, (_TILE_GU, _TILE_DN))
+    counts = np.bincount(idx_r.ravel(), minlength=spec.n_experts)
+    assert (counts > _SMAX).sum() >= 32 and counts.max() > 8 * _TILE_GU   # the tile path is exercised
+    rng = np.random.default_rng(0)
+    check = np.union1d(edges, rng.choice(T, 32, replace=False))
+    assert check.size >= 64
+    ref, denom, drops = oracle_forward(spec, x_np, idx_r, w_r, tokens=check)
+    assert drops == 0
+    err = rel_err(out[check], ref, denom)
+    print(f"[full T=2048 zipf] max rel err {err:.3g} over {check.size} tokens "
+          f"({len(edges)} on tile edges of {(counts > _SMAX).sum()} experts)", flush=True)
+    assert err <= REL_TOL
 
 
 @pytest.mark.parametrize("latent", [0, 256])
@@ -478,15 +497,19 @@ def test_full_largest_batch_and_one_past_it():
     spec, t, layer = _full()
     T = 43690
     x_np = synth.make_x(spec, T, attempt=3)
-    x, idx, w, _ = _route_gpu(layer, x_np, T, spec.topk)
-    idx_g, w_g = idx.cpu().numpy(), w.cpu().numpy()
     sample = [0, 12345, 30001, T - 1]
     Wr, bias = synth.make_router(spec), synth.make_bias(spec)
-    idx_r, w_r, _, ch = oracle.route(x_np[sample], Wr, bias, spec.topk, want_detail=True)
-    check_route(idx_g[sample], w_g[sample], idx_r, w_r, ch, spec.topk)
+    idx_r, w_r, _, ch = certify_rows(spec, x_np, Wr, bias, rows=sample)
+    x, idx, w, _ = _route_gpu(layer, x_np, T, spec.topk)
+    idx_g, w_g = idx.cpu().numpy(), w.cpu().numpy()
+    assert check_route(idx_g[sample], w_g[sample], idx_r, w_r, ch, spec.topk) == len(sample)
     out = _forward_gpu(layer, x, idx_g, w_g)
-    ref, denom, _ = oracle_forward(spec, x_np, idx_g, w_g, tokens=sample)
-    assert rel_err(out[sample], ref, denom) <= REL_TOL
+    # plus the tile edges of the two most loaded experts (ids as run: the GPU's)
+    counts = np.bincount(idx_g.ravel(), minlength=spec.n_experts)
+    hot = np.argsort(-counts, kind="stable")[:2]
+    check = np.union1d(sample, tile_edge_tokens(idx_g, spec.n_experts, _SMAX, (_TILE_GU, _TILE_DN), hot))
+    ref, denom, _ = oracle_forward(spec, x_np, idx_g, w_g, tokens=check)
+    assert rel_err(out[check], ref, denom) <= REL_TOL
     del out
     with pytest.raises(k3.K3MoeError):
         layer.workspace_size(T + 1)

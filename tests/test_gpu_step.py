@@ -17,7 +17,8 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import REL_TOL, bf16_rne_np, check_route, oracle_forward
+from gpu_helpers import (_REDRAW, _REDRAW_MAX, REL_TOL, bf16_rne_np, check_route, oracle_forward,
+                         route_certificate)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,9 +50,27 @@ def _inv_certified(h, eps):
     return ok
 
 
-def _step(spec, layer, T, scale=4.0, tokens=None, with_outputs=True, attempt=0):
+def _certified_stream(spec, T, scale, attempt, gamma_np):
+    """A residual stream whose normed tokens all have certified routes: row t
+    of an uncertified token is redrawn as the single row
+    make_residual(spec, 1, attempt=_REDRAW + 64 t + a) for the next a."""
     h_np = synth.make_residual(spec, T, scale=scale, attempt=attempt)
+    Wr, bias = synth.make_router(spec), synth.make_bias(spec)
+    for a in range(_REDRAW_MAX):
+        x_ref = oracle.prenorm_bf16(h_np, gamma_np, EPS)
+        _, _, _, ch = oracle.route(x_ref, Wr, bias, spec.topk, renorm=spec.renorm,
+                                   routed_scale=spec.routed_scale, want_detail=True)
+        bad = np.nonzero(~route_certificate(ch, spec.topk))[0]
+        if bad.size == 0:
+            return h_np
+        for t in bad:
+            h_np[t] = synth.make_residual(spec, 1, scale=scale, attempt=_REDRAW + int(t) * _REDRAW_MAX + a)[0]
+    raise AssertionError("a token stayed uncertified")
+
+
+def _step(spec, layer, T, scale=4.0, tokens=None, with_outputs=True, attempt=0):
     gamma_np = synth.make_post_norm(spec)
+    h_np = _certified_stream(spec, T, scale, attempt, gamma_np)
     h = torch.from_numpy(h_np).to(DEV)
     gamma = torch.from_numpy(gamma_np).to(DEV)
     idx = torch.empty((T, spec.topk), dtype=torch.int32, device=DEV)
@@ -73,7 +92,7 @@ def _step(spec, layer, T, scale=4.0, tokens=None, with_outputs=True, attempt=0):
     idx_r, w_r, _, ch = oracle.route(x_ref[tokens], synth.make_router(spec), synth.make_bias(spec),
                                      spec.topk, renorm=spec.renorm, routed_scale=spec.routed_scale,
                                      want_detail=True)
-    check_route(idx_g[tokens], w_g[tokens], idx_r, w_r, ch, spec.topk)
+    assert check_route(idx_g[tokens], w_g[tokens], idx_r, w_r, ch, spec.topk) == tokens.size
     # the layer output for the GPU's own routes, added to the stream
     ref, denom, drops = oracle_forward(spec, x_ref, idx_g, w_g, tokens=tokens)
     assert drops == 0
@@ -158,7 +177,7 @@ def test_full_step_T1():
 
 def test_full_step_T64_sampled():
     spec, _, layer = _full()
-    _step(spec, layer, 64, tokens=[0, 21, 42, 63])
+    _step(spec, layer, 64, tokens=np.arange(0, 64, 4))
     _FULL.clear()
 
 
