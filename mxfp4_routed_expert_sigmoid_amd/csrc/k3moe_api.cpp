@@ -6,6 +6,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <new>
 
@@ -822,7 +823,11 @@ void k3moe_layer_destroy(k3moe_layer *l)
 
 const char *k3moe_status_string(k3moe_status s)
 {
-    switch (s) {
+    // a C caller may pass any int; read it as one (loading a C++ enum
+    // outside its value range is undefined)
+    int v;
+    std::memcpy(&v, &s, sizeof v);
+    switch (v) {
     case K3MOE_OK: return "ok";
     case K3MOE_E_INVALID_ARG: return "invalid argument";
     case K3MOE_E_CONFIG: return "invalid or incomplete config";
