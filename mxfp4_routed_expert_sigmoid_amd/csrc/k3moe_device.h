@@ -1,5 +1,6 @@
 // Device helpers shared by the gfx950 kernel files: vector types, bf16 and
-// E8M0 conversions, the fp4 -> bf16 expansion, MFMA wrappers, the gated
+// E8M0 conversions, the fp4 -> bf16 expansion, MFMA wrappers and the
+// operands of the scaled MFMA, the e4m3 term expansion, the gated
 // activation, wave-level reductions and the top-k of one token.
 #pragma once
 
@@ -67,6 +68,102 @@ template <int S = 0>
 __device__ __forceinline__ v4f mfma_fp4_fp8(const v8i &a, const v8i &b, v4f c, int sa, int sb)
 {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, S, sa, S, sb);
+}
+
+// A lane's scale bytes for 4 consecutive K steps: from the 16 bytes holding
+// K-blocks 4s+g (step s, lane group g) of a row, byte g of each dword.
+__device__ __forceinline__ uint32_t gather_scales(u4 v, uint32_t grp)
+{
+    const uint32_t lo = __builtin_amdgcn_perm(v.y, v.x, grp | ((4u + grp) << 8) | 0x0c0c0000u);
+    const uint32_t hi = __builtin_amdgcn_perm(v.w, v.z, 0x00000c0cu | (grp << 16) | ((4u + grp) << 24));
+    return lo | hi;
+}
+
+// 0x80 in each byte of x that is 0xFF (E8M0 255), 0 elsewhere.
+__device__ __forceinline__ uint32_t ff_bytes(uint32_t x)
+{
+    const uint32_t y = ~x;
+    return ~(((y & 0x7f7f7f7fu) + 0x7f7f7f7fu) | y | 0x7f7f7f7fu);
+}
+
+// Operands of the scaled MFMA: fp4 A (16 bytes in the low 4 registers) and
+// fp8 B (two 16-byte halves).
+__device__ __forceinline__ v8i a_operand(u4 v) { return v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0}; }
+
+__device__ __forceinline__ v8i b_operand(u4 lo, u4 hi)
+{
+    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// Maximum over the 8 lanes of each aligned lane octet (DPP: swap neighbours,
+// swap pairs, mirror the half-row).
+__device__ __forceinline__ float octet_max(float m)
+{
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xb1, 0xf, 0xf, false)));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4e, 0xf, 0xf, false)));
+    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xf, 0xf, false)));
+    return m;
+}
+
+// Split values into NT e4m3 terms, x = sum_t 2^(S_t - 127) q_t, in the
+// layout of the scaled MFMA's fp8 operand. This lane holds NV consecutive
+// values of a 32-element block whose other values sit in the lanes that
+// block_max reduces over; the block shares one E8M0 scale per term. The
+// scale puts the block's largest remainder in [224, 448]; a term takes only
+// the elements within 6 binades of that maximum (the rest stay in the
+// remainder) and each term's rounding error is carried exactly into the
+// next term. code[t][q] packs the codes of values 4q..4q+3 of term t, first
+// value lowest; sbyte[t] is the term's E8M0 byte.
+template <int NT, int NV, class MaxFn>
+__device__ __forceinline__ void split_e4m3_terms(float (&r)[NV], MaxFn block_max, uint32_t (&code)[NT][NV / 4],
+                                                 int (&sbyte)[NT])
+{
+    static_assert(NV % 4 == 0, "whole code words");
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        float lm = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) lm = fmaxf(lm, fabsf(r[i]));
+        const float m = block_max(lm);
+        int S = 0;
+        float keep_min = INFINITY;
+        if (m > 0.0f) {
+            int ex;
+            frexpf(m, &ex);  // m in [2^(ex-1), 2^ex)
+            S = ex - 9;      // m / 2^S in [256, 512)
+            if (ldexpf(m, -S) > 448.0f) S += 1;
+            if (S < -127) S = -127;
+            frexpf(ldexpf(m, -S), &ex);
+            keep_min = ldexpf(1.0f, ex - 7);  // 6 binades below the block maximum
+        }
+#pragma unroll
+        for (int w = 0; w < NV / 4; ++w) {
+            uint32_t c4 = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float q = ldexpf(r[4 * w + i], -S);
+                if (fabsf(q) >= keep_min) {
+                    const uint32_t c = __builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xffu;
+                    r[4 * w + i] -= ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)c, 0), S);
+                    c4 |= c << (8 * i);
+                }
+            }
+            code[t][w] = c4;
+        }
+        sbyte[t] = S + 127;
+    }
+}
+
+// The octet form: the 8 lanes of an aligned lane octet hold one 32-element
+// block, 4 consecutive values each.
+template <int NT>
+__device__ __forceinline__ void split_e4m3_octet(const float4 v, uint32_t (&code4)[NT], int (&sbyte)[NT])
+{
+    float r[4] = {v.x, v.y, v.z, v.w};
+    uint32_t code[NT][1];
+    split_e4m3_terms<NT, 4>(r, [](float m) { return octet_max(m); }, code, sbyte);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) code4[t] = code[t][0];
 }
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).

@@ -6,21 +6,28 @@
 //
 // Design. Once several tokens share an expert the projections are GEMMs:
 // for an active expert e with n_e assignments, G = W1_e X_e^T, U = W3_e X_e^T
-// (I x n_e), A_e = act(G, U), Y_e = W2_e A_e (H x n_e). They run on the bf16
-// MFMA v_mfma_f32_16x16x32_bf16 (products exact, fp32 accumulation):
-//  * the fp4 weights are expanded to bf16 in registers with
+// (I x n_e), A_e = act(G, U), Y_e = W2_e A_e (H x n_e).
+//  * Gate/up tiles run on the bf16 MFMA v_mfma_f32_16x16x32_bf16: the fp4
+//    weights are expanded to bf16 in registers with
 //    v_cvt_scalef32_pk_bf16_fp4, which applies the block's E8M0 scale
 //    exactly (2^(s-127), byte 0 included; byte 255 makes the group zero),
-//    so a weight is the exact value the MXFP4 format defines;
-//  * the token activations x are bf16 already: one B operand, exact;
-//  * the expert activation a (fp32) is fed as two bf16 terms hi + lo
-//    (hi = bf16(a), lo = bf16(a - hi); |a - hi - lo| <= 2^-17 |a|), each a
-//    separate MFMA into the same accumulator.
-// A block owns 256 rows of one expert and a tile of its tokens; weights and
-// token rows pass through double-buffered LDS (one barrier per K chunk), the
-// next chunk's global loads in flight while the current one is multiplied.
-// The shared expert (bf16 weights) runs on the same kernels with the weight
-// rows loaded as bf16.
+//    and the bf16 tokens are the B operand as they are: every product exact,
+//    fp32 accumulation.
+//  * Down tiles of the routed experts run on the scaled MFMA
+//    v_mfma_scale_f32_16x16x128_f8f6f4: the fp4 weight bytes are the A
+//    operand as loaded (their E8M0 byte the A scale) and the activation is
+//    fed as kATerms e4m3 terms with one E8M0 byte per 32-block each, which
+//    the gate/up epilogue writes; one MFMA per term into the same
+//    accumulator (about 2^-19 of each block's maximum is left out).
+//  * Where the streamed down projection reads an expert's activation (or
+//    the down tiles cannot use terms), the activation goes as two bf16
+//    planes hi + lo (hi = bf16(a), lo = bf16(a - hi); |a - hi - lo| <=
+//    2^-17 |a|) on the bf16 MFMA, as does the shared expert (bf16 weights).
+// A block owns 256 rows of one expert and a tile of its tokens; each wave
+// loads its weight rows from HBM straight into registers (one 16-byte load
+// per lane per K chunk, the next chunk in flight while the current one is
+// multiplied), and the token side passes through double-buffered LDS, one
+// barrier per K chunk.
 //
 // The expert outputs go to the staging rows ys[t][j][.] (and ys[t][k][.] for
 // the shared expert); the combine sums them in router order.
@@ -130,10 +137,21 @@ template <> struct GemmShape<kDN> {   // down: 4 waves x 64 rows, 64 tokens (hi,
 template <> struct GemmShape<kGU2> {  // gate/up, tokens as hi and lo: 8 waves x 32 rows, 64 tokens
     static constexpr int WAVES = 8, RF = 2, TF = 4, NMAT = 2, NPL = 2, TOK = 64;
 };
+// The down tile on the scaled MFMA v_mfma_scale_f32_16x16x128_f8f6f4: the
+// fp4 weights go in as loaded (A operand, the E8M0 byte as the lane's A
+// scale) and the activation as kATerms e4m3 terms (B operands with their own
+// E8M0 bytes), one MFMA per term into the same accumulator.
+constexpr int kDN8 = 4;
+template <> struct GemmShape<kDN8> {   // down: 4 waves x 64 rows, 64 tokens, the activation as kATerms terms
+    static constexpr int WAVES = 4, RF = 4, TF = 4, NMAT = 1, NPL = kATerms, TOK = 64;
+};
 constexpr int kTileRows = 256;  // weight rows per block (every shape)
 static_assert(GemmShape<kGU>::WAVES * GemmShape<kGU>::RF * 16 == kTileRows, "gate/up tile rows");
 static_assert(GemmShape<kDN>::WAVES * GemmShape<kDN>::RF * 16 == kTileRows, "down tile rows");
 static_assert(GemmShape<kGU2>::WAVES * GemmShape<kGU2>::RF * 16 == kTileRows, "gate/up tile rows");
+static_assert(GemmShape<kDN8>::WAVES * GemmShape<kDN8>::RF * 16 == kTileRows, "down tile rows");
+static_assert(GemmShape<kDN8>::TOK == GemmShape<kDN>::TOK, "one tile list serves both down forms");
+constexpr int kB8Row = 128 + 16;  // LDS bytes per term row per chunk (128 e4m3 codes + padding)
 
 struct GemmParams {
     int rows, KD, K, T, act;   // weight rows (I / I_s or H), reduction length (H or I / I_s), top-k
@@ -148,16 +166,122 @@ struct GemmParams {
     const int32_t *active_e, *active_off, *sorted;
     const int2 *tiles;
     const int32_t *tile_n;
+    // f8 down tiles: the activation as e4m3 terms [row][NPL][KD] and their
+    // E8M0 bytes [row][NPL][KD / 32] (row: the sorted assignment)
+    const uint8_t *bq, *bsc;
     int sh_blocks;             // leading blocks that run the shared expert
-    uint16_t *ohi, *olo;       // gate/up: activation hi/lo [row][rows]
+    uint16_t *ohi, *olo;       // gate/up: activation hi/lo [row][rows] (null: not written)
+    uint8_t *oq, *osc;         // gate/up: activation as kATerms e4m3 terms [row][kATerms][rows]
+                               // and E8M0 bytes [row][kATerms][rows / 32] (null: not written)
     float *ys;                 // down: staging [T][K + 1][H]
 };
+
+// One buffer of an f8 tile's token side: the term rows, then one scale word
+// (4 E8M0 bytes, a chunk's 4 blocks) per term row.
+template <int KIND>
+__host__ __device__ constexpr int f8_buf_bytes()
+{
+    using S = GemmShape<KIND>;
+    return S::NPL * S::TOK * (kB8Row + 4);
+}
+
+template <int KIND>
+__host__ __device__ constexpr int gemm_tok_bytes()
+{
+    using S = GemmShape<KIND>;
+    return KIND == kDN8 ? 2 * f8_buf_bytes<KIND>() : 2 * S::NPL * S::TOK * (128 * 2 + kBPad);
+}
 
 template <int KIND>
 __host__ __device__ constexpr int gemm_lds_bytes()
 {
-    using S = GemmShape<KIND>;
-    return 2 * S::NPL * S::TOK * (128 * 2 + kBPad) + 2 * S::TOK * 4;
+    return gemm_tok_bytes<KIND>() + 2 * GemmShape<KIND>::TOK * 4;
+}
+
+// Gate/up epilogue: the activation of this lane's rows row0 + 16 rf + 4 g +
+// [0, 4) for token column col, written as bf16 hi and lo planes and/or as
+// kATerms e4m3 terms. For the terms a wave's 32 rows are one E8M0 block: the
+// 4 lanes holding a column (lane groups 0..3) reduce its maximum. Every lane
+// runs the split (the shuffles need the whole wave); only columns with a
+// token store.
+template <int RF>
+__device__ __forceinline__ void gu_epilogue(const GemmParams &p, const float (&av)[RF][4], int row0, int g,
+                                            int orow, bool store)
+{
+    const int rows = p.rows;
+    if (p.ohi && store) {
+#pragma unroll
+        for (int rf = 0; rf < RF; ++rf) {
+            uint32_t hi2[2], lo2[2];
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+                const uint16_t h0 = bf16_rne(av[rf][i]), h1 = bf16_rne(av[rf][i + 1]);
+                const uint16_t q0 = bf16_rne(av[rf][i] - bf16f(h0)), q1 = bf16_rne(av[rf][i + 1] - bf16f(h1));
+                hi2[i / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                lo2[i / 2] = (uint32_t)q0 | ((uint32_t)q1 << 16);
+            }
+            const size_t o = (size_t)orow * rows + row0 + 16 * rf + 4 * g;
+            *reinterpret_cast<uint2 *>(p.ohi + o) = uint2{hi2[0], hi2[1]};
+            *reinterpret_cast<uint2 *>(p.olo + o) = uint2{lo2[0], lo2[1]};
+        }
+    }
+    if (p.oq) {
+        static_assert(RF == 2, "a wave's rows are one 32-row block");
+        float r[4 * RF];
+#pragma unroll
+        for (int rf = 0; rf < RF; ++rf)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r[4 * rf + i] = av[rf][i];
+        uint32_t code[kATerms][RF];
+        int sb[kATerms];
+        split_e4m3_terms<kATerms, 4 * RF>(
+            r, [](float m) {
+                m = fmaxf(m, __shfl_xor(m, 16));
+                return fmaxf(m, __shfl_xor(m, 32));
+            },
+            code, sb);
+        if (store) {
+            const int nb = rows >> 5;
+#pragma unroll
+            for (int t = 0; t < kATerms; ++t) {
+                uint8_t *q = p.oq + ((size_t)orow * kATerms + t) * rows + row0 + 4 * g;
+#pragma unroll
+                for (int rf = 0; rf < RF; ++rf) *reinterpret_cast<uint32_t *>(q + 16 * rf) = code[t][rf];
+                if (g == 0) p.osc[((size_t)orow * kATerms + t) * nb + (row0 >> 5)] = (uint8_t)sb[t];
+            }
+        }
+    }
+}
+
+// Epilogue of a tile: lane holds rows 4g + i (i = 0..3) of token column
+// 16 tf + l16 in each 16-row fragment rf; gate/up writes the activation,
+// down its fp32 rows to the staging rows.
+template <int KIND, int NMAT, int RF, int TF>
+__device__ __forceinline__ void tile_epilogue(const GemmParams &p, const v4f (&acc)[NMAT][RF][TF], int row0, int ntf,
+                                              int n, const int *oro_l)
+{
+    constexpr bool GU = KIND != kDN && KIND != kDN8;
+    const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
+#pragma unroll
+    for (int tf = 0; tf < TF; ++tf) {
+        if (tf >= ntf) break;  // wave-uniform
+        const int col = 16 * tf + l16;
+        const bool store = col < n;
+        if constexpr (GU) {
+            float av[RF][4];
+#pragma unroll
+            for (int rf = 0; rf < RF; ++rf)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    av[rf][i] = act_fn(acc[0][rf][tf][i], acc[1][rf][tf][i], p.act, p.b1, p.b2);
+            gu_epilogue<RF>(p, av, row0, g, oro_l[min(col, n - 1)], store);
+        } else if (store) {
+#pragma unroll
+            for (int rf = 0; rf < RF; ++rf)
+                *reinterpret_cast<float4 *>(p.ys + (size_t)oro_l[col] * p.rows + row0 + 16 * rf + 4 * g) =
+                    float4{acc[0][rf][tf][0], acc[0][rf][tf][1], acc[0][rf][tf][2], acc[0][rf][tf][3]};
+        }
+    }
 }
 
 template <int KIND, bool FP4>
@@ -165,7 +289,6 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &p, int e, int rb, in
                                           const int *oro_l, uint8_t *B_l)
 {
     using S = GemmShape<KIND>;
-    constexpr bool GU = KIND != kDN;
     constexpr int WAVES = S::WAVES, RF = S::RF, TF = S::TF, NMAT = S::NMAT, NPL = S::NPL, TOK = S::TOK;
     constexpr int NT = 64 * WAVES;
     constexpr int KC = FP4 ? 128 : 32;           // K per chunk
@@ -321,35 +444,171 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &p, int e, int rb, in
         __syncthreads();
     }
 
-    // epilogue: lane holds rows 4g + i (i = 0..3) of token column 16 tf + l16
+    tile_epilogue<KIND>(p, acc, row0, ntf, n, oro_l);
+}
+
+// A down tile on the scaled MFMA (kind kDN8): routed fp4 weights only.
+// Rows and chunks as in gemm_tile; per K chunk of 128 a lane's 16 weight
+// bytes (row l16, K-block g) are the A operand as loaded, its E8M0 byte the A
+// scale (byte 255: the fragment is zeroed and the scale made finite, so the
+// group adds exactly nothing). The token side's NPL term rows are staged
+// through double-buffered LDS with one scale word per term row; a B operand
+// is bytes [16g, 16g + 16) and [64 + 16g, 80 + 16g) of a term row, its scale
+// byte g of the row's word.
+template <int KIND>
+__device__ __forceinline__ void gemm_tile_f8(const GemmParams &p, int e, int rb, int n, const int *bro_l,
+                                             const int *oro_l, uint8_t *B_l)
+{
+    using S = GemmShape<KIND>;
+    constexpr int WAVES = S::WAVES, RF = S::RF, TF = S::TF, NMAT = S::NMAT, NTB = S::NPL, TOK = S::TOK;
+    constexpr int NT = 64 * WAVES;
+    constexpr int KC = 128;
+    constexpr int BSEG = KC / 16;                // u4 per term row per chunk
+    constexpr int NBU4 = NTB * TOK * BSEG;       // u4 of one chunk's token side
+    constexpr int NB = (NBU4 + NT - 1) / NT;
+    constexpr int NS = NTB * TOK;                // scale words per chunk
+    constexpr int NSB = (NS + NT - 1) / NT;
+    constexpr int BBUF = f8_buf_bytes<KIND>();
+    constexpr int SOFF = NTB * TOK * kB8Row;     // scale words after the term rows
+    const int KD = p.KD, rows = p.rows, NCH = KD / KC;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
+    const int nrows = min(kTileRows, rows - rb * kTileRows);
+    const int row0 = rb * kTileRows + wave * RF * 16;
+    const int ntf = wave * RF * 16 < nrows ? (n + 15) / 16 : 0;
+
+    const uint32_t rowb = (uint32_t)KD / 2;
+    const uint8_t *wbase[NMAT];
+    const uint8_t *sbase[NMAT];
 #pragma unroll
-    for (int tf = 0; tf < TF; ++tf) {
-        const int col = 16 * tf + l16;
-        if (tf < ntf && col < n) {
+    for (int m = 0; m < NMAT; ++m) {
+        wbase[m] = p.wp[m] + e * p.wsp[m];
+        sbase[m] = p.ws[m] + e * p.wss[m];
+    }
+    uint32_t woff[RF], soff[RF];
+#pragma unroll
+    for (int rf = 0; rf < RF; ++rf) {
+        const uint32_t r = (uint32_t)min(row0 + 16 * rf + l16, rows - 1);
+        woff[rf] = r * rowb + 16 * g;
+        soff[rf] = r * ((uint32_t)KD / 32);
+    }
+    struct Chunk {
+        u4 a[NMAT][RF];
+        uint32_t s[NMAT][RF];
+    };
+    auto aload = [&](int c, Chunk &b) {
+        const uint32_t cc = (uint32_t)min(c, NCH - 1);
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
 #pragma unroll
             for (int rf = 0; rf < RF; ++rf) {
-                const int row = row0 + 16 * rf + 4 * g;
-                if constexpr (GU) {
-                    uint32_t hi2[2], lo2[2];
+                b.a[m][rf] = *reinterpret_cast<const u4 *>(wbase[m] + (woff[rf] + cc * 64));
+                b.s[m][rf] = *reinterpret_cast<const uint32_t *>(sbase[m] + (soff[rf] + cc * 4));
+            }
+    };
+    // token side: fixed per-thread source offsets (32-bit), chunk added per load
+    uint32_t boff[NB], toff[NSB];
 #pragma unroll
-                    for (int i = 0; i < 4; i += 2) {
-                        const float a0 = act_fn(acc[0][rf][tf][i], acc[1][rf][tf][i], p.act, p.b1, p.b2);
-                        const float a1 = act_fn(acc[0][rf][tf][i + 1], acc[1][rf][tf][i + 1], p.act, p.b1, p.b2);
-                        const uint16_t h0 = bf16_rne(a0), h1 = bf16_rne(a1);
-                        const uint16_t q0 = bf16_rne(a0 - bf16f(h0)), q1 = bf16_rne(a1 - bf16f(h1));
-                        hi2[i / 2] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                        lo2[i / 2] = (uint32_t)q0 | ((uint32_t)q1 << 16);
-                    }
-                    const size_t o = (size_t)oro_l[col] * rows + row;
-                    *reinterpret_cast<uint2 *>(p.ohi + o) = uint2{hi2[0], hi2[1]};
-                    *reinterpret_cast<uint2 *>(p.olo + o) = uint2{lo2[0], lo2[1]};
-                } else {
-                    *reinterpret_cast<float4 *>(p.ys + (size_t)oro_l[col] * rows + row) =
-                        float4{acc[0][rf][tf][0], acc[0][rf][tf][1], acc[0][rf][tf][2], acc[0][rf][tf][3]};
-                }
+    for (int q = 0; q < NB; ++q) {
+        const int v = min(tid + NT * q, NBU4 - 1);
+        const int pl = v / (TOK * BSEG), vv = v - pl * (TOK * BSEG);
+        const int col = vv / BSEG, seg = vv - col * BSEG;
+        boff[q] = ((uint32_t)bro_l[col] * NTB + pl) * (uint32_t)KD + 16 * seg;
+    }
+#pragma unroll
+    for (int q = 0; q < NSB; ++q) {
+        const int v = min(tid + NT * q, NS - 1);
+        const int pl = v / TOK, col = v - pl * TOK;
+        toff[q] = ((uint32_t)bro_l[col] * NTB + pl) * ((uint32_t)KD / 32);
+    }
+    u4 xs[NB];
+    uint32_t xsc[NSB];
+    auto bload = [&](int c) {
+        const uint32_t cc = (uint32_t)min(c, NCH - 1);
+#pragma unroll
+        for (int q = 0; q < NB; ++q) xs[q] = *reinterpret_cast<const u4 *>(p.bq + (boff[q] + cc * KC));
+#pragma unroll
+        for (int q = 0; q < NSB; ++q) xsc[q] = *reinterpret_cast<const uint32_t *>(p.bsc + (toff[q] + cc * 4));
+    };
+    auto bstore = [&](int buf) {
+        uint8_t *Bb = B_l + buf * BBUF;
+#pragma unroll
+        for (int q = 0; q < NB; ++q) {
+            const int v = tid + NT * q;
+            if (NBU4 % NT == 0 || v < NBU4) {
+                const int pl = v / (TOK * BSEG), vv = v - pl * (TOK * BSEG);
+                const int col = vv / BSEG, seg = vv - col * BSEG;
+                *reinterpret_cast<u4 *>(Bb + (pl * TOK + col) * kB8Row + 16 * seg) = xs[q];
             }
         }
+#pragma unroll
+        for (int q = 0; q < NSB; ++q) {
+            const int v = tid + NT * q;
+            if (NS % NT == 0 || v < NS) *reinterpret_cast<uint32_t *>(Bb + SOFF + 4 * v) = xsc[q];
+        }
+    };
+
+    v4f acc[NMAT][RF][TF];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int rf = 0; rf < RF; ++rf)
+#pragma unroll
+            for (int tf = 0; tf < TF; ++tf) acc[m][rf][tf] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // Every chunk runs over all TF fragments (a partial tile multiplies
+    // clamped copies of its last token, never stored).
+    auto compute = [&](const Chunk &b, int buf) {
+        if (ntf == 0) return;
+        const uint8_t *Bb = B_l + buf * BBUF;
+        v8i a[NMAT][RF];
+        int sa[NMAT][RF];
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+            for (int rf = 0; rf < RF; ++rf) {
+                const uint32_t sbyte = (b.s[m][rf] >> (8 * g)) & 0xffu;
+                const uint32_t keep = sbyte == 255u ? 0u : ~0u;
+                const u4 w = b.a[m][rf];
+                a[m][rf] = a_operand(u4{w.x & keep, w.y & keep, w.z & keep, w.w & keep});
+                sa[m][rf] = (int)(sbyte ^ (~keep & 0x80u));   // 255 -> 127
+            }
+#pragma unroll
+        for (int t = 0; t < NTB; ++t) {
+#pragma unroll
+            for (int tf = 0; tf < TF; ++tf) {
+                const int r = t * TOK + 16 * tf + l16;
+                const uint8_t *row = Bb + r * kB8Row;
+                const v8i bv = b_operand(*reinterpret_cast<const u4 *>(row + 16 * g),
+                                         *reinterpret_cast<const u4 *>(row + 64 + 16 * g));
+                const int sb = (int)((*reinterpret_cast<const uint32_t *>(Bb + SOFF + 4 * r) >> (8 * g)) & 0xffu);
+#pragma unroll
+                for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                    for (int rf = 0; rf < RF; ++rf)
+                        acc[m][rf][tf] = mfma_fp4_fp8<0>(a[m][rf], bv, acc[m][rf][tf], sa[m][rf], sb);
+            }
+        }
+    };
+
+    Chunk c0, c1;
+    bload(0);
+    aload(0, c0);
+    bstore(0);
+    __syncthreads();
+    for (int c = 0; c < NCH; c += 2) {
+        bload(c + 1);
+        aload(c + 1, c1);
+        compute(c0, 0);
+        bstore(1);
+        __syncthreads();
+        if (c + 1 >= NCH) break;
+        bload(c + 2);
+        aload(c + 2, c0);
+        compute(c1, 1);
+        bstore(0);
+        __syncthreads();
     }
+    tile_epilogue<KIND>(p, acc, row0, ntf, n, oro_l);
 }
 
 // One launch: the shared expert's tiles first (bf16 weights, tokens in
@@ -358,14 +617,15 @@ template <int KIND>
 __global__ __launch_bounds__(64 * GemmShape<KIND>::WAVES) void k_gemm(GemmParams p)
 {
     using S = GemmShape<KIND>;
-    constexpr bool GU = KIND != kDN;
+    constexpr bool F8 = KIND == kDN8;
+    constexpr bool GU = KIND != kDN && KIND != kDN8;
     extern __shared__ __align__(16) uint8_t lds[];
     uint8_t *B_l = lds;
-    int *bro_l = reinterpret_cast<int *>(lds + 2 * S::NPL * S::TOK * (128 * 2 + kBPad));  // token plane row per column
-    int *oro_l = bro_l + S::TOK;                                                          // output row per column
+    int *bro_l = reinterpret_cast<int *>(lds + gemm_tok_bytes<KIND>());  // token side row per column
+    int *oro_l = bro_l + S::TOK;                                         // output row per column
     const int RB = (p.rows + kTileRows - 1) / kTileRows;
     int b = blockIdx.x;
-    if (b < p.sh_blocks) {
+    if (!F8 && b < p.sh_blocks) {
         // shared expert: rows of I_s (gate/up) or H (down); p.rows/KD already
         // describe the shared matrices when sh_blocks > 0 in a shared launch
         const int tile = b / RB, rb = b - tile * RB;
@@ -376,7 +636,7 @@ __global__ __launch_bounds__(64 * GemmShape<KIND>::WAVES) void k_gemm(GemmParams
             oro_l[c] = GU ? t : t * (p.K + 1) + p.K;
         }
         __syncthreads();
-        gemm_tile<KIND, false>(p, 0, rb, p0, n, bro_l, oro_l, B_l);
+        if constexpr (!F8) gemm_tile<KIND, false>(p, 0, rb, p0, n, bro_l, oro_l, B_l);
         return;
     }
     b -= p.sh_blocks;
@@ -392,7 +652,10 @@ __global__ __launch_bounds__(64 * GemmShape<KIND>::WAVES) void k_gemm(GemmParams
         oro_l[c] = GU ? p0 + cc : (a / p.K) * (p.K + 1) + a % p.K;
     }
     __syncthreads();
-    gemm_tile<KIND, true>(p, e, rb, p0, n, bro_l, oro_l, B_l);
+    if constexpr (F8)
+        gemm_tile_f8<KIND>(p, e, rb, n, bro_l, oro_l, B_l);
+    else
+        gemm_tile<KIND, true>(p, e, rb, p0, n, bro_l, oro_l, B_l);
 }
 
 }  // namespace
@@ -407,6 +670,8 @@ static bool set_lds_limits()
                               hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes<kDN>());
     (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm<kGU2>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes<kGU2>());
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_gemm<kDN8>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, gemm_lds_bytes<kDN8>());
     return true;
 }
 
@@ -431,7 +696,8 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t 
                           const int32_t *active_n, const int32_t *active_e, const int32_t *active_off,
                           const int32_t *sorted, uint16_t *act_hi, uint16_t *act_lo, uint16_t *ash_hi,
                           uint16_t *ash_lo, float *sh_part, int2 *tiles_gu, int2 *tiles_dn, int32_t *light,
-                          int32_t *counts, float *ys, float *ysh, hipStream_t s, Profiler *prof)
+                          int32_t *counts, float *ys, float *ysh, hipStream_t s, Profiler *prof,
+                          const TermBufs &tb)
 {
     static const bool lds_set = set_lds_limits();  // once per process (thread-safe static)
     (void)lds_set;
@@ -452,6 +718,12 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t 
     // streamed limit, no tile is heavy and the tile GEMMs would only exit
     const int64_t most = L.routes_distinct ? (int64_t)T : (int64_t)T * L.K;
     const bool gemm_gu = !(stream && most <= smax_gu), gemm_dn = !(stream_dn && most <= smax_dn);
+    // the scaled-MFMA down tiles: when every expert on down tiles also ran
+    // gate/up on tiles (smax_dn >= smax_gu), whose epilogue then writes the
+    // activation's terms; it also writes hi/lo when the streamed down
+    // projection reads rows of experts that ran gate/up on tiles
+    const bool f8_dn = gemm_dn && gemm_gu && smax_dn >= smax_gu && tb.aq != nullptr;
+    const bool hilo_from_tiles = !f8_dn || smax_dn > smax_gu;
     k_tiles<<<1, 1024, 0, s>>>(active_n, active_off, TG, TD, smax_gu, smax_dn, tiles_gu, tiles_dn, light_gu, light_dn,
                                counts);
 
@@ -487,18 +759,22 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t 
         gp.sorted = sorted;
         gp.tiles = tiles_gu;
         gp.tile_n = counts;
-        gp.ohi = act_hi;
-        gp.olo = act_lo;
+        gp.ohi = hilo_from_tiles ? act_hi : nullptr;
+        gp.olo = hilo_from_tiles ? act_lo : nullptr;
+        gp.oq = f8_dn ? tb.aq : nullptr;
+        gp.osc = f8_dn ? tb.aqs : nullptr;
         if (gemm_gu) {
             StageMark mt(prof, K3MOE_STAGE_GATEUP_TILES, s);
-            if (two)
+            if (two) {
                 k_gemm<kGU2><<<(unsigned)(cap_gu * rb_i), 64 * GemmShape<kGU2>::WAVES, gemm_lds_bytes<kGU2>(), s>>>(gp);
-            else
+            } else {
                 k_gemm<kGU><<<(unsigned)(cap_gu * rb_i), 64 * GemmShape<kGU>::WAVES, gemm_lds_bytes<kGU>(), s>>>(gp);
+            }
         }
         if (L.Is > 0 && !sh_stream) {
             StageMark m2(prof, K3MOE_STAGE_SHARED_GATEUP, s);
             GemmParams sp = gp;
+            sp.oq = sp.osc = nullptr;
             sp.rows = L.Is;
             sp.KD = L.H;
             sp.bp[0] = sp.bp[1] = x;
@@ -536,7 +812,14 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t 
         dp.ys = ys;
         if (gemm_dn) {
             StageMark mt(prof, K3MOE_STAGE_DOWN_TILES, s);
-            k_gemm<kDN><<<(unsigned)(cap_dn * rb_r), 64 * GemmShape<kDN>::WAVES, gemm_lds_bytes<kDN>(), s>>>(dp);
+            if (f8_dn) {
+                GemmParams fp = dp;
+                fp.bq = tb.aq;
+                fp.bsc = tb.aqs;
+                k_gemm<kDN8><<<(unsigned)(cap_dn * rb_r), 64 * GemmShape<kDN8>::WAVES, gemm_lds_bytes<kDN8>(), s>>>(fp);
+            } else {
+                k_gemm<kDN><<<(unsigned)(cap_dn * rb_r), 64 * GemmShape<kDN>::WAVES, gemm_lds_bytes<kDN>(), s>>>(dp);
+            }
         }
         if (L.Is > 0 && !sh_stream) {
             // shared rows of H: to slot k of ys (flat), or to ysh [T][H] (K = 0 makes the row t)

@@ -13,8 +13,8 @@
 namespace k3moe {
 
 // Activation split widths (number of e4m3 terms in the fp8 expansion that
-// feeds the scaled MFMA's B operand): 4 for a bf16 token vector (exact) and
-// 4 for the fp32 expert activation.
+// feeds the scaled MFMA's B operand): 4 for the fp32 expert activation (and
+// for the single-token kernels' bf16 token).
 constexpr int kATerms = 4;
 constexpr int kMaxExperts = 4096;
 constexpr int kMaxTopk = 64;
@@ -38,6 +38,9 @@ struct WsLayout {
     size_t tiles_gu, tiles_dn;  // grouped-GEMM tile lists, int2 each
     size_t light;             // int32 [2][E]: experts for the weight-streaming kernels (gate/up, down)
     size_t tile_n;            // int32 [4]: gate/up tiles, down tiles, light gate/up, light down
+    // f8 down tiles: the routed activation as kATerms e4m3 terms
+    // [T*k][kATerms][I] and their E8M0 bytes [T*k][kATerms][I/32]
+    size_t aq = 0, aqs = 0;
     // latent layer only (0 otherwise)
     size_t lat_z = 0;         // z = Wd x as bf16 hi then lo planes [T][L] (4 bytes per element)
     size_t lat_acc = 0;       // routed aggregate fp32 [T][L]
@@ -216,11 +219,24 @@ size_t grouped_tile_cap_dn(int64_t T, int K, int E);
 // a second plane (lo of an fp32 input) or null. ysh: the shared expert's
 // output fp32 [T][H], or null for slot k of ys. Routed outputs go to ys
 // [T][k + 1][EK].
+// term buffers of the f8 down tiles (null: those tiles run on bf16)
+struct TermBufs {
+    uint8_t *aq = nullptr, *aqs = nullptr;   // the routed activation's terms
+};
+// The term regions of a workspace.
+inline TermBufs term_bufs(char *ws, const WsLayout &lay)
+{
+    TermBufs t;
+    t.aq = reinterpret_cast<uint8_t *>(ws + lay.aq);
+    t.aqs = reinterpret_cast<uint8_t *>(ws + lay.aqs);
+    return t;
+}
 hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t *xr, const uint16_t *xr_lo, int T,
                           const int32_t *active_n, const int32_t *active_e, const int32_t *active_off,
                           const int32_t *sorted, uint16_t *act_hi, uint16_t *act_lo, uint16_t *ash_hi,
                           uint16_t *ash_lo, float *sh_part, int2 *tiles_gu, int2 *tiles_dn, int32_t *light,
-                          int32_t *counts, float *ys, float *ysh, hipStream_t s, Profiler *prof);
+                          int32_t *counts, float *ys, float *ysh, hipStream_t s, Profiler *prof,
+                          const TermBufs &tb = TermBufs());
 
 // Weight-streaming kernels for experts with few tokens (k3moe_stream.hip).
 bool stream_path_ok(const LayerView &L);

@@ -6,16 +6,20 @@
 // weights, low nibble = even weight, scale byte 255 drops its group).
 //
 // Design (MI355X-first, not the README's CPU loop):
-//  * Expert weights go from HBM straight into the fp4 A operand of the
-//    scaled MFMA v_mfma_scale_f32_16x16x128_f8f6f4, in the storage layout:
-//    lane l of a wave takes 16 bytes = one 32-weight block of row (l % 16),
-//    K-block (l / 16), plus that block's E8M0 byte as the lane's A scale.
-//    Nothing is dequantised, nothing is repacked, no weight touches LDS.
-//  * Activations are the fp8 (e4m3) B operand, as a short expansion
-//    x = sum_t 2^(S_t) * q_t with one E8M0 scale per 32-element block per
-//    term (4 terms for a bf16 token vector and for an fp32 expert
-//    activation). Each term is a separate B column, so one MFMA yields every
-//    term's dot product and the terms are added in fp32 afterwards.
+//  * Single-token gate/up (k_gateup_dec): weights go from HBM straight into
+//    registers, lane l of a wave taking 16 bytes = one 32-weight block of
+//    row (l % 16), K-block (l / 16); they are expanded to bf16 in registers
+//    (v_cvt_scalef32_pk_bf16_fp4 applies the E8M0 scale exactly) and
+//    multiplied on v_mfma_f32_16x16x32_bf16 with the bf16 token (one or two
+//    planes) staged in LDS: every product exact, fp32 accumulation.
+//  * Single-token down (k_down_dec): the weight bytes are the fp4 A operand
+//    of the scaled MFMA v_mfma_scale_f32_16x16x128_f8f6f4 as loaded, the
+//    E8M0 byte the lane's A scale; nothing is dequantised or repacked and no
+//    weight touches LDS. The fp32 activation is the fp8 (e4m3) B operand as
+//    a short expansion a = sum_t 2^(S_t) * q_t with one E8M0 scale per
+//    32-element block per term (kATerms = 4 terms). Each term is a separate
+//    B column, so one MFMA yields every term's dot product and the terms are
+//    added in fp32 afterwards.
 //  * The fp8 B operand of this instruction holds, in lane group g = l / 16,
 //    K elements [16g, 16g+16) in bytes 0..15 and [64+16g, 64+16g+16) in
 //    bytes 16..31; its scale for K-block g comes from lane group g.
@@ -39,78 +43,6 @@
 
 namespace k3moe {
 namespace {
-
-// A lane's scale bytes for 4 consecutive K steps: from the 16 bytes holding
-// K-blocks 4s+g (step s, lane group g) of a row, byte g of each dword.
-__device__ __forceinline__ uint32_t gather_scales(u4 v, uint32_t grp)
-{
-    const uint32_t lo = __builtin_amdgcn_perm(v.y, v.x, grp | ((4u + grp) << 8) | 0x0c0c0000u);
-    const uint32_t hi = __builtin_amdgcn_perm(v.w, v.z, 0x00000c0cu | (grp << 16) | ((4u + grp) << 24));
-    return lo | hi;
-}
-
-// 0x80 in each byte of x that is 0xFF (E8M0 255), 0 elsewhere.
-__device__ __forceinline__ uint32_t ff_bytes(uint32_t x)
-{
-    const uint32_t y = ~x;
-    return ~(((y & 0x7f7f7f7fu) + 0x7f7f7f7fu) | y | 0x7f7f7f7fu);
-}
-
-__device__ __forceinline__ v8i a_operand(u4 v) { return v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0}; }
-
-__device__ __forceinline__ v8i b_operand(u4 lo, u4 hi)
-{
-    return v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-}
-
-// Maximum over the 8 lanes of each aligned lane octet (DPP: swap neighbours,
-// swap pairs, mirror the half-row).
-__device__ __forceinline__ float octet_max(float m)
-{
-    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0xb1, 0xf, 0xf, false)));
-    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x4e, 0xf, 0xf, false)));
-    m = fmaxf(m, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(m), 0x141, 0xf, 0xf, false)));
-    return m;
-}
-
-// Split this lane's 4 consecutive values into NT e4m3 terms; the 8 lanes of
-// an aligned octet hold one 32-element block and share one E8M0 scale per
-// term. The scale puts the block's largest remainder in [224, 448]; a term
-// takes only the elements within 6 binades of that maximum (the rest stay in
-// the remainder) and each term's rounding error is carried exactly into the
-// next term. code4[t] packs the 4 codes of term t, first value lowest.
-template <int NT>
-__device__ __forceinline__ void split_e4m3_octet(const float4 v, uint32_t (&code4)[NT], int (&sbyte)[NT])
-{
-    float r[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        const float m = octet_max(fmaxf(fmaxf(fabsf(r[0]), fabsf(r[1])), fmaxf(fabsf(r[2]), fabsf(r[3]))));
-        int S = 0;
-        float keep_min = INFINITY;
-        if (m > 0.0f) {
-            int ex;
-            frexpf(m, &ex);  // m in [2^(ex-1), 2^ex)
-            S = ex - 9;      // m / 2^S in [256, 512)
-            if (ldexpf(m, -S) > 448.0f) S += 1;
-            if (S < -127) S = -127;
-            frexpf(ldexpf(m, -S), &ex);
-            keep_min = ldexpf(1.0f, ex - 7);  // 6 binades below the block maximum
-        }
-        uint32_t c4 = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float q = ldexpf(r[i], -S);
-            if (fabsf(q) >= keep_min) {
-                const uint32_t c = __builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xffu;
-                r[i] -= ldexpf(__builtin_amdgcn_cvt_f32_fp8((int)c, 0), S);
-                c4 |= c << (8 * i);
-            }
-        }
-        code4[t] = c4;
-        sbyte[t] = S + 127;
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Router epilogue for one (token, expert): the fp32 logit, the fp32 score
@@ -502,9 +434,9 @@ struct GateUpParams {
 // gate and up, over the whole K range: 2 weight fragments per K step straight
 // from HBM into the MFMA A operand. A block of 4 waves runs 3 units (waves
 // 0..2) and a slice of the shared expert's rows (wave 3); with two blocks per
-// CU every CU moves the same bytes. The token's e4m3 terms and scales and the
-// units' E8M0 rows are staged in LDS once per block; K is walked in chunks of
-// 4 steps, double-buffered in registers. The activation is written in fp32
+// CU every CU moves the same bytes. The bf16 token planes and the units'
+// E8M0 rows are staged in LDS once per block; K is walked in chunks of 4
+// steps, double-buffered in registers. The activation is written in fp32
 // (act_f[slot][I]); the down kernel expands it into e4m3 terms.
 constexpr int kGuDecWaves = 4;                 // waves per block
 constexpr int kGuDecMaxUnits = 3;              // routed units per block (waves 0..UNITS-1), at most
@@ -1432,7 +1364,8 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const in
                                   reinterpret_cast<int2 *>(ws + lay.tiles_gu),
                                   reinterpret_cast<int2 *>(ws + lay.tiles_dn),
                                   reinterpret_cast<int32_t *>(ws + lay.light),
-                                  reinterpret_cast<int32_t *>(ws + lay.tile_n), ys, nullptr, s, prof);
+                                  reinterpret_cast<int32_t *>(ws + lay.tile_n), ys, nullptr, s, prof,
+                                  term_bufs(ws, lay));
     if (e != hipSuccess) return e;
     {
         StageMark m(prof, K3MOE_STAGE_COMBINE, s);

@@ -479,7 +479,7 @@ hipError_t launch_latent_forward(const LayerView &L, const uint16_t *x, int T, c
                            act_hi, act_lo, ash_hi, ash_lo, reinterpret_cast<float *>(ws + lay.sh_part),
                            reinterpret_cast<int2 *>(ws + lay.tiles_gu), reinterpret_cast<int2 *>(ws + lay.tiles_dn),
                            reinterpret_cast<int32_t *>(ws + lay.light), reinterpret_cast<int32_t *>(ws + lay.tile_n),
-                           ys, ysh, s, prof);
+                           ys, ysh, s, prof, term_bufs(ws, lay));
         ysh_slices = stream_shared_ok(L, T) ? stream_shared_down_slices(L.Lt, L.Is, T, L.I) : 1;
     }
     if (e != hipSuccess) return e;
