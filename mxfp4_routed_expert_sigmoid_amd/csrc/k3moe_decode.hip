@@ -4,10 +4,10 @@
 // experts already ship at half a byte": the MXFP4 format).
 //
 //   R  (k_router)            the router rows (logits, scores)
-//   G  (k_dec_gateup)        the shared expert's gate/up rows (blocks that
-//                            need no routes, first in the grid), then the
-//                            top-k and the routed experts' gate/up rows and
-//                            activations (written as e4m3 terms)
+//   G  (k_dec_gateup)        the top-k, the routed experts' gate/up rows
+//                            and activations (written as e4m3 terms), and
+//                            an equal share of the shared expert's rows in
+//                            every block
 //   D  (k_dec_down)          the shared expert's down rows, the routed
 //                            experts' down rows, the router-order weighted
 //                            sum, the output
@@ -91,22 +91,32 @@ __device__ __forceinline__ float diag_sum(const v4f acc)
 // ---------------------------------------------------------------------------
 // G: the routed experts' gate/up rows, one E8M0 block of a slot's activation
 // per 4-wave block: block q of slot j takes rows [32 q', 32 q' + 32) of gate
-// and up (q' = q mod I/32). Wave w streams ONE matrix (w & 1: gate, up) over
-// 16 rows (w >> 1: the first or second half), one weight stream per wave: on
-// MI355X a wave with one contiguous stream and two rows in flight keeps HBM
-// busier than one interleaving two streams. Each wave
-//  1. loads the token into registers at its lanes' K positions (lane l of
-//     row piece s: elements 2048 s + 32 l + [0, 32)),
-//  2. reads the slot's expert from the top-k that wave 0 takes from the
-//     router's scores (or from the ids given),
-//  3. stages its 16 E8M0 rows (contiguous) in LDS,
-//  4. streams its 16 rows, two in flight, each row piece as 4 bf16 MFMAs
-//     after an exact fp4 -> bf16 expansion (the diagonal dot product),
-//  5. parks its 16 sums in LDS; after the block barrier wave 0 takes the
-//     32 activations and splits them into 4 e4m3 terms with one E8M0 scale
-//     per term (the form the down kernel's scaled MFMA takes).
+// and up (q' = q mod I/32), and an equal share of the shared expert's row
+// pairs (pairs [Is q / NB, Is (q + 1) / NB) of the NB = K I / 32 blocks), so
+// every block streams the same bytes and the grid is one even round of
+// blocks (768 of 280 KB at the full shape, three per CU). Wave w streams ONE
+// matrix (w & 1: gate, up) over 16 routed rows (w >> 1: the first or second
+// half), one weight stream per wave: on MI355X a wave with one contiguous
+// stream and two rows in flight keeps HBM busier than one interleaving two
+// streams. Each wave
+//  1. stages the token in LDS with the block;
+//  2. issues the loads of its first shared row (row t = w, w + 4, ... of the
+//     block's 2P rows, gate and up of pair t / 2 alternating); wave 0 first
+//     takes the top-k from the router's scores (or reads the given ids);
+//  3. after the block barrier, finishes its shared rows (bf16 x bf16 fp32
+//     FMA in slice order, one wave-wide sum each, parked in LDS);
+//  4. takes the token from LDS into registers at its lanes' K positions
+//     (lane l of row piece s: elements 2048 s + 32 l + [0, 32)), stages its
+//     16 routed E8M0 rows (contiguous) in LDS and streams its 16 routed
+//     rows, two in flight, each row piece as 4 bf16 MFMAs after an
+//     exact fp4 -> bf16 expansion (the diagonal dot product);
+//  5. parks its 16 sums in LDS; after the block barrier wave 0 takes the 32
+//     routed activations and splits them into 4 e4m3 terms with one E8M0
+//     scale per term (the form the down kernel's scaled MFMA takes), and
+//     wave 1 writes the block's shared activations.
 constexpr int kDecGuPieces = 4;    // 1 KB pieces per row: H <= 8192
 constexpr int kDecUnitRows = 16;   // rows per wave
+constexpr int kDecShPairs = 64;    // shared row pairs per block, at most
 
 struct DecGuParams {
     const uint8_t *gp, *gs, *up, *us;
@@ -123,65 +133,15 @@ struct DecGuParams {
     uint8_t *as;                // their E8M0 scales [K][4][I / 32]
     const uint16_t *sh_gate, *sh_up;  // bf16 [Is][H]
     float *ash;                 // [Is] out: the shared expert's activation
-    int Is, nsh;                // shared row pairs; blocks given to them (first in the grid)
+    int Is;
 };
 
 // LDS: the 4 waves' E8M0 rows (16 x H/32 bytes each), the top-k scratch,
-// the expert id, the parked sums [4][16].
-__host__ __device__ constexpr int dec_gu_lds_bytes(int H) { return 4 * (H / 2) + (int)sizeof(TopkLds) + 16 + 4 * 16 * 4; }
-
-// A shared gate/up block: wave w takes row pair n = 4 b + w (gate row n, up
-// row n), both rows' loads issued together, the token read from LDS at the
-// same slice positions (lane l: elements 512 s + 8 l + [0, 8) of slice s);
-// fp32 products in slice order, one wave-wide sum per row, the activation
-// into ash.
-template <int NS>
-__device__ void dec_shared_gateup(const DecGuParams &p, int b, uint8_t *lds)
+// the expert id, the parked routed sums [4][16], the shared rows' sums
+// [2 kDecShPairs], the token as bf16 slices [NS][64] u4.
+__host__ __device__ constexpr int dec_gu_lds_bytes(int H, int NS)
 {
-    u4 *x_l = reinterpret_cast<u4 *>(lds);  // [NS][64]
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, H = p.H;
-    const int n = 4 * b + wave;
-    const bool live = n < p.Is;
-    const uint16_t *r0 = p.sh_gate + (size_t)(live ? n : 0) * H, *r1 = p.sh_up + (size_t)(live ? n : 0) * H;
-    u4 w0[NS], w1[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {  // the rows first: they are the block's bytes
-        const int i = 512 * s + 8 * lane;
-        const int ic = i < H ? i : 0;  // off lanes meet a zero token
-        w0[s] = ld16(r0 + ic);
-        w1[s] = ld16(r1 + ic);
-    }
-    constexpr int XQ = (NS * 64 + 255) / 256;
-    u4 xs[XQ];
-#pragma unroll
-    for (int q = 0; q < XQ; ++q) {
-        const int i = threadIdx.x + 256 * q;
-        const bool on = i < NS * 64 && 8 * i < H;
-        xs[q] = ld16m(p.x + (on ? 8 * i : 0), lane_mask(on));
-    }
-#pragma unroll
-    for (int q = 0; q < XQ; ++q) {
-        const int i = threadIdx.x + 256 * q;
-        if (i < NS * 64) x_l[i] = xs[q];
-    }
-    __syncthreads();
-    if (!live) return;
-    float g = 0.0f, u = 0.0f;
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-        const u4 xv = x_l[s * 64 + lane];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float xl = bf16f(xv[q] & 0xffffu), xh = bf16f(xv[q] >> 16);
-            g = fmaf(bf16f(w0[s][q] & 0xffffu), xl, g);
-            g = fmaf(bf16f(w0[s][q] >> 16), xh, g);
-            u = fmaf(bf16f(w1[s][q] & 0xffffu), xl, u);
-            u = fmaf(bf16f(w1[s][q] >> 16), xh, u);
-        }
-    }
-    g = wave_sum(g);
-    u = wave_sum(u);
-    if (lane == 0) p.ash[n] = act_fn(g, u, p.act, p.b1, p.b2);
+    return 4 * (H / 2) + (int)sizeof(TopkLds) + 16 + 4 * 16 * 4 + 2 * kDecShPairs * 4 + NS * 64 * 16;
 }
 
 // Split the activations held by lanes 0..31 (one E8M0 block) into 4 e4m3
@@ -222,16 +182,13 @@ __device__ __forceinline__ void split_terms_32(float r, uint8_t *term, size_t te
 }
 
 // NQ > 0: wave 0 takes the top-k here (16-byte score loads, NQ experts per
-// lane); NQ == 0: the ids are read from p.idx.
+// lane); NQ == 0: the ids are read from p.idx. NS: 512-element slices of a
+// shared row (H <= 512 NS).
 template <int NQ, int NS>
 __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
 {
     extern __shared__ __align__(16) uint8_t lds[];
-    if ((int)blockIdx.x < p.nsh) {
-        dec_shared_gateup<NS>(p, blockIdx.x, lds);
-        return;
-    }
-    const int bid = blockIdx.x - p.nsh;
+    const int bid = blockIdx.x, nb = gridDim.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int H = p.H, HB = H >> 1, HG = H >> 5;  // packed bytes and E8M0 groups per row
     const int NG = p.I >> 5;                      // E8M0 blocks per slot activation
@@ -241,18 +198,44 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
     TopkLds &tl = *reinterpret_cast<TopkLds *>(lds + 2 * H);
     int *e_l = reinterpret_cast<int *>(lds + 2 * H + sizeof(TopkLds));
     float *sum_l = reinterpret_cast<float *>(lds + 2 * H + sizeof(TopkLds) + 16);  // [4][16]
+    float *shs_l = sum_l + 4 * kDecUnitRows;                                      // [2 kDecShPairs]
+    u4 *x_l = reinterpret_cast<u4 *>(shs_l + 2 * kDecShPairs);                    // [NS][64]
 
-    // 1. the token at this lane's K positions
-    u4 xv[kDecGuPieces][4];
+    // 1. the token in LDS (u4 i: elements 8i .. 8i + 7, zero past H)
+    constexpr int XQ = (NS * 64 + 255) / 256;
+    {
+        u4 xs[XQ];
 #pragma unroll
-    for (int s = 0; s < kDecGuPieces; ++s)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int i = 2048 * s + 32 * lane + 8 * c;
-            xv[s][c] = ld16m(p.x + (i < H ? i : 0), lane_mask(i < H));
+        for (int q = 0; q < XQ; ++q) {
+            const int i = threadIdx.x + 256 * q;
+            const bool on = i < NS * 64 && 8 * i < H;
+            xs[q] = ld16m(p.x + (on ? 8 * i : 0), lane_mask(on));
         }
+#pragma unroll
+        for (int q = 0; q < XQ; ++q) {
+            const int i = threadIdx.x + 256 * q;
+            if (i < NS * 64) x_l[i] = xs[q];
+        }
+    }
 
-    // 2. the slot's expert
+    // 2. this block's shared rows: pairs [sp0, sp1), row t = pair sp0 + t/2 of
+    // gate (t even) or up (t odd); wave w takes rows w, w + 4, ...
+    const int sp0 = (int)((int64_t)p.Is * bid / nb), sp1 = (int)((int64_t)p.Is * (bid + 1) / nb);
+    const int nsr = 2 * (sp1 - sp0);
+    auto sh_row = [&](int t) {
+        const int n = sp0 + (t >> 1);
+        return ((t & 1) ? p.sh_up : p.sh_gate) + (size_t)n * H;
+    };
+    u4 shw[NS];
+    auto sh_load = [&](int t) {
+        const uint16_t *r = sh_row(t < nsr ? t : 0);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int i = 512 * s + 8 * lane;
+            shw[s] = ld16(r + (i < H ? i : 0));  // off lanes meet a zero token
+        }
+    };
+    if (wave != 0 && wave < nsr) sh_load(wave);
     if constexpr (NQ > 0) {
         if (wave == 0) {
             int pick;
@@ -264,16 +247,45 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
             }
             if (lane == 0) e_l[0] = __builtin_amdgcn_readlane(pick, j);
         }
-        __syncthreads();
     } else {
         if (threadIdx.x == 0) e_l[0] = p.idx[j];
-        __syncthreads();
     }
+    if (wave == 0 && nsr > 0) sh_load(0);
+    __syncthreads();  // the token slices and the expert id
+
+    // 3. the shared rows
+    for (int t = wave; t < nsr; t += 4) {
+        if (t != wave) sh_load(t);
+        float a = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const u4 xq = x_l[s * 64 + lane];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                a = fmaf(bf16f(shw[s][q] & 0xffffu), bf16f(xq[q] & 0xffffu), a);
+                a = fmaf(bf16f(shw[s][q] >> 16), bf16f(xq[q] >> 16), a);
+            }
+        }
+        a = wave_sum(a);
+        if (lane == 0) shs_l[t] = a;
+    }
+
     int e = e_l[0];
     const bool ok = e >= 0 && e < p.E;  // an invalid id: zero activations (the down kernel drops it)
     e = ok ? e : 0;
 
-    // 3. this wave's 16 E8M0 rows (contiguous: 16 x H/32 bytes)
+    // 4. the token at this lane's K positions (lane l of row piece s:
+    // elements 2048 s + 32 l + [0, 32)), from LDS
+    u4 xv[kDecGuPieces][4];
+#pragma unroll
+    for (int s = 0; s < kDecGuPieces; ++s)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int i = 2048 * s + 32 * lane + 8 * c;
+            xv[s][c] = ld16m(x_l + (i < H ? i / 8 : 0), lane_mask(i < H));
+        }
+
+    // this wave's 16 E8M0 rows (contiguous: 16 x H/32 bytes)
     const int row0 = 32 * qb + kDecUnitRows * half;
     const uint8_t *sbase = (mat ? p.us + (int64_t)e * p.u_ss : p.gs + (int64_t)e * p.g_ss) + (size_t)row0 * HG;
     const uint8_t *wbase = (mat ? p.up + (int64_t)e * p.u_sp : p.gp + (int64_t)e * p.g_sp) + (size_t)row0 * HB;
@@ -285,7 +297,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
         scv[k] = ld16(sbase + (i < H / 2 ? i : 0));
     }
 
-    // 4. the rows, two in flight (named buffers, so the compiler's wait
+    // the rows, two in flight (named buffers, so the compiler's wait
     // counts follow the rotation); row r's sum is parked in lane r
     int soff[kDecGuPieces];        // this lane's offset in a row piece (off lanes: 0)
     int gidx[kDecGuPieces];        // this lane's E8M0 group (off lanes: 0)
@@ -335,13 +347,16 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
     if (lane < kDecUnitRows) sum_l[wave * kDecUnitRows + lane] = mine;
     __syncthreads();
 
-    // 5. wave 0: the 32 activations (lane l: row 32 qb + l) as e4m3 terms
+    // 5. wave 0: the 32 activations (lane l: row 32 qb + l) as e4m3 terms;
+    // wave 1: the block's shared activations
     if (wave == 0) {
         const int hl = (lane >> 4) & 1, rl = lane & 15;  // lanes 32..63 repeat 0..31 (unused)
         const float g = sum_l[(2 * hl) * kDecUnitRows + rl], u = sum_l[(2 * hl + 1) * kDecUnitRows + rl];
         const float a = ok ? act_fn(g, u, p.act, p.b1, p.b2) : 0.0f;
         split_terms_32(lane < 32 ? a : 0.0f, p.aq + ((size_t)j * kATerms) * p.I + (size_t)qb * 32, p.I,
                        p.as + ((size_t)j * kATerms) * NG + qb, NG);
+    } else if (wave == 1 && 2 * lane < nsr) {
+        p.ash[sp0 + lane] = act_fn(shs_l[2 * lane], shs_l[2 * lane + 1], p.act, p.b1, p.b2);
     }
 }
 
@@ -538,7 +553,8 @@ __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
 bool decode_fused_ok(const LayerView &L)
 {
     return L.Lt == 0 && L.H <= 8192 && L.H % 128 == 0 && L.I <= 2048 && L.I % 128 == 0 && L.Is <= 2048 &&
-           L.K <= 2 * kDecDnWaves && L.E <= kMaxExperts && 32 * L.H >= L.I;
+           L.K <= 2 * kDecDnWaves && L.E <= kMaxExperts && 32 * L.H >= L.I &&
+           L.Is <= kDecShPairs * L.K * (L.I / 32);  // a block's share of the shared rows fits its LDS
 }
 
 // Workspace use (the T = 1 layout): sc, ch; ash; the e4m3 terms in act
@@ -598,10 +614,9 @@ hipError_t launch_decode_fused(const LayerView &L, const uint16_t *x, int32_t *i
         gp.sh_up = L.sh_up;
         gp.ash = ash;
         gp.Is = L.Is;
-        gp.nsh = (L.Is + 3) / 4;
-        const unsigned nb = (unsigned)(gp.nsh + L.K * (L.I / 32));
+        const unsigned nb = (unsigned)(L.K * (L.I / 32));
         const int NS = L.H <= 2048 ? 4 : L.H <= 4096 ? 8 : L.H <= 7168 ? 14 : 16;
-        const size_t lds = std::max<size_t>(dec_gu_lds_bytes(L.H), (size_t)NS * 64 * 16);
+        const size_t lds = dec_gu_lds_bytes(L.H, NS);
 #define K3_GU(NQ, NSL) k_dec_gateup<NQ, NSL><<<nb, 256, lds, s>>>(gp)
         if (fused_topk) {
             if (NS == 4) K3_GU(16, 4); else if (NS == 8) K3_GU(16, 8); else if (NS == 14) K3_GU(16, 14); else K3_GU(16, 16);
