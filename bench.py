@@ -418,8 +418,8 @@ def main():
 def measured_traffic(kernel):
     """HBM bytes per dispatch of `kernel` from the committed rocprofv3 counter
     runs (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for
-    a copy of known size), or None when no such run exists or the kernel
-    source has changed since it was taken."""
+    a copy of known size), or None when no such run exists or the kernel's
+    source file has changed since it was taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "decode_T1_pmc_traffic.json")
     if not os.path.exists(path):
@@ -427,10 +427,13 @@ def measured_traffic(kernel):
     with open(path) as f:
         rec = json.load(f)
     k = rec.get("kernels", {}).get(kernel)
-    if k is None:
+    if k is None or "source" not in k or "source_sha256" not in k:
         return None
-    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != rec["kernel_source_sha256"]:
+    src = os.path.join(ROOT, k["source"])
+    if not os.path.exists(src):
+        return None
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != k["source_sha256"]:
             return None
     return k["hbm_bytes"]
 
