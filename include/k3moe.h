@@ -211,7 +211,7 @@ k3moe_status k3moe_route_forward(const k3moe_layer *layer, const uint16_t *x, in
  * allocates nothing (no hipMalloc, no event, no library allocation) and
  * takes no workspace argument.
  *   T whose workspace (k3moe_workspace_size) exceeds 64 MiB is refused with
- *   K3MOE_E_WORKSPACE before any launch (about 100 tokens at hidden 7168,
+ *   K3MOE_E_WORKSPACE before any launch (71 tokens at hidden 7168,
  *   top-16, inter 1536).
  *   Every call on one GPU shares that GPU's array: calls that overlap on one
  *   GPU (on different streams, or from different threads or layers) race.
