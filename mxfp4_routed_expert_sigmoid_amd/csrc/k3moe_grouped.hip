@@ -169,7 +169,10 @@ struct GemmParams {
     // f8 down tiles: the activation as e4m3 terms [row][NPL][KD] and their
     // E8M0 bytes [row][NPL][KD / 32] (row: the sorted assignment)
     const uint8_t *bq, *bsc;
-    int sh_blocks;             // leading blocks that run the shared expert
+    int sh_blocks;             // leading blocks that run the shared expert, on:
+    int sh_rows, sh_KD;        //   its weight rows (I_s or H) and reduction length (H or I_s),
+    const uint16_t *sh_bp[2];  //   its token planes [T][sh_KD] (x, or the activation's hi and lo),
+    uint16_t *sh_ohi, *sh_olo; //   its activation outputs (gate/up)
     uint16_t *ohi, *olo;       // gate/up: activation hi/lo [row][rows] (null: not written)
     uint8_t *oq, *osc;         // gate/up: activation as kATerms e4m3 terms [row][kATerms][rows]
                                // and E8M0 bytes [row][kATerms][rows / 32] (null: not written)
@@ -626,9 +629,19 @@ __global__ __launch_bounds__(64 * GemmShape<KIND>::WAVES) void k_gemm(GemmParams
     const int RB = (p.rows + kTileRows - 1) / kTileRows;
     int b = blockIdx.x;
     if (!F8 && b < p.sh_blocks) {
-        // shared expert: rows of I_s (gate/up) or H (down); p.rows/KD already
-        // describe the shared matrices when sh_blocks > 0 in a shared launch
-        const int tile = b / RB, rb = b - tile * RB;
+        // the shared expert's tiles (bf16 weights p.wb, tokens in order), on
+        // their own rows, reduction length, token planes and outputs
+        GemmParams q = p;
+        q.rows = p.sh_rows;
+        q.KD = p.sh_KD;
+        q.bp[0] = p.sh_bp[0];
+        q.bp[1] = p.sh_bp[1];
+        q.ohi = p.sh_ohi;
+        q.olo = p.sh_olo;
+        q.oq = nullptr;
+        q.osc = nullptr;
+        const int RBs = (q.rows + kTileRows - 1) / kTileRows;
+        const int tile = b / RBs, rb = b - tile * RBs;
         const int p0 = tile * S::TOK, n = min(S::TOK, p.T - p0);
         for (int c = threadIdx.x; c < S::TOK; c += 64 * S::WAVES) {
             const int t = p0 + min(c, n - 1);
@@ -636,7 +649,7 @@ __global__ __launch_bounds__(64 * GemmShape<KIND>::WAVES) void k_gemm(GemmParams
             oro_l[c] = GU ? t : t * (p.K + 1) + p.K;
         }
         __syncthreads();
-        if constexpr (!F8) gemm_tile<KIND, false>(p, 0, rb, p0, n, bro_l, oro_l, B_l);
+        if constexpr (!F8) gemm_tile<KIND, false>(q, 0, rb, p0, n, bro_l, oro_l, B_l);
         return;
     }
     b -= p.sh_blocks;
@@ -763,26 +776,35 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t 
         gp.olo = hilo_from_tiles ? act_lo : nullptr;
         gp.oq = f8_dn ? tb.aq : nullptr;
         gp.osc = f8_dn ? tb.aqs : nullptr;
+        // the shared expert's gate/up tiles: in the routed tiles' launch when
+        // both are one bf16 token plane (its long blocks first in the grid,
+        // beside the routed ones), else in a launch of their own
+        const bool sh_tiles = L.Is > 0 && !sh_stream;
+        const bool sh_merged = sh_tiles && gemm_gu && !two;
+        if (sh_tiles) {
+            gp.wb[0] = L.sh_gate;
+            gp.wb[1] = L.sh_up;
+            gp.sh_rows = L.Is;
+            gp.sh_KD = L.H;
+            gp.sh_bp[0] = gp.sh_bp[1] = x;
+            gp.sh_ohi = ash_hi;
+            gp.sh_olo = ash_lo;
+        }
+        const int sh_blocks = sh_tiles ? ((T + TGS - 1) / TGS) * rb_s : 0;
         if (gemm_gu) {
             StageMark mt(prof, K3MOE_STAGE_GATEUP_TILES, s);
             if (two) {
                 k_gemm<kGU2><<<(unsigned)(cap_gu * rb_i), 64 * GemmShape<kGU2>::WAVES, gemm_lds_bytes<kGU2>(), s>>>(gp);
             } else {
-                k_gemm<kGU><<<(unsigned)(cap_gu * rb_i), 64 * GemmShape<kGU>::WAVES, gemm_lds_bytes<kGU>(), s>>>(gp);
+                gp.sh_blocks = sh_merged ? sh_blocks : 0;
+                k_gemm<kGU><<<(unsigned)(gp.sh_blocks + cap_gu * rb_i), 64 * GemmShape<kGU>::WAVES,
+                               gemm_lds_bytes<kGU>(), s>>>(gp);
             }
         }
-        if (L.Is > 0 && !sh_stream) {
+        if (sh_tiles && !sh_merged) {
             StageMark m2(prof, K3MOE_STAGE_SHARED_GATEUP, s);
             GemmParams sp = gp;
-            sp.oq = sp.osc = nullptr;
-            sp.rows = L.Is;
-            sp.KD = L.H;
-            sp.bp[0] = sp.bp[1] = x;
-            sp.wb[0] = L.sh_gate;
-            sp.wb[1] = L.sh_up;
-            sp.ohi = ash_hi;
-            sp.olo = ash_lo;
-            sp.sh_blocks = ((T + TGS - 1) / TGS) * rb_s;
+            sp.sh_blocks = sh_blocks;
             k_gemm<kGU><<<(unsigned)sp.sh_blocks, 64 * GemmShape<kGU>::WAVES, gemm_lds_bytes<kGU>(), s>>>(sp);
         }
     }
@@ -824,13 +846,13 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t 
         if (L.Is > 0 && !sh_stream) {
             // shared rows of H: to slot k of ys (flat), or to ysh [T][H] (K = 0 makes the row t)
             GemmParams sp = dp;
-            sp.rows = L.H;
-            sp.KD = L.Is;
+            sp.sh_rows = L.H;
+            sp.sh_KD = L.Is;
             sp.K = ysh ? 0 : L.K;
             sp.ys = ysh ? ysh : ys;
             sp.wb[0] = sp.wb[1] = L.sh_down;
-            sp.bp[0] = ash_hi;
-            sp.bp[1] = ash_lo;
+            sp.sh_bp[0] = ash_hi;
+            sp.sh_bp[1] = ash_lo;
             sp.sh_blocks = ((T + TD - 1) / TD) * rb_h;
             k_gemm<kDN><<<(unsigned)sp.sh_blocks, 64 * GemmShape<kDN>::WAVES, gemm_lds_bytes<kDN>(), s>>>(sp);
         }

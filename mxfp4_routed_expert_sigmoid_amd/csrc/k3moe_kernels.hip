@@ -995,7 +995,7 @@ __global__ __launch_bounds__(64 * kDnDecWaves) void k_down_dec(DownDecParams p)
 // A slot with an out-of-range id adds nothing (its staging row is loaded but
 // dropped) and is counted once here. A thread takes 4 consecutive outputs
 // (16-byte loads); the loads of up to 16 slots are issued before the first fma.
-constexpr int kCombineThreads = 64;
+constexpr int kCombineThreads = 256;
 __global__ __launch_bounds__(kCombineThreads) void k_combine(const float *__restrict__ ys,
                                                              const float *__restrict__ w,
                                                              const int32_t *__restrict__ idx, int T, int K,
