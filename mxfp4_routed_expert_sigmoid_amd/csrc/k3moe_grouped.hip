@@ -128,14 +128,16 @@ __global__ __launch_bounds__(1024) void k_tiles(const int32_t *__restrict__ acti
 // gate/up on tokens given as hi and lo (a latent layer's fp32 z).
 constexpr int kGU = 0, kDN = 1, kGU2 = 2;
 template <int KIND> struct GemmShape;
+// MINB: blocks per CU the kernel is built for (registers at most 512 / (4 waves
+// per SIMD / ... ) per lane)
 template <> struct GemmShape<kGU> {   // gate/up: 8 waves x 32 rows, 128 tokens
-    static constexpr int WAVES = 8, RF = 2, TF = 8, NMAT = 2, NPL = 1, TOK = 128;
+    static constexpr int WAVES = 8, RF = 2, TF = 8, NMAT = 2, NPL = 1, TOK = 128, MINB = 1;
 };
 template <> struct GemmShape<kDN> {   // down: 4 waves x 64 rows, 64 tokens (hi, lo)
-    static constexpr int WAVES = 4, RF = 4, TF = 4, NMAT = 1, NPL = 2, TOK = 64;
+    static constexpr int WAVES = 4, RF = 4, TF = 4, NMAT = 1, NPL = 2, TOK = 64, MINB = 1;
 };
 template <> struct GemmShape<kGU2> {  // gate/up, tokens as hi and lo: 8 waves x 32 rows, 64 tokens
-    static constexpr int WAVES = 8, RF = 2, TF = 4, NMAT = 2, NPL = 2, TOK = 64;
+    static constexpr int WAVES = 8, RF = 2, TF = 4, NMAT = 2, NPL = 2, TOK = 64, MINB = 1;
 };
 // The down tile on the scaled MFMA v_mfma_scale_f32_16x16x128_f8f6f4: the
 // fp4 weights go in as loaded (A operand, the E8M0 byte as the lane's A
@@ -143,14 +145,17 @@ template <> struct GemmShape<kGU2> {  // gate/up, tokens as hi and lo: 8 waves x
 // E8M0 bytes), one MFMA per term into the same accumulator.
 constexpr int kDN8 = 4;
 template <> struct GemmShape<kDN8> {   // down: 4 waves x 64 rows, 64 tokens, the activation as kATerms terms
-    static constexpr int WAVES = 4, RF = 4, TF = 4, NMAT = 1, NPL = kATerms, TOK = 64;
+    static constexpr int WAVES = 4, RF = 4, TF = 4, NMAT = 1, NPL = kATerms, TOK = 64, MINB = 1;
 };
-constexpr int kTileRows = 256;  // weight rows per block (every shape)
-static_assert(GemmShape<kGU>::WAVES * GemmShape<kGU>::RF * 16 == kTileRows, "gate/up tile rows");
-static_assert(GemmShape<kDN>::WAVES * GemmShape<kDN>::RF * 16 == kTileRows, "down tile rows");
-static_assert(GemmShape<kGU2>::WAVES * GemmShape<kGU2>::RF * 16 == kTileRows, "gate/up tile rows");
-static_assert(GemmShape<kDN8>::WAVES * GemmShape<kDN8>::RF * 16 == kTileRows, "down tile rows");
+// weight rows per block: waves x 16-row fragments per wave x 16
+template <int KIND>
+__host__ __device__ constexpr int tile_rows()
+{
+    return GemmShape<KIND>::WAVES * GemmShape<KIND>::RF * 16;
+}
 static_assert(GemmShape<kDN8>::TOK == GemmShape<kDN>::TOK, "one tile list serves both down forms");
+static_assert(tile_rows<kGU>() == tile_rows<kGU2>() && tile_rows<kDN>() == tile_rows<kDN8>(),
+              "one row-block count per projection");
 constexpr int kB8Row = 128 + 16;  // LDS bytes per term row per chunk (128 e4m3 codes + padding)
 
 struct GemmParams {
@@ -303,8 +308,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &p, int e, int rb, in
     constexpr int BBUF = NPL * TOK * BROW;
     const int KD = p.KD, rows = p.rows, NCH = KD / KC;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
-    const int nrows = min(kTileRows, rows - rb * kTileRows);
-    const int row0 = rb * kTileRows + wave * RF * 16;
+    constexpr int TR = tile_rows<KIND>();
+    const int nrows = min(TR, rows - rb * TR);
+    const int row0 = rb * TR + wave * RF * 16;
     const int ntf = wave * RF * 16 < nrows ? (n + 15) / 16 : 0;  // token fragments with data
 
     // weight rows: a uniform base per matrix and 32-bit per-lane offsets
@@ -475,8 +481,9 @@ __device__ __forceinline__ void gemm_tile_f8(const GemmParams &p, int e, int rb,
     constexpr int SOFF = NTB * TOK * kB8Row;     // scale words after the term rows
     const int KD = p.KD, rows = p.rows, NCH = KD / KC;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, l16 = lane & 15;
-    const int nrows = min(kTileRows, rows - rb * kTileRows);
-    const int row0 = rb * kTileRows + wave * RF * 16;
+    constexpr int TR = tile_rows<KIND>();
+    const int nrows = min(TR, rows - rb * TR);
+    const int row0 = rb * TR + wave * RF * 16;
     const int ntf = wave * RF * 16 < nrows ? (n + 15) / 16 : 0;
 
     const uint32_t rowb = (uint32_t)KD / 2;
@@ -617,7 +624,7 @@ __device__ __forceinline__ void gemm_tile_f8(const GemmParams &p, int e, int rb,
 // One launch: the shared expert's tiles first (bf16 weights, tokens in
 // order), then the routed tiles from the list (fp4 weights).
 template <int KIND>
-__global__ __launch_bounds__(64 * GemmShape<KIND>::WAVES) void k_gemm(GemmParams p)
+__global__ __launch_bounds__(64 * GemmShape<KIND>::WAVES, GemmShape<KIND>::MINB) void k_gemm(GemmParams p)
 {
     using S = GemmShape<KIND>;
     constexpr bool F8 = KIND == kDN8;
@@ -626,7 +633,8 @@ __global__ __launch_bounds__(64 * GemmShape<KIND>::WAVES) void k_gemm(GemmParams
     uint8_t *B_l = lds;
     int *bro_l = reinterpret_cast<int *>(lds + gemm_tok_bytes<KIND>());  // token side row per column
     int *oro_l = bro_l + S::TOK;                                         // output row per column
-    const int RB = (p.rows + kTileRows - 1) / kTileRows;
+    constexpr int TR = tile_rows<KIND>();
+    const int RB = (p.rows + TR - 1) / TR;
     int b = blockIdx.x;
     if (!F8 && b < p.sh_blocks) {
         // the shared expert's tiles (bf16 weights p.wb, tokens in order), on
@@ -640,7 +648,7 @@ __global__ __launch_bounds__(64 * GemmShape<KIND>::WAVES) void k_gemm(GemmParams
         q.olo = p.sh_olo;
         q.oq = nullptr;
         q.osc = nullptr;
-        const int RBs = (q.rows + kTileRows - 1) / kTileRows;
+        const int RBs = (q.rows + TR - 1) / TR;
         const int tile = b / RBs, rb = b - tile * RBs;
         const int p0 = tile * S::TOK, n = min(S::TOK, p.T - p0);
         for (int c = threadIdx.x; c < S::TOK; c += 64 * S::WAVES) {
@@ -717,9 +725,11 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t 
     const bool two = xr_lo != nullptr;  // routed tokens as hi and lo planes
     const int TG = two ? GemmShape<kGU2>::TOK : GemmShape<kGU>::TOK, TD = GemmShape<kDN>::TOK;
     constexpr int TGS = GemmShape<kGU>::TOK;  // the shared expert's gate/up tiles
-    const int rb_i = (L.I + kTileRows - 1) / kTileRows, rb_h = (L.H + kTileRows - 1) / kTileRows;
-    const int rb_r = (L.EK + kTileRows - 1) / kTileRows;  // routed down rows
-    const int rb_s = (L.Is + kTileRows - 1) / kTileRows;
+    auto blocks = [](int rows, int tr) { return (rows + tr - 1) / tr; };
+    const int rb_i = blocks(L.I, tile_rows<kGU>());    // gate/up rows (every gate/up kind: the same rows per block)
+    const int rb_h = blocks(L.H, tile_rows<kDN>());    // the shared expert's down rows
+    const int rb_r = blocks(L.EK, tile_rows<kDN>());   // routed down rows (every down kind)
+    const int rb_s = blocks(L.Is, tile_rows<kGU>());   // the shared expert's gate/up rows
     const bool stream = stream_path_ok(L), stream_dn = stream_down_ok(L, T);
     const bool sh_stream = stream_shared_ok(L, T);
     const int smax_gu = stream ? stream_max_tokens() : 0, smax_dn = stream_dn ? stream_down_rows(L, T) : 0;
