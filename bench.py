@@ -59,6 +59,7 @@ STEP_EPS = 1e-5  # the pre-MoE norm's epsilon (the pages' rms_eps)
 STREAM_MAX_TOKENS = 16  # experts with more assignments go to the tile GEMMs
 BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA
 MXFP4_PEAK_TFLOPS = 10100.0  # dense MXFP4 MFMA
+FP8_PEAK_TFLOPS = 5000.0    # dense fp8 MFMA (the rate of an fp4 x fp8 scaled MFMA)
 EXPERT_MATRIX_BYTES = None  # filled from the spec
 
 
@@ -306,16 +307,24 @@ def main():
                          else dict(one_tok, prenorm="k_prenorm") if per_token
                          else {"gateup": "k_gu_stream", "down": "k_dn_stream", "prenorm": "k_prenorm"})}[args.workload]
     # the hot experts' tile GEMMs: algorithmic flops (2 per multiply-add,
-    # gate and up, per assignment) and issued flops (whole token tiles; the
-    # down tiles multiply the activation's hi and lo planes)
+    # gate and up, per assignment) and issued flops (whole token tiles). A flat
+    # layer's shared gate/up tiles run in the same launch once the shared
+    # expert leaves the streaming kernels (T > 128): their flops count too.
+    # The routed down tiles multiply four e4m3 terms of the activation (a
+    # latent layer's: bf16 hi and lo).
     tile_tok_gu = 64 if Lt else 128
+    sh_in_tiles = not Lt and Is > 0 and T > 128
+    dn_terms = 2 if Lt else 4
     mf = {"alg_gu": 0.0, "iss_gu": 0.0, "alg_dn": 0.0, "iss_dn": 0.0}
     for i in range(args.steps):
         c = heavy[i % pool]
         mf["alg_gu"] += c.sum() * 2 * 2 * I * EKw
         mf["iss_gu"] += (np.ceil(c / tile_tok_gu) * tile_tok_gu).sum() * 2 * 2 * I * EKw * (2 if Lt else 1)
+        if sh_in_tiles and c.size:
+            mf["alg_gu"] += T * 2 * 2 * Is * H
+            mf["iss_gu"] += np.ceil(T / 128) * 128 * 2 * 2 * Is * H
         mf["alg_dn"] += c.sum() * 2 * EKw * I
-        mf["iss_dn"] += (np.ceil(c / 64) * 64).sum() * 2 * EKw * I * 2
+        mf["iss_dn"] += (np.ceil(c / 64) * 64).sum() * 2 * EKw * I * dn_terms
     mf = {k: v / args.steps / nl for k, v in mf.items()}
     dom = max(stage_bytes, key=lambda s: stage_us.get(s, 0.0))
     dom_us = stage_us.get(dom, 0.0)
@@ -380,13 +389,15 @@ def main():
     if mf["alg_gu"] > 0 and stage_us.get("gateup_tiles", 0) > 0:
         tu, td = stage_us["gateup_tiles"] * 1e-6, max(stage_us.get("down_tiles", 0), 1e-9) * 1e-6
         result["mfma"] = {
-            "kernel": "k_gemm gate/up tiles (experts with > 16 assignments)",
+            "kernel": "k_gemm gate/up tiles (experts with > 16 assignments"
+                      + (", and the shared expert's)" if sh_in_tiles else ")"),
             "alg_TFLOPs": round(mf["alg_gu"] / tu / 1e12, 2),
             "issued_TFLOPs": round(mf["iss_gu"] / tu / 1e12, 2),
             "alg_frac_of_mxfp4_peak": round(mf["alg_gu"] / tu / 1e12 / MXFP4_PEAK_TFLOPS, 4),
             "issued_frac_of_bf16_peak": round(mf["iss_gu"] / tu / 1e12 / BF16_PEAK_TFLOPS, 4),
             "down_alg_TFLOPs": round(mf["alg_dn"] / td / 1e12, 2),
-            "down_issued_frac_of_bf16_peak": round(mf["iss_dn"] / td / 1e12 / BF16_PEAK_TFLOPS, 4),
+            ("down_issued_frac_of_bf16_peak" if Lt else "down_issued_frac_of_fp8_peak"):
+                round(mf["iss_dn"] / td / 1e12 / (BF16_PEAK_TFLOPS if Lt else FP8_PEAK_TFLOPS), 4),
             "tile_us": [round(stage_us["gateup_tiles"], 2), round(stage_us.get("down_tiles", 0.0), 2)],
         }
         if args.workload == "prefill":   # the dominant kernel is the hot experts' gate/up tiles
