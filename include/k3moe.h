@@ -16,7 +16,9 @@
  * up-projection, with an RMSNorm on their aggregate).
  *
  * Per token x (bf16, hidden H):
- *   route:   logit[e] = Wr[e] . x                (exact products, fp64 sum)
+ *   route:   logit[e] = Wr[e] . x                (exact products, fp64 sum;
+ *                                                 T > 4: fp32 sums of runs of
+ *                                                 32 products, added in fp64)
  *            sc[e] = fp32(sigmoid(fp32(logit[e])))   unbiased score
  *            ch[e] = sc[e] + bias[e]  (fp32)          selection score
  *            idx[0..k) = the k largest ch, largest first, equal ch -> lower e

@@ -56,9 +56,9 @@ WsLayout ws_layout(const k3moe_config &c, int64_t T)
     {
         // a call may take fewer tokens than the workspace was sized for, and
         // the slice count falls as T grows: the largest partial buffer over
-        // every T' <= T (no batch of more than 64 * 512 tokens is sliced)
+        // every T' <= T (no batch of more than 128 * 512 tokens is sliced: 512 tiles of 128)
         size_t part = 0;
-        for (int64_t t = kRouterWaveMaxT + 1; t <= std::min<int64_t>(T, 64 * 512); ++t) {
+        for (int64_t t = kRouterWaveMaxT + 1; t <= std::min<int64_t>(T, 128 * 512); ++t) {
             const int S = router_splits(t, (int)E, (int)H);
             if (S > 1) part = std::max(part, sizeof(double) * S * t * E);
         }

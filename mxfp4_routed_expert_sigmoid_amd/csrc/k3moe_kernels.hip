@@ -99,81 +99,130 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t *__restrict__ x,
     if (lane == 0) router_finish(acc, t, e, E, bias, sc, ch, logits);
 }
 
-// Batched router: logits = Wr X^T on the fp64 MFMA v_mfma_f64_16x16x4_f64
-// (bf16 inputs converted exactly to fp64, fp64 accumulation), so each logit
-// is an fp64 sum of the exact products, as in the one-wave kernel above. A
-// block of 4 waves takes 64 experts x 64 tokens over one slice of the hidden
-// dimension (the grid's z); each wave a 32 x 32 tile (2 x 2 MFMA tiles).
-// Within a 32-element chunk the lane group g (lanes 16g..16g+15) carries the
-// elements 8g..8g+7, one per MFMA step, so one 16-byte load per lane and
-// operand covers the chunk; the summation order is immaterial to an fp64 sum
-// of this kind up to its rounding. One slice: finished in place; several:
+// Batched router: logits = Wr X^T. Each 32-element chunk of the hidden
+// dimension is one v_mfma_f32_16x16x32_bf16 per 16 x 16 tile, started from
+// zero: its 32 bf16 products are exact in fp32 and the instruction sums them
+// in fp32; the chunk sums are then added in fp64, in chunk order. The logit
+// is therefore the fp64 sum of fp32 sums of 32 exact products each, not of
+// the products themselves: on N(0,1) tokens and N(0, 1/H) router rows at
+// H = 7168 it stays within about 2^-22 of the exact sum, far inside the
+// selection-score margin the routes are compared with.
+// A block takes 128 experts x 32 WT tokens over one slice of the hidden
+// dimension (the grid's z), 64 elements per stage: the stage's rows (experts
+// first, then tokens) go through double-buffered LDS, eight threads per
+// row's 128 bytes, so every row is read from the caches once per block.
+// Wave (we, wt) computes experts 32 we .. 32 we + 31 of tokens 32 wt ..
+// 32 wt + 31 (2 x 2 MFMA tiles); lane group g reads elements 8g .. 8g + 7 of
+// a chunk, the MFMA operand layout. One slice: finished in place; several:
 // fp64 partial sums [slice][T][E], added in slice order by k_router_reduce.
 typedef double v4d __attribute__((ext_vector_type(4)));
-constexpr int kRtTile = 64;   // experts and tokens per block
-constexpr int kRtDepth = 3;   // chunks in flight ahead of the MFMAs
+constexpr int kRtE = 128;              // experts per block
+constexpr int kRtK = 64;               // hidden elements per stage
+constexpr int kRtRow = 2 * kRtK + 16;  // LDS bytes per staged row (16 of padding)
+constexpr int kRtDepth = 3;            // stages whose loads are in flight
 
-__global__ __launch_bounds__(256) void k_router_mm(const uint16_t *__restrict__ x,
-                                                   const uint16_t *__restrict__ Wr, int T, int H, int E,
-                                                   int kspan, double *__restrict__ part,
-                                                   const float *__restrict__ bias, float *__restrict__ sc,
-                                                   float *__restrict__ ch, float *__restrict__ logits)
+template <int WT>
+__host__ __device__ constexpr int rt_lds_bytes()
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave & 1, wn = wave >> 1, g = lane >> 4, l16 = lane & 15;
-    const int e0 = blockIdx.x * kRtTile + wm * 32, t0 = blockIdx.y * kRtTile + wn * 32;
-    const int k0 = blockIdx.z * kspan, nch = (min(H, k0 + kspan) - k0) / 32;
-    const uint16_t *ap[2], *bp[2];
+    return 2 * (kRtE + 32 * WT) * kRtRow;
+}
+
+template <int WT>
+__global__ __launch_bounds__(256 * WT) void k_router_mm(const uint16_t *__restrict__ x,
+                                                        const uint16_t *__restrict__ Wr, int T, int H, int E,
+                                                        int kspan, double *__restrict__ part,
+                                                        const float *__restrict__ bias, float *__restrict__ sc,
+                                                        float *__restrict__ ch, float *__restrict__ logits)
+{
+    extern __shared__ __align__(16) uint8_t rt_l[];
+    constexpr int TT = 32 * WT, NROW = kRtE + TT, NT = 256 * WT;
+    constexpr int NU = NROW * (kRtK / 8);  // 16-byte pieces per stage
+    static_assert(NU % NT == 0, "whole pieces per thread");
+    constexpr int NQ = NU / NT;
+    constexpr int BUF = NROW * kRtRow;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int we = wave & 3, wt = wave >> 2, g = lane >> 4, l16 = lane & 15;
+    const int eb = blockIdx.x * kRtE, tb = blockIdx.y * TT;
+    const int k0 = blockIdx.z * kspan, nst = (min(H, k0 + kspan) - k0) / kRtK;
+
+    // piece v = tid + NT q: staged row v / 8 (rows past E or T repeat the
+    // last one; their results are never stored), 16-byte segment v % 8
+    const uint16_t *src[NQ];
+    uint32_t dst[NQ];
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
-        ap[f] = Wr + (size_t)min(e0 + 16 * f + l16, E - 1) * H + k0 + 8 * g;
-        bp[f] = x + (size_t)min(t0 + 16 * f + l16, T - 1) * H + k0 + 8 * g;
+    for (int q = 0; q < NQ; ++q) {
+        const int v = tid + NT * q, row = v >> 3, seg = v & 7;
+        src[q] = row < kRtE ? Wr + (size_t)min(eb + row, E - 1) * H + k0 + 8 * seg
+                            : x + (size_t)min(tb + row - kRtE, T - 1) * H + k0 + 8 * seg;
+        dst[q] = (uint32_t)(row * kRtRow + 16 * seg);
     }
+    // three stages in flight: register sets st[0..2] rotate (named, so the
+    // compiler's wait counts follow the rotation); loads past the last stage
+    // repeat it (never computed)
+    u4 st[kRtDepth][NQ];
+    auto gload = [&](int s, u4 (&r)[NQ]) {
+        const int sc = min(s, nst - 1);
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) r[q] = *reinterpret_cast<const u4 *>(src[q] + kRtK * sc);
+    };
+    auto lstore = [&](int buf, const u4 (&r)[NQ]) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) *reinterpret_cast<u4 *>(rt_l + buf * BUF + dst[q]) = r[q];
+    };
     v4d acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = v4d{0.0, 0.0, 0.0, 0.0};
-    u4 buf[kRtDepth + 1][4];
-    auto load = [&](int c, u4 (&b)[4]) {
-        const int cc = min(c, nch - 1) * 32;
-        b[0] = *reinterpret_cast<const u4 *>(ap[0] + cc);
-        b[1] = *reinterpret_cast<const u4 *>(ap[1] + cc);
-        b[2] = *reinterpret_cast<const u4 *>(bp[0] + cc);
-        b[3] = *reinterpret_cast<const u4 *>(bp[1] + cc);
-    };
-    auto half = [](uint32_t w, int hi) { return (double)bf16f(hi ? w >> 16 : w & 0xffffu); };
+    auto compute = [&](int buf) {
+        const uint8_t *Ab = rt_l + buf * BUF + (32 * we + l16) * kRtRow;
+        const uint8_t *Bb = rt_l + buf * BUF + (kRtE + 32 * wt + l16) * kRtRow;
 #pragma unroll
-    for (int d = 0; d < kRtDepth; ++d) load(d, buf[d]);
-    for (int c = 0; c < nch; c += kRtDepth + 1) {
+        for (int c = 0; c < kRtK / 32; ++c) {
+            const int kb = 64 * c + 16 * g;  // bytes: elements 32 c + 8 g .. + 7
+            bf8 a[2], b[2];
 #pragma unroll
-        for (int u = 0; u <= kRtDepth; ++u) {
-            load(c + u + kRtDepth, buf[(u + kRtDepth) % (kRtDepth + 1)]);
-            if (c + u < nch) {
-                const u4(&b)[4] = buf[u];
+            for (int i = 0; i < 2; ++i) a[i] = as_bf8(*reinterpret_cast<const u4 *>(Ab + 16 * i * kRtRow + kb));
 #pragma unroll
-                for (int st = 0; st < 8; ++st) {
-                    const double a0 = half(b[0][st >> 1], st & 1), a1 = half(b[1][st >> 1], st & 1);
-                    const double x0 = half(b[2][st >> 1], st & 1), x1 = half(b[3][st >> 1], st & 1);
-                    acc[0][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, x0, acc[0][0], 0, 0, 0);
-                    acc[0][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0, x1, acc[0][1], 0, 0, 0);
-                    acc[1][0] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, x0, acc[1][0], 0, 0, 0);
-                    acc[1][1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1, x1, acc[1][1], 0, 0, 0);
+            for (int j = 0; j < 2; ++j) b[j] = as_bf8(*reinterpret_cast<const u4 *>(Bb + 16 * j * kRtRow + kb));
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const v4f cs = mfma_bf16(a[i], b[j], v4f{0.0f, 0.0f, 0.0f, 0.0f});
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[i][j][r] += (double)cs[r];
                 }
+        }
+    };
+#pragma unroll
+    for (int d = 0; d < kRtDepth; ++d) gload(d, st[d]);
+    lstore(0, st[0]);
+    __syncthreads();
+    // stage i: st[i % 3] (already in LDS buffer i % 2) takes stage i + 3;
+    // st[(i + 1) % 3] goes to the other buffer
+    for (int s = 0; s < nst; s += kRtDepth) {
+#pragma unroll
+        for (int u = 0; u < kRtDepth; ++u) {
+            if (s + u < nst) {  // uniform
+                gload(s + u + kRtDepth, st[u]);
+                compute((s + u) & 1);
+                lstore((s + u + 1) & 1, st[(u + 1) % kRtDepth]);
+                __syncthreads();
             }
         }
     }
-    // tile (i, j): the fp64 MFMA leaves row 4 r + g of column l16 in result
-    // register r, i.e. expert e0 + 16 i + 4 r + g of token t0 + 16 j + l16
+    // tile (i, j): lane l holds rows 4 (l / 16) + r of column l % 16 in result
+    // register r, i.e. expert 32 we + 16 i + 4 g + r of token 32 wt + 16 j + l16
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int t = t0 + 16 * j + l16;
+            const int t = tb + 32 * wt + 16 * j + l16;
             if (t >= T) continue;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int e = e0 + 16 * i + 4 * r + g;
+                const int e = eb + 32 * we + 16 * i + 4 * g + r;
                 if (e >= E) continue;
                 if (part)
                     part[((size_t)blockIdx.z * T + t) * E + e] = acc[i][j][r];
@@ -183,7 +232,8 @@ __global__ __launch_bounds__(256) void k_router_mm(const uint16_t *__restrict__ 
         }
 }
 
-// Slice partial sums -> logits, in slice order.
+// Slice partial sums -> logits, in slice order (eight slices' loads in flight
+// at a time).
 __global__ __launch_bounds__(256) void k_router_reduce(const double *__restrict__ part, int S, int T, int E,
                                                        const float *__restrict__ bias, float *__restrict__ sc,
                                                        float *__restrict__ ch, float *__restrict__ logits)
@@ -191,7 +241,14 @@ __global__ __launch_bounds__(256) void k_router_reduce(const double *__restrict_
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x, n = (int64_t)T * E;
     if (i >= n) return;
     double acc = part[i];
-    for (int s = 1; s < S; ++s) acc += part[(size_t)s * n + i];
+    for (int s0 = 1; s0 < S; s0 += 8) {
+        double v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = s0 + u < S ? part[(size_t)(s0 + u) * n + i] : 0.0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (s0 + u < S) acc += v[u];
+    }
     const int t = (int)(i / E);
     router_finish(acc, t, (int)(i - (int64_t)t * E), E, bias, sc, ch, logits);
 }
@@ -1060,17 +1117,32 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const float *__rest
 
 }  // namespace
 
-// Hidden-dimension slices of the batched router: enough blocks to cover the
-// chip about twice (512 blocks), slices of at least 256 elements.
+// Tokens per batched-router block: 128 from 128 tokens on, else 64.
+static int router_wt(int64_t T) { return T >= 128 ? 4 : 2; }
+
+// Hidden-dimension slices of the batched router: about one block per block
+// slot of the chip (256 CUs; a CU holds one 1024-thread block or two
+// 512-thread ones), slices of at least 256 elements (whole 64-element
+// stages).
 int router_splits(int64_t T, int E, int H)
 {
-    const int64_t tiles = (int64_t)((E + kRtTile - 1) / kRtTile) * ((T + kRtTile - 1) / kRtTile);
-    const int64_t want = (512 + tiles - 1) / tiles;
+    const int64_t wt = router_wt(T), slots = wt == 4 ? 256 : 512;
+    const int64_t tiles = (int64_t)((E + kRtE - 1) / kRtE) * ((T + 32 * wt - 1) / (32 * wt));
+    const int64_t want = (slots + tiles / 2) / tiles;
     const int64_t S = std::max<int64_t>(1, std::min<int64_t>(want, H / 256));
     return (int)((H + router_kspan(H, (int)S) - 1) / router_kspan(H, (int)S));
 }
 
-int router_kspan(int H, int S) { return (H / 32 + S - 1) / S * 32; }
+int router_kspan(int H, int S) { return (H / kRtK + S - 1) / S * kRtK; }
+
+static bool set_router_lds()
+{
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_router_mm<2>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, rt_lds_bytes<2>());
+    (void)hipFuncSetAttribute(reinterpret_cast<const void *>(&k_router_mm<4>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, rt_lds_bytes<4>());
+    return true;
+}
 
 template <int NQ>
 static void topk_launch(int T, hipStream_t s, const float *sc, const float *ch, const LayerView &L,
@@ -1095,12 +1167,19 @@ hipError_t launch_route(const LayerView &L, const uint16_t *x, int T, int32_t *i
             k_router<<<dim3((L.E + 3) / 4, T), 256, 0, s>>>(x, L.router_w, L.router_bias, L.H, L.E, sc,
                                                             ch, logits);
         } else {
+            static const bool lds_set = set_router_lds();  // once per process (thread-safe static)
+            (void)lds_set;
             const int S = router_splits(T, L.E, L.H);
             const int kspan = router_kspan(L.H, S);
             double *part = S > 1 ? reinterpret_cast<double *>(ws + lay.rt_part) : nullptr;
-            const dim3 grid((L.E + kRtTile - 1) / kRtTile, (T + kRtTile - 1) / kRtTile, S);
-            k_router_mm<<<grid, 256, 0, s>>>(x, L.router_w, T, L.H, L.E, kspan, part, L.router_bias, sc, ch,
-                                             logits);
+            const int WT = router_wt(T);
+            const dim3 grid((L.E + kRtE - 1) / kRtE, (unsigned)((T + 32 * WT - 1) / (32 * WT)), S);
+            if (WT == 4)
+                k_router_mm<4><<<grid, 1024, rt_lds_bytes<4>(), s>>>(x, L.router_w, T, L.H, L.E, kspan, part,
+                                                                      L.router_bias, sc, ch, logits);
+            else
+                k_router_mm<2><<<grid, 512, rt_lds_bytes<2>(), s>>>(x, L.router_w, T, L.H, L.E, kspan, part,
+                                                                     L.router_bias, sc, ch, logits);
             if (S > 1) {
                 const int64_t n = (int64_t)T * L.E;
                 k_router_reduce<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(part, S, T, L.E, L.router_bias, sc,
