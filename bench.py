@@ -310,11 +310,11 @@ def main():
     # gate and up, per assignment) and issued flops (whole token tiles). A flat
     # layer's shared gate/up tiles run in the same launch once the shared
     # expert leaves the streaming kernels (T > 128): their flops count too.
-    # The routed down tiles multiply four e4m3 terms of the activation (a
+    # The routed down tiles multiply three e4m3 terms of the activation (a
     # latent layer's: bf16 hi and lo).
     tile_tok_gu = 64 if Lt else 128
     sh_in_tiles = not Lt and Is > 0 and T > 128
-    dn_terms = 2 if Lt else 4
+    dn_terms = 2 if Lt else 3
     mf = {"alg_gu": 0.0, "iss_gu": 0.0, "alg_dn": 0.0, "iss_dn": 0.0}
     for i in range(args.steps):
         c = heavy[i % pool]

@@ -16,9 +16,9 @@
 //  * Down tiles of the routed experts run on the scaled MFMA
 //    v_mfma_scale_f32_16x16x128_f8f6f4: the fp4 weight bytes are the A
 //    operand as loaded (their E8M0 byte the A scale) and the activation is
-//    fed as kATerms e4m3 terms with one E8M0 byte per 32-block each, which
+//    fed as kTileTerms e4m3 terms with one E8M0 byte per 32-block each, which
 //    the gate/up epilogue writes; one MFMA per term into the same
-//    accumulator (about 2^-19 of each block's maximum is left out).
+//    accumulator (about 2^-14 of each block's maximum is left out).
 //  * Where the streamed down projection reads an expert's activation (or
 //    the down tiles cannot use terms), the activation goes as two bf16
 //    planes hi + lo (hi = bf16(a), lo = bf16(a - hi); |a - hi - lo| <=
@@ -40,6 +40,9 @@ namespace k3moe {
 namespace {
 
 constexpr int kBPad = 16;       // LDS padding per token row
+// e4m3 terms of the activation the down tiles take: three leave about 2^-14
+// of each 32-block's maximum out (the one-token path keeps kATerms)
+constexpr int kTileTerms = 3;
 
 // ---------------------------------------------------------------------------
 // Work lists. Active expert q (ascending id) with n_q assignments goes to the
@@ -141,11 +144,11 @@ template <> struct GemmShape<kGU2> {  // gate/up, tokens as hi and lo: 8 waves x
 };
 // The down tile on the scaled MFMA v_mfma_scale_f32_16x16x128_f8f6f4: the
 // fp4 weights go in as loaded (A operand, the E8M0 byte as the lane's A
-// scale) and the activation as kATerms e4m3 terms (B operands with their own
+// scale) and the activation as kTileTerms e4m3 terms (B operands with their own
 // E8M0 bytes), one MFMA per term into the same accumulator.
 constexpr int kDN8 = 4;
-template <> struct GemmShape<kDN8> {   // down: 4 waves x 64 rows, 64 tokens, the activation as kATerms terms
-    static constexpr int WAVES = 4, RF = 4, TF = 4, NMAT = 1, NPL = kATerms, TOK = 64, MINB = 1;
+template <> struct GemmShape<kDN8> {   // down: 4 waves x 64 rows, 64 tokens, the activation as kTileTerms terms
+    static constexpr int WAVES = 4, RF = 4, TF = 4, NMAT = 1, NPL = kTileTerms, TOK = 64, MINB = 1;
 };
 // weight rows per block: waves x 16-row fragments per wave x 16
 template <int KIND>
@@ -179,8 +182,8 @@ struct GemmParams {
     const uint16_t *sh_bp[2];  //   its token planes [T][sh_KD] (x, or the activation's hi and lo),
     uint16_t *sh_ohi, *sh_olo; //   its activation outputs (gate/up)
     uint16_t *ohi, *olo;       // gate/up: activation hi/lo [row][rows] (null: not written)
-    uint8_t *oq, *osc;         // gate/up: activation as kATerms e4m3 terms [row][kATerms][rows]
-                               // and E8M0 bytes [row][kATerms][rows / 32] (null: not written)
+    uint8_t *oq, *osc;         // gate/up: activation as kTileTerms e4m3 terms [row][kTileTerms][rows]
+                               // and E8M0 bytes [row][kTileTerms][rows / 32] (null: not written)
     float *ys;                 // down: staging [T][K + 1][H]
 };
 
@@ -208,7 +211,7 @@ __host__ __device__ constexpr int gemm_lds_bytes()
 
 // Gate/up epilogue: the activation of this lane's rows row0 + 16 rf + 4 g +
 // [0, 4) for token column col, written as bf16 hi and lo planes and/or as
-// kATerms e4m3 terms. For the terms a wave's 32 rows are one E8M0 block: the
+// kTileTerms e4m3 terms. For the terms a wave's 32 rows are one E8M0 block: the
 // 4 lanes holding a column (lane groups 0..3) reduce its maximum. Every lane
 // runs the split (the shuffles need the whole wave); only columns with a
 // token store.
@@ -240,9 +243,9 @@ __device__ __forceinline__ void gu_epilogue(const GemmParams &p, const float (&a
         for (int rf = 0; rf < RF; ++rf)
 #pragma unroll
             for (int i = 0; i < 4; ++i) r[4 * rf + i] = av[rf][i];
-        uint32_t code[kATerms][RF];
-        int sb[kATerms];
-        split_e4m3_terms<kATerms, 4 * RF>(
+        uint32_t code[kTileTerms][RF];
+        int sb[kTileTerms];
+        split_e4m3_terms<kTileTerms, 4 * RF>(
             r, [](float m) {
                 m = fmaxf(m, __shfl_xor(m, 16));
                 return fmaxf(m, __shfl_xor(m, 32));
@@ -251,11 +254,11 @@ __device__ __forceinline__ void gu_epilogue(const GemmParams &p, const float (&a
         if (store) {
             const int nb = rows >> 5;
 #pragma unroll
-            for (int t = 0; t < kATerms; ++t) {
-                uint8_t *q = p.oq + ((size_t)orow * kATerms + t) * rows + row0 + 4 * g;
+            for (int t = 0; t < kTileTerms; ++t) {
+                uint8_t *q = p.oq + ((size_t)orow * kTileTerms + t) * rows + row0 + 4 * g;
 #pragma unroll
                 for (int rf = 0; rf < RF; ++rf) *reinterpret_cast<uint32_t *>(q + 16 * rf) = code[t][rf];
-                if (g == 0) p.osc[((size_t)orow * kATerms + t) * nb + (row0 >> 5)] = (uint8_t)sb[t];
+                if (g == 0) p.osc[((size_t)orow * kTileTerms + t) * nb + (row0 >> 5)] = (uint8_t)sb[t];
             }
         }
     }

@@ -38,8 +38,9 @@ struct WsLayout {
     size_t tiles_gu, tiles_dn;  // grouped-GEMM tile lists, int2 each
     size_t light;             // int32 [2][E]: experts for the weight-streaming kernels (gate/up, down)
     size_t tile_n;            // int32 [4]: gate/up tiles, down tiles, light gate/up, light down
-    // f8 down tiles: the routed activation as kATerms e4m3 terms
-    // [T*k][kATerms][I] and their E8M0 bytes [T*k][kATerms][I/32]
+    // f8 down tiles: the routed activation as n e4m3 terms [T*k][n][I] and
+    // their E8M0 bytes [T*k][n][I/32] (the tiles write n = 3; sized for
+    // kATerms)
     size_t aq = 0, aqs = 0;
     // latent layer only (0 otherwise)
     size_t lat_z = 0;         // z = Wd x as bf16 hi then lo planes [T][L] (4 bytes per element)
