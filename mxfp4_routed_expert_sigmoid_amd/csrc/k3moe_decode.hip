@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
 // lanes). The per-slot results go to LDS and one pass sums them in router
 // order, adds the shared row and applies the epilogue.
 constexpr int kDecDnWaves = 8;
-constexpr int kDecDnDepth = 4;     // rows (two slots each) in flight per wave
+constexpr int kDecDnDepth = 2;     // rows (two slots each) in flight per wave
 constexpr int kDecShRows = 4;      // shared rows per wave: a block owns at most 32 rows
 constexpr int kDecShSl = 4;        // 512-element slices of a shared row (I_s <= 2048)
 
