@@ -237,28 +237,31 @@ __device__ __forceinline__ void gu_epilogue(const GemmParams &p, const float (&a
         }
     }
     if (p.oq) {
-        static_assert(RF == 2, "a wave's rows are one 32-row block");
-        float r[4 * RF];
+        static_assert(RF % 2 == 0, "whole 32-row blocks per wave");
 #pragma unroll
-        for (int rf = 0; rf < RF; ++rf)
+        for (int h = 0; h < RF / 2; ++h) {  // the wave's 32-row block h: fragments 2h, 2h + 1
+            float r[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) r[4 * rf + i] = av[rf][i];
-        uint32_t code[kTileTerms][RF];
-        int sb[kTileTerms];
-        split_e4m3_terms<kTileTerms, 4 * RF>(
-            r, [](float m) {
-                m = fmaxf(m, __shfl_xor(m, 16));
-                return fmaxf(m, __shfl_xor(m, 32));
-            },
-            code, sb);
-        if (store) {
-            const int nb = rows >> 5;
+            for (int f = 0; f < 2; ++f)
 #pragma unroll
-            for (int t = 0; t < kTileTerms; ++t) {
-                uint8_t *q = p.oq + ((size_t)orow * kTileTerms + t) * rows + row0 + 4 * g;
+                for (int i = 0; i < 4; ++i) r[4 * f + i] = av[2 * h + f][i];
+            uint32_t code[kTileTerms][2];
+            int sb[kTileTerms];
+            split_e4m3_terms<kTileTerms, 8>(
+                r, [](float m) {
+                    m = fmaxf(m, __shfl_xor(m, 16));
+                    return fmaxf(m, __shfl_xor(m, 32));
+                },
+                code, sb);
+            if (store) {
+                const int nb = rows >> 5, rb0 = row0 + 32 * h;
 #pragma unroll
-                for (int rf = 0; rf < RF; ++rf) *reinterpret_cast<uint32_t *>(q + 16 * rf) = code[t][rf];
-                if (g == 0) p.osc[((size_t)orow * kTileTerms + t) * nb + (row0 >> 5)] = (uint8_t)sb[t];
+                for (int t = 0; t < kTileTerms; ++t) {
+                    uint8_t *q = p.oq + ((size_t)orow * kTileTerms + t) * rows + rb0 + 4 * g;
+#pragma unroll
+                    for (int f = 0; f < 2; ++f) *reinterpret_cast<uint32_t *>(q + 16 * f) = code[t][f];
+                    if (g == 0) p.osc[((size_t)orow * kTileTerms + t) * nb + (rb0 >> 5)] = (uint8_t)sb[t];
+                }
             }
         }
     }
