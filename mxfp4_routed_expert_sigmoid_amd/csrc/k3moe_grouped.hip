@@ -426,6 +426,15 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &p, int e, int rb, in
                         for (int rf = 0; rf < RF; ++rf) acc[m][rf][tf] = mfma_bf16(a[m][rf], bv, acc[m][rf][tf]);
                 }
             }
+            // Schedule: each token fragment's LDS read two fragments ahead of
+            // its MFMAs (left to itself the compiler reuses one register for
+            // every fragment's read and waits on each read in turn)
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * NPL, 0);
+#pragma unroll
+            for (int tf = 0; tf < NTF; ++tf) {
+                __builtin_amdgcn_sched_group_barrier(0x008, NPL * NMAT * RF, 0);
+                if (tf + 2 < NTF) __builtin_amdgcn_sched_group_barrier(0x100, NPL, 0);
+            }
         }
     };
     // Every chunk runs over all TF fragments (a partial tile multiplies
@@ -603,6 +612,13 @@ __device__ __forceinline__ void gemm_tile_f8(const GemmParams &p, int e, int rb,
                     for (int rf = 0; rf < RF; ++rf)
                         acc[m][rf][tf] = mfma_fp4_fp8<0>(a[m][rf], bv, acc[m][rf][tf], sa[m][rf], sb);
             }
+        }
+        // each fragment's three LDS reads two fragments ahead of its MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+        for (int f = 0; f < NTB * TF; ++f) {
+            __builtin_amdgcn_sched_group_barrier(0x008, NMAT * RF, 0);
+            if (f + 2 < NTB * TF) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
         }
     };
 
