@@ -282,7 +282,10 @@ def main():
             "down": nd * dn + Is * H * 2 + act_b + T * (K + 1) * EKw * 4 + (T * H * 4 if Lt else 0),
         }
     if args.workload in ("step", "stack"):
-        stage_bytes["prenorm"] = T * H * 4 + H * 4 + T * H * 2
+        if T == 1 and fused:   # the norm runs in the router's launch
+            stage_bytes["router"] += T * H * 4 + H * 4 + T * H * 2
+        else:
+            stage_bytes["prenorm"] = T * H * 4 + H * 4 + T * H * 2
     if cache is not None:
         stage_bytes = {"cache_fill": cd["bytes_read"] / max(1, cd["steps"])}
     if Lt:
@@ -297,13 +300,13 @@ def main():
                            "latent_out": "k_gv_up"} if T == 1 else
                           {"gateup": "k_gu_stream", "down": "k_dn_stream", "latent_in": "k_proj",
                            "latent_out": "k_proj + k_rms_split"}),
-               "step": ({"router": "k_router", "gateup": "k_dec_gateup", "down": "k_dec_down",
-                         "prenorm": "k_prenorm"} if T == 1
+               "step": ({"router": "k_prenorm_router", "gateup": "k_dec_gateup", "down": "k_dec_down"}
+                        if T == 1
                         else dict(one_tok, prenorm="k_prenorm") if per_token
                         else {"gateup": "k_gu_stream", "down": "k_dn_stream", "prenorm": "k_prenorm"}),
                "cache": {"cache_fill": "k_cache_fill"},
-               "stack": ({"router": "k_router", "gateup": "k_dec_gateup", "down": "k_dec_down",
-                          "prenorm": "k_prenorm"} if T == 1
+               "stack": ({"router": "k_prenorm_router", "gateup": "k_dec_gateup", "down": "k_dec_down"}
+                         if T == 1
                          else dict(one_tok, prenorm="k_prenorm") if per_token
                          else {"gateup": "k_gu_stream", "down": "k_dn_stream", "prenorm": "k_prenorm"})}[args.workload]
     # the hot experts' tile GEMMs: algorithmic flops (2 per multiply-add,

@@ -544,17 +544,24 @@ k3moe_status k3moe_step(const k3moe_layer *l, float *h, int32_t T, const float *
     hipStream_t st = static_cast<hipStream_t>(stream);
     LayerView v = view(l);
     v.routes_distinct = true;  // the routes below come from the router
-    {
-        StageMark m(l->prof, K3MOE_STAGE_PRENORM, st);
-        if (launch_prenorm(h, T, v.H, gamma, eps, x, st) != hipSuccess) return K3MOE_E_HIP;
-    }
     OutEpi epi;
     epi.resid = true;
     epi.ob = hb;
-    if (T == 1 && decode_fused_ok(v)) {
-        if (launch_decode_fused(v, x, idx, w, nullptr, true, h, wsc, lay, st, l->prof, epi) != hipSuccess)
+    if (T == 1 && decode_fused_ok(v) && prenorm_router_ok(v)) {
+        // the norm and the router in one launch, then the top-k and the experts
+        {
+            StageMark m(l->prof, K3MOE_STAGE_ROUTER, st);
+            if (launch_prenorm_router(v, h, gamma, eps, x, reinterpret_cast<float *>(wsc + lay.sc),
+                                      reinterpret_cast<float *>(wsc + lay.ch), st) != hipSuccess)
+                return K3MOE_E_HIP;
+        }
+        if (launch_decode_fused(v, x, idx, w, nullptr, true, h, wsc, lay, st, l->prof, epi, true) != hipSuccess)
             return K3MOE_E_HIP;
         return K3MOE_OK;
+    }
+    {
+        StageMark m(l->prof, K3MOE_STAGE_PRENORM, st);
+        if (launch_prenorm(h, T, v.H, gamma, eps, x, st) != hipSuccess) return K3MOE_E_HIP;
     }
     if (launch_route(v, x, T, idx, w, nullptr, wsc, lay, st, l->prof) != hipSuccess) return K3MOE_E_HIP;
     if (launch_forward(v, x, T, idx, w, h, wsc, lay, st, l->prof, epi) != hipSuccess) return K3MOE_E_HIP;

@@ -561,7 +561,7 @@ bool decode_fused_ok(const LayerView &L)
 // (k * 4 * I bytes); their E8M0 scales in ys.
 hipError_t launch_decode_fused(const LayerView &L, const uint16_t *x, int32_t *idx, float *w, float *logits,
                                bool route, float *out, char *ws, const WsLayout &lay, hipStream_t s,
-                               Profiler *prof, const OutEpi &epi)
+                               Profiler *prof, const OutEpi &epi, bool routed)
 {
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
@@ -572,7 +572,7 @@ hipError_t launch_decode_fused(const LayerView &L, const uint16_t *x, int32_t *i
     uint8_t *as = reinterpret_cast<uint8_t *>(ws + lay.ys);
 
     // R: the router rows (logits, scores)
-    if (route) {
+    if (route && !routed) {
         StageMark m(prof, K3MOE_STAGE_ROUTER, s);
         if (launch_router_t1(L, x, sc, ch, logits, s) != hipSuccess) return hipGetLastError();
     }

@@ -368,4 +368,18 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ sc, const fl
     *wt = v0 * rscale;
 }
 
+// Router epilogue for one (token, expert): the fp32 logit, the fp32 score
+// (sigmoid evaluated in fp64, rounded once) and the fp32 selection score.
+__device__ __forceinline__ void router_finish(double acc, int t, int e, int E, const float *__restrict__ bias,
+                                              float *__restrict__ sc, float *__restrict__ ch,
+                                              float *__restrict__ logits)
+{
+    const float l32 = (float)acc;
+    const float s = (float)(1.0 / (1.0 + exp(-(double)l32)));
+    const size_t o = (size_t)t * E + e;
+    sc[o] = s;
+    ch[o] = s + (bias ? bias[e] : 0.0f);
+    if (logits) logits[o] = l32;
+}
+
 }  // namespace k3moe

@@ -147,9 +147,11 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T,
 // `route`; else idx/w are read) + experts + router-order combine into out
 // with the epilogue. decode_fused_ok: the shapes it takes.
 bool decode_fused_ok(const LayerView &L);
+// routed: the router's scores are already in the workspace (sc, ch) and
+// only the top-k and the experts run.
 hipError_t launch_decode_fused(const LayerView &L, const uint16_t *x, int32_t *idx, float *w, float *logits,
                                bool route, float *out, char *ws, const WsLayout &lay, hipStream_t s,
-                               Profiler *prof, const OutEpi &epi = OutEpi());
+                               Profiler *prof, const OutEpi &epi = OutEpi(), bool routed = false);
 
 // Expert slot cache (k3moe_cache.hip). Device counters, in this order:
 enum {
@@ -198,6 +200,10 @@ hipError_t launch_cache_plan_fill(const CachePlanParams &pp, const CacheFillPara
 
 // Pre-MoE norm (k3moe_step.hip): x[t] = bf16_RNE(RMSNorm(h[t]) * gamma).
 hipError_t launch_prenorm(const float *h, int T, int H, const float *gamma, float eps, uint16_t *x, hipStream_t s);
+// The same norm and the one-token router (scores sc, ch) in one launch, T = 1.
+bool prenorm_router_ok(const LayerView &L);
+hipError_t launch_prenorm_router(const LayerView &L, const float *h, const float *gamma, float eps, uint16_t *x,
+                                 float *sc, float *ch, hipStream_t s);
 
 // A latent layer's experts for one token on the single-token kernels
 // (k3moe_kernels.hip): routed rows (width EK) to the staging rows ys, the

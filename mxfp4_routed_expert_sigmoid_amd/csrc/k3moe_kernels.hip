@@ -44,21 +44,6 @@
 namespace k3moe {
 namespace {
 
-// ---------------------------------------------------------------------------
-// Router epilogue for one (token, expert): the fp32 logit, the fp32 score
-// (sigmoid evaluated in fp64, rounded once) and the fp32 selection score.
-__device__ __forceinline__ void router_finish(double acc, int t, int e, int E, const float *__restrict__ bias,
-                                              float *__restrict__ sc, float *__restrict__ ch,
-                                              float *__restrict__ logits)
-{
-    const float l32 = (float)acc;
-    const float s = (float)(1.0 / (1.0 + exp(-(double)l32)));
-    const size_t o = (size_t)t * E + e;
-    sc[o] = s;
-    ch[o] = s + (bias ? bias[e] : 0.0f);
-    if (logits) logits[o] = l32;
-}
-
 // Router (README §9, k3_router). One wave per (expert, token): 16-byte loads
 // of the router row and the token, exact bf16 products summed in fp64, a
 // fixed-order butterfly across the wave. Lane 0 then forms the fp32 logit,
