@@ -42,6 +42,10 @@
 namespace k3moe {
 namespace {
 
+// e4m3 terms of a routed activation: three leave about 2^-14 of each
+// 32-element block's maximum out
+constexpr int kDecTerms = 3;
+
 // Loads in the streaming loops are plain loads from clamped (always valid)
 // addresses: a lane past a row's end reads real weights that meet a zero
 // operand on the other side (or a zero scale), so nothing is masked after
@@ -111,7 +115,7 @@ __device__ __forceinline__ float diag_sum(const v4f acc)
 //     rows, two in flight, each row piece as 4 bf16 MFMAs after an
 //     exact fp4 -> bf16 expansion (the diagonal dot product);
 //  5. parks its 16 sums in LDS; after the block barrier wave 0 takes the 32
-//     routed activations and splits them into 4 e4m3 terms with one E8M0
+//     routed activations and splits them into kDecTerms e4m3 terms with one E8M0
 //     scale per term (the form the down kernel's scaled MFMA takes), and
 //     wave 1 writes the block's shared activations.
 constexpr int kDecGuPieces = 4;    // 1 KB pieces per row: H <= 8192
@@ -129,8 +133,8 @@ struct DecGuParams {
     const float *sc, *ch;       // router scores [E] (fused top-k)
     int32_t *idx;               // [K]: written by block 0 (fused top-k) or read
     float *w;                   // [K]: written by block 0 (fused top-k)
-    uint8_t *aq;                // e4m3 terms [K][4][I]
-    uint8_t *as;                // their E8M0 scales [K][4][I / 32]
+    uint8_t *aq;                // e4m3 terms [K][kATerms][I] (the first kDecTerms written)
+    uint8_t *as;                // their E8M0 scales [K][kATerms][I / 32]
     const uint16_t *sh_gate, *sh_up;  // bf16 [Is][H]
     float *ash;                 // [Is] out: the shared expert's activation
     int Is;
@@ -144,8 +148,8 @@ __host__ __device__ constexpr int dec_gu_lds_bytes(int H, int NS)
     return 4 * (H / 2) + (int)sizeof(TopkLds) + 16 + 4 * 16 * 4 + 2 * kDecShPairs * 4 + NS * 64 * 16;
 }
 
-// Split the activations held by lanes 0..31 (one E8M0 block) into 4 e4m3
-// terms: per term, the scale puts the block's largest remainder in
+// Split the activations held by lanes 0..31 (one E8M0 block) into kDecTerms
+// e4m3 terms: per term, the scale puts the block's largest remainder in
 // [224, 448], the term takes only the elements within 6 binades of that
 // maximum (the scaled MFMA sums 16-product runs to about 14 bits below the
 // run's largest product) and its rounding error is carried exactly into the
@@ -155,7 +159,7 @@ __device__ __forceinline__ void split_terms_32(float r, uint8_t *term, size_t te
 {
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int t = 0; t < kATerms; ++t) {
+    for (int t = 0; t < kDecTerms; ++t) {
         float m = fabsf(r);
 #pragma unroll
         for (int o = 16; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));  // within lanes 0..31
@@ -201,22 +205,21 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
     float *shs_l = sum_l + 4 * kDecUnitRows;                                      // [2 kDecShPairs]
     u4 *x_l = reinterpret_cast<u4 *>(shs_l + 2 * kDecShPairs);                    // [NS][64]
 
-    // 1. the token in LDS (u4 i: elements 8i .. 8i + 7, zero past H)
+    // 1. wave 0's score loads first, then the token's: the shared rows'
+    // burst (below, after a barrier) queues behind them, not they behind it
+    constexpr int NQL = NQ > 0 ? NQ : 1;
+    float raw[NQL], sv[NQL];
+    if constexpr (NQ > 0)
+        if (wave == 0) topk_load<NQ, true>(p.sc, p.ch, p.E, raw, sv);
     constexpr int XQ = (NS * 64 + 255) / 256;
-    {
-        u4 xs[XQ];
+    u4 xs[XQ];  // the token (u4 i: elements 8i .. 8i + 7, zero past H)
 #pragma unroll
-        for (int q = 0; q < XQ; ++q) {
-            const int i = threadIdx.x + 256 * q;
-            const bool on = i < NS * 64 && 8 * i < H;
-            xs[q] = ld16m(p.x + (on ? 8 * i : 0), lane_mask(on));
-        }
-#pragma unroll
-        for (int q = 0; q < XQ; ++q) {
-            const int i = threadIdx.x + 256 * q;
-            if (i < NS * 64) x_l[i] = xs[q];
-        }
+    for (int q = 0; q < XQ; ++q) {
+        const int i = threadIdx.x + 256 * q;
+        const bool on = i < NS * 64 && 8 * i < H;
+        xs[q] = ld16m(p.x + (on ? 8 * i : 0), lane_mask(on));
     }
+    __syncthreads();  // issue order only
 
     // 2. this block's shared rows: pairs [sp0, sp1), row t = pair sp0 + t/2 of
     // gate (t even) or up (t odd); wave w takes rows w, w + 4, ...
@@ -236,11 +239,16 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
         }
     };
     if (wave != 0 && wave < nsr) sh_load(wave);
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+        const int i = threadIdx.x + 256 * q;
+        if (i < NS * 64) x_l[i] = xs[q];
+    }
     if constexpr (NQ > 0) {
         if (wave == 0) {
             int pick;
             float wt;
-            topk_wave<NQ, true>(p.sc, p.ch, p.E, p.K, p.renorm, p.rscale, tl, &pick, &wt);
+            topk_rank<NQ>(raw, sv, p.E, p.K, p.renorm, p.rscale, tl, &pick, &wt);
             if (bid == 0 && lane < p.K) {
                 p.idx[lane] = pick;
                 p.w[lane] = wt;
@@ -253,52 +261,15 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
     if (wave == 0 && nsr > 0) sh_load(0);
     __syncthreads();  // the token slices and the expert id
 
-    // 3. the shared rows
-    for (int t = wave; t < nsr; t += 4) {
-        if (t != wave) sh_load(t);
-        float a = 0.0f;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            const u4 xq = x_l[s * 64 + lane];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                a = fmaf(bf16f(shw[s][q] & 0xffffu), bf16f(xq[q] & 0xffffu), a);
-                a = fmaf(bf16f(shw[s][q] >> 16), bf16f(xq[q] >> 16), a);
-            }
-        }
-        a = wave_sum(a);
-        if (lane == 0) shs_l[t] = a;
-    }
-
     int e = e_l[0];
     const bool ok = e >= 0 && e < p.E;  // an invalid id: zero activations (the down kernel drops it)
     e = ok ? e : 0;
 
-    // 4. the token at this lane's K positions (lane l of row piece s:
-    // elements 2048 s + 32 l + [0, 32)), from LDS
-    u4 xv[kDecGuPieces][4];
-#pragma unroll
-    for (int s = 0; s < kDecGuPieces; ++s)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int i = 2048 * s + 32 * lane + 8 * c;
-            xv[s][c] = ld16m(x_l + (i < H ? i / 8 : 0), lane_mask(i < H));
-        }
-
-    // this wave's 16 E8M0 rows (contiguous: 16 x H/32 bytes)
+    // the routed rows' first loads go out before the shared rows are
+    // multiplied
     const int row0 = 32 * qb + kDecUnitRows * half;
     const uint8_t *sbase = (mat ? p.us + (int64_t)e * p.u_ss : p.gs + (int64_t)e * p.g_ss) + (size_t)row0 * HG;
     const uint8_t *wbase = (mat ? p.up + (int64_t)e * p.u_sp : p.gp + (int64_t)e * p.g_sp) + (size_t)row0 * HB;
-    constexpr int SQ = 8192 / 2 / 1024;  // 16-byte pieces per lane (H <= 8192)
-    u4 scv[SQ];
-#pragma unroll
-    for (int k = 0; k < SQ; ++k) {
-        const int i = 16 * lane + 1024 * k;
-        scv[k] = ld16(sbase + (i < H / 2 ? i : 0));
-    }
-
-    // the rows, two in flight (named buffers, so the compiler's wait
-    // counts follow the rotation); row r's sum is parked in lane r
     int soff[kDecGuPieces];        // this lane's offset in a row piece (off lanes: 0)
     int gidx[kDecGuPieces];        // this lane's E8M0 group (off lanes: 0)
     uint32_t smask[kDecGuPieces];  // off lanes scale their weights by 0
@@ -317,6 +288,47 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
 #pragma unroll
         for (int s = 0; s < kDecGuPieces; ++s) b.a[s] = ld16(wbase + ro + soff[s]);
     };
+    constexpr int GD = 2;  // rows in flight (four measured slower)
+    Row bq[GD];
+#pragma unroll
+    for (int d = 0; d < GD; ++d) load(d, bq[d]);
+
+    // 3. the shared rows
+    for (int t = wave; t < nsr; t += 4) {
+        if (t != wave) sh_load(t);
+        float a = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const u4 xq = x_l[s * 64 + lane];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                a = fmaf(bf16f(shw[s][q] & 0xffffu), bf16f(xq[q] & 0xffffu), a);
+                a = fmaf(bf16f(shw[s][q] >> 16), bf16f(xq[q] >> 16), a);
+            }
+        }
+        a = wave_sum(a);
+        if (lane == 0) shs_l[t] = a;
+    }
+
+    constexpr int SQ = 8192 / 2 / 1024;  // 16-byte pieces per lane (H <= 8192)
+    u4 scv[SQ];
+#pragma unroll
+    for (int k = 0; k < SQ; ++k) {
+        const int i = 16 * lane + 1024 * k;
+        scv[k] = ld16(sbase + (i < H / 2 ? i : 0));
+    }
+
+    // 4. the token at this lane's K positions (lane l of row piece s:
+    // elements 2048 s + 32 l + [0, 32)), from LDS
+    u4 xv[kDecGuPieces][4];
+#pragma unroll
+    for (int s = 0; s < kDecGuPieces; ++s)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int i = 2048 * s + 32 * lane + 8 * c;
+            xv[s][c] = ld16m(x_l + (i < H ? i / 8 : 0), lane_mask(i < H));
+        }
+
     float mine = 0.0f;
     auto compute = [&](int r, const Row &b) {
         v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
@@ -329,20 +341,18 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
         const float v = diag_sum(acc);
         mine = lane == r ? v : mine;
     };
-    Row b0, b1;
-    load(0, b0);
-    load(1, b1);
 #pragma unroll
     for (int k = 0; k < SQ; ++k) {
         const int i = 16 * lane + 1024 * k;
         if (i < H / 2) *reinterpret_cast<u4 *>(sc_l + i) = scv[k];
     }
     wave_lds_sync();  // the E8M0 rows are in LDS
-    for (int r = 0; r < kDecUnitRows; r += 2) {
-        compute(r, b0);
-        load(r + 2, b0);
-        compute(r + 1, b1);
-        load(r + 3, b1);
+    for (int r = 0; r < kDecUnitRows; r += GD) {
+#pragma unroll
+        for (int d = 0; d < GD; ++d) {
+            compute(r + d, bq[d]);
+            load(r + d + GD, bq[d]);
+        }
     }
     if (lane < kDecUnitRows) sum_l[wave * kDecUnitRows + lane] = mine;
     __syncthreads();
@@ -361,17 +371,21 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
 }
 
 // ---------------------------------------------------------------------------
-// D: the routed experts' down rows, the router-order sum and the shared rows.
-// Block b owns output rows [b RB, b RB + RB) for every slot; wave w takes
-// slots w and w + 8. A slot's B operands (4 e4m3 terms of its activation,
-// arranged for the diagonal) and their scales stay in registers for all the
-// block's rows; a row of W2 is one wave instruction (lane l: group l, I/32
-// lanes). The per-slot results go to LDS and one pass sums them in router
-// order, adds the shared row and applies the epilogue.
-constexpr int kDecDnWaves = 8;
-constexpr int kDecDnDepth = 2;     // rows (two slots each) in flight per wave
-constexpr int kDecShRows = 4;      // shared rows per wave: a block owns at most 32 rows
-constexpr int kDecShSl = 4;        // 512-element slices of a shared row (I_s <= 2048)
+// D: the routed experts' down rows, the shared expert's down rows and the
+// router-order sum. Block b owns output rows [b RB, b RB + RB) for every
+// slot; wave w takes slot w. A slot's B operands (kDecTerms e4m3 terms of its
+// activation, arranged for the diagonal) and their scales stay in registers
+// for all the block's rows; a row of W2 is one wave instruction (lane l:
+// group l, I/32 lanes), kDecDnDepth rows in flight. The shared expert's rows
+// of the block (wave w: rows w and w + NW) are loaded first, while the routes
+// are read, and multiplied after the routed rows. The per-slot results go to
+// LDS and one pass sums them in router order, adds the shared row and
+// applies the epilogue.
+constexpr int kDecDnWaves = 16;            // one slot per wave
+constexpr int kDecDnDepth = 4;             // rows in flight per wave
+constexpr int kDecDnRowsMax = 32;          // rows a block owns, at most
+constexpr int kDecShRows = kDecDnRowsMax / kDecDnWaves;  // shared rows per wave
+constexpr int kDecShSl = 4;                // 512-element slices of a shared row (I_s <= 2048)
 
 struct DecDnParams {
     const uint8_t *dp, *ds;
@@ -391,138 +405,118 @@ struct DecDnParams {
 
 __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
 {
-    extern __shared__ __align__(16) float y_l[];  // [K][RB]
+    extern __shared__ __align__(16) float y_l[];  // [K][RB], then (16-byte aligned) the shared activation [Is]
+    __shared__ float wk_l[kMaxTopk];  // routing weights, 0 for an id outside [0, E)
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int I = p.I, NG = I >> 5, IB = I >> 1;
     const int r0 = blockIdx.x * p.RB, nr = min(p.RB, p.H - r0);
-    const int ns = (p.K - wave + kDecDnWaves - 1) / kDecDnWaves;  // slots of this wave (0..2)
+    const bool has = wave < p.K;  // this wave's slot exists (else it computes slot 0 and drops it)
+    const int jj = has ? wave : 0;
+    const int e0 = p.idx[jj];
+    const bool ok = has && e0 >= 0 && e0 < p.E;  // an id outside [0, E) adds nothing
+    const int e = ok ? e0 : 0;
 
-    // the shared expert's rows of this block first (they need no routes):
-    // wave w takes rows r0 + w + 8 k, all its loads issued together
-    __shared__ float sh_l[kDecShRows * kDecDnWaves];
+    // the shared expert's rows of this block: wave w takes rows r0 + w + NW k
+    __shared__ float sh_l[kDecDnRowsMax];
+    float *ash_l = y_l + ((p.K * p.RB + 3) & ~3);  // 16-byte aligned
     const int NSS = (p.Is + 511) >> 9;
     u4 shw[kDecShRows][kDecShSl];
-    float4 sha[kDecShSl][2];
     if (p.Is > 0) {
 #pragma unroll
         for (int k = 0; k < kDecShRows; ++k) {
             const int r = r0 + min(wave + kDecDnWaves * k, nr - 1);
 #pragma unroll
             for (int sl = 0; sl < kDecShSl; ++sl) {
-                const bool on = sl < NSS && 512 * sl + 8 * lane < p.Is;
-                shw[k][sl] = ld16(p.sh_down + (size_t)r * p.Is + (on ? 512 * sl + 8 * lane : 0));
+                const bool son = sl < NSS && 512 * sl + 8 * lane < p.Is;
+                shw[k][sl] = ld16(p.sh_down + (size_t)r * p.Is + (son ? 512 * sl + 8 * lane : 0));
             }
         }
-#pragma unroll
-        for (int sl = 0; sl < kDecShSl; ++sl) {
-            const bool on = sl < NSS && 512 * sl + 8 * lane < p.Is;
-            const int i = on ? 512 * sl + 8 * lane : 0;
-            const uint32_t m = lane_mask(on);  // off lanes: a zero activation
-            const u4 a0 = ld16m(p.ash + i, m), a1 = ld16m(p.ash + i + 4, m);
-            sha[sl][0] = float4{__uint_as_float(a0.x), __uint_as_float(a0.y), __uint_as_float(a0.z), __uint_as_float(a0.w)};
-            sha[sl][1] = float4{__uint_as_float(a1.x), __uint_as_float(a1.y), __uint_as_float(a1.z), __uint_as_float(a1.w)};
-        }
     }
 
-    // the routing weights, zero for an id outside [0, E) (its slot adds
-    // nothing), loaded once
-    float wk[2 * kDecDnWaves];
-#pragma unroll
-    for (int j = 0; j < 2 * kDecDnWaves; ++j) {
-        const int jc = min(j, p.K - 1);
-        const int e = p.idx[jc];
-        const float wv = p.w[jc];
-        wk[j] = (j < p.K && e >= 0 && e < p.E) ? wv : 0.0f;
-    }
-    int ej[2];
-    v8i bt[2][kATerms];
-    int bs[2][kATerms];
-    const int i16 = lane & 15, g4 = lane >> 4;
-    const int p0 = 32 * (i16 + 16 * (g4 >> 1)) + 16 * (g4 & 1);
-    const int p1 = 32 * (i16 + 16 * (2 + (g4 >> 1))) + 16 * (g4 & 1);
+    // the rows' first loads; loads past the last row re-read it (never
+    // used). Lanes past I/32 read group 0 of the row and meet a zero B operand.
     const bool on = lane < NG;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-        const int j = wave + kDecDnWaves * m;
-        const int jj = m < ns ? j : 0;
-        const int e = p.idx[jj];
-        ej[m] = (m < ns && e >= 0 && e < p.E) ? e : -1;
-#pragma unroll
-        for (int t = 0; t < kATerms; ++t) {
-            const uint8_t *tr = p.aq + ((size_t)jj * kATerms + t) * I;
-            const u4 l2 = ld16m(tr + (p0 < I ? p0 : 0), lane_mask(p0 < I));
-            const u4 h2 = ld16m(tr + (p1 < I ? p1 : 0), lane_mask(p1 < I));
-            bt[m][t] = v8i{(int)l2.x, (int)l2.y, (int)l2.z, (int)l2.w, (int)h2.x, (int)h2.y, (int)h2.z, (int)h2.w};
-            bs[m][t] = on ? (int)p.as[((size_t)jj * kATerms + t) * NG + lane] : 127;
-        }
-    }
-
-    // the block's rows, both slots of the wave per row (a wave with one slot
-    // computes the second on its first slot's data and drops it); loads past
-    // the last row re-read it (never used). Lanes past I/32 read group 0 of
-    // the row and meet a zero B operand.
     const int nrow = max(nr, 1);
-    const int e0 = max(ej[0], 0), e1 = max(ns > 1 ? ej[1] : ej[0], 0);
-    const uint8_t *pa0 = p.dp + (int64_t)e0 * p.d_sp + (on ? 16 * lane : 0);
-    const uint8_t *pa1 = p.dp + (int64_t)e1 * p.d_sp + (on ? 16 * lane : 0);
-    const uint8_t *ps0 = p.ds + (int64_t)e0 * p.d_ss + (on ? lane : 0);
-    const uint8_t *ps1 = p.ds + (int64_t)e1 * p.d_ss + (on ? lane : 0);
+    const uint8_t *pa = p.dp + (int64_t)e * p.d_sp + (on ? 16 * lane : 0);
+    const uint8_t *ps = p.ds + (int64_t)e * p.d_ss + (on ? lane : 0);
     struct Row {
-        u4 a0, a1;
-        uint32_t s0, s1;
+        u4 a;
+        uint32_t s;
     };
     auto load = [&](int rr, Row &b) {
         const size_t r = (size_t)(r0 + min(rr, nrow - 1));
-        b.a0 = ld16(pa0 + r * IB);
-        b.a1 = ld16(pa1 + r * IB);
-        b.s0 = ps0[r * NG];
-        b.s1 = ps1[r * NG];
-    };
-    auto mma = [&](const u4 a, uint32_t sb, const v8i (&B)[kATerms], const int (&S)[kATerms]) {
-        const bool drop = sb == 255u;  // E8M0 255: the group contributes nothing
-        const u4 av = drop ? u4{0u, 0u, 0u, 0u} : a;
-        const int sa = drop ? 127 : (int)sb;
-        const v8i A = v8i{(int)av.x, (int)av.y, (int)av.z, (int)av.w, 0, 0, 0, 0};
-        v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int t = 0; t < kATerms; ++t) acc = mfma_fp4_fp8(A, B[t], acc, sa, S[t]);
-        return acc;
+        b.a = ld16(pa + r * IB);
+        b.s = ps[r * NG];
     };
     Row buf[kDecDnDepth];
 #pragma unroll
     for (int d = 0; d < kDecDnDepth; ++d) load(d, buf[d]);
+
+    // the slot's B operands: the e4m3 terms arranged for the diagonal
+    v8i bt[kDecTerms];
+    int bs[kDecTerms];
+    {
+        const int i16 = lane & 15, g4 = lane >> 4;
+        const int p0 = 32 * (i16 + 16 * (g4 >> 1)) + 16 * (g4 & 1);
+        const int p1 = 32 * (i16 + 16 * (2 + (g4 >> 1))) + 16 * (g4 & 1);
+#pragma unroll
+        for (int t = 0; t < kDecTerms; ++t) {
+            const uint8_t *tr = p.aq + ((size_t)jj * kATerms + t) * I;
+            const u4 l2 = ld16m(tr + (p0 < I ? p0 : 0), lane_mask(p0 < I));
+            const u4 h2 = ld16m(tr + (p1 < I ? p1 : 0), lane_mask(p1 < I));
+            bt[t] = v8i{(int)l2.x, (int)l2.y, (int)l2.z, (int)l2.w, (int)h2.x, (int)h2.y, (int)h2.z, (int)h2.w};
+            bs[t] = on ? (int)p.as[((size_t)jj * kATerms + t) * NG + lane] : 127;
+        }
+    }
+
+    // the routing weights and the shared activation, staged in LDS while
+    // the rows stream (read after the block barrier below)
+    if (threadIdx.x < p.K) {
+        const int ej = p.idx[threadIdx.x];
+        wk_l[threadIdx.x] = (ej >= 0 && ej < p.E) ? p.w[threadIdx.x] : 0.0f;
+    }
+    for (int i = threadIdx.x; 4 * i < p.Is; i += blockDim.x)
+        reinterpret_cast<float4 *>(ash_l)[i] = reinterpret_cast<const float4 *>(p.ash)[i];
+
+    for (int r = 0; r < nrow; r += kDecDnDepth) {
+#pragma unroll
+        for (int d = 0; d < kDecDnDepth; ++d) {
+            const bool drop = buf[d].s == 255u;  // E8M0 255: the group contributes nothing
+            const u4 a = buf[d].a;
+            const u4 av = drop ? u4{0u, 0u, 0u, 0u} : a;
+            const int sa = drop ? 127 : (int)buf[d].s;
+            const v8i A = v8i{(int)av.x, (int)av.y, (int)av.z, (int)av.w, 0, 0, 0, 0};
+            v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int t = 0; t < kDecTerms; ++t) acc = mfma_fp4_fp8(A, bt[t], acc, sa, bs[t]);
+            load(r + d + kDecDnDepth, buf[d]);
+            const float y = diag_sum(acc);
+            if (lane == 0 && r + d < nr && has) y_l[wave * p.RB + r + d] = ok ? y : 0.0f;
+        }
+    }
+    __syncthreads();  // the staged weights and activation
     if (p.Is > 0) {  // the shared rows: fp32 products in slice order, one wave-wide sum per row
 #pragma unroll
         for (int k = 0; k < kDecShRows; ++k) {
             float acc = 0.0f;
 #pragma unroll
             for (int sl = 0; sl < kDecShSl; ++sl) {
+                const bool son = sl < NSS && 512 * sl + 8 * lane < p.Is;
+                const int i = son ? 512 * sl + 8 * lane : 0;
+                const uint32_t msk = lane_mask(son);  // off lanes: a zero activation
+                const u4 a0 = ld16m(ash_l + i, msk), a1 = ld16m(ash_l + i + 4, msk);
                 const u4 w = shw[k][sl];
-                const float4 x0 = sha[sl][0], x1 = sha[sl][1];
-                acc = fmaf(bf16f(w[0] & 0xffffu), x0.x, acc);
-                acc = fmaf(bf16f(w[0] >> 16), x0.y, acc);
-                acc = fmaf(bf16f(w[1] & 0xffffu), x0.z, acc);
-                acc = fmaf(bf16f(w[1] >> 16), x0.w, acc);
-                acc = fmaf(bf16f(w[2] & 0xffffu), x1.x, acc);
-                acc = fmaf(bf16f(w[2] >> 16), x1.y, acc);
-                acc = fmaf(bf16f(w[3] & 0xffffu), x1.z, acc);
-                acc = fmaf(bf16f(w[3] >> 16), x1.w, acc);
+                acc = fmaf(bf16f(w[0] & 0xffffu), __uint_as_float(a0.x), acc);
+                acc = fmaf(bf16f(w[0] >> 16), __uint_as_float(a0.y), acc);
+                acc = fmaf(bf16f(w[1] & 0xffffu), __uint_as_float(a0.z), acc);
+                acc = fmaf(bf16f(w[1] >> 16), __uint_as_float(a0.w), acc);
+                acc = fmaf(bf16f(w[2] & 0xffffu), __uint_as_float(a1.x), acc);
+                acc = fmaf(bf16f(w[2] >> 16), __uint_as_float(a1.y), acc);
+                acc = fmaf(bf16f(w[3] & 0xffffu), __uint_as_float(a1.z), acc);
+                acc = fmaf(bf16f(w[3] >> 16), __uint_as_float(a1.w), acc);
             }
             acc = wave_sum(acc);
             if (lane == 0) sh_l[wave + kDecDnWaves * k] = acc;
-        }
-    }
-    for (int r = 0; r < nrow; r += kDecDnDepth) {
-#pragma unroll
-        for (int d = 0; d < kDecDnDepth; ++d) {
-            const v4f c0 = mma(buf[d].a0, buf[d].s0, bt[0], bs[0]);
-            const v4f c1 = mma(buf[d].a1, buf[d].s1, bt[1], bs[1]);
-            load(r + d + kDecDnDepth, buf[d]);
-            const float y0 = diag_sum(c0), y1 = diag_sum(c1);
-            if (lane == 0 && r + d < nr) {
-                if (ns > 0) y_l[wave * p.RB + r + d] = ej[0] >= 0 ? y0 : 0.0f;
-                if (ns > 1) y_l[(wave + kDecDnWaves) * p.RB + r + d] = ej[1] >= 0 ? y1 : 0.0f;
-            }
         }
     }
     __syncthreads();
@@ -530,10 +524,8 @@ __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
     // router-order sum (ids outside [0, E) add nothing), the shared row, the epilogue
     for (int r = threadIdx.x; r < nr; r += blockDim.x) {
         float acc = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 2 * kDecDnWaves; ++j)
-            if (j < p.K) acc = fmaf(wk[j], y_l[j * p.RB + r], acc);  // a dropped slot: 0 * 0
-        if (p.Is > 0) acc += sh_l[r];  // row r0 + r: wave r % 8, k = r / 8
+        for (int j = 0; j < p.K; ++j) acc = fmaf(wk_l[j], y_l[j * p.RB + r], acc);  // a dropped slot: 0 * 0
+        if (p.Is > 0) acc += sh_l[r];  // row r0 + r: wave r % NW, k = r / NW
         float *op = p.out + r0 + r;
         if (p.resid) acc = *op + acc;
         *op = acc;
@@ -548,12 +540,12 @@ __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
 
 // The shapes the three kernels take: a flat layer, H <= 8192 (four 1 KB
 // pieces per gate/up row, sixteen 512-element router slices), I <= 2048 (a
-// down row in one wave instruction), I_s <= 2048, top-k <= 16 (two slots per
+// down row in one wave instruction), I_s <= 2048, top-k <= 16 (one slot per
 // down wave).
 bool decode_fused_ok(const LayerView &L)
 {
     return L.Lt == 0 && L.H <= 8192 && L.H % 128 == 0 && L.I <= 2048 && L.I % 128 == 0 && L.Is <= 2048 &&
-           L.K <= 2 * kDecDnWaves && L.E <= kMaxExperts && 32 * L.H >= L.I &&
+           L.K <= kDecDnWaves && L.E <= kMaxExperts && 32 * L.H >= L.I &&
            L.Is <= kDecShPairs * L.K * (L.I / 32);  // a block's share of the shared rows fits its LDS
 }
 
@@ -638,7 +630,7 @@ hipError_t launch_decode_fused(const LayerView &L, const uint16_t *x, int32_t *i
         dp.E = L.E;
         dp.K = L.K;
         // one block per CU, at most kDecShRows rows per wave
-        const int nb = std::max(std::min(ncu, L.H), (L.H + kDecShRows * kDecDnWaves - 1) / (kDecShRows * kDecDnWaves));
+        const int nb = std::max(std::min(ncu, L.H), (L.H + kDecDnRowsMax - 1) / kDecDnRowsMax);
         dp.RB = (L.H + nb - 1) / nb;
         dp.idx = idx;
         dp.w = w;
@@ -652,7 +644,7 @@ hipError_t launch_decode_fused(const LayerView &L, const uint16_t *x, int32_t *i
         dp.ob = epi.ob;
         dp.errors = L.errors;
         const unsigned grid = (unsigned)((L.H + dp.RB - 1) / dp.RB);
-        k_dec_down<<<grid, 64 * kDecDnWaves, sizeof(float) * L.K * dp.RB, s>>>(dp);
+        k_dec_down<<<grid, 64 * kDecDnWaves, sizeof(float) * (((L.K * dp.RB + 3) & ~3) + L.Is), s>>>(dp);
     }
     return hipGetLastError();
 }

@@ -244,17 +244,18 @@ struct TopkLds {
 // falls back to k rounds of a wave-wide maximum, the lowest lane holding it
 // winning and rescanning its keys.
 //
-// Returns, in lane j < k, pick j's expert (*pick) and weight (*wt). V4:
-// E a multiple of 4 and rows 16-byte aligned (16-byte loads).
+// topk_load issues the loads of a lane's selection scores (raw) and scores
+// (sv); topk_rank then takes the top-k from them, so a kernel can put other
+// work between the two. Returns, in lane j < k, pick j's expert (*pick) and
+// weight (*wt). V4: E a multiple of 4 and rows 16-byte aligned (16-byte loads).
 template <int NQ, bool V4>
-__device__ __forceinline__ void topk_wave(const float *__restrict__ sc, const float *__restrict__ ch, int E, int K,
-                                          int renorm, float rscale, TopkLds &L, int *pick, float *wt)
+__device__ __forceinline__ void topk_load(const float *__restrict__ sc, const float *__restrict__ ch, int E,
+                                          float (&raw)[NQ], float (&sv)[NQ])
 {
     const int lane = threadIdx.x & 63;
     const int e0 = lane * NQ;
     // the selection scores and the scores are loaded together, every load
     // issued before the first is used (clamped index, no branch)
-    float raw[NQ], sv[NQ];
     if constexpr (V4) {
 #pragma unroll
         for (int q = 0; q < NQ; q += 4) {
@@ -271,6 +272,14 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ sc, const fl
             sv[q] = sc[min(e0 + q, E - 1)];
         }
     }
+}
+
+template <int NQ>
+__device__ __forceinline__ void topk_rank(const float (&raw)[NQ], const float (&sv)[NQ], int E, int K, int renorm,
+                                          float rscale, TopkLds &L, int *pick, float *wt)
+{
+    const int lane = threadIdx.x & 63;
+    const int e0 = lane * NQ;
     uint32_t v[NQ];
 #pragma unroll
     for (int q = 0; q < NQ; ++q) v[q] = e0 + q < E ? order_key(raw[q]) : 0u;  // 0: none / taken
@@ -366,6 +375,15 @@ __device__ __forceinline__ void topk_wave(const float *__restrict__ sc, const fl
     if (renorm && s > 0.0f) v0 /= s;
     *pick = mine;
     *wt = v0 * rscale;
+}
+
+template <int NQ, bool V4>
+__device__ __forceinline__ void topk_wave(const float *__restrict__ sc, const float *__restrict__ ch, int E, int K,
+                                          int renorm, float rscale, TopkLds &L, int *pick, float *wt)
+{
+    float raw[NQ], sv[NQ];
+    topk_load<NQ, V4>(sc, ch, E, raw, sv);
+    topk_rank<NQ>(raw, sv, E, K, renorm, rscale, L, pick, wt);
 }
 
 // Router epilogue for one (token, expert): the fp32 logit, the fp32 score
