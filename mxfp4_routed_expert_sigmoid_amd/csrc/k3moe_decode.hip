@@ -103,20 +103,24 @@ __device__ __forceinline__ float diag_sum(const v4f acc)
 // half), one weight stream per wave: on MI355X a wave with one contiguous
 // stream and two rows in flight keeps HBM busier than one interleaving two
 // streams. Each wave
-//  1. stages the token in LDS with the block;
-//  2. issues the loads of its first shared row (row t = w, w + 4, ... of the
-//     block's 2P rows, gate and up of pair t / 2 alternating); wave 0 first
-//     takes the top-k from the router's scores (or reads the given ids);
-//  3. after the block barrier, finishes its shared rows (bf16 x bf16 fp32
-//     FMA in slice order, one wave-wide sum each, parked in LDS);
+//  1. wave 0 issues the loads of the router's scores; after a block barrier
+//     (issue order: the scores ahead of the shared rows' burst) waves 1..3
+//     issue the loads of their first shared row (row t = w, w + 4, ... of
+//     the block's 2P rows, gate and up of pair t / 2 alternating) while wave
+//     0 takes the top-k (or reads the given ids);
+//  2. after the block barrier that publishes the expert id, each wave issues
+//     its first two routed rows, its 16 E8M0 rows and its share of the
+//     token (wave 0 then its shared row), and stores the token and the E8M0
+//     rows to LDS;
+//  3. after a block barrier, finishes its shared rows (bf16 x bf16 fp32 FMA
+//     in slice order, one wave-wide sum each, parked in LDS);
 //  4. takes the token from LDS into registers at its lanes' K positions
-//     (lane l of row piece s: elements 2048 s + 32 l + [0, 32)), stages its
-//     16 routed E8M0 rows (contiguous) in LDS and streams its 16 routed
-//     rows, two in flight, each row piece as 4 bf16 MFMAs after an
-//     exact fp4 -> bf16 expansion (the diagonal dot product);
+//     (lane l of row piece s: elements 2048 s + 32 l + [0, 32)) and streams
+//     its 16 routed rows, two in flight, each row piece as 4 bf16 MFMAs
+//     after an exact fp4 -> bf16 expansion (the diagonal dot product);
 //  5. parks its 16 sums in LDS; after the block barrier wave 0 takes the 32
-//     routed activations and splits them into kDecTerms e4m3 terms with one E8M0
-//     scale per term (the form the down kernel's scaled MFMA takes), and
+//     routed activations and splits them into kDecTerms e4m3 terms with one
+//     E8M0 scale per term (the form the down kernel's scaled MFMA takes), and
 //     wave 1 writes the block's shared activations.
 constexpr int kDecGuPieces = 4;    // 1 KB pieces per row: H <= 8192
 constexpr int kDecUnitRows = 16;   // rows per wave
@@ -205,24 +209,18 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
     float *shs_l = sum_l + 4 * kDecUnitRows;                                      // [2 kDecShPairs]
     u4 *x_l = reinterpret_cast<u4 *>(shs_l + 2 * kDecShPairs);                    // [NS][64]
 
-    // 1. wave 0's score loads first, then the token's: the shared rows'
-    // burst (below, after a barrier) queues behind them, not they behind it
+    // 1. wave 0 issues the router scores' loads; the block barrier then
+    // orders them ahead of every shared row's load
     constexpr int NQL = NQ > 0 ? NQ : 1;
     float raw[NQL], sv[NQL];
     if constexpr (NQ > 0)
         if (wave == 0) topk_load<NQ, true>(p.sc, p.ch, p.E, raw, sv);
-    constexpr int XQ = (NS * 64 + 255) / 256;
-    u4 xs[XQ];  // the token (u4 i: elements 8i .. 8i + 7, zero past H)
-#pragma unroll
-    for (int q = 0; q < XQ; ++q) {
-        const int i = threadIdx.x + 256 * q;
-        const bool on = i < NS * 64 && 8 * i < H;
-        xs[q] = ld16m(p.x + (on ? 8 * i : 0), lane_mask(on));
-    }
     __syncthreads();  // issue order only
 
     // 2. this block's shared rows: pairs [sp0, sp1), row t = pair sp0 + t/2 of
-    // gate (t even) or up (t odd); wave w takes rows w, w + 4, ...
+    // gate (t even) or up (t odd); wave w takes rows w, w + 4, ...; waves
+    // 1..3 issue their first row's loads now, wave 0 takes the top-k (no
+    // memory access but the scores) and loads its shared row later
     const int sp0 = (int)((int64_t)p.Is * bid / nb), sp1 = (int)((int64_t)p.Is * (bid + 1) / nb);
     const int nsr = 2 * (sp1 - sp0);
     auto sh_row = [&](int t) {
@@ -239,11 +237,6 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
         }
     };
     if (wave != 0 && wave < nsr) sh_load(wave);
-#pragma unroll
-    for (int q = 0; q < XQ; ++q) {
-        const int i = threadIdx.x + 256 * q;
-        if (i < NS * 64) x_l[i] = xs[q];
-    }
     if constexpr (NQ > 0) {
         if (wave == 0) {
             int pick;
@@ -258,15 +251,15 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
     } else {
         if (threadIdx.x == 0) e_l[0] = p.idx[j];
     }
-    if (wave == 0 && nsr > 0) sh_load(0);
-    __syncthreads();  // the token slices and the expert id
+    __syncthreads();  // the expert id
 
     int e = e_l[0];
     const bool ok = e >= 0 && e < p.E;  // an invalid id: zero activations (the down kernel drops it)
     e = ok ? e : 0;
 
-    // the routed rows' first loads go out before the shared rows are
-    // multiplied
+    // 3. the routed rows' first loads, this wave's 16 E8M0 rows (contiguous:
+    // 16 x H/32 bytes) and the token (u4 i: elements 8i .. 8i + 7, zero past
+    // H); wave 0's shared row last
     const int row0 = 32 * qb + kDecUnitRows * half;
     const uint8_t *sbase = (mat ? p.us + (int64_t)e * p.u_ss : p.gs + (int64_t)e * p.g_ss) + (size_t)row0 * HG;
     const uint8_t *wbase = (mat ? p.up + (int64_t)e * p.u_sp : p.gp + (int64_t)e * p.g_sp) + (size_t)row0 * HB;
@@ -292,6 +285,35 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
     Row bq[GD];
 #pragma unroll
     for (int d = 0; d < GD; ++d) load(d, bq[d]);
+    constexpr int SQ = 8192 / 2 / 1024;  // 16-byte pieces per lane (H <= 8192)
+    u4 scv[SQ];
+#pragma unroll
+    for (int k = 0; k < SQ; ++k) {
+        const int i = 16 * lane + 1024 * k;
+        scv[k] = ld16(sbase + (i < H / 2 ? i : 0));
+    }
+    constexpr int XQ = (NS * 64 + 255) / 256;
+    {
+        u4 xs[XQ];
+#pragma unroll
+        for (int q = 0; q < XQ; ++q) {
+            const int i = threadIdx.x + 256 * q;
+            const bool on = i < NS * 64 && 8 * i < H;
+            xs[q] = ld16m(p.x + (on ? 8 * i : 0), lane_mask(on));
+        }
+        if (wave == 0 && nsr > 0) sh_load(0);
+#pragma unroll
+        for (int q = 0; q < XQ; ++q) {
+            const int i = threadIdx.x + 256 * q;
+            if (i < NS * 64) x_l[i] = xs[q];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < SQ; ++k) {
+        const int i = 16 * lane + 1024 * k;
+        if (i < H / 2) *reinterpret_cast<u4 *>(sc_l + i) = scv[k];
+    }
+    __syncthreads();  // the token slices (and this wave's E8M0 rows)
 
     // 3. the shared rows
     for (int t = wave; t < nsr; t += 4) {
@@ -308,14 +330,6 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
         }
         a = wave_sum(a);
         if (lane == 0) shs_l[t] = a;
-    }
-
-    constexpr int SQ = 8192 / 2 / 1024;  // 16-byte pieces per lane (H <= 8192)
-    u4 scv[SQ];
-#pragma unroll
-    for (int k = 0; k < SQ; ++k) {
-        const int i = 16 * lane + 1024 * k;
-        scv[k] = ld16(sbase + (i < H / 2 ? i : 0));
     }
 
     // 4. the token at this lane's K positions (lane l of row piece s:
@@ -341,12 +355,6 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
         const float v = diag_sum(acc);
         mine = lane == r ? v : mine;
     };
-#pragma unroll
-    for (int k = 0; k < SQ; ++k) {
-        const int i = 16 * lane + 1024 * k;
-        if (i < H / 2) *reinterpret_cast<u4 *>(sc_l + i) = scv[k];
-    }
-    wave_lds_sync();  // the E8M0 rows are in LDS
     for (int r = 0; r < kDecUnitRows; r += GD) {
 #pragma unroll
         for (int d = 0; d < GD; ++d) {

@@ -217,7 +217,6 @@ __device__ __forceinline__ uint32_t order_key(float v)
 
 // LDS a wave's top-k works in.
 struct TopkLds {
-    uint32_t lmax[64];
     uint64_t cc[64];   // candidates: key << 32 | ~expert
     float cs[64];      // their unbiased scores
     int pi[64];        // picks in router order: expert, score
@@ -232,17 +231,17 @@ struct TopkLds {
 // contiguous range, so a lower lane always holds lower expert indices) as
 // order-preserving keys.
 //
-// Threshold and rank: tau = the k-th largest of the 64 lane maxima. k lanes
-// hold a key >= tau, so the k-th largest key is >= tau and every pick is
-// among the candidates {key >= tau}. When there are at most 64 candidates
-// (the usual case: about k of them), they are gathered in LDS, each takes
-// its rank in the order above by comparing against all of them, and the
-// first k ranks are the picks. A candidate is one 64-bit word, key in the
+// Threshold and rank: tau = the k-th largest of the 64 lane maxima (a
+// bitwise search on ballots). k lanes hold a key >= tau, so the k-th largest
+// key is >= tau and every pick is among the candidates {key >= tau}. When
+// there are at most 64 candidates (the usual case: about k of them), they
+// are gathered one per lane through LDS, each takes its rank in the order
+// above by comparing against every candidate (broadcast by readlane), and
+// the first k ranks are the picks. A candidate is one 64-bit word, key in the
 // high half and the complement of its expert index in the low half, so that
-// order is a single unsigned comparison; the 64 slots are prefilled with 0,
-// which no candidate is below. With more candidates (heavy ties) the wave
-// falls back to k rounds of a wave-wide maximum, the lowest lane holding it
-// winning and rescanning its keys.
+// order is a single unsigned comparison. With more candidates (heavy ties)
+// the wave falls back to k rounds of a wave-wide maximum, the lowest lane
+// holding it winning and rescanning its keys.
 //
 // topk_load issues the loads of a lane's selection scores (raw) and scores
 // (sv); topk_rank then takes the top-k from them, so a kernel can put other
@@ -287,21 +286,18 @@ __device__ __forceinline__ void topk_rank(const float (&raw)[NQ], const float (&
 #pragma unroll
     for (int q = 0; q < NQ; ++q) lm = v[q] > lm ? v[q] : lm;
 
-    // tau: the lane maximum of rank k-1 (ranks 0..63 distinct: equal maxima
-    // by lane)
-    L.lmax[lane] = lm;
-    L.cc[lane] = 0ull;
-    wave_lds_sync();
-    int rank = 0;
-#pragma unroll 16
-    for (int j = 0; j < 64; ++j) {
-        const uint32_t u = L.lmax[j];
-        rank += (u > lm || (u == lm && j < lane)) ? 1 : 0;
+    // tau: the k-th largest of the 64 lane maxima, i.e. the largest t with
+    // at least k lane maxima >= t, found bit by bit on the wave's ballots (no
+    // memory round trip)
+    uint32_t tau = 0u;
+#pragma unroll
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t c = tau | (1u << b);
+        if (__popcll(__ballot(lm >= c)) >= K) tau = c;
     }
-    const uint64_t at = __ballot(rank == K - 1);
-    const uint32_t tau = (uint32_t)__builtin_amdgcn_readlane((int)lm, (int)__builtin_ctzll(at));
 
-    // gather the candidates (key >= tau; a key of 0 is no expert)
+    // gather the candidates (key >= tau; a key of 0 is no expert): candidate
+    // i goes to slot i of the LDS list
     int C = 0;
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
@@ -319,13 +315,20 @@ __device__ __forceinline__ void topk_rank(const float (&raw)[NQ], const float (&
     int mine = 0;
     float mine_s = 0.0f;  // score of pick j, held by lane j
     if (C <= 64) {
-        const uint64_t k0 = L.cc[lane];
+        // lane i holds candidate i; its rank is the number of larger
+        // candidates, counted against each candidate broadcast in turn
+        const uint64_t k0 = lane < C ? L.cc[lane] : 0ull;
+        const float s0 = lane < C ? L.cs[lane] : 0.0f;
+        const uint32_t k0h = (uint32_t)(k0 >> 32), k0l = (uint32_t)k0;
         int r = 0;
-#pragma unroll
-        for (int j = 0; j < 64; ++j) r += L.cc[j] > k0 ? 1 : 0;
+        for (int j = 0; j < C; ++j) {
+            const uint64_t kj = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)k0h, j) << 32) |
+                                (uint32_t)__builtin_amdgcn_readlane((int)k0l, j);
+            r += kj > k0 ? 1 : 0;
+        }
         if (lane < C && r < K) {
             L.pi[r] = (int)~(uint32_t)k0;
-            L.ps[r] = L.cs[lane];
+            L.ps[r] = s0;
         }
         wave_lds_sync();
         if (lane < K) {
