@@ -429,7 +429,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &p, int e, int rb, in
             // Schedule: each token fragment's LDS read two fragments ahead of
             // its MFMAs (left to itself the compiler reuses one register for
             // every fragment's read and waits on each read in turn)
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * NPL, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, (NTF < 2 ? NTF : 2) * NPL, 0);
 #pragma unroll
             for (int tf = 0; tf < NTF; ++tf) {
                 __builtin_amdgcn_sched_group_barrier(0x008, NPL * NMAT * RF, 0);
@@ -437,12 +437,26 @@ __device__ __forceinline__ void gemm_tile(const GemmParams &p, int e, int rb, in
             }
         }
     };
-    // Every chunk runs over all TF fragments (a partial tile multiplies
-    // clamped copies of its last token, never stored): one branch-free body
-    // lets the compiler keep the accumulators in registers and overlap the
-    // LDS reads with the MFMAs; per-fragment branches serialised them.
+    // A chunk runs over TF, TF / 2 or TF / 4 fragments, the fewest that hold
+    // the tile's tokens (a partial fragment multiplies clamped copies of the
+    // last token, never stored): each is one branch-free body, so the
+    // compiler keeps the accumulators in registers and overlaps the LDS reads
+    // with the MFMAs (per-fragment branches serialised them); the choice is
+    // one uniform branch per chunk.
     auto compute = [&](const Chunk &b, int buf) {
         if (ntf == 0) return;
+        if constexpr (TF % 4 == 0) {
+            if (ntf <= TF / 4) {
+                compute_n(b, buf, std::integral_constant<int, TF / 4>{});
+                return;
+            }
+        }
+        if constexpr (TF % 2 == 0) {
+            if (ntf <= TF / 2) {
+                compute_n(b, buf, std::integral_constant<int, TF / 2>{});
+                return;
+            }
+        }
         compute_n(b, buf, std::integral_constant<int, TF>{});
     };
 
@@ -580,10 +594,11 @@ __device__ __forceinline__ void gemm_tile_f8(const GemmParams &p, int e, int rb,
 #pragma unroll
             for (int tf = 0; tf < TF; ++tf) acc[m][rf][tf] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Every chunk runs over all TF fragments (a partial tile multiplies
-    // clamped copies of its last token, never stored).
-    auto compute = [&](const Chunk &b, int buf) {
-        if (ntf == 0) return;
+    // A chunk runs over TF or TF / 2 fragments, the fewer that hold the
+    // tile's tokens (as in gemm_tile; a partial fragment multiplies clamped
+    // copies of the last token, never stored).
+    auto compute_n = [&](const Chunk &b, int buf, auto ntf_c) {
+        constexpr int NTF = decltype(ntf_c)::value;
         const uint8_t *Bb = B_l + buf * BBUF;
         v8i a[NMAT][RF];
         int sa[NMAT][RF];
@@ -600,7 +615,7 @@ __device__ __forceinline__ void gemm_tile_f8(const GemmParams &p, int e, int rb,
 #pragma unroll
         for (int t = 0; t < NTB; ++t) {
 #pragma unroll
-            for (int tf = 0; tf < TF; ++tf) {
+            for (int tf = 0; tf < NTF; ++tf) {
                 const int r = t * TOK + 16 * tf + l16;
                 const uint8_t *row = Bb + r * kB8Row;
                 const v8i bv = b_operand(*reinterpret_cast<const u4 *>(row + 16 * g),
@@ -616,10 +631,20 @@ __device__ __forceinline__ void gemm_tile_f8(const GemmParams &p, int e, int rb,
         // each fragment's three LDS reads two fragments ahead of its MFMAs
         __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
 #pragma unroll
-        for (int f = 0; f < NTB * TF; ++f) {
+        for (int f = 0; f < NTB * NTF; ++f) {
             __builtin_amdgcn_sched_group_barrier(0x008, NMAT * RF, 0);
-            if (f + 2 < NTB * TF) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+            if (f + 2 < NTB * NTF) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
         }
+    };
+    auto compute = [&](const Chunk &b, int buf) {
+        if (ntf == 0) return;
+        if constexpr (TF % 2 == 0) {
+            if (ntf <= TF / 2) {
+                compute_n(b, buf, std::integral_constant<int, TF / 2>{});
+                return;
+            }
+        }
+        compute_n(b, buf, std::integral_constant<int, TF>{});
     };
 
     Chunk c0, c1;
