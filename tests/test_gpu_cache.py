@@ -126,6 +126,46 @@ def test_full_expert_shape_decode():
     assert drops > 0 and model.stats["bytes_read"] == reads * 17547264
 
 
+def test_back_to_back_calls_share_the_workspace():
+    # Calls of 1..4 tokens issued one after another on one stream with one
+    # workspace and no host synchronisation in between: each call's resident
+    # experts run on the cache's own stream while its reads are in flight, so
+    # the next call's work must wait for this call's combine. Every output must
+    # equal the resident layer's on the same (drop-adjusted) routes.
+    import synth.device as sd
+    import mxfp4_routed_expert_sigmoid_amd as k3
+    spec = synth.LayerSpec(hidden=256, inter=128, n_experts=8, topk=2, shared_inter=128,
+                           bias_std=0.0, seed=204)
+    resident, host, _ = _setup(spec)
+    cache = k3.Cache(host, 3)
+    model = SlotCache(3, spec.n_experts)
+    rng = np.random.default_rng(4)
+    Ts = [1, 2, 4, 1, 3, 2, 1, 4, 1, 1]
+    ws = cache.workspace(max(Ts))
+    calls = []
+    for i, T in enumerate(Ts):
+        idx, w = _routes(rng, spec, T)
+        x_np = synth.make_x(spec, T, attempt=50 + i)
+        x = sd.bf16_tensor(x_np, DEV)
+        idx_d, w_d = torch.from_numpy(idx).to(DEV), torch.from_numpy(w).to(DEV)
+        out = torch.empty((T, spec.hidden), dtype=torch.float32, device=DEV)
+        print(f"[cache] back-to-back call {i} T={T}", flush=True)
+        cache.forward(x, idx_d, w_d, out, workspace=ws)
+        calls.append((x, idx, w_d, out))
+    torch.cuda.synchronize()
+    for i, (x, idx, w_d, out) in enumerate(calls):
+        slot_map, _ = model.step(idx, _expert_bytes(spec))
+        dropped = np.array(slot_map).reshape(idx.shape) < 0
+        idx_ref = np.where(dropped, -1, idx).astype(np.int32)
+        out_r = torch.empty_like(out)
+        resident.forward(x, torch.from_numpy(idx_ref).to(DEV), w_d, out_r)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), out_r.cpu().numpy()), f"call {i}"
+    assert cache.slots() == model.key
+    assert cache.stats() == model.stats
+    assert model.stats["misses"] > 0 and model.stats["resident_hits"] > 0
+
+
 def test_reset_and_refusals():
     import mxfp4_routed_expert_sigmoid_amd as k3
     spec = synth.LayerSpec(hidden=256, inter=128, n_experts=8, topk=2, shared_inter=0,
