@@ -262,7 +262,7 @@ def main():
     # flat layers at 2..4 tokens run the single-token kernels once per token
     per_token = not fused and not Lt and T <= 4 and cache is None
     if fused:
-        terms = K * 4 * I + K * 4 * (I // 32)   # the activations as e4m3 terms and their scales
+        terms = K * 3 * I + K * 3 * (I // 32)   # the activations as three e4m3 terms and their scales
         stage_bytes = {
             "router": router_bytes + H * 2 + E * 8,
             "gateup": nd * 2 * gu + 2 * Is * H * 2 + H * 2 + E * 8 + terms + Is * 4 + K * 8,
@@ -333,7 +333,8 @@ def main():
     dom_us = stage_us.get(dom, 0.0)
     achieved = stage_bytes[dom] / (dom_us * 1e-6) / 1e9 if dom_us > 0 else 0.0
     peak = HBM_PEAK_GBPS if cache is None else HOST_LINK_PEAK_GBPS
-    traffic = measured_traffic(kernels[dom])
+    prof_rec = profiled_kernel(kernels[dom])
+    traffic = prof_rec.get("hbm_bytes") if prof_rec else None
     value = nl * routed_bytes / (ms * 1e-3) / 1e9
     layer_bytes = routed_bytes + router_bytes + shared_bytes + proj_bytes + T * H * 2 + T * H * 4
     if args.workload == "stack":
@@ -388,6 +389,13 @@ def main():
             "traffic": traffic,
         },
     }
+    if prof_rec and prof_rec.get("rocprof_avg_us") and launches.get(dom, 0.0) == 1.0:
+        # the same kernel's average duration from the committed rocprofv3 kernel trace
+        # (profiles/layer_decode_T1_kernel_stats.md), for the same source file
+        pu = prof_rec["rocprof_avg_us"]
+        result["roofline"]["rocprof"] = {"avg_us": pu,
+                                         "achieved": round(stage_bytes[dom] / (pu * 1e-6) / 1e9, 2),
+                                         "frac": round(stage_bytes[dom] / (pu * 1e-6) / 1e9 / peak, 4)}
 
     if mf["alg_gu"] > 0 and stage_us.get("gateup_tiles", 0) > 0:
         tu, td = stage_us["gateup_tiles"] * 1e-6, max(stage_us.get("down_tiles", 0), 1e-9) * 1e-6
@@ -429,11 +437,12 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def measured_traffic(kernel):
-    """HBM bytes per dispatch of `kernel` from the committed rocprofv3 counter
-    runs (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for
-    a copy of known size), or None when no such run exists or the kernel's
-    source file has changed since it was taken."""
+def profiled_kernel(kernel):
+    """The committed rocprofv3 record of `kernel` (profiles/decode_T1_pmc_traffic.json):
+    HBM bytes per dispatch from the FETCH_SIZE and WRITE_SIZE counter runs
+    (each scaled by what the counter reads for a copy of known size) and the
+    kernel's average duration in the kernel trace, or None when no such
+    record exists or the kernel's source file has changed since it was taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "decode_T1_pmc_traffic.json")
     if not os.path.exists(path):
@@ -449,7 +458,7 @@ def measured_traffic(kernel):
     with open(src, "rb") as f:
         if hashlib.sha256(f.read()).hexdigest() != k["source_sha256"]:
             return None
-    return k["hbm_bytes"]
+    return k
 
 
 def cpu_baseline(spec, xs_np, T, budget_s, expert_b, gamma=None, distinct=16):
