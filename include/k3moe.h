@@ -312,14 +312,7 @@ k3moe_status k3moe_profile_read(k3moe_layer *layer, double *ms, int64_t *launche
  *      counted in k3moe_error_count and in the cache's `dropped`);
  *   4. reads each reserved expert's six tensors from host memory into its
  *      slot, then runs the layer's expert kernels on the slots (k3moe_forward
- *      semantics: router-order sum, shared expert; `out` written). For 1..4
- *      tokens of a flat layer the assignments whose expert was resident when
- *      the call began, and the shared expert, are computed while the reads
- *      are in flight (on a stream the cache owns, forked from and joined
- *      back to the caller's stream with events, so the call stays ordered on
- *      the caller's stream and can be captured in a graph); the read experts
- *      follow the reads (the Kimi-K3.cpp README, "The consumer-memory idea",
- *      step 6).
+ *      semantics: router-order sum, shared expert; `out` written).
  * The result is bit-identical to k3moe_forward on the same inputs when no
  * request is dropped. Calls on one cache must be serialised on one stream
  * (the slot table lives on the device and each call updates it). */

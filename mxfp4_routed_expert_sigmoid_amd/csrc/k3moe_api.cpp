@@ -33,10 +33,6 @@ struct k3moe_cache {
     unsigned long long *ctr;
     int32_t *slot_of, *key_of;
     long long *used_at;
-    // the cache's own stream: a few tokens' resident experts and the shared
-    // expert run on it while the missing experts are read on the caller's
-    hipStream_t side;
-    hipEvent_t ev_planned, ev_side_done;
 };
 
 namespace k3moe {
@@ -329,7 +325,7 @@ static LayerView cache_view(const k3moe_cache *c)
 
 struct CacheWs {
     WsLayout lay;          // the layer's workspace at S experts
-    size_t remap, pass, fill, nfill, total;
+    size_t remap, fill, nfill, total;
 };
 
 static CacheWs cache_ws(const k3moe_cache *c, int64_t T)
@@ -341,8 +337,6 @@ static CacheWs cache_ws(const k3moe_cache *c, int64_t T)
     size_t o = align256(w.lay.total);
     w.remap = o;
     o = align256(o + std::max<size_t>(sizeof(int32_t) * T * cs.topk, 1));
-    w.pass = o;
-    o = align256(o + std::max<size_t>((size_t)T * cs.topk, 1));
     w.fill = o;
     o = align256(o + sizeof(int2) * c->S);
     w.nfill = o;
@@ -693,16 +687,8 @@ k3moe_status k3moe_cache_create(const k3moe_layer *l, int32_t n_slots, k3moe_cac
     cc->key_of = reinterpret_cast<int32_t *>(cc->table + o);
     o += align256(sizeof(int32_t) * n_slots);
     cc->used_at = reinterpret_cast<long long *>(cc->table + o);
-    cc->side = nullptr;
-    cc->ev_planned = cc->ev_side_done = nullptr;
     if (launch_cache_init(cc->ctr, cc->slot_of, (int)E, cc->key_of, cc->used_at, n_slots, nullptr) != hipSuccess ||
-        hipDeviceSynchronize() != hipSuccess ||
-        hipStreamCreateWithFlags(&cc->side, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&cc->ev_planned, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&cc->ev_side_done, hipEventDisableTiming) != hipSuccess) {
-        (void)hipGetLastError();
-        if (cc->ev_planned) (void)hipEventDestroy(cc->ev_planned);
-        if (cc->side) (void)hipStreamDestroy(cc->side);
+        hipDeviceSynchronize() != hipSuccess) {
         (void)hipFree(cc->table);
         (void)hipFree(cc->arena);
         delete cc;
@@ -760,7 +746,6 @@ k3moe_status k3moe_cache_forward(k3moe_cache *c, const uint16_t *x, int32_t T, c
     pp.used_at = c->used_at;
     pp.ctr = c->ctr;
     pp.remap = reinterpret_cast<int32_t *>(wsc + cw.remap);
-    pp.pass = reinterpret_cast<int8_t *>(wsc + cw.pass);
     pp.fill = reinterpret_cast<int2 *>(wsc + cw.fill);
     pp.nfill = reinterpret_cast<int32_t *>(wsc + cw.nfill);
     CacheFillParams fp{};
@@ -777,33 +762,9 @@ k3moe_status k3moe_cache_forward(k3moe_cache *c, const uint16_t *x, int32_t T, c
     fp.expert_bytes = c->expert_bytes;
     fp.nchunk = (int)((c->expert_bytes + kFillChunk - 1) / kFillChunk);
     const int max_fill = (int)std::min<int64_t>(c->S, std::min<int64_t>(cfg.n_experts, n));
-    const LayerView v = cache_view(c);
-    Profiler *prof = c->layer->prof;
-    if (launch_cache_plan(pp, st, prof) != hipSuccess) return K3MOE_E_HIP;
-    if (t1_pass_ok(v, T)) {
-        // A few tokens: the slots whose experts were resident when the call
-        // began, and the shared expert, run on the cache's stream while the
-        // missing experts are read on the caller's; the missing experts run
-        // once their reads are done; one router-order combine over the
-        // staging rows both passes wrote (disjoint rows), so the result is
-        // the serial one bit for bit.
-        if (hipEventRecord(c->ev_planned, st) != hipSuccess ||
-            hipStreamWaitEvent(c->side, c->ev_planned, 0) != hipSuccess)
-            return K3MOE_E_HIP;
-        if (launch_t1_pass(v, x, T, pp.remap, pp.pass, 0, true, wsc, cw.lay, c->side, prof) != hipSuccess ||
-            hipEventRecord(c->ev_side_done, c->side) != hipSuccess)
-            return K3MOE_E_HIP;
-        if (launch_cache_fill(fp, max_fill, st, prof) != hipSuccess) return K3MOE_E_HIP;
-        if (launch_t1_pass(v, x, T, pp.remap, pp.pass, 1, false, wsc, cw.lay, st, prof) != hipSuccess ||
-            hipStreamWaitEvent(st, c->ev_side_done, 0) != hipSuccess)
-            return K3MOE_E_HIP;
-        StageMark m(prof, K3MOE_STAGE_COMBINE, st);
-        launch_combine(v, reinterpret_cast<float *>(wsc + cw.lay.ys), w, pp.remap, T, v.H, v.Is > 0, out, st,
-                       OutEpi());
-        return hipGetLastError() == hipSuccess ? K3MOE_OK : K3MOE_E_HIP;
-    }
-    if (launch_cache_fill(fp, max_fill, st, prof) != hipSuccess) return K3MOE_E_HIP;
-    if (launch_forward(v, x, T, pp.remap, w, out, wsc, cw.lay, st, prof) != hipSuccess) return K3MOE_E_HIP;
+    if (launch_cache_plan_fill(pp, fp, max_fill, st, c->layer->prof) != hipSuccess) return K3MOE_E_HIP;
+    if (launch_forward(cache_view(c), x, T, pp.remap, w, out, wsc, cw.lay, st, c->layer->prof) != hipSuccess)
+        return K3MOE_E_HIP;
     return K3MOE_OK;
 }
 
@@ -850,9 +811,6 @@ void k3moe_cache_destroy(k3moe_cache *c)
 {
     if (!c) return;
     (void)hipDeviceSynchronize();
-    (void)hipEventDestroy(c->ev_side_done);
-    (void)hipEventDestroy(c->ev_planned);
-    (void)hipStreamDestroy(c->side);
     (void)hipFree(c->table);
     (void)hipFree(c->arena);
     delete c;

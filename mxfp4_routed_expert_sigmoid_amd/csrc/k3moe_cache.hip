@@ -35,8 +35,6 @@ typedef unsigned u4 __attribute__((ext_vector_type(4)));
 constexpr int kPlanThreads = 1024;
 constexpr int kFillThreads = 256;
 constexpr int kFillQ = 8;  // 16-byte loads in flight per thread
-constexpr int kFillBlocks = 256;  // fill grid, at most (fewer left the host link short: 128, 64, 16 blocks
-                                  // read at 56.5, 55.8, 48.9 GB/s against 57.1)
 
 __device__ __forceinline__ unsigned long long shfl_xor_u64(unsigned long long v, int m)
 {
@@ -163,7 +161,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_cache_plan(CachePlanParams p)
                 key_of[s] = e;
                 slot_of[e] = s;
                 used_at[s] = tick0 + r + 1;
-                pinned[s] = 2;  // reserved: read in this call
+                pinned[s] = 1;
                 p.fill[nfill] = make_int2(e, s);
                 rescan();
             }
@@ -185,9 +183,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_cache_plan(CachePlanParams p)
 
     for (int64_t a = tid; a < p.n; a += kPlanThreads) {
         const int e = p.idx[a];
-        const int sl = (e >= 0 && e < E) ? slot_of[e] : -1;
-        p.remap[a] = sl;
-        if (p.pass) p.pass[a] = (int8_t)(sl >= 0 && pinned[sl] == 2 ? 1 : 0);
+        p.remap[a] = (e >= 0 && e < E) ? slot_of[e] : -1;
     }
     for (int e = tid; e < E; e += kPlanThreads) p.slot_of[e] = slot_of[e];
     for (int s = tid; s < S; s += kPlanThreads) {
@@ -196,45 +192,41 @@ __global__ __launch_bounds__(kPlanThreads) void k_cache_plan(CachePlanParams p)
     }
 }
 
-// Work item w copies bytes [c * kFillChunk, ...) of fill entry f = w / nchunk
-// (c = w % nchunk) of the expert's six tensors, seen as one run of
+// Block b copies bytes [c * kFillChunk, ...) of fill entry f = b / nchunk
+// (c = b % nchunk) of the expert's six tensors, seen as one run of
 // expert_bytes (segment i: seg_len[i] bytes, from src[i] + e * src_stride[i]
 // to the slot's offset seg_off[i]). Every length and offset is a multiple of
-// 16 bytes. A bounded grid walks the items (the host link, not the number
-// of blocks, sets the rate), so the rest of the chip stays free for expert
-// kernels on another stream.
+// 16 bytes.
 __global__ __launch_bounds__(kFillThreads) void k_cache_fill(CacheFillParams p)
 {
-    const int64_t nwork = (int64_t)*p.nfill * p.nchunk;
-    for (int64_t wk = blockIdx.x; wk < nwork; wk += gridDim.x) {
-        const int f = (int)(wk / p.nchunk), c = (int)(wk - (int64_t)f * p.nchunk);
-        const int2 es = p.fill[f];
-        const int64_t lo = (int64_t)c * kFillChunk;
-        const int64_t hi = lo + kFillChunk < p.expert_bytes ? lo + kFillChunk : p.expert_bytes;
-        int64_t base = 0;
-        for (int i = 0; i < 6; ++i) {
-            const int64_t a = lo > base ? lo : base;
-            const int64_t b = hi < base + p.seg_len[i] ? hi : base + p.seg_len[i];
-            if (a < b) {
-                const u4 *src = reinterpret_cast<const u4 *>(p.src[i] + (int64_t)es.x * p.src_stride[i] + (a - base));
-                u4 *dst = reinterpret_cast<u4 *>(p.arena + (int64_t)es.y * p.slot_bytes + p.seg_off[i] + (a - base));
-                const int64_t n = (b - a) / 16;
-                for (int64_t v0 = 0; v0 < n; v0 += (int64_t)kFillThreads * kFillQ) {
-                    u4 t[kFillQ];
+    const int f = blockIdx.x / p.nchunk, c = blockIdx.x - f * p.nchunk;
+    if (f >= *p.nfill) return;
+    const int2 es = p.fill[f];
+    const int64_t lo = (int64_t)c * kFillChunk;
+    const int64_t hi = lo + kFillChunk < p.expert_bytes ? lo + kFillChunk : p.expert_bytes;
+    int64_t base = 0;
+    for (int i = 0; i < 6; ++i) {
+        const int64_t a = lo > base ? lo : base;
+        const int64_t b = hi < base + p.seg_len[i] ? hi : base + p.seg_len[i];
+        if (a < b) {
+            const u4 *src = reinterpret_cast<const u4 *>(p.src[i] + (int64_t)es.x * p.src_stride[i] + (a - base));
+            u4 *dst = reinterpret_cast<u4 *>(p.arena + (int64_t)es.y * p.slot_bytes + p.seg_off[i] + (a - base));
+            const int64_t n = (b - a) / 16;
+            for (int64_t v0 = 0; v0 < n; v0 += (int64_t)kFillThreads * kFillQ) {
+                u4 t[kFillQ];
 #pragma unroll
-                    for (int q = 0; q < kFillQ; ++q) {
-                        const int64_t v = v0 + threadIdx.x + (int64_t)q * kFillThreads;
-                        if (v < n) t[q] = src[v];
-                    }
+                for (int q = 0; q < kFillQ; ++q) {
+                    const int64_t v = v0 + threadIdx.x + (int64_t)q * kFillThreads;
+                    if (v < n) t[q] = src[v];
+                }
 #pragma unroll
-                    for (int q = 0; q < kFillQ; ++q) {
-                        const int64_t v = v0 + threadIdx.x + (int64_t)q * kFillThreads;
-                        if (v < n) dst[v] = t[q];
-                    }
+                for (int q = 0; q < kFillQ; ++q) {
+                    const int64_t v = v0 + threadIdx.x + (int64_t)q * kFillThreads;
+                    if (v < n) dst[v] = t[q];
                 }
             }
-            base += p.seg_len[i];
         }
+        base += p.seg_len[i];
     }
 }
 
@@ -263,7 +255,8 @@ hipError_t launch_cache_init(unsigned long long *ctr, int32_t *slot_of, int E, i
     return hipGetLastError();
 }
 
-hipError_t launch_cache_plan(const CachePlanParams &pp, hipStream_t s, Profiler *prof)
+hipError_t launch_cache_plan_fill(const CachePlanParams &pp, const CacheFillParams &fp, int max_fill,
+                                  hipStream_t s, Profiler *prof)
 {
     static const bool lds_set = [] {
         // the largest table (the kernel's static LDS comes on top)
@@ -273,17 +266,13 @@ hipError_t launch_cache_plan(const CachePlanParams &pp, hipStream_t s, Profiler 
         return true;
     }();
     (void)lds_set;
-    StageMark m(prof, K3MOE_STAGE_CACHE_PLAN, s);
-    k_cache_plan<<<1, kPlanThreads, cache_plan_lds_bytes(pp.E, pp.S), s>>>(pp);
-    return hipGetLastError();
-}
-
-hipError_t launch_cache_fill(const CacheFillParams &fp, int max_fill, hipStream_t s, Profiler *prof)
-{
+    {
+        StageMark m(prof, K3MOE_STAGE_CACHE_PLAN, s);
+        k_cache_plan<<<1, kPlanThreads, cache_plan_lds_bytes(pp.E, pp.S), s>>>(pp);
+    }
     if (max_fill > 0) {
         StageMark m(prof, K3MOE_STAGE_CACHE_FILL, s);
-        const int64_t work = (int64_t)max_fill * fp.nchunk;
-        k_cache_fill<<<(unsigned)std::min<int64_t>(work, kFillBlocks), kFillThreads, 0, s>>>(fp);
+        k_cache_fill<<<(unsigned)((int64_t)max_fill * fp.nchunk), kFillThreads, 0, s>>>(fp);
     }
     return hipGetLastError();
 }

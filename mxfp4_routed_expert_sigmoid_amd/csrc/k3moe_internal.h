@@ -178,7 +178,6 @@ struct CachePlanParams {
     long long *used_at;  // [S]
     unsigned long long *ctr;
     int32_t *remap;      // [n] out: slot ids
-    int8_t *pass;        // [n] out: 1 where the assignment's expert is read in this call, else 0
     int2 *fill;          // [S] out: (expert, slot)
     int32_t *nfill;      // out
 };
@@ -196,8 +195,8 @@ struct CacheFillParams {
 size_t cache_plan_lds_bytes(int E, int S);
 hipError_t launch_cache_init(unsigned long long *ctr, int32_t *slot_of, int E, int32_t *key_of, long long *used_at,
                              int S, hipStream_t s);
-hipError_t launch_cache_plan(const CachePlanParams &pp, hipStream_t s, Profiler *prof);
-hipError_t launch_cache_fill(const CacheFillParams &fp, int max_fill, hipStream_t s, Profiler *prof);
+hipError_t launch_cache_plan_fill(const CachePlanParams &pp, const CacheFillParams &fp, int max_fill,
+                                  hipStream_t s, Profiler *prof);
 
 // Pre-MoE norm (k3moe_step.hip): x[t] = bf16_RNE(RMSNorm(h[t]) * gamma).
 hipError_t launch_prenorm(const float *h, int T, int H, const float *gamma, float eps, uint16_t *x, hipStream_t s);
@@ -266,14 +265,6 @@ hipError_t launch_stream_dn(const LayerView &L, int T, const int32_t *active_e, 
 // Token -> expert permutation and router-order combine (k3moe_kernels.hip).
 void launch_perm(const LayerView &L, const int32_t *idx, int T, char *ws, const WsLayout &lay, hipStream_t s,
                  Profiler *prof);
-// A flat layer's tokens [0, T) (T <= 4) on the single-token kernels, over
-// the slots j whose pass byte ph[t*K + j] equals pass (and the shared expert
-// when shared): each token's activations and staging rows ys[t] are its own,
-// so two passes over disjoint slots may run on two streams at once. No
-// combine. t1_pass_ok: the shapes it takes.
-bool t1_pass_ok(const LayerView &L, int T);
-hipError_t launch_t1_pass(const LayerView &L, const uint16_t *x, int T, const int32_t *idx, const int8_t *ph,
-                          int pass, bool shared, char *ws, const WsLayout &lay, hipStream_t s, Profiler *prof);
 void launch_combine(const LayerView &L, const float *ys, const float *w, const int32_t *idx, int T, int width,
                     bool shared, float *out, hipStream_t s, const OutEpi &epi = OutEpi());
 

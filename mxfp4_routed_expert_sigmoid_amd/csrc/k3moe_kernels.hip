@@ -461,10 +461,6 @@ struct GateUpParams {
     float *act_f;  // fp32 activations [k][I]
     const uint16_t *sh_gate, *sh_up;
     float *ash;
-    // a pass over part of the slots (null ph: every slot): only slots whose
-    // pass byte ph[j] equals pass run; sh_off: no shared rows
-    const int8_t *ph;
-    int pass, sh_off;
 };
 
 // ---------------------------------------------------------------------------
@@ -587,8 +583,7 @@ __global__ __launch_bounds__(64 * kGuDecWaves) void k_gateup_dec(GateUpParams p)
     const bool routed = wave < UNITS && u < nunits;
     const int slot = routed ? u / RT : 0, rt = routed ? u - (u / RT) * RT : 0;
     int e = routed ? p.idx[slot] : 0;
-    const bool mine = !p.ph || p.ph[slot] == p.pass;  // the slot belongs to this pass
-    const bool active = routed && mine && e >= 0 && e < p.E;  // an invalid id: nothing (the combine counts it)
+    const bool active = routed && e >= 0 && e < p.E;  // an invalid id: nothing (the combine counts it)
     e = active ? e : 0;
     const uint8_t *gpe = p.gp + e * p.g_sp, *upe = p.up + e * p.u_sp;
     const uint32_t po = ((uint32_t)rt * kGuUnitRows + (lane & 15)) * ((uint32_t)H >> 1) + grp * 16;
@@ -672,7 +667,7 @@ __global__ __launch_bounds__(64 * kGuDecWaves) void k_gateup_dec(GateUpParams p)
     __syncthreads();
 
     if (wave >= UNITS) {  // the shared expert's slice of rows, split over the shared waves
-        if (p.Is > 0 && !p.sh_off) {
+        if (p.Is > 0) {
             const int64_t ns = (int64_t)gridDim.x * (kGuDecWaves - UNITS), si = (int64_t)b * (kGuDecWaves - UNITS) + (wave - UNITS);
             shared_gateup_rows(p, (int)(p.Is * si / ns), (int)(p.Is * (si + 1) / ns));
         }
@@ -763,8 +758,6 @@ struct DownDecParams {
     const uint16_t *sh_down;
     const float *ash;
     float *ys;
-    const int8_t *ph;  // as GateUpParams: only slots with ph[j] == pass, no shared rows when sh_off
-    int pass, sh_off;
 };
 
 constexpr int kDnDecWaves = 4;
@@ -797,7 +790,6 @@ __global__ __launch_bounds__(64 * kDnDecWaves) void k_down_dec(DownDecParams p)
     const int e_raw = p.idx[j];
     const bool ok = e_raw >= 0 && e_raw < p.E;  // an invalid id: zeros (the combine counts it)
     const int e = ok ? e_raw : 0;
-    const bool mine = !p.ph || p.ph[j] == p.pass;  // slot j's rows belong to this pass
 
     extern __shared__ __align__(16) uint8_t lds[];
     uint8_t *aq_l = lds;                                   // [4][I + pad] activation terms of slot j
@@ -810,13 +802,13 @@ __global__ __launch_bounds__(64 * kDnDecWaves) void k_down_dec(DownDecParams p)
     const uint8_t *ase = p.ds + (int64_t)e * p.d_ss + (size_t)t0 * 16 * SR;
     const float *afj = p.act_f + (size_t)j * I;
     const int ntw = (nt - wave + kDnDecWaves - 1) / kDnDecWaves;  // tiles of this wave
-    const int nq = ok && mine ? ntw * NCH : 0;                    // chunks of this wave
+    const int nq = ok ? ntw * NCH : 0;                            // chunks of this wave
     const uint32_t rowb = (uint32_t)I >> 1;
     const uint32_t pl = (uint32_t)(lane & 15) * rowb + grp * 16;
 
     // shared rows of this wave (prefetched) and the shared activation
     const int nsr = (r1 - r0 - wave + kDnDecWaves - 1) / kDnDecWaves;
-    const int Is = p.sh_off ? 0 : p.Is;
+    const int Is = p.Is;
     u4 shw[kDnShPerWave][kDnShSl];
     float4 shx[kDnShSl][2];
     const bool sh_pf = Is > 0 && nsr <= kDnShPerWave;  // the first kDnShSl slices of the shared rows
@@ -1032,9 +1024,8 @@ __global__ __launch_bounds__(64 * kDnDecWaves) void k_down_dec(DownDecParams p)
         }
     }
     __syncthreads();
-    if (mine)
-        for (int ii = threadIdx.x; ii < nt * 16; ii += blockDim.x)
-            p.ys[(size_t)j * p.Hr + (size_t)t0 * 16 + ii] = ok ? y_l[ii] : 0.0f;
+    for (int ii = threadIdx.x; ii < nt * 16; ii += blockDim.x)
+        p.ys[(size_t)j * p.Hr + (size_t)t0 * 16 + ii] = ok ? y_l[ii] : 0.0f;
     if (Is > 0) {
         float *yshr = p.ysh ? p.ysh : p.ys + (size_t)p.K * p.Hr;
         for (int ii = threadIdx.x; ii < r1 - r0; ii += blockDim.x) yshr[r0 + ii] = sh_l[ii];
@@ -1261,8 +1252,7 @@ static bool decode_path_ok(const LayerView &L)
 static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const uint16_t *xr,
                                     const uint16_t *xr_lo, const int32_t *idx, const float *w, float *out,
                                     float *act, float *ash, char *ys_base, float *ysh, hipStream_t s,
-                                    Profiler *prof, const OutEpi &epi, const int8_t *ph = nullptr, int pass = 0,
-                                    bool sh_off = false)
+                                    Profiler *prof, const OutEpi &epi)
 {
     int dev = 0, ncu = 256;
     if (hipGetDevice(&dev) == hipSuccess) (void)hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
@@ -1292,9 +1282,6 @@ static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const
     gp.sh_gate = L.sh_gate;
     gp.sh_up = L.sh_up;
     gp.ash = ash;
-    gp.ph = ph;
-    gp.pass = pass;
-    gp.sh_off = sh_off ? 1 : 0;
     {
         StageMark m(prof, K3MOE_STAGE_GATEUP, s);
         const int nunits = L.K * (L.I / kGuUnitRows), units = gu_dec_units(L);
@@ -1330,9 +1317,6 @@ static hipError_t launch_forward_t1(const LayerView &L, const uint16_t *x, const
     dp.sh_down = L.sh_down;
     dp.ash = ash;
     dp.ys = ys;
-    dp.ph = ph;
-    dp.pass = pass;
-    dp.sh_off = sh_off ? 1 : 0;
     {
         StageMark m(prof, K3MOE_STAGE_DOWN, s);
         const unsigned nblk = (unsigned)(L.K * dp.M);
@@ -1398,25 +1382,6 @@ void launch_combine(const LayerView &L, const float *ys, const float *w, const i
 // (full flat shape: T = 2 165 us against 216, T = 4 310 against 354); from
 // about 5 tokens on, streaming each distinct expert once wins.
 constexpr int kT1LoopMax = 4;
-
-bool t1_pass_ok(const LayerView &L, int T) { return L.Lt == 0 && T >= 1 && T <= kT1LoopMax && decode_path_ok(L); }
-
-hipError_t launch_t1_pass(const LayerView &L, const uint16_t *x, int T, const int32_t *idx, const int8_t *ph,
-                          int pass, bool shared, char *ws, const WsLayout &lay, hipStream_t s, Profiler *prof)
-{
-    float *act = reinterpret_cast<float *>(ws + lay.act);
-    float *ash = reinterpret_cast<float *>(ws + lay.ash);
-    float *ys = reinterpret_cast<float *>(ws + lay.ys);
-    for (int t = 0; t < T; ++t) {
-        const uint16_t *xt = x + (size_t)t * L.H;
-        const hipError_t e = launch_forward_t1(
-            L, xt, xt, nullptr, idx + (size_t)t * L.K, nullptr, nullptr, act + (size_t)t * L.K * L.I,
-            ash + (size_t)t * std::max(L.Is, 1), reinterpret_cast<char *>(ys + (size_t)t * (L.K + 1) * L.H), nullptr,
-            s, prof, OutEpi(), ph + (size_t)t * L.K, pass, !shared);
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
-}
 
 hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const int32_t *idx,
                           const float *w, float *out, char *ws, const WsLayout &lay, hipStream_t s,
