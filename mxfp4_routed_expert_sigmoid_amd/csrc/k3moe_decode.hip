@@ -82,6 +82,20 @@ __device__ __forceinline__ float wave_sum(float v)
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+
+// Wave priority from the work this wave has left (0..3): waves that share a
+// SIMD are issued oldest first at equal priority, so without this the oldest
+// finishes first and the youngest runs its last rows with nobody to hide
+// its loads behind.
+__device__ __forceinline__ void prio_left(int left, int total)
+{
+    const int lv = (4 * left - 1) / total;  // left in (0, total]: 3 .. 0
+    if (lv >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (lv == 2) __builtin_amdgcn_s_setprio(2);
+    else if (lv == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
 // Diagonal of a 16 x 16 MFMA result, summed: lane L holds
 // C[4 (L / 16) + r][L % 16] in acc[r], so C[i][i] sits in the lanes with
 // (L % 16) / 4 == L / 16, register L % 4.
@@ -356,12 +370,14 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
         mine = lane == r ? v : mine;
     };
     for (int r = 0; r < kDecUnitRows; r += GD) {
+        prio_left(kDecUnitRows - r, kDecUnitRows);
 #pragma unroll
         for (int d = 0; d < GD; ++d) {
             compute(r + d, bq[d]);
             load(r + d + GD, bq[d]);
         }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (lane < kDecUnitRows) sum_l[wave * kDecUnitRows + lane] = mine;
     __syncthreads();
 
@@ -487,6 +503,7 @@ __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
         reinterpret_cast<float4 *>(ash_l)[i] = reinterpret_cast<const float4 *>(p.ash)[i];
 
     for (int r = 0; r < nrow; r += kDecDnDepth) {
+        prio_left(nrow - r, nrow);
 #pragma unroll
         for (int d = 0; d < kDecDnDepth; ++d) {
             const bool drop = buf[d].s == 255u;  // E8M0 255: the group contributes nothing
@@ -502,6 +519,7 @@ __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
             if (lane == 0 && r + d < nr && has) y_l[wave * p.RB + r + d] = ok ? y : 0.0f;
         }
     }
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // the staged weights and activation
     if (p.Is > 0) {  // the shared rows: fp32 products in slice order, one wave-wide sum per row
 #pragma unroll
