@@ -83,19 +83,6 @@ __device__ __forceinline__ float wave_sum(float v)
 }
 
 
-// Wave priority from the work this wave has left (0..3): waves that share a
-// SIMD are issued oldest first at equal priority, so without this the oldest
-// finishes first and the youngest runs its last rows with nobody to hide
-// its loads behind.
-__device__ __forceinline__ void prio_left(int left, int total)
-{
-    const int lv = (4 * left - 1) / total;  // left in (0, total]: 3 .. 0
-    if (lv >= 3) __builtin_amdgcn_s_setprio(3);
-    else if (lv == 2) __builtin_amdgcn_s_setprio(2);
-    else if (lv == 1) __builtin_amdgcn_s_setprio(1);
-    else __builtin_amdgcn_s_setprio(0);
-}
-
 // Diagonal of a 16 x 16 MFMA result, summed: lane L holds
 // C[4 (L / 16) + r][L % 16] in acc[r], so C[i][i] sits in the lanes with
 // (L % 16) / 4 == L / 16, register L % 4.

@@ -185,6 +185,19 @@ __device__ __forceinline__ float act_fn(float g, float u, int kind, float b1, fl
     return g * sg * u;
 }
 
+// Wave priority from the work this wave has left (0..3): waves that share a
+// SIMD are issued oldest first at equal priority, so without this the oldest
+// finishes first and the youngest runs its last rows with nobody to hide
+// its loads behind.
+__device__ __forceinline__ void prio_left(int left, int total)
+{
+    const int lv = (4 * left - 1) / total;  // left in (0, total]: 3 .. 0
+    if (lv >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (lv == 2) __builtin_amdgcn_s_setprio(2);
+    else if (lv == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
 // Orders LDS traffic of one wave: its earlier LDS stores are complete and
 // visible to every lane of the wave before its later LDS loads (the wave's
 // LDS operations complete in order; the clobber stops the compiler moving
