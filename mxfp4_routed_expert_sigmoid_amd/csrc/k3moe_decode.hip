@@ -93,6 +93,39 @@ __device__ __forceinline__ float diag_sum(const v4f acc)
     return wave_sum((((L & 15) >> 2) == (L >> 4)) ? v : 0.0f);
 }
 
+// The diagonals of four 16 x 16 MFMA results, summed together (lane L holds
+// C[4 (L / 16) + r][L % 16] in acc[k][r]; the diagonal entries sit in the
+// lanes with (L % 16) / 4 == L / 16, register L % 4). Every lane keeps its
+// diagonal value of each result (0 elsewhere); an exchange with lane L ^ 32
+// leaves lanes 0..31 the partial sums of results 0 and 1 and lanes 32..63
+// those of 2 and 3, an exchange with lane L ^ 16 leaves lane group L / 16
+// with result L / 16 alone, and four DPP steps sum each 16-lane group: every
+// lane of group k returns result k. The same sums as four separate wave
+// sums, in another order, with a quarter of the cross-lane steps.
+__device__ __forceinline__ float diag_sum4(const v4f (&acc)[4])
+{
+    const int L = threadIdx.x & 63, r = L & 3;
+    const bool dg = ((L & 15) >> 2) == (L >> 4);
+    float v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float e = r == 0 ? acc[k][0] : r == 1 ? acc[k][1] : r == 2 ? acc[k][2] : acc[k][3];
+        v[k] = dg ? e : 0.0f;
+    }
+    const bool hi = L >= 32;
+    const float g0 = __shfl_xor(hi ? v[0] : v[2], 32), g1 = __shfl_xor(hi ? v[1] : v[3], 32);
+    const float a0 = (hi ? v[2] : v[0]) + g0, a1 = (hi ? v[3] : v[1]) + g1;
+    const bool b4 = (L & 16) != 0;
+    float w = (b4 ? a1 : a0) + __shfl_xor(b4 ? a0 : a1, 16);
+#define K3_DPP(x, ctrl) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xf, 0xf, false))
+    w += K3_DPP(w, 0xb1);   // quad [1,0,3,2]
+    w += K3_DPP(w, 0x4e);   // quad [2,3,0,1]
+    w += K3_DPP(w, 0x141);  // row_half_mirror
+    w += K3_DPP(w, 0x140);  // row_mirror
+#undef K3_DPP
+    return w;
+}
+
 // ---------------------------------------------------------------------------
 // G: the routed experts' gate/up rows, one E8M0 block of a slot's activation
 // per 4-wave block: block q of slot j takes rows [32 q', 32 q' + 32) of gate
@@ -393,7 +426,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
 // LDS and one pass sums them in router order, adds the shared row and
 // applies the epilogue.
 constexpr int kDecDnWaves = 16;            // one slot per wave
-constexpr int kDecDnDepth = 4;             // rows in flight per wave
+constexpr int kDecDnDepth = 4;             // rows in flight per wave (diag_sum4 takes four)
 constexpr int kDecDnRowsMax = 32;          // rows a block owns, at most
 constexpr int kDecShRows = kDecDnRowsMax / kDecDnWaves;  // shared rows per wave
 constexpr int kDecShSl = 4;                // 512-element slices of a shared row (I_s <= 2048)
@@ -491,6 +524,7 @@ __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
 
     for (int r = 0; r < nrow; r += kDecDnDepth) {
         prio_left(nrow - r, nrow);
+        v4f acc[kDecDnDepth];
 #pragma unroll
         for (int d = 0; d < kDecDnDepth; ++d) {
             const bool drop = buf[d].s == 255u;  // E8M0 255: the group contributes nothing
@@ -498,13 +532,14 @@ __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
             const u4 av = drop ? u4{0u, 0u, 0u, 0u} : a;
             const int sa = drop ? 127 : (int)buf[d].s;
             const v8i A = v8i{(int)av.x, (int)av.y, (int)av.z, (int)av.w, 0, 0, 0, 0};
-            v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+            acc[d] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int t = 0; t < kDecTerms; ++t) acc = mfma_fp4_fp8(A, bt[t], acc, sa, bs[t]);
+            for (int t = 0; t < kDecTerms; ++t) acc[d] = mfma_fp4_fp8(A, bt[t], acc[d], sa, bs[t]);
             load(r + d + kDecDnDepth, buf[d]);
-            const float y = diag_sum(acc);
-            if (lane == 0 && r + d < nr && has) y_l[wave * p.RB + r + d] = ok ? y : 0.0f;
         }
+        const float y = diag_sum4(acc);  // lane group k: row r + k
+        const int rk = r + (lane >> 4);
+        if ((lane & 15) == 0 && rk < nr && has) y_l[wave * p.RB + rk] = ok ? y : 0.0f;
     }
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // the staged weights and activation
