@@ -424,12 +424,15 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
 // of the block (wave w: rows w and w + NW) are loaded first, while the routes
 // are read, and multiplied after the routed rows. The per-slot results go to
 // LDS and one pass sums them in router order, adds the shared row and
-// applies the epilogue.
+// applies the epilogue. Every load before the routed loop is unconditional
+// (clamped addresses, a compile-time slice count, the routing weights and
+// the shared activation held in registers and written to LDS after the
+// loop), so the compiler's wait counts keep the rows in flight instead of
+// draining them at a branch.
 constexpr int kDecDnWaves = 16;            // one slot per wave
 constexpr int kDecDnDepth = 4;             // rows in flight per wave (diag_sum4 takes four)
 constexpr int kDecDnRowsMax = 32;          // rows a block owns, at most
 constexpr int kDecShRows = kDecDnRowsMax / kDecDnWaves;  // shared rows per wave
-constexpr int kDecShSl = 4;                // 512-element slices of a shared row (I_s <= 2048)
 
 struct DecDnParams {
     const uint8_t *dp, *ds;
@@ -447,6 +450,9 @@ struct DecDnParams {
     unsigned long long *errors;
 };
 
+// NSS: 512-element slices of a shared row, ceil(I_s / 512) <= 4 (0: no
+// shared expert)
+template <int NSS>
 __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
 {
     extern __shared__ __align__(16) float y_l[];  // [K][RB], then (16-byte aligned) the shared activation [Is]
@@ -456,47 +462,10 @@ __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
     const int r0 = blockIdx.x * p.RB, nr = min(p.RB, p.H - r0);
     const bool has = wave < p.K;  // this wave's slot exists (else it computes slot 0 and drops it)
     const int jj = has ? wave : 0;
-    const int e0 = p.idx[jj];
-    const bool ok = has && e0 >= 0 && e0 < p.E;  // an id outside [0, E) adds nothing
-    const int e = ok ? e0 : 0;
-
-    // the shared expert's rows of this block: wave w takes rows r0 + w + NW k
-    __shared__ float sh_l[kDecDnRowsMax];
-    float *ash_l = y_l + ((p.K * p.RB + 3) & ~3);  // 16-byte aligned
-    const int NSS = (p.Is + 511) >> 9;
-    u4 shw[kDecShRows][kDecShSl];
-    if (p.Is > 0) {
-#pragma unroll
-        for (int k = 0; k < kDecShRows; ++k) {
-            const int r = r0 + min(wave + kDecDnWaves * k, nr - 1);
-#pragma unroll
-            for (int sl = 0; sl < kDecShSl; ++sl) {
-                const bool son = sl < NSS && 512 * sl + 8 * lane < p.Is;
-                shw[k][sl] = ld16(p.sh_down + (size_t)r * p.Is + (son ? 512 * sl + 8 * lane : 0));
-            }
-        }
-    }
-
-    // the rows' first loads; loads past the last row re-read it (never
-    // used). Lanes past I/32 read group 0 of the row and meet a zero B operand.
     const bool on = lane < NG;
-    const int nrow = max(nr, 1);
-    const uint8_t *pa = p.dp + (int64_t)e * p.d_sp + (on ? 16 * lane : 0);
-    const uint8_t *ps = p.ds + (int64_t)e * p.d_ss + (on ? lane : 0);
-    struct Row {
-        u4 a;
-        uint32_t s;
-    };
-    auto load = [&](int rr, Row &b) {
-        const size_t r = (size_t)(r0 + min(rr, nrow - 1));
-        b.a = ld16(pa + r * IB);
-        b.s = ps[r * NG];
-    };
-    Row buf[kDecDnDepth];
-#pragma unroll
-    for (int d = 0; d < kDecDnDepth; ++d) load(d, buf[d]);
 
-    // the slot's B operands: the e4m3 terms arranged for the diagonal
+    // the slot's B operands: the e4m3 terms arranged for the diagonal (the
+    // first loads, so that using them waits for nothing else)
     v8i bt[kDecTerms];
     int bs[kDecTerms];
     {
@@ -513,14 +482,55 @@ __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
         }
     }
 
-    // the routing weights and the shared activation, staged in LDS while
-    // the rows stream (read after the block barrier below)
-    if (threadIdx.x < p.K) {
-        const int ej = p.idx[threadIdx.x];
-        wk_l[threadIdx.x] = (ej >= 0 && ej < p.E) ? p.w[threadIdx.x] : 0.0f;
+    const int e0 = p.idx[jj];
+
+    // the shared expert's rows of this block: wave w takes rows r0 + w + NW k,
+    // issued before the wait for the expert id (the barrier keeps them there)
+    __shared__ float sh_l[kDecDnRowsMax];
+    float *ash_l = y_l + ((p.K * p.RB + 3) & ~3);  // 16-byte aligned
+    u4 shw[kDecShRows][NSS > 0 ? NSS : 1];
+    if constexpr (NSS > 0) {
+#pragma unroll
+        for (int k = 0; k < kDecShRows; ++k) {
+            const int r = r0 + min(wave + kDecDnWaves * k, nr - 1);
+#pragma unroll
+            for (int sl = 0; sl < NSS; ++sl) {
+                const bool son = 512 * sl + 8 * lane < p.Is;
+                shw[k][sl] = ld16(p.sh_down + (size_t)r * p.Is + (son ? 512 * sl + 8 * lane : 0));
+            }
+        }
     }
-    for (int i = threadIdx.x; 4 * i < p.Is; i += blockDim.x)
-        reinterpret_cast<float4 *>(ash_l)[i] = reinterpret_cast<const float4 *>(p.ash)[i];
+    __builtin_amdgcn_sched_barrier(0);
+    const bool ok = has && e0 >= 0 && e0 < p.E;  // an id outside [0, E) adds nothing
+    const int e = ok ? e0 : 0;
+
+    // the rows' first loads; loads past the last row re-read it (never
+    // used). Lanes past I/32 read group 0 of the row and meet a zero B operand.
+    const int nrow = max(nr, 1);
+    const uint8_t *pa = p.dp + (int64_t)e * p.d_sp + (on ? 16 * lane : 0);
+    const uint8_t *ps = p.ds + (int64_t)e * p.d_ss + (on ? lane : 0);
+    struct Row {
+        u4 a;
+        uint32_t s;
+    };
+    auto load = [&](int rr, Row &b) {
+        const size_t r = (size_t)(r0 + min(rr, nrow - 1));
+        b.a = ld16(pa + r * IB);
+        b.s = ps[r * NG];
+    };
+    Row buf[kDecDnDepth];
+#pragma unroll
+    for (int d = 0; d < kDecDnDepth; ++d) load(d, buf[d]);
+
+    // the routing weights and the shared activation (4 I_s <= 64 NW
+    // elements: one float4 per thread at most), loaded now and written to
+    // LDS after the routed rows
+    const int tk = min((int)threadIdx.x, p.K - 1);
+    const int ek = p.idx[tk];
+    const float wkv = p.w[tk];
+    float4 ashv = float4{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (NSS > 0)
+        ashv = reinterpret_cast<const float4 *>(p.ash)[min((int)threadIdx.x, (p.Is >> 2) - 1)];
 
     for (int r = 0; r < nrow; r += kDecDnDepth) {
         prio_left(nrow - r, nrow);
@@ -542,14 +552,16 @@ __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
         if ((lane & 15) == 0 && rk < nr && has) y_l[wave * p.RB + rk] = ok ? y : 0.0f;
     }
     __builtin_amdgcn_s_setprio(0);
+    if (threadIdx.x < p.K) wk_l[threadIdx.x] = (ek >= 0 && ek < p.E) ? wkv : 0.0f;
+    if (4 * (int)threadIdx.x < p.Is) reinterpret_cast<float4 *>(ash_l)[threadIdx.x] = ashv;
     __syncthreads();  // the staged weights and activation
-    if (p.Is > 0) {  // the shared rows: fp32 products in slice order, one wave-wide sum per row
+    if constexpr (NSS > 0) {  // the shared rows: fp32 products in slice order, one wave-wide sum per row
 #pragma unroll
         for (int k = 0; k < kDecShRows; ++k) {
             float acc = 0.0f;
 #pragma unroll
-            for (int sl = 0; sl < kDecShSl; ++sl) {
-                const bool son = sl < NSS && 512 * sl + 8 * lane < p.Is;
+            for (int sl = 0; sl < NSS; ++sl) {
+                const bool son = 512 * sl + 8 * lane < p.Is;
                 const int i = son ? 512 * sl + 8 * lane : 0;
                 const uint32_t msk = lane_mask(son);  // off lanes: a zero activation
                 const u4 a0 = ld16m(ash_l + i, msk), a1 = ld16m(ash_l + i + 4, msk);
@@ -573,7 +585,7 @@ __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
     for (int r = threadIdx.x; r < nr; r += blockDim.x) {
         float acc = 0.0f;
         for (int j = 0; j < p.K; ++j) acc = fmaf(wk_l[j], y_l[j * p.RB + r], acc);  // a dropped slot: 0 * 0
-        if (p.Is > 0) acc += sh_l[r];  // row r0 + r: wave r % NW, k = r / NW
+        if (NSS > 0) acc += sh_l[r];  // row r0 + r: wave r % NW, k = r / NW
         float *op = p.out + r0 + r;
         if (p.resid) acc = *op + acc;
         *op = acc;
@@ -692,7 +704,13 @@ hipError_t launch_decode_fused(const LayerView &L, const uint16_t *x, int32_t *i
         dp.ob = epi.ob;
         dp.errors = L.errors;
         const unsigned grid = (unsigned)((L.H + dp.RB - 1) / dp.RB);
-        k_dec_down<<<grid, 64 * kDecDnWaves, sizeof(float) * (((L.K * dp.RB + 3) & ~3) + L.Is), s>>>(dp);
+        const size_t lds = sizeof(float) * (((L.K * dp.RB + 3) & ~3) + L.Is);
+        const int nss = (L.Is + 511) / 512;
+        if (nss == 0) k_dec_down<0><<<grid, 64 * kDecDnWaves, lds, s>>>(dp);
+        else if (nss == 1) k_dec_down<1><<<grid, 64 * kDecDnWaves, lds, s>>>(dp);
+        else if (nss == 2) k_dec_down<2><<<grid, 64 * kDecDnWaves, lds, s>>>(dp);
+        else if (nss == 3) k_dec_down<3><<<grid, 64 * kDecDnWaves, lds, s>>>(dp);
+        else k_dec_down<4><<<grid, 64 * kDecDnWaves, lds, s>>>(dp);
     }
     return hipGetLastError();
 }
