@@ -591,9 +591,10 @@ __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
         *op = acc;
         if (p.ob) p.ob[r0 + r] = bf16_rne(acc);
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0)
-        for (int j = 0; j < p.K; ++j)
-            if (p.idx[j] < 0 || p.idx[j] >= p.E) atomicAdd(p.errors, 1ull);
+    // ids outside [0, E), counted once: thread j of block 0 checks slot j
+    // (the id it already holds; a serial loop of loads here would hold the
+    // block's end by one cache round trip per slot)
+    if (blockIdx.x == 0 && threadIdx.x < p.K && (ek < 0 || ek >= p.E)) atomicAdd(p.errors, 1ull);
 }
 
 }  // namespace

@@ -1095,9 +1095,11 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(const float *__rest
                 make_uint2(bf16_rne_u32(acc.x) | (bf16_rne_u32(acc.y) << 16),
                            bf16_rne_u32(acc.z) | (bf16_rne_u32(acc.w) << 16));
     }
-    if (blockIdx.x == 0)
-        for (int64_t a = threadIdx.x; a < (int64_t)T * K; a += kCombineThreads)
-            if (idx[a] < 0 || idx[a] >= E) atomicAdd(errors, 1ull);
+    // ids outside [0, E), counted once each, spread over the grid (one
+    // assignment per thread: the grid has T H/4 >= T K threads; a loop in one
+    // block would hold the kernel's end by a cache round trip per iteration)
+    for (int64_t a = i4; a < (int64_t)T * K; a += (int64_t)gridDim.x * kCombineThreads)
+        if (idx[a] < 0 || idx[a] >= E) atomicAdd(errors, 1ull);
 }
 
 }  // namespace
