@@ -267,7 +267,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             const int i = 512 * s + 8 * lane;
-            shw[s] = ld16(r + (i < H ? i : 0));  // off lanes meet a zero token
+            shw[s] = ld16_stream(r + (i < H ? i : 0));  // off lanes meet a zero token
         }
     };
     if (wave != 0 && wave < nsr) sh_load(wave);
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
     auto load = [&](int r, Row &b) {
         const size_t ro = (size_t)min(r, kDecUnitRows - 1) * HB;
 #pragma unroll
-        for (int s = 0; s < kDecGuPieces; ++s) b.a[s] = ld16(wbase + ro + soff[s]);
+        for (int s = 0; s < kDecGuPieces; ++s) b.a[s] = ld16_stream(wbase + ro + soff[s]);
     };
     constexpr int GD = 2;  // rows in flight (four measured slower)
     Row bq[GD];
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
 #pragma unroll
     for (int k = 0; k < SQ; ++k) {
         const int i = 16 * lane + 1024 * k;
-        scv[k] = ld16(sbase + (i < H / 2 ? i : 0));
+        scv[k] = ld16_stream(sbase + (i < H / 2 ? i : 0));
     }
     constexpr int XQ = (NS * 64 + 255) / 256;
     {
@@ -496,7 +496,7 @@ __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
 #pragma unroll
             for (int sl = 0; sl < NSS; ++sl) {
                 const bool son = 512 * sl + 8 * lane < p.Is;
-                shw[k][sl] = ld16(p.sh_down + (size_t)r * p.Is + (son ? 512 * sl + 8 * lane : 0));
+                shw[k][sl] = ld16_stream(p.sh_down + (size_t)r * p.Is + (son ? 512 * sl + 8 * lane : 0));
             }
         }
     }
@@ -515,8 +515,8 @@ __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
     };
     auto load = [&](int rr, Row &b) {
         const size_t r = (size_t)(r0 + min(rr, nrow - 1));
-        b.a = ld16(pa + r * IB);
-        b.s = ps[r * NG];
+        b.a = ld16_stream(pa + r * IB);
+        b.s = ps[r * NG];  // 48 bytes, sharing lines with the next rows' (a plain load)
     };
     Row buf[kDecDnDepth];
 #pragma unroll

@@ -48,7 +48,9 @@ namespace {
 // of the router row and the token, exact bf16 products summed in fp64, a
 // fixed-order butterfly across the wave. Lane 0 then forms the fp32 logit,
 // the fp32 score (sigmoid evaluated in fp64, rounded once) and the fp32
-// selection score.
+// selection score. NT: one token, so each router row is read once (a
+// streaming load); with more tokens the rows are read once per token.
+template <bool NT>
 __global__ __launch_bounds__(256) void k_router(const uint16_t *__restrict__ x,
                                                 const uint16_t *__restrict__ Wr,
                                                 const float *__restrict__ bias, int H, int E,
@@ -68,7 +70,10 @@ __global__ __launch_bounds__(256) void k_router(const uint16_t *__restrict__ x,
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int i = i0 + 512 * c;
-            wv[c] = i < H ? *reinterpret_cast<const u4 *>(wr + i) : u4{0u, 0u, 0u, 0u};
+            if constexpr (NT)
+                wv[c] = i < H ? ld16_stream(wr + i) : u4{0u, 0u, 0u, 0u};
+            else
+                wv[c] = i < H ? *reinterpret_cast<const u4 *>(wr + i) : u4{0u, 0u, 0u, 0u};
             xv[c] = i < H ? *reinterpret_cast<const u4 *>(xr + i) : u4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
@@ -1151,8 +1156,12 @@ hipError_t launch_route(const LayerView &L, const uint16_t *x, int T, int32_t *i
     {
         StageMark m(prof, K3MOE_STAGE_ROUTER, s);
         if (T <= kRouterWaveMaxT) {
-            k_router<<<dim3((L.E + 3) / 4, T), 256, 0, s>>>(x, L.router_w, L.router_bias, L.H, L.E, sc,
-                                                            ch, logits);
+            if (T == 1)
+                k_router<true><<<dim3((L.E + 3) / 4, 1), 256, 0, s>>>(x, L.router_w, L.router_bias, L.H, L.E,
+                                                                      sc, ch, logits);
+            else
+                k_router<false><<<dim3((L.E + 3) / 4, T), 256, 0, s>>>(x, L.router_w, L.router_bias, L.H, L.E,
+                                                                       sc, ch, logits);
         } else {
             static const bool lds_set = set_router_lds();  // once per process (thread-safe static)
             (void)lds_set;
@@ -1186,7 +1195,8 @@ hipError_t launch_route(const LayerView &L, const uint16_t *x, int T, int32_t *i
 hipError_t launch_router_t1(const LayerView &L, const uint16_t *x, float *sc, float *ch, float *logits,
                             hipStream_t s)
 {
-    k_router<<<dim3((L.E + 3) / 4, 1), 256, 0, s>>>(x, L.router_w, L.router_bias, L.H, L.E, sc, ch, logits);
+    k_router<true><<<dim3((L.E + 3) / 4, 1), 256, 0, s>>>(x, L.router_w, L.router_bias, L.H, L.E, sc, ch,
+                                                          logits);
     return hipGetLastError();
 }
 

@@ -137,7 +137,7 @@ __global__ __launch_bounds__(kPnThreads) void k_prenorm_router(const float *__re
 #pragma unroll
     for (int c = 0; c < kPrSl; ++c) {
         const int i = 8 * lane + 512 * c;
-        wv[c] = i < n ? *reinterpret_cast<const u4 *>(wr + i) : u4{0u, 0u, 0u, 0u};
+        wv[c] = i < n ? ld16_stream(wr + i) : u4{0u, 0u, 0u, 0u};
     }
     const float4 *a = reinterpret_cast<const float4 *>(h);
     const float4 *gm = reinterpret_cast<const float4 *>(gamma);
