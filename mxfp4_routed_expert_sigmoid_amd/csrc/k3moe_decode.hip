@@ -65,7 +65,6 @@ __device__ __forceinline__ u4 ld16m(const void *p, uint32_t m)
     const u4 v = *reinterpret_cast<const u4 *>(p);
     return u4{v.x & m, v.y & m, v.z & m, v.w & m};
 }
-__device__ __forceinline__ u4 ld16(const void *p) { return *reinterpret_cast<const u4 *>(p); }
 
 // Sum over the wave, fixed order, through DPP (quad steps, half-row and row
 // mirrors, then the row broadcasts into lane 63), read back from lane 63.
@@ -297,13 +296,16 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
     const int row0 = 32 * qb + kDecUnitRows * half;
     const uint8_t *sbase = (mat ? p.us + (int64_t)e * p.u_ss : p.gs + (int64_t)e * p.g_ss) + (size_t)row0 * HG;
     const uint8_t *wbase = (mat ? p.up + (int64_t)e * p.u_sp : p.gp + (int64_t)e * p.g_sp) + (size_t)row0 * HB;
-    int soff[kDecGuPieces];        // this lane's offset in a row piece (off lanes: 0)
+    int soff[kDecGuPieces];        // this lane's offset in a row piece (off lanes: the last on lane's)
     int gidx[kDecGuPieces];        // this lane's E8M0 group (off lanes: 0)
     uint32_t smask[kDecGuPieces];  // off lanes scale their weights by 0
 #pragma unroll
     for (int s = 0; s < kDecGuPieces; ++s) {
         const bool on = 64 * s + lane < HG;
-        soff[s] = on ? 1024 * s + 16 * lane : 0;
+        // an off lane repeats the last on lane's address (in the same
+        // instruction when the piece has on lanes, so no line is fetched
+        // twice: the streaming loads leave nothing in the caches to re-read)
+        soff[s] = min(1024 * s + 16 * lane, HB - 16);
         gidx[s] = on ? 64 * s + lane : 0;
         smask[s] = lane_mask(on);
     }
@@ -324,7 +326,7 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
 #pragma unroll
     for (int k = 0; k < SQ; ++k) {
         const int i = 16 * lane + 1024 * k;
-        scv[k] = ld16_stream(sbase + (i < H / 2 ? i : 0));
+        scv[k] = ld16_stream(sbase + min(i, H / 2 - 16));  // off lanes: the last on lane's address
     }
     constexpr int XQ = (NS * 64 + 255) / 256;
     {
@@ -389,12 +391,15 @@ __global__ __launch_bounds__(256, 3) void k_dec_gateup(DecGuParams p)
         const float v = diag_sum(acc);
         mine = lane == r ? v : mine;
     };
+    // fully unrolled: the rows' next loads stop at the last row (a load past
+    // it would re-read a row the streaming loads have not kept)
+#pragma unroll
     for (int r = 0; r < kDecUnitRows; r += GD) {
         prio_left(kDecUnitRows - r, kDecUnitRows);
 #pragma unroll
         for (int d = 0; d < GD; ++d) {
             compute(r + d, bq[d]);
-            load(r + d + GD, bq[d]);
+            if (r + d + GD < kDecUnitRows) load(r + d + GD, bq[d]);
         }
     }
     __builtin_amdgcn_s_setprio(0);
@@ -532,7 +537,11 @@ __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
     if constexpr (NSS > 0)
         ashv = reinterpret_cast<const float4 *>(p.ash)[min((int)threadIdx.x, (p.Is >> 2) - 1)];
 
-    for (int r = 0; r < nrow; r += kDecDnDepth) {
+    // rows r .. r + 3; NEXT: issue each row's successor in the ring (the
+    // last group issues none: a load past the last row would re-read a row
+    // the streaming loads have not kept)
+    auto four = [&](int r, auto next_c) {
+        constexpr bool NEXT = decltype(next_c)::value;
         prio_left(nrow - r, nrow);
         v4f acc[kDecDnDepth];
 #pragma unroll
@@ -545,12 +554,15 @@ __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
             acc[d] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int t = 0; t < kDecTerms; ++t) acc[d] = mfma_fp4_fp8(A, bt[t], acc[d], sa, bs[t]);
-            load(r + d + kDecDnDepth, buf[d]);
+            if constexpr (NEXT) load(r + d + kDecDnDepth, buf[d]);
         }
         const float y = diag_sum4(acc);  // lane group k: row r + k
         const int rk = r + (lane >> 4);
         if ((lane & 15) == 0 && rk < nr && has) y_l[wave * p.RB + rk] = ok ? y : 0.0f;
-    }
+    };
+    int r = 0;
+    for (; r + kDecDnDepth < nrow; r += kDecDnDepth) four(r, std::true_type{});
+    four(r, std::false_type{});
     __builtin_amdgcn_s_setprio(0);
     if (threadIdx.x < p.K) wk_l[threadIdx.x] = (ek >= 0 && ek < p.E) ? wkv : 0.0f;
     if (4 * (int)threadIdx.x < p.Is) reinterpret_cast<float4 *>(ash_l)[threadIdx.x] = ashv;
