@@ -609,6 +609,155 @@ __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
     if (blockIdx.x == 0 && threadIdx.x < p.K && (ek < 0 || ek >= p.E)) atomicAdd(p.errors, 1ull);
 }
 
+
+// ---------------------------------------------------------------------------
+// Gate/up of a batch's light experts that hold exactly one assignment: G's
+// routed rows without the top-k and the shared rows. Block (item li, unit
+// qb) takes rows [32 qb, 32 qb + 32) of gate and up of the item's expert for
+// its one token; wave w streams one matrix (w & 1) over 16 rows (w >> 1), two
+// rows in flight, each 1 KB row piece as 4 bf16 MFMAs after the exact fp4 ->
+// bf16 expansion (the diagonal dot product), with the token at the lanes' K
+// positions in registers; wave 0 then writes the 32 activations as bf16 hi
+// and lo, the rows the streamed down projection reads. The rows are read in
+// whole 1 KB pieces (the many-token streaming kernel reads 64 bytes of 16
+// rows per instruction), so the streaming loads apply.
+struct GuOneParams {
+    const uint8_t *gp, *gs, *up, *us;
+    int64_t g_sp, g_ss, u_sp, u_ss;
+    int H, I, K, act;
+    float b1, b2;
+    const uint16_t *x;                             // tokens, bf16 [T][H]
+    const int32_t *active_e, *active_off, *sorted;
+    const int32_t *items, *items_n;                // the items (active-list positions), their count
+    uint16_t *act_hi, *act_lo;                     // [assignment][I]
+};
+
+__host__ __device__ constexpr int gu_one_lds_bytes(int H, int NS) { return 2 * H + 4 * 16 * 4 + NS * 64 * 16; }
+
+// NS: 512-element token slices (H <= 512 NS)
+template <int NS>
+__global__ __launch_bounds__(256, 3) void k_gu_one(GuOneParams p)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int NG = p.I >> 5;
+    const int li = blockIdx.x / NG, qb = blockIdx.x - li * NG;
+    if (li >= *p.items_n) return;  // the grid covers the most items a batch can have
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int H = p.H, HB = H >> 1, HG = H >> 5;  // packed bytes and E8M0 groups per row
+    const int mat = wave & 1, half = wave >> 1;
+    uint8_t *sc_l = lds + wave * (H / 2);                                  // this wave's 16 E8M0 rows
+    float *sum_l = reinterpret_cast<float *>(lds + 2 * H);                 // [4][16]
+    u4 *x_l = reinterpret_cast<u4 *>(sum_l + 4 * kDecUnitRows);            // [NS][64]
+    const int q = p.items[li];
+    const int e = p.active_e[q], off = p.active_off[q];
+    const int t = p.sorted[off] / p.K;  // the assignment's token
+
+    // the rows' first loads, the wave's 16 E8M0 rows (contiguous), the token
+    const int row0 = 32 * qb + kDecUnitRows * half;
+    const uint8_t *sbase = (mat ? p.us + (int64_t)e * p.u_ss : p.gs + (int64_t)e * p.g_ss) + (size_t)row0 * HG;
+    const uint8_t *wbase = (mat ? p.up + (int64_t)e * p.u_sp : p.gp + (int64_t)e * p.g_sp) + (size_t)row0 * HB;
+    int soff[kDecGuPieces];        // this lane's offset in a row piece (off lanes: the last on lane's)
+    int gidx[kDecGuPieces];        // this lane's E8M0 group (off lanes: 0)
+    uint32_t smask[kDecGuPieces];  // off lanes scale their weights by 0
+#pragma unroll
+    for (int s = 0; s < kDecGuPieces; ++s) {
+        const bool on = 64 * s + lane < HG;
+        soff[s] = min(1024 * s + 16 * lane, HB - 16);
+        gidx[s] = on ? 64 * s + lane : 0;
+        smask[s] = lane_mask(on);
+    }
+    struct Row {
+        u4 a[kDecGuPieces];
+    };
+    auto load = [&](int r, Row &b) {
+        const size_t ro = (size_t)r * HB;
+#pragma unroll
+        for (int s = 0; s < kDecGuPieces; ++s) b.a[s] = ld16_stream(wbase + ro + soff[s]);
+    };
+    // issue order: the token (cache hits), the E8M0 rows, then the routed
+    // rows, so the LDS stores wait only for the first two and the rows stay
+    // in flight across the barrier (memory counters retire in issue order)
+    constexpr int XQ = (NS * 64 + 255) / 256;
+    const uint16_t *xt = p.x + (size_t)t * H;
+    u4 xs[XQ];
+#pragma unroll
+    for (int k = 0; k < XQ; ++k) {
+        const int i = threadIdx.x + 256 * k;
+        const bool on = i < NS * 64 && 8 * i < H;
+        xs[k] = ld16m(xt + (on ? 8 * i : 0), lane_mask(on));
+    }
+    constexpr int SQ = 8192 / 2 / 1024;  // 16-byte pieces per lane (H <= 8192)
+    u4 scv[SQ];
+#pragma unroll
+    for (int k = 0; k < SQ; ++k) {
+        const int i = 16 * lane + 1024 * k;
+        scv[k] = ld16_stream(sbase + min(i, H / 2 - 16));  // off lanes: the last on lane's address
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keeps that issue order
+    constexpr int GD = 2;  // rows in flight
+    Row bq[GD];
+#pragma unroll
+    for (int d = 0; d < GD; ++d) load(d, bq[d]);
+#pragma unroll
+    for (int k = 0; k < XQ; ++k) {
+        const int i = threadIdx.x + 256 * k;
+        if (i < NS * 64) x_l[i] = xs[k];
+    }
+#pragma unroll
+    for (int k = 0; k < SQ; ++k) {
+        const int i = 16 * lane + 1024 * k;
+        if (i < H / 2) *reinterpret_cast<u4 *>(sc_l + i) = scv[k];
+    }
+    __syncthreads();  // the token slices and this wave's E8M0 rows
+
+    // the token at this lane's K positions (lane l of row piece s: elements
+    // 2048 s + 32 l + [0, 32))
+    u4 xv[kDecGuPieces][4];
+#pragma unroll
+    for (int s = 0; s < kDecGuPieces; ++s)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int i = 2048 * s + 32 * lane + 8 * c;
+            xv[s][c] = ld16m(x_l + (i < H ? i / 8 : 0), lane_mask(i < H));
+        }
+
+    float mine = 0.0f;
+    auto compute = [&](int r, const Row &b) {
+        v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < kDecGuPieces; ++s) {
+            const float f = __uint_as_float(__float_as_uint(e8m0_to_f32(sc_l[r * HG + gidx[s]])) & smask[s]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc = mfma_bf16(dequant8_bf16(b.a[s][c], f), as_bf8(xv[s][c]), acc);
+        }
+        const float v = diag_sum(acc);
+        mine = lane == r ? v : mine;
+    };
+    // fully unrolled: the rows' next loads stop at the last row
+#pragma unroll
+    for (int r = 0; r < kDecUnitRows; r += GD) {
+        prio_left(kDecUnitRows - r, kDecUnitRows);
+#pragma unroll
+        for (int d = 0; d < GD; ++d) {
+            compute(r + d, bq[d]);
+            if (r + d + GD < kDecUnitRows) load(r + d + GD, bq[d]);
+        }
+    }
+    __builtin_amdgcn_s_setprio(0);
+    if (lane < kDecUnitRows) sum_l[wave * kDecUnitRows + lane] = mine;
+    __syncthreads();
+
+    // wave 0, lane l < 32: row 32 qb + l (half l / 16, row l % 16)
+    if (wave == 0 && lane < 32) {
+        const int hl = lane >> 4, rl = lane & 15;
+        const float g = sum_l[(2 * hl) * kDecUnitRows + rl], u = sum_l[(2 * hl + 1) * kDecUnitRows + rl];
+        const float a = act_fn(g, u, p.act, p.b1, p.b2);
+        const uint16_t h = bf16_rne(a);
+        const size_t o = (size_t)off * p.I + 32 * qb + lane;
+        p.act_hi[o] = h;
+        p.act_lo[o] = bf16_rne(a - bf16f(h));
+    }
+}
 }  // namespace
 
 // The shapes the three kernels take: a flat layer, H <= 8192 (four 1 KB
@@ -725,6 +874,49 @@ hipError_t launch_decode_fused(const LayerView &L, const uint16_t *x, int32_t *i
         else if (nss == 3) k_dec_down<3><<<grid, 64 * kDecDnWaves, lds, s>>>(dp);
         else k_dec_down<4><<<grid, 64 * kDecDnWaves, lds, s>>>(dp);
     }
+    return hipGetLastError();
+}
+
+
+// Gate/up of the light items with one assignment (a flat layer: the routed
+// input is x itself).
+bool gu_one_ok(const LayerView &L) { return L.Lt == 0 && L.H <= 8192 && L.H % 128 == 0 && L.I % 32 == 0; }
+
+hipError_t launch_gu_one(const LayerView &L, const uint16_t *x, int T, const int32_t *active_e,
+                         const int32_t *active_off, const int32_t *sorted, const int32_t *items,
+                         const int32_t *items_n, uint16_t *act_hi, uint16_t *act_lo, hipStream_t s)
+{
+    GuOneParams p{};
+    p.gp = L.gp;
+    p.gs = L.gs;
+    p.up = L.up;
+    p.us = L.us;
+    p.g_sp = L.g_sp;
+    p.g_ss = L.g_ss;
+    p.u_sp = L.u_sp;
+    p.u_ss = L.u_ss;
+    p.H = L.H;
+    p.I = L.I;
+    p.K = L.K;
+    p.act = L.act;
+    p.b1 = L.b1;
+    p.b2 = L.b2;
+    p.x = x;
+    p.active_e = active_e;
+    p.active_off = active_off;
+    p.sorted = sorted;
+    p.items = items;
+    p.items_n = items_n;
+    p.act_hi = act_hi;
+    p.act_lo = act_lo;
+    const int64_t cap = std::min<int64_t>(L.E, (int64_t)T * L.K);  // the most items a batch can have
+    const unsigned nb = (unsigned)(cap * (L.I / 32));
+    const int NS = L.H <= 2048 ? 4 : L.H <= 4096 ? 8 : L.H <= 7168 ? 14 : 16;
+    const size_t lds = gu_one_lds_bytes(L.H, NS);
+    if (NS == 4) k_gu_one<4><<<nb, 256, lds, s>>>(p);
+    else if (NS == 8) k_gu_one<8><<<nb, 256, lds, s>>>(p);
+    else if (NS == 14) k_gu_one<14><<<nb, 256, lds, s>>>(p);
+    else k_gu_one<16><<<nb, 256, lds, s>>>(p);
     return hipGetLastError();
 }
 
