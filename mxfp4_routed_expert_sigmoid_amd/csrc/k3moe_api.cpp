@@ -83,8 +83,8 @@ WsLayout ws_layout(const k3moe_config &c, int64_t T)
     }
     L.tiles_gu = take(sizeof(int2) * grouped_tile_cap_gu(T, (int)K, (int)E));
     L.tiles_dn = take(sizeof(int2) * grouped_tile_cap_dn(T, (int)K, (int)E));
-    L.light = take(sizeof(int32_t) * 3 * E);
-    L.tile_n = take(5 * sizeof(int32_t));
+    L.light = take(sizeof(int32_t) * 4 * E);
+    L.tile_n = take(6 * sizeof(int32_t));
     L.aq = take((size_t)T * K * kATerms * I);
     L.aqs = take((size_t)T * K * kATerms * (I / 32));
     if (Lt > 0) {

@@ -611,16 +611,17 @@ __global__ __launch_bounds__(64 * kDecDnWaves) void k_dec_down(DecDnParams p)
 
 
 // ---------------------------------------------------------------------------
-// Gate/up of a batch's light experts that hold exactly one assignment: G's
-// routed rows without the top-k and the shared rows. Block (item li, unit
-// qb) takes rows [32 qb, 32 qb + 32) of gate and up of the item's expert for
-// its one token; wave w streams one matrix (w & 1) over 16 rows (w >> 1), two
-// rows in flight, each 1 KB row piece as 4 bf16 MFMAs after the exact fp4 ->
-// bf16 expansion (the diagonal dot product), with the token at the lanes' K
-// positions in registers; wave 0 then writes the 32 activations as bf16 hi
-// and lo, the rows the streamed down projection reads. The rows are read in
-// whole 1 KB pieces (the many-token streaming kernel reads 64 bytes of 16
-// rows per instruction), so the streaming loads apply.
+// Gate/up of a batch's light experts that hold one or two assignments (NT):
+// G's routed rows without the top-k and the shared rows. Block (item li,
+// unit qb) takes rows [32 qb, 32 qb + 32) of gate and up of the item's expert
+// for its NT tokens; wave w streams one matrix (w & 1) over 16 rows (w >> 1),
+// two rows in flight, each 1 KB row piece as 4 bf16 MFMAs per token after the
+// exact fp4 -> bf16 expansion (the diagonal dot product), the first token at
+// the lanes' K positions in registers, the second read from LDS per use;
+// wave 0 then writes the 32 NT activations as bf16 hi and lo, the rows the
+// streamed down projection reads. The rows are read in whole 1 KB pieces
+// (the many-token streaming kernel reads 64 bytes of 16 rows per
+// instruction), so the streaming loads apply.
 struct GuOneParams {
     const uint8_t *gp, *gs, *up, *us;
     int64_t g_sp, g_ss, u_sp, u_ss;
@@ -632,10 +633,14 @@ struct GuOneParams {
     uint16_t *act_hi, *act_lo;                     // [assignment][I]
 };
 
-__host__ __device__ constexpr int gu_one_lds_bytes(int H, int NS) { return 2 * H + 4 * 16 * 4 + NS * 64 * 16; }
+// the 4 waves' E8M0 rows, the sums [NT][4][16], the tokens [NT][NS][64] u4
+__host__ __device__ constexpr int gu_one_lds_bytes(int H, int NS, int NT)
+{
+    return 2 * H + NT * 4 * 16 * 4 + NT * NS * 64 * 16;
+}
 
-// NS: 512-element token slices (H <= 512 NS)
-template <int NS>
+// NS: 512-element token slices (H <= 512 NS); NT: assignments per item (1, 2)
+template <int NS, int NT>
 __global__ __launch_bounds__(256, 3) void k_gu_one(GuOneParams p)
 {
     extern __shared__ __align__(16) uint8_t lds[];
@@ -646,13 +651,12 @@ __global__ __launch_bounds__(256, 3) void k_gu_one(GuOneParams p)
     const int H = p.H, HB = H >> 1, HG = H >> 5;  // packed bytes and E8M0 groups per row
     const int mat = wave & 1, half = wave >> 1;
     uint8_t *sc_l = lds + wave * (H / 2);                                  // this wave's 16 E8M0 rows
-    float *sum_l = reinterpret_cast<float *>(lds + 2 * H);                 // [4][16]
-    u4 *x_l = reinterpret_cast<u4 *>(sum_l + 4 * kDecUnitRows);            // [NS][64]
+    float *sum_l = reinterpret_cast<float *>(lds + 2 * H);                 // [NT][4][16]
+    u4 *x_l = reinterpret_cast<u4 *>(sum_l + NT * 4 * kDecUnitRows);       // [NT][NS][64]
     const int q = p.items[li];
     const int e = p.active_e[q], off = p.active_off[q];
-    const int t = p.sorted[off] / p.K;  // the assignment's token
 
-    // the rows' first loads, the wave's 16 E8M0 rows (contiguous), the token
+    // the rows' first loads, the wave's 16 E8M0 rows (contiguous), the tokens
     const int row0 = 32 * qb + kDecUnitRows * half;
     const uint8_t *sbase = (mat ? p.us + (int64_t)e * p.u_ss : p.gs + (int64_t)e * p.g_ss) + (size_t)row0 * HG;
     const uint8_t *wbase = (mat ? p.up + (int64_t)e * p.u_sp : p.gp + (int64_t)e * p.g_sp) + (size_t)row0 * HB;
@@ -674,17 +678,20 @@ __global__ __launch_bounds__(256, 3) void k_gu_one(GuOneParams p)
 #pragma unroll
         for (int s = 0; s < kDecGuPieces; ++s) b.a[s] = ld16_stream(wbase + ro + soff[s]);
     };
-    // issue order: the token (cache hits), the E8M0 rows, then the routed
+    // issue order: the tokens (cache hits), the E8M0 rows, then the routed
     // rows, so the LDS stores wait only for the first two and the rows stay
     // in flight across the barrier (memory counters retire in issue order)
     constexpr int XQ = (NS * 64 + 255) / 256;
-    const uint16_t *xt = p.x + (size_t)t * H;
-    u4 xs[XQ];
+    u4 xs[NT][XQ];
 #pragma unroll
-    for (int k = 0; k < XQ; ++k) {
-        const int i = threadIdx.x + 256 * k;
-        const bool on = i < NS * 64 && 8 * i < H;
-        xs[k] = ld16m(xt + (on ? 8 * i : 0), lane_mask(on));
+    for (int c = 0; c < NT; ++c) {
+        const uint16_t *xt = p.x + (size_t)(p.sorted[off + c] / p.K) * H;  // assignment c's token
+#pragma unroll
+        for (int k = 0; k < XQ; ++k) {
+            const int i = threadIdx.x + 256 * k;
+            const bool on = i < NS * 64 && 8 * i < H;
+            xs[c][k] = ld16m(xt + (on ? 8 * i : 0), lane_mask(on));
+        }
     }
     constexpr int SQ = 8192 / 2 / 1024;  // 16-byte pieces per lane (H <= 8192)
     u4 scv[SQ];
@@ -699,10 +706,12 @@ __global__ __launch_bounds__(256, 3) void k_gu_one(GuOneParams p)
 #pragma unroll
     for (int d = 0; d < GD; ++d) load(d, bq[d]);
 #pragma unroll
-    for (int k = 0; k < XQ; ++k) {
-        const int i = threadIdx.x + 256 * k;
-        if (i < NS * 64) x_l[i] = xs[k];
-    }
+    for (int c = 0; c < NT; ++c)
+#pragma unroll
+        for (int k = 0; k < XQ; ++k) {
+            const int i = threadIdx.x + 256 * k;
+            if (i < NS * 64) x_l[c * NS * 64 + i] = xs[c][k];
+        }
 #pragma unroll
     for (int k = 0; k < SQ; ++k) {
         const int i = 16 * lane + 1024 * k;
@@ -710,8 +719,9 @@ __global__ __launch_bounds__(256, 3) void k_gu_one(GuOneParams p)
     }
     __syncthreads();  // the token slices and this wave's E8M0 rows
 
-    // the token at this lane's K positions (lane l of row piece s: elements
-    // 2048 s + 32 l + [0, 32))
+    // the first token at this lane's K positions (lane l of row piece s:
+    // elements 2048 s + 32 l + [0, 32)); an off lane's weights are scaled by
+    // 0, so what it reads for a token does not matter (index 0)
     u4 xv[kDecGuPieces][4];
 #pragma unroll
     for (int s = 0; s < kDecGuPieces; ++s)
@@ -721,17 +731,36 @@ __global__ __launch_bounds__(256, 3) void k_gu_one(GuOneParams p)
             xv[s][c] = ld16m(x_l + (i < H ? i / 8 : 0), lane_mask(i < H));
         }
 
-    float mine = 0.0f;
+    float mine[NT];
+#pragma unroll
+    for (int c = 0; c < NT; ++c) mine[c] = 0.0f;
     auto compute = [&](int r, const Row &b) {
-        v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        v4f acc[NT];
+#pragma unroll
+        for (int c = 0; c < NT; ++c) acc[c] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        // the second token's slice base, opaque to the compiler: its reads
+        // are the same for every row and would otherwise be hoisted out of
+        // the unrolled row loop into 64 registers (it spilled)
+        int x1 = NS * 64;
+        asm volatile("" : "+v"(x1));
 #pragma unroll
         for (int s = 0; s < kDecGuPieces; ++s) {
             const float f = __uint_as_float(__float_as_uint(e8m0_to_f32(sc_l[r * HG + gidx[s]])) & smask[s]);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) acc = mfma_bf16(dequant8_bf16(b.a[s][c], f), as_bf8(xv[s][c]), acc);
+            for (int st = 0; st < 4; ++st) {
+                const bf8 a = dequant8_bf16(b.a[s][st], f);
+                acc[0] = mfma_bf16(a, as_bf8(xv[s][st]), acc[0]);
+                if constexpr (NT > 1) {
+                    const int i = 2048 * s + 32 * lane + 8 * st;
+                    acc[1] = mfma_bf16(a, as_bf8(x_l[x1 + (i < H ? i / 8 : 0)]), acc[1]);
+                }
+            }
         }
-        const float v = diag_sum(acc);
-        mine = lane == r ? v : mine;
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+            const float v = diag_sum(acc[c]);
+            mine[c] = lane == r ? v : mine[c];
+        }
     };
     // fully unrolled: the rows' next loads stop at the last row
 #pragma unroll
@@ -744,20 +773,25 @@ __global__ __launch_bounds__(256, 3) void k_gu_one(GuOneParams p)
         }
     }
     __builtin_amdgcn_s_setprio(0);
-    if (lane < kDecUnitRows) sum_l[wave * kDecUnitRows + lane] = mine;
+    if (lane < kDecUnitRows)
+#pragma unroll
+        for (int c = 0; c < NT; ++c) sum_l[(c * 4 + wave) * kDecUnitRows + lane] = mine[c];
     __syncthreads();
 
-    // wave 0, lane l < 32: row 32 qb + l (half l / 16, row l % 16)
-    if (wave == 0 && lane < 32) {
-        const int hl = lane >> 4, rl = lane & 15;
-        const float g = sum_l[(2 * hl) * kDecUnitRows + rl], u = sum_l[(2 * hl + 1) * kDecUnitRows + rl];
+    // wave 0, lane l < 32 NT: assignment c = l / 32, row 32 qb + l % 32
+    // (half (l % 32) / 16, row l % 16)
+    if (wave == 0 && lane < 32 * NT) {
+        const int c = lane >> 5, ll = lane & 31, hl = ll >> 4, rl = ll & 15;
+        const float g = sum_l[(c * 4 + 2 * hl) * kDecUnitRows + rl];
+        const float u = sum_l[(c * 4 + 2 * hl + 1) * kDecUnitRows + rl];
         const float a = act_fn(g, u, p.act, p.b1, p.b2);
         const uint16_t h = bf16_rne(a);
-        const size_t o = (size_t)off * p.I + 32 * qb + lane;
+        const size_t o = (size_t)(off + c) * p.I + 32 * qb + ll;
         p.act_hi[o] = h;
         p.act_lo[o] = bf16_rne(a - bf16f(h));
     }
 }
+
 }  // namespace
 
 // The shapes the three kernels take: a flat layer, H <= 8192 (four 1 KB
@@ -878,11 +912,11 @@ hipError_t launch_decode_fused(const LayerView &L, const uint16_t *x, int32_t *i
 }
 
 
-// Gate/up of the light items with one assignment (a flat layer: the routed
-// input is x itself).
+// Gate/up of the light items with nt (1 or 2) assignments (a flat layer:
+// the routed input is x itself).
 bool gu_one_ok(const LayerView &L) { return L.Lt == 0 && L.H <= 8192 && L.H % 128 == 0 && L.I % 32 == 0; }
 
-hipError_t launch_gu_one(const LayerView &L, const uint16_t *x, int T, const int32_t *active_e,
+hipError_t launch_gu_one(const LayerView &L, const uint16_t *x, int T, int nt, const int32_t *active_e,
                          const int32_t *active_off, const int32_t *sorted, const int32_t *items,
                          const int32_t *items_n, uint16_t *act_hi, uint16_t *act_lo, hipStream_t s)
 {
@@ -912,11 +946,17 @@ hipError_t launch_gu_one(const LayerView &L, const uint16_t *x, int T, const int
     const int64_t cap = std::min<int64_t>(L.E, (int64_t)T * L.K);  // the most items a batch can have
     const unsigned nb = (unsigned)(cap * (L.I / 32));
     const int NS = L.H <= 2048 ? 4 : L.H <= 4096 ? 8 : L.H <= 7168 ? 14 : 16;
-    const size_t lds = gu_one_lds_bytes(L.H, NS);
-    if (NS == 4) k_gu_one<4><<<nb, 256, lds, s>>>(p);
-    else if (NS == 8) k_gu_one<8><<<nb, 256, lds, s>>>(p);
-    else if (NS == 14) k_gu_one<14><<<nb, 256, lds, s>>>(p);
-    else k_gu_one<16><<<nb, 256, lds, s>>>(p);
+    const size_t lds = gu_one_lds_bytes(L.H, NS, nt);
+#define K3_ONE(NSL)                                                    \
+    do {                                                               \
+        if (nt == 1) k_gu_one<NSL, 1><<<nb, 256, lds, s>>>(p);         \
+        else k_gu_one<NSL, 2><<<nb, 256, lds, s>>>(p);                 \
+    } while (0)
+    if (NS == 4) K3_ONE(4);
+    else if (NS == 8) K3_ONE(8);
+    else if (NS == 14) K3_ONE(14);
+    else K3_ONE(16);
+#undef K3_ONE
     return hipGetLastError();
 }
 

@@ -47,36 +47,38 @@ constexpr int kTileTerms = 3;
 // ---------------------------------------------------------------------------
 // Work lists. Active expert q (ascending id) with n_q assignments goes to the
 // gate/up weight-streaming kernel when n_q <= smax_gu (light_gu[] lists such
-// q in order; with one_gu, those with n_q == 1 go to light1[] instead, for
-// the one-assignment gate/up kernel), else gets ceil(n_q / bn_gu) GEMM tiles
-// (q, token block); the same for the down projection with smax_dn, bn_dn.
+// q in order; with one_gu, those with n_q == 1 or 2 go to light1[] or
+// light2[] instead, for the whole-row gate/up kernel), else gets
+// ceil(n_q / bn_gu) GEMM tiles (q, token block); the same for the down
+// projection with smax_dn, bn_dn.
 // counts: [0] gate/up tiles, [1] down tiles, [2] gate/up light, [3] down
-// light, [4] gate/up light with one assignment.
-constexpr int kTileCounts = 5;
+// light, [4] gate/up light with one assignment, [5] with two.
+constexpr int kTileCounts = 6;
 __global__ __launch_bounds__(1024) void k_tiles(const int32_t *__restrict__ active_n,
                                                 const int32_t *__restrict__ active_off, int bn_gu,
                                                 int bn_dn, int smax_gu, int smax_dn, int one_gu,
                                                 int2 *__restrict__ tiles_gu, int2 *__restrict__ tiles_dn,
                                                 int32_t *__restrict__ light_gu, int32_t *__restrict__ light_dn,
-                                                int32_t *__restrict__ light1, int32_t *counts)
+                                                int32_t *__restrict__ light1, int32_t *__restrict__ light2,
+                                                int32_t *counts)
 {
     __shared__ int wsum[kTileCounts][16];
     const int n = *active_n;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int per = (n + 1023) / 1024;
     const int q0 = tid * per;
-    int cnt[kTileCounts] = {0, 0, 0, 0, 0};
+    int cnt[kTileCounts] = {0, 0, 0, 0, 0, 0};
     for (int i = 0; i < per; ++i) {
         const int q = q0 + i;
         if (q < n) {
             const int m = active_off[q + 1] - active_off[q];
-            if (m <= smax_gu) cnt[one_gu && m == 1 ? 4 : 2] += 1;
+            if (m <= smax_gu) cnt[one_gu && m <= 2 ? 3 + m : 2] += 1;
             else cnt[0] += (m + bn_gu - 1) / bn_gu;
             if (m <= smax_dn) cnt[3] += 1;
             else cnt[1] += (m + bn_dn - 1) / bn_dn;
         }
     }
-    int inc[kTileCounts] = {cnt[0], cnt[1], cnt[2], cnt[3], cnt[4]};  // inclusive scans across the wave
+    int inc[kTileCounts] = {cnt[0], cnt[1], cnt[2], cnt[3], cnt[4], cnt[5]};  // inclusive scans across the wave
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
 #pragma unroll
@@ -102,13 +104,14 @@ __global__ __launch_bounds__(1024) void k_tiles(const int32_t *__restrict__ acti
     __syncthreads();
     int bg = wsum[0][wv] + inc[0] - cnt[0], bd = wsum[1][wv] + inc[1] - cnt[1];
     int lg = wsum[2][wv] + inc[2] - cnt[2], ld = wsum[3][wv] + inc[3] - cnt[3];
-    int l1 = wsum[4][wv] + inc[4] - cnt[4];
+    int l1 = wsum[4][wv] + inc[4] - cnt[4], l2 = wsum[5][wv] + inc[5] - cnt[5];
     for (int i = 0; i < per; ++i) {
         const int q = q0 + i;
         if (q < n) {
             const int m = active_off[q + 1] - active_off[q];
             if (m <= smax_gu) {
                 if (one_gu && m == 1) light1[l1++] = q;
+                else if (one_gu && m == 2) light2[l2++] = q;
                 else light_gu[lg++] = q;
             }
             else
@@ -789,7 +792,7 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t 
     const int smax_gu = stream ? stream_max_tokens() : 0, smax_dn = stream_dn ? stream_down_rows(L, T) : 0;
     // grids cover the most tiles the split can produce (most blocks exit at once)
     const size_t cap_gu = grouped_tile_cap(T, L.K, L.E, TG, smax_gu), cap_dn = grouped_tile_cap(T, L.K, L.E, TD, smax_dn);
-    int32_t *light_gu = light, *light_dn = light + L.E, *light1 = light + 2 * L.E;
+    int32_t *light_gu = light, *light_dn = light + L.E, *light1 = light + 2 * L.E, *light2 = light + 3 * L.E;
     // no expert can hold more than T * K assignments (T when the ids come
     // from the router: no expert twice in a token): when that fits the
     // streamed limit, no tile is heavy and the tile GEMMs would only exit
@@ -801,11 +804,11 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t 
     // projection reads rows of experts that ran gate/up on tiles
     const bool f8_dn = gemm_dn && gemm_gu && smax_dn >= smax_gu && tb.aq != nullptr;
     const bool hilo_from_tiles = !f8_dn || smax_dn > smax_gu;
-    // light experts with one assignment (a flat layer) stream their gate/up
-    // rows through the one-token kernel's whole-piece loads
+    // light experts with one or two assignments (a flat layer) stream their
+    // gate/up rows through the one-token kernel's whole-piece loads
     const bool one_gu = stream && !two && gu_one_ok(L);
     k_tiles<<<1, 1024, 0, s>>>(active_n, active_off, TG, TD, smax_gu, smax_dn, one_gu ? 1 : 0, tiles_gu, tiles_dn,
-                               light_gu, light_dn, light1, counts);
+                               light_gu, light_dn, light1, light2, counts);
 
     // gate/up: routed tiles (fp4); the shared expert's tiles go in a launch of
     // their own (different weight rows) unless they stream with the light experts
@@ -816,9 +819,9 @@ hipError_t launch_grouped(const LayerView &L, const uint16_t *x, const uint16_t 
                                                   counts + 2, sh_stream, act_hi, act_lo, ash_hi, ash_lo, sh_part, s);
             if (e != hipSuccess) return e;
         }
-        if (one_gu) {
-            const hipError_t e = launch_gu_one(L, xr, T, active_e, active_off, sorted, light1, counts + 4, act_hi,
-                                               act_lo, s);
+        for (int nt = 1; one_gu && nt <= 2; ++nt) {
+            const hipError_t e = launch_gu_one(L, xr, T, nt, active_e, active_off, sorted, nt == 1 ? light1 : light2,
+                                               counts + 3 + nt, act_hi, act_lo, s);
             if (e != hipSuccess) return e;
         }
         GemmParams gp{};

@@ -36,10 +36,10 @@ struct WsLayout {
     size_t sh_part;           // shared gate/up fp32 slice sums [slices][T][2][I_s] (small batches)
     size_t ys;                // expert outputs fp32 [T][k + 1][H] (slot k: shared expert)
     size_t tiles_gu, tiles_dn;  // grouped-GEMM tile lists, int2 each
-    size_t light;             // int32 [3][E]: experts for the weight-streaming kernels (gate/up, down,
-                              //   gate/up with one assignment)
-    size_t tile_n;            // int32 [5]: gate/up tiles, down tiles, light gate/up, light down,
-                              //   light gate/up with one assignment
+    size_t light;             // int32 [4][E]: experts for the weight-streaming kernels (gate/up, down,
+                              //   gate/up with one assignment, with two)
+    size_t tile_n;            // int32 [6]: gate/up tiles, down tiles, light gate/up, light down,
+                              //   light gate/up with one assignment, with two
     // f8 down tiles: the routed activation as n e4m3 terms [T*k][n][I] and
     // their E8M0 bytes [T*k][n][I/32] (the tiles write n = 3; sized for
     // kATerms)
@@ -155,12 +155,12 @@ hipError_t launch_decode_fused(const LayerView &L, const uint16_t *x, int32_t *i
                                bool route, float *out, char *ws, const WsLayout &lay, hipStream_t s,
                                Profiler *prof, const OutEpi &epi = OutEpi(), bool routed = false);
 
-// Gate/up of a batch's light experts that hold one assignment each
+// Gate/up of a batch's light experts that hold nt (1 or 2) assignments each
 // (k3moe_decode.hip): items[0 .. *items_n) are active-list positions; the
 // activation goes to act_hi/act_lo rows (the assignment's position), as the
 // streamed gate/up writes it. gu_one_ok: the shapes it takes.
 bool gu_one_ok(const LayerView &L);
-hipError_t launch_gu_one(const LayerView &L, const uint16_t *x, int T, const int32_t *active_e,
+hipError_t launch_gu_one(const LayerView &L, const uint16_t *x, int T, int nt, const int32_t *active_e,
                          const int32_t *active_off, const int32_t *sorted, const int32_t *items,
                          const int32_t *items_n, uint16_t *act_hi, uint16_t *act_lo, hipStream_t s);
 
