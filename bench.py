@@ -255,22 +255,24 @@ def main():
     # (4 B per element: fp32, or bf16 hi + lo), expert outputs staged in fp32
     x_read = T * H * 2 + (T * Lt * 4 if Lt else 0)   # the bf16 tokens (+ the latent's hi/lo planes)
     act_b = T * K * I * 4 + T * Is * 4
-    # the one-token fused path (a flat layer, one token, through route_forward
-    # or step): router | shared gate/up + top-k + routed gate/up | shared
-    # down + routed down + router-order sum (no separate combine)
-    fused = "combine" not in stage_us and not Lt and T == 1 and cache is None
-    # flat layers at 2..4 tokens run the single-token kernels once per token
+    # the fused one-token kernels (a flat layer, 1..8 tokens, no combine
+    # stage), once per token: router | shared gate/up + (at one token the
+    # top-k) + routed gate/up | shared down + routed down + router-order sum;
+    # each token's pass reads its own experts and the shared expert again
+    fused = "combine" not in stage_us and not Lt and T <= 8 and cache is None
+    # the older single-token kernels once per token, then one combine
     per_token = not fused and not Lt and T <= 4 and cache is None
     if fused:
         terms = K * 3 * I + K * 3 * (I // 32)   # the activations as three e4m3 terms and their scales
+        scores = E * 8 if T == 1 else 0          # the fused top-k reads the scores
+        epi = H * 4 * (2 if args.workload in ("step", "stack") else 1)
         stage_bytes = {
-            "router": router_bytes + H * 2 + E * 8,
-            "gateup": nd * 2 * gu + 2 * Is * H * 2 + H * 2 + E * 8 + terms + Is * 4 + K * 8,
-            "down": nd * dn + Is * H * 2 + terms + Is * 4 + K * 8 + H * 4 * (2 if args.workload in ("step", "stack") else 1),
+            "router": router_bytes + T * H * 2 + T * E * 8,
+            "gateup": T * (K * 2 * gu + 2 * Is * H * 2 + H * 2 + terms + Is * 4 + K * 8) + scores,
+            "down": T * (K * dn + Is * H * 2 + terms + Is * 4 + K * 8 + epi),
         }
     elif per_token:
-        # a few tokens (2..4) on the single-token kernels, one pass per token:
-        # each pass reads its token's experts and the shared expert again
+        # the older single-token kernels, one pass per token
         stage_bytes = {
             "gateup": T * (K * 2 * gu + 2 * Is * H * 2 + H * 2 + K * I * 4 + Is * 4),
             "down": T * (K * dn + Is * H * 2 + K * I * 4 + Is * 4 + (K + 1) * H * 4),
@@ -291,24 +293,23 @@ def main():
     if Lt:
         stage_bytes["latent_in"] = Lt * H * 2 + T * H * 2 + T * Lt * 4
         stage_bytes["latent_out"] = H * Lt * 2 + Lt * 4 + T * Lt * 12 + T * H * 8
-    one_tok = {"gateup": "k_gateup_dec", "down": "k_down_dec"}   # the per-token loop's kernels
-    kernels = {"decode": ({"router": "k_router", "gateup": "k_dec_gateup", "down": "k_dec_down"} if fused
-                          else one_tok),
-               "batched": one_tok if per_token else {"gateup": "k_gu_stream", "down": "k_dn_stream"},
+    one_tok = {"gateup": "k_gateup_dec", "down": "k_down_dec"}   # the older per-token loop's kernels
+    fused_k = {"router": "k_router", "gateup": "k_dec_gateup", "down": "k_dec_down"}
+    stream_k = {"gateup": "k_gu_stream", "down": "k_dn_stream"}
+    step_k = (dict(fused_k, router="k_prenorm_router") if fused and T == 1
+              else dict(fused_k, prenorm="k_prenorm") if fused
+              else dict(one_tok, prenorm="k_prenorm") if per_token
+              else dict(stream_k, prenorm="k_prenorm"))
+    kernels = {"decode": fused_k if fused else one_tok,
+               "batched": fused_k if fused else one_tok if per_token else stream_k,
                "prefill": {"gateup": "k_gu_gemm + k_gu_stream", "down": "k_dn_gemm + k_dn_stream"},
                "latent": ({"gateup": "k_gateup_dec", "down": "k_down_dec", "latent_in": "k_gv_down",
                            "latent_out": "k_gv_up"} if T == 1 else
                           {"gateup": "k_gu_stream", "down": "k_dn_stream", "latent_in": "k_proj",
                            "latent_out": "k_proj + k_rms_split"}),
-               "step": ({"router": "k_prenorm_router", "gateup": "k_dec_gateup", "down": "k_dec_down"}
-                        if T == 1
-                        else dict(one_tok, prenorm="k_prenorm") if per_token
-                        else {"gateup": "k_gu_stream", "down": "k_dn_stream", "prenorm": "k_prenorm"}),
+               "step": step_k,
                "cache": {"cache_fill": "k_cache_fill"},
-               "stack": ({"router": "k_prenorm_router", "gateup": "k_dec_gateup", "down": "k_dec_down"}
-                         if T == 1
-                         else dict(one_tok, prenorm="k_prenorm") if per_token
-                         else {"gateup": "k_gu_stream", "down": "k_dn_stream", "prenorm": "k_prenorm"})}[args.workload]
+               "stack": step_k}[args.workload]
     # the hot experts' tile GEMMs: algorithmic flops (2 per multiply-add,
     # gate and up, per assignment) and issued flops (whole token tiles). A flat
     # layer's shared gate/up tiles run in the same launch once the shared
@@ -333,7 +334,7 @@ def main():
     dom_us = stage_us.get(dom, 0.0)
     achieved = stage_bytes[dom] / (dom_us * 1e-6) / 1e9 if dom_us > 0 else 0.0
     peak = HBM_PEAK_GBPS if cache is None else HOST_LINK_PEAK_GBPS
-    prof_rec = profiled_kernel(kernels[dom])
+    prof_rec = profiled_kernel(kernels[dom]) if T == 1 else None   # the record is of one-token dispatches
     traffic = prof_rec.get("hbm_bytes") if prof_rec else None
     value = nl * routed_bytes / (ms * 1e-3) / 1e9
     layer_bytes = routed_bytes + router_bytes + shared_bytes + proj_bytes + T * H * 2 + T * H * 4

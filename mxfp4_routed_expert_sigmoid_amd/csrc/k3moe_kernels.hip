@@ -1389,11 +1389,18 @@ void launch_combine(const LayerView &L, const float *ys, const float *w, const i
         ys, w, idx, T, L.K, width, L.E, shared, out, L.errors, epi.resid, epi.ob);
 }
 
-// Batches up to this size take the single-token kernels once per token: at
-// T <= 4 that beats one weight-streaming pass over the union of their experts
-// (full flat shape: T = 2 165 us against 216, T = 4 310 against 354); from
-// about 5 tokens on, streaming each distinct expert once wins.
+// Batches up to these sizes run one-token kernels once per token instead of
+// one weight-streaming pass over the union of their experts. With the fused
+// one-token kernels (full flat shape, a decoder-layer step of distinct
+// routes per token) the per-token loop costs ~63 us a token and wins up to
+// 8 tokens: T = 2 139 us against 166 for the older one-token kernels and a
+// combine, T = 4 263 against 311, T = 5 322 against 357 streamed, T = 6 383
+// against 415, T = 8 503 against 533. A batch whose tokens share most of
+// their experts would stream faster, but the routes are on the device when
+// this is decided. Shapes the fused kernels do not take use the older
+// one-token kernels up to 4 tokens (T = 4 310 us against 354 streamed).
 constexpr int kT1LoopMax = 4;
+constexpr int kFusedLoopMax = 8;
 
 hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const int32_t *idx,
                           const float *w, float *out, char *ws, const WsLayout &lay, hipStream_t s,
@@ -1406,13 +1413,27 @@ hipError_t launch_forward(const LayerView &L, const uint16_t *x, int T, const in
     int32_t *sorted = reinterpret_cast<int32_t *>(ws + lay.sorted);
     float *ys = reinterpret_cast<float *>(ws + lay.ys);
 
+    // up to kFusedLoopMax tokens: the fused one-token kernels (gate/up with the
+    // shared rows, down with the router-order sum and the epilogue) once per
+    // token, in token order, each writing its own output row; the workspace
+    // regions they use are reused, stream order keeping the passes apart.
+    // The ids and weights are only read (no routing here).
+    if (T <= kFusedLoopMax && decode_fused_ok(L)) {
+        for (int t = 0; t < T; ++t) {
+            OutEpi et = epi;
+            if (et.ob) et.ob += (size_t)t * L.H;
+            const hipError_t e = launch_decode_fused(L, x + (size_t)t * L.H, const_cast<int32_t *>(idx + (size_t)t * L.K),
+                                                     const_cast<float *>(w + (size_t)t * L.K), nullptr, false,
+                                                     out + (size_t)t * L.H, ws, lay, s, prof, et, false);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    // shapes the fused kernels do not take: the single-token kernels once per
+    // token, each writing its token's staging rows of ys, then one combine
     if (T == 1 && decode_path_ok(L))
         return launch_forward_t1(L, x, x, nullptr, idx, w, out, reinterpret_cast<float *>(ws + lay.act),
                                  reinterpret_cast<float *>(ws + lay.ash), ws + lay.ys, nullptr, s, prof, epi);
-    // up to kT1LoopMax tokens: the single-token kernels once per token, in
-    // token order, each writing its token's staging rows of ys (the
-    // activation rows are reused: stream order keeps the passes apart), then
-    // one combine over the batch
     if (T <= kT1LoopMax && decode_path_ok(L)) {
         for (int t = 0; t < T; ++t) {
             const uint16_t *xt = x + (size_t)t * L.H;

@@ -227,7 +227,7 @@ def _mid(seed, routing="normal", T_bad=False):
     return spec, t, sd.make_layer(spec, t)
 
 
-@pytest.mark.parametrize("T,routing", [(1, "normal"), (2, "normal"), (5, "normal"), (17, "normal"),
+@pytest.mark.parametrize("T,routing", [(1, "normal"), (2, "normal"), (5, "normal"), (9, "normal"), (17, "normal"),
                                        (40, "normal"), (128, "normal"), (129, "zipf"), (300, "zipf")])
 def test_mid_stream_and_gemm_mix(T, routing):
     spec, t, layer = _mid(seed=20 + T, routing=routing)
@@ -374,9 +374,9 @@ def test_full_decode_T1():
     assert np.array_equal(out, _forward_gpu(layer, x, idx_r, w_r))
 
 
-@pytest.mark.parametrize("T", [3, 4])
+@pytest.mark.parametrize("T", [3, 4, 8])
 def test_full_small_batch_per_token(T):
-    # batches of a few tokens run the single-token kernels once per token,
+    # batches of up to 8 tokens run the single-token kernels once per token,
     # sharing one token's workspace rows in stream order
     spec, t, layer = _full()
     Wr, bias = synth.make_router(spec), synth.make_bias(spec)
